@@ -1,0 +1,306 @@
+/* k3o: CPU oracle for the Kimi K3 Stable LatentMoE routed-expert layer.
+ * TEST INFRASTRUCTURE: only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg use this file. Source tags ([K3C-4] ...) are listed in k3o.h. */
+#include "k3o.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* [K3C-4] the E2M1 value table printed with the checkpoint fixture, and [COL]:
+ * sign in bit 3, two exponent bits, one mantissa bit. Code 8 is -0. */
+static const float K3O_E2M1[16] = {
+    0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f,
+    -0.0f, -0.5f, -1.0f, -1.5f, -2.0f, -3.0f, -4.0f, -6.0f,
+};
+
+float k3o_e2m1(int code) { return K3O_E2M1[code & 15]; }
+
+/* [K3C-4]: a ue8m0 byte b is the power of two 2^(b-127); the byte 255 (NaN in the
+ * MX specification) is read as 0 so that a corrupt byte zeroes one group. */
+float k3o_e8m0(int byte)
+{
+    if (byte == 255) return 0.0f;
+    return ldexpf(1.0f, byte - 127);
+}
+
+/* [K3C-5]: bf16 is the top half of an fp32; widening appends 16 zero bits. */
+float k3o_bf16_to_f32(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* [K3C-4], [COL]: column c of a row lives in byte c/2; an even column is the low
+ * nibble and an odd column the high nibble. Column c uses the scale byte of its
+ * group c/group. The product E2M1 * 2^k is exact in fp32 (two significant bits).
+ * A row of odd width ends with a byte whose high nibble is unused. */
+void k3o_mxfp4_decode_row(float *w, const uint8_t *packed_row, const uint8_t *scale_row,
+                          int cols, int group)
+{
+    for (int c = 0; c < cols; c++) {
+        const uint8_t byte = packed_row[c / 2];
+        const int code = (c % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
+        w[c] = k3o_e2m1(code) * k3o_e8m0(scale_row[c / group]);
+    }
+}
+
+/* [K3C-4]: y = W x with W kept in its packed form; every product and sum in fp64,
+ * one rounding to fp32 at the end of each row. Decoding a row into a small buffer
+ * first is the same arithmetic: each weight is an exact fp32 value. */
+void k3o_mxfp4_matvec(float *y, const float *x, const uint8_t *packed, const uint8_t *scales,
+                      int cols, int rows, int group)
+{
+    const size_t row_bytes = (size_t)(cols + 1) / 2;
+    const size_t row_groups = (size_t)(cols + group - 1) / group;
+    float *w = (float *)malloc(sizeof(float) * (size_t)cols);
+    for (int r = 0; r < rows; r++) {
+        k3o_mxfp4_decode_row(w, packed + (size_t)r * row_bytes, scales + (size_t)r * row_groups,
+                             cols, group);
+        double acc = 0.0;
+        for (int c = 0; c < cols; c++) acc += (double)x[c] * (double)w[c];
+        y[r] = (float)acc;
+    }
+    free(w);
+}
+
+/* [K3C-5]: W is [out][in] bf16, widened exactly; fp64 sum, fp32 result. */
+void k3o_bf16_matvec(float *y, const float *x, const uint16_t *W, int in, int out)
+{
+    for (int o = 0; o < out; o++) {
+        const uint16_t *row = W + (size_t)o * in;
+        double acc = 0.0;
+        for (int i = 0; i < in; i++) acc += (double)x[i] * (double)k3o_bf16_to_f32(row[i]);
+        y[o] = (float)acc;
+    }
+}
+
+static int k3o_cmp_int(const void *a, const void *b)
+{
+    const int x = *(const int *)a, y = *(const int *)b;
+    return (x > y) - (x < y);
+}
+
+/* [K3C-9], [COL]: score every expert with a sigmoid of its logit (the unbiased
+ * score sc); add the score-correction bias to get the selection score ch; take K
+ * times the not-yet-chosen expert with the largest ch, where a later expert must be
+ * strictly larger to win (so the lowest id wins a tie); weight each chosen expert
+ * by its unbiased score, renormalised over the K chosen when renorm is set, then
+ * multiplied by routed_scale.
+ * Readings: the logit is an fp64 sum; sc is the fp64 sigmoid rounded to fp32;
+ * ch = sc + bias in fp64; the renormalisation sum and division are fp64 and the
+ * weight is rounded to fp32 once; the K ids are returned in ascending order (the
+ * selection order is available separately). */
+double k3o_router(int *idx, float *w, int *sel_order, const float *x, const float *Wr,
+                  const float *bias, int hidden, int n_experts, int topk, int renorm,
+                  float routed_scale)
+{
+    float *sc = (float *)malloc(sizeof(float) * (size_t)n_experts);
+    double *ch = (double *)malloc(sizeof(double) * (size_t)n_experts);
+    unsigned char *taken = (unsigned char *)calloc((size_t)n_experts, 1);
+    int *pick = (int *)malloc(sizeof(int) * (size_t)topk);
+
+    for (int e = 0; e < n_experts; e++) {
+        const float *row = Wr + (size_t)e * hidden;
+        double logit = 0.0;
+        for (int i = 0; i < hidden; i++) logit += (double)x[i] * (double)row[i];
+        sc[e] = (float)(1.0 / (1.0 + exp(-logit)));
+        ch[e] = (double)sc[e] + (bias ? (double)bias[e] : 0.0);
+    }
+
+    double last = 0.0;
+    for (int j = 0; j < topk; j++) {
+        int best = -1;
+        for (int e = 0; e < n_experts; e++) {
+            if (taken[e]) continue;
+            if (best < 0 || ch[e] > ch[best]) best = e;
+        }
+        taken[best] = 1;
+        pick[j] = best;
+        last = ch[best];
+    }
+    double next = -INFINITY;
+    for (int e = 0; e < n_experts; e++)
+        if (!taken[e] && ch[e] > next) next = ch[e];
+    const double gap = (topk < n_experts) ? (last - next) : INFINITY;
+
+    if (sel_order) memcpy(sel_order, pick, sizeof(int) * (size_t)topk);
+    memcpy(idx, pick, sizeof(int) * (size_t)topk);
+    qsort(idx, (size_t)topk, sizeof(int), k3o_cmp_int);
+
+    double s = 0.0;
+    for (int j = 0; j < topk; j++) s += (double)sc[idx[j]];
+    for (int j = 0; j < topk; j++) {
+        double v = (double)sc[idx[j]];
+        if (renorm && s > 0.0) v /= s;
+        w[j] = (float)(v * (double)routed_scale);
+    }
+
+    free(sc);
+    free(ch);
+    free(taken);
+    free(pick);
+    return gap;
+}
+
+/* [K3C-9], [COL]: SiTU-GLU, b1*tanh(g/b1)*sigmoid(g) * b2*tanh(u/b2); the sigmoid
+ * reads the uncapped gate g. fp64 inside, fp32 result (the GLU intermediate is fp32). */
+float k3o_situ(float g, float u, float b1, float b2)
+{
+    const double gd = (double)g, ud = (double)u;
+    const double a = (double)b1 * tanh(gd / (double)b1) * (1.0 / (1.0 + exp(-gd)));
+    const double v = (double)b2 * tanh(ud / (double)b2);
+    return (float)(a * v);
+}
+
+/* [K3C-5]: inv = 1/sqrt(sum(x^2)/n + eps), eps inside the root; out = x*inv*w.
+ * Reading: fp64 throughout, one rounding per output element. */
+void k3o_rmsnorm(float *out, const float *x, const float *w, int n, float eps)
+{
+    double ss = 0.0;
+    for (int i = 0; i < n; i++) ss += (double)x[i] * (double)x[i];
+    const double inv = 1.0 / sqrt(ss / (double)n + (double)eps);
+    for (int i = 0; i < n; i++)
+        out[i] = (float)((double)x[i] * inv * (w ? (double)w[i] : 1.0));
+}
+
+/* [K3C-9], [COL]: one routed expert in the latent space: gate and up rows of w1, w3
+ * read z; SiTU-GLU; w2 maps the fp32 intermediate back to the latent width. */
+void k3o_expert(float *edn, float *g, float *u, float *act, const float *z,
+                const k3o_experts *ex, int e, const k3o_dims *d)
+{
+    const int L = d->latent, I = d->inter;
+    float *gg = (float *)malloc(sizeof(float) * (size_t)I * 3);
+    float *uu = gg + I, *aa = uu + I;
+    k3o_mxfp4_matvec(gg, z, ex->w1.packed + (size_t)e * ex->w1.packed_stride,
+                     ex->w1.scales + (size_t)e * ex->w1.scales_stride, L, I, d->group);
+    k3o_mxfp4_matvec(uu, z, ex->w3.packed + (size_t)e * ex->w3.packed_stride,
+                     ex->w3.scales + (size_t)e * ex->w3.scales_stride, L, I, d->group);
+    for (int r = 0; r < I; r++) aa[r] = k3o_situ(gg[r], uu[r], d->b1, d->b2);
+    k3o_mxfp4_matvec(edn, aa, ex->w2.packed + (size_t)e * ex->w2.packed_stride,
+                     ex->w2.scales + (size_t)e * ex->w2.scales_stride, I, L, d->group);
+    if (g) memcpy(g, gg, sizeof(float) * (size_t)I);
+    if (u) memcpy(u, uu, sizeof(float) * (size_t)I);
+    if (act) memcpy(act, aa, sizeof(float) * (size_t)I);
+    free(gg);
+}
+
+/* Grouping the (token, slot) pairs by expert is the GPU path's way to read each
+ * expert once per call; its plain definition is a stable counting sort by expert id
+ * (the pages' CPU analogue is loading each unique expert of a chunk once, colibri
+ * docs/kimi_k3.md "Chunked prefill"). */
+int k3o_dispatch(const int *topk_idx, int T, int K, int E, int *expert_off,
+                 int *sorted_pair, int *pair_slot)
+{
+    const int P = T * K;
+    for (int p = 0; p < P; p++)
+        if (topk_idx[p] < 0 || topk_idx[p] >= E) return -1;
+    int *fill = (int *)calloc((size_t)E, sizeof(int));
+    for (int e = 0; e <= E; e++) expert_off[e] = 0;
+    for (int p = 0; p < P; p++) expert_off[topk_idx[p] + 1]++;
+    for (int e = 0; e < E; e++) expert_off[e + 1] += expert_off[e];
+    for (int p = 0; p < P; p++) { /* p = t*K + j in increasing order: stable in t */
+        const int e = topk_idx[p];
+        const int pos = expert_off[e] + fill[e]++;
+        sorted_pair[pos] = p;
+        pair_slot[p] = pos;
+    }
+    free(fill);
+    return 0;
+}
+
+static void k3o_token(const k3o_dims *d, const uint16_t *xt_bf16, const k3o_weights *w,
+                      float *yt, int *idx, float *wt, float *z_out, float *acc_out,
+                      float *nrm_out)
+{
+    const int H = d->hidden, L = d->latent, K = d->topk;
+    float *xf = (float *)malloc(sizeof(float) * (size_t)H);
+    float *z = (float *)malloc(sizeof(float) * (size_t)L * 3);
+    float *edn = z + L, *nrm = edn + L;
+    double *acc = (double *)calloc((size_t)L, sizeof(double));
+    float *accf = (float *)malloc(sizeof(float) * (size_t)L);
+
+    for (int i = 0; i < H; i++) xf[i] = k3o_bf16_to_f32(xt_bf16[i]);
+
+    /* [K3C-9] step order: route on the full width, project down to the latent,
+     * run the chosen experts and sum them weighted, norm the AGGREGATE, project up. */
+    k3o_router(idx, wt, NULL, xf, w->w_router, w->bias, H, d->n_experts, K, d->renorm,
+               d->routed_scale);
+    k3o_bf16_matvec(z, xf, w->w_down, H, L);
+    for (int j = 0; j < K; j++) {
+        k3o_expert(edn, NULL, NULL, NULL, z, &w->ex, idx[j], d);
+        for (int c = 0; c < L; c++) acc[c] += (double)wt[j] * (double)edn[c];
+    }
+    for (int c = 0; c < L; c++) accf[c] = (float)acc[c];
+    k3o_rmsnorm(nrm, accf, w->norm_w, L, d->eps);
+    k3o_bf16_matvec(yt, nrm, w->w_up, L, H);
+
+    if (z_out) memcpy(z_out, z, sizeof(float) * (size_t)L);
+    if (acc_out) memcpy(acc_out, accf, sizeof(float) * (size_t)L);
+    if (nrm_out) memcpy(nrm_out, nrm, sizeof(float) * (size_t)L);
+    free(xf);
+    free(z);
+    free(acc);
+    free(accf);
+}
+
+int k3o_layer(const k3o_dims *d, int T, const uint16_t *x, const k3o_weights *w,
+              float *y, int *idx, float *wt, float *z, float *acc, float *nrm, int nthreads)
+{
+    const int H = d->hidden, L = d->latent, K = d->topk;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+    for (int t = 0; t < T; t++)
+        k3o_token(d, x + (size_t)t * H, w, y + (size_t)t * H, idx + (size_t)t * K,
+                  wt + (size_t)t * K, z ? z + (size_t)t * L : NULL,
+                  acc ? acc + (size_t)t * L : NULL, nrm ? nrm + (size_t)t * L : NULL);
+    (void)nthreads;
+    return 0;
+}
+
+void k3o_route_batch(const k3o_dims *d, int T, const uint16_t *x, const float *Wr,
+                     const float *bias, int *idx, float *wt, double *gaps, int nthreads)
+{
+    const int H = d->hidden, K = d->topk;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 4) num_threads(nthreads)
+#endif
+    for (int t = 0; t < T; t++) {
+        float *xf = (float *)malloc(sizeof(float) * (size_t)H);
+        int *ii = (int *)malloc(sizeof(int) * (size_t)K);
+        float *ww = (float *)malloc(sizeof(float) * (size_t)K);
+        for (int i = 0; i < H; i++) xf[i] = k3o_bf16_to_f32(x[(size_t)t * H + i]);
+        const double g = k3o_router(ii, ww, NULL, xf, Wr, bias, H, d->n_experts, K, d->renorm,
+                                    d->routed_scale);
+        if (gaps) gaps[t] = g;
+        if (idx) memcpy(idx + (size_t)t * K, ii, sizeof(int) * (size_t)K);
+        if (wt) memcpy(wt + (size_t)t * K, ww, sizeof(float) * (size_t)K);
+        free(xf);
+        free(ii);
+        free(ww);
+    }
+    (void)nthreads;
+}
+
+void k3o_expert_pairs(const k3o_dims *d, int npairs, const int *tok, const int *ex_id,
+                      const float *z, const k3o_experts *ex, float *edn, float *act,
+                      int nthreads)
+{
+    const int L = d->latent, I = d->inter;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+    for (int q = 0; q < npairs; q++)
+        k3o_expert(edn + (size_t)q * L, NULL, NULL, act ? act + (size_t)q * I : NULL,
+                   z + (size_t)tok[q] * L, ex, ex_id[q], d);
+    (void)nthreads;
+}

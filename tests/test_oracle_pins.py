@@ -1,0 +1,335 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself:
+values printed on the pages (tests/golden/mxfp4_format.json), hand-worked decodes,
+the E2M1 element format's bit-field definition, closed forms and limits, invariants,
+and brute force (tests/_brute.py: dense numpy decode, full sort, fp64 matmul).
+
+Each test is chosen so that a plausible slip in the oracle (a swapped nibble, a
+dropped scale, a wrong sign, the capped gate fed to the sigmoid, eps outside the
+root, biased scores used as weights, a transposed weight) fails at least one.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import k3gen
+import oracle
+from tests import _brute
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "mxfp4_format.json")))
+
+
+# ---------------------------------------------------------------- decode tables
+def test_e2m1_table_matches_page_lut():
+    vals = [oracle.e2m1(c) for c in range(16)]
+    assert vals == GOLDEN["e2m1_lut"]
+    # -0.0 for code 8: sign bit kept
+    assert math.copysign(1.0, oracle.e2m1(8)) == -1.0
+
+
+def test_e2m1_table_matches_bit_field_definition():
+    for c in range(16):
+        assert oracle.e2m1(c) == _brute.e2m1_from_bits(c)
+
+
+@pytest.mark.parametrize("s", [118, 124, 127, 130])
+def test_all_codes_at_scale(s):
+    # every code at four scales against the format definition: value * 2^(s-127)
+    for c in range(16):
+        packed = np.array([[c | (c << 4)] * 16], np.uint8)      # 32 columns, all code c
+        scales = np.array([[s]], np.uint8)
+        row = oracle.mxfp4_decode(packed, scales, 32)[0]
+        want = _brute.e2m1_from_bits(c) * 2.0 ** (s - 127)
+        assert np.all(row == np.float32(want)), (c, s)
+
+
+def test_e8m0_special_bytes():
+    assert oracle.e8m0(127) == 1.0
+    assert oracle.e8m0(255) == 0.0                       # NaN byte zeroes the group
+    assert oracle.e8m0(254) == 2.0 ** 127
+    assert oracle.e8m0(0) == 2.0 ** -127                 # fp32 subnormal, still exact
+
+
+def test_hand_worked_decodes():
+    for byte, s, even, odd in GOLDEN["hand_decodes"]:
+        packed = np.full((1, 16), byte, np.uint8)
+        row = oracle.mxfp4_decode(packed, np.array([[s]], np.uint8), 32)[0]
+        assert row[0] == even and row[1] == odd, (byte, s, row[:2])
+        assert math.copysign(1.0, row[0]) == math.copysign(1.0, even)
+        assert math.copysign(1.0, row[1]) == math.copysign(1.0, odd)
+
+
+def test_nibble_order_one_hot():
+    # A one-hot x = e_c must read column c. Treating the low nibble as the odd
+    # element has the same statistics and fails here.
+    rng = np.random.default_rng(5)
+    rows, cols = 8, 64
+    packed = rng.integers(0, 256, (rows, cols // 2), dtype=np.uint8)
+    scales = rng.integers(120, 130, (rows, cols // 32), dtype=np.uint8)
+    for c in (0, 1, 2, 31, 32, 33, 62, 63):
+        x = np.zeros(cols, np.float32)
+        x[c] = 1.0
+        y = oracle.mxfp4_matvec(x, packed, scales, cols, rows)
+        byte = packed[:, c // 2]
+        code = (byte & 15) if c % 2 == 0 else (byte >> 4)
+        want = np.array([_brute.e2m1_from_bits(int(k)) for k in code]) * 2.0 ** (scales[:, c // 32].astype(np.int64) - 127)
+        assert np.array_equal(y, want.astype(np.float32)), c
+
+
+def test_scale_255_zeroes_only_its_group():
+    packed = np.full((1, 32), 0x22, np.uint8)             # 64 columns of 1.0
+    scales = np.array([[255, 127]], np.uint8)
+    y = oracle.mxfp4_matvec(np.ones(64, np.float32), packed, scales, 64, 1)
+    assert y[0] == 32.0
+
+
+def test_odd_width_tail():
+    # 33 columns: 17 bytes, the last high nibble unused; 2 groups of 32 + 1
+    packed = np.full((1, 17), 0x2F, np.uint8)            # even -6, odd +1
+    packed[0, 16] = 0xF2                                 # column 32 = 1.0, high nibble ignored
+    scales = np.array([[127, 127]], np.uint8)
+    y = oracle.mxfp4_matvec(np.ones(33, np.float32), packed, scales, 33, 1)
+    assert y[0] == 16 * (-6.0) + 16 * 1.0 + 1.0
+
+
+def test_expert_byte_count_closed_form():
+    lay = k3gen.ExpertLayout(k3gen.K3)
+    assert lay.blob_bytes == GOLDEN["bytes_per_expert"]
+    d = k3gen.K3
+    params = 3 * d.inter * d.latent
+    assert params == GOLDEN["params_per_expert"]
+    assert lay.blob_bytes == params * GOLDEN["bytes_per_param"]
+    # the fixture's shape: one w1 slice of 64 rows at width 3584
+    fs = GOLDEN["fixture_shape"]
+    assert fs["packed_cols"] == d.latent // 2 and fs["scale_cols"] == d.latent // d.group
+    assert k3gen.ExpertLayout(k3gen.TINY).blob_bytes == 3 * (96 * 64 + 96 * 4)
+
+
+# ---------------------------------------------------------------- matvecs
+def test_mxfp4_matvec_vs_dense_decode():
+    rng = np.random.default_rng(11)
+    for rows, cols in [(5, 32), (7, 96), (16, 256)]:
+        packed = rng.integers(0, 256, (rows, cols // 2), dtype=np.uint8)
+        scales = rng.integers(110, 135, (rows, cols // 32), dtype=np.uint8)
+        x = rng.standard_normal(cols).astype(np.float32)
+        y = oracle.mxfp4_matvec(x, packed, scales, cols, rows)
+        W = _brute.decode_mxfp4(packed, scales)
+        ref = (W @ x.astype(np.float64)).astype(np.float32)
+        assert np.max(np.abs(y - ref)) <= 1e-6 * np.max(np.abs(ref)), (rows, cols)
+
+
+def test_bf16_matvec_layout_out_by_in():
+    rng = np.random.default_rng(3)
+    out, inn = 6, 10
+    W = k3gen.normal_bf16(out * inn, 9, 99).reshape(out, inn)
+    x = rng.standard_normal(inn).astype(np.float32)
+    y = oracle.bf16_matvec(x, W)
+    ref = (_brute.bf16_bits_to_f64(W) @ x.astype(np.float64)).astype(np.float32)
+    assert np.allclose(y, ref, rtol=1e-6, atol=0)
+    # a one-hot x picks column i of W (not row i): catches a transposed operand
+    x1 = np.zeros(inn, np.float32)
+    x1[3] = 1.0
+    assert np.array_equal(oracle.bf16_matvec(x1, W), _brute.bf16_bits_to_f64(W[:, 3]).astype(np.float32))
+
+
+def test_bf16_widening_is_a_shift():
+    assert oracle.lib().k3o_bf16_to_f32(0x3F80) == 1.0
+    assert oracle.lib().k3o_bf16_to_f32(0xC040) == -3.0
+    assert oracle.lib().k3o_bf16_to_f32(0x0001) == 2.0 ** -133
+
+
+# ---------------------------------------------------------------- router
+def _logit_case(logits, bias, K):
+    """H = 1, x = [1]: each expert's logit is its single router weight."""
+    Wr = np.array(logits, np.float32).reshape(-1, 1)
+    x = np.ones(1, np.float32)
+    return oracle.router(x, Wr, np.array(bias, np.float32), K)
+
+
+def test_router_bias_steers_selection_only():
+    logits = [2.0, 1.0, 0.0, -1.0, 0.5, 3.0]
+    bias = [0.0, 0.0, 0.6, 0.0, 0.0, -0.5]
+    idx, w, sel, gap = _logit_case(logits, bias, 2)
+    # selection scores: sigma + bias = [.8808, .7311, 1.1, .2689, .6225, .4526]
+    assert list(sel) == [2, 0]                       # expert 5 (largest sigma) is NOT chosen
+    assert list(idx) == [0, 2]
+    s0 = 1.0 / (1.0 + math.exp(-2.0))                # unbiased scores weight the winners
+    s2 = 0.5
+    assert w[0] == pytest.approx(s0 / (s0 + s2), rel=1e-7)
+    assert w[1] == pytest.approx(s2 / (s0 + s2), rel=1e-7)
+    assert gap == pytest.approx(s0 - (1.0 / (1.0 + math.exp(-1.0))), rel=1e-6)
+
+
+def test_router_tie_lowest_index_wins():
+    idx, w, sel, gap = _logit_case([0.3] * 6, [0.0] * 6, 3)
+    assert list(sel) == [0, 1, 2]
+    assert gap == 0.0
+    assert np.allclose(w, 1.0 / 3.0, rtol=1e-7)
+
+
+def test_router_renorm_off_and_routed_scale():
+    Wr = np.array([[1.0], [0.0], [-1.0]], np.float32)
+    x = np.ones(1, np.float32)
+    idx, w, _, _ = oracle.router(x, Wr, np.zeros(3, np.float32), 2, renorm=0, routed_scale=2.5)
+    assert list(idx) == [0, 1]
+    assert w[0] == pytest.approx(2.5 / (1.0 + math.exp(-1.0)), rel=1e-7)
+    assert w[1] == pytest.approx(1.25, rel=1e-7)
+
+
+def test_router_brute_force_and_invariants():
+    d = k3gen.TINY
+    dense = k3gen.gen_dense(d, 0)
+    x = k3gen.gen_x(d, 0, 32)
+    idx, w, gaps = oracle.route_batch(d, x, dense["w_router"], dense["bias"])
+    for t in range(32):
+        xf = _brute.bf16_bits_to_f64(x[t])
+        bi, bw = _brute.route(xf, dense["w_router"], dense["bias"], d.topk)
+        if gaps[t] > 1e-9:
+            assert np.array_equal(idx[t], bi)
+            assert np.allclose(w[t], bw, rtol=1e-6)
+        assert len(set(idx[t].tolist())) == d.topk
+        assert np.all((idx[t] >= 0) & (idx[t] < d.n_experts))
+        assert np.all(np.diff(idx[t]) > 0)
+        assert np.all(w[t] > 0)
+        assert abs(float(np.sum(w[t].astype(np.float64))) - 1.0) < 1e-6
+
+
+# ---------------------------------------------------------------- SiTU, RMSNorm
+def test_situ_zero_and_sign():
+    assert oracle.situ(0.0, 7.0) == 0.0
+    assert oracle.situ(3.0, 0.0) == 0.0
+    assert oracle.situ(2.0, -5.0) == -oracle.situ(2.0, 5.0)     # odd in u
+
+
+def test_situ_bound_reached():
+    bound = GOLDEN["situ_bound"]
+    assert oracle.situ(1000.0, 1000.0) == bound
+    assert oracle.situ(1000.0, -1000.0) == -bound
+    for g in (0.1, 1.0, 10.0, 100.0, 1000.0):
+        for u in (0.1, 1.0, 10.0, 100.0, 1000.0):
+            assert abs(oracle.situ(g, u)) <= bound
+
+
+def test_situ_sigmoid_reads_uncapped_gate():
+    # g = -40: sigmoid(-40) ~ 4e-18 gives ~0; a sigmoid fed the capped gate
+    # 4*tanh(-10) ~ -4 would give about -4 * 0.018 * 19 = -1.37.
+    assert abs(oracle.situ(-40.0, 25.0)) < 1e-12
+    # g large: gate factor -> b1 = 4 and sigmoid -> 1, so y -> 4 * 25 tanh(u/25)
+    assert oracle.situ(1000.0, 25.0) == pytest.approx(100.0 * 0.7615941559557649, rel=1e-7)
+
+
+def test_situ_small_argument_limit():
+    # near 0: 4 tanh(g/4) ~ g, sigmoid ~ 1/2, 25 tanh(u/25) ~ u  =>  y ~ g*u/2
+    g = u = 1e-4
+    assert oracle.situ(g, u) == pytest.approx(0.5 * g * u, rel=1e-3)
+
+
+def test_rmsnorm_constant_vector_closed_form():
+    c, n, eps = 3.0, 128, 1e-5
+    out = oracle.rmsnorm(np.full(n, c, np.float32), None, eps)
+    assert np.allclose(out, c / math.sqrt(c * c + eps), rtol=1e-7)
+    gam = np.linspace(-2, 2, n).astype(np.float32)
+    out = oracle.rmsnorm(np.full(n, c, np.float32), gam, eps)
+    assert np.allclose(out, gam * (c / math.sqrt(c * c + eps)), rtol=1e-6, atol=1e-7)
+
+
+def test_rmsnorm_eps_inside_root():
+    # x = [3, 4]: mean square 12.5. With a large eps the two placements differ a lot.
+    out = oracle.rmsnorm(np.array([3.0, 4.0], np.float32), None, 12.5)
+    assert out[0] == pytest.approx(3.0 / 5.0, rel=1e-7)          # 3 / sqrt(12.5 + 12.5)
+    assert out[1] == pytest.approx(4.0 / 5.0, rel=1e-7)
+
+
+# ---------------------------------------------------------------- dispatch
+def test_dispatch_is_stable_counting_sort():
+    rng = np.random.default_rng(2)
+    T, K, E = 50, 4, 13
+    ti = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int32)
+    off, sp, ps = oracle.dispatch(ti, E)
+    flat = ti.reshape(-1)
+    order = np.argsort(flat, kind="stable")          # library stable sort
+    assert np.array_equal(sp, order)
+    assert np.array_equal(off, np.concatenate([[0], np.cumsum(np.bincount(flat, minlength=E))]))
+    assert np.array_equal(ps[sp], np.arange(T * K))
+    with pytest.raises(ValueError):
+        oracle.dispatch(np.array([[0, E]], np.int32), E)
+
+
+# ---------------------------------------------------------------- whole layer
+def _tiny_layer(seed=0, T=4):
+    d = k3gen.TINY
+    dense = k3gen.gen_dense(d, seed)
+    lay = k3gen.ExpertLayout(d)
+    blobs = k3gen.gen_experts(d, seed, 0, d.n_experts)
+    ex = oracle.ExpertSet(blobs, lay.blob_bytes, lay.offsets)
+    x = k3gen.gen_x(d, seed, T)
+    return d, dense, lay, blobs, ex, x
+
+
+def test_layer_matches_brute_force_tiny():
+    d, dense, lay, blobs, ex, x = _tiny_layer(0, 8)
+    r = oracle.layer(d, x, dense, ex, want_inner=True)
+    B = lay.blob_bytes
+    for t in range(x.shape[0]):
+        b = _brute.layer_token(d, x[t], dense, lambda e: blobs[e * B:(e + 1) * B], lay.offsets)
+        assert np.array_equal(r["idx"][t], b["idx"])
+        for k in ("z", "acc", "nrm", "y"):
+            ref = b[k].astype(np.float64)
+            err = np.linalg.norm(r[k][t] - ref) / np.linalg.norm(ref)
+            assert err < 1e-6, (t, k, err)
+
+
+def test_layer_thread_count_invariant():
+    d, dense, lay, blobs, ex, x = _tiny_layer(0, 6)
+    a = oracle.layer(d, x, dense, ex, nthreads=1)
+    b = oracle.layer(d, x, dense, ex, nthreads=4)
+    assert np.array_equal(a["y"], b["y"]) and np.array_equal(a["idx"], b["idx"])
+
+
+def test_combine_identical_experts_and_order():
+    # all experts identical => sum_j w_j edn_j = edn (weights sum to 1)
+    d, dense, lay, blobs, ex, x = _tiny_layer(0, 3)
+    B = lay.blob_bytes
+    same = np.tile(blobs[:B], d.n_experts)
+    exs = oracle.ExpertSet(same, B, lay.offsets)
+    r = oracle.layer(d, x, dense, exs, want_inner=True)
+    for t in range(3):
+        edn, _, _, _ = oracle.expert(d, exs, 0, r["z"][t])
+        assert np.allclose(r["acc"][t], edn, rtol=2e-6, atol=1e-6 * np.max(np.abs(edn)))
+    # order invariance: recombining the per-expert outputs in reverse id order
+    r = oracle.layer(d, x, dense, ex, want_inner=True)
+    for t in range(3):
+        edns = [oracle.expert(d, ex, int(e), r["z"][t])[0].astype(np.float64) for e in r["idx"][t]]
+        rev = sum(float(w) * e for w, e in reversed(list(zip(r["w"][t], edns))))
+        assert np.max(np.abs(rev.astype(np.float32) - r["acc"][t])) <= np.max(np.abs(r["acc"][t])) * 2 ** -23
+
+
+def test_layer_per_expert_norm_would_differ():
+    # the norm is applied to the aggregate: norming each expert first gives another function
+    d, dense, lay, blobs, ex, x = _tiny_layer(0, 2)
+    r = oracle.layer(d, x, dense, ex, want_inner=True)
+    t = 0
+    per = sum(float(w) * oracle.rmsnorm(oracle.expert(d, ex, int(e), r["z"][t])[0], None, d.eps).astype(np.float64)
+              for w, e in zip(r["w"][t], r["idx"][t]))
+    assert np.linalg.norm(per - r["nrm"][t]) / np.linalg.norm(r["nrm"][t]) > 1e-2
+    assert np.allclose(r["nrm"][t], oracle.rmsnorm(r["acc"][t], None, d.eps))
+
+
+@pytest.mark.slow
+def test_layer_matches_brute_force_k3_shape_subproblem():
+    # K3 widths (H 7168, L 3584, I 3072, K 16) with 24 experts, one token.
+    d = k3gen.Dims(hidden=7168, latent=3584, inter=3072, n_experts=24, topk=16, eps=1e-5)
+    dense = k3gen.gen_dense(d, 1)
+    lay = k3gen.ExpertLayout(d)
+    blobs = k3gen.gen_experts(d, 1, 0, d.n_experts)
+    ex = oracle.ExpertSet(blobs, lay.blob_bytes, lay.offsets)
+    x = k3gen.gen_x(d, 1, 1)
+    r = oracle.layer(d, x, dense, ex, want_inner=True)
+    B = lay.blob_bytes
+    b = _brute.layer_token(d, x[0], dense, lambda e: blobs[e * B:(e + 1) * B], lay.offsets)
+    assert np.array_equal(r["idx"][0], b["idx"])
+    for k in ("z", "acc", "nrm", "y"):
+        ref = b[k].astype(np.float64)
+        assert np.linalg.norm(r[k][0] - ref) / np.linalg.norm(ref) < 1e-6, k
