@@ -1,0 +1,249 @@
+"""Benchmark of the Kimi K3 LatentMoE routed-expert layer on one MI355X.
+
+A step is one pass of the whole layer (router, latent projection, dispatch, MXFP4
+experts, combine + RMSNorm, up-projection) over one batch of synthetic input already
+resident in HBM. The headline workload is the K3-shape decode layer: T = 1 token per
+step, hidden 7168, latent 3584, inter 3072, 896 MXFP4 experts (15.7 GB resident),
+top-16. Each step reads a different token from a pool of 64, so the routed experts
+change from step to step. A K3-shape prefill pass (T = 4096) is reported beside it.
+
+Prints one JSON line (rank 0). Per-kernel times come from HIP events recorded between
+the kernels of the same steps (k3moe_layer_profiled) on the stream they run on.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 matrix cores
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime (timing enabled)."""
+
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(h)) == 0
+            self.ev.append(h.value)
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        assert self.hip.hipEventSynchronize(b) == 0
+        assert self.hip.hipEventElapsedTime(ctypes.byref(out), a, b) == 0
+        return out.value
+
+    def close(self):
+        for h in self.ev:
+            self.hip.hipEventDestroy(h)
+
+
+def algorithmic(dims, T, n_distinct):
+    """Bytes the layer must move and flops it must do for one step."""
+    import k3gen
+    H, L, I, E, K = dims.hidden, dims.latent, dims.inter, dims.n_experts, dims.topk
+    blob = k3gen.ExpertLayout(dims).blob_bytes
+    gateup_unit = 2 * (I * L // 2 + I * L // 32)     # w1 + w3 of one expert
+    down_unit = L * I // 2 + L * I // 32             # w2 of one expert
+    dense_bytes = E * H * 4 + L * H * 2 + H * L * 2 + E * 4 + L * 4
+    act_bytes = T * H * 2 + T * H * 4
+    flops = T * (2 * E * H + 2 * L * H + K * 2 * 3 * I * L + 2 * H * L)
+    return {
+        "layer_bytes": n_distinct * blob + dense_bytes + act_bytes,
+        "gateup_bytes": n_distinct * gateup_unit,
+        "down_bytes": n_distinct * down_unit,
+        "flops": flops,
+        "expert_flops": T * K * 2 * 3 * I * L,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--prefill-steps", type=int, default=3)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=32)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the layer is built and timed on a single MI355X; "
+              "run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import k3gen
+    from mxfp4_routed_expert_amd import device, k3moe
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    dims = k3gen.K3
+    lay = k3gen.ExpertLayout(dims)
+    B = lay.blob_bytes
+
+    t0 = time.time()
+    dense = k3gen.gen_dense(dims, 1)
+    host_blobs = None if args.no_cpu_baseline else np.empty(dims.n_experts * B, np.uint8)
+
+    def chunks():
+        for e0 in range(0, dims.n_experts, 32):
+            e1 = min(dims.n_experts, e0 + 32)
+            out = host_blobs[e0 * B:e1 * B] if host_blobs is not None else None
+            yield e0, k3gen.gen_experts(dims, 1, e0, e1, out=out)
+    dev = device.upload_layer(dims, dense, chunks(), B, lay.offsets)
+    torch.cuda.synchronize()
+    log(f"layer generated and uploaded in {time.time() - t0:.1f} s")
+
+    stream = torch.cuda.Stream()
+    wts = dev.weights_struct()
+
+    # ---------------------------------------------------------------- decode, T = 1
+    T = 1
+    pool = 64
+    xs = torch.from_numpy(k3gen.gen_x(dims, 1, pool).view(np.int16)).cuda()
+    y = torch.empty((T, dims.hidden), dtype=torch.float32, device="cuda")
+    idx = torch.empty((pool, dims.topk), dtype=torch.int32, device="cuda")
+    tw = torch.empty((pool, dims.topk), dtype=torch.float32, device="cuda")
+    ws = device.workspace(dims, T)
+    row = dims.hidden * 2
+
+    def step(i):
+        j = i % pool
+        k3moe.k3moe_layer(dims, T, xs.data_ptr() + j * row, wts, y, idx[j], tw[j], ws, stream=stream)
+
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i)
+    torch.cuda.synchronize()
+    ev = HipEvents(2)
+    hip_record = ctypes.CDLL("libamdhip64.so").hipEventRecord
+    hip_record.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    hip_record(ev.ev[0], stream.cuda_stream)
+    for i in range(args.steps):
+        step(i)
+    hip_record(ev.ev[1], stream.cuda_stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = ev.ms(ev.ev[0], ev.ev[1]) / args.steps
+    ev.close()
+    log(f"decode T=1: {ms_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us/step)")
+
+    # per-kernel event marks over the same kind of steps
+    nprof = min(args.steps, 100)
+    pe = HipEvents(16)
+    sums = {}
+    names = []
+    for i in range(nprof):
+        j = i % pool
+        names = k3moe.k3moe_layer_profiled(dims, T, xs.data_ptr() + j * row, wts, y, idx[j], tw[j], ws,
+                                           pe.ev, stream=stream)
+        torch.cuda.synchronize()
+        for k, n in enumerate(names):
+            sums[n] = sums.get(n, 0.0) + pe.ms(pe.ev[k], pe.ev[k + 1])
+    pe.close()
+    kern_us = {n: sums[n] / nprof * 1e3 for n in names}
+    log("per-kernel us: " + ", ".join(f"{n} {v:.1f}" for n, v in kern_us.items()))
+
+    alg = algorithmic(dims, T, dims.topk)
+    layer_gbs = alg["layer_bytes"] / (ms_step * 1e-3) / 1e9
+    dom = max(("expert_gateup_situ", "expert_down"), key=lambda n: kern_us.get(n, 0.0))
+    dom_bytes = alg["gateup_bytes"] if dom == "expert_gateup_situ" else alg["down_bytes"]
+    dom_gbs = dom_bytes / (kern_us[dom] * 1e-6) / 1e9
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "layer_achieved": round(layer_gbs, 1), "layer_frac": round(layer_gbs / HBM_PEAK_GBS, 4),
+                "kernel_us": {k: round(v, 2) for k, v in kern_us.items()}}
+
+    # ---------------------------------------------------------------- prefill, T = 4096
+    prefill = None
+    if not args.no_prefill:
+        Tp = 4096
+        xp = torch.from_numpy(k3gen.gen_x(dims, 3, Tp).view(np.int16)).cuda()
+        yp = torch.empty((Tp, dims.hidden), dtype=torch.float32, device="cuda")
+        wsp = device.workspace(dims, Tp)
+        with torch.cuda.stream(stream):
+            k3moe.k3moe_layer(dims, Tp, xp, wts, yp, None, None, wsp, stream=stream)
+        torch.cuda.synchronize()
+        evp = HipEvents(2)
+        hip_record(evp.ev[0], stream.cuda_stream)
+        for _ in range(args.prefill_steps):
+            k3moe.k3moe_layer(dims, Tp, xp, wts, yp, None, None, wsp, stream=stream)
+        hip_record(evp.ev[1], stream.cuda_stream)
+        torch.cuda.synchronize()
+        msp = evp.ms(evp.ev[0], evp.ev[1]) / args.prefill_steps
+        evp.close()
+        algp = algorithmic(dims, Tp, dims.n_experts)
+        tf = algp["flops"] / (msp * 1e-3) / 1e12
+        prefill = {"T": Tp, "ms_per_step": round(msp, 3), "tokens_per_s": round(Tp / (msp * 1e-3), 1),
+                   "algorithmic_TFLOPs": round(tf, 2), "bf16_peak_frac": round(tf / BF16_PEAK_TFLOPS, 4)}
+        log(f"prefill T=4096: {msp:.2f} ms/step, {tf:.1f} TFLOP/s algorithmic")
+        del wsp, yp, xp
+        torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        nthreads = min(16, os.cpu_count() or 1)
+        n = args.cpu_tokens
+        x = k3gen.gen_x(dims, 1, n)
+        ex = oracle.ExpertSet(host_blobs, B, lay.offsets)
+        c0 = time.perf_counter()
+        oracle.layer(dims, x, dense, ex, nthreads=nthreads)
+        cs = time.perf_counter() - c0
+        cpu = {"value": round(n / cs, 3), "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+               "sample": f"{n} K3-shape decode tokens (T=1 problems, one per thread at a time), "
+                         f"{cs:.1f} s wall"}
+        log(f"cpu oracle: {n / cs:.2f} tokens/s on {nthreads} threads")
+
+    out = {
+        "metric": "LatentMoE layer tokens/s (K3 decode, T=1); HBM GB/s @T=1, TFLOP/s @T=4096, % of MI355X peak",
+        "value": round(1.0 / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4 weights, bf16 matrix cores, fp32 accumulate/output",
+        "data": "synthetic",
+        "config": {"workload": "K3-shape decode layer T=1: H=7168 L=3584 I=3072 E=896 K=16, "
+                               "896 MXFP4 experts resident (15.7 GB)", "T": T, "global_batch": T,
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "prefill": prefill,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,157 @@
+/* k3moe: the Kimi K3 Stable LatentMoE routed-expert layer on one MI355X (gfx950).
+ *
+ * What the layer computes, per token x (bf16, width H):
+ *   1. router: logit_e = Wr[e] . x; sc_e = sigmoid(logit_e); ch_e = sc_e + bias_e;
+ *      the K experts with the largest ch are chosen (equal ch: the lower id wins);
+ *      each chosen expert is weighted by its UNBIASED score sc, renormalised over the
+ *      K chosen when renorm is set, times routed_scale.
+ *      ("kimi-k3-in-c" README, section 9 "Picking 16 experts of 896"; colibri
+ *      docs/kimi_k3.md, "Architecture notes", Stable LatentMoE.)
+ *   2. latent projection z = W_down x (bf16 weights, [L][H]).
+ *   3. for each chosen expert e: g = W1_e z, u = W3_e z, act = SiTU-GLU(g, u) =
+ *      b1 tanh(g/b1) sigmoid(g) * b2 tanh(u/b2), edn = W2_e act. W1, W3 are [I][L],
+ *      W2 is [L][I], all MXFP4 (same README, section 9, and section 4 "Reduction one:
+ *      the experts already ship at half a byte").
+ *   4. acc = sum_j w_j edn_j; n = RMSNorm(acc) = acc / sqrt(mean(acc^2) + eps) * gamma,
+ *      applied to the AGGREGATE (section 9; RMSNorm as in section 5 "Kernels with a
+ *      floating point contract").
+ *   5. y = W_up n (bf16 weights, [H][L]).
+ *
+ * MXFP4 layout (section 4; colibri "Weights"): a matrix [rows][cols] is stored as
+ * packed bytes [rows][cols/2], column 2k in the LOW nibble of byte k and column 2k+1
+ * in the HIGH nibble, each nibble an E2M1 code (bit 3 = sign), plus scale bytes
+ * [rows][cols/32], one ue8m0 per 32 columns: w = E2M1(code) * 2^(scale - 127). A scale
+ * byte of 255 zeroes its group. Expert e of a stacked matrix starts at
+ * base + e * stride (strides in bytes), which describes both separate [E][rows][..]
+ * tensors and the pages' per-expert records of six tensors back to back.
+ *
+ * Conventions shared by every entry point:
+ *  - All data pointers are DEVICE pointers on the current HIP device unless stated.
+ *    The caller owns every buffer and the stream; the library allocates nothing and
+ *    keeps no pointer after the call returns.
+ *  - stream is a hipStream_t (NULL = the default stream). Calls are asynchronous and
+ *    stream-ordered; they never synchronise the host. Inputs must stay valid and
+ *    unmodified until the stream has executed the call.
+ *  - Workspace: ws points to at least the bytes k3moe_workspace_size() reports for
+ *    the same dims and T (any larger T works too), 256-byte aligned. Its content on
+ *    entry does not matter and on return is unspecified.
+ *  - Row-major everywhere. bf16 values are passed as their 16-bit patterns.
+ *  - Supported shapes: every dimension >= 1; hidden, latent and inter multiples of
+ *    32; latent <= 16384; group == 32; topk <= 32 and topk <= n_experts <= 1024; T >= 0 (T == 0 is a
+ *    no-op); T * topk < 2^31. Scale bytes 2..254 and 255 are exact on the GPU path;
+ *    0 and 1 give weights below 2^-126, which the matrix cores may flush to zero.
+ *  - Errors: every call returns K3MOE_OK (0) or a negative code. All argument
+ *    checks happen on the host before any launch, so a refused call has launched
+ *    nothing; on K3MOE_EHIP the outputs are unspecified. Nothing prints or aborts.
+ *  - Expert ids in topk_idx outside [0, n_experts) are not dereferenced: the pair is
+ *    dropped from dispatch (its pair_slot is -1) and from the weighted sum.
+ */
+#ifndef K3MOE_H
+#define K3MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define K3MOE_OK 0
+#define K3MOE_EINVAL (-1)       /* null pointer, negative or zero dimension */
+#define K3MOE_EUNSUPPORTED (-2) /* a shape or alignment outside the supported set */
+#define K3MOE_EWORKSPACE (-3)   /* workspace missing or smaller than required */
+#define K3MOE_EHIP (-4)         /* a HIP launch or device query failed */
+
+typedef struct {
+    int32_t hidden;     /* H: token width (K3: 7168) */
+    int32_t latent;     /* L: expert width (3584) */
+    int32_t inter;      /* I: expert intermediate width (3072) */
+    int32_t n_experts;  /* E (896) */
+    int32_t topk;       /* K (16) */
+    int32_t group;      /* MXFP4 group size, must be 32 */
+    int32_t renorm;     /* 1: renormalise the K weights to sum 1 (K3: 1) */
+    float routed_scale; /* multiplies every routing weight (K3: 1.0) */
+    float eps;          /* RMSNorm epsilon, inside the square root (K3: 1e-5) */
+    float b1, b2;       /* SiTU-GLU caps (K3: 4 and 25) */
+} k3moe_dims;
+
+typedef struct {
+    const uint8_t *packed;        /* expert e: packed + e*packed_expert_stride, [rows][cols/2] */
+    const uint8_t *scales;        /* expert e: scales + e*scales_expert_stride, [rows][cols/32] */
+    int64_t packed_expert_stride; /* bytes */
+    int64_t scales_expert_stride; /* bytes */
+} k3moe_mxfp4;
+
+typedef struct {
+    k3moe_mxfp4 w1; /* gate: rows = inter, cols = latent */
+    k3moe_mxfp4 w3; /* up:   rows = inter, cols = latent */
+    k3moe_mxfp4 w2; /* down: rows = latent, cols = inter */
+} k3moe_experts;
+
+typedef struct {
+    const float *w_router; /* [E][H] fp32 */
+    const float *bias;     /* [E] fp32 score-correction bias (selection only) */
+    const uint16_t *w_down;/* [L][H] bf16 */
+    const uint16_t *w_up;  /* [H][L] bf16 */
+    const float *norm_w;   /* [L] fp32 RMSNorm weight gamma */
+    k3moe_experts ex;
+} k3moe_weights;
+
+/* Host-only. Bytes of workspace every entry point below needs for this dims and T.
+ * Returns K3MOE_EINVAL / K3MOE_EUNSUPPORTED for bad arguments. */
+int k3moe_workspace_size(const k3moe_dims *d, int32_t T, size_t *bytes);
+
+/* Step 1, the router (README section 9; colibri Stable LatentMoE).
+ * x [T][H] bf16; w_router [E][H] fp32; bias [E] fp32 (required; pass zeros for none).
+ * Out: topk_idx [T][K] int32, each row the K chosen expert ids in ASCENDING order;
+ * topk_w [T][K] fp32, the weight of the expert in the same position. */
+int k3moe_route(const k3moe_dims *d, int32_t T, const uint16_t *x, const float *w_router,
+                const float *bias, int32_t *topk_idx, float *topk_w,
+                void *ws, size_t ws_bytes, void *stream);
+
+/* Step 2, the latent projection z = W_down x (README section 9, step 2; bf16 matrix
+ * product as in section 5). x [T][H] bf16, w_down [L][H] bf16 -> z [T][L] fp32. */
+int k3moe_latent_proj_bf16(const k3moe_dims *d, int32_t T, const uint16_t *x,
+                           const uint16_t *w_down, float *z, void *ws, size_t ws_bytes,
+                           void *stream);
+
+/* Grouping of the T*K (token, slot) pairs by expert, so that each expert's weights
+ * are read once per call. topk_idx [T][K] int32 in. Out: expert_off [E+1] (expert e's
+ * pairs are positions expert_off[e] .. expert_off[e+1]-1), sorted_pair [T*K] (the pair
+ * id t*K + j at each position, ordered by expert id, then by t), pair_slot [T*K] (the
+ * position of pair t*K + j, or -1 if its expert id is out of range). Deterministic. */
+int k3moe_dispatch(const k3moe_dims *d, int32_t T, const int32_t *topk_idx,
+                   int32_t *expert_off, int32_t *sorted_pair, int32_t *pair_slot,
+                   void *ws, size_t ws_bytes, void *stream);
+
+/* Step 3 for every dispatched pair (README section 9, step 3; MXFP4 as in section 4).
+ * z [T][L] fp32; expert_off / sorted_pair as k3moe_dispatch wrote them.
+ * Out: edn [T*K][L] fp32, row p = W2_e SiTU(W1_e z_t, W3_e z_t) for the pair at sorted
+ * position p (token t = sorted_pair[p] / K, expert e = the expert whose range holds p). */
+int k3moe_expert_glu_mxfp4(const k3moe_dims *d, int32_t T, const float *z,
+                           const k3moe_experts *ex, const int32_t *expert_off,
+                           const int32_t *sorted_pair, float *edn,
+                           void *ws, size_t ws_bytes, void *stream);
+
+/* Steps 4 and 5 (README section 9, steps 4 and 5): acc_t = sum_j topk_w[t][j] *
+ * edn[pair_slot[t*K+j]] (slots of -1 are skipped), n_t = RMSNorm(acc_t) with norm_w,
+ * y_t = W_up n_t. edn [T*K][L] fp32, pair_slot [T*K], topk_w [T][K], norm_w [L] fp32,
+ * w_up [H][L] bf16 -> y [T][H] fp32. */
+int k3moe_combine(const k3moe_dims *d, int32_t T, const float *edn, const int32_t *pair_slot,
+                  const float *topk_w, const float *norm_w, const uint16_t *w_up, float *y,
+                  void *ws, size_t ws_bytes, void *stream);
+
+/* The whole layer, steps 1-5 (README section 9, the per-token LatentMoE, without the
+ * shared experts). x [T][H] bf16 -> y [T][H] fp32. topk_idx_out [T][K] and
+ * topk_w_out [T][K] are optional (NULL: kept in the workspace). */
+int k3moe_layer(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_weights *w,
+                float *y, int32_t *topk_idx_out, float *topk_w_out,
+                void *ws, size_t ws_bytes, void *stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *k3moe_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

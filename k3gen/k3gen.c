@@ -75,8 +75,23 @@ void k3g_uniform_f32(float *out, size_t n, uint64_t seed, uint32_t tensor,
 
 void k3g_bytes(uint8_t *out, size_t n, uint64_t seed, uint32_t tensor, uint64_t idx0)
 {
-#pragma omp parallel for schedule(static) if (n > 65536)
-    for (size_t i = 0; i < n; i++) {
+    /* byte f of the tensor is byte (f % 8) of the draw at counter f / 8; whole 8-byte
+     * words are produced from one draw */
+    size_t head = (size_t)((8u - (idx0 & 7u)) & 7u);
+    if (head > n) head = n;
+    for (size_t i = 0; i < head; i++) {
+        const uint64_t f = idx0 + i;
+        out[i] = (uint8_t)(k3g_hash(seed, tensor, f >> 3) >> (8u * (unsigned)(f & 7u)));
+    }
+    const size_t words = (n - head) / 8;
+    const uint64_t w0 = (idx0 + head) >> 3;
+#pragma omp parallel for schedule(static) if (words > 8192)
+    for (size_t k = 0; k < words; k++) {
+        const uint64_t h = k3g_hash(seed, tensor, w0 + k);
+        uint8_t *o = out + head + 8 * k;
+        for (unsigned b = 0; b < 8; b++) o[b] = (uint8_t)(h >> (8u * b));
+    }
+    for (size_t i = head + 8 * words; i < n; i++) {
         const uint64_t f = idx0 + i;
         out[i] = (uint8_t)(k3g_hash(seed, tensor, f >> 3) >> (8u * (unsigned)(f & 7u)));
     }

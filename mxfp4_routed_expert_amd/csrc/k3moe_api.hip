@@ -1,0 +1,365 @@
+// The k3moe C-ABI: argument checks, workspace carving and launch order. Every check
+// runs on the host before the first launch, so a refused call has launched nothing.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "k3moe.h"
+#include "k3moe_prof.h"
+#include "k3moe_kernels.h"
+
+using namespace k3;
+
+namespace {
+
+constexpr int kRouterSplits = 8;  // K-splits of the router product (partials summed by top-k)
+constexpr int kPieces = 3;        // bf16 pieces per fp32 activation
+
+bool al16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool al8(const void *p) { return ((uintptr_t)p & 7u) == 0; }
+
+int check_dims(const k3moe_dims *d) {
+  if (!d) return K3MOE_EINVAL;
+  if (d->hidden <= 0 || d->latent <= 0 || d->inter <= 0 || d->n_experts <= 0 || d->topk <= 0)
+    return K3MOE_EINVAL;
+  if (d->renorm != 0 && d->renorm != 1) return K3MOE_EINVAL;
+  if (!(d->eps >= 0.f) || !isfinite(d->eps) || !isfinite(d->b1) || !isfinite(d->b2) ||
+      d->b1 == 0.f || d->b2 == 0.f || !isfinite(d->routed_scale))
+    return K3MOE_EINVAL;
+  if (d->group != 32) return K3MOE_EUNSUPPORTED;
+  if (d->hidden % 32 || d->latent % 32 || d->inter % 32) return K3MOE_EUNSUPPORTED;
+  if (d->topk > 32 || d->topk > d->n_experts || d->n_experts > 1024) return K3MOE_EUNSUPPORTED;
+  // the combine kernel stages one latent row (fp32) in LDS
+  if (d->latent > 16384 || d->hidden > (1 << 20)) return K3MOE_EUNSUPPORTED;
+  return K3MOE_OK;
+}
+
+int check_T(const k3moe_dims *d, int32_t T) {
+  if (T < 0) return K3MOE_EINVAL;
+  if ((int64_t)T * d->topk >= (int64_t)1 << 31) return K3MOE_EUNSUPPORTED;
+  return K3MOE_OK;
+}
+
+int check_mx(const k3moe_mxfp4 &m) {
+  if (!m.packed || !m.scales) return K3MOE_EINVAL;
+  if (m.packed_expert_stride < 0 || m.scales_expert_stride < 0) return K3MOE_EINVAL;
+  if (!al16(m.packed) || (m.packed_expert_stride & 15)) return K3MOE_EUNSUPPORTED;
+  return K3MOE_OK;
+}
+
+struct Ws {
+  float *router_part;          // [splits][T][E]
+  uint16_t *zp[3];             // [T][L] pieces of z
+  int32_t *idx;                // [T][K]
+  float *w;                    // [T][K]
+  int32_t *expert_off;         // [E+1]
+  int32_t *sorted_pair;        // [P]
+  int32_t *pair_slot;          // [P]
+  int32_t *active;             // [E]
+  int32_t *counters;           // [0] active experts, [1] dropped pairs
+  int32_t *lrank;              // [P]
+  int32_t *cnt;                // [chunks][E]
+  uint16_t *actp[3];           // [P][I]
+  float *edn;                  // [P][L]
+  uint16_t *np[3];             // [T][L]
+  size_t bytes;
+};
+
+Ws carve(const k3moe_dims *d, int32_t T, void *base) {
+  Ws w;
+  char *b = (char *)base;
+  size_t o = 0;
+  auto take = [&](size_t n) {
+    char *p = b ? b + o : nullptr;
+    o += (n + 255) & ~(size_t)255;
+    return (void *)p;
+  };
+  const size_t t = (size_t)T, E = (size_t)d->n_experts, L = (size_t)d->latent, I = (size_t)d->inter;
+  const size_t P = t * (size_t)d->topk;
+  const size_t nch = (t + 63) / 64;
+  w.router_part = (float *)take(kRouterSplits * t * E * 4);
+  for (int q = 0; q < 3; ++q) w.zp[q] = (uint16_t *)take(t * L * 2);
+  w.idx = (int32_t *)take(P * 4);
+  w.w = (float *)take(P * 4);
+  w.expert_off = (int32_t *)take((E + 1) * 4);
+  w.sorted_pair = (int32_t *)take(P * 4);
+  w.pair_slot = (int32_t *)take(P * 4);
+  w.active = (int32_t *)take(E * 4);
+  w.counters = (int32_t *)take(64);
+  w.lrank = (int32_t *)take(P * 4);
+  w.cnt = (int32_t *)take(nch * E * 4);
+  for (int q = 0; q < 3; ++q) w.actp[q] = (uint16_t *)take(P * I * 2);
+  w.edn = (float *)take(P * L * 4);
+  for (int q = 0; q < 3; ++q) w.np[q] = (uint16_t *)take(t * L * 2);
+  w.bytes = o;
+  return w;
+}
+
+int check_ws(const k3moe_dims *d, int32_t T, void *ws, size_t ws_bytes, Ws *out) {
+  Ws need = carve(d, T, nullptr);
+  if (!ws || ws_bytes < need.bytes) return K3MOE_EWORKSPACE;
+  if (((uintptr_t)ws & 255u) != 0) return K3MOE_EUNSUPPORTED;
+  *out = carve(d, T, ws);
+  return K3MOE_OK;
+}
+
+// Optional per-kernel event marks (k3moe_layer_profiled): an event is recorded on the
+// stream before the first kernel and after each kernel of the call.
+struct ProfMarks {
+  void **events = nullptr;
+  int max_events = 0;
+  int n = 0;
+  const char *names[64];
+};
+ProfMarks g_prof;
+
+hipError_t mark(const char *name, hipStream_t s) {
+  if (!g_prof.events || g_prof.n + 1 >= g_prof.max_events || g_prof.n >= 64) return hipSuccess;
+  g_prof.names[g_prof.n] = name;
+  ++g_prof.n;
+  return hipEventRecord((hipEvent_t)g_prof.events[g_prof.n], s);
+}
+
+#define K3_TRY(expr)                 \
+  do {                               \
+    int rc_ = (expr);                \
+    if (rc_ != K3MOE_OK) return rc_; \
+  } while (0)
+#define K3_HIP(expr)                                 \
+  do {                                               \
+    if ((expr) != hipSuccess) return K3MOE_EHIP;     \
+  } while (0)
+
+// ---- step launchers (arguments already checked)
+int run_route(const k3moe_dims *d, int32_t T, const uint16_t *x, const float *wr, const float *bias,
+              int32_t *idx, float *wt, const Ws &w, hipStream_t s) {
+  DenseArgs a = {};
+  a.A = wr;
+  a.M = d->n_experts;
+  a.K = d->hidden;
+  a.ng = d->hidden / 32;
+  a.B[0] = a.B[1] = a.B[2] = x;
+  a.N = T;
+  a.out = w.router_part;
+  K3_HIP(launch_dense_router(a, kRouterSplits, s));
+  K3_HIP(mark("router_gemv", s));
+  K3_HIP(launch_topk(w.router_part, kRouterSplits, T, d->n_experts, bias, d->topk, d->renorm,
+                     d->routed_scale, idx, wt, s));
+  K3_HIP(mark("topk", s));
+  return K3MOE_OK;
+}
+
+int run_down(const k3moe_dims *d, int32_t T, const uint16_t *x, const uint16_t *wd, float *z,
+             uint16_t *const zp[3], hipStream_t s) {
+  DenseArgs a = {};
+  a.A = wd;
+  a.M = d->latent;
+  a.K = d->hidden;
+  a.ng = d->hidden / 32;
+  a.B[0] = a.B[1] = a.B[2] = x;
+  a.N = T;
+  a.out = z;
+  for (int q = 0; q < 3; ++q) a.planes[q] = zp[q];
+  K3_HIP(launch_dense_bf16(a, 1, kEpiStorePlanes, s));
+  K3_HIP(mark("latent_down_gemv", s));
+  return K3MOE_OK;
+}
+
+int run_experts(const k3moe_dims *d, int32_t T, uint16_t *const zp[3], const k3moe_experts *ex,
+                const int32_t *expert_off, const int32_t *sorted_pair, const int32_t *active,
+                const int32_t *counters, float *edn, const Ws &w, hipStream_t s) {
+  const int grid_y = (int)((int64_t)T * d->topk < d->n_experts ? (int64_t)T * d->topk : d->n_experts);
+  GroupedArgs g = {};
+  g.A[0] = MxMat{ex->w1.packed, ex->w1.scales, ex->w1.packed_expert_stride, ex->w1.scales_expert_stride};
+  g.A[1] = MxMat{ex->w3.packed, ex->w3.scales, ex->w3.packed_expert_stride, ex->w3.scales_expert_stride};
+  g.M = d->inter;
+  g.K = d->latent;
+  g.ng = d->latent / 32;
+  for (int q = 0; q < 3; ++q) g.B[q] = zp[q];
+  g.gather = 1;
+  g.topk = d->topk;
+  g.expert_off = expert_off;
+  g.sorted_pair = sorted_pair;
+  g.active = active;
+  g.n_active = counters;
+  for (int q = 0; q < 3; ++q) g.planes[q] = w.actp[q];
+  g.b1 = d->b1;
+  g.b2 = d->b2;
+  K3_HIP(launch_grouped(g, kEpiSitu, kPieces, grid_y, s));
+  K3_HIP(mark("expert_gateup_situ", s));
+
+  GroupedArgs h = g;
+  h.A[0] = MxMat{ex->w2.packed, ex->w2.scales, ex->w2.packed_expert_stride, ex->w2.scales_expert_stride};
+  h.A[1] = h.A[0];
+  h.M = d->latent;
+  h.K = d->inter;
+  h.ng = d->inter / 32;
+  for (int q = 0; q < 3; ++q) h.B[q] = w.actp[q];
+  h.gather = 0;
+  h.out = edn;
+  K3_HIP(launch_grouped(h, kEpiEdn, kPieces, grid_y, s));
+  K3_HIP(mark("expert_down", s));
+  return K3MOE_OK;
+}
+
+int run_combine(const k3moe_dims *d, int32_t T, const float *edn, const int32_t *pair_slot,
+                const float *topk_w, const float *norm_w, const uint16_t *w_up, float *y,
+                const Ws &w, hipStream_t s) {
+  K3_HIP(launch_combine(edn, pair_slot, topk_w, norm_w, T, d->topk, d->latent, d->eps, w.np[0],
+                        w.np[1], w.np[2], s));
+  K3_HIP(mark("combine_rmsnorm", s));
+  DenseArgs a = {};
+  a.A = w_up;
+  a.M = d->hidden;
+  a.K = d->latent;
+  a.ng = d->latent / 32;
+  for (int q = 0; q < 3; ++q) a.B[q] = w.np[q];
+  a.N = T;
+  a.out = y;
+  K3_HIP(launch_dense_bf16(a, kPieces, kEpiStore, s));
+  K3_HIP(mark("up_gemv", s));
+  return K3MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int k3moe_workspace_size(const k3moe_dims *d, int32_t T, size_t *bytes) {
+  K3_TRY(check_dims(d));
+  K3_TRY(check_T(d, T));
+  if (!bytes) return K3MOE_EINVAL;
+  *bytes = carve(d, T, nullptr).bytes;
+  return K3MOE_OK;
+}
+
+int k3moe_route(const k3moe_dims *d, int32_t T, const uint16_t *x, const float *w_router,
+                const float *bias, int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
+                void *stream) {
+  K3_TRY(check_dims(d));
+  K3_TRY(check_T(d, T));
+  if (!x || !w_router || !bias || !topk_idx || !topk_w) return K3MOE_EINVAL;
+  if (!al16(x) || !al16(w_router)) return K3MOE_EUNSUPPORTED;
+  Ws w;
+  K3_TRY(check_ws(d, T, ws, ws_bytes, &w));
+  if (T == 0) return K3MOE_OK;
+  return run_route(d, T, x, w_router, bias, topk_idx, topk_w, w, (hipStream_t)stream);
+}
+
+int k3moe_latent_proj_bf16(const k3moe_dims *d, int32_t T, const uint16_t *x, const uint16_t *w_down,
+                           float *z, void *ws, size_t ws_bytes, void *stream) {
+  K3_TRY(check_dims(d));
+  K3_TRY(check_T(d, T));
+  if (!x || !w_down || !z) return K3MOE_EINVAL;
+  if (!al16(x) || !al16(w_down)) return K3MOE_EUNSUPPORTED;
+  Ws w;
+  K3_TRY(check_ws(d, T, ws, ws_bytes, &w));
+  if (T == 0) return K3MOE_OK;
+  return run_down(d, T, x, w_down, z, w.zp, (hipStream_t)stream);
+}
+
+int k3moe_dispatch(const k3moe_dims *d, int32_t T, const int32_t *topk_idx, int32_t *expert_off,
+                   int32_t *sorted_pair, int32_t *pair_slot, void *ws, size_t ws_bytes, void *stream) {
+  K3_TRY(check_dims(d));
+  K3_TRY(check_T(d, T));
+  if (!topk_idx || !expert_off || !sorted_pair || !pair_slot) return K3MOE_EINVAL;
+  Ws w;
+  K3_TRY(check_ws(d, T, ws, ws_bytes, &w));
+  // T == 0 still defines expert_off (all zero): the one-block path handles it
+  K3_HIP(launch_dispatch(topk_idx, T, d->topk, d->n_experts, expert_off, sorted_pair, pair_slot,
+                         w.active, w.counters, w.lrank, w.cnt, (hipStream_t)stream));
+  return K3MOE_OK;
+}
+
+int k3moe_expert_glu_mxfp4(const k3moe_dims *d, int32_t T, const float *z, const k3moe_experts *ex,
+                           const int32_t *expert_off, const int32_t *sorted_pair, float *edn,
+                           void *ws, size_t ws_bytes, void *stream) {
+  K3_TRY(check_dims(d));
+  K3_TRY(check_T(d, T));
+  if (!z || !ex || !expert_off || !sorted_pair || !edn) return K3MOE_EINVAL;
+  K3_TRY(check_mx(ex->w1));
+  K3_TRY(check_mx(ex->w3));
+  K3_TRY(check_mx(ex->w2));
+  if (!al16(z) || !al16(edn)) return K3MOE_EUNSUPPORTED;
+  Ws w;
+  K3_TRY(check_ws(d, T, ws, ws_bytes, &w));
+  if (T == 0) return K3MOE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  K3_HIP(launch_active_from_off(expert_off, d->n_experts, w.active, w.counters, s));
+  K3_HIP(launch_split_planes(z, (size_t)T * d->latent, w.zp[0], w.zp[1], w.zp[2], s));
+  return run_experts(d, T, w.zp, ex, expert_off, sorted_pair, w.active, w.counters, edn, w, s);
+}
+
+int k3moe_combine(const k3moe_dims *d, int32_t T, const float *edn, const int32_t *pair_slot,
+                  const float *topk_w, const float *norm_w, const uint16_t *w_up, float *y, void *ws,
+                  size_t ws_bytes, void *stream) {
+  K3_TRY(check_dims(d));
+  K3_TRY(check_T(d, T));
+  if (!edn || !pair_slot || !topk_w || !norm_w || !w_up || !y) return K3MOE_EINVAL;
+  if (!al16(w_up)) return K3MOE_EUNSUPPORTED;
+  Ws w;
+  K3_TRY(check_ws(d, T, ws, ws_bytes, &w));
+  if (T == 0) return K3MOE_OK;
+  return run_combine(d, T, edn, pair_slot, topk_w, norm_w, w_up, y, w, (hipStream_t)stream);
+}
+
+int k3moe_layer(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_weights *wt, float *y,
+                int32_t *topk_idx_out, float *topk_w_out, void *ws, size_t ws_bytes, void *stream) {
+  K3_TRY(check_dims(d));
+  K3_TRY(check_T(d, T));
+  if (!x || !wt || !y || !wt->w_router || !wt->bias || !wt->w_down || !wt->w_up || !wt->norm_w)
+    return K3MOE_EINVAL;
+  K3_TRY(check_mx(wt->ex.w1));
+  K3_TRY(check_mx(wt->ex.w3));
+  K3_TRY(check_mx(wt->ex.w2));
+  if (!al16(x) || !al16(wt->w_router) || !al16(wt->w_down) || !al16(wt->w_up))
+    return K3MOE_EUNSUPPORTED;
+  Ws w;
+  K3_TRY(check_ws(d, T, ws, ws_bytes, &w));
+  if (T == 0) return K3MOE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  int32_t *idx = topk_idx_out ? topk_idx_out : w.idx;
+  float *tw = topk_w_out ? topk_w_out : w.w;
+  K3_TRY(run_route(d, T, x, wt->w_router, wt->bias, idx, tw, w, s));
+  K3_TRY(run_down(d, T, x, wt->w_down, nullptr, w.zp, s));
+  K3_HIP(launch_dispatch(idx, T, d->topk, d->n_experts, w.expert_off, w.sorted_pair, w.pair_slot,
+                         w.active, w.counters, w.lrank, w.cnt, s));
+  K3_HIP(mark("dispatch", s));
+  K3_TRY(run_experts(d, T, w.zp, &wt->ex, w.expert_off, w.sorted_pair, w.active, w.counters, w.edn,
+                     w, s));
+  return run_combine(d, T, w.edn, w.pair_slot, tw, wt->norm_w, wt->w_up, y, w, s);
+}
+
+int k3moe_layer_profiled(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_weights *wt,
+                         float *y, int32_t *topk_idx_out, float *topk_w_out, void *ws, size_t ws_bytes,
+                         void *stream, void **events, int max_events, int *n_kernels) {
+  if (!events || max_events < 2 || !n_kernels) return K3MOE_EINVAL;
+  g_prof = ProfMarks();
+  g_prof.events = events;
+  g_prof.max_events = max_events;
+  if (hipEventRecord((hipEvent_t)events[0], (hipStream_t)stream) != hipSuccess) {
+    g_prof = ProfMarks();
+    return K3MOE_EHIP;
+  }
+  const int rc = k3moe_layer(d, T, x, wt, y, topk_idx_out, topk_w_out, ws, ws_bytes, stream);
+  *n_kernels = g_prof.n;
+  g_prof.events = nullptr;
+  return rc;
+}
+
+const char *k3moe_prof_name(int i) {
+  return (i >= 0 && i < g_prof.n && i < 64) ? g_prof.names[i] : "";
+}
+
+const char *k3moe_status_str(int status) {
+  switch (status) {
+    case K3MOE_OK: return "ok";
+    case K3MOE_EINVAL: return "invalid argument";
+    case K3MOE_EUNSUPPORTED: return "unsupported shape or alignment";
+    case K3MOE_EWORKSPACE: return "workspace missing or too small";
+    case K3MOE_EHIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

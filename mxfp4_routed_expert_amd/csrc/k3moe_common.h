@@ -1,0 +1,87 @@
+// Shared device helpers for the k3moe HIP kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace k3 {
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kGroup = 32;  // MXFP4 group: 32 columns share one ue8m0 scale
+
+// One 16x16x32 bf16 matrix-core step: c[m][n] += sum_k a[m][k] * b[k][n].
+// Lane l supplies row (l % 16) of A and column (l % 16) of B, each with 8 values of
+// the k-chunk (l / 16); lane l receives c[4 * (l / 16) + i][l % 16], i = 0..3.
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// fp32 -> bf16 bits, round to nearest, ties to even (inputs are finite).
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ float bf16_val(uint32_t b) { return __uint_as_float(b << 16); }
+
+// x = p0 + p1 (+ p2) + r with each p a bf16: every difference below is exact in fp32,
+// so three pieces carry all 24 significant bits and two carry 16.
+template <int P>
+__device__ __forceinline__ void split_bf16(float x, uint32_t (&p)[3]) {
+  p[0] = bf16_bits(x);
+  float r = x - bf16_val(p[0]);
+  if (P > 1) {
+    p[1] = bf16_bits(r);
+    r = r - bf16_val(p[1]);
+  }
+  if (P > 2) p[2] = bf16_bits(r);
+}
+
+// 8 fp32 -> P bf16x8 fragments.
+template <int P>
+__device__ __forceinline__ void split_x8(const float (&v)[8], u32x4 (&out)[3]) {
+  uint32_t w[3][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t p[3] = {0, 0, 0};
+    split_bf16<P>(v[i], p);
+#pragma unroll
+    for (int q = 0; q < 3; ++q) w[q][i] = p[q];
+  }
+#pragma unroll
+  for (int q = 0; q < 3; ++q)
+    out[q] = u32x4{w[q][0] | (w[q][1] << 16), w[q][2] | (w[q][3] << 16),
+                   w[q][4] | (w[q][5] << 16), w[q][6] | (w[q][7] << 16)};
+}
+
+// ue8m0 scale byte -> the fp32 scale handed to the fp4 converter. Byte 255 is handled
+// by the caller (its group is zeroed, as the pages prescribe).
+__device__ __forceinline__ float e8m0_f32(uint32_t s) {
+  return s == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(s << 23);
+}
+
+// Four packed bytes (8 E2M1 codes, low nibble = even column) -> 8 bf16 = code * scale,
+// in column order. e2m1 * 2^k has two significant bits, so every value is exact.
+__device__ __forceinline__ u32x4 fp4x8_to_bf16(uint32_t w, float scale) {
+  bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+  bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+  bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+  bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+  return u32x4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+               __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
+}
+
+// SiTU-GLU: b1 tanh(g/b1) sigmoid(g) * b2 tanh(u/b2); the sigmoid reads the uncapped g.
+__device__ __forceinline__ float situ(float g, float u, float b1, float b2) {
+  const float gate = b1 * tanhf(g / b1) * (1.0f / (1.0f + expf(-g)));
+  return gate * (b2 * tanhf(u / b2));
+}
+
+}  // namespace k3

@@ -1,0 +1,62 @@
+// Kernel argument blocks and launcher declarations for the k3moe library (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace k3 {
+
+// ---------------------------------------------------------------- dense products
+// out[n][m] = sum_k A[m][k] * B[n][k] for a weight matrix A [M][K] (bf16, or fp32 split
+// into three bf16 pieces) and activations B [N][K] given as PB bf16 pieces that sum to
+// the fp32 value.
+enum AFormat { kA_BF16 = 0, kA_F32 = 1 };
+enum DenseEpi { kEpiStore = 0, kEpiStorePlanes = 1 };
+
+struct DenseArgs {
+  const void *A;        // [M][K]
+  int M, K, ng;         // ng = K / 32
+  const uint16_t *B[3]; // pieces [N][K]
+  int N;
+  float *out;           // [ks][N][M] (kEpiStore) or [N][M] (nullable with planes)
+  uint16_t *planes[3];  // [N][M] bf16 pieces of the fp32 result (kEpiStorePlanes)
+};
+
+// ---------------------------------------------------------------- grouped MXFP4
+struct MxMat {
+  const uint8_t *packed;
+  const uint8_t *scales;
+  int64_t pstride, sstride;  // bytes between experts
+};
+
+enum GroupedEpi { kEpiSitu = 0, kEpiEdn = 1 };
+
+struct GroupedArgs {
+  MxMat A[2];             // gate/up: {w1, w3}; down: {w2}
+  int M, K, ng;           // rows, cols, groups per row
+  const uint16_t *B[3];   // activation pieces, row = token (gather) or sorted slot
+  int gather, topk;
+  const int32_t *expert_off, *sorted_pair, *active, *n_active;
+  float *out;             // kEpiEdn: [slot][M] fp32
+  uint16_t *planes[3];    // kEpiSitu: [slot][M] bf16 pieces of act
+  float b1, b2;
+};
+
+// ---------------------------------------------------------------- launchers
+hipError_t launch_dense_router(const DenseArgs &a, int ks, hipStream_t s);
+hipError_t launch_dense_bf16(const DenseArgs &a, int pieces, int epi, hipStream_t s);
+hipError_t launch_topk(const float *part, int ks, int T, int E, const float *bias, int K,
+                       int renorm, float rscale, int32_t *idx, float *w, hipStream_t s);
+hipError_t launch_dispatch(const int32_t *topk_idx, int T, int K, int E, int32_t *expert_off,
+                           int32_t *sorted_pair, int32_t *pair_slot, int32_t *active,
+                           int32_t *counters, int32_t *lrank, int32_t *cnt, hipStream_t s);
+hipError_t launch_active_from_off(const int32_t *expert_off, int E, int32_t *active,
+                                  int32_t *counters, hipStream_t s);
+hipError_t launch_split_planes(const float *src, size_t n, uint16_t *p0, uint16_t *p1,
+                               uint16_t *p2, hipStream_t s);
+hipError_t launch_grouped(const GroupedArgs &a, int epi, int pieces, int grid_y, hipStream_t s);
+hipError_t launch_combine(const float *edn, const int32_t *pair_slot, const float *topk_w,
+                          const float *gamma, int T, int K, int L, float eps, uint16_t *p0,
+                          uint16_t *p1, uint16_t *p2, hipStream_t s);
+
+}  // namespace k3

@@ -1,0 +1,64 @@
+"""Device-memory plumbing: torch allocates HBM, the generated host arrays are copied in,
+and the ctypes views of the weights are assembled for the C-ABI. No arithmetic of the
+layer happens here."""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import torch
+
+from . import k3moe
+
+
+def _dev(a: np.ndarray, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+@dataclasses.dataclass
+class DeviceLayer:
+    dims: object
+    w_router: torch.Tensor
+    bias: torch.Tensor
+    w_down: torch.Tensor
+    w_up: torch.Tensor
+    norm_w: torch.Tensor
+    experts: torch.Tensor       # uint8 [E * blob_bytes]: per-expert records back to back
+    blob_bytes: int
+    offsets: dict
+
+    def experts_struct(self) -> k3moe.k3moe_experts:
+        base = self.experts.data_ptr()
+        B = self.blob_bytes
+
+        def mx(p, s):
+            return k3moe.k3moe_mxfp4(base + self.offsets[p], base + self.offsets[s], B, B)
+        return k3moe.k3moe_experts(mx("w1p", "w1s"), mx("w3p", "w3s"), mx("w2p", "w2s"))
+
+    def weights_struct(self) -> k3moe.k3moe_weights:
+        return k3moe.k3moe_weights(self.w_router.data_ptr(), self.bias.data_ptr(), self.w_down.data_ptr(),
+                                   self.w_up.data_ptr(), self.norm_w.data_ptr(), self.experts_struct())
+
+
+def upload_layer(dims, dense: dict, expert_chunks, blob_bytes: int, offsets: dict, device="cuda") -> DeviceLayer:
+    """dense: host arrays (w_router fp32 [E,H], bias fp32 [E], w_down/w_up bf16 bits, norm_w fp32).
+    expert_chunks: iterable of (first expert, uint8 blob array) covering experts 0..E-1 in order;
+    each chunk is copied into one preallocated device buffer, so host memory stays at one chunk."""
+    E = dims.n_experts
+    ex = torch.empty(E * blob_bytes, dtype=torch.uint8, device=device)
+    for e0, arr in expert_chunks:
+        n = arr.size
+        ex[e0 * blob_bytes: e0 * blob_bytes + n].copy_(torch.from_numpy(arr), non_blocking=False)
+    return DeviceLayer(
+        dims=dims,
+        w_router=_dev(dense["w_router"].astype(np.float32), device),
+        bias=_dev(dense["bias"].astype(np.float32), device),
+        w_down=_dev(dense["w_down"].view(np.int16), device),
+        w_up=_dev(dense["w_up"].view(np.int16), device),
+        norm_w=_dev(dense["norm_w"].astype(np.float32), device),
+        experts=ex, blob_bytes=blob_bytes, offsets=dict(offsets))
+
+
+def workspace(dims, T: int, device="cuda") -> torch.Tensor:
+    n = k3moe.k3moe_workspace_size(dims, T)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)

@@ -1,0 +1,117 @@
+"""Host-side checks of the C-ABI: the library loads, exports every entry point the
+header declares, and refuses bad arguments before launching anything (so these run
+without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import k3gen
+from mxfp4_routed_expert_amd import k3moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "k3moe.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(k3moe_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert set(names) >= set(k3moe.EXPORTS[:-1])
+    lib = ctypes.CDLL(k3moe.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    assert k3moe.status_str(0) == "ok"
+    for c in (-1, -2, -3, -4):
+        assert k3moe.status_str(c) != "unknown status"
+
+
+def _d(**kw):
+    base = dict(hidden=256, latent=128, inter=96, n_experts=32, topk=4, group=32, renorm=1,
+                routed_scale=1.0, eps=1e-6, b1=4.0, b2=25.0)
+    base.update(kw)
+    return k3moe.k3moe_dims(**base)
+
+
+def test_workspace_size_grows_with_T_and_refuses_bad_dims():
+    a = k3moe.k3moe_workspace_size(k3gen.TINY, 4)
+    b = k3moe.k3moe_workspace_size(k3gen.TINY, 400)
+    assert 0 < a < b
+    assert k3moe.k3moe_workspace_size(k3gen.TINY, 0) >= 0
+    n = ctypes.c_size_t()
+    L = k3moe.load()
+    bad = {
+        k3moe.K3MOE_EINVAL: [dict(hidden=0), dict(topk=0), dict(renorm=2), dict(eps=-1.0), dict(b1=0.0)],
+        k3moe.K3MOE_EUNSUPPORTED: [dict(group=16), dict(latent=100), dict(inter=40), dict(hidden=250),
+                                   dict(topk=33, n_experts=64), dict(topk=8, n_experts=4),
+                                   dict(n_experts=1025)],
+    }
+    for code, cases in bad.items():
+        for kw in cases:
+            assert L.k3moe_workspace_size(ctypes.byref(_d(**kw)), 4, ctypes.byref(n)) == code, kw
+    assert L.k3moe_workspace_size(ctypes.byref(_d()), -1, ctypes.byref(n)) == k3moe.K3MOE_EINVAL
+    assert L.k3moe_workspace_size(None, 4, ctypes.byref(n)) == k3moe.K3MOE_EINVAL
+    assert L.k3moe_workspace_size(ctypes.byref(_d()), 4, None) == k3moe.K3MOE_EINVAL
+    # T * topk must fit in int32
+    assert L.k3moe_workspace_size(ctypes.byref(_d(topk=4)), 2 ** 29, ctypes.byref(n)) == k3moe.K3MOE_EUNSUPPORTED
+
+
+FAKE = 1 << 20          # an aligned, never dereferenced address
+WS = (1 << 24, 1 << 40)  # aligned fake workspace, large
+
+
+def test_route_refuses_before_launch():
+    d = _d()
+    f = k3moe.k3moe_route
+    assert f(d, 4, None, FAKE, FAKE, FAKE, FAKE, WS, check=False) == k3moe.K3MOE_EINVAL
+    assert f(d, 4, FAKE, FAKE, None, FAKE, FAKE, WS, check=False) == k3moe.K3MOE_EINVAL
+    assert f(d, 4, FAKE + 2, FAKE, FAKE, FAKE, FAKE, WS, check=False) == k3moe.K3MOE_EUNSUPPORTED
+    assert f(d, 4, FAKE, FAKE, FAKE, FAKE, FAKE, (1 << 24, 100), check=False) == k3moe.K3MOE_EWORKSPACE
+    assert f(d, 4, FAKE, FAKE, FAKE, FAKE, FAKE, (None, 0), check=False) == k3moe.K3MOE_EWORKSPACE
+    assert f(d, 4, FAKE, FAKE, FAKE, FAKE, FAKE, ((1 << 24) + 64, 1 << 40), check=False) == k3moe.K3MOE_EUNSUPPORTED
+    assert f(_d(topk=40), 4, FAKE, FAKE, FAKE, FAKE, FAKE, WS, check=False) == k3moe.K3MOE_EUNSUPPORTED
+    assert f(d, -3, FAKE, FAKE, FAKE, FAKE, FAKE, WS, check=False) == k3moe.K3MOE_EINVAL
+    # T == 0 is a no-op that launches nothing
+    assert f(d, 0, FAKE, FAKE, FAKE, FAKE, FAKE, WS, check=False) == k3moe.K3MOE_OK
+
+
+def _experts(packed=FAKE, stride=1 << 16):
+    m = k3moe.k3moe_mxfp4(packed, FAKE, stride, 4096)
+    return k3moe.k3moe_experts(m, m, m)
+
+
+def test_expert_stage_refuses_before_launch():
+    d = _d()
+    f = k3moe.k3moe_expert_glu_mxfp4
+    assert f(d, 4, FAKE, None, FAKE, FAKE, FAKE, WS, check=False) == k3moe.K3MOE_EINVAL
+    assert f(d, 4, FAKE, _experts(packed=FAKE + 8), FAKE, FAKE, FAKE, WS, check=False) == k3moe.K3MOE_EUNSUPPORTED
+    assert f(d, 4, FAKE, _experts(stride=(1 << 16) + 4), FAKE, FAKE, FAKE, WS, check=False) == k3moe.K3MOE_EUNSUPPORTED
+    assert f(d, 4, FAKE, _experts(stride=-16), FAKE, FAKE, FAKE, WS, check=False) == k3moe.K3MOE_EINVAL
+    assert f(d, 4, FAKE + 4, _experts(), FAKE, FAKE, FAKE, WS, check=False) == k3moe.K3MOE_EUNSUPPORTED
+    assert f(d, 4, FAKE, _experts(), None, FAKE, FAKE, WS, check=False) == k3moe.K3MOE_EINVAL
+    assert f(d, 0, FAKE, _experts(), FAKE, FAKE, FAKE, WS, check=False) == k3moe.K3MOE_OK
+
+
+def test_other_entry_points_refuse_before_launch():
+    d = _d()
+    assert k3moe.k3moe_latent_proj_bf16(d, 4, FAKE, None, FAKE, WS, check=False) == k3moe.K3MOE_EINVAL
+    assert k3moe.k3moe_latent_proj_bf16(d, 4, FAKE, FAKE + 2, FAKE, WS, check=False) == k3moe.K3MOE_EUNSUPPORTED
+    assert k3moe.k3moe_dispatch(d, 4, None, FAKE, FAKE, FAKE, WS, check=False) == k3moe.K3MOE_EINVAL
+    assert k3moe.k3moe_dispatch(d, 4, FAKE, FAKE, FAKE, FAKE, (FAKE, 8), check=False) == k3moe.K3MOE_EWORKSPACE
+    assert k3moe.k3moe_combine(d, 4, FAKE, FAKE, FAKE, None, FAKE, FAKE, WS, check=False) == k3moe.K3MOE_EINVAL
+    assert k3moe.k3moe_combine(d, 4, FAKE, FAKE, FAKE, FAKE, FAKE + 2, FAKE, WS, check=False) == k3moe.K3MOE_EUNSUPPORTED
+    w = k3moe.k3moe_weights(FAKE, FAKE, FAKE, FAKE, FAKE, _experts())
+    assert k3moe.k3moe_layer(d, 4, FAKE, None, FAKE, None, None, WS, check=False) == k3moe.K3MOE_EINVAL
+    assert k3moe.k3moe_layer(d, 4, FAKE, w, None, None, None, WS, check=False) == k3moe.K3MOE_EINVAL
+    wb = k3moe.k3moe_weights(FAKE, None, FAKE, FAKE, FAKE, _experts())
+    assert k3moe.k3moe_layer(d, 4, FAKE, wb, FAKE, None, None, WS, check=False) == k3moe.K3MOE_EINVAL
+    assert k3moe.k3moe_layer(d, 0, FAKE, w, FAKE, None, None, WS, check=False) == k3moe.K3MOE_OK
+    with pytest.raises(k3moe.K3MoeError):
+        k3moe.k3moe_layer(d, 4, FAKE, None, FAKE, None, None, WS)

@@ -1,0 +1,238 @@
+"""GPU parity: the HIP path (through the C-ABI) against the CPU oracle, on the same
+seeded inputs. Expert indices and all integer outputs bit-exact; floating outputs per
+token row within rel-L2 <= 1e-5 and max-abs <= 1e-4 * max|ref| (the layer's stated
+tolerance; stage outputs are held to the same bar)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+import k3gen
+import oracle
+from tests import _inputs
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+from mxfp4_routed_expert_amd import device, k3moe  # noqa: E402
+
+REL = 1e-5
+ABSF = 1e-4
+
+
+def say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def check_rows(got: np.ndarray, ref: np.ndarray, what: str, rel=REL, absf=ABSF):
+    got = np.asarray(got, np.float64).reshape(ref.shape[0], -1)
+    ref = np.asarray(ref, np.float64).reshape(ref.shape[0], -1)
+    assert np.all(np.isfinite(got)), what
+    err = np.linalg.norm(got - ref, axis=1) / np.maximum(np.linalg.norm(ref, axis=1), 1e-30)
+    mabs = np.max(np.abs(got - ref), axis=1) / np.maximum(np.max(np.abs(ref), axis=1), 1e-30)
+    say(f"  {what}: max row rel-L2 {err.max():.3e}, max abs/max|ref| {mabs.max():.3e}")
+    assert err.max() <= rel, (what, float(err.max()))
+    assert mabs.max() <= absf, (what, float(mabs.max()))
+    return float(err.max())
+
+
+class Host:
+    def __init__(self, dims, seed, dense=None):
+        self.dims = dims
+        self.dense = dense if dense is not None else k3gen.gen_dense(dims, seed)
+        self.lay = k3gen.ExpertLayout(dims)
+        self.blobs = k3gen.gen_experts(dims, seed, 0, dims.n_experts)
+        self.ex = oracle.ExpertSet(self.blobs, self.lay.blob_bytes, self.lay.offsets)
+        B = self.lay.blob_bytes
+        chunks = ((e0, self.blobs[e0 * B:min(dims.n_experts, e0 + 64) * B])
+                  for e0 in range(0, dims.n_experts, 64))
+        self.dev = device.upload_layer(dims, self.dense, chunks, B, self.lay.offsets)
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    return Host(k3gen.TINY, 0)
+
+
+@pytest.fixture(scope="module")
+def k3():
+    say("generating and uploading the K3-shape layer (896 experts, 15.7 GB)")
+    return Host(k3gen.K3, 1)
+
+
+def t_(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    return t if dtype is None else t.to(dtype)
+
+
+def run_layer(h: Host, x: np.ndarray):
+    d = h.dims
+    T = x.shape[0]
+    xd = t_(x.view(np.int16))
+    y = torch.empty((T, d.hidden), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, d.topk), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, d.topk), dtype=torch.float32, device="cuda")
+    ws = device.workspace(d, T)
+    k3moe.k3moe_layer(d, T, xd, h.dev.weights_struct(), y, idx, w, ws)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
+
+
+def compare_layer(h: Host, x: np.ndarray, rows=None, what="layer"):
+    y, idx, w = run_layer(h, x)
+    rows = np.arange(x.shape[0]) if rows is None else np.asarray(rows)
+    ref = oracle.layer(h.dims, x[rows], h.dense, h.ex)
+    assert np.array_equal(idx[rows], ref["idx"]), f"{what}: expert ids differ"
+    check_rows(w[rows], ref["w"], f"{what} weights", rel=1e-6, absf=1e-6)
+    return check_rows(y[rows], ref["y"], f"{what} y")
+
+
+def stages(h: Host, x: np.ndarray):
+    """Each ABI stage alone, fed the oracle's own inputs for that stage."""
+    d = h.dims
+    T, K, L, E = x.shape[0], d.topk, d.latent, d.n_experts
+    ws = device.workspace(d, T)
+    ref = oracle.layer(d, x, h.dense, h.ex, want_inner=True)
+    xd = t_(x.view(np.int16))
+    # route
+    idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    k3moe.k3moe_route(d, T, xd, h.dev.w_router, h.dev.bias, idx, w, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), ref["idx"])
+    check_rows(w.cpu().numpy(), ref["w"], "route weights", rel=1e-6, absf=1e-6)
+    # latent projection
+    z = torch.empty((T, L), dtype=torch.float32, device="cuda")
+    k3moe.k3moe_latent_proj_bf16(d, T, xd, h.dev.w_down, z, ws)
+    torch.cuda.synchronize()
+    check_rows(z.cpu().numpy(), ref["z"], "latent z", rel=1e-6, absf=1e-6)
+    # dispatch on the oracle's ids
+    off_r, sp_r, ps_r = oracle.dispatch(ref["idx"], E)
+    off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    sp = torch.empty(T * K, dtype=torch.int32, device="cuda")
+    ps = torch.empty(T * K, dtype=torch.int32, device="cuda")
+    k3moe.k3moe_dispatch(d, T, t_(ref["idx"]), off, sp, ps, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(off.cpu().numpy(), off_r)
+    assert np.array_equal(sp.cpu().numpy(), sp_r)
+    assert np.array_equal(ps.cpu().numpy(), ps_r)
+    # experts on the oracle's z, in the oracle's sorted order
+    edn = torch.empty((T * K, L), dtype=torch.float32, device="cuda")
+    k3moe.k3moe_expert_glu_mxfp4(d, T, t_(ref["z"]), h.dev.experts_struct(), t_(off_r), t_(sp_r), edn, ws)
+    torch.cuda.synchronize()
+    tok = sp_r // K
+    exid = ref["idx"].reshape(-1)[sp_r]
+    edn_ref = oracle.expert_pairs(d, tok, exid, ref["z"], h.ex)
+    check_rows(edn.cpu().numpy(), edn_ref, "expert edn")
+    # combine on the oracle's edn
+    y = torch.empty((T, d.hidden), dtype=torch.float32, device="cuda")
+    k3moe.k3moe_combine(d, T, t_(edn_ref), t_(ps_r), t_(ref["w"]), h.dev.norm_w, h.dev.w_up, y, ws)
+    torch.cuda.synchronize()
+    check_rows(y.cpu().numpy(), ref["y"], "combine y")
+
+
+# ------------------------------------------------------------------ tiny (config 0)
+def test_tiny_stages(tiny):
+    x, _ = _inputs.gap_fixed_x(tiny.dims, 0, 4, tiny.dense["w_router"], tiny.dense["bias"])
+    stages(tiny, x)
+
+
+def test_tiny_layer_config0(tiny):
+    x, _ = _inputs.gap_fixed_x(tiny.dims, 0, 4, tiny.dense["w_router"], tiny.dense["bias"])
+    compare_layer(tiny, x, what="tiny T=4")
+
+
+@pytest.mark.parametrize("T", [1, 3, 16, 64, 65, 129, 300])
+def test_tiny_layer_ragged_T(tiny, T):
+    say(f"tiny layer T={T}")
+    x, _ = _inputs.gap_fixed_x(tiny.dims, 100 + T, T, tiny.dense["w_router"], tiny.dense["bias"])
+    compare_layer(tiny, x, what=f"tiny T={T}")
+
+
+def test_tiny_dispatch_chunked_and_invalid_ids(tiny):
+    d = tiny.dims
+    rng = np.random.default_rng(7)
+    for T in (1, 63, 64, 65, 200, 1000):
+        ids = np.stack([rng.choice(d.n_experts, d.topk, replace=False) for _ in range(T)]).astype(np.int32)
+        ids.sort(axis=1)
+        ws = device.workspace(d, T)
+        off = torch.empty(d.n_experts + 1, dtype=torch.int32, device="cuda")
+        sp = torch.empty(T * d.topk, dtype=torch.int32, device="cuda")
+        ps = torch.empty(T * d.topk, dtype=torch.int32, device="cuda")
+        k3moe.k3moe_dispatch(d, T, t_(ids), off, sp, ps, ws)
+        torch.cuda.synchronize()
+        o, s, p = oracle.dispatch(ids, d.n_experts)
+        assert np.array_equal(off.cpu().numpy(), o) and np.array_equal(sp.cpu().numpy(), s)
+        assert np.array_equal(ps.cpu().numpy(), p)
+    # out-of-range ids are dropped: pair_slot -1, the rest still a stable sort
+    ids = np.array([[0, 5, 40, 2], [1, -3, 5, 9]], np.int32)
+    ws = device.workspace(d, 2)
+    off = torch.empty(d.n_experts + 1, dtype=torch.int32, device="cuda")
+    sp = torch.full((8,), -7, dtype=torch.int32, device="cuda")
+    ps = torch.empty(8, dtype=torch.int32, device="cuda")
+    k3moe.k3moe_dispatch(d, 2, t_(ids), off, sp, ps, ws)
+    torch.cuda.synchronize()
+    ps = ps.cpu().numpy()
+    assert ps[2] == -1 and ps[5] == -1
+    assert off.cpu().numpy()[-1] == 6
+    valid = [p for p in range(8) if ps[p] >= 0]
+    assert sorted(ps[valid].tolist()) == list(range(6))
+    flat = ids.reshape(-1)
+    order = sp.cpu().numpy()[:6]
+    assert list(order) == sorted(valid, key=lambda p: (flat[p], p))
+
+
+def test_tiny_combine_random_gamma_and_scale(tiny):
+    """RMSNorm weight and routed_scale other than 1 reach the result."""
+    import dataclasses
+    d = dataclasses.replace(tiny.dims, routed_scale=2.5, renorm=1)
+    dense = dict(tiny.dense)
+    dense["norm_w"] = k3gen.uniform_f32(d.latent, 3, k3gen.T_GAMMA, 0.5, 1.5)
+    h = tiny
+    x, _ = _inputs.gap_fixed_x(d, 5, 8, dense["w_router"], dense["bias"])
+    ref = oracle.layer(d, x, dense, h.ex)
+    T = 8
+    y = torch.empty((T, d.hidden), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, d.topk), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, d.topk), dtype=torch.float32, device="cuda")
+    ws = device.workspace(d, T)
+    ww = h.dev.weights_struct()
+    gam = t_(dense["norm_w"])
+    ww.norm_w = gam.data_ptr()
+    k3moe.k3moe_layer(d, T, t_(x.view(np.int16)), ww, y, idx, w, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), ref["idx"])
+    check_rows(w.cpu().numpy(), ref["w"], "scaled weights", rel=1e-6, absf=1e-6)
+    check_rows(y.cpu().numpy(), ref["y"], "gamma y")
+
+
+# ------------------------------------------------------------------ K3 shape
+def test_k3_stages_T1(k3):
+    x, _ = _inputs.gap_fixed_x(k3.dims, 1, 1, k3.dense["w_router"], k3.dense["bias"])
+    stages(k3, x)
+
+
+def test_k3_layer_config1_T1(k3):
+    x, _ = _inputs.gap_fixed_x(k3.dims, 1, 1, k3.dense["w_router"], k3.dense["bias"])
+    compare_layer(k3, x, what="K3 T=1")
+
+
+def test_k3_layer_config2_T64(k3):
+    x, _ = _inputs.gap_fixed_x(k3.dims, 2, 64, k3.dense["w_router"], k3.dense["bias"])
+    compare_layer(k3, x, what="K3 T=64")
+
+
+def test_k3_layer_config3_T4096_sampled(k3):
+    T = 4096
+    say("K3 T=4096: gap rule over all tokens (oracle router)")
+    x, _ = _inputs.gap_fixed_x(k3.dims, 3, T, k3.dense["w_router"], k3.dense["bias"])
+    y, idx, w = run_layer(k3, x)
+    ridx, rw, _ = oracle.route_batch(k3.dims, x, k3.dense["w_router"], k3.dense["bias"])
+    assert np.array_equal(idx, ridx), "expert ids differ"
+    check_rows(w, rw, "T=4096 weights", rel=1e-6, absf=1e-6)
+    rows = np.random.default_rng(3).choice(T, 24, replace=False)
+    rows = np.concatenate([[0, T - 1], rows])
+    ref = oracle.layer(k3.dims, x[rows], k3.dense, k3.ex)
+    check_rows(y[rows], ref["y"], "T=4096 sampled y")
