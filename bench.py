@@ -87,6 +87,9 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=32)
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="first run one plain device-to-device copy of this many MiB (a known-size "
+                         "kernel for scaling hardware byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -120,6 +123,16 @@ def main():
 
     stream = torch.cuda.Stream()
     wts = dev.weights_struct()
+
+    if args.copy_calib_mib:
+        n = args.copy_calib_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {n} bytes device to device")
+        del src, dst
 
     # ---------------------------------------------------------------- decode, T = 1
     T = 1

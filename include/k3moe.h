@@ -37,7 +37,7 @@
  *    entry does not matter and on return is unspecified.
  *  - Row-major everywhere. bf16 values are passed as their 16-bit patterns.
  *  - Supported shapes: every dimension >= 1; hidden, latent and inter multiples of
- *    32; latent <= 16384; group == 32; topk <= 32 and topk <= n_experts <= 1024; T >= 0 (T == 0 is a
+ *    32; latent, inter <= 8192; latent * hidden < 2^30 and n_experts * hidden < 2^29; group == 32; topk <= 32 and topk <= n_experts <= 1024; T >= 0 (T == 0 is a
  *    no-op); T * topk < 2^31. Scale bytes 2..254 and 255 are exact on the GPU path;
  *    0 and 1 give weights below 2^-126, which the matrix cores may flush to zero.
  *  - Errors: every call returns K3MOE_OK (0) or a negative code. All argument

@@ -12,7 +12,7 @@ using namespace k3;
 
 namespace {
 
-constexpr int kRouterSplits = 8;  // K-splits of the router product (partials summed by top-k)
+constexpr int kRouterSplits = 7;  // K-splits of the router product (partials summed by top-k)
 constexpr int kPieces = 3;        // bf16 pieces per fp32 activation
 
 bool al16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -29,8 +29,11 @@ int check_dims(const k3moe_dims *d) {
   if (d->group != 32) return K3MOE_EUNSUPPORTED;
   if (d->hidden % 32 || d->latent % 32 || d->inter % 32) return K3MOE_EUNSUPPORTED;
   if (d->topk > 32 || d->topk > d->n_experts || d->n_experts > 1024) return K3MOE_EUNSUPPORTED;
-  // the combine kernel stages one latent row (fp32) in LDS
-  if (d->latent > 16384 || d->hidden > (1 << 20)) return K3MOE_EUNSUPPORTED;
+  // one token's activation pieces (3 x bf16) are staged in 64 KB of LDS
+  if (d->latent > 8192 || d->inter > 8192 || d->hidden > (1 << 20)) return K3MOE_EUNSUPPORTED;
+  // each dense weight matrix is read through one 32-bit-sized buffer descriptor
+  if ((int64_t)d->n_experts * d->hidden * 4 > INT32_MAX || (int64_t)d->latent * d->hidden * 2 > INT32_MAX)
+    return K3MOE_EUNSUPPORTED;
   return K3MOE_OK;
 }
 
@@ -61,7 +64,8 @@ struct Ws {
   int32_t *cnt;                // [chunks][E]
   uint16_t *actp[3];           // [P][I]
   float *edn;                  // [P][L]
-  uint16_t *np[3];             // [T][L]
+  uint16_t *np[3];             // [T][L] pieces of gamma * acc
+  float *ss;                   // [T][ceil(L/256)] partial sums of acc^2
   size_t bytes;
 };
 
@@ -91,6 +95,7 @@ Ws carve(const k3moe_dims *d, int32_t T, void *base) {
   for (int q = 0; q < 3; ++q) w.actp[q] = (uint16_t *)take(P * I * 2);
   w.edn = (float *)take(P * L * 4);
   for (int q = 0; q < 3; ++q) w.np[q] = (uint16_t *)take(t * L * 2);
+  w.ss = (float *)take(t * ((L + 255) / 256) * 4);
   w.bytes = o;
   return w;
 }
@@ -131,8 +136,7 @@ hipError_t mark(const char *name, hipStream_t s) {
   } while (0)
 
 // ---- step launchers (arguments already checked)
-int run_route(const k3moe_dims *d, int32_t T, const uint16_t *x, const float *wr, const float *bias,
-              int32_t *idx, float *wt, const Ws &w, hipStream_t s) {
+DenseArgs router_args(const k3moe_dims *d, int32_t T, const uint16_t *x, const float *wr, const Ws &w) {
   DenseArgs a = {};
   a.A = wr;
   a.M = d->n_experts;
@@ -141,16 +145,11 @@ int run_route(const k3moe_dims *d, int32_t T, const uint16_t *x, const float *wr
   a.B[0] = a.B[1] = a.B[2] = x;
   a.N = T;
   a.out = w.router_part;
-  K3_HIP(launch_dense_router(a, kRouterSplits, s));
-  K3_HIP(mark("router_gemv", s));
-  K3_HIP(launch_topk(w.router_part, kRouterSplits, T, d->n_experts, bias, d->topk, d->renorm,
-                     d->routed_scale, idx, wt, s));
-  K3_HIP(mark("topk", s));
-  return K3MOE_OK;
+  return a;
 }
 
-int run_down(const k3moe_dims *d, int32_t T, const uint16_t *x, const uint16_t *wd, float *z,
-             uint16_t *const zp[3], hipStream_t s) {
+DenseArgs down_args(const k3moe_dims *d, int32_t T, const uint16_t *x, const uint16_t *wd, float *z,
+                    uint16_t *const zp[3]) {
   DenseArgs a = {};
   a.A = wd;
   a.M = d->latent;
@@ -160,6 +159,25 @@ int run_down(const k3moe_dims *d, int32_t T, const uint16_t *x, const uint16_t *
   a.N = T;
   a.out = z;
   for (int q = 0; q < 3; ++q) a.planes[q] = zp[q];
+  return a;
+}
+
+// router product (and, when `down` is given, the latent projection in the same launch),
+// then the top-k
+int run_route(const k3moe_dims *d, int32_t T, const uint16_t *x, const float *wr, const float *bias,
+              int32_t *idx, float *wt, const DenseArgs *down, const Ws &w, hipStream_t s) {
+  const DenseArgs a = router_args(d, T, x, wr, w);
+  K3_HIP(launch_route_down(a, kRouterSplits, down, s));
+  K3_HIP(mark(down ? "router_and_latent_down" : "router_gemv", s));
+  K3_HIP(launch_topk(w.router_part, kRouterSplits, T, d->n_experts, bias, d->topk, d->renorm,
+                     d->routed_scale, idx, wt, s));
+  K3_HIP(mark("topk", s));
+  return K3MOE_OK;
+}
+
+int run_down(const k3moe_dims *d, int32_t T, const uint16_t *x, const uint16_t *wd, float *z,
+             uint16_t *const zp[3], hipStream_t s) {
+  const DenseArgs a = down_args(d, T, x, wd, z, zp);
   K3_HIP(launch_dense_bf16(a, 1, kEpiStorePlanes, s));
   K3_HIP(mark("latent_down_gemv", s));
   return K3MOE_OK;
@@ -169,6 +187,10 @@ int run_experts(const k3moe_dims *d, int32_t T, uint16_t *const zp[3], const k3m
                 const int32_t *expert_off, const int32_t *sorted_pair, const int32_t *active,
                 const int32_t *counters, float *edn, const Ws &w, hipStream_t s) {
   const int grid_y = (int)((int64_t)T * d->topk < d->n_experts ? (int64_t)T * d->topk : d->n_experts);
+  // tokens staged per tile (an expert holds at most T tokens), as many as fit in LDS
+  const int kmax = d->latent > d->inter ? d->latent : d->inter;
+  int tt = T <= 1 ? 1 : 2;
+  if (grouped_dec_lds(kmax, tt) > kMaxBlockLds) tt = 1;
   GroupedArgs g = {};
   g.A[0] = MxMat{ex->w1.packed, ex->w1.scales, ex->w1.packed_expert_stride, ex->w1.scales_expert_stride};
   g.A[1] = MxMat{ex->w3.packed, ex->w3.scales, ex->w3.packed_expert_stride, ex->w3.scales_expert_stride};
@@ -185,7 +207,7 @@ int run_experts(const k3moe_dims *d, int32_t T, uint16_t *const zp[3], const k3m
   for (int q = 0; q < 3; ++q) g.planes[q] = w.actp[q];
   g.b1 = d->b1;
   g.b2 = d->b2;
-  K3_HIP(launch_grouped(g, kEpiSitu, kPieces, grid_y, s));
+  K3_HIP(launch_grouped(g, kEpiSitu, tt, grid_y, s));
   K3_HIP(mark("expert_gateup_situ", s));
 
   GroupedArgs h = g;
@@ -197,7 +219,7 @@ int run_experts(const k3moe_dims *d, int32_t T, uint16_t *const zp[3], const k3m
   for (int q = 0; q < 3; ++q) h.B[q] = w.actp[q];
   h.gather = 0;
   h.out = edn;
-  K3_HIP(launch_grouped(h, kEpiEdn, kPieces, grid_y, s));
+  K3_HIP(launch_grouped(h, kEpiEdn, tt, grid_y, s));
   K3_HIP(mark("expert_down", s));
   return K3MOE_OK;
 }
@@ -205,9 +227,9 @@ int run_experts(const k3moe_dims *d, int32_t T, uint16_t *const zp[3], const k3m
 int run_combine(const k3moe_dims *d, int32_t T, const float *edn, const int32_t *pair_slot,
                 const float *topk_w, const float *norm_w, const uint16_t *w_up, float *y,
                 const Ws &w, hipStream_t s) {
-  K3_HIP(launch_combine(edn, pair_slot, topk_w, norm_w, T, d->topk, d->latent, d->eps, w.np[0],
-                        w.np[1], w.np[2], s));
-  K3_HIP(mark("combine_rmsnorm", s));
+  K3_HIP(launch_combine(edn, pair_slot, topk_w, norm_w, T, d->topk, d->latent, w.np[0], w.np[1],
+                        w.np[2], w.ss, s));
+  K3_HIP(mark("combine", s));
   DenseArgs a = {};
   a.A = w_up;
   a.M = d->hidden;
@@ -216,8 +238,11 @@ int run_combine(const k3moe_dims *d, int32_t T, const float *edn, const int32_t 
   for (int q = 0; q < 3; ++q) a.B[q] = w.np[q];
   a.N = T;
   a.out = y;
-  K3_HIP(launch_dense_bf16(a, kPieces, kEpiStore, s));
-  K3_HIP(mark("up_gemv", s));
+  a.ss = w.ss;
+  a.nss = (d->latent + 255) / 256;
+  a.eps = d->eps;
+  K3_HIP(launch_dense_bf16(a, kPieces, kEpiStoreScaled, s));
+  K3_HIP(mark("rmsnorm_up_gemv", s));
   return K3MOE_OK;
 }
 
@@ -243,7 +268,7 @@ int k3moe_route(const k3moe_dims *d, int32_t T, const uint16_t *x, const float *
   Ws w;
   K3_TRY(check_ws(d, T, ws, ws_bytes, &w));
   if (T == 0) return K3MOE_OK;
-  return run_route(d, T, x, w_router, bias, topk_idx, topk_w, w, (hipStream_t)stream);
+  return run_route(d, T, x, w_router, bias, topk_idx, topk_w, nullptr, w, (hipStream_t)stream);
 }
 
 int k3moe_latent_proj_bf16(const k3moe_dims *d, int32_t T, const uint16_t *x, const uint16_t *w_down,
@@ -320,8 +345,8 @@ int k3moe_layer(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_w
   hipStream_t s = (hipStream_t)stream;
   int32_t *idx = topk_idx_out ? topk_idx_out : w.idx;
   float *tw = topk_w_out ? topk_w_out : w.w;
-  K3_TRY(run_route(d, T, x, wt->w_router, wt->bias, idx, tw, w, s));
-  K3_TRY(run_down(d, T, x, wt->w_down, nullptr, w.zp, s));
+  const DenseArgs down = down_args(d, T, x, wt->w_down, nullptr, w.zp);
+  K3_TRY(run_route(d, T, x, wt->w_router, wt->bias, idx, tw, &down, w, s));
   K3_HIP(launch_dispatch(idx, T, d->topk, d->n_experts, w.expert_off, w.sorted_pair, w.pair_slot,
                          w.active, w.counters, w.lrank, w.cnt, s));
   K3_HIP(mark("dispatch", s));

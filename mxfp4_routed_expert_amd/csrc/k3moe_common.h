@@ -13,6 +13,22 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
+
+// Raw buffer loads: a uniform base and size (an SGPR descriptor) plus 32-bit per-lane
+// and uniform offsets. An access past the size returns zeros instead of faulting, so
+// masked lanes load branch-free by pointing past the end (kOOB).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOOB = 0x80000000u;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint32_t bload8(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
+}
 constexpr int kGroup = 32;  // MXFP4 group: 32 columns share one ue8m0 scale
 
 // One 16x16x32 bf16 matrix-core step: c[m][n] += sum_k a[m][k] * b[k][n].

@@ -6,12 +6,15 @@
 
 namespace k3 {
 
+constexpr int kMaxRouterSplits = 8;  // partial router products summed by the top-k
+constexpr int kMaxNormParts = 64;    // column blocks of 256 in one latent row (latent <= 16384)
+
 // ---------------------------------------------------------------- dense products
 // out[n][m] = sum_k A[m][k] * B[n][k] for a weight matrix A [M][K] (bf16, or fp32 split
 // into three bf16 pieces) and activations B [N][K] given as PB bf16 pieces that sum to
 // the fp32 value.
 enum AFormat { kA_BF16 = 0, kA_F32 = 1 };
-enum DenseEpi { kEpiStore = 0, kEpiStorePlanes = 1 };
+enum DenseEpi { kEpiStore = 0, kEpiStorePlanes = 1, kEpiStoreScaled = 2 };
 
 struct DenseArgs {
   const void *A;        // [M][K]
@@ -20,6 +23,9 @@ struct DenseArgs {
   int N;
   float *out;           // [ks][N][M] (kEpiStore) or [N][M] (nullable with planes)
   uint16_t *planes[3];  // [N][M] bf16 pieces of the fp32 result (kEpiStorePlanes)
+  const float *ss;      // kEpiStoreScaled: [N][nss] partial sums of squares of the
+  int nss;              //   un-normed aggregate; out = acc / sqrt(sum(ss)/K + eps)
+  float eps;
 };
 
 // ---------------------------------------------------------------- grouped MXFP4
@@ -43,7 +49,7 @@ struct GroupedArgs {
 };
 
 // ---------------------------------------------------------------- launchers
-hipError_t launch_dense_router(const DenseArgs &a, int ks, hipStream_t s);
+hipError_t launch_route_down(const DenseArgs &router, int ks, const DenseArgs *down, hipStream_t s);
 hipError_t launch_dense_bf16(const DenseArgs &a, int pieces, int epi, hipStream_t s);
 hipError_t launch_topk(const float *part, int ks, int T, int E, const float *bias, int K,
                        int renorm, float rscale, int32_t *idx, float *w, hipStream_t s);
@@ -54,9 +60,12 @@ hipError_t launch_active_from_off(const int32_t *expert_off, int E, int32_t *act
                                   int32_t *counters, hipStream_t s);
 hipError_t launch_split_planes(const float *src, size_t n, uint16_t *p0, uint16_t *p1,
                                uint16_t *p2, hipStream_t s);
-hipError_t launch_grouped(const GroupedArgs &a, int epi, int pieces, int grid_y, hipStream_t s);
+// tokens_per_tile: 1, 2 or 5 activation rows staged in LDS per tile (grouped_dec_lds bytes)
+constexpr size_t kMaxBlockLds = 65536;
+size_t grouped_dec_lds(int K, int tokens_per_tile);
+hipError_t launch_grouped(const GroupedArgs &a, int epi, int tokens_per_tile, int grid_y, hipStream_t s);
 hipError_t launch_combine(const float *edn, const int32_t *pair_slot, const float *topk_w,
-                          const float *gamma, int T, int K, int L, float eps, uint16_t *p0,
-                          uint16_t *p1, uint16_t *p2, hipStream_t s);
+                          const float *gamma, int T, int K, int L, uint16_t *p0, uint16_t *p1,
+                          uint16_t *p2, float *ss_part, hipStream_t s);
 
 }  // namespace k3

@@ -17,73 +17,88 @@
 namespace k3 {
 
 // ============================================================== dense decode products
-// Grid: x = 16-row blocks of A, y = K splits (partial sums, router only),
-// z = column tiles. A tile of 16 MFMA columns holds 16/PB tokens x PB pieces; the
-// pieces are summed across lanes in the epilogue, so a token costs PB columns.
+// One block = 16 rows of A x one column tile; the block's waves split the K range (and
+// gridDim-level splits write partial sums). A tile of 16 MFMA columns holds 16/PB
+// tokens x PB pieces; the pieces are summed across lanes in the epilogue, so a token
+// costs PB columns. A and B of the next super-step are loaded while the current one
+// is multiplied.
 template <int AF, int PB, int EPI, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void k_dense_dec(DenseArgs a) {
+__device__ __forceinline__ void dense_body(const DenseArgs &a, int rbk, int ks, int nks, int tile) {
   constexpr int TPT = 16 / PB;
+  constexpr int ESZ = AF == kA_F32 ? 4 : 2;
+  constexpr int NRAW = AF == kA_F32 ? 8 : 4;
   __shared__ f32x4 red[WAVES][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rl = lane & 15, kq = lane >> 4;
   const int tn = rl / PB, piece = rl % PB;
-  const int row = blockIdx.x * 16 + rl;
-  const int tok = blockIdx.z * TPT + tn;
+  const int row = rbk * 16 + rl;
+  const int tok = tile * TPT + tn;
   const bool rok = row < a.M;
   const bool bok = (rl < TPT * PB) && (tok < a.N);
 
   const int nsup = (a.ng + 3) >> 2;
-  const int sps = (nsup + gridDim.y - 1) / gridDim.y;
-  const int s_lo = blockIdx.y * sps;
+  const int sps = (nsup + nks - 1) / nks;
+  const int s_lo = ks * sps;
   const int s_hi = min(nsup, s_lo + sps);
   const int spw = (max(s_hi - s_lo, 0) + WAVES - 1) / WAVES;
   const int w_lo = s_lo + wave * spw;
   const int w_hi = min(s_hi, w_lo + spw);
 
-  constexpr int ESZ = AF == kA_F32 ? 4 : 2;
-  constexpr int NRAW = AF == kA_F32 ? 8 : 4;
-  const char *arow = (const char *)a.A + (size_t)(rok ? row : 0) * a.K * ESZ;
-  const uint16_t *brow = a.B[piece < PB ? piece : 0] + (size_t)(bok ? tok : 0) * a.K;
+  // A through a buffer descriptor (rows past M and groups past K read as zero); B by
+  // clamped global loads and a select, so no load sits behind a branch
+  const rsrc_t rA = make_rsrc(a.A, (uint32_t)((size_t)a.M * a.K * ESZ));
+  const uint32_t aoff = rok ? (uint32_t)row * (uint32_t)a.K * ESZ + (uint32_t)kq * kGroup * ESZ : kOOB;
+  const int last_ok = a.ng - 4 * (nsup - 1);
+  const uint16_t *brow = a.B[piece < PB ? piece : 0] + (size_t)(bok ? tok : 0) * a.K + kq * kGroup;
 
+  struct Step {
+    u32x4 a[NRAW];
+    u32x4 b[4];
+    bool bv;
+  };
+  // every wave runs the same number of steps; steps past its range read zeros
+  auto load = [&](int S, Step &st) {
+    const bool in = S < w_hi;
+    const bool gok = in && ((S < nsup - 1) || (kq < last_ok));
+    const uint32_t va = gok ? aoff : kOOB;
+    const uint32_t sa = (in ? (uint32_t)S : 0u) * 4u * kGroup * ESZ;
+#pragma unroll
+    for (int i = 0; i < NRAW; ++i) st.a[i] = bload16(rA, va + 16u * i, sa);
+    st.bv = bok && gok;
+    const u32x4 *p = (const u32x4 *)(brow + (size_t)(gok ? S : 0) * 4 * kGroup);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st.b[i] = p[i];
+  };
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int S = w_lo; S < w_hi; ++S) {
-    const int g = S * 4 + kq;
-    const bool gok = g < a.ng;
-    u32x4 ar[NRAW], br[4];
-    if (rok && gok) {
-      const u32x4 *p = (const u32x4 *)(arow + (size_t)g * kGroup * ESZ);
-#pragma unroll
-      for (int i = 0; i < NRAW; ++i) ar[i] = p[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < NRAW; ++i) ar[i] = u32x4{0, 0, 0, 0};
-    }
-    if (bok && gok) {
-      const u32x4 *p = (const u32x4 *)(brow + (size_t)g * kGroup);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) br[i] = p[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) br[i] = u32x4{0, 0, 0, 0};
-    }
+  auto compute = [&](const Step &st) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
+      const u32x4 bq = st.bv ? st.b[s] : u32x4{0, 0, 0, 0};
       if constexpr (AF == kA_F32) {
         float v[8];
-        const u32x4 lo = ar[2 * s], hi = ar[2 * s + 1];
+        const u32x4 lo = st.a[2 * s], hi = st.a[2 * s + 1];
         v[0] = __uint_as_float(lo.x); v[1] = __uint_as_float(lo.y);
         v[2] = __uint_as_float(lo.z); v[3] = __uint_as_float(lo.w);
         v[4] = __uint_as_float(hi.x); v[5] = __uint_as_float(hi.y);
         v[6] = __uint_as_float(hi.z); v[7] = __uint_as_float(hi.w);
         u32x4 ap[3];
         split_x8<3>(v, ap);
-        acc = mfma16(ap[0], br[s], acc);
-        acc = mfma16(ap[1], br[s], acc);
-        acc = mfma16(ap[2], br[s], acc);
+        acc = mfma16(ap[0], bq, acc);
+        acc = mfma16(ap[1], bq, acc);
+        acc = mfma16(ap[2], bq, acc);
       } else {
-        acc = mfma16(ar[s], br[s], acc);
+        acc = mfma16(st.a[s], bq, acc);
       }
     }
+  };
+  const int nsteps = spw;  // uniform: the same count for every wave of the block
+  Step X, Y;
+  load(w_lo, X);
+  for (int i = 0; i < nsteps; i += 2) {
+    load(w_lo + i + 1, Y);
+    compute(X);
+    load(w_lo + i + 2, X);
+    compute(Y);
   }
 
   if constexpr (WAVES > 1) {
@@ -104,14 +119,27 @@ __global__ __launch_bounds__(WAVES * 64) void k_dense_dec(DenseArgs a) {
     acc = t;
   }
   if (piece != 0 || !bok) return;
-  const int m0 = blockIdx.x * 16 + 4 * kq;
+  float scale = 1.f;
+  if constexpr (EPI == kEpiStoreScaled) {
+    // RMSNorm folded in: y = W (gamma * acc) / sqrt(mean(acc^2) + eps)
+    float sv[kMaxNormParts];
+#pragma unroll
+    for (int i = 0; i < kMaxNormParts; ++i) sv[i] = i < a.nss ? a.ss[(size_t)tok * a.nss + i] : 0.f;
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < kMaxNormParts; ++i) ss += sv[i];
+    scale = 1.0f / sqrtf(ss / (float)a.K + a.eps);
+  }
+  const int m0 = rbk * 16 + 4 * kq;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int m = m0 + i;
     if (m >= a.M) break;
     const size_t o = (size_t)tok * a.M + m;
     if constexpr (EPI == kEpiStore) {
-      a.out[(size_t)blockIdx.y * a.N * a.M + o] = acc[i];
+      a.out[(size_t)ks * a.N * a.M + o] = acc[i];
+    } else if constexpr (EPI == kEpiStoreScaled) {
+      a.out[o] = acc[i] * scale;
     } else {
       if (a.out) a.out[o] = acc[i];
       uint32_t p[3] = {0, 0, 0};
@@ -123,11 +151,31 @@ __global__ __launch_bounds__(WAVES * 64) void k_dense_dec(DenseArgs a) {
   }
 }
 
-hipError_t launch_dense_router(const DenseArgs &a, int ks, hipStream_t s) {
-  // router: fp32 weights in three pieces, bf16 x (exact) in one
-  constexpr int PB = 1, TPT = 16;
-  dim3 grid((a.M + 15) / 16, ks, (a.N + TPT - 1) / TPT);
-  k_dense_dec<kA_F32, PB, kEpiStore, 4><<<grid, 256, 0, s>>>(a);
+template <int AF, int PB, int EPI, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void k_dense(DenseArgs a) {
+  dense_body<AF, PB, EPI, WAVES>(a, blockIdx.x, blockIdx.y, gridDim.y, blockIdx.z);
+}
+
+// Router (fp32 weights, three pieces; K split over kRouterSplits blocks) and the
+// latent down-projection (bf16 weights) in one launch: both read only x.
+constexpr int kRouteDownWaves = 8;
+
+__global__ __launch_bounds__(kRouteDownWaves * 64) void k_route_down(DenseArgs r, int r_rb, int r_ks,
+                                                                     DenseArgs d, int d_rb) {
+  const int b = blockIdx.x;
+  if (b < r_rb * r_ks) {
+    dense_body<kA_F32, 1, kEpiStore, kRouteDownWaves>(r, b % r_rb, b / r_rb, r_ks, blockIdx.z);
+  } else {
+    dense_body<kA_BF16, 1, kEpiStorePlanes, kRouteDownWaves>(d, b - r_rb * r_ks, 0, 1, blockIdx.z);
+  }
+}
+
+hipError_t launch_route_down(const DenseArgs &r, int ks, const DenseArgs *d, hipStream_t s) {
+  const int r_rb = (r.M + 15) / 16;
+  const int d_rb = d ? (d->M + 15) / 16 : 0;
+  DenseArgs dd = d ? *d : r;
+  dim3 grid(r_rb * ks + d_rb, 1, (r.N + 15) / 16);
+  k_route_down<<<grid, kRouteDownWaves * 64, 0, s>>>(r, r_rb, ks, dd, d_rb);
   return hipGetLastError();
 }
 
@@ -135,90 +183,106 @@ hipError_t launch_dense_bf16(const DenseArgs &a, int pieces, int epi, hipStream_
   const int tpt = 16 / pieces;
   dim3 grid((a.M + 15) / 16, 1, (a.N + tpt - 1) / tpt);
   if (pieces == 1 && epi == kEpiStorePlanes)
-    k_dense_dec<kA_BF16, 1, kEpiStorePlanes, 8><<<grid, 512, 0, s>>>(a);
-  else if (pieces == 3 && epi == kEpiStore)
-    k_dense_dec<kA_BF16, 3, kEpiStore, 4><<<grid, 256, 0, s>>>(a);
+    k_dense<kA_BF16, 1, kEpiStorePlanes, 8><<<grid, 512, 0, s>>>(a);
+  else if (pieces == 3 && epi == kEpiStoreScaled)
+    k_dense<kA_BF16, 3, kEpiStoreScaled, 4><<<grid, 256, 0, s>>>(a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 // ============================================================== router top-k
-// One wave per token. Each lane holds the experts e = lane + 64 i. K rounds of a wave
-// arg-max over the selection scores ch = sigmoid(logit) + bias (ties: lower id); the
-// weights are the unbiased sigmoid scores of the winners, renormalised, times
-// routed_scale; the K results are written in ascending expert id.
-__global__ __launch_bounds__(64) void k_topk(const float *__restrict__ part, int ks, int T, int E,
-                                             const float *__restrict__ bias, int K, int renorm,
-                                             float rscale, int32_t *__restrict__ idx_out,
-                                             float *__restrict__ w_out) {
-  const int t = blockIdx.x, lane = threadIdx.x;
-  float ch[16], sc[16];
-  uint32_t taken = 0;
+// One block per token. Its threads turn the partial logits into unbiased scores
+// sc = sigmoid(logit) and selection scores ch = sc + bias, kept in LDS as ch's
+// order-preserving 32-bit key. Wave 0 then finds the K-th largest key by a binary
+// search on the key bits (each probe counts keys >= the probe with ballots), takes every
+// expert above it plus, among those equal to it, the lowest ids (so equal selection
+// scores go to the lower id), and writes the chosen ids in ascending order with their
+// unbiased scores renormalised over the chosen and times routed_scale.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__global__ __launch_bounds__(1024) void k_topk(const float *__restrict__ part, int ks, int T, int E,
+                                               const float *__restrict__ bias, int K, int renorm,
+                                               float rscale, int32_t *__restrict__ idx_out,
+                                               float *__restrict__ w_out) {
+  __shared__ float s_sc[1024];
+  __shared__ uint32_t s_key[1024];
+  const int t = blockIdx.x, e = threadIdx.x;
+  if (e < E) {
+    // the partial sums were written by blocks on every XCD: issue all loads at once
+    float pv[kMaxRouterSplits];
+#pragma unroll
+    for (int k = 0; k < kMaxRouterSplits; ++k)
+      pv[k] = k < ks ? part[((size_t)k * T + t) * E + e] : 0.f;
+    float logit = 0.f;
+#pragma unroll
+    for (int k = 0; k < kMaxRouterSplits; ++k) logit += pv[k];
+    const float sgm = 1.0f / (1.0f + expf(-logit));
+    s_sc[e] = sgm;
+    s_key[e] = order_key(sgm + bias[e]);
+  } else {
+    s_sc[e] = 0.f;
+    s_key[e] = 0u;  // below every real key
+  }
+  __syncthreads();
+  if (e >= 64) return;
+  const int lane = e;
+  uint32_t key[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) key[i] = s_key[lane + 64 * i];
+  auto count_ge = [&](uint32_t v) {
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) c += __popcll(__ballot(key[i] >= v));
+    return c;
+  };
+  // largest v with count(key >= v) >= K: the K-th largest key
+  uint32_t tau = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = tau | (1u << bit);
+    if (count_ge(cand) >= K) tau = cand;
+  }
+  int n_gt = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) n_gt += __popcll(__ballot(key[i] > tau));
+  const int need_eq = K - n_gt;
+  // ascending expert id e = lane + 64 i: i-major, then lane
+  const unsigned long long below = (1ull << lane) - 1ull;
+  int eq_before = 0, sel_before = 0;
+  float ssum = 0.f;
+  bool sel[16];
+  int pos[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const int e = lane + 64 * i;
-    if (e < E) {
-      float logit = 0.f;
-      for (int k = 0; k < ks; ++k) logit += part[((size_t)k * T + t) * E + e];
-      const float s = 1.0f / (1.0f + expf(-logit));
-      sc[i] = s;
-      ch[i] = s + bias[e];
-    } else {
-      sc[i] = 0.f;
-      ch[i] = -INFINITY;
-      taken |= 1u << i;
-    }
+    const bool eq = key[i] == tau;
+    const unsigned long long eqm = __ballot(eq);
+    const int eq_rank = eq_before + __popcll(eqm & below);
+    sel[i] = key[i] > tau || (eq && eq_rank < need_eq);
+    eq_before += __popcll(eqm);
+    const unsigned long long sm = __ballot(sel[i]);
+    pos[i] = sel_before + __popcll(sm & below);
+    sel_before += __popcll(sm);
+    if (sel[i]) ssum += s_sc[lane + 64 * i];
   }
-  int my_e = 0;
-  float my_s = 0.f;
-  for (int j = 0; j < K; ++j) {
-    float bc = -INFINITY, bs = 0.f;
-    int be = 0x7FFFFFFF;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (!((taken >> i) & 1u) && ch[i] > bc) {
-        bc = ch[i];
-        bs = sc[i];
-        be = lane + 64 * i;
-      }
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float oc = __shfl_xor(bc, off, 64);
-      const float os = __shfl_xor(bs, off, 64);
-      const int oe = __shfl_xor(be, off, 64);
-      if (oc > bc || (oc == bc && oe < be)) {
-        bc = oc;
-        bs = os;
-        be = oe;
-      }
-    }
-    if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    if (lane == j) {
-      my_e = be;
-      my_s = bs;
-    }
-  }
-  float ssum = lane < K ? my_s : 0.f;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) ssum += __shfl_xor(ssum, off, 64);
-  float w = (renorm && ssum > 0.f) ? my_s / ssum : my_s;
-  w *= rscale;
-  int rank = 0;
-  for (int i = 0; i < K; ++i) {
-    const int ei = __shfl(my_e, i, 64);
-    rank += ei < my_e;
-  }
-  if (lane < K) {
-    idx_out[(size_t)t * K + rank] = my_e;
-    w_out[(size_t)t * K + rank] = w;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (sel[i]) {
+      const int ee = lane + 64 * i;
+      const float sc = s_sc[ee];
+      idx_out[(size_t)t * K + pos[i]] = ee;
+      w_out[(size_t)t * K + pos[i]] = ((renorm && ssum > 0.f) ? sc / ssum : sc) * rscale;
+    }
   }
 }
 
 hipError_t launch_topk(const float *part, int ks, int T, int E, const float *bias, int K,
                        int renorm, float rscale, int32_t *idx, float *w, hipStream_t s) {
-  k_topk<<<T, 64, 0, s>>>(part, ks, T, E, bias, K, renorm, rscale, idx, w);
+  k_topk<<<T, 1024, 0, s>>>(part, ks, T, E, bias, K, renorm, rscale, idx, w);
   return hipGetLastError();
 }
 
@@ -417,129 +481,228 @@ hipError_t launch_split_planes(const float *src, size_t n, uint16_t *p0, uint16_
   return hipGetLastError();
 }
 
+// Copy nbytes (a multiple of 16, 16-byte aligned) from global memory to LDS with the
+// whole block: each thread issues up to BATCH 16-byte loads before storing any, so
+// the loads overlap instead of paying one memory latency each.
+template <int BATCH>
+__device__ __forceinline__ void stage16(uint8_t *dst, const uint8_t *src, int nbytes) {
+  const int n16 = nbytes >> 4;
+  for (int base = threadIdx.x; base < n16; base += BATCH * blockDim.x) {
+    u32x4 v[BATCH];
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b) {
+      const int i = base + b * blockDim.x;
+      if (i < n16) v[b] = *(const u32x4 *)(src + (size_t)i * 16);
+    }
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b) {
+      const int i = base + b * blockDim.x;
+      if (i < n16) *(u32x4 *)(dst + (size_t)i * 16) = v[b];
+    }
+  }
+}
+
 // ============================================================== grouped MXFP4 (decode)
-// Grid: x = 64-row blocks (16 rows per wave), y = active-expert slots. Each block walks
-// its expert's sorted pairs in tiles of 16/PB tokens; each wave streams its 16 rows of
-// the NA matrices once per tile, one 512-column macro-step (64 contiguous bytes per
-// lane plus 4 scale bytes) prefetched ahead.
-template <int NA, int PB, int EPI>
-__global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
-  constexpr int TPT = 16 / PB;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// Grid: x = 64-row blocks, y = active-expert slots. The block's four waves share the
+// same 64 rows (four 16-row MFMA blocks). With one matrix (down) the waves split K four
+// ways; with two (gate w1 and up w3) waves 0-1 stream w1 and waves 2-3 stream w3, each
+// pair splitting K in halves. Partial sums meet in LDS, where wave w finishes row block
+// w (SiTU pairs the gate and up sums of the same row and token there).
+// Each block walks its expert's sorted pairs in tiles of TT tokens. A tile's activations
+// (TT tokens x 3 bf16 pieces x K) are staged in LDS once; the 16 MFMA columns hold the
+// TT x 3 (token, piece) pairs, summed across lanes in the epilogue. Weights and scales
+// stream from HBM through three register sets: two super-steps are in flight while the
+// third is multiplied.
+constexpr int kDecPieces = 3;
+#ifndef K3_GATEUP_DEPTH
+#define K3_GATEUP_DEPTH 3
+#endif
+#ifndef K3_DOWN_DEPTH
+#define K3_DOWN_DEPTH 2
+#endif
+#ifndef K3_GPL
+#define K3_GPL 1
+#endif
+
+template <int NA, int TT, int EPI, int DEPTH, int GPL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NA == 1 && DEPTH * GPL <= 3 ? 4 : 3)))
+void k_grouped_dec(GroupedArgs a) {
+  constexpr int RB = 4;
+  constexpr int KSPLIT = 4 / NA;
+  constexpr int PB = kDecPieces;
+  static_assert(TT * PB <= 16, "a tile's (token, piece) pairs fill at most 16 MFMA columns");
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rl = lane & 15, kq = lane >> 4;
   const int tn = rl / PB, piece = rl % PB;
   const int j = blockIdx.y;
   if (j >= *a.n_active) return;
-  const int e = a.active[j];
-  const int lo = a.expert_off[e], hi = a.expert_off[e + 1];
-  const int row0 = blockIdx.x * 64 + wave * 16;
-  if (row0 >= a.M) return;  // M is a multiple of 16: a wave's rows are all in or all out
-  const int row = row0 + rl;
-  const int rowb = a.K / 2;
-  const uint8_t *pk[NA], *sc[NA];
-#pragma unroll
-  for (int m = 0; m < NA; ++m) {
-    pk[m] = a.A[m].packed + (size_t)e * a.A[m].pstride + (size_t)row * rowb;
-    sc[m] = a.A[m].scales + (size_t)e * a.A[m].sstride + (size_t)row * a.ng;
-  }
-  const int nmacro = (a.ng + 15) >> 4;
+  // uniform across the block: scalar registers, so the buffer descriptors are scalar
+  const int e = __builtin_amdgcn_readfirstlane(a.active[j]);
+  const int lo = __builtin_amdgcn_readfirstlane(a.expert_off[e]);
+  const int hi = __builtin_amdgcn_readfirstlane(a.expert_off[e + 1]);
+  const int row0 = blockIdx.x * 64;
+  const uint32_t rowb = (uint32_t)a.K / 2, ng = (uint32_t)a.ng;
+  const int nrb = min(RB, (a.M - row0) >> 4);  // row blocks inside M (M % 16 == 0)
+  const int mw = wave / KSPLIT, kp = wave % KSPLIT;
+  // this wave's matrix, over the block's rows of expert e: rows past M and groups past
+  // K read as zero
+  const MxMat &mx = a.A[mw];
+  const rsrc_t rA = make_rsrc(mx.packed + (size_t)e * mx.pstride + (size_t)row0 * rowb,
+                              (uint32_t)nrb * 16u * rowb);
+  // A step covers 4*GPL groups of every row: lane group kq holds GPL consecutive groups,
+  // so a row's four lanes read 64*GPL contiguous bytes per step.
+  const uint32_t aoff0 = (uint32_t)rl * rowb + (uint32_t)kq * 16u * GPL;
+  const int nstep = (a.ng + 4 * GPL - 1) / (4 * GPL);
+  const int spw = (nstep + KSPLIT - 1) / KSPLIT;
+  const int s_lo = kp * spw, s_hi = min(nstep, s_lo + spw);
 
-  for (int n0 = lo; n0 < hi; n0 += TPT) {
-    const int slot = n0 + tn;
-    const bool bok = (rl < TPT * PB) && (slot < hi);
-    int brow = 0;
-    if (bok) brow = a.gather ? a.sorted_pair[slot] / a.topk : slot;
-    const uint16_t *bp = a.B[piece < PB ? piece : 0] + (size_t)brow * a.K;
-
-    f32x4 acc[NA];
-#pragma unroll
-    for (int m = 0; m < NA; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    u32x4 pa[NA][4];
-    uint32_t ps[NA][4];
-    auto load_macro = [&](int mi, u32x4 (&ra)[NA][4], uint32_t (&rs)[NA][4]) {
-#pragma unroll
-      for (int m = 0; m < NA; ++m)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int g = mi * 16 + kq * 4 + q;
-          if (g < a.ng) {
-            ra[m][q] = *(const u32x4 *)(pk[m] + (size_t)g * 16);
-            rs[m][q] = sc[m][g];
-          } else {
-            ra[m][q] = u32x4{0, 0, 0, 0};
-            rs[m][q] = 127;
-          }
-        }
-    };
-    load_macro(0, pa, ps);
-    for (int mi = 0; mi < nmacro; ++mi) {
-      u32x4 na[NA][4];
-      uint32_t ns[NA][4];
-      if (mi + 1 < nmacro) load_macro(mi + 1, na, ns);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int g = mi * 16 + kq * 4 + q;
-        u32x4 br[4];
-        if (bok && g < a.ng) {
-          const u32x4 *p = (const u32x4 *)(bp + (size_t)g * kGroup);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) br[i] = p[i];
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) br[i] = u32x4{0, 0, 0, 0};
-        }
-        float scf[NA];
-        u32x4 raw[NA];
-#pragma unroll
-        for (int m = 0; m < NA; ++m) {
-          raw[m] = pa[m][q];
-          if (ps[m][q] == 255u) raw[m] = u32x4{0, 0, 0, 0};  // NaN scale: the group is zero
-          scf[m] = e8m0_f32(ps[m][q] == 255u ? 127u : ps[m][q]);
-        }
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-#pragma unroll
-          for (int m = 0; m < NA; ++m) {
-            const u32x4 af = fp4x8_to_bf16(raw[m][s], scf[m]);
-            acc[m] = mfma16(af, br[s], acc[m]);
-          }
-        }
+  // LDS: the block's scale bytes [NA][64 rows][ng] (staged once), then the staged
+  // activations [TT * PB rows][brs] bf16, whose bytes after the K loop hold the waves'
+  // partial sums
+  const int sc_bytes = (NA * 64 * (int)ng + 15) & ~15;
+  uint8_t *sS = smem;
+  const int brs = a.K + 8;  // padded row: consecutive rows start on different banks
+  uint16_t *sB = (uint16_t *)(smem + sc_bytes);
+  f32x4(*red)[RB][64] = (f32x4(*)[RB][64])(smem + sc_bytes);
+  {
+    // scales depend on the rows only: one coalesced copy per block
+    const int nb = nrb * 16 * (int)ng;
+    for (int m = 0; m < NA; ++m) {
+      const uint8_t *src = a.A[m].scales + (size_t)e * a.A[m].sstride + (size_t)row0 * ng;
+      uint8_t *dst = sS + m * 64 * (int)ng;
+      if ((((uintptr_t)src) & 15) == 0 && (nb & 15) == 0) {
+        stage16<4>(dst, src, nb);
+      } else {
+        for (int i = threadIdx.x; i < nb; i += blockDim.x) dst[i] = src[i];
       }
-      if (mi + 1 < nmacro) {
+    }
+  }
+  const uint8_t *sSw = sS + mw * 64 * (int)ng + rl * (int)ng;  // this lane's row of its matrix
+
+  struct Step {
+    u32x4 a[RB][GPL];
+    uint32_t s[RB][GPL];
+  };
+  auto group_of = [&](int S, int u) { return (4 * S + kq) * GPL + u; };
+  // weights from HBM; their scale bytes from LDS (staged below before the first use)
+  auto load = [&](int S, Step &st) {
+    const bool in = S < s_hi;
+    const uint32_t Sc = in ? (uint32_t)S : 0u;
 #pragma unroll
-        for (int m = 0; m < NA; ++m)
+    for (int u = 0; u < GPL; ++u) {
+      const bool gok = in && group_of(S, u) < a.ng;
+      const uint32_t va = gok ? aoff0 : kOOB;
+#pragma unroll
+      for (int r = 0; r < RB; ++r)
+        st.a[r][u] = bload16(rA, va, Sc * 64u * GPL + (uint32_t)r * 16u * rowb + 16u * u);
+    }
+  };
+  auto load_scales = [&](int S, Step &st) {
+#pragma unroll
+    for (int u = 0; u < GPL; ++u) {
+      const int g = group_of(S, u);
+      const bool gok = (S < s_hi) && g < a.ng;
+#pragma unroll
+      for (int r = 0; r < RB; ++r) st.s[r][u] = gok ? (uint32_t)sSw[r * 16 * (int)ng + g] : 127u;
+    }
+  };
+
+  for (int n0 = lo; n0 < hi; n0 += TT) {
+    const int ntok = min(TT, hi - n0);
+    Step st[DEPTH];
+#pragma unroll
+    for (int d = 0; d + 1 < DEPTH; ++d) load(s_lo + d, st[d]);
+    // stage the tile's activations: row (tt, p) = piece p of token tt's vector
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      if (tt < ntok) {
+        const int slot = n0 + tt;
+        const int brow = __builtin_amdgcn_readfirstlane(a.gather ? a.sorted_pair[slot] / a.topk : slot);
+#pragma unroll
+        for (int p = 0; p < PB; ++p)
+          stage16<4>((uint8_t *)(sB + (size_t)(tt * PB + p) * brs),
+                     (const uint8_t *)(a.B[p] + (size_t)brow * a.K), a.K * 2);
+      }
+    }
+    __syncthreads();
+    const bool bok = (tn < ntok) && (rl < TT * PB);
+    const uint16_t *bl = sB + (size_t)(bok ? rl : 0) * brs;
+
+    f32x4 acc[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](int S, const Step &sx) {
+#pragma unroll
+      for (int u = 0; u < GPL; ++u) {
+        const int g = group_of(S, u);
+        const bool gok = (S < s_hi) && g < a.ng;
+        u32x4 bm[4];
+        const bool bv = bok && gok;
+        const u32x4 *bq = (const u32x4 *)(bl + (size_t)(gok ? g : 0) * kGroup);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const u32x4 t = bq[i];
+          bm[i] = bv ? t : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+          const uint32_t sb = sx.s[r][u];
+          const bool nan_scale = sb == 255u;  // the pages' rule: the group is zero
+          const float scf = e8m0_f32(nan_scale ? 127u : sb);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            pa[m][q] = na[m][q];
-            ps[m][q] = ns[m][q];
+            const uint32_t wv = nan_scale ? 0u : sx.a[r][u][q];
+            acc[r] = mfma16(fp4x8_to_bf16(wv, scf), bm[q], acc[r]);
           }
+        }
+      }
+    };
+    // DEPTH register sets rotate: DEPTH-1 steps are in flight while one is multiplied.
+    // Every wave runs the same number of steps; steps past its range read zeros.
+    load_scales(s_lo, st[0]);
+    for (int i = 0; i < spw; i += DEPTH) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) {
+        load(s_lo + i + d + DEPTH - 1, st[(d + DEPTH - 1) % DEPTH]);
+        load_scales(s_lo + i + d + 1, st[(d + 1) % DEPTH]);
+        compute(s_lo + i + d, st[d]);
       }
     }
 
-    if constexpr (PB > 1) {
+    __syncthreads();  // every wave is done reading the staged activations
 #pragma unroll
-      for (int m = 0; m < NA; ++m) {
-        f32x4 t = {0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < RB; ++r) red[wave][r][lane] = acc[r];
+    __syncthreads();
+    const int r = wave;
+    f32x4 v[NA];
 #pragma unroll
-        for (int p = 0; p < PB; ++p) {
-          const int src = (lane & 48) | min(tn * PB + p, 15);
+    for (int m = 0; m < NA; ++m) {
+      v[m] = red[m * KSPLIT][r][lane];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) t[i] += __shfl(acc[m][i], src, 64);
-        }
-        acc[m] = t;
-      }
+      for (int k = 1; k < KSPLIT; ++k) v[m] += red[m * KSPLIT + k][r][lane];
     }
-    if (piece == 0 && bok) {
-      const int m0 = row0 + 4 * kq;
-      const size_t o = (size_t)slot * a.M + m0;
+#pragma unroll
+    for (int m = 0; m < NA; ++m) {
+      f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int p = 0; p < PB; ++p) {
+        const int src = (lane & 48) | min(tn * PB + p, 15);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t[i] += __shfl(v[m][i], src, 64);
+      }
+      v[m] = t;
+    }
+    if (piece == 0 && bok && r < nrb) {
+      const int m0 = row0 + 16 * r + 4 * kq;
+      const size_t o = (size_t)(n0 + tn) * a.M + m0;
       if constexpr (EPI == kEpiSitu) {
         uint32_t pl[3][4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float v = situ(acc[0][i], acc[NA - 1][i], a.b1, a.b2);
+          const float val = situ(v[0][i], v[NA - 1][i], a.b1, a.b2);
           uint32_t p[3] = {0, 0, 0};
-          split_bf16<3>(v, p);
+          split_bf16<3>(val, p);
           pl[0][i] = p[0];
           pl[1][i] = p[1];
           pl[2][i] = p[2];
@@ -548,75 +711,95 @@ __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
         for (int q = 0; q < 3; ++q)
           *(u32x2 *)(a.planes[q] + o) = u32x2{pl[q][0] | (pl[q][1] << 16), pl[q][2] | (pl[q][3] << 16)};
       } else {
-        *(f32x4 *)(a.out + o) = acc[0];
+        *(f32x4 *)(a.out + o) = v[0];
       }
     }
+    __syncthreads();  // the next tile rewrites the staged activations
   }
 }
 
-hipError_t launch_grouped(const GroupedArgs &a, int epi, int pieces, int grid_y, hipStream_t s) {
-  if (grid_y <= 0) return hipSuccess;
-  dim3 grid((a.M + 63) / 64, grid_y);
-  if (epi == kEpiSitu && pieces == 3)
-    k_grouped_dec<2, 3, kEpiSitu><<<grid, 256, 0, s>>>(a);
-  else if (epi == kEpiEdn && pieces == 3)
-    k_grouped_dec<1, 3, kEpiEdn><<<grid, 256, 0, s>>>(a);
-  else
-    return hipErrorInvalidValue;
+size_t grouped_dec_lds(int K, int tt) {
+  // scale bytes of up to two matrices, then max(staged activations, partial sums)
+  const size_t scales = ((size_t)2 * 64 * (K / kGroup) + 15) & ~(size_t)15;
+  const size_t stage = (size_t)tt * kDecPieces * (K + 8) * 2;
+  const size_t red = (size_t)4 * 4 * 64 * 16;
+  return scales + (stage > red ? stage : red);
+}
+
+template <int NA, int EPI, int DEPTH, int GPL>
+static hipError_t launch_grouped_tt(const GroupedArgs &a, int tt, dim3 grid, hipStream_t s) {
+  const size_t lds = grouped_dec_lds(a.K, tt);
+  if (lds > kMaxBlockLds) return hipErrorInvalidValue;
+  switch (tt) {
+    case 1: k_grouped_dec<NA, 1, EPI, DEPTH, GPL><<<grid, 256, lds, s>>>(a); break;
+    case 2: k_grouped_dec<NA, 2, EPI, DEPTH, GPL><<<grid, 256, lds, s>>>(a); break;
+    default: k_grouped_dec<NA, 5, EPI, DEPTH, GPL><<<grid, 256, lds, s>>>(a); break;
+  }
   return hipGetLastError();
 }
 
-// ============================================================== combine + RMSNorm
-// One block per token: acc = sum_j w_j edn[slot_j] in slot order j = 0..K-1, then
-// n = acc / sqrt(mean(acc^2) + eps) * gamma, written as three bf16 pieces for W_up.
+hipError_t launch_grouped(const GroupedArgs &a, int epi, int tokens_per_tile, int grid_y, hipStream_t s) {
+  if (grid_y <= 0) return hipSuccess;
+  dim3 grid((a.M + 63) / 64, grid_y);
+  if (epi == kEpiSitu)
+    return launch_grouped_tt<2, kEpiSitu, K3_GATEUP_DEPTH, K3_GPL>(a, tokens_per_tile, grid, s);
+  return launch_grouped_tt<1, kEpiEdn, K3_DOWN_DEPTH, K3_GPL>(a, tokens_per_tile, grid, s);
+}
+
+// ============================================================== combine
+// Grid (column blocks of 256, tokens). acc = sum_j w_j edn[slot_j] in slot order
+// j = 0..K-1 (all K loads issued before the sums); the block writes gamma * acc as
+// three bf16 pieces for the up-projection and its share of sum(acc^2), from which the
+// up-projection's epilogue forms the RMSNorm factor 1/sqrt(mean(acc^2) + eps).
 __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ edn,
                                                  const int32_t *__restrict__ pair_slot,
                                                  const float *__restrict__ topk_w,
                                                  const float *__restrict__ gamma, int K, int L,
-                                                 float eps, uint16_t *p0, uint16_t *p1, uint16_t *p2) {
-  extern __shared__ float accs[];
+                                                 uint16_t *p0, uint16_t *p1, uint16_t *p2,
+                                                 float *__restrict__ ss_part) {
   __shared__ int slot[32];
   __shared__ float wt[32];
   __shared__ float red[4];
-  const int t = blockIdx.x;
-  if (threadIdx.x < K) {
-    slot[threadIdx.x] = pair_slot[(size_t)t * K + threadIdx.x];
-    wt[threadIdx.x] = topk_w[(size_t)t * K + threadIdx.x];
+  const int t = blockIdx.y;
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (threadIdx.x < 32) {
+    const bool ok = threadIdx.x < K;
+    slot[threadIdx.x] = ok ? pair_slot[(size_t)t * K + threadIdx.x] : -1;
+    wt[threadIdx.x] = ok ? topk_w[(size_t)t * K + threadIdx.x] : 0.f;
   }
   __syncthreads();
-  float ss = 0.f;
-  for (int c = threadIdx.x; c < L; c += blockDim.x) {
-    float v = 0.f;
-    for (int j = 0; j < K; ++j) {
-      const int s = slot[j];
-      if (s >= 0) v = fmaf(wt[j], edn[(size_t)s * L + c], v);
-    }
-    accs[c] = v;
-    ss = fmaf(v, v, ss);
-  }
+  float v = 0.f;
+  if (c < L) {
+    float ev[32];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
-  const float inv = 1.0f / sqrtf(tot / (float)L + eps);
-  for (int c = threadIdx.x; c < L; c += blockDim.x) {
-    const float n = accs[c] * inv * gamma[c];
+    for (int j = 0; j < 32; ++j) {
+      const int sj = slot[j];
+      ev[j] = (j < K && sj >= 0) ? edn[(size_t)sj * L + c] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 32; ++j)
+      if (j < K) v = fmaf(wt[j], ev[j], v);
     uint32_t p[3] = {0, 0, 0};
-    split_bf16<3>(n, p);
+    split_bf16<3>(v * gamma[c], p);
     const size_t o = (size_t)t * L + c;
     p0[o] = (uint16_t)p[0];
     p1[o] = (uint16_t)p[1];
     p2[o] = (uint16_t)p[2];
   }
+  float ss = v * v;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  if (threadIdx.x == 0) ss_part[(size_t)t * gridDim.x + blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
 }
 
 hipError_t launch_combine(const float *edn, const int32_t *pair_slot, const float *topk_w,
-                          const float *gamma, int T, int K, int L, float eps, uint16_t *p0,
-                          uint16_t *p1, uint16_t *p2, hipStream_t s) {
+                          const float *gamma, int T, int K, int L, uint16_t *p0, uint16_t *p1,
+                          uint16_t *p2, float *ss_part, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  k_combine<<<T, 256, (size_t)L * sizeof(float), s>>>(edn, pair_slot, topk_w, gamma, K, L, eps, p0,
-                                                      p1, p2);
+  dim3 grid((L + 255) / 256, T);
+  k_combine<<<grid, 256, 0, s>>>(edn, pair_slot, topk_w, gamma, K, L, p0, p1, p2, ss_part);
   return hipGetLastError();
 }
 
