@@ -52,7 +52,8 @@ int check_mx(const k3moe_mxfp4 &m) {
 
 struct Ws {
   float *router_part;          // [splits][T][E]
-  uint16_t *zp[3];             // [T][L] pieces of z
+  float *z32;                  // [T][L] latent (layer path)
+  uint8_t *zq;                 // [T][L/32] fp6 piece records of the latent
   int32_t *idx;                // [T][K]
   float *w;                    // [T][K]
   int32_t *expert_off;         // [E+1]
@@ -62,7 +63,7 @@ struct Ws {
   int32_t *counters;           // [0] active experts, [1] dropped pairs
   int32_t *lrank;              // [P]
   int32_t *cnt;                // [chunks][E]
-  uint16_t *actp[3];           // [P][I]
+  uint8_t *actq;               // [P][I/32] fp6 piece records of the SiTU outputs
   float *edn;                  // [P][L]
   uint16_t *np[3];             // [T][L] pieces of gamma * acc
   float *ss;                   // [T][ceil(L/256)] partial sums of acc^2
@@ -82,7 +83,8 @@ Ws carve(const k3moe_dims *d, int32_t T, void *base) {
   const size_t P = t * (size_t)d->topk;
   const size_t nch = (t + 63) / 64;
   w.router_part = (float *)take(kRouterSplits * t * E * 4);
-  for (int q = 0; q < 3; ++q) w.zp[q] = (uint16_t *)take(t * L * 2);
+  w.z32 = (float *)take(t * L * 4);
+  w.zq = (uint8_t *)take(t * L * 4);
   w.idx = (int32_t *)take(P * 4);
   w.w = (float *)take(P * 4);
   w.expert_off = (int32_t *)take((E + 1) * 4);
@@ -92,7 +94,7 @@ Ws carve(const k3moe_dims *d, int32_t T, void *base) {
   w.counters = (int32_t *)take(64);
   w.lrank = (int32_t *)take(P * 4);
   w.cnt = (int32_t *)take(nch * E * 4);
-  for (int q = 0; q < 3; ++q) w.actp[q] = (uint16_t *)take(P * I * 2);
+  w.actq = (uint8_t *)take(P * I * 4);
   w.edn = (float *)take(P * L * 4);
   for (int q = 0; q < 3; ++q) w.np[q] = (uint16_t *)take(t * L * 2);
   w.ss = (float *)take(t * ((L + 255) / 256) * 4);
@@ -148,8 +150,7 @@ DenseArgs router_args(const k3moe_dims *d, int32_t T, const uint16_t *x, const f
   return a;
 }
 
-DenseArgs down_args(const k3moe_dims *d, int32_t T, const uint16_t *x, const uint16_t *wd, float *z,
-                    uint16_t *const zp[3]) {
+DenseArgs down_args(const k3moe_dims *d, int32_t T, const uint16_t *x, const uint16_t *wd, float *z) {
   DenseArgs a = {};
   a.A = wd;
   a.M = d->latent;
@@ -158,7 +159,6 @@ DenseArgs down_args(const k3moe_dims *d, int32_t T, const uint16_t *x, const uin
   a.B[0] = a.B[1] = a.B[2] = x;
   a.N = T;
   a.out = z;
-  for (int q = 0; q < 3; ++q) a.planes[q] = zp[q];
   return a;
 }
 
@@ -166,45 +166,47 @@ DenseArgs down_args(const k3moe_dims *d, int32_t T, const uint16_t *x, const uin
 // then the top-k
 int run_route(const k3moe_dims *d, int32_t T, const uint16_t *x, const float *wr, const float *bias,
               int32_t *idx, float *wt, const DenseArgs *down, const Ws &w, hipStream_t s) {
+  // with the latent projection in the same launch, the top-k blocks also quantize z
   const DenseArgs a = router_args(d, T, x, wr, w);
   K3_HIP(launch_route_down(a, kRouterSplits, down, s));
   K3_HIP(mark(down ? "router_and_latent_down" : "router_gemv", s));
   K3_HIP(launch_topk(w.router_part, kRouterSplits, T, d->n_experts, bias, d->topk, d->renorm,
-                     d->routed_scale, idx, wt, s));
+                     d->routed_scale, idx, wt, down ? w.z32 : nullptr, d->latent, w.zq, s));
   K3_HIP(mark("topk", s));
   return K3MOE_OK;
 }
 
 int run_down(const k3moe_dims *d, int32_t T, const uint16_t *x, const uint16_t *wd, float *z,
-             uint16_t *const zp[3], hipStream_t s) {
-  const DenseArgs a = down_args(d, T, x, wd, z, zp);
-  K3_HIP(launch_dense_bf16(a, 1, kEpiStorePlanes, s));
+             hipStream_t s) {
+  const DenseArgs a = down_args(d, T, x, wd, z);
+  K3_HIP(launch_dense_bf16(a, 1, kEpiStore, s));
   K3_HIP(mark("latent_down_gemv", s));
   return K3MOE_OK;
 }
 
-int run_experts(const k3moe_dims *d, int32_t T, uint16_t *const zp[3], const k3moe_experts *ex,
+int run_experts(const k3moe_dims *d, int32_t T, const uint8_t *zq, const k3moe_experts *ex,
                 const int32_t *expert_off, const int32_t *sorted_pair, const int32_t *active,
                 const int32_t *counters, float *edn, const Ws &w, hipStream_t s) {
   const int grid_y = (int)((int64_t)T * d->topk < d->n_experts ? (int64_t)T * d->topk : d->n_experts);
   // tokens staged per tile (an expert holds at most T tokens), as many as fit in LDS
   const int kmax = d->latent > d->inter ? d->latent : d->inter;
-  int tt = T <= 1 ? 1 : 2;
-  if (grouped_dec_lds(kmax, tt) > kMaxBlockLds) tt = 1;
+  int tt = T <= 1 ? 1 : (T <= 2 ? 2 : 4);
+  while (tt > 1 && grouped_dec_lds(kmax, tt) > kMaxBlockLds) tt >>= 1;
+
   GroupedArgs g = {};
   g.A[0] = MxMat{ex->w1.packed, ex->w1.scales, ex->w1.packed_expert_stride, ex->w1.scales_expert_stride};
   g.A[1] = MxMat{ex->w3.packed, ex->w3.scales, ex->w3.packed_expert_stride, ex->w3.scales_expert_stride};
   g.M = d->inter;
   g.K = d->latent;
   g.ng = d->latent / 32;
-  for (int q = 0; q < 3; ++q) g.B[q] = zp[q];
+  g.Bq = zq;
   g.gather = 1;
   g.topk = d->topk;
   g.expert_off = expert_off;
   g.sorted_pair = sorted_pair;
   g.active = active;
   g.n_active = counters;
-  for (int q = 0; q < 3; ++q) g.planes[q] = w.actp[q];
+  g.outq = w.actq;
   g.b1 = d->b1;
   g.b2 = d->b2;
   K3_HIP(launch_grouped(g, kEpiSitu, tt, grid_y, s));
@@ -216,7 +218,7 @@ int run_experts(const k3moe_dims *d, int32_t T, uint16_t *const zp[3], const k3m
   h.M = d->latent;
   h.K = d->inter;
   h.ng = d->inter / 32;
-  for (int q = 0; q < 3; ++q) h.B[q] = w.actp[q];
+  h.Bq = w.actq;
   h.gather = 0;
   h.out = edn;
   K3_HIP(launch_grouped(h, kEpiEdn, tt, grid_y, s));
@@ -280,7 +282,7 @@ int k3moe_latent_proj_bf16(const k3moe_dims *d, int32_t T, const uint16_t *x, co
   Ws w;
   K3_TRY(check_ws(d, T, ws, ws_bytes, &w));
   if (T == 0) return K3MOE_OK;
-  return run_down(d, T, x, w_down, z, w.zp, (hipStream_t)stream);
+  return run_down(d, T, x, w_down, z, (hipStream_t)stream);
 }
 
 int k3moe_dispatch(const k3moe_dims *d, int32_t T, const int32_t *topk_idx, int32_t *expert_off,
@@ -311,8 +313,8 @@ int k3moe_expert_glu_mxfp4(const k3moe_dims *d, int32_t T, const float *z, const
   if (T == 0) return K3MOE_OK;
   hipStream_t s = (hipStream_t)stream;
   K3_HIP(launch_active_from_off(expert_off, d->n_experts, w.active, w.counters, s));
-  K3_HIP(launch_split_planes(z, (size_t)T * d->latent, w.zp[0], w.zp[1], w.zp[2], s));
-  return run_experts(d, T, w.zp, ex, expert_off, sorted_pair, w.active, w.counters, edn, w, s);
+  K3_HIP(launch_quant_rows(z, (size_t)T * d->latent, w.zq, s));
+  return run_experts(d, T, w.zq, ex, expert_off, sorted_pair, w.active, w.counters, edn, w, s);
 }
 
 int k3moe_combine(const k3moe_dims *d, int32_t T, const float *edn, const int32_t *pair_slot,
@@ -345,12 +347,12 @@ int k3moe_layer(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_w
   hipStream_t s = (hipStream_t)stream;
   int32_t *idx = topk_idx_out ? topk_idx_out : w.idx;
   float *tw = topk_w_out ? topk_w_out : w.w;
-  const DenseArgs down = down_args(d, T, x, wt->w_down, nullptr, w.zp);
+  const DenseArgs down = down_args(d, T, x, wt->w_down, w.z32);
   K3_TRY(run_route(d, T, x, wt->w_router, wt->bias, idx, tw, &down, w, s));
   K3_HIP(launch_dispatch(idx, T, d->topk, d->n_experts, w.expert_off, w.sorted_pair, w.pair_slot,
                          w.active, w.counters, w.lrank, w.cnt, s));
   K3_HIP(mark("dispatch", s));
-  K3_TRY(run_experts(d, T, w.zp, &wt->ex, w.expert_off, w.sorted_pair, w.active, w.counters, w.edn,
+  K3_TRY(run_experts(d, T, w.zq, &wt->ex, w.expert_off, w.sorted_pair, w.active, w.counters, w.edn,
                      w, s));
   return run_combine(d, T, w.edn, w.pair_slot, tw, wt->norm_w, wt->w_up, y, w, s);
 }

@@ -40,19 +40,22 @@ enum GroupedEpi { kEpiSitu = 0, kEpiEdn = 1 };
 struct GroupedArgs {
   MxMat A[2];             // gate/up: {w1, w3}; down: {w2}
   int M, K, ng;           // rows, cols, groups per row
-  const uint16_t *B[3];   // activation pieces, row = token (gather) or sorted slot
+  const uint8_t *Bq;      // activation fp6 piece records, row = token (gather) or sorted slot
   int gather, topk;
   const int32_t *expert_off, *sorted_pair, *active, *n_active;
   float *out;             // kEpiEdn: [slot][M] fp32
-  uint16_t *planes[3];    // kEpiSitu: [slot][M] bf16 pieces of act
+  uint8_t *outq;          // kEpiSitu: [slot][M/32] fp6 piece records of act
   float b1, b2;
 };
 
 // ---------------------------------------------------------------- launchers
 hipError_t launch_route_down(const DenseArgs &router, int ks, const DenseArgs *down, hipStream_t s);
 hipError_t launch_dense_bf16(const DenseArgs &a, int pieces, int epi, hipStream_t s);
+// z (nullable) [T][L] fp32: block t also writes row t's fp6 piece records to zq
 hipError_t launch_topk(const float *part, int ks, int T, int E, const float *bias, int K,
-                       int renorm, float rscale, int32_t *idx, float *w, hipStream_t s);
+                       int renorm, float rscale, int32_t *idx, float *w, const float *z, int L,
+                       uint8_t *zq, hipStream_t s);
+hipError_t launch_quant_rows(const float *src, size_t n, uint8_t *dst, hipStream_t s);
 hipError_t launch_dispatch(const int32_t *topk_idx, int T, int K, int E, int32_t *expert_off,
                            int32_t *sorted_pair, int32_t *pair_slot, int32_t *active,
                            int32_t *counters, int32_t *lrank, int32_t *cnt, hipStream_t s);
@@ -60,7 +63,7 @@ hipError_t launch_active_from_off(const int32_t *expert_off, int E, int32_t *act
                                   int32_t *counters, hipStream_t s);
 hipError_t launch_split_planes(const float *src, size_t n, uint16_t *p0, uint16_t *p1,
                                uint16_t *p2, hipStream_t s);
-// tokens_per_tile: 1, 2 or 5 activation rows staged in LDS per tile (grouped_dec_lds bytes)
+// tokens_per_tile: 1, 2 or 4 tokens' piece records staged in LDS per tile (grouped_dec_lds bytes)
 constexpr size_t kMaxBlockLds = 65536;
 size_t grouped_dec_lds(int K, int tokens_per_tile);
 hipError_t launch_grouped(const GroupedArgs &a, int epi, int tokens_per_tile, int grid_y, hipStream_t s);

@@ -166,7 +166,7 @@ __global__ __launch_bounds__(kRouteDownWaves * 64) void k_route_down(DenseArgs r
   if (b < r_rb * r_ks) {
     dense_body<kA_F32, 1, kEpiStore, kRouteDownWaves>(r, b % r_rb, b / r_rb, r_ks, blockIdx.z);
   } else {
-    dense_body<kA_BF16, 1, kEpiStorePlanes, kRouteDownWaves>(d, b - r_rb * r_ks, 0, 1, blockIdx.z);
+    dense_body<kA_BF16, 1, kEpiStore, kRouteDownWaves>(d, b - r_rb * r_ks, 0, 1, blockIdx.z);
   }
 }
 
@@ -182,8 +182,8 @@ hipError_t launch_route_down(const DenseArgs &r, int ks, const DenseArgs *d, hip
 hipError_t launch_dense_bf16(const DenseArgs &a, int pieces, int epi, hipStream_t s) {
   const int tpt = 16 / pieces;
   dim3 grid((a.M + 15) / 16, 1, (a.N + tpt - 1) / tpt);
-  if (pieces == 1 && epi == kEpiStorePlanes)
-    k_dense<kA_BF16, 1, kEpiStorePlanes, 8><<<grid, 512, 0, s>>>(a);
+  if (pieces == 1 && epi == kEpiStore)
+    k_dense<kA_BF16, 1, kEpiStore, 8><<<grid, 512, 0, s>>>(a);
   else if (pieces == 3 && epi == kEpiStoreScaled)
     k_dense<kA_BF16, 3, kEpiStoreScaled, 4><<<grid, 256, 0, s>>>(a);
   else
@@ -207,7 +207,8 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 __global__ __launch_bounds__(1024) void k_topk(const float *__restrict__ part, int ks, int T, int E,
                                                const float *__restrict__ bias, int K, int renorm,
                                                float rscale, int32_t *__restrict__ idx_out,
-                                               float *__restrict__ w_out) {
+                                               float *__restrict__ w_out, const float *__restrict__ z,
+                                               int L, uint8_t *__restrict__ zq) {
   __shared__ float s_sc[1024];
   __shared__ uint32_t s_key[1024];
   const int t = blockIdx.x, e = threadIdx.x;
@@ -228,7 +229,19 @@ __global__ __launch_bounds__(1024) void k_topk(const float *__restrict__ part, i
     s_key[e] = 0u;  // below every real key
   }
   __syncthreads();
-  if (e >= 64) return;
+  if (e >= 64) {
+    // the other waves meanwhile quantize this token's latent row into fp6 pieces
+    if (z) {
+      const float *zr = z + (size_t)t * L;
+      uint8_t *dst = zq + (size_t)t * (L / 32) * kGroupRec;
+      for (int q = e - 64; q < L / 8; q += blockDim.x - 64) {
+        const float4 lo = *(const float4 *)(zr + 8 * q), hi = *(const float4 *)(zr + 8 * q + 4);
+        float rv[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        quant_group_fp6(rv, q & 3, dst + (q >> 2) * kGroupRec);
+      }
+    }
+    return;
+  }
   const int lane = e;
   uint32_t key[16];
 #pragma unroll
@@ -281,8 +294,9 @@ __global__ __launch_bounds__(1024) void k_topk(const float *__restrict__ part, i
 }
 
 hipError_t launch_topk(const float *part, int ks, int T, int E, const float *bias, int K,
-                       int renorm, float rscale, int32_t *idx, float *w, hipStream_t s) {
-  k_topk<<<T, 1024, 0, s>>>(part, ks, T, E, bias, K, renorm, rscale, idx, w);
+                       int renorm, float rscale, int32_t *idx, float *w, const float *z, int L,
+                       uint8_t *zq, hipStream_t s) {
+  k_topk<<<T, 1024, 0, s>>>(part, ks, T, E, bias, K, renorm, rscale, idx, w, z, L, zq);
   return hipGetLastError();
 }
 
@@ -503,33 +517,28 @@ __device__ __forceinline__ void stage16(uint8_t *dst, const uint8_t *src, int nb
 }
 
 // ============================================================== grouped MXFP4 (decode)
-// Grid: x = 64-row blocks, y = active-expert slots. The block's four waves share the
-// same 64 rows (four 16-row MFMA blocks). With one matrix (down) the waves split K four
-// ways; with two (gate w1 and up w3) waves 0-1 stream w1 and waves 2-3 stream w3, each
-// pair splitting K in halves. Partial sums meet in LDS, where wave w finishes row block
-// w (SiTU pairs the gate and up sums of the same row and token there).
-// Each block walks its expert's sorted pairs in tiles of TT tokens. A tile's activations
-// (TT tokens x 3 bf16 pieces x K) are staged in LDS once; the 16 MFMA columns hold the
-// TT x 3 (token, piece) pairs, summed across lanes in the epilogue. Weights and scales
-// stream from HBM through three register sets: two super-steps are in flight while the
-// third is multiplied.
-constexpr int kDecPieces = 3;
 #ifndef K3_GATEUP_DEPTH
 #define K3_GATEUP_DEPTH 3
 #endif
 #ifndef K3_DOWN_DEPTH
-#define K3_DOWN_DEPTH 2
+#define K3_DOWN_DEPTH 3
 #endif
-#ifndef K3_GPL
-#define K3_GPL 1
-#endif
-
-template <int NA, int TT, int EPI, int DEPTH, int GPL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NA == 1 && DEPTH * GPL <= 3 ? 4 : 3)))
-void k_grouped_dec(GroupedArgs a) {
+// Grid: x = 64-row blocks, y = active-expert slots. The block's four waves share the
+// same 64 rows (four 16-row blocks). With one matrix (down) the waves split K four
+// ways; with two (gate w1 and up w3) waves 0-1 stream w1 and waves 2-3 stream w3, each
+// pair splitting K in halves. Partial sums meet in LDS, where wave w finishes row block
+// w (SiTU pairs the gate and up sums of the same row and token there).
+// The weights enter the matrix cores as stored: each lane's 16 packed bytes of one
+// 32-column group are the MXFP4 operand and the group's scale byte is its scale. The
+// activations enter as fp6 pieces: the 16 columns of a step are TT tokens x 4 pieces,
+// summed across lanes in the epilogue. A tile's piece records are staged in LDS once;
+// the block's scale bytes are staged once per block; weights stream from HBM through
+// DEPTH register sets (DEPTH-1 steps in flight while one is multiplied).
+template <int NA, int TT, int EPI, int DEPTH>
+__global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
   constexpr int RB = 4;
   constexpr int KSPLIT = 4 / NA;
-  constexpr int PB = kDecPieces;
+  constexpr int PB = kFp6Pieces;
   static_assert(TT * PB <= 16, "a tile's (token, piece) pairs fill at most 16 MFMA columns");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -543,30 +552,29 @@ void k_grouped_dec(GroupedArgs a) {
   const int hi = __builtin_amdgcn_readfirstlane(a.expert_off[e + 1]);
   const int row0 = blockIdx.x * 64;
   const uint32_t rowb = (uint32_t)a.K / 2, ng = (uint32_t)a.ng;
-  const int nrb = min(RB, (a.M - row0) >> 4);  // row blocks inside M (M % 16 == 0)
+  const int nrb = min(RB, (a.M - row0) >> 4);  // row blocks inside M (M % 32 == 0)
   const int mw = wave / KSPLIT, kp = wave % KSPLIT;
-  // this wave's matrix, over the block's rows of expert e: rows past M and groups past
-  // K read as zero
   const MxMat &mx = a.A[mw];
+  // this wave's matrix over the block's rows of expert e: rows past M and groups past K
+  // read as zero
   const rsrc_t rA = make_rsrc(mx.packed + (size_t)e * mx.pstride + (size_t)row0 * rowb,
                               (uint32_t)nrb * 16u * rowb);
-  // A step covers 4*GPL groups of every row: lane group kq holds GPL consecutive groups,
-  // so a row's four lanes read 64*GPL contiguous bytes per step.
-  const uint32_t aoff0 = (uint32_t)rl * rowb + (uint32_t)kq * 16u * GPL;
-  const int nstep = (a.ng + 4 * GPL - 1) / (4 * GPL);
-  const int spw = (nstep + KSPLIT - 1) / KSPLIT;
-  const int s_lo = kp * spw, s_hi = min(nstep, s_lo + spw);
+  const uint32_t aoff0 = (uint32_t)rl * rowb + (uint32_t)kq * 16u;
+  const int nsup = (a.ng + 3) >> 2;  // steps of 4 groups (128 columns)
+  const int spw = (nsup + KSPLIT - 1) / KSPLIT;
+  const int s_lo = kp * spw, s_hi = min(nsup, s_lo + spw);
+  const int last_ok = a.ng - 4 * (nsup - 1);  // groups in the last step
 
-  // LDS: the block's scale bytes [NA][64 rows][ng] (staged once), then the staged
-  // activations [TT * PB rows][brs] bf16, whose bytes after the K loop hold the waves'
-  // partial sums
+  // LDS: scale bytes [NA][64 rows][ng] | staged piece records [TT][ng * 128] (whose bytes
+  // after the K loop hold the waves' partial sums, then the SiTU outputs)
   const int sc_bytes = (NA * 64 * (int)ng + 15) & ~15;
   uint8_t *sS = smem;
-  const int brs = a.K + 8;  // padded row: consecutive rows start on different banks
-  uint16_t *sB = (uint16_t *)(smem + sc_bytes);
-  f32x4(*red)[RB][64] = (f32x4(*)[RB][64])(smem + sc_bytes);
+  uint8_t *sB = smem + sc_bytes;
+  const int brow_bytes = (int)ng * kGroupRec;
+  f32x4(*red)[RB][64] = (f32x4(*)[RB][64])sB;
+  float *sAct = (float *)(sB + 4 * RB * 64 * 16);  // [TT][64] SiTU outputs of the tile
   {
-    // scales depend on the rows only: one coalesced copy per block
+    // the scales depend on the rows only: one coalesced copy per block
     const int nb = nrb * 16 * (int)ng;
     for (int m = 0; m < NA; ++m) {
       const uint8_t *src = a.A[m].scales + (size_t)e * a.A[m].sstride + (size_t)row0 * ng;
@@ -581,31 +589,21 @@ void k_grouped_dec(GroupedArgs a) {
   const uint8_t *sSw = sS + mw * 64 * (int)ng + rl * (int)ng;  // this lane's row of its matrix
 
   struct Step {
-    u32x4 a[RB][GPL];
-    uint32_t s[RB][GPL];
+    u32x4 a[RB];
+    uint32_t s[RB];
   };
-  auto group_of = [&](int S, int u) { return (4 * S + kq) * GPL + u; };
-  // weights from HBM; their scale bytes from LDS (staged below before the first use)
   auto load = [&](int S, Step &st) {
-    const bool in = S < s_hi;
-    const uint32_t Sc = in ? (uint32_t)S : 0u;
+    const bool gok = (S < s_hi) && ((S < nsup - 1) || (kq < last_ok));
+    const uint32_t va = gok ? aoff0 : kOOB;
+    const uint32_t Sc = (S < s_hi) ? (uint32_t)S : 0u;
 #pragma unroll
-    for (int u = 0; u < GPL; ++u) {
-      const bool gok = in && group_of(S, u) < a.ng;
-      const uint32_t va = gok ? aoff0 : kOOB;
-#pragma unroll
-      for (int r = 0; r < RB; ++r)
-        st.a[r][u] = bload16(rA, va, Sc * 64u * GPL + (uint32_t)r * 16u * rowb + 16u * u);
-    }
+    for (int r = 0; r < RB; ++r) st.a[r] = bload16(rA, va, Sc * 64u + (uint32_t)r * 16u * rowb);
   };
   auto load_scales = [&](int S, Step &st) {
+    const int g = 4 * S + kq;
+    const bool gok = (S < s_hi) && g < a.ng;
 #pragma unroll
-    for (int u = 0; u < GPL; ++u) {
-      const int g = group_of(S, u);
-      const bool gok = (S < s_hi) && g < a.ng;
-#pragma unroll
-      for (int r = 0; r < RB; ++r) st.s[r][u] = gok ? (uint32_t)sSw[r * 16 * (int)ng + g] : 127u;
-    }
+    for (int r = 0; r < RB; ++r) st.s[r] = gok ? (uint32_t)sSw[r * 16 * (int)ng + g] : 127u;
   };
 
   for (int n0 = lo; n0 < hi; n0 += TT) {
@@ -613,53 +611,39 @@ void k_grouped_dec(GroupedArgs a) {
     Step st[DEPTH];
 #pragma unroll
     for (int d = 0; d + 1 < DEPTH; ++d) load(s_lo + d, st[d]);
-    // stage the tile's activations: row (tt, p) = piece p of token tt's vector
+    // stage the tile's activation piece records (one row of ng * 128 bytes per token)
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
       if (tt < ntok) {
         const int slot = n0 + tt;
         const int brow = __builtin_amdgcn_readfirstlane(a.gather ? a.sorted_pair[slot] / a.topk : slot);
-#pragma unroll
-        for (int p = 0; p < PB; ++p)
-          stage16<4>((uint8_t *)(sB + (size_t)(tt * PB + p) * brs),
-                     (const uint8_t *)(a.B[p] + (size_t)brow * a.K), a.K * 2);
+        stage16<4>(sB + tt * brow_bytes, a.Bq + (size_t)brow * brow_bytes, brow_bytes);
       }
     }
     __syncthreads();
     const bool bok = (tn < ntok) && (rl < TT * PB);
-    const uint16_t *bl = sB + (size_t)(bok ? rl : 0) * brs;
+    const uint8_t *bl = sB + (bok ? tn : 0) * brow_bytes + piece * kPieceRec;
 
     f32x4 acc[RB];
 #pragma unroll
     for (int r = 0; r < RB; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
     auto compute = [&](int S, const Step &sx) {
+      const int g = 4 * S + kq;
+      const bool gok = (S < s_hi) && g < a.ng;
+      const bool bv = bok && gok;
+      const u32x4 *bq = (const u32x4 *)(bl + (size_t)(gok ? g : 0) * kGroupRec);
+      const u32x4 b0 = bq[0], b1 = bq[1];
+      const uint32_t b[6] = {bv ? b0.x : 0u, bv ? b0.y : 0u, bv ? b0.z : 0u,
+                             bv ? b0.w : 0u, bv ? b1.x : 0u, bv ? b1.y : 0u};
+      const uint32_t sb = bv ? (b1.z & 255u) : 127u;
 #pragma unroll
-      for (int u = 0; u < GPL; ++u) {
-        const int g = group_of(S, u);
-        const bool gok = (S < s_hi) && g < a.ng;
-        u32x4 bm[4];
-        const bool bv = bok && gok;
-        const u32x4 *bq = (const u32x4 *)(bl + (size_t)(gok ? g : 0) * kGroup);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const u32x4 t = bq[i];
-          bm[i] = bv ? t : u32x4{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int r = 0; r < RB; ++r) {
-          const uint32_t sb = sx.s[r][u];
-          const bool nan_scale = sb == 255u;  // the pages' rule: the group is zero
-          const float scf = e8m0_f32(nan_scale ? 127u : sb);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t wv = nan_scale ? 0u : sx.a[r][u][q];
-            acc[r] = mfma16(fp4x8_to_bf16(wv, scf), bm[q], acc[r]);
-          }
-        }
+      for (int r = 0; r < RB; ++r) {
+        const bool nan_scale = sx.s[r] == 255u;  // the pages' rule: the group is zero
+        const u32x4 av = nan_scale ? u32x4{0, 0, 0, 0} : sx.a[r];
+        acc[r] = mfma_fp4_fp6(av, b, nan_scale ? 127u : sx.s[r], sb, acc[r]);
       }
     };
-    // DEPTH register sets rotate: DEPTH-1 steps are in flight while one is multiplied.
-    // Every wave runs the same number of steps; steps past its range read zeros.
+    // every wave runs the same number of steps; steps past its range read zeros
     load_scales(s_lo, st[0]);
     for (int i = 0; i < spw; i += DEPTH) {
 #pragma unroll
@@ -682,58 +666,60 @@ void k_grouped_dec(GroupedArgs a) {
 #pragma unroll
       for (int k = 1; k < KSPLIT; ++k) v[m] += red[m * KSPLIT + k][r][lane];
     }
+    // sum the 4 piece columns of each token (lanes tn*4 .. tn*4+3 of the row group)
 #pragma unroll
     for (int m = 0; m < NA; ++m) {
-      f32x4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int p = 0; p < PB; ++p) {
-        const int src = (lane & 48) | min(tn * PB + p, 15);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) t[i] += __shfl(v[m][i], src, 64);
+      for (int i = 0; i < 4; ++i) {
+        float t = v[m][i];
+        t += __shfl_xor(t, 1, 4);
+        t += __shfl_xor(t, 2, 4);
+        v[m][i] = t;
       }
-      v[m] = t;
     }
-    if (piece == 0 && bok && r < nrb) {
-      const int m0 = row0 + 16 * r + 4 * kq;
-      const size_t o = (size_t)(n0 + tn) * a.M + m0;
-      if constexpr (EPI == kEpiSitu) {
-        uint32_t pl[3][4];
+    const bool out_ok = piece == 0 && bok && r < nrb;
+    if constexpr (EPI == kEpiSitu) {
+      // SiTU, then quantize each 32-row group of each token into fp6 piece records
+      if (out_ok) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float val = situ(v[0][i], v[NA - 1][i], a.b1, a.b2);
-          uint32_t p[3] = {0, 0, 0};
-          split_bf16<3>(val, p);
-          pl[0][i] = p[0];
-          pl[1][i] = p[1];
-          pl[2][i] = p[2];
-        }
-#pragma unroll
-        for (int q = 0; q < 3; ++q)
-          *(u32x2 *)(a.planes[q] + o) = u32x2{pl[q][0] | (pl[q][1] << 16), pl[q][2] | (pl[q][3] << 16)};
-      } else {
-        *(f32x4 *)(a.out + o) = v[0];
+        for (int i = 0; i < 4; ++i)
+          sAct[tn * 64 + 16 * r + 4 * kq + i] = situ(v[0][i], v[NA - 1][i], a.b1, a.b2);
       }
+      __syncthreads();
+      const int t = threadIdx.x;
+      const int grp = t >> 2, k4 = t & 3;  // 4 lanes per group, 2 groups per token
+      const int tt = grp >> 1, gq = grp & 1;
+      if (tt < ntok && row0 + 32 * gq < a.M) {
+        float rv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) rv[i] = sAct[tt * 64 + 32 * gq + 8 * k4 + i];
+        uint8_t *rec = a.outq + (size_t)(n0 + tt) * (size_t)(a.M / 32) * kGroupRec +
+                       (size_t)(row0 / 32 + gq) * kGroupRec;
+        quant_group_fp6(rv, k4, rec);
+      }
+    } else {
+      if (out_ok) *(f32x4 *)(a.out + (size_t)(n0 + tn) * a.M + row0 + 16 * r + 4 * kq) = v[0];
     }
     __syncthreads();  // the next tile rewrites the staged activations
   }
 }
 
 size_t grouped_dec_lds(int K, int tt) {
-  // scale bytes of up to two matrices, then max(staged activations, partial sums)
+  // scale bytes of up to two matrices, then max(staged pieces, partial sums + SiTU outputs)
   const size_t scales = ((size_t)2 * 64 * (K / kGroup) + 15) & ~(size_t)15;
-  const size_t stage = (size_t)tt * kDecPieces * (K + 8) * 2;
-  const size_t red = (size_t)4 * 4 * 64 * 16;
+  const size_t stage = (size_t)tt * (K / kGroup) * kGroupRec;
+  const size_t red = (size_t)4 * 4 * 64 * 16 + (size_t)tt * 64 * 4;
   return scales + (stage > red ? stage : red);
 }
 
-template <int NA, int EPI, int DEPTH, int GPL>
+template <int NA, int EPI, int DEPTH>
 static hipError_t launch_grouped_tt(const GroupedArgs &a, int tt, dim3 grid, hipStream_t s) {
   const size_t lds = grouped_dec_lds(a.K, tt);
   if (lds > kMaxBlockLds) return hipErrorInvalidValue;
   switch (tt) {
-    case 1: k_grouped_dec<NA, 1, EPI, DEPTH, GPL><<<grid, 256, lds, s>>>(a); break;
-    case 2: k_grouped_dec<NA, 2, EPI, DEPTH, GPL><<<grid, 256, lds, s>>>(a); break;
-    default: k_grouped_dec<NA, 5, EPI, DEPTH, GPL><<<grid, 256, lds, s>>>(a); break;
+    case 1: k_grouped_dec<NA, 1, EPI, DEPTH><<<grid, 256, lds, s>>>(a); break;
+    case 2: k_grouped_dec<NA, 2, EPI, DEPTH><<<grid, 256, lds, s>>>(a); break;
+    default: k_grouped_dec<NA, 4, EPI, DEPTH><<<grid, 256, lds, s>>>(a); break;
   }
   return hipGetLastError();
 }
@@ -741,9 +727,38 @@ static hipError_t launch_grouped_tt(const GroupedArgs &a, int tt, dim3 grid, hip
 hipError_t launch_grouped(const GroupedArgs &a, int epi, int tokens_per_tile, int grid_y, hipStream_t s) {
   if (grid_y <= 0) return hipSuccess;
   dim3 grid((a.M + 63) / 64, grid_y);
-  if (epi == kEpiSitu)
-    return launch_grouped_tt<2, kEpiSitu, K3_GATEUP_DEPTH, K3_GPL>(a, tokens_per_tile, grid, s);
-  return launch_grouped_tt<1, kEpiEdn, K3_DOWN_DEPTH, K3_GPL>(a, tokens_per_tile, grid, s);
+  if (epi == kEpiSitu) return launch_grouped_tt<2, kEpiSitu, K3_GATEUP_DEPTH>(a, tokens_per_tile, grid, s);
+  return launch_grouped_tt<1, kEpiEdn, K3_DOWN_DEPTH>(a, tokens_per_tile, grid, s);
+}
+
+// ============================================================== fp32 rows -> fp6 pieces
+// Thread t quantizes values 8t .. 8t+7 of the flattened [rows][K] array; four
+// consecutive threads form one 32-value group (K % 32 == 0).
+__global__ __launch_bounds__(256) void k_quant_rows(const float *__restrict__ src, size_t n8,
+                                                    uint8_t *__restrict__ dst) {
+  for (size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x; t < ((n8 + 3) & ~(size_t)3);
+       t += (size_t)gridDim.x * blockDim.x) {
+    float rv[8];
+    const bool ok = t < n8;
+    const float4 *p = (const float4 *)(src + (ok ? t : 0) * 8);
+    const float4 lo = p[0], hi = p[1];
+    rv[0] = lo.x; rv[1] = lo.y; rv[2] = lo.z; rv[3] = lo.w;
+    rv[4] = hi.x; rv[5] = hi.y; rv[6] = hi.z; rv[7] = hi.w;
+    if (!ok) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) rv[i] = 0.f;
+    }
+    quant_group_fp6(rv, (int)(t & 3), dst + (t >> 2) * kGroupRec);
+  }
+}
+
+hipError_t launch_quant_rows(const float *src, size_t n, uint8_t *dst, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const size_t n8 = n / 8;
+  size_t blocks = (n8 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  k_quant_rows<<<(unsigned)blocks, 256, 0, s>>>(src, n8, dst);
+  return hipGetLastError();
 }
 
 // ============================================================== combine

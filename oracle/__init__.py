@@ -81,6 +81,8 @@ def lib():
         L.k3o_layer.restype = i
         L.k3o_route_batch.argtypes = [ctypes.POINTER(Dims), i, vp, vp, vp, vp, vp, vp, i]
         L.k3o_route_batch.restype = None
+        L.k3o_scores_batch.argtypes = [ctypes.POINTER(Dims), i, vp, vp, vp, i]
+        L.k3o_scores_batch.restype = None
         L.k3o_expert_pairs.argtypes = [ctypes.POINTER(Dims), i, vp, vp, vp, ctypes.POINTER(Experts), vp, vp, i]
         L.k3o_expert_pairs.restype = None
         _lib = L
@@ -235,6 +237,16 @@ def route_batch(dims, x: np.ndarray, Wr: np.ndarray, bias: np.ndarray, nthreads:
                           _p(np.ascontiguousarray(Wr, np.float32)), _p(np.ascontiguousarray(bias, np.float32)),
                           _p(idx), _p(w), _p(gaps), nthreads)
     return idx, w, gaps
+
+
+def scores_batch(dims, x: np.ndarray, Wr: np.ndarray, nthreads: int = 0) -> np.ndarray:
+    """Unbiased router scores sigmoid(Wr x_t) [T, E] (fp32), as the router computes them."""
+    T = x.shape[0]
+    sc = np.empty((T, dims.n_experts), np.float32)
+    d = make_dims(dims)
+    lib().k3o_scores_batch(ctypes.byref(d), T, _p(np.ascontiguousarray(x, np.uint16)),
+                           _p(np.ascontiguousarray(Wr, np.float32)), _p(sc), nthreads)
+    return sc
 
 
 def expert_pairs(dims, tok: np.ndarray, ex_id: np.ndarray, z: np.ndarray, ex: ExpertSet,

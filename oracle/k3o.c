@@ -290,6 +290,28 @@ void k3o_route_batch(const k3o_dims *d, int T, const uint16_t *x, const float *W
     (void)nthreads;
 }
 
+void k3o_scores_batch(const k3o_dims *d, int T, const uint16_t *x, const float *Wr, float *sc,
+                      int nthreads)
+{
+    const int H = d->hidden, E = d->n_experts;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 4) num_threads(nthreads)
+#endif
+    for (int t = 0; t < T; t++) {
+        float *xf = (float *)malloc(sizeof(float) * (size_t)H);
+        for (int i = 0; i < H; i++) xf[i] = k3o_bf16_to_f32(x[(size_t)t * H + i]);
+        for (int e = 0; e < E; e++) {
+            const float *row = Wr + (size_t)e * H;
+            double logit = 0.0;
+            for (int i = 0; i < H; i++) logit += (double)xf[i] * (double)row[i];
+            sc[(size_t)t * E + e] = (float)(1.0 / (1.0 + exp(-logit)));
+        }
+        free(xf);
+    }
+    (void)nthreads;
+}
+
 void k3o_expert_pairs(const k3o_dims *d, int npairs, const int *tok, const int *ex_id,
                       const float *z, const k3o_experts *ex, float *edn, float *act,
                       int nthreads)

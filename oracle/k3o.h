@@ -124,6 +124,11 @@ int k3o_layer(const k3o_dims *d, int T, const uint16_t *x, const k3o_weights *w,
 void k3o_route_batch(const k3o_dims *d, int T, const uint16_t *x, const float *Wr,
                      const float *bias, int *idx, float *wt, double *gaps, int nthreads);
 
+/* Unbiased router scores sc[t][e] = sigmoid(Wr[e] . x_t) for T tokens (fp64 sum, fp32
+ * result), the same values k3o_router weights by. OpenMP over tokens. */
+void k3o_scores_batch(const k3o_dims *d, int T, const uint16_t *x, const float *Wr, float *sc,
+                      int nthreads);
+
 /* Expert stage on a list of pairs: for pair q, token row zt = z + tok[q]*L, expert
  * ex_id[q]; edn[q][L]; act[q][I] nullable. OpenMP over pairs. */
 void k3o_expert_pairs(const k3o_dims *d, int npairs, const int *tok, const int *ex_id,

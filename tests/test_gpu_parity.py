@@ -224,15 +224,64 @@ def test_k3_layer_config2_T64(k3):
     compare_layer(k3, x, what="K3 T=64")
 
 
+def check_dispatch_of(h: Host, ids: np.ndarray, what: str):
+    d = h.dims
+    T = ids.shape[0]
+    ws = device.workspace(d, T)
+    off = torch.empty(d.n_experts + 1, dtype=torch.int32, device="cuda")
+    sp = torch.empty(T * d.topk, dtype=torch.int32, device="cuda")
+    ps = torch.empty(T * d.topk, dtype=torch.int32, device="cuda")
+    k3moe.k3moe_dispatch(d, T, t_(ids), off, sp, ps, ws)
+    torch.cuda.synchronize()
+    o, s_, p = oracle.dispatch(ids, d.n_experts)
+    assert np.array_equal(off.cpu().numpy(), o), what
+    assert np.array_equal(sp.cpu().numpy(), s_), what
+    assert np.array_equal(ps.cpu().numpy(), p), what
+    return o
+
+
+def prefill_case(h: Host, dense: dict, T: int, x_seed: int, nsample: int, what: str):
+    say(f"{what}: gap rule over all tokens (oracle router)")
+    x, _ = _inputs.gap_fixed_x(h.dims, x_seed, T, dense["w_router"], dense["bias"])
+    xd = t_(x.view(np.int16))
+    y = torch.empty((T, h.dims.hidden), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, h.dims.topk), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, h.dims.topk), dtype=torch.float32, device="cuda")
+    ws = device.workspace(h.dims, T)
+    wts = h.dev.weights_struct()
+    bias_d = t_(dense["bias"].astype(np.float32))
+    wts.bias = bias_d.data_ptr()
+    k3moe.k3moe_layer(h.dims, T, xd, wts, y, idx, w, ws)
+    torch.cuda.synchronize()
+    y, idx, w = y.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
+    ridx, rw, _ = oracle.route_batch(h.dims, x, dense["w_router"], dense["bias"])
+    assert np.array_equal(idx, ridx), f"{what}: expert ids differ"
+    check_rows(w, rw, f"{what} weights", rel=1e-6, absf=1e-6)
+    off = check_dispatch_of(h, ridx, what)
+    rng = np.random.default_rng(x_seed)
+    rows = np.concatenate([[0, T - 1], rng.choice(T, nsample, replace=False)])
+    ref = oracle.layer(h.dims, x[rows], dense, h.ex)
+    check_rows(y[rows], ref["y"], f"{what} sampled y")
+    return off
+
+
 def test_k3_layer_config3_T4096_sampled(k3):
-    T = 4096
-    say("K3 T=4096: gap rule over all tokens (oracle router)")
-    x, _ = _inputs.gap_fixed_x(k3.dims, 3, T, k3.dense["w_router"], k3.dense["bias"])
-    y, idx, w = run_layer(k3, x)
-    ridx, rw, _ = oracle.route_batch(k3.dims, x, k3.dense["w_router"], k3.dense["bias"])
-    assert np.array_equal(idx, ridx), "expert ids differ"
-    check_rows(w, rw, "T=4096 weights", rel=1e-6, absf=1e-6)
-    rows = np.random.default_rng(3).choice(T, 24, replace=False)
-    rows = np.concatenate([[0, T - 1], rows])
-    ref = oracle.layer(k3.dims, x[rows], k3.dense, k3.ex)
-    check_rows(y[rows], ref["y"], "T=4096 sampled y")
+    off = prefill_case(k3, k3.dense, 4096, 3, 24, "K3 T=4096")
+    counts = np.diff(off)
+    say(f"  experts touched {np.count_nonzero(counts)}/{k3.dims.n_experts}, max tokens {counts.max()}")
+    # the bias spread makes routing uneven: both empty experts and experts whose token
+    # list spans several tiles occur, so both edges of the grouped stage are exercised
+    assert (counts == 0).any() and counts.max() > 64
+
+
+def test_k3_layer_config4_T8192_skewed_sampled(k3):
+    dense = dict(k3.dense)
+    p = _inputs.skew_params()
+    dense["bias"] = k3gen.skew_bias(k3.dense["bias"], p["beta"], p["gamma"], p["hot_every"])
+    off = prefill_case(k3, dense, 8192, 4, 24, "K3 skewed T=8192")
+    counts = np.diff(off)
+    hot = (np.arange(k3.dims.n_experts) % p["hot_every"]) == 0
+    share = counts[hot].sum() / counts.sum()
+    say(f"  skewed routing: hot share {share:.3f}, hot tokens max {counts[hot].max()}, "
+        f"cold tokens median {np.median(counts[~hot]):.0f}, cold with 0 tokens {np.mean(counts[~hot] == 0):.2f}")
+    assert 0.75 <= share <= 0.85

@@ -196,6 +196,23 @@ def test_router_brute_force_and_invariants():
         assert abs(float(np.sum(w[t].astype(np.float64))) - 1.0) < 1e-6
 
 
+def test_router_scores_vs_tanh_logistic_and_weights():
+    """The unbiased scores are the logistic of the fp64 logit (checked against the tanh
+    form of the logistic), and the router's weights are exactly those scores renormalised
+    over the chosen ids (weights use the raw scores, not the biased ones)."""
+    d = k3gen.TINY
+    dense = k3gen.gen_dense(d, 0)
+    x = k3gen.gen_x(d, 1, 24)
+    sc = oracle.scores_batch(d, x, dense["w_router"])
+    idx, w, _ = oracle.route_batch(d, x, dense["w_router"], dense["bias"])
+    for t in range(24):
+        logit = dense["w_router"].astype(np.float64) @ _brute.bf16_bits_to_f64(x[t])
+        ref = 0.5 * (1.0 + np.tanh(0.5 * logit))
+        assert np.allclose(sc[t], ref, rtol=2 ** -23, atol=0)
+        s = sc[t, idx[t]].astype(np.float64)
+        assert np.allclose(w[t], (s / s.sum()).astype(np.float32), rtol=2 ** -23, atol=0)
+
+
 # ---------------------------------------------------------------- SiTU, RMSNorm
 def test_situ_zero_and_sign():
     assert oracle.situ(0.0, 7.0) == 0.0
