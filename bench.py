@@ -5,7 +5,9 @@ experts, combine + RMSNorm, up-projection) over one batch of synthetic input alr
 resident in HBM. The headline workload is the K3-shape decode layer: T = 1 token per
 step, hidden 7168, latent 3584, inter 3072, 896 MXFP4 experts (15.7 GB resident),
 top-16. Each step reads a different token from a pool of 64, so the routed experts
-change from step to step. A K3-shape prefill pass (T = 4096) is reported beside it.
+change from step to step, and the steps rotate over copies of the dense weights (4 by
+default, 128 MB each), so those are not served from the 256 MB MALL either. A
+K3-shape prefill pass (T = 4096) is reported beside it.
 
 Prints one JSON line (rank 0). Per-kernel times come from HIP events recorded between
 the kernels of the same steps (k3moe_layer_profiled) on the stream they run on.
@@ -87,6 +89,9 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=32)
+    ap.add_argument("--dense-copies", type=int, default=4,
+                    help="copies of the dense weights (router, projections) the decode steps rotate "
+                         "over, so no step finds them still cached in the MALL from the step before")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB (a known-size "
                          "kernel for scaling hardware byte counters)")
@@ -123,6 +128,15 @@ def main():
 
     stream = torch.cuda.Stream()
     wts = dev.weights_struct()
+    # Decode steps rotate over copies of the dense weights (4 x 128 MB by default) on top of
+    # the pool of tokens, so each step's dense weights and experts come from HBM.
+    copies = [dev]
+    for _ in range(max(1, args.dense_copies) - 1):
+        copies.append(device.DeviceLayer(dims=dims, w_router=dev.w_router.clone(), bias=dev.bias.clone(),
+                                         w_down=dev.w_down.clone(), w_up=dev.w_up.clone(),
+                                         norm_w=dev.norm_w.clone(), experts=dev.experts,
+                                         blob_bytes=dev.blob_bytes, offsets=dev.offsets))
+    wts_rot = [c.weights_struct() for c in copies]
 
     if args.copy_calib_mib:
         n = args.copy_calib_mib << 20
@@ -146,7 +160,8 @@ def main():
 
     def step(i):
         j = i % pool
-        k3moe.k3moe_layer(dims, T, xs.data_ptr() + j * row, wts, y, idx[j], tw[j], ws, stream=stream)
+        k3moe.k3moe_layer(dims, T, xs.data_ptr() + j * row, wts_rot[i % len(wts_rot)], y, idx[j], tw[j], ws,
+                          stream=stream)
 
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
@@ -174,8 +189,8 @@ def main():
     names = []
     for i in range(nprof):
         j = i % pool
-        names = k3moe.k3moe_layer_profiled(dims, T, xs.data_ptr() + j * row, wts, y, idx[j], tw[j], ws,
-                                           pe.ev, stream=stream)
+        names = k3moe.k3moe_layer_profiled(dims, T, xs.data_ptr() + j * row, wts_rot[i % len(wts_rot)], y,
+                                           idx[j], tw[j], ws, pe.ev, stream=stream)
         torch.cuda.synchronize()
         for k, n in enumerate(names):
             sums[n] = sums.get(n, 0.0) + pe.ms(pe.ev[k], pe.ev[k + 1])
@@ -211,11 +226,20 @@ def main():
         torch.cuda.synchronize()
         msp = evp.ms(evp.ev[0], evp.ev[1]) / args.prefill_steps
         evp.close()
+        pep = HipEvents(16)
+        names_p = k3moe.k3moe_layer_profiled(dims, Tp, xp, wts, yp, None, None, wsp, pep.ev, stream=stream)
+        torch.cuda.synchronize()
+        kern_p = {n: round(pep.ms(pep.ev[k], pep.ev[k + 1]) * 1e3, 1) for k, n in enumerate(names_p)}
+        pep.close()
         algp = algorithmic(dims, Tp, dims.n_experts)
         tf = algp["flops"] / (msp * 1e-3) / 1e12
+        ex_us = kern_p.get("expert_gateup_situ", 0.0) + kern_p.get("expert_down", 0.0)
+        ex_tf = algp["expert_flops"] / (ex_us * 1e-6) / 1e12 if ex_us > 0 else None
         prefill = {"T": Tp, "ms_per_step": round(msp, 3), "tokens_per_s": round(Tp / (msp * 1e-3), 1),
-                   "algorithmic_TFLOPs": round(tf, 2), "bf16_peak_frac": round(tf / BF16_PEAK_TFLOPS, 4)}
-        log(f"prefill T=4096: {msp:.2f} ms/step, {tf:.1f} TFLOP/s algorithmic")
+                   "algorithmic_TFLOPs": round(tf, 2), "bf16_peak_frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                   "expert_TFLOPs": round(ex_tf, 2) if ex_tf else None, "kernel_us": kern_p}
+        log(f"prefill T=4096: {msp:.2f} ms/step, {tf:.1f} TFLOP/s algorithmic; per-kernel us: "
+            + ", ".join(f"{n} {v:.0f}" for n, v in kern_p.items()))
         del wsp, yp, xp
         torch.cuda.empty_cache()
 
@@ -246,10 +270,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp4 weights, bf16 matrix cores, fp32 accumulate/output",
+        "dtype": "fp32",
         "data": "synthetic",
         "config": {"workload": "K3-shape decode layer T=1: H=7168 L=3584 I=3072 E=896 K=16, "
-                               "896 MXFP4 experts resident (15.7 GB)", "T": T, "global_batch": T,
+                               "896 MXFP4 experts resident (15.7 GB), 64-token pool, dense weights "
+                               f"rotated over {len(wts_rot)} copies", "T": T, "global_batch": T,
                    "parallelism": "single GPU"},
         "roofline": roofline,
         "prefill": prefill,

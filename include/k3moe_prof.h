@@ -22,6 +22,16 @@ int k3moe_layer_profiled(const k3moe_dims *d, int32_t T, const uint16_t *x, cons
                          void *stream, void **events, int max_events, int *n_kernels);
 const char *k3moe_prof_name(int i);
 
+/* Which kernels run the expert passes, for tests and measurement that compare the two
+ * forms on the same inputs: 0 = by batch size (the default: the grouped GEMM form when
+ * the batch averages at least two token-expert pairs per expert), 1 = always the
+ * grouped GEMV form, 2 = the grouped GEMM form wherever its shape limits allow (the
+ * pass's K a multiple of 128 and its activation records under 2 GiB). Both forms give
+ * the same result up to fp32 summation order. Process-wide, not synchronised with calls
+ * in flight on other threads. Returns the previous mode, or K3MOE_EINVAL for another
+ * value. */
+int k3moe_set_expert_path(int mode);
+
 #ifdef __cplusplus
 }
 #endif

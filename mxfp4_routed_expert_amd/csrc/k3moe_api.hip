@@ -60,7 +60,8 @@ struct Ws {
   int32_t *sorted_pair;        // [P]
   int32_t *pair_slot;          // [P]
   int32_t *active;             // [E]
-  int32_t *counters;           // [0] active experts, [1] dropped pairs
+  int32_t *counters;           // [0] active experts, [1] dropped pairs, [2] GEMM column tiles
+  int4 *tiles;                 // [max_mm_tiles] GEMM column-tile table
   int32_t *lrank;              // [P]
   int32_t *cnt;                // [chunks][E]
   uint8_t *actq;               // [P][I/32] fp6 piece records of the SiTU outputs
@@ -69,6 +70,24 @@ struct Ws {
   float *ss;                   // [T][ceil(L/256)] partial sums of acc^2
   size_t bytes;
 };
+
+int g_expert_path = 0;  // k3moe_set_expert_path
+
+int64_t max_mm_tiles(const k3moe_dims *d, int32_t T) {
+  const int64_t P = (int64_t)T * d->topk;
+  return (P + kMmBN - 1) / kMmBN + (P < d->n_experts ? P : d->n_experts);
+}
+
+// grouped GEMM form for a pass with K columns and activation records of rec_bytes
+bool use_mm(const k3moe_dims *d, int32_t T, int K, int64_t rec_bytes, const k3moe_mxfp4 &m0,
+            const k3moe_mxfp4 &m1) {
+  if (g_expert_path == 1 || K % 128 != 0 || rec_bytes >= ((int64_t)1 << 31)) return false;
+  // scale rows are copied a dword (4 groups) at a time
+  for (const k3moe_mxfp4 *m : {&m0, &m1})
+    if (((uintptr_t)m->scales & 3u) || (m->scales_expert_stride & 3)) return false;
+  if (g_expert_path == 2) return true;
+  return (int64_t)T * d->topk >= 2 * (int64_t)d->n_experts;
+}
 
 Ws carve(const k3moe_dims *d, int32_t T, void *base) {
   Ws w;
@@ -92,6 +111,7 @@ Ws carve(const k3moe_dims *d, int32_t T, void *base) {
   w.pair_slot = (int32_t *)take(P * 4);
   w.active = (int32_t *)take(E * 4);
   w.counters = (int32_t *)take(64);
+  w.tiles = (int4 *)take((size_t)max_mm_tiles(d, T) * sizeof(int4));
   w.lrank = (int32_t *)take(P * 4);
   w.cnt = (int32_t *)take(nch * E * 4);
   w.actq = (uint8_t *)take(P * I * 4);
@@ -187,41 +207,92 @@ int run_down(const k3moe_dims *d, int32_t T, const uint16_t *x, const uint16_t *
 int run_experts(const k3moe_dims *d, int32_t T, const uint8_t *zq, const k3moe_experts *ex,
                 const int32_t *expert_off, const int32_t *sorted_pair, const int32_t *active,
                 const int32_t *counters, float *edn, const Ws &w, hipStream_t s) {
-  const int grid_y = (int)((int64_t)T * d->topk < d->n_experts ? (int64_t)T * d->topk : d->n_experts);
+  const int64_t P = (int64_t)T * d->topk;
+  const bool mm_gu = use_mm(d, T, d->latent, (int64_t)T * d->latent * 4, ex->w1, ex->w3);
+  const bool mm_dn = use_mm(d, T, d->inter, P * d->inter * 4, ex->w2, ex->w2);
+  const int grid_y = (int)(P < d->n_experts ? P : d->n_experts);
   // tokens staged per tile (an expert holds at most T tokens), as many as fit in LDS
   const int kmax = d->latent > d->inter ? d->latent : d->inter;
   int tt = T <= 1 ? 1 : (T <= 2 ? 2 : 4);
   while (tt > 1 && grouped_dec_lds(kmax, tt) > kMaxBlockLds) tt >>= 1;
+  if (mm_gu || mm_dn) K3_HIP(launch_mm_tiles(expert_off, d->n_experts, w.tiles, w.counters + 2, s));
+  const int max_tiles = (int)max_mm_tiles(d, T);
 
-  GroupedArgs g = {};
-  g.A[0] = MxMat{ex->w1.packed, ex->w1.scales, ex->w1.packed_expert_stride, ex->w1.scales_expert_stride};
-  g.A[1] = MxMat{ex->w3.packed, ex->w3.scales, ex->w3.packed_expert_stride, ex->w3.scales_expert_stride};
-  g.M = d->inter;
-  g.K = d->latent;
-  g.ng = d->latent / 32;
-  g.Bq = zq;
-  g.gather = 1;
-  g.topk = d->topk;
-  g.expert_off = expert_off;
-  g.sorted_pair = sorted_pair;
-  g.active = active;
-  g.n_active = counters;
-  g.outq = w.actq;
-  g.b1 = d->b1;
-  g.b2 = d->b2;
-  K3_HIP(launch_grouped(g, kEpiSitu, tt, grid_y, s));
+  const MxMat w1{ex->w1.packed, ex->w1.scales, ex->w1.packed_expert_stride, ex->w1.scales_expert_stride};
+  const MxMat w3{ex->w3.packed, ex->w3.scales, ex->w3.packed_expert_stride, ex->w3.scales_expert_stride};
+  const MxMat w2{ex->w2.packed, ex->w2.scales, ex->w2.packed_expert_stride, ex->w2.scales_expert_stride};
+  if (mm_gu) {
+    MmArgs m = {};
+    m.A[0] = w1;
+    m.A[1] = w3;
+    m.M = d->inter;
+    m.K = d->latent;
+    m.ng = d->latent / 32;
+    m.Bq = zq;
+    m.bq_bytes = (uint32_t)((int64_t)T * d->latent * 4);
+    m.gather = 1;
+    m.topk = d->topk;
+    m.expert_off = expert_off;
+    m.sorted_pair = sorted_pair;
+    m.tiles = w.tiles;
+    m.n_tiles = w.counters + 2;
+    m.outq = w.actq;
+    m.b1 = d->b1;
+    m.b2 = d->b2;
+    K3_HIP(launch_grouped_mm(m, kEpiSitu, max_tiles, s));
+  } else {
+    GroupedArgs g = {};
+    g.A[0] = w1;
+    g.A[1] = w3;
+    g.M = d->inter;
+    g.K = d->latent;
+    g.ng = d->latent / 32;
+    g.Bq = zq;
+    g.gather = 1;
+    g.topk = d->topk;
+    g.expert_off = expert_off;
+    g.sorted_pair = sorted_pair;
+    g.active = active;
+    g.n_active = counters;
+    g.outq = w.actq;
+    g.b1 = d->b1;
+    g.b2 = d->b2;
+    K3_HIP(launch_grouped(g, kEpiSitu, tt, grid_y, s));
+  }
   K3_HIP(mark("expert_gateup_situ", s));
 
-  GroupedArgs h = g;
-  h.A[0] = MxMat{ex->w2.packed, ex->w2.scales, ex->w2.packed_expert_stride, ex->w2.scales_expert_stride};
-  h.A[1] = h.A[0];
-  h.M = d->latent;
-  h.K = d->inter;
-  h.ng = d->inter / 32;
-  h.Bq = w.actq;
-  h.gather = 0;
-  h.out = edn;
-  K3_HIP(launch_grouped(h, kEpiEdn, tt, grid_y, s));
+  if (mm_dn) {
+    MmArgs m = {};
+    m.A[0] = m.A[1] = w2;
+    m.M = d->latent;
+    m.K = d->inter;
+    m.ng = d->inter / 32;
+    m.Bq = w.actq;
+    m.bq_bytes = (uint32_t)(P * d->inter * 4);
+    m.gather = 0;
+    m.topk = d->topk;
+    m.expert_off = expert_off;
+    m.sorted_pair = sorted_pair;
+    m.tiles = w.tiles;
+    m.n_tiles = w.counters + 2;
+    m.out = edn;
+    K3_HIP(launch_grouped_mm(m, kEpiEdn, max_tiles, s));
+  } else {
+    GroupedArgs h = {};
+    h.A[0] = h.A[1] = w2;
+    h.M = d->latent;
+    h.K = d->inter;
+    h.ng = d->inter / 32;
+    h.Bq = w.actq;
+    h.gather = 0;
+    h.topk = d->topk;
+    h.expert_off = expert_off;
+    h.sorted_pair = sorted_pair;
+    h.active = active;
+    h.n_active = counters;
+    h.out = edn;
+    K3_HIP(launch_grouped(h, kEpiEdn, tt, grid_y, s));
+  }
   K3_HIP(mark("expert_down", s));
   return K3MOE_OK;
 }
@@ -372,6 +443,13 @@ int k3moe_layer_profiled(const k3moe_dims *d, int32_t T, const uint16_t *x, cons
   *n_kernels = g_prof.n;
   g_prof.events = nullptr;
   return rc;
+}
+
+int k3moe_set_expert_path(int mode) {
+  if (mode < 0 || mode > 2) return K3MOE_EINVAL;
+  const int prev = g_expert_path;
+  g_expert_path = mode;
+  return prev;
 }
 
 const char *k3moe_prof_name(int i) {

@@ -170,6 +170,30 @@ __device__ __forceinline__ void quant_group_fp6(float (&r)[8], int k4, uint8_t *
   }
 }
 
+// Exclusive prefix sum of one int per thread over the block (blockDim.x <= 1024);
+// sh_wave holds 16 ints. Every thread gets the block total.
+__device__ __forceinline__ int block_excl_scan(int v, int *sh_wave, int *total) {
+  // blockDim.x <= 1024; sh_wave holds 16 ints
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) sh_wave[wave] = x;
+  __syncthreads();
+  int base = 0, all = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int s = sh_wave[w];
+    if (w < wave) base += s;
+    all += s;
+  }
+  __syncthreads();
+  *total = all;
+  return base + x - v;
+}
+
 // SiTU-GLU: b1 tanh(g/b1) sigmoid(g) * b2 tanh(u/b2); the sigmoid reads the uncapped g.
 __device__ __forceinline__ float situ(float g, float u, float b1, float b2) {
   const float gate = b1 * tanhf(g / b1) * (1.0f / (1.0f + expf(-g)));

@@ -48,6 +48,25 @@ struct GroupedArgs {
   float b1, b2;
 };
 
+// Grouped GEMM form of the same two passes (many tokens per expert); K % 128 == 0.
+constexpr int kMmBN = 64;      // tokens per column tile
+constexpr int kMmFrags = 16;   // 16-row weight fragments per block
+constexpr int kMmStages = 3;   // LDS ring depth of the weight stream
+
+struct MmArgs {
+  MxMat A[2];             // gate/up: {w1, w3}; down: {w2}
+  int M, K, ng;           // rows, cols, groups per row (ng % 4 == 0)
+  const uint8_t *Bq;      // activation fp6 piece records, row = token (gather) or sorted slot
+  uint32_t bq_bytes;      // bytes of Bq (< 2^31)
+  int gather, topk;
+  const int32_t *expert_off, *sorted_pair;
+  const int4 *tiles;      // column-tile table (launch_mm_tiles)
+  const int32_t *n_tiles;
+  float *out;             // kEpiEdn: [slot][M] fp32
+  uint8_t *outq;          // kEpiSitu: [slot][M/32] fp6 piece records of act
+  float b1, b2;
+};
+
 // ---------------------------------------------------------------- launchers
 hipError_t launch_route_down(const DenseArgs &router, int ks, const DenseArgs *down, hipStream_t s);
 hipError_t launch_dense_bf16(const DenseArgs &a, int pieces, int epi, hipStream_t s);
@@ -67,6 +86,10 @@ hipError_t launch_split_planes(const float *src, size_t n, uint16_t *p0, uint16_
 constexpr size_t kMaxBlockLds = 65536;
 size_t grouped_dec_lds(int K, int tokens_per_tile);
 hipError_t launch_grouped(const GroupedArgs &a, int epi, int tokens_per_tile, int grid_y, hipStream_t s);
+// column tiles of kMmBN slots per expert: at most ceil(P / kMmBN) + min(E, P) entries
+hipError_t launch_mm_tiles(const int32_t *expert_off, int E, int4 *tiles, int32_t *n_tiles, hipStream_t s);
+size_t grouped_mm_lds();
+hipError_t launch_grouped_mm(const MmArgs &a, int epi, int max_tiles, hipStream_t s);
 hipError_t launch_combine(const float *edn, const int32_t *pair_slot, const float *topk_w,
                           const float *gamma, int T, int K, int L, uint16_t *p0, uint16_t *p1,
                           uint16_t *p2, float *ss_part, hipStream_t s);

@@ -306,28 +306,6 @@ hipError_t launch_topk(const float *part, int ks, int T, int E, const float *bia
 // pair among its expert's pairs in the chunk is a popcount of the mask below its token.
 constexpr int kChunk = 64;
 
-__device__ __forceinline__ int block_excl_scan(int v, int *sh_wave, int *total) {
-  // blockDim.x <= 1024; sh_wave holds 16 ints
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
-  int x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  if (lane == 63) sh_wave[wave] = x;
-  __syncthreads();
-  int base = 0, all = 0;
-  for (int w = 0; w < nw; ++w) {
-    const int s = sh_wave[w];
-    if (w < wave) base += s;
-    all += s;
-  }
-  __syncthreads();
-  *total = all;
-  return base + x - v;
-}
-
 __device__ __forceinline__ void chunk_masks(const int32_t *topk_idx, int T, int K, int E, int c,
                                             unsigned long long *mask) {
   for (int e = threadIdx.x; e < E; e += blockDim.x) mask[e] = 0ull;

@@ -80,6 +80,8 @@ def load(path: str | None = None):
     L.k3moe_layer_profiled.restype = ctypes.c_int
     L.k3moe_prof_name.argtypes = [ctypes.c_int]
     L.k3moe_prof_name.restype = ctypes.c_char_p
+    L.k3moe_set_expert_path.argtypes = [ctypes.c_int]
+    L.k3moe_set_expert_path.restype = ctypes.c_int
     for n in EXPORTS[:-1]:
         getattr(L, n).restype = ctypes.c_int
     if path is None:
@@ -210,3 +212,15 @@ def k3moe_layer_profiled(dims, T, x, weights: k3moe_weights, y, topk_idx_out, to
                                      len(events), ctypes.byref(nk))
     _check(rc, "k3moe_layer_profiled")
     return [load().k3moe_prof_name(i).decode() for i in range(nk.value)]
+
+
+EXPERT_PATH_AUTO, EXPERT_PATH_GEMV, EXPERT_PATH_GEMM = 0, 1, 2
+
+
+def k3moe_set_expert_path(mode: int) -> int:
+    """Select the expert-pass kernels (0 by batch size, 1 grouped GEMV, 2 grouped GEMM
+    where its shape limits allow); returns the previous mode."""
+    rc = load().k3moe_set_expert_path(int(mode))
+    if rc < 0:
+        raise K3MoeError(rc, "k3moe_set_expert_path")
+    return rc

@@ -11,12 +11,16 @@ import k3gen
 from mxfp4_routed_expert_amd import k3moe
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "k3moe.h")
+INCLUDE = os.path.join(ROOT, "include")
 
 
 def header_functions():
-    text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(k3moe_\w+)\s*\(", text, re.M)))
+    names = set()
+    for h in sorted(os.listdir(INCLUDE)):
+        if h.endswith(".h"):
+            text = open(os.path.join(INCLUDE, h)).read()
+            names |= set(re.findall(r"^\s*(?:int|const char \*)\s*(k3moe_\w+)\s*\(", text, re.M))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_function():
@@ -115,3 +119,14 @@ def test_other_entry_points_refuse_before_launch():
     assert k3moe.k3moe_layer(d, 0, FAKE, w, FAKE, None, None, WS, check=False) == k3moe.K3MOE_OK
     with pytest.raises(k3moe.K3MoeError):
         k3moe.k3moe_layer(d, 4, FAKE, None, FAKE, None, None, WS)
+
+
+def test_expert_path_switch_host_only():
+    prev = k3moe.k3moe_set_expert_path(k3moe.EXPERT_PATH_GEMM)
+    try:
+        assert k3moe.k3moe_set_expert_path(k3moe.EXPERT_PATH_GEMV) == k3moe.EXPERT_PATH_GEMM
+        assert k3moe.load().k3moe_set_expert_path(3) == k3moe.K3MOE_EINVAL
+        assert k3moe.load().k3moe_set_expert_path(-1) == k3moe.K3MOE_EINVAL
+        assert k3moe.k3moe_set_expert_path(k3moe.EXPERT_PATH_AUTO) == k3moe.EXPERT_PATH_GEMV
+    finally:
+        k3moe.k3moe_set_expert_path(prev)

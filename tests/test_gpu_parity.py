@@ -4,6 +4,7 @@ token row within rel-L2 <= 1e-5 and max-abs <= 1e-4 * max|ref| (the layer's stat
 tolerance; stage outputs are held to the same bar)."""
 from __future__ import annotations
 
+import dataclasses
 import sys
 
 import numpy as np
@@ -54,6 +55,23 @@ class Host:
 @pytest.fixture(scope="module")
 def tiny():
     return Host(k3gen.TINY, 0)
+
+
+# a tiny shape whose expert passes both have K % 128 == 0, so both can run as grouped GEMMs
+TINY_MM = dataclasses.replace(k3gen.TINY, inter=128)
+
+
+@pytest.fixture(scope="module")
+def tiny_mm():
+    return Host(TINY_MM, 0)
+
+
+@pytest.fixture
+def expert_path():
+    """Set the expert-pass form for one test; the default is restored afterwards."""
+    prev = k3moe.k3moe_set_expert_path(k3moe.EXPERT_PATH_AUTO)
+    yield k3moe.k3moe_set_expert_path
+    k3moe.k3moe_set_expert_path(prev)
 
 
 @pytest.fixture(scope="module")
@@ -151,6 +169,23 @@ def test_tiny_layer_ragged_T(tiny, T):
     compare_layer(tiny, x, what=f"tiny T={T}")
 
 
+@pytest.mark.parametrize("mode", [k3moe.EXPERT_PATH_GEMV, k3moe.EXPERT_PATH_GEMM])
+@pytest.mark.parametrize("T", [1, 5, 16, 64, 65, 300, 700])
+def test_tiny_mm_shape_both_expert_forms(tiny_mm, expert_path, mode, T):
+    """Both expert-pass forms on the same inputs; T = 700 gives experts of more than one
+    64-token column tile, T = 1 and 5 experts with a single token."""
+    expert_path(mode)
+    say(f"tiny (inter 128) layer T={T} expert form {mode}")
+    x, _ = _inputs.gap_fixed_x(tiny_mm.dims, 200 + T, T, tiny_mm.dense["w_router"], tiny_mm.dense["bias"])
+    compare_layer(tiny_mm, x, what=f"tiny-mm T={T} form {mode}")
+
+
+def test_tiny_mm_stages_gemm(tiny_mm, expert_path):
+    expert_path(k3moe.EXPERT_PATH_GEMM)
+    x, _ = _inputs.gap_fixed_x(tiny_mm.dims, 7, 200, tiny_mm.dense["w_router"], tiny_mm.dense["bias"])
+    stages(tiny_mm, x)
+
+
 def test_tiny_dispatch_chunked_and_invalid_ids(tiny):
     d = tiny.dims
     rng = np.random.default_rng(7)
@@ -222,6 +257,19 @@ def test_k3_layer_config1_T1(k3):
 def test_k3_layer_config2_T64(k3):
     x, _ = _inputs.gap_fixed_x(k3.dims, 2, 64, k3.dense["w_router"], k3.dense["bias"])
     compare_layer(k3, x, what="K3 T=64")
+
+
+def test_k3_layer_T64_grouped_gemm(k3, expert_path):
+    expert_path(k3moe.EXPERT_PATH_GEMM)
+    x, _ = _inputs.gap_fixed_x(k3.dims, 2, 64, k3.dense["w_router"], k3.dense["bias"])
+    compare_layer(k3, x, what="K3 T=64 grouped GEMM")
+
+
+@pytest.mark.parametrize("mode", [k3moe.EXPERT_PATH_GEMV, k3moe.EXPERT_PATH_GEMM])
+def test_k3_layer_T256_both_expert_forms(k3, expert_path, mode):
+    expert_path(mode)
+    x, _ = _inputs.gap_fixed_x(k3.dims, 5, 256, k3.dense["w_router"], k3.dense["bias"])
+    compare_layer(k3, x, what=f"K3 T=256 form {mode}")
 
 
 def check_dispatch_of(h: Host, ids: np.ndarray, what: str):
