@@ -14,6 +14,8 @@ namespace {
 
 constexpr int kRouterSplits = 7;  // K-splits of the router product (partials summed by top-k)
 constexpr int kPieces = 3;        // bf16 pieces per fp32 activation
+// batches of at least this many tokens run the dense products as GEMMs (k3moe_dense_mm)
+constexpr int kDenseMmMinT = 128;
 
 bool al16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 bool al8(const void *p) { return ((uintptr_t)p & 7u) == 0; }
@@ -68,6 +70,7 @@ struct Ws {
   float *edn;                  // [P][L]
   uint16_t *np[3];             // [T][L] pieces of gamma * acc
   float *ss;                   // [T][ceil(L/256)] partial sums of acc^2
+  uint16_t *wr_planes;         // [3][E][H] bf16 pieces of the router weights (GEMM form)
   size_t bytes;
 };
 
@@ -118,6 +121,7 @@ Ws carve(const k3moe_dims *d, int32_t T, void *base) {
   w.edn = (float *)take(P * L * 4);
   for (int q = 0; q < 3; ++q) w.np[q] = (uint16_t *)take(t * L * 2);
   w.ss = (float *)take(t * ((L + 255) / 256) * 4);
+  w.wr_planes = T >= kDenseMmMinT ? (uint16_t *)take(3 * E * (size_t)d->hidden * 2) : nullptr;
   w.bytes = o;
   return w;
 }
@@ -158,6 +162,34 @@ hipError_t mark(const char *name, hipStream_t s) {
   } while (0)
 
 // ---- step launchers (arguments already checked)
+bool use_dense_mm(int32_t T) { return T >= kDenseMmMinT; }
+
+// The router's three weight planes (row segments 0..2) and optionally W_down
+// (segment 3), all against x.
+int run_route_down_mm(const k3moe_dims *d, int32_t T, const uint16_t *x, const float *wr,
+                      const uint16_t *wd, float *z, const Ws &w, hipStream_t s) {
+  const size_t EH = (size_t)d->n_experts * d->hidden;
+  K3_HIP(launch_split_planes(wr, EH, w.wr_planes, w.wr_planes + EH, w.wr_planes + 2 * EH, s));
+  K3_HIP(mark("router_weight_split", s));
+  DenseMmArgs a = {};
+  const int E = d->n_experts;
+  for (int p = 0; p < 3; ++p)
+    a.seg[p] = DenseSeg{w.wr_planes + p * EH, p * E, E, w.router_part + (size_t)p * T * E, E};
+  a.nseg = 3;
+  a.M = 3 * E;
+  if (wd) {
+    a.seg[3] = DenseSeg{wd, 3 * E, d->latent, z, d->latent};
+    a.nseg = 4;
+    a.M += d->latent;
+  }
+  a.K = d->hidden;
+  a.N = T;
+  a.B = x;
+  a.plane_elems = (int64_t)T * d->hidden;
+  K3_HIP(launch_dense_mm(a, 1, kEpiStore, s));
+  return K3MOE_OK;
+}
+
 DenseArgs router_args(const k3moe_dims *d, int32_t T, const uint16_t *x, const float *wr, const Ws &w) {
   DenseArgs a = {};
   a.A = wr;
@@ -187,10 +219,18 @@ DenseArgs down_args(const k3moe_dims *d, int32_t T, const uint16_t *x, const uin
 int run_route(const k3moe_dims *d, int32_t T, const uint16_t *x, const float *wr, const float *bias,
               int32_t *idx, float *wt, const DenseArgs *down, const Ws &w, hipStream_t s) {
   // with the latent projection in the same launch, the top-k blocks also quantize z
-  const DenseArgs a = router_args(d, T, x, wr, w);
-  K3_HIP(launch_route_down(a, kRouterSplits, down, s));
+  int splits = kRouterSplits;
+  // the router planes are row segments, which start at multiples of 64 rows
+  if (use_dense_mm(T) && d->n_experts % 64 == 0) {
+    K3_TRY(run_route_down_mm(d, T, x, wr, down ? (const uint16_t *)down->A : nullptr, down ? down->out : nullptr,
+                             w, s));
+    splits = 3;
+  } else {
+    const DenseArgs a = router_args(d, T, x, wr, w);
+    K3_HIP(launch_route_down(a, kRouterSplits, down, s));
+  }
   K3_HIP(mark(down ? "router_and_latent_down" : "router_gemv", s));
-  K3_HIP(launch_topk(w.router_part, kRouterSplits, T, d->n_experts, bias, d->topk, d->renorm,
+  K3_HIP(launch_topk(w.router_part, splits, T, d->n_experts, bias, d->topk, d->renorm,
                      d->routed_scale, idx, wt, down ? w.z32 : nullptr, d->latent, w.zq, s));
   K3_HIP(mark("topk", s));
   return K3MOE_OK;
@@ -198,8 +238,20 @@ int run_route(const k3moe_dims *d, int32_t T, const uint16_t *x, const float *wr
 
 int run_down(const k3moe_dims *d, int32_t T, const uint16_t *x, const uint16_t *wd, float *z,
              hipStream_t s) {
-  const DenseArgs a = down_args(d, T, x, wd, z);
-  K3_HIP(launch_dense_bf16(a, 1, kEpiStore, s));
+  if (use_dense_mm(T)) {
+    DenseMmArgs a = {};
+    a.seg[0] = DenseSeg{wd, 0, d->latent, z, d->latent};
+    a.nseg = 1;
+    a.M = d->latent;
+    a.K = d->hidden;
+    a.N = T;
+    a.B = x;
+    a.plane_elems = (int64_t)T * d->hidden;
+    K3_HIP(launch_dense_mm(a, 1, kEpiStore, s));
+  } else {
+    const DenseArgs a = down_args(d, T, x, wd, z);
+    K3_HIP(launch_dense_bf16(a, 1, kEpiStore, s));
+  }
   K3_HIP(mark("latent_down_gemv", s));
   return K3MOE_OK;
 }
@@ -303,18 +355,33 @@ int run_combine(const k3moe_dims *d, int32_t T, const float *edn, const int32_t 
   K3_HIP(launch_combine(edn, pair_slot, topk_w, norm_w, T, d->topk, d->latent, w.np[0], w.np[1],
                         w.np[2], w.ss, s));
   K3_HIP(mark("combine", s));
-  DenseArgs a = {};
-  a.A = w_up;
-  a.M = d->hidden;
-  a.K = d->latent;
-  a.ng = d->latent / 32;
-  for (int q = 0; q < 3; ++q) a.B[q] = w.np[q];
-  a.N = T;
-  a.out = y;
-  a.ss = w.ss;
-  a.nss = (d->latent + 255) / 256;
-  a.eps = d->eps;
-  K3_HIP(launch_dense_bf16(a, kPieces, kEpiStoreScaled, s));
+  if (use_dense_mm(T)) {
+    DenseMmArgs a = {};
+    a.seg[0] = DenseSeg{w_up, 0, d->hidden, y, d->hidden};
+    a.nseg = 1;
+    a.M = d->hidden;
+    a.K = d->latent;
+    a.N = T;
+    a.B = w.np[0];
+    a.plane_elems = (int64_t)(w.np[1] - w.np[0]);  // the three planes are carved back to back
+    a.ss = w.ss;
+    a.nss = (d->latent + 255) / 256;
+    a.eps = d->eps;
+    K3_HIP(launch_dense_mm(a, kPieces, kEpiStoreScaled, s));
+  } else {
+    DenseArgs a = {};
+    a.A = w_up;
+    a.M = d->hidden;
+    a.K = d->latent;
+    a.ng = d->latent / 32;
+    for (int q = 0; q < 3; ++q) a.B[q] = w.np[q];
+    a.N = T;
+    a.out = y;
+    a.ss = w.ss;
+    a.nss = (d->latent + 255) / 256;
+    a.eps = d->eps;
+    K3_HIP(launch_dense_bf16(a, kPieces, kEpiStoreScaled, s));
+  }
   K3_HIP(mark("rmsnorm_up_gemv", s));
   return K3MOE_OK;
 }

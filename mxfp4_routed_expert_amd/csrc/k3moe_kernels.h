@@ -28,6 +28,26 @@ struct DenseArgs {
   float eps;
 };
 
+// GEMM form for many tokens: C[n][m] = sum_p sum_k A[m][k] * B_p[n][k]. The rows of A
+// are the concatenation of up to kDmMaxSegs segments (each a bf16 matrix [rows][K]
+// with its own output), placed at multiples of 64 rows.
+constexpr int kDmMaxSegs = 4;
+struct DenseSeg {
+  const uint16_t *A;  // [rows][K]
+  int row0, rows;     // place in the concatenated row space
+  float *out;         // out[n * ld + (row - row0)]
+  int ld;
+};
+struct DenseMmArgs {
+  DenseSeg seg[kDmMaxSegs];
+  int nseg, M, K, N;
+  const uint16_t *B;    // plane p at B + p * plane_elems, each [N][K]
+  int64_t plane_elems;
+  const float *ss;      // kEpiStoreScaled: as DenseArgs
+  int nss;
+  float eps;
+};
+
 // ---------------------------------------------------------------- grouped MXFP4
 struct MxMat {
   const uint8_t *packed;
@@ -70,6 +90,8 @@ struct MmArgs {
 // ---------------------------------------------------------------- launchers
 hipError_t launch_route_down(const DenseArgs &router, int ks, const DenseArgs *down, hipStream_t s);
 hipError_t launch_dense_bf16(const DenseArgs &a, int pieces, int epi, hipStream_t s);
+// pieces 1 with kEpiStore, or 3 with kEpiStoreScaled
+hipError_t launch_dense_mm(const DenseMmArgs &a, int pieces, int epi, hipStream_t s);
 // z (nullable) [T][L] fp32: block t also writes row t's fp6 piece records to zq
 hipError_t launch_topk(const float *part, int ks, int T, int E, const float *bias, int K,
                        int renorm, float rscale, int32_t *idx, float *w, const float *z, int L,

@@ -57,8 +57,9 @@ def tiny():
     return Host(k3gen.TINY, 0)
 
 
-# a tiny shape whose expert passes both have K % 128 == 0, so both can run as grouped GEMMs
-TINY_MM = dataclasses.replace(k3gen.TINY, inter=128)
+# a tiny shape whose expert passes both have K % 128 == 0 (both can run as grouped
+# GEMMs) and whose expert count is a multiple of 64 (the router can run as a GEMM)
+TINY_MM = dataclasses.replace(k3gen.TINY, inter=128, n_experts=64)
 
 
 @pytest.fixture(scope="module")
