@@ -119,22 +119,39 @@ __device__ __forceinline__ f32x4 mfma_fp4_fp6(u32x4 a, const uint32_t (&b)[6], u
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 2, 0, (int)sa, 0, (int)sb);
 }
 
-// Round |q| <= 8 to the nearest e2m3 magnitude (ties to even), saturating at 7.5;
-// returns the code (sign in bit 5) and the rounded value.
+// Round |q| < 8 to the nearest e2m3 magnitude (ties to even), saturating at 7.5;
+// returns the code (sign in bit 5) and the rounded value. At or above 1 the value keeps
+// 3 mantissa bits (an fp32 round-to-nearest-even on the bit pattern, whose carry moves
+// into the exponent); below 1 the grid is the multiples of 1/8 (the subnormal codes).
 __device__ __forceinline__ uint32_t e2m3_round(float q, float &rounded) {
   const float a = fabsf(q);
-  const float step = a < 2.f ? 0.125f : (a < 4.f ? 0.25f : 0.5f);
-  float ar = rintf(a / step) * step;
-  ar = fminf(ar, 7.5f);
-  uint32_t code;
-  if (ar < 1.f) {
-    code = (uint32_t)(ar * 8.f);
-  } else {
-    const uint32_t u = __float_as_uint(ar);
-    code = ((((u >> 23) & 255u) - 126u) << 3) | ((u >> 20) & 7u);
+  const uint32_t u = __float_as_uint(a);
+  const float big = fminf(__uint_as_float((u + 0x7FFFFu + ((u >> 20) & 1u)) & 0xFFF00000u), 7.5f);
+  // a * 8 + 2^23 rounds a * 8 to an integer (ties to even) in the low mantissa bits
+  const uint32_t k = __float_as_uint(fmaf(a, 8.f, 8388608.f)) & 15u;  // 0 .. 8
+  // both candidates are computed and blended with a mask (no divergent branch)
+  const uint32_t msk = (uint32_t)-(int32_t)(a < 1.f);
+  const uint32_t code = (k & msk) | (((__float_as_uint(big) >> 20) - (126u << 3)) & ~msk);
+  const uint32_t arb = (__float_as_uint((float)k * 0.125f) & msk) | (__float_as_uint(big) & ~msk);
+  const uint32_t sgn = __float_as_uint(q) & 0x80000000u;
+  rounded = __uint_as_float(arb | sgn);
+  return code | (sgn >> 26);
+}
+
+// One piece of a group: m is the group's largest residual magnitude. The scale puts m in
+// [4, 8) (scale = 2^(floor(log2 m) - 2)); the lane's 8 residuals become codes c and lose
+// the rounded piece, which is exact. Returns the scale exponent.
+__device__ __forceinline__ int fp6_piece(float (&r)[8], float m, uint32_t (&c)[8]) {
+  int e = 0;
+  if (m > 0.f) e = (int)((__float_as_uint(m) >> 23) & 255u) - 127 - 2;
+  e = max(-127, min(127, e));
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float rq;
+    c[i] = e2m3_round(ldexpf(r[i], -e), rq);
+    r[i] -= ldexpf(rq, e);
   }
-  rounded = q < 0.f ? -ar : ar;
-  return code | (q < 0.f ? 32u : 0u);
+  return e;
 }
 
 // Quantize one group of 32 values held by 4 consecutive lanes (8 values each, lane
@@ -150,23 +167,43 @@ __device__ __forceinline__ void quant_group_fp6(float (&r)[8], int k4, uint8_t *
     for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(r[i]));
     m = fmaxf(m, __shfl_xor(m, 1, 4));
     m = fmaxf(m, __shfl_xor(m, 2, 4));
-    int e = 0;
-    if (m > 0.f) e = (int)((__float_as_uint(m) >> 23) & 255u) - 127 - 2;
-    e = max(-127, min(127, e));
+    uint32_t c[8];
+    const int e = fp6_piece(r, m, c);
     uint64_t bits = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float rq;
-      const uint32_t c = e2m3_round(ldexpf(r[i], -e), rq);
-      r[i] -= ldexpf(rq, e);
-      bits |= (uint64_t)c << (6 * i);
-    }
+    for (int i = 0; i < 8; ++i) bits |= (uint64_t)c[i] << (6 * i);
     uint8_t *dst = rec + p * kPieceRec;
     // lane k4's 48 bits are bytes 6*k4 .. 6*k4+5 of the code stream
     *(uint16_t *)(dst + 6 * k4) = (uint16_t)bits;
     *(uint16_t *)(dst + 6 * k4 + 2) = (uint16_t)(bits >> 16);
     *(uint16_t *)(dst + 6 * k4 + 4) = (uint16_t)(bits >> 32);
     if (k4 == 0) dst[24] = (uint8_t)(e + 127);
+  }
+}
+
+// The same for a group laid out as a 16x16 matrix-core result: lanes l, l^16, l^32,
+// l^48 (kq = l / 16) hold the group's values 4kq .. 4kq+3 (r[0..3]) and 16+4kq .. 19+4kq
+// (r[4..7]). rec is the group's record (LDS or global).
+__device__ __forceinline__ void quant_group_fp6_kq(float (&r)[8], int kq, uint8_t *rec) {
+#pragma unroll
+  for (int p = 0; p < kFp6Pieces; ++p) {
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(r[i]));
+    m = fmaxf(m, __shfl_xor(m, 16, 64));
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    uint32_t c[8];
+    const int e = fp6_piece(r, m, c);
+    const uint32_t lo = c[0] | (c[1] << 6) | (c[2] << 12) | (c[3] << 18);  // values 4kq .. 4kq+3
+    const uint32_t hi = c[4] | (c[5] << 6) | (c[6] << 12) | (c[7] << 18);  // values 16+4kq ..
+    uint8_t *dst = rec + p * kPieceRec;
+    dst[3 * kq] = (uint8_t)lo;
+    dst[3 * kq + 1] = (uint8_t)(lo >> 8);
+    dst[3 * kq + 2] = (uint8_t)(lo >> 16);
+    dst[12 + 3 * kq] = (uint8_t)hi;
+    dst[12 + 3 * kq + 1] = (uint8_t)(hi >> 8);
+    dst[12 + 3 * kq + 2] = (uint8_t)(hi >> 16);
+    if (kq == 0) dst[24] = (uint8_t)(e + 127);
   }
 }
 
@@ -194,10 +231,34 @@ __device__ __forceinline__ int block_excl_scan(int v, int *sh_wave, int *total) 
   return base + x - v;
 }
 
+// tanh in fp32 to about 2e-7 relative: below |x| = 0.55 its odd Taylor series through
+// x^17 (next term under 3e-9), above it 1 - 2 / (exp(2|x|) + 1) with the hardware exp2
+// and reciprocal (the relative error stays near that of exp there).
+__device__ __forceinline__ float tanh_f(float x) {
+  const float a = fabsf(x);
+  const float x2 = x * x;
+  float p = 6404582.f / 10854718875.f;
+  p = fmaf(p, x2, -929569.f / 638512875.f);
+  p = fmaf(p, x2, 21844.f / 6081075.f);
+  p = fmaf(p, x2, -1382.f / 155925.f);
+  p = fmaf(p, x2, 62.f / 2835.f);
+  p = fmaf(p, x2, -17.f / 315.f);
+  p = fmaf(p, x2, 2.f / 15.f);
+  p = fmaf(p, x2, -1.f / 3.f);
+  const float series = fmaf(x * x2, p, x);
+  const float e = __builtin_amdgcn_exp2f(2.8853900817779268f * a);  // exp(2a)
+  const float big = copysignf(1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f), x);
+  return a < 0.55f ? series : big;
+}
+
+// logistic 1 / (1 + exp(-g)) with the hardware exp2 and reciprocal
+__device__ __forceinline__ float sigmoid_f(float g) {
+  return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g));
+}
+
 // SiTU-GLU: b1 tanh(g/b1) sigmoid(g) * b2 tanh(u/b2); the sigmoid reads the uncapped g.
 __device__ __forceinline__ float situ(float g, float u, float b1, float b2) {
-  const float gate = b1 * tanhf(g / b1) * (1.0f / (1.0f + expf(-g)));
-  return gate * (b2 * tanhf(u / b2));
+  return (b1 * tanh_f(g * (1.f / b1))) * sigmoid_f(g) * (b2 * tanh_f(u * (1.f / b2)));
 }
 
 }  // namespace k3

@@ -65,9 +65,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (idx >= chunk) return;
   const int t = xcd * chunk + idx;
   if (t >= total) return;
-  const int grp = t / (8 * nN), in = t % (8 * nN);
+  // integer division runs on the vector unit: pin the results to scalar registers
+  const int grp = __builtin_amdgcn_readfirstlane(t / (8 * nN));
+  const int in = t - grp * 8 * nN;
   const int gm = min(8, nM - 8 * grp);  // row blocks in this group
-  const int mb = 8 * grp + in % gm, nb = in / gm;
+  const int nb = __builtin_amdgcn_readfirstlane(in / gm);
+  const int mb = 8 * grp + (in - nb * gm);
   const int n0 = nb * BN;
 
   // ---- this wave's 64 rows: one weight segment (segment boundaries are multiples of 64)
@@ -79,7 +82,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (i < a.nseg && r0 >= a.seg[i].row0) sg = i;
   const DenseSeg &seg = a.seg[sg];
   const int lr0 = r0 - seg.row0;  // first row inside the segment
-  const int nrows = wave_on ? min(64, seg.rows - lr0) : 0;
+  const int nrows = __builtin_amdgcn_readfirstlane(wave_on ? min(64, seg.rows - lr0) : 0);
   const uint32_t rowb = (uint32_t)a.K * 2u;
   const rsrc_t rA = make_rsrc(seg.A + (size_t)lr0 * a.K, (uint32_t)max(nrows, 0) * rowb);
   const rsrc_t rB = make_rsrc(a.B, (uint32_t)(PB * a.plane_elems * 2));

@@ -70,8 +70,7 @@ struct GroupedArgs {
 
 // Grouped GEMM form of the same two passes (many tokens per expert); K % 128 == 0.
 constexpr int kMmBN = 64;      // tokens per column tile
-constexpr int kMmFrags = 16;   // 16-row weight fragments per block
-constexpr int kMmStages = 3;   // LDS ring depth of the weight stream
+constexpr int kMmStages = 3;   // LDS ring depth of the token stream (and weight register ring)
 
 struct MmArgs {
   MxMat A[2];             // gate/up: {w1, w3}; down: {w2}
