@@ -76,6 +76,15 @@ struct Ws {
 
 int g_expert_path = 0;  // k3moe_set_expert_path
 
+// The GEMM form reads its token planes through one 32-bit buffer descriptor: x [T][H]
+// bf16, and the three planes of gamma*acc [T][L] (each padded to 256 bytes).
+bool use_dense_mm(const k3moe_dims *d, int32_t T) {
+  if (T < kDenseMmMinT) return false;
+  const int64_t x_bytes = (int64_t)T * d->hidden * 2;
+  const int64_t np_bytes = 3 * (((int64_t)T * d->latent * 2 + 255) & ~(int64_t)255);
+  return x_bytes < ((int64_t)1 << 31) && np_bytes < ((int64_t)1 << 31);
+}
+
 int64_t max_mm_tiles(const k3moe_dims *d, int32_t T) {
   const int64_t P = (int64_t)T * d->topk;
   return (P + kMmBN - 1) / kMmBN + (P < d->n_experts ? P : d->n_experts);
@@ -121,7 +130,7 @@ Ws carve(const k3moe_dims *d, int32_t T, void *base) {
   w.edn = (float *)take(P * L * 4);
   for (int q = 0; q < 3; ++q) w.np[q] = (uint16_t *)take(t * L * 2);
   w.ss = (float *)take(t * ((L + 255) / 256) * 4);
-  w.wr_planes = T >= kDenseMmMinT ? (uint16_t *)take(3 * E * (size_t)d->hidden * 2) : nullptr;
+  w.wr_planes = use_dense_mm(d, T) ? (uint16_t *)take(3 * E * (size_t)d->hidden * 2) : nullptr;
   w.bytes = o;
   return w;
 }
@@ -162,7 +171,6 @@ hipError_t mark(const char *name, hipStream_t s) {
   } while (0)
 
 // ---- step launchers (arguments already checked)
-bool use_dense_mm(int32_t T) { return T >= kDenseMmMinT; }
 
 // The router's three weight planes (row segments 0..2) and optionally W_down
 // (segment 3), all against x.
@@ -221,7 +229,7 @@ int run_route(const k3moe_dims *d, int32_t T, const uint16_t *x, const float *wr
   // with the latent projection in the same launch, the top-k blocks also quantize z
   int splits = kRouterSplits;
   // the router planes are row segments, which start at multiples of 64 rows
-  if (use_dense_mm(T) && d->n_experts % 64 == 0) {
+  if (use_dense_mm(d, T) && d->n_experts % 64 == 0) {
     K3_TRY(run_route_down_mm(d, T, x, wr, down ? (const uint16_t *)down->A : nullptr, down ? down->out : nullptr,
                              w, s));
     splits = 3;
@@ -238,7 +246,7 @@ int run_route(const k3moe_dims *d, int32_t T, const uint16_t *x, const float *wr
 
 int run_down(const k3moe_dims *d, int32_t T, const uint16_t *x, const uint16_t *wd, float *z,
              hipStream_t s) {
-  if (use_dense_mm(T)) {
+  if (use_dense_mm(d, T)) {
     DenseMmArgs a = {};
     a.seg[0] = DenseSeg{wd, 0, d->latent, z, d->latent};
     a.nseg = 1;
@@ -355,7 +363,7 @@ int run_combine(const k3moe_dims *d, int32_t T, const float *edn, const int32_t 
   K3_HIP(launch_combine(edn, pair_slot, topk_w, norm_w, T, d->topk, d->latent, w.np[0], w.np[1],
                         w.np[2], w.ss, s));
   K3_HIP(mark("combine", s));
-  if (use_dense_mm(T)) {
+  if (use_dense_mm(d, T)) {
     DenseMmArgs a = {};
     a.seg[0] = DenseSeg{w_up, 0, d->hidden, y, d->hidden};
     a.nseg = 1;
