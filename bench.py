@@ -16,6 +16,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -59,6 +60,35 @@ class HipEvents:
     def close(self):
         for h in self.ev:
             self.hip.hipEventDestroy(h)
+
+
+def traffic_from_profile(kernel: str):
+    """HBM-side bytes per launch of `kernel` from the committed counter summary
+    (calibrated FETCH_SIZE + WRITE_SIZE), or None when the kernel sources have changed
+    since the counters were taken (their sha256 is recorded with the figures)."""
+    path = os.path.join(ROOT, "profiles", "expert_gateup_decode_T1_traffic.txt")
+    try:
+        lines = open(path).read().splitlines()
+    except OSError:
+        return None
+    vals, srcs, sha = {}, [], None
+    for line in lines:
+        parts = line.split()
+        if len(parts) == 3 and parts[0] == "traffic_bytes_per_launch":
+            vals[parts[1]] = int(parts[2])
+        elif parts and parts[0] == "kernel_sources":
+            srcs = parts[1:]
+        elif len(parts) == 2 and parts[0] == "kernel_source_sha256":
+            sha = parts[1]
+    h = hashlib.sha256()
+    for src in srcs:
+        try:
+            h.update(open(os.path.join(ROOT, src), "rb").read())
+        except OSError:
+            return None
+    if sha is None or h.hexdigest() != sha:
+        return None
+    return vals.get(kernel)
 
 
 def algorithmic(dims, T, n_distinct):
@@ -203,8 +233,11 @@ def main():
     dom = max(("expert_gateup_situ", "expert_down"), key=lambda n: kern_us.get(n, 0.0))
     dom_bytes = alg["gateup_bytes"] if dom == "expert_gateup_situ" else alg["down_bytes"]
     dom_gbs = dom_bytes / (kern_us[dom] * 1e-6) / 1e9
+    traffic = traffic_from_profile(dom)
     roofline = {"kernel": dom, "bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "traffic_unit": "bytes per launch", "algorithmic_bytes": dom_bytes,
+                "traffic_over_algorithmic": round(traffic / dom_bytes, 4) if traffic else None,
                 "layer_achieved": round(layer_gbs, 1), "layer_frac": round(layer_gbs / HBM_PEAK_GBS, 4),
                 "kernel_us": {k: round(v, 2) for k, v in kern_us.items()}}
 
