@@ -76,6 +76,7 @@ struct Ws {
 
 int g_expert_path = 0;  // k3moe_set_expert_path
 
+
 // The GEMM form reads its token planes through one 32-bit buffer descriptor: x [T][H]
 // bf16, and the three planes of gamma*acc [T][L] (each padded to 256 bytes).
 bool use_dense_mm(const k3moe_dims *d, int32_t T) {
@@ -224,23 +225,78 @@ DenseArgs down_args(const k3moe_dims *d, int32_t T, const uint16_t *x, const uin
 
 // router product (and, when `down` is given, the latent projection in the same launch),
 // then the top-k
+TopkArgs topk_args(const k3moe_dims *d, int32_t T, const float *part, int ks, const float *bias,
+                   int32_t *idx, float *wt) {
+  TopkArgs a = {};
+  a.part = part;
+  a.ks = ks;
+  a.T = T;
+  a.E = d->n_experts;
+  a.bias = bias;
+  a.K = d->topk;
+  a.renorm = d->renorm;
+  a.rscale = d->routed_scale;
+  a.idx = idx;
+  a.w = wt;
+  a.L = d->latent;
+  return a;
+}
+
+// Router and top-k alone (k3moe_route).
 int run_route(const k3moe_dims *d, int32_t T, const uint16_t *x, const float *wr, const float *bias,
-              int32_t *idx, float *wt, const DenseArgs *down, const Ws &w, hipStream_t s) {
-  // with the latent projection in the same launch, the top-k blocks also quantize z
+              int32_t *idx, float *wt, const Ws &w, hipStream_t s) {
   int splits = kRouterSplits;
-  // the router planes are row segments, which start at multiples of 64 rows
   if (use_dense_mm(d, T) && d->n_experts % 64 == 0) {
-    K3_TRY(run_route_down_mm(d, T, x, wr, down ? (const uint16_t *)down->A : nullptr, down ? down->out : nullptr,
-                             w, s));
+    K3_TRY(run_route_down_mm(d, T, x, wr, nullptr, nullptr, w, s));
     splits = 3;
   } else {
-    const DenseArgs a = router_args(d, T, x, wr, w);
-    K3_HIP(launch_route_down(a, kRouterSplits, down, s));
+    K3_HIP(launch_route_down(router_args(d, T, x, wr, w), kRouterSplits, nullptr, s));
   }
-  K3_HIP(mark(down ? "router_and_latent_down" : "router_gemv", s));
-  K3_HIP(launch_topk(w.router_part, splits, T, d->n_experts, bias, d->topk, d->renorm,
-                     d->routed_scale, idx, wt, down ? w.z32 : nullptr, d->latent, w.zq, s));
+  K3_HIP(mark("router_gemv", s));
+  K3_HIP(launch_topk(topk_args(d, T, w.router_part, splits, bias, idx, wt), s));
   K3_HIP(mark("topk", s));
+  return K3MOE_OK;
+}
+
+// The layer's front: router, latent projection z (fp32, w.z32), top-k and dispatch.
+// Returns in *zq_ready whether z's piece records (w.zq) were written too.
+int run_front(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_weights *wt, int32_t *idx,
+              float *tw, const Ws &w, bool *zq_ready, hipStream_t s) {
+  const DenseArgs down = down_args(d, T, x, wt->w_down, w.z32);
+  if (use_dense_mm(d, T) && d->n_experts % 64 == 0) {
+    // GEMM form: router planes and W_down in one launch, then the top-k, whose spare
+    // waves quantize z
+    K3_TRY(run_route_down_mm(d, T, x, wt->w_router, wt->w_down, w.z32, w, s));
+    K3_HIP(mark("router_and_latent_down", s));
+    TopkArgs tk = topk_args(d, T, w.router_part, 3, wt->bias, idx, tw);
+    tk.z = w.z32;
+    tk.zq = w.zq;
+    K3_HIP(launch_topk(tk, s));
+    K3_HIP(mark("topk", s));
+    *zq_ready = true;
+  } else {
+    // GEMV form: the router alone, then W_down streams while other blocks of the same
+    // launch select the experts (and, for one token, dispatch its pairs); z is
+    // quantized once afterwards
+    K3_HIP(launch_route_down(router_args(d, T, x, wt->w_router, w), kRouterSplits, nullptr, s));
+    K3_HIP(mark("router_gemv", s));
+    TopkArgs tk = topk_args(d, T, w.router_part, kRouterSplits, wt->bias, idx, tw);
+    if (T == 1) {
+      tk.expert_off = w.expert_off;
+      tk.sorted_pair = w.sorted_pair;
+      tk.pair_slot = w.pair_slot;
+      tk.active = w.active;
+      tk.counters = w.counters;
+    }
+    K3_HIP(launch_down_topk(down, tk, s));
+    K3_HIP(mark(T == 1 ? "latent_down_topk_dispatch" : "latent_down_topk", s));
+    *zq_ready = false;
+  }
+  if (T != 1) {
+    K3_HIP(launch_dispatch(idx, T, d->topk, d->n_experts, w.expert_off, w.sorted_pair, w.pair_slot,
+                           w.active, w.counters, w.lrank, w.cnt, s));
+    K3_HIP(mark("dispatch", s));
+  }
   return K3MOE_OK;
 }
 
@@ -264,9 +320,11 @@ int run_down(const k3moe_dims *d, int32_t T, const uint16_t *x, const uint16_t *
   return K3MOE_OK;
 }
 
-int run_experts(const k3moe_dims *d, int32_t T, const uint8_t *zq, const k3moe_experts *ex,
+// z: the latent [T][L] fp32; zq_ready: w.zq already holds its piece records.
+int run_experts(const k3moe_dims *d, int32_t T, const float *z, bool zq_ready, const k3moe_experts *ex,
                 const int32_t *expert_off, const int32_t *sorted_pair, const int32_t *active,
                 const int32_t *counters, float *edn, const Ws &w, hipStream_t s) {
+  const uint8_t *zq = w.zq;
   const int64_t P = (int64_t)T * d->topk;
   const bool mm_gu = use_mm(d, T, d->latent, (int64_t)T * d->latent * 4, ex->w1, ex->w3);
   const bool mm_dn = use_mm(d, T, d->inter, P * d->inter * 4, ex->w2, ex->w2);
@@ -281,6 +339,10 @@ int run_experts(const k3moe_dims *d, int32_t T, const uint8_t *zq, const k3moe_e
   const MxMat w1{ex->w1.packed, ex->w1.scales, ex->w1.packed_expert_stride, ex->w1.scales_expert_stride};
   const MxMat w3{ex->w3.packed, ex->w3.scales, ex->w3.packed_expert_stride, ex->w3.scales_expert_stride};
   const MxMat w2{ex->w2.packed, ex->w2.scales, ex->w2.packed_expert_stride, ex->w2.scales_expert_stride};
+  if (!zq_ready) {
+    K3_HIP(launch_quant_rows(z, (size_t)T * d->latent, w.zq, s));
+    K3_HIP(mark("latent_quant", s));
+  }
   if (mm_gu) {
     MmArgs m = {};
     m.A[0] = w1;
@@ -416,7 +478,7 @@ int k3moe_route(const k3moe_dims *d, int32_t T, const uint16_t *x, const float *
   Ws w;
   K3_TRY(check_ws(d, T, ws, ws_bytes, &w));
   if (T == 0) return K3MOE_OK;
-  return run_route(d, T, x, w_router, bias, topk_idx, topk_w, nullptr, w, (hipStream_t)stream);
+  return run_route(d, T, x, w_router, bias, topk_idx, topk_w, w, (hipStream_t)stream);
 }
 
 int k3moe_latent_proj_bf16(const k3moe_dims *d, int32_t T, const uint16_t *x, const uint16_t *w_down,
@@ -459,8 +521,7 @@ int k3moe_expert_glu_mxfp4(const k3moe_dims *d, int32_t T, const float *z, const
   if (T == 0) return K3MOE_OK;
   hipStream_t s = (hipStream_t)stream;
   K3_HIP(launch_active_from_off(expert_off, d->n_experts, w.active, w.counters, s));
-  K3_HIP(launch_quant_rows(z, (size_t)T * d->latent, w.zq, s));
-  return run_experts(d, T, w.zq, ex, expert_off, sorted_pair, w.active, w.counters, edn, w, s);
+  return run_experts(d, T, z, false, ex, expert_off, sorted_pair, w.active, w.counters, edn, w, s);
 }
 
 int k3moe_combine(const k3moe_dims *d, int32_t T, const float *edn, const int32_t *pair_slot,
@@ -493,13 +554,10 @@ int k3moe_layer(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_w
   hipStream_t s = (hipStream_t)stream;
   int32_t *idx = topk_idx_out ? topk_idx_out : w.idx;
   float *tw = topk_w_out ? topk_w_out : w.w;
-  const DenseArgs down = down_args(d, T, x, wt->w_down, w.z32);
-  K3_TRY(run_route(d, T, x, wt->w_router, wt->bias, idx, tw, &down, w, s));
-  K3_HIP(launch_dispatch(idx, T, d->topk, d->n_experts, w.expert_off, w.sorted_pair, w.pair_slot,
-                         w.active, w.counters, w.lrank, w.cnt, s));
-  K3_HIP(mark("dispatch", s));
-  K3_TRY(run_experts(d, T, w.zq, &wt->ex, w.expert_off, w.sorted_pair, w.active, w.counters, w.edn,
-                     w, s));
+  bool zq_ready = false;
+  K3_TRY(run_front(d, T, x, wt, idx, tw, w, &zq_ready, s));
+  K3_TRY(run_experts(d, T, w.z32, zq_ready, &wt->ex, w.expert_off, w.sorted_pair, w.active, w.counters,
+                     w.edn, w, s));
   return run_combine(d, T, w.edn, w.pair_slot, tw, wt->norm_w, wt->w_up, y, w, s);
 }
 

@@ -91,10 +91,25 @@ hipError_t launch_route_down(const DenseArgs &router, int ks, const DenseArgs *d
 hipError_t launch_dense_bf16(const DenseArgs &a, int pieces, int epi, hipStream_t s);
 // pieces 1 with kEpiStore, or 3 with kEpiStoreScaled
 hipError_t launch_dense_mm(const DenseMmArgs &a, int pieces, int epi, hipStream_t s);
-// z (nullable) [T][L] fp32: block t also writes row t's fp6 piece records to zq
-hipError_t launch_topk(const float *part, int ks, int T, int E, const float *bias, int K,
-                       int renorm, float rscale, int32_t *idx, float *w, const float *z, int L,
-                       uint8_t *zq, hipStream_t s);
+// Router top-k of T tokens from ks partial logit arrays [ks][T][E]. Optional: z [T][L]
+// fp32 quantized into zq piece records meanwhile; for T == 1, expert_off .. counters
+// receive that token's dispatch (as launch_dispatch would write it).
+struct TopkArgs {
+  const float *part;
+  int ks, T, E;
+  const float *bias;
+  int K, renorm;
+  float rscale;
+  int32_t *idx;
+  float *w;
+  const float *z;
+  int L;
+  uint8_t *zq;
+  int32_t *expert_off, *sorted_pair, *pair_slot, *active, *counters;
+};
+hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
+// the latent projection (DenseArgs, bf16 weights, kEpiStore) and the top-k in one launch
+hipError_t launch_down_topk(const DenseArgs &d, const TopkArgs &tk, hipStream_t s);
 hipError_t launch_quant_rows(const float *src, size_t n, uint8_t *dst, hipStream_t s);
 hipError_t launch_dispatch(const int32_t *topk_idx, int T, int K, int E, int32_t *expert_off,
                            int32_t *sorted_pair, int32_t *pair_slot, int32_t *active,

@@ -22,7 +22,9 @@ namespace k3 {
 // tokens x PB pieces; the pieces are summed across lanes in the epilogue, so a token
 // costs PB columns. A and B of the next super-step are loaded while the current one
 // is multiplied.
-template <int AF, int PB, int EPI, int WAVES>
+// The weight stream runs one super-step ahead (two register sets in rotation; deeper
+// rings measured no faster for these shapes).
+template <int AF, int PB, int EPI, int WAVES, int DEPTH = 2>
 __device__ __forceinline__ void dense_body(const DenseArgs &a, int rbk, int ks, int nks, int tile) {
   constexpr int TPT = 16 / PB;
   constexpr int ESZ = AF == kA_F32 ? 4 : 2;
@@ -92,13 +94,15 @@ __device__ __forceinline__ void dense_body(const DenseArgs &a, int rbk, int ks, 
     }
   };
   const int nsteps = spw;  // uniform: the same count for every wave of the block
-  Step X, Y;
-  load(w_lo, X);
-  for (int i = 0; i < nsteps; i += 2) {
-    load(w_lo + i + 1, Y);
-    compute(X);
-    load(w_lo + i + 2, X);
-    compute(Y);
+  Step st[DEPTH];
+#pragma unroll
+  for (int d = 0; d + 1 < DEPTH; ++d) load(w_lo + d, st[d]);
+  for (int i = 0; i < nsteps; i += DEPTH) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      load(w_lo + i + d + DEPTH - 1, st[(d + DEPTH - 1) % DEPTH]);
+      compute(st[d]);
+    }
   }
 
   if constexpr (WAVES > 1) {
@@ -204,37 +208,38 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__global__ __launch_bounds__(1024) void k_topk(const float *__restrict__ part, int ks, int T, int E,
-                                               const float *__restrict__ bias, int K, int renorm,
-                                               float rscale, int32_t *__restrict__ idx_out,
-                                               float *__restrict__ w_out, const float *__restrict__ z,
-                                               int L, uint8_t *__restrict__ zq) {
+// One token's top-k with the block's threads (any block size that is a multiple of 64).
+// With a.expert_off set (a batch of one token) the block also writes the dispatch of
+// that token: its K pairs in ascending expert order are the K slots themselves.
+__device__ __forceinline__ void topk_body(const TopkArgs &a, int t) {
   __shared__ float s_sc[1024];
   __shared__ uint32_t s_key[1024];
-  const int t = blockIdx.x, e = threadIdx.x;
-  if (e < E) {
-    // the partial sums were written by blocks on every XCD: issue all loads at once
-    float pv[kMaxRouterSplits];
+  const int E = a.E;
+  for (int e = threadIdx.x; e < 1024; e += blockDim.x) {
+    if (e < E) {
+      // the partial sums were written by blocks on every XCD: issue all loads at once
+      float pv[kMaxRouterSplits];
 #pragma unroll
-    for (int k = 0; k < kMaxRouterSplits; ++k)
-      pv[k] = k < ks ? part[((size_t)k * T + t) * E + e] : 0.f;
-    float logit = 0.f;
+      for (int k = 0; k < kMaxRouterSplits; ++k)
+        pv[k] = k < a.ks ? a.part[((size_t)k * a.T + t) * E + e] : 0.f;
+      float logit = 0.f;
 #pragma unroll
-    for (int k = 0; k < kMaxRouterSplits; ++k) logit += pv[k];
-    const float sgm = 1.0f / (1.0f + expf(-logit));
-    s_sc[e] = sgm;
-    s_key[e] = order_key(sgm + bias[e]);
-  } else {
-    s_sc[e] = 0.f;
-    s_key[e] = 0u;  // below every real key
+      for (int k = 0; k < kMaxRouterSplits; ++k) logit += pv[k];
+      const float sgm = 1.0f / (1.0f + expf(-logit));
+      s_sc[e] = sgm;
+      s_key[e] = order_key(sgm + a.bias[e]);
+    } else {
+      s_sc[e] = 0.f;
+      s_key[e] = 0u;  // below every real key
+    }
   }
   __syncthreads();
-  if (e >= 64) {
+  if (threadIdx.x >= 64) {
     // the other waves meanwhile quantize this token's latent row into fp6 pieces
-    if (z) {
-      const float *zr = z + (size_t)t * L;
-      uint8_t *dst = zq + (size_t)t * (L / 32) * kGroupRec;
-      for (int q = e - 64; q < L / 8; q += blockDim.x - 64) {
+    if (a.z) {
+      const float *zr = a.z + (size_t)t * a.L;
+      uint8_t *dst = a.zq + (size_t)t * (a.L / 32) * kGroupRec;
+      for (int q = threadIdx.x - 64; q < a.L / 8; q += blockDim.x - 64) {
         const float4 lo = *(const float4 *)(zr + 8 * q), hi = *(const float4 *)(zr + 8 * q + 4);
         float rv[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
         quant_group_fp6(rv, q & 3, dst + (q >> 2) * kGroupRec);
@@ -242,7 +247,8 @@ __global__ __launch_bounds__(1024) void k_topk(const float *__restrict__ part, i
     }
     return;
   }
-  const int lane = e;
+  const int K = a.K;
+  const int lane = threadIdx.x;
   uint32_t key[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) key[i] = s_key[lane + 64 * i];
@@ -267,7 +273,7 @@ __global__ __launch_bounds__(1024) void k_topk(const float *__restrict__ part, i
   int eq_before = 0, sel_before = 0;
   float ssum = 0.f;
   bool sel[16];
-  int pos[16];
+  int pos[16];  // chosen experts with a lower id (for every lane, chosen or not)
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const bool eq = key[i] == tau;
@@ -287,16 +293,53 @@ __global__ __launch_bounds__(1024) void k_topk(const float *__restrict__ part, i
     if (sel[i]) {
       const int ee = lane + 64 * i;
       const float sc = s_sc[ee];
-      idx_out[(size_t)t * K + pos[i]] = ee;
-      w_out[(size_t)t * K + pos[i]] = ((renorm && ssum > 0.f) ? sc / ssum : sc) * rscale;
+      a.idx[(size_t)t * K + pos[i]] = ee;
+      a.w[(size_t)t * K + pos[i]] = ((a.renorm && ssum > 0.f) ? sc / ssum : sc) * a.rscale;
+    }
+  }
+  if (a.expert_off) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int ee = lane + 64 * i;
+      if (ee < E) a.expert_off[ee] = pos[i];
+      if (sel[i]) a.active[pos[i]] = ee;
+    }
+    for (int p = lane; p < K; p += 64) {
+      a.sorted_pair[p] = p;
+      a.pair_slot[p] = p;
+    }
+    if (lane == 0) {
+      a.expert_off[E] = K;
+      a.counters[0] = K;
+      a.counters[1] = 0;
     }
   }
 }
 
-hipError_t launch_topk(const float *part, int ks, int T, int E, const float *bias, int K,
-                       int renorm, float rscale, int32_t *idx, float *w, const float *z, int L,
-                       uint8_t *zq, hipStream_t s) {
-  k_topk<<<T, 1024, 0, s>>>(part, ks, T, E, bias, K, renorm, rscale, idx, w, z, L, zq);
+__global__ __launch_bounds__(1024) void k_topk(TopkArgs a) { topk_body(a, blockIdx.x); }
+
+// The latent projection and the top-k in one launch: blocks 0 .. d_rb-1 of every token
+// tile stream W_down, blocks d_rb .. d_rb+T-1 of tile 0 select each token's experts
+// from the router's partial sums (written by the previous launch), concurrently.
+__global__ __launch_bounds__(kRouteDownWaves * 64) void k_down_topk(DenseArgs d, int d_rb, TopkArgs tk) {
+  const int b = blockIdx.x;
+  if (b < d_rb) {
+    dense_body<kA_BF16, 1, kEpiStore, kRouteDownWaves>(d, b, 0, 1, blockIdx.z);
+    return;
+  }
+  if (blockIdx.z != 0) return;
+  topk_body(tk, b - d_rb);
+}
+
+hipError_t launch_down_topk(const DenseArgs &d, const TopkArgs &tk, hipStream_t s) {
+  const int d_rb = (d.M + 15) / 16;
+  dim3 grid(d_rb + tk.T, 1, (d.N + 15) / 16);
+  k_down_topk<<<grid, kRouteDownWaves * 64, 0, s>>>(d, d_rb, tk);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const TopkArgs &a, hipStream_t s) {
+  k_topk<<<a.T, 1024, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -543,6 +586,22 @@ __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
   const int s_lo = kp * spw, s_hi = min(nsup, s_lo + spw);
   const int last_ok = a.ng - 4 * (nsup - 1);  // groups in the last step
 
+  struct Step {
+    u32x4 a[RB];
+    uint32_t s[RB];
+  };
+  auto load = [&](int S, Step &st) {
+    const bool gok = (S < s_hi) && ((S < nsup - 1) || (kq < last_ok));
+    const uint32_t va = gok ? aoff0 : kOOB;
+    const uint32_t Sc = (S < s_hi) ? (uint32_t)S : 0u;
+#pragma unroll
+    for (int r = 0; r < RB; ++r) st.a[r] = bload16(rA, va, Sc * 64u + (uint32_t)r * 16u * rowb);
+  };
+  // the weight stream of the first tile starts before anything is staged
+  Step st[DEPTH];
+#pragma unroll
+  for (int d = 0; d + 1 < DEPTH; ++d) load(s_lo + d, st[d]);
+
   // LDS: scale bytes [NA][64 rows][ng] | staged piece records [TT][ng * 128] (whose bytes
   // after the K loop hold the waves' partial sums, then the SiTU outputs)
   const int sc_bytes = (NA * 64 * (int)ng + 15) & ~15;
@@ -566,17 +625,6 @@ __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
   }
   const uint8_t *sSw = sS + mw * 64 * (int)ng + rl * (int)ng;  // this lane's row of its matrix
 
-  struct Step {
-    u32x4 a[RB];
-    uint32_t s[RB];
-  };
-  auto load = [&](int S, Step &st) {
-    const bool gok = (S < s_hi) && ((S < nsup - 1) || (kq < last_ok));
-    const uint32_t va = gok ? aoff0 : kOOB;
-    const uint32_t Sc = (S < s_hi) ? (uint32_t)S : 0u;
-#pragma unroll
-    for (int r = 0; r < RB; ++r) st.a[r] = bload16(rA, va, Sc * 64u + (uint32_t)r * 16u * rowb);
-  };
   auto load_scales = [&](int S, Step &st) {
     const int g = 4 * S + kq;
     const bool gok = (S < s_hi) && g < a.ng;
@@ -586,9 +634,10 @@ __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
 
   for (int n0 = lo; n0 < hi; n0 += TT) {
     const int ntok = min(TT, hi - n0);
-    Step st[DEPTH];
+    if (n0 != lo) {
 #pragma unroll
-    for (int d = 0; d + 1 < DEPTH; ++d) load(s_lo + d, st[d]);
+      for (int d = 0; d + 1 < DEPTH; ++d) load(s_lo + d, st[d]);
+    }
     // stage the tile's activation piece records (one row of ng * 128 bytes per token)
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
