@@ -537,6 +537,15 @@ __device__ __forceinline__ void stage16(uint8_t *dst, const uint8_t *src, int nb
   }
 }
 
+// s_waitcnt with vmcnt <= n and no wait on the other counters (gfx9 encoding)
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// 16 bytes per lane from a buffer into LDS at lds + 16 * lane (an LDS-destination load)
+__device__ __forceinline__ void dma16(rsrc_t r, uint8_t *lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voff,
+                                           soff, 0, 0);
+}
+
 // ============================================================== grouped MXFP4 (decode)
 #ifndef K3_GATEUP_DEPTH
 #define K3_GATEUP_DEPTH 3
@@ -597,11 +606,6 @@ __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
 #pragma unroll
     for (int r = 0; r < RB; ++r) st.a[r] = bload16(rA, va, Sc * 64u + (uint32_t)r * 16u * rowb);
   };
-  // the weight stream of the first tile starts before anything is staged
-  Step st[DEPTH];
-#pragma unroll
-  for (int d = 0; d + 1 < DEPTH; ++d) load(s_lo + d, st[d]);
-
   // LDS: scale bytes [NA][64 rows][ng] | staged piece records [TT][ng * 128] (whose bytes
   // after the K loop hold the waves' partial sums, then the SiTU outputs)
   const int sc_bytes = (NA * 64 * (int)ng + 15) & ~15;
@@ -610,9 +614,46 @@ __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
   const int brow_bytes = (int)ng * kGroupRec;
   f32x4(*red)[RB][64] = (f32x4(*)[RB][64])sB;
   float *sAct = (float *)(sB + 4 * RB * 64 * 16);  // [TT][64] SiTU outputs of the tile
-  {
+  const int nb = nrb * 16 * (int)ng;  // scale bytes of one matrix for this block's rows
+
+  // When the block's scale rows and token records are whole kilobytes, the memory unit
+  // copies them straight into LDS (buffer loads with an LDS destination) ahead of the
+  // weight stream, and one wait before the K loop covers them.
+  bool dma = (nb % 1024 == 0) && (brow_bytes % 1024 == 0);
+#pragma unroll
+  for (int m = 0; m < NA; ++m)
+    dma = dma && ((((uintptr_t)(a.A[m].scales + (size_t)e * a.A[m].sstride + (size_t)row0 * ng)) & 15) == 0);
+  const int ntok0 = min(TT, hi - lo);
+  int brow0[TT];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt)
+    brow0[tt] = __builtin_amdgcn_readfirstlane(tt < ntok0 ? (a.gather ? a.sorted_pair[lo + tt] / a.topk : lo + tt) : 0);
+  if (dma) {
+    const int nsc = nb / 1024, nbc = brow_bytes / 1024;
+    for (int i = wave; i < NA * nsc; i += 4) {
+      const int m = i / nsc, c = i - m * nsc;
+      const rsrc_t rS = make_rsrc(a.A[m].scales + (size_t)e * a.A[m].sstride + (size_t)row0 * ng, (uint32_t)nb);
+      dma16(rS, sS + m * 64 * (int)ng + c * 1024, (uint32_t)lane * 16u, (uint32_t)c * 1024u);
+    }
+    for (int i = wave; i < ntok0 * nbc; i += 4) {
+      const int tt = i / nbc, c = i - tt * nbc;
+      int br = brow0[0];
+#pragma unroll
+      for (int u = 1; u < TT; ++u) br = tt == u ? brow0[u] : br;
+      const rsrc_t rB = make_rsrc(a.Bq + (size_t)br * brow_bytes, (uint32_t)brow_bytes);
+      dma16(rB, sB + tt * brow_bytes + c * 1024, (uint32_t)lane * 16u, (uint32_t)c * 1024u);
+    }
+  }
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+
+  // the weight stream of the first tile starts before any staged byte is needed
+  Step st[DEPTH];
+#pragma unroll
+  for (int d = 0; d + 1 < DEPTH; ++d) load(s_lo + d, st[d]);
+
+  if (!dma) {
     // the scales depend on the rows only: one coalesced copy per block
-    const int nb = nrb * 16 * (int)ng;
     for (int m = 0; m < NA; ++m) {
       const uint8_t *src = a.A[m].scales + (size_t)e * a.A[m].sstride + (size_t)row0 * ng;
       uint8_t *dst = sS + m * 64 * (int)ng;
@@ -638,13 +679,19 @@ __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
 #pragma unroll
       for (int d = 0; d + 1 < DEPTH; ++d) load(s_lo + d, st[d]);
     }
-    // stage the tile's activation piece records (one row of ng * 128 bytes per token)
+    if (dma && n0 == lo) {
+      // this wave's copies precede exactly the DEPTH-1 steps of weight loads issued since
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(RB * (DEPTH - 1)));
+    } else {
+      // stage the tile's activation piece records (one row of ng * 128 bytes per token)
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-      if (tt < ntok) {
-        const int slot = n0 + tt;
-        const int brow = __builtin_amdgcn_readfirstlane(a.gather ? a.sorted_pair[slot] / a.topk : slot);
-        stage16<4>(sB + tt * brow_bytes, a.Bq + (size_t)brow * brow_bytes, brow_bytes);
+      for (int tt = 0; tt < TT; ++tt) {
+        if (tt < ntok) {
+          const int slot = n0 + tt;
+          const int brow = __builtin_amdgcn_readfirstlane(a.gather ? a.sorted_pair[slot] / a.topk : slot);
+          stage16<4>(sB + tt * brow_bytes, a.Bq + (size_t)brow * brow_bytes, brow_bytes);
+        }
       }
     }
     __syncthreads();
