@@ -33,18 +33,18 @@ namespace k3 {
 namespace {
 
 constexpr int kStageB = kMmBN * 4 * kGroupRec;  // 64 tokens x 4 groups of piece records
-constexpr int kVmPerStep = 4 + 4 + 4;           // A, scale and token copies per step per wave
 
 // s_waitcnt with vmcnt <= n and no wait on the other counters (gfx9 encoding)
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 // Wait until this wave's copies for the step about to be computed have landed (only the
-// kMmStages-2 later steps' loads may still be in flight), then meet the block. Neither
-// the compiler nor the scheduler may move memory accesses across.
+// N_OUT later loads may still be in flight), then meet the block. Neither the compiler
+// nor the scheduler may move memory accesses across.
+template <int N_OUT>
 __device__ __forceinline__ void wait_ring_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm((kMmStages - 2) * kVmPerStep));
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(N_OUT));
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("" ::: "memory");
@@ -73,11 +73,39 @@ __global__ __launch_bounds__(1024) void k_mm_tiles(const int32_t *__restrict__ e
   if (threadIdx.x == 0) *n_tiles = total;
 }
 
-template <int NA, int EPI>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_grouped_mm(MmArgs a) {
-  constexpr int RW = NA == 2 ? 32 : 64;  // rows per wave of each matrix
-  constexpr int BM = 8 * RW;             // rows per block of each matrix
-  constexpr int NS = kMmStages;
+template <int N>
+struct IC {
+  static constexpr int value = N;
+};
+
+__device__ __forceinline__ u32x3 bload12(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x3, __builtin_amdgcn_raw_buffer_load_b96(r, voff, soff, 0));
+}
+
+// The scaled matrix-core step with the A scale taken from byte SEL of sa (the instruction's
+// byte select; the other bytes are ignored) and the B scale from the low byte of sb.
+template <int SEL>
+__device__ __forceinline__ f32x4 mfma_fp4_fp6_sel(u32x4 a, const uint32_t (&b)[6], uint32_t sa,
+                                                  uint32_t sb, f32x4 c) {
+  const i32x8 av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  const i32x8 bv = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], (int)b[4], (int)b[5], 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 2, SEL, (int)sa, 0, (int)sb);
+}
+
+// NWV waves per block: 8 (two waves per SIMD, 4 fragments each) or 4 (one wave per SIMD,
+// 8 fragments each, accumulators in the accumulation registers).
+template <int NA, int EPI, int NWV>
+__global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(NWV / 4, NWV / 4)))
+void k_grouped_mm(MmArgs a) {
+  constexpr int BM = NA == 2 ? 256 : 512;  // rows per block of each matrix
+  constexpr int RW = BM / NWV;             // rows per wave of each matrix
+  constexpr int FPM = RW / 16;             // fragments per matrix per wave
+  constexpr int NF = NA * FPM;             // fragments per wave
+  constexpr int DPW = 32 / NWV;            // token copies per wave per step (32 per block)
+  constexpr int GPW = RW / 32;             // 32-row quantization groups per wave
+  constexpr int VMG = NF + DPW;            // loads of one step: weight fragments, token copies
+  static_assert(RW % 32 == 0, "a wave's rows are whole quantization groups");
+  static_assert(kMmStages == 3, "the ring is unrolled by three steps, one scale triple");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -102,11 +130,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int hi = __builtin_amdgcn_readfirstlane(a.expert_off[e + 1]);
   const int s0 = lo + ct * kMmBN;
   const int ncols = min(kMmBN, hi - s0);
+  const int ncb = __builtin_amdgcn_readfirstlane((ncols + 15) >> 4);  // 16-token column blocks
   const uint32_t rowb = (uint32_t)a.K / 2, ng = (uint32_t)a.ng;
   const int nsteps = a.ng >> 2;
 
-  // ---- this wave's weight rows: fragment i is rows 16 * (i % (4 / NA)) + l % 16 of
-  // matrix i / (4 / NA), counted from rw0
+  // ---- this wave's weight rows: fragment i is rows 16 * (i % FPM) + l % 16 of matrix
+  // i / FPM, counted from rw0
   const int rw0 = rb * BM + RW * wave;
   const int nrw = __builtin_amdgcn_readfirstlane(max(0, min(RW, a.M - rw0)));
   rsrc_t rA[NA], rS[NA];
@@ -115,26 +144,25 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     rA[m] = make_rsrc(a.A[m].packed + (size_t)e * a.A[m].pstride + (size_t)rw0 * rowb, (uint32_t)nrw * rowb);
     rS[m] = make_rsrc(a.A[m].scales + (size_t)e * a.A[m].sstride + (size_t)rw0 * ng, (uint32_t)nrw * ng);
   }
-  constexpr int FPM = 4 / NA;  // fragments per matrix per wave
   // lane part of the offsets; a fragment's 16-row offset is uniform and rides in soffset
   const uint32_t aoff = (uint32_t)rl * rowb + (uint32_t)kq * 16u;
-  const uint32_t soff = (uint32_t)rl * ng + (uint32_t)kq;
+  const uint32_t soff = (uint32_t)rl * ng;
 
-  // ---- token copies: wave w issues copies 4w .. 4w+3; copy j moves tokens 2j (lanes
-  // 0-31) and 2j+1 (lanes 32-63), lane slot i of token t holding its 16-byte chunk
+  // ---- token copies: wave w issues copies DPW*w .. DPW*w+DPW-1; copy j moves tokens 2j
+  // (lanes 0-31) and 2j+1 (lanes 32-63), lane slot i of token t holding its 16-byte chunk
   // (i - t) mod 32 of the step's 512 bytes (4 groups x 4 piece records)
   const uint32_t browb = ng * kGroupRec;
-  uint32_t bsrc[4];
-  int braw[4];
+  uint32_t bsrc[DPW];
+  int braw[DPW];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {  // all four index loads in flight together
-    const int t = 2 * (4 * wave + u) + (lane >> 5);
+  for (int u = 0; u < DPW; ++u) {  // all index loads in flight together
+    const int t = 2 * (DPW * wave + u) + (lane >> 5);
     const int slot = s0 + min(t, ncols - 1);
     braw[u] = a.gather ? a.sorted_pair[slot] : slot;
   }
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int t = 2 * (4 * wave + u) + (lane >> 5);
+  for (int u = 0; u < DPW; ++u) {
+    const int t = 2 * (DPW * wave + u) + (lane >> 5);
     const int c = ((lane & 31) - (t & 15)) & 31;
     const int brow = a.gather ? braw[u] / a.topk : braw[u];
     bsrc[u] = t < ncols ? (uint32_t)brow * browb + (uint32_t)c * 16u : kOOB;
@@ -142,98 +170,150 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const rsrc_t rB = make_rsrc(a.Bq, a.bq_bytes);
 
   struct AStep {
-    u32x4 v[4];
-    uint32_t s[4];
+    u32x4 v[NF];
   };
+  // weight fragments and token copies of step S (zeros past the end)
   auto issue = [&](int S, AStep &as) {
     const bool ok = S < nsteps;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NF; ++i)
       as.v[i] = bload16(rA[i / FPM], aoff, ok ? (uint32_t)S * 64u + (uint32_t)(16 * (i % FPM)) * rowb : kOOB);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      as.s[i] = bload8(rS[i / FPM], soff, ok ? (uint32_t)S * 4u + (uint32_t)(16 * (i % FPM)) * ng : kOOB);
-    uint8_t *stage = smem + (S % NS) * kStageB;
+    uint8_t *stage = smem + (S % kMmStages) * kStageB;
     const uint32_t sb = ok ? (uint32_t)S * (4u * kGroupRec) : kOOB;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) dma16(rB, stage + (4 * wave + u) * 1024, bsrc[u], sb);
+    for (int u = 0; u < DPW; ++u) dma16(rB, stage + (DPW * wave + u) * 1024, bsrc[u], sb);
+  };
+  // Weight scales come three steps at a time: 12 bytes of the lane's row (4 k-blocks of
+  // steps 3j, 3j+1, 3j+2), one load per fragment; the lane keeps byte kq of each step,
+  // which the matrix core then picks by its byte select.
+  u32x3 sraw[NF];
+  auto sissue = [&](int j) {
+    const bool ok = 3 * j < nsteps;
+#pragma unroll
+    for (int i = 0; i < NF; ++i)
+      sraw[i] = bload12(rS[i / FPM], soff, ok ? (uint32_t)j * 12u + (uint32_t)(16 * (i % FPM)) * ng : kOOB);
+  };
+  const uint32_t sel1 = (uint32_t)kq | ((4u + kq) << 8) | 0x0c0c0000u;    // x[kq], y[kq], 0, 0
+  const uint32_t sel2 = 0x0c000100u | ((4u + kq) << 16);                  // t[0], t[1], z[kq], 0
+  uint32_t sp[NF];
+  bool nan_scales = false;
+  auto sperm = [&]() {
+    uint32_t ff = 0;
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+      const uint32_t t = __builtin_amdgcn_perm(sraw[i].y, sraw[i].x, sel1);
+      sp[i] = __builtin_amdgcn_perm(sraw[i].z, t, sel2);
+      const uint32_t n = ~sp[i];  // a byte of n is zero where sp holds the NaN code 0xFF
+      ff |= (n - 0x01010101u) & sp[i] & 0x80808080u;
+    }
+    nan_scales = __builtin_amdgcn_ballot_w64(ff != 0u) != 0;
   };
 
-  f32x4 acc[4][4];
+  f32x4 acc[NF][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NF; ++i)
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[i][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int st, const AStep &as) {
-    const uint8_t *stage = smem + st * kStageB;
-    u32x4 av[4];
-    uint32_t sa[4];
+  // one step on NCB column blocks; D = the step's place in its scale triple. Consecutive
+  // matrix-core instructions update different accumulators (all NCB x NF of them between
+  // two updates of one), so their latency overlaps.
+  auto step = [&](auto dc, auto ncbc, AStep &as) {
+    constexpr int D = decltype(dc)::value;
+    constexpr int NCB = decltype(ncbc)::value;
+    if (nan_scales) {  // rare: a group whose scale is the NaN code contributes zero
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool nan_scale = as.s[i] == 255u;  // the pages' rule: the group is zero
-      av[i] = nan_scale ? u32x4{0, 0, 0, 0} : as.v[i];
-      sa[i] = nan_scale ? 127u : as.s[i];
+      for (int i = 0; i < NF; ++i) {
+        const bool z = ((sp[i] >> (8 * D)) & 255u) == 255u;
+        as.v[i] = z ? u32x4{0, 0, 0, 0} : as.v[i];
+        sp[i] = z ? (sp[i] & ~(255u << (8 * D))) | (127u << (8 * D)) : sp[i];
+      }
     }
+    const uint8_t *stage = smem + D * kStageB;
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      if (16 * cb >= ncols) break;  // uniform: no token in this column block
-      const int t = 16 * cb + rl;
-      const uint8_t *tok = stage + t * 512;
+    for (int p = 0; p < 4; ++p) {
+      const int c0 = kq * 8 + p * 2;
+      uint32_t bw[NCB][6], sb[NCB];
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int c0 = kq * 8 + p * 2;
+      for (int cb = 0; cb < NCB; ++cb) {
+        const uint8_t *tok = stage + (16 * cb + rl) * 512;
         const u32x4 b0 = *(const u32x4 *)(tok + ((c0 + rl) & 31) * 16);
         const u32x3 b1 = *(const u32x3 *)(tok + ((c0 + 1 + rl) & 31) * 16);
-        const uint32_t bw[6] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y};
-        const uint32_t sb = b1.z & 255u;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i][cb] = mfma_fp4_fp6(av[i], bw, sa[i], sb, acc[i][cb]);
+        bw[cb][0] = b0.x; bw[cb][1] = b0.y; bw[cb][2] = b0.z; bw[cb][3] = b0.w;
+        bw[cb][4] = b1.x; bw[cb][5] = b1.y;
+        sb[cb] = b1.z;  // the piece's scale byte (record offset 24) and padding
       }
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int i = 0; i < NF; ++i) acc[i][cb] = mfma_fp4_fp6_sel<D>(as.v[i], bw[cb], sp[i], sb[cb], acc[i][cb]);
     }
   };
 
-  // ---- K loop: weights (registers) and token stages (LDS) run NS-1 steps ahead. Every
-  // step issues the same loads (zeros past the end), so the wait count is exact;
-  // compute of steps past the end is skipped.
-  AStep as[NS];
-#pragma unroll
-  for (int d = 0; d + 1 < NS; ++d) issue(d, as[d]);
-  for (int S0 = 0; S0 < nsteps; S0 += NS) {
-#pragma unroll
-    for (int d = 0; d < NS; ++d) {
-      const int S = S0 + d;
-      wait_ring_barrier();
-      issue(S + NS - 1, as[(d + NS - 1) % NS]);
-      if (S < nsteps && nrw > 0) compute(d, as[d]);
+  // ---- K loop, unrolled by the three ring stages: weights (registers) and token stages
+  // (LDS) run two steps ahead, the scale triple of the next three steps rides with the
+  // loads issued at the triple's first step. Every step issues the same loads (zeros past
+  // the end), so the wait counts are exact; compute of steps past the end is skipped.
+  auto kloop = [&](auto ncbc) {
+    AStep as[3];
+    sissue(0);
+    issue(0, as[0]);
+    // keep each step's loads in issue order, as inside the loop, so the wait counts that
+    // the compiler derives for the first computed step match the loop's own
+    __builtin_amdgcn_sched_barrier(0);
+    issue(1, as[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    const bool on = nrw > 0;
+    for (int S0 = 0; S0 < nsteps; S0 += 3) {
+      wait_ring_barrier<VMG>();  // step S0 landed; S0+1 may be in flight
+      sperm();
+      issue(S0 + 2, as[2]);
+      sissue(S0 / 3 + 1);
+      if (on) step(IC<0>{}, ncbc, as[0]);
+      wait_ring_barrier<VMG + NF>();  // S0+2 (with the next triple) may be in flight
+      issue(S0 + 3, as[0]);
+      if (on && S0 + 1 < nsteps) step(IC<1>{}, ncbc, as[1]);
+      wait_ring_barrier<VMG>();
+      issue(S0 + 4, as[1]);
+      if (on && S0 + 2 < nsteps) step(IC<2>{}, ncbc, as[2]);
     }
+  };
+  switch (ncb) {
+    case 1: kloop(IC<1>{}); break;
+    case 2: kloop(IC<2>{}); break;
+    case 3: kloop(IC<3>{}); break;
+    default: kloop(IC<4>{}); break;
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the ring's last copies land before LDS is reused
   __syncthreads();
 
   if constexpr (EPI == kEpiSitu) {
-    // SiTU of (w1 row, w3 row) pairs in registers; the wave's 32 rows are one group of
-    // each token, quantized into this wave's LDS records, then copied out whole.
-    uint8_t *recs = smem + wave * (kMmBN * kGroupRec);
+    // SiTU of (w1 row, w3 row) pairs in registers; each 32 rows of the wave are one group
+    // of each token, quantized into this wave's LDS records, then copied out whole.
+    uint8_t *recs = smem + wave * (kMmBN * GPW * kGroupRec);  // [token][group] records
     const float b1 = a.b1, b2 = a.b2;
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
-      if (16 * cb >= ncols) break;
-      float v[8];
+      if (cb >= ncb) break;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int g = 0; g < GPW; ++g) {
+        float v[8];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v[4 * i + j] = situ(acc[i][cb][j], acc[i + 2][cb][j], b1, b2);
-      quant_group_fp6_kq(v, kq, recs + (16 * cb + rl) * kGroupRec);
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            v[4 * i + j] = situ(acc[2 * g + i][cb][j], acc[FPM + 2 * g + i][cb][j], b1, b2);
+        quant_group_fp6_kq(v, kq, recs + ((16 * cb + rl) * GPW + g) * kGroupRec);
+      }
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's record bytes are in LDS
     __builtin_amdgcn_wave_barrier();
     const int t = lane;
     if (t < ncols && nrw > 0) {
       uint8_t *dst = a.outq + (size_t)(s0 + t) * (size_t)(a.M / 32) * kGroupRec + (size_t)(rw0 / 32) * kGroupRec;
-#pragma unroll
-      for (int c = 0; c < kGroupRec / 16; ++c)
-        *(u32x4 *)(dst + 16 * c) = *(const u32x4 *)(recs + t * kGroupRec + 16 * c);
+      const int nb = (nrw / 32) * kGroupRec;  // this wave's groups inside M
+      for (int c = 0; c < nb / 16; ++c)
+        *(u32x4 *)(dst + 16 * c) = *(const u32x4 *)(recs + t * GPW * kGroupRec + 16 * c);
     }
   } else {
 #pragma unroll
@@ -242,7 +322,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (t >= ncols) continue;
       float *orow = a.out + (size_t)(s0 + t) * a.M + rw0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < NF; ++i) {
         const int r = 16 * i + 4 * kq;
         if (r < nrw) *(f32x4 *)(orow + r) = acc[i][cb];
       }
@@ -258,34 +338,33 @@ hipError_t launch_mm_tiles(const int32_t *expert_off, int E, int4 *tiles, int32_
   return hipGetLastError();
 }
 
+#ifndef K3_MM_WAVES
+#define K3_MM_WAVES 8
+#endif
+
+template <int NA, int EPI>
+static hipError_t launch_mm_t(const MmArgs &a, unsigned grid, size_t lds, hipStream_t s) {
+  static bool attr = false;
+  if (!attr) {
+    if (hipFuncSetAttribute((const void *)k_grouped_mm<NA, EPI, K3_MM_WAVES>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+      return hipErrorInvalidValue;
+    attr = true;
+  }
+  k_grouped_mm<NA, EPI, K3_MM_WAVES><<<grid, K3_MM_WAVES * 64, lds, s>>>(a);
+  return hipGetLastError();
+}
+
 hipError_t launch_grouped_mm(const MmArgs &a, int epi, int max_tiles, hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
   if (a.ng % 4 != 0) return hipErrorInvalidValue;
-  const int bm = epi == kEpiSitu ? 8 * 32 : 8 * 64;
+  const int bm = epi == kEpiSitu ? 256 : 512;
   const int64_t total = (int64_t)max_tiles * ((a.M + bm - 1) / bm);
   const int64_t grid = 8 * ((total + 7) / 8);
   if (grid > INT32_MAX) return hipErrorInvalidValue;
   const size_t lds = grouped_mm_lds();
-  if (epi == kEpiSitu) {
-    static bool attr = false;
-    if (!attr) {
-      if (hipFuncSetAttribute((const void *)k_grouped_mm<2, kEpiSitu>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-        return hipErrorInvalidValue;
-      attr = true;
-    }
-    k_grouped_mm<2, kEpiSitu><<<(unsigned)grid, 512, lds, s>>>(a);
-  } else {
-    static bool attr = false;
-    if (!attr) {
-      if (hipFuncSetAttribute((const void *)k_grouped_mm<1, kEpiEdn>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-        return hipErrorInvalidValue;
-      attr = true;
-    }
-    k_grouped_mm<1, kEpiEdn><<<(unsigned)grid, 512, lds, s>>>(a);
-  }
-  return hipGetLastError();
+  if (epi == kEpiSitu) return launch_mm_t<2, kEpiSitu>(a, (unsigned)grid, lds, s);
+  return launch_mm_t<1, kEpiEdn>(a, (unsigned)grid, lds, s);
 }
 
 }  // namespace k3

@@ -40,11 +40,11 @@ def check_rows(got: np.ndarray, ref: np.ndarray, what: str, rel=REL, absf=ABSF):
 
 
 class Host:
-    def __init__(self, dims, seed, dense=None):
+    def __init__(self, dims, seed, dense=None, blobs=None):
         self.dims = dims
         self.dense = dense if dense is not None else k3gen.gen_dense(dims, seed)
         self.lay = k3gen.ExpertLayout(dims)
-        self.blobs = k3gen.gen_experts(dims, seed, 0, dims.n_experts)
+        self.blobs = blobs if blobs is not None else k3gen.gen_experts(dims, seed, 0, dims.n_experts)
         self.ex = oracle.ExpertSet(self.blobs, self.lay.blob_bytes, self.lay.offsets)
         B = self.lay.blob_bytes
         chunks = ((e0, self.blobs[e0 * B:min(dims.n_experts, e0 + 64) * B])
@@ -65,6 +65,26 @@ TINY_MM = dataclasses.replace(k3gen.TINY, inter=128, n_experts=64)
 @pytest.fixture(scope="module")
 def tiny_mm():
     return Host(TINY_MM, 0)
+
+
+def nan_scale_blobs(dims, seed, frac=0.03):
+    """Expert blobs with a seeded fraction of every weight-scale tensor set to the ue8m0
+    NaN code 255 (each such 32-column group contributes zero)."""
+    lay = k3gen.ExpertLayout(dims)
+    blobs = k3gen.gen_experts(dims, seed, 0, dims.n_experts).copy()
+    rng = np.random.default_rng(seed + 1000)
+    sizes = dict(lay.sizes)
+    per = blobs.reshape(dims.n_experts, lay.blob_bytes)
+    for name in ("w1s", "w3s", "w2s"):
+        o, n = lay.offsets[name], sizes[name]
+        sel = rng.random((dims.n_experts, n)) < frac
+        per[:, o:o + n][sel] = 255
+    return blobs
+
+
+@pytest.fixture(scope="module")
+def tiny_mm_nan():
+    return Host(TINY_MM, 0, blobs=nan_scale_blobs(TINY_MM, 0))
 
 
 @pytest.fixture
@@ -168,6 +188,16 @@ def test_tiny_layer_ragged_T(tiny, T):
     say(f"tiny layer T={T}")
     x, _ = _inputs.gap_fixed_x(tiny.dims, 100 + T, T, tiny.dense["w_router"], tiny.dense["bias"])
     compare_layer(tiny, x, what=f"tiny T={T}")
+
+
+@pytest.mark.parametrize("mode", [k3moe.EXPERT_PATH_GEMV, k3moe.EXPERT_PATH_GEMM])
+@pytest.mark.parametrize("T", [1, 64, 300])
+def test_tiny_mm_nan_scales_both_expert_forms(tiny_mm_nan, expert_path, mode, T):
+    """Weight groups whose scale byte is the NaN code contribute zero in both forms."""
+    expert_path(mode)
+    say(f"tiny (inter 128) layer with NaN weight scales T={T} expert form {mode}")
+    x, _ = _inputs.gap_fixed_x(TINY_MM, 20 + T, T, tiny_mm_nan.dense["w_router"], tiny_mm_nan.dense["bias"])
+    compare_layer(tiny_mm_nan, x, what=f"nan scales T={T} form {mode}")
 
 
 @pytest.mark.parametrize("mode", [k3moe.EXPERT_PATH_GEMV, k3moe.EXPERT_PATH_GEMM])
