@@ -56,6 +56,10 @@ __device__ __forceinline__ void dma16(rsrc_t r, uint8_t *lds, uint32_t voff, uin
 }
 
 typedef unsigned u32x3 __attribute__((ext_vector_type(3)));
+typedef unsigned u32x6 __attribute__((ext_vector_type(6)));
+typedef int i32x6 __attribute__((ext_vector_type(6)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x32 __attribute__((ext_vector_type(32)));
 
 }  // namespace
 
@@ -134,8 +138,15 @@ void k_grouped_mm(MmArgs a) {
   const uint32_t rowb = (uint32_t)a.K / 2, ng = (uint32_t)a.ng;
   const int nsteps = a.ng >> 2;
 
-  // ---- this wave's weight rows: fragment i is rows 16 * (i % FPM) + l % 16 of matrix
-  // i / FPM, counted from rw0
+  // ---- this wave's weight rows, counted from rw0. Down pass: fragment f of the matrix
+  // is rows 16 f + l % 16. Gate/up pass: the rows of each 32-row group are dealt so that
+  // lane (r, kq) of fragments 2c and 2c+1 computes rows 32c + 8kq + 0..3 and + 4..7: each
+  // lane then holds 8 consecutive activations of a group, which its quantization packs
+  // into 6 consecutive record bytes. Fragment f starts at row frow(f) and lane l reads
+  // row frow(f) + lrow.
+  constexpr bool PERM = EPI == kEpiSitu;
+  const int lrow = PERM ? 8 * (rl >> 2) + (rl & 3) : rl;
+  auto frow = [](int f) { return PERM ? 32 * (f >> 1) + 4 * (f & 1) : 16 * f; };
   const int rw0 = rb * BM + RW * wave;
   const int nrw = __builtin_amdgcn_readfirstlane(max(0, min(RW, a.M - rw0)));
   rsrc_t rA[NA], rS[NA];
@@ -145,8 +156,8 @@ void k_grouped_mm(MmArgs a) {
     rS[m] = make_rsrc(a.A[m].scales + (size_t)e * a.A[m].sstride + (size_t)rw0 * ng, (uint32_t)nrw * ng);
   }
   // lane part of the offsets; a fragment's 16-row offset is uniform and rides in soffset
-  const uint32_t aoff = (uint32_t)rl * rowb + (uint32_t)kq * 16u;
-  const uint32_t soff = (uint32_t)rl * ng;
+  const uint32_t aoff = (uint32_t)lrow * rowb + (uint32_t)kq * 16u;
+  const uint32_t soff = (uint32_t)lrow * ng;
 
   // ---- token copies: wave w issues copies DPW*w .. DPW*w+DPW-1; copy j moves tokens 2j
   // (lanes 0-31) and 2j+1 (lanes 32-63), lane slot i of token t holding its 16-byte chunk
@@ -177,7 +188,7 @@ void k_grouped_mm(MmArgs a) {
     const bool ok = S < nsteps;
 #pragma unroll
     for (int i = 0; i < NF; ++i)
-      as.v[i] = bload16(rA[i / FPM], aoff, ok ? (uint32_t)S * 64u + (uint32_t)(16 * (i % FPM)) * rowb : kOOB);
+      as.v[i] = bload16(rA[i / FPM], aoff, ok ? (uint32_t)S * 64u + (uint32_t)frow(i % FPM) * rowb : kOOB);
     uint8_t *stage = smem + (S % kMmStages) * kStageB;
     const uint32_t sb = ok ? (uint32_t)S * (4u * kGroupRec) : kOOB;
 #pragma unroll
@@ -191,7 +202,7 @@ void k_grouped_mm(MmArgs a) {
     const bool ok = 3 * j < nsteps;
 #pragma unroll
     for (int i = 0; i < NF; ++i)
-      sraw[i] = bload12(rS[i / FPM], soff, ok ? (uint32_t)j * 12u + (uint32_t)(16 * (i % FPM)) * ng : kOOB);
+      sraw[i] = bload12(rS[i / FPM], soff, ok ? (uint32_t)j * 12u + (uint32_t)frow(i % FPM) * ng : kOOB);
   };
   const uint32_t sel1 = (uint32_t)kq | ((4u + kq) << 8) | 0x0c0c0000u;    // x[kq], y[kq], 0, 0
   const uint32_t sel2 = 0x0c000100u | ((4u + kq) << 16);                  // t[0], t[1], z[kq], 0
@@ -288,22 +299,67 @@ void k_grouped_mm(MmArgs a) {
   __syncthreads();
 
   if constexpr (EPI == kEpiSitu) {
-    // SiTU of (w1 row, w3 row) pairs in registers; each 32 rows of the wave are one group
-    // of each token, quantized into this wave's LDS records, then copied out whole.
+    // SiTU of (w1 row, w3 row) pairs in registers: lane (r, kq) holds activations
+    // 32c + 8kq + 0..7 of token 16 cb + r for each of its GPW groups c. Each group becomes
+    // kFp6Pieces piece records in this wave's LDS area (then copied out whole): every
+    // piece takes the residual of the previous ones, scaled by 2^-e so that the group's
+    // largest magnitude lies in [4, 8), rounded to e2m3 (nearest, ties to even,
+    // saturating) by the hardware conversion, 32 values (4 groups) per instruction, and
+    // converted back exactly to form the next residual.
+    constexpr int NG = 4 * GPW;  // groups per lane
     uint8_t *recs = smem + wave * (kMmBN * GPW * kGroupRec);  // [token][group] records
     const float b1 = a.b1, b2 = a.b2;
+    float y[NG][8];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      if (cb >= ncb) break;
+    for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-      for (int g = 0; g < GPW; ++g) {
-        float v[8];
+      for (int g = 0; g < GPW; ++g)
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int j = 0; j < 8; ++j) {
+          const int f = 2 * g + (j >> 2);
+          y[cb * GPW + g][j] = cb < ncb ? situ(acc[f][cb][j & 3], acc[FPM + f][cb][j & 3], b1, b2) : 0.f;
+        }
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            v[4 * i + j] = situ(acc[2 * g + i][cb][j], acc[FPM + 2 * g + i][cb][j], b1, b2);
-        quant_group_fp6_kq(v, kq, recs + ((16 * cb + rl) * GPW + g) * kGroupRec);
+    for (int p = 0; p < kFp6Pieces; ++p) {
+      int ex[NG];
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        float m = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(y[gi][j]));
+        m = fmaxf(m, __shfl_xor(m, 16, 64));
+        m = fmaxf(m, __shfl_xor(m, 32, 64));
+        const int eb = (int)((__float_as_uint(m) >> 23) & 255u) - 127 - 2;
+        ex[gi] = m > 0.f ? max(-127, min(127, eb)) : 0;
+      }
+#pragma unroll
+      for (int bt = 0; bt < NG / 4; ++bt) {
+        f32x16 va, vb;  // value 2i of group q at va[4q + i], value 2i+1 at vb[4q + i]
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            va[4 * q + i] = ldexpf(y[4 * bt + q][2 * i], -ex[4 * bt + q]);
+            vb[4 * q + i] = ldexpf(y[4 * bt + q][2 * i + 1], -ex[4 * bt + q]);
+          }
+        // codes in value order: group q's 8 codes are bits 48q .. 48q+47
+        const u32x6 c = __builtin_bit_cast(u32x6, __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(va, vb, 1.0f));
+        const f32x32 r = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(__builtin_bit_cast(i32x6, c), 1.0f);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int gi = 4 * bt + q, cb = gi / GPW, g = gi % GPW;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) y[gi][j] -= ldexpf(r[8 * q + j], ex[gi]);
+          if (cb < ncb) {
+            uint8_t *dst = recs + ((16 * cb + rl) * GPW + g) * kGroupRec + p * kPieceRec;
+#pragma unroll
+            for (int h = 0; h < 3; ++h) {
+              const int bit = 48 * q + 16 * h;
+              *(uint16_t *)(dst + 6 * kq + 2 * h) = (uint16_t)(c[bit >> 5] >> (bit & 31));
+            }
+            if (kq == 0) dst[24] = (uint8_t)(ex[gi] + 127);
+          }
+        }
       }
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's record bytes are in LDS
