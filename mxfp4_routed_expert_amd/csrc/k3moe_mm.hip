@@ -98,7 +98,7 @@ __device__ __forceinline__ f32x4 mfma_fp4_fp6_sel(u32x4 a, const uint32_t (&b)[6
 
 // NWV waves per block: 8 (two waves per SIMD, 4 fragments each) or 4 (one wave per SIMD,
 // 8 fragments each, accumulators in the accumulation registers).
-template <int NA, int EPI, int NWV>
+template <int NA, int EPI, int NWV, int NS>
 __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(NWV / 4, NWV / 4)))
 void k_grouped_mm(MmArgs a) {
   constexpr int BM = NA == 2 ? 256 : 512;  // rows per block of each matrix
@@ -109,7 +109,7 @@ void k_grouped_mm(MmArgs a) {
   constexpr int GPW = RW / 32;             // 32-row quantization groups per wave
   constexpr int VMG = NF + DPW;            // loads of one step: weight fragments, token copies
   static_assert(RW % 32 == 0, "a wave's rows are whole quantization groups");
-  static_assert(kMmStages == 3, "the ring is unrolled by three steps, one scale triple");
+  static_assert(NS == 3 || NS == 4, "ring depth: one scale load (12 or 16 bytes) per ring turn");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -183,26 +183,36 @@ void k_grouped_mm(MmArgs a) {
   struct AStep {
     u32x4 v[NF];
   };
-  // weight fragments and token copies of step S (zeros past the end)
-  auto issue = [&](int S, AStep &as) {
+  // weight fragments and token copies of step S (zeros past the end), in four parts
+  // that the compute of the current step interleaves with its matrix-core work
+  auto issue_part = [&](int S, AStep &as, int part) {
     const bool ok = S < nsteps;
 #pragma unroll
-    for (int i = 0; i < NF; ++i)
+    for (int i = part * NF / 4; i < (part + 1) * NF / 4; ++i)
       as.v[i] = bload16(rA[i / FPM], aoff, ok ? (uint32_t)S * 64u + (uint32_t)frow(i % FPM) * rowb : kOOB);
-    uint8_t *stage = smem + (S % kMmStages) * kStageB;
+    uint8_t *stage = smem + (S % NS) * kStageB;
     const uint32_t sb = ok ? (uint32_t)S * (4u * kGroupRec) : kOOB;
 #pragma unroll
-    for (int u = 0; u < DPW; ++u) dma16(rB, stage + (DPW * wave + u) * 1024, bsrc[u], sb);
+    for (int u = part * DPW / 4; u < (part + 1) * DPW / 4; ++u)
+      dma16(rB, stage + (DPW * wave + u) * 1024, bsrc[u], sb);
   };
-  // Weight scales come three steps at a time: 12 bytes of the lane's row (4 k-blocks of
-  // steps 3j, 3j+1, 3j+2), one load per fragment; the lane keeps byte kq of each step,
-  // which the matrix core then picks by its byte select.
-  u32x3 sraw[NF];
-  auto sissue = [&](int j) {
-    const bool ok = 3 * j < nsteps;
+  auto issue = [&](int S, AStep &as) {
 #pragma unroll
-    for (int i = 0; i < NF; ++i)
-      sraw[i] = bload12(rS[i / FPM], soff, ok ? (uint32_t)j * 12u + (uint32_t)frow(i % FPM) * ng : kOOB);
+    for (int part = 0; part < 4; ++part) issue_part(S, as, part);
+  };
+  // Weight scales come NS steps at a time: 4 NS bytes of the lane's row (the 4 k-blocks
+  // of each of the ring's NS steps), one load per fragment; the lane keeps byte kq of
+  // each step, which the matrix core then picks by its byte select.
+  typedef unsigned sgrp_t __attribute__((ext_vector_type(NS)));
+  sgrp_t sraw[NF];
+  auto sissue = [&](int j) {
+    const bool ok = NS * j < nsteps;
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+      const uint32_t so = ok ? (uint32_t)j * (4u * NS) + (uint32_t)frow(i % FPM) * ng : kOOB;
+      if constexpr (NS == 3) sraw[i] = bload12(rS[i / FPM], soff, so);
+      else sraw[i] = bload16(rS[i / FPM], soff, so);
+    }
   };
   const uint32_t sel1 = (uint32_t)kq | ((4u + kq) << 8) | 0x0c0c0000u;    // x[kq], y[kq], 0, 0
   const uint32_t sel2 = 0x0c000100u | ((4u + kq) << 16);                  // t[0], t[1], z[kq], 0
@@ -213,7 +223,12 @@ void k_grouped_mm(MmArgs a) {
 #pragma unroll
     for (int i = 0; i < NF; ++i) {
       const uint32_t t = __builtin_amdgcn_perm(sraw[i].y, sraw[i].x, sel1);
-      sp[i] = __builtin_amdgcn_perm(sraw[i].z, t, sel2);
+      if constexpr (NS == 3) {
+        sp[i] = __builtin_amdgcn_perm(sraw[i].z, t, sel2);
+      } else {
+        const uint32_t u = __builtin_amdgcn_perm(sraw[i].w, sraw[i].z, sel1);
+        sp[i] = __builtin_amdgcn_perm(u, t, 0x05040100u);  // t[0], t[1], u[0], u[1]
+      }
       const uint32_t n = ~sp[i];  // a byte of n is zero where sp holds the NaN code 0xFF
       ff |= (n - 0x01010101u) & sp[i] & 0x80808080u;
     }
@@ -226,13 +241,13 @@ void k_grouped_mm(MmArgs a) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[i][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // one step on NCB column blocks; D = the step's place in its scale triple. Consecutive
+  // one step on NCB column blocks; D = the step's place in its scale group. Consecutive
   // matrix-core instructions update different accumulators (all NCB x NF of them between
   // two updates of one), so their latency overlaps.
-  auto step = [&](auto dc, auto ncbc, AStep &as) {
+  auto step = [&](auto dc, auto ncbc, AStep &as, bool work, auto &&mid) {
     constexpr int D = decltype(dc)::value;
     constexpr int NCB = decltype(ncbc)::value;
-    if (nan_scales) {  // rare: a group whose scale is the NaN code contributes zero
+    if (work && nan_scales) {  // rare: a group whose scale is the NaN code contributes zero
 #pragma unroll
       for (int i = 0; i < NF; ++i) {
         const bool z = ((sp[i] >> (8 * D)) & 255u) == 255u;
@@ -243,6 +258,11 @@ void k_grouped_mm(MmArgs a) {
     const uint8_t *stage = smem + D * kStageB;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
+      // a quarter of the loads of a later step, kept after the previous piece's
+      // matrix-core instructions (the scheduler would otherwise hoist them all)
+      if (p > 0) __builtin_amdgcn_sched_barrier(0);
+      mid(p);
+      if (!work) continue;
       const int c0 = kq * 8 + p * 2;
       uint32_t bw[NCB][6], sb[NCB];
 #pragma unroll
@@ -261,32 +281,42 @@ void k_grouped_mm(MmArgs a) {
     }
   };
 
-  // ---- K loop, unrolled by the three ring stages: weights (registers) and token stages
-  // (LDS) run two steps ahead, the scale triple of the next three steps rides with the
-  // loads issued at the triple's first step. Every step issues the same loads (zeros past
+  // ---- K loop, unrolled by the NS ring stages: weights (registers) and token stages
+  // (LDS) run NS-1 steps ahead, the scale group of the next NS steps rides with the
+  // loads issued at the group's first step. Every step issues the same loads (zeros past
   // the end), so the wait counts are exact; compute of steps past the end is skipped.
   auto kloop = [&](auto ncbc) {
-    AStep as[3];
+    AStep as[NS];
     sissue(0);
-    issue(0, as[0]);
-    // keep each step's loads in issue order, as inside the loop, so the wait counts that
-    // the compiler derives for the first computed step match the loop's own
-    __builtin_amdgcn_sched_barrier(0);
-    issue(1, as[1]);
-    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int d = 0; d + 1 < NS; ++d) {
+      issue(d, as[d]);
+      // keep each step's loads in issue order, as inside the loop, so the wait counts
+      // that the compiler derives for the first computed step match the loop's own
+      __builtin_amdgcn_sched_barrier(0);
+    }
     const bool on = nrw > 0;
-    for (int S0 = 0; S0 < nsteps; S0 += 3) {
-      wait_ring_barrier<VMG>();  // step S0 landed; S0+1 may be in flight
-      sperm();
-      issue(S0 + 2, as[2]);
-      sissue(S0 / 3 + 1);
-      if (on) step(IC<0>{}, ncbc, as[0]);
-      wait_ring_barrier<VMG + NF>();  // S0+2 (with the next triple) may be in flight
-      issue(S0 + 3, as[0]);
-      if (on && S0 + 1 < nsteps) step(IC<1>{}, ncbc, as[1]);
-      wait_ring_barrier<VMG>();
-      issue(S0 + 4, as[1]);
-      if (on && S0 + 2 < nsteps) step(IC<2>{}, ncbc, as[2]);
+    for (int S0 = 0; S0 < nsteps; S0 += NS) {
+      // step S0+D: wait until its loads have landed (the NS-2 later groups may still be in
+      // flight, one of them with the next scale group when 1 <= D <= NS-2), then meet
+      auto body = [&](auto dc) {
+        constexpr int D = decltype(dc)::value;
+        wait_ring_barrier<(NS - 2) * VMG + (D >= 1 && D <= NS - 2 ? NF : 0)>();
+        if constexpr (D == 0) sperm();
+        // the loads of step S0+D+NS-1 (and at D = 0 the next scale group) are issued
+        // during this step's compute, a quarter before each piece's matrix-core work, so
+        // the memory pipeline fills while the matrix cores run
+        AStep &nx = as[(D + NS - 1) % NS];
+        const int Sn = S0 + D + NS - 1;
+        step(dc, ncbc, as[D], on && S0 + D < nsteps, [&](int p) {
+          issue_part(Sn, nx, p);
+          if (D == 0 && p == 0) sissue(S0 / NS + 1);
+        });
+      };
+      body(IC<0>{});
+      body(IC<1>{});
+      body(IC<2>{});
+      if constexpr (NS == 4) body(IC<3>{});
     }
   };
   switch (ncb) {
@@ -386,7 +416,11 @@ void k_grouped_mm(MmArgs a) {
   }
 }
 
-size_t grouped_mm_lds() { return (size_t)kMmStages * kStageB; }
+#ifndef K3_MM_STAGES
+#define K3_MM_STAGES 4
+#endif
+
+size_t grouped_mm_lds() { return (size_t)K3_MM_STAGES * kStageB; }
 
 hipError_t launch_mm_tiles(const int32_t *expert_off, int E, int4 *tiles, int32_t *n_tiles, hipStream_t s) {
   if (E > 1024) return hipErrorInvalidValue;
@@ -402,12 +436,12 @@ template <int NA, int EPI>
 static hipError_t launch_mm_t(const MmArgs &a, unsigned grid, size_t lds, hipStream_t s) {
   static bool attr = false;
   if (!attr) {
-    if (hipFuncSetAttribute((const void *)k_grouped_mm<NA, EPI, K3_MM_WAVES>,
+    if (hipFuncSetAttribute((const void *)k_grouped_mm<NA, EPI, K3_MM_WAVES, K3_MM_STAGES>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
       return hipErrorInvalidValue;
     attr = true;
   }
-  k_grouped_mm<NA, EPI, K3_MM_WAVES><<<grid, K3_MM_WAVES * 64, lds, s>>>(a);
+  k_grouped_mm<NA, EPI, K3_MM_WAVES, K3_MM_STAGES><<<grid, K3_MM_WAVES * 64, lds, s>>>(a);
   return hipGetLastError();
 }
 
