@@ -223,6 +223,55 @@ DenseArgs down_args(const k3moe_dims *d, int32_t T, const uint16_t *x, const uin
   return a;
 }
 
+// one-token forms (vector-ALU products over contiguous weight streams)
+constexpr int kRouterParts1 = 2;  // K parts of the one-token router product
+
+Gemv1Args router1_args(const k3moe_dims *d, const uint16_t *x, const float *wr, const Ws &w) {
+  Gemv1Args a = {};
+  a.A = wr;
+  a.M = d->n_experts;
+  a.K = d->hidden;
+  a.ks = kRouterParts1;
+  a.xb = x;
+  a.out = w.router_part;
+  return a;
+}
+
+Gemv1Args down1_args(const k3moe_dims *d, const uint16_t *x, const uint16_t *wd, float *z) {
+  Gemv1Args a = {};
+  a.A = wd;
+  a.M = d->latent;
+  a.K = d->hidden;
+  a.ks = 1;
+  a.xb = x;
+  a.out = z;
+  return a;
+}
+
+Gemv1Args up1_args(const k3moe_dims *d, const uint16_t *w_up, float *y, const Ws &w) {
+  Gemv1Args a = {};
+  a.A = w_up;
+  a.M = d->hidden;
+  a.K = d->latent;
+  a.ks = 1;
+  for (int q = 0; q < 3; ++q) a.xp[q] = w.np[q];
+  a.out = y;
+  a.ss = w.ss;
+  a.nss = (d->latent + 255) / 256;
+  a.eps = d->eps;
+  return a;
+}
+
+bool use_gemv1(const k3moe_dims *d, int32_t T, const uint16_t *x) {
+  (void)x;
+  if (T != 1) return false;
+  Gemv1Args r = {}, dn = {}, up = {};
+  r.M = d->n_experts; r.K = d->hidden; r.ks = kRouterParts1;
+  dn.M = d->latent; dn.K = d->hidden; dn.ks = 1;
+  up.M = d->hidden; up.K = d->latent; up.ks = 1;
+  return gemv1_supported(r, kA_F32) && gemv1_supported(dn, kA_BF16) && gemv1_supported(up, kA_BF16);
+}
+
 // router product (and, when `down` is given, the latent projection in the same launch),
 // then the top-k
 TopkArgs topk_args(const k3moe_dims *d, int32_t T, const float *part, int ks, const float *bias,
@@ -249,6 +298,9 @@ int run_route(const k3moe_dims *d, int32_t T, const uint16_t *x, const float *wr
   if (use_dense_mm(d, T) && d->n_experts % 64 == 0) {
     K3_TRY(run_route_down_mm(d, T, x, wr, nullptr, nullptr, w, s));
     splits = 3;
+  } else if (use_gemv1(d, T, x)) {
+    K3_HIP(launch_gemv1(router1_args(d, x, wr, w), kA_F32, kX_BF16, kEpiStore, 1, s));
+    splits = kRouterParts1;
   } else {
     K3_HIP(launch_route_down(router_args(d, T, x, wr, w), kRouterSplits, nullptr, s));
   }
@@ -274,10 +326,26 @@ int run_front(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_wei
     K3_HIP(launch_topk(tk, s));
     K3_HIP(mark("topk", s));
     *zq_ready = true;
+  } else if (use_gemv1(d, T, x)) {
+    // one token: the router product and W_down stream in one launch; then one block
+    // selects the experts and writes the token's dispatch while its other waves
+    // quantize z
+    K3_HIP(launch_gemv1_front(router1_args(d, x, wt->w_router, w), down1_args(d, x, wt->w_down, w.z32), s));
+    K3_HIP(mark("router_and_latent_down", s));
+    TopkArgs tk = topk_args(d, T, w.router_part, kRouterParts1, wt->bias, idx, tw);
+    tk.expert_off = w.expert_off;
+    tk.sorted_pair = w.sorted_pair;
+    tk.pair_slot = w.pair_slot;
+    tk.active = w.active;
+    tk.counters = w.counters;
+    tk.z = w.z32;
+    tk.zq = w.zq;
+    K3_HIP(launch_topk(tk, s));
+    K3_HIP(mark("topk_dispatch_quant", s));
+    *zq_ready = true;
   } else {
     // GEMV form: the router alone, then W_down streams while other blocks of the same
-    // launch select the experts (and, for one token, dispatch its pairs); z is
-    // quantized once afterwards
+    // launch select the experts; z is quantized once afterwards
     K3_HIP(launch_route_down(router_args(d, T, x, wt->w_router, w), kRouterSplits, nullptr, s));
     K3_HIP(mark("router_gemv", s));
     TopkArgs tk = topk_args(d, T, w.router_part, kRouterSplits, wt->bias, idx, tw);
@@ -312,6 +380,8 @@ int run_down(const k3moe_dims *d, int32_t T, const uint16_t *x, const uint16_t *
     a.B = x;
     a.plane_elems = (int64_t)T * d->hidden;
     K3_HIP(launch_dense_mm(a, 1, kEpiStore, s));
+  } else if (use_gemv1(d, T, x)) {
+    K3_HIP(launch_gemv1(down1_args(d, x, wd, z), kA_BF16, kX_BF16, kEpiStore, 1, s));
   } else {
     const DenseArgs a = down_args(d, T, x, wd, z);
     K3_HIP(launch_dense_bf16(a, 1, kEpiStore, s));
@@ -438,6 +508,8 @@ int run_combine(const k3moe_dims *d, int32_t T, const float *edn, const int32_t 
     a.nss = (d->latent + 255) / 256;
     a.eps = d->eps;
     K3_HIP(launch_dense_mm(a, kPieces, kEpiStoreScaled, s));
+  } else if (use_gemv1(d, T, nullptr)) {
+    K3_HIP(launch_gemv1(up1_args(d, w_up, y, w), kA_BF16, kX_PLANES, kEpiStoreScaled, 2, s));
   } else {
     DenseArgs a = {};
     a.A = w_up;

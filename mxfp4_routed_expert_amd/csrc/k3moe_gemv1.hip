@@ -1,0 +1,254 @@
+// Dense products of one token (decode): the router logits, the latent down-projection
+// and the RMSNormed up-projection, y[m] = sum_k A[m][k] * x[k], on the vector ALUs.
+//
+// With one token the matrix cores have nothing to reuse, so the weights are streamed
+// in the order that suits HBM: a wave owns RPW whole rows (or a K part of a row), and
+// each of its load instructions reads 1 KB of contiguous row bytes (lane l: bytes
+// 16l .. 16l+15), all of the wave's loads in flight at once. A lane multiplies its 16
+// bytes (8 bf16 or 4 fp32 weights) with the matching activations, which the block
+// stages once in LDS as fp32, by fused multiply-adds (one rounding each), and the wave
+// sums its 64 lanes at the end. Each wave's rows and K part are chosen so that the
+// launch is one block per compute unit with equal work in every block.
+#include "k3moe_common.h"
+#include "k3moe_kernels.h"
+#include "k3moe_topk.h"
+
+namespace k3 {
+
+namespace {
+
+constexpr int kG1MaxChunks = 16;  // 1 KB loads in flight per wave
+
+// bf16 bits -> fp32 (exact)
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Stage x (the K activations, fp32) in LDS: from bf16, or as the exact sum of three bf16
+// planes. Each thread converts 8 consecutive values from one 16-byte load per source.
+template <int XF>
+__device__ __forceinline__ void stage_x(const Gemv1Args &a, float *sx) {
+  for (int q = threadIdx.x; q < a.K / 8; q += blockDim.x) {
+    float v[8];
+    if constexpr (XF == kX_BF16) {
+      const u32x4 b = *(const u32x4 *)(a.xb + 8 * q);
+      const uint32_t w[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { v[2 * i] = bf_lo(w[i]); v[2 * i + 1] = bf_hi(w[i]); }
+    } else {
+      const u32x4 b0 = *(const u32x4 *)(a.xp[0] + 8 * q);
+      const u32x4 b1 = *(const u32x4 *)(a.xp[1] + 8 * q);
+      const u32x4 b2 = *(const u32x4 *)(a.xp[2] + 8 * q);
+      const uint32_t w0[4] = {b0.x, b0.y, b0.z, b0.w}, w1[4] = {b1.x, b1.y, b1.z, b1.w},
+                     w2[4] = {b2.x, b2.y, b2.z, b2.w};
+      // the planes are the exact pieces of one fp32 value
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = (bf_lo(w0[i]) + bf_lo(w1[i])) + bf_lo(w2[i]);
+        v[2 * i + 1] = (bf_hi(w0[i]) + bf_hi(w1[i])) + bf_hi(w2[i]);
+      }
+    }
+    *(float4 *)(sx + 8 * q) = float4{v[0], v[1], v[2], v[3]};
+    *(float4 *)(sx + 8 * q + 4) = float4{v[4], v[5], v[6], v[7]};
+  }
+}
+
+// One wave item: rows row0 .. row0+RPW-1 over the columns of K part `part`. The
+// weight loads of the first batch are issued before the block stages x (they do not
+// depend on it); `staged` runs the staging and the block barrier.
+template <int AF, int EPI, int RPW, typename Stage>
+__device__ __forceinline__ void gemv1_item(const Gemv1Args &a, float *sx, int item, bool live, float scale,
+                                           Stage &&staged) {
+  constexpr int ESZ = AF == kA_F32 ? 4 : 2;
+  constexpr int VPL = 16 / ESZ;  // weights per lane per load
+  constexpr int NC = kG1MaxChunks / RPW;
+  const int lane = threadIdx.x & 63;
+  // integer division runs on the vector unit: pin the results to scalar registers, so
+  // the buffer descriptors stay scalar
+  const int kp = __builtin_amdgcn_readfirstlane(a.K / a.ks);  // columns per part
+  const int part = __builtin_amdgcn_readfirstlane(item % a.ks);
+  const int row0 = __builtin_amdgcn_readfirstlane((item / a.ks) * RPW);
+  const int k0 = part * kp;
+  const uint32_t slice = (uint32_t)kp * ESZ;  // bytes of one row part
+  const int nchunk = live ? (int)((slice + 1023) / 1024) : 0;
+  rsrc_t rA[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int row = row0 + r;
+    rA[r] = make_rsrc((const uint8_t *)a.A + ((size_t)min(row, a.M - 1) * a.K + k0) * ESZ,
+                      (live && row < a.M) ? slice : 0u);
+  }
+  u32x4 w[RPW][NC];
+  auto load = [&](int c0) {
+    // every load of the batch before any arithmetic: the row bytes stream back to back
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        w[r][c] = bload16(rA[r], (uint32_t)lane * 16u, c0 + c < nchunk ? (uint32_t)(c0 + c) * 1024u : kOOB);
+  };
+  float acc[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) acc[r] = 0.f;
+  load(0);
+  staged();
+  for (int c0 = 0; c0 < nchunk; c0 += NC) {
+    if (c0 > 0) load(c0);
+    // (chunks past nchunk were loaded as zeros and meet zero activations)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int e0 = ((c0 + c) * 1024 + lane * 16) / ESZ;  // first column of the lane's bytes
+      const bool in = e0 < kp;
+      const float *xs = sx + k0 + (in ? e0 : 0);
+      float xv[VPL];
+#pragma unroll
+      for (int i = 0; i < VPL; i += 4) {
+        const float4 t = *(const float4 *)(xs + i);
+        xv[i] = in ? t.x : 0.f; xv[i + 1] = in ? t.y : 0.f;
+        xv[i + 2] = in ? t.z : 0.f; xv[i + 3] = in ? t.w : 0.f;
+      }
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        const u32x4 q = w[r][c];
+        if constexpr (AF == kA_F32) {
+          acc[r] = fmaf(__uint_as_float(q.x), xv[0], acc[r]);
+          acc[r] = fmaf(__uint_as_float(q.y), xv[1], acc[r]);
+          acc[r] = fmaf(__uint_as_float(q.z), xv[2], acc[r]);
+          acc[r] = fmaf(__uint_as_float(q.w), xv[3], acc[r]);
+        } else {
+          acc[r] = fmaf(bf_lo(q.x), xv[0], acc[r]);
+          acc[r] = fmaf(bf_hi(q.x), xv[1], acc[r]);
+          acc[r] = fmaf(bf_lo(q.y), xv[2], acc[r]);
+          acc[r] = fmaf(bf_hi(q.y), xv[3], acc[r]);
+          acc[r] = fmaf(bf_lo(q.z), xv[4], acc[r]);
+          acc[r] = fmaf(bf_hi(q.z), xv[5], acc[r]);
+          acc[r] = fmaf(bf_lo(q.w), xv[6], acc[r]);
+          acc[r] = fmaf(bf_hi(q.w), xv[7], acc[r]);
+        }
+      }
+    }
+  }
+  if (!live) return;
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const float v = wave_sum(acc[r]);
+    const int row = row0 + r;
+    if (lane == 0 && row < a.M) {
+      if constexpr (EPI == kEpiStore) a.out[(size_t)part * a.M + row] = v;
+      else a.out[row] = v * scale;
+    }
+  }
+}
+
+// RMSNorm factor 1 / sqrt(mean(acc^2) + eps) from the partial sums of squares
+__device__ __forceinline__ float rms_inv(const Gemv1Args &a) {
+  float ss = 0.f;
+  for (int i = 0; i < a.nss; ++i) ss += a.ss[i];
+  return 1.0f / sqrtf(ss / (float)a.K + a.eps);
+}
+
+template <int AF, int XF, int EPI, int RPW>
+__global__ __launch_bounds__(1024) void k_gemv1(Gemv1Args a, int items) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  float *sx = (float *)smem;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int item = blockIdx.x * (blockDim.x >> 6) + wave;
+  const bool live = item < items;  // every wave takes part in the staging
+  const float scale = EPI == kEpiStoreScaled ? rms_inv(a) : 1.f;
+  gemv1_item<AF, EPI, RPW>(a, sx, live ? item : 0, live, scale, [&] {
+    stage_x<XF>(a, sx);
+    __syncthreads();
+  });
+}
+
+// The router product and the latent down-projection of one token in one launch (both
+// read only x): wave items [0, r_items) are router row parts, the rest W_down rows. The
+// two kinds of item stream the same number of bytes. Every wave reaches exactly one
+// block barrier, inside the staging of whichever branch it takes (the branch is
+// uniform per wave).
+__global__ __launch_bounds__(1024) void k_gemv1_front(Gemv1Args r, Gemv1Args d, int r_items, int items) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  float *sx = (float *)smem;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int item = blockIdx.x * (blockDim.x >> 6) + wave;
+  auto staged = [&] {
+    stage_x<kX_BF16>(d, sx);
+    __syncthreads();
+  };
+  if (item < r_items) {
+    gemv1_item<kA_F32, kEpiStore, 1>(r, sx, item, true, 1.f, staged);
+  } else {
+    const bool live = item < items;
+    gemv1_item<kA_BF16, kEpiStore, 1>(d, sx, live ? item - r_items : 0, live, 1.f, staged);
+  }
+}
+
+int num_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Waves per block for `items` equal wave items: the per-unit share, or its largest
+// divisor up to 16 (so whole blocks divide evenly over the compute units).
+int gemv1_waves(int items) {
+  const int per = (items + num_cus() - 1) / num_cus();
+  if (per <= 16) return per < 1 ? 1 : per;
+  for (int w = 16; w >= 4; --w)
+    if (per % w == 0) return w;
+  return 16;
+}
+
+bool gemv1_ok(const Gemv1Args &a, int esz) {
+  if (a.M <= 0 || a.K <= 0 || a.K % 8 != 0 || a.ks < 1 || a.K % a.ks != 0) return false;
+  const int kp = a.K / a.ks;
+  // 16-byte aligned row parts; x fits the LDS
+  return ((size_t)kp * esz) % 16 == 0 && ((size_t)a.K * esz) % 16 == 0 && (size_t)a.K * 4 <= 65536 &&
+         ((size_t)a.M * a.K * esz) < ((size_t)1 << 40);
+}
+
+}  // namespace
+
+bool gemv1_supported(const Gemv1Args &a, int af) { return gemv1_ok(a, af == kA_F32 ? 4 : 2); }
+
+hipError_t launch_gemv1(const Gemv1Args &a, int af, int xf, int epi, int rpw, hipStream_t s) {
+  if (!gemv1_ok(a, af == kA_F32 ? 4 : 2) || (rpw != 1 && rpw != 2)) return hipErrorInvalidValue;
+  const int items = ((a.M + rpw - 1) / rpw) * a.ks;
+  const int waves = gemv1_waves(items);
+  const int grid = (items + waves - 1) / waves;
+  const size_t lds = (size_t)a.K * 4;
+#define G1(AF_, XF_, EPI_, R_) \
+  if (af == AF_ && xf == XF_ && epi == EPI_ && rpw == R_) { \
+    k_gemv1<AF_, XF_, EPI_, R_><<<grid, waves * 64, lds, s>>>(a, items); \
+    return hipGetLastError(); \
+  }
+  G1(kA_F32, kX_BF16, kEpiStore, 1)
+  G1(kA_BF16, kX_BF16, kEpiStore, 1)
+  G1(kA_BF16, kX_PLANES, kEpiStoreScaled, 1)
+  G1(kA_BF16, kX_PLANES, kEpiStoreScaled, 2)
+#undef G1
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemv1_front(const Gemv1Args &r, const Gemv1Args &d, hipStream_t s) {
+  // one x for both; the item kinds must stream the same bytes for the blocks to balance
+  if (!gemv1_ok(r, 4) || !gemv1_ok(d, 2) || r.K != d.K || r.xb != d.xb || d.ks != 1) return hipErrorInvalidValue;
+  const int r_items = r.M * r.ks, items = r_items + d.M;
+  const int waves = gemv1_waves(items);
+  const int grid = (items + waves - 1) / waves;
+  k_gemv1_front<<<grid, waves * 64, (size_t)d.K * 4, s>>>(r, d, r_items, items);
+  return hipGetLastError();
+}
+
+}  // namespace k3

@@ -48,6 +48,22 @@ struct DenseMmArgs {
   float eps;
 };
 
+// One token's dense product on the vector ALUs: out = A x, A [M][K] (bf16 or fp32),
+// x [K] as bf16 (kX_BF16) or as three bf16 planes summing to the fp32 value (kX_PLANES).
+// K is cut into ks parts; kEpiStore writes the part products out[part][M], kEpiStoreScaled
+// (ks = 1) writes out[m] / sqrt(sum(ss)/K + eps).
+enum XFormat { kX_BF16 = 0, kX_PLANES = 1 };
+struct Gemv1Args {
+  const void *A;
+  int M, K, ks;
+  const uint16_t *xb;
+  const uint16_t *xp[3];
+  float *out;
+  const float *ss;
+  int nss;
+  float eps;
+};
+
 // ---------------------------------------------------------------- grouped MXFP4
 struct MxMat {
   const uint8_t *packed;
@@ -108,6 +124,13 @@ struct TopkArgs {
   int32_t *expert_off, *sorted_pair, *pair_slot, *active, *counters;
 };
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
+// one token: af kA_BF16/kA_F32, xf kX_BF16/kX_PLANES, epi kEpiStore/kEpiStoreScaled, rpw
+// rows per wave (1 or 2)
+bool gemv1_supported(const Gemv1Args &a, int af);
+hipError_t launch_gemv1(const Gemv1Args &a, int af, int xf, int epi, int rpw, hipStream_t s);
+// the router product (fp32 weights, kEpiStore, its K parts) and the latent projection
+// (bf16 weights, ks = 1) of one token, same x, in one launch
+hipError_t launch_gemv1_front(const Gemv1Args &r, const Gemv1Args &d, hipStream_t s);
 // the latent projection (DenseArgs, bf16 weights, kEpiStore) and the top-k in one launch
 hipError_t launch_down_topk(const DenseArgs &d, const TopkArgs &tk, hipStream_t s);
 hipError_t launch_quant_rows(const float *src, size_t n, uint8_t *dst, hipStream_t s);

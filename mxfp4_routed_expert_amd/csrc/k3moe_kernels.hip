@@ -13,6 +13,7 @@
 // and B use the same one; this one makes every lane's loads 16..128 contiguous bytes.
 #include "k3moe_common.h"
 #include "k3moe_kernels.h"
+#include "k3moe_topk.h"
 
 namespace k3 {
 
@@ -196,127 +197,17 @@ hipError_t launch_dense_bf16(const DenseArgs &a, int pieces, int epi, hipStream_
 }
 
 // ============================================================== router top-k
-// One block per token. Its threads turn the partial logits into unbiased scores
-// sc = sigmoid(logit) and selection scores ch = sc + bias, kept in LDS as ch's
-// order-preserving 32-bit key. Wave 0 then finds the K-th largest key by a binary
-// search on the key bits (each probe counts keys >= the probe with ballots), takes every
-// expert above it plus, among those equal to it, the lowest ids (so equal selection
-// scores go to the lower id), and writes the chosen ids in ascending order with their
-// unbiased scores renormalised over the chosen and times routed_scale.
-__device__ __forceinline__ uint32_t order_key(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// One token's top-k with the block's threads (any block size that is a multiple of 64).
-// With a.expert_off set (a batch of one token) the block also writes the dispatch of
-// that token: its K pairs in ascending expert order are the K slots themselves.
-__device__ __forceinline__ void topk_body(const TopkArgs &a, int t) {
-  __shared__ float s_sc[1024];
-  __shared__ uint32_t s_key[1024];
-  const int E = a.E;
-  for (int e = threadIdx.x; e < 1024; e += blockDim.x) {
-    if (e < E) {
-      // the partial sums were written by blocks on every XCD: issue all loads at once
-      float pv[kMaxRouterSplits];
-#pragma unroll
-      for (int k = 0; k < kMaxRouterSplits; ++k)
-        pv[k] = k < a.ks ? a.part[((size_t)k * a.T + t) * E + e] : 0.f;
-      float logit = 0.f;
-#pragma unroll
-      for (int k = 0; k < kMaxRouterSplits; ++k) logit += pv[k];
-      const float sgm = 1.0f / (1.0f + expf(-logit));
-      s_sc[e] = sgm;
-      s_key[e] = order_key(sgm + a.bias[e]);
-    } else {
-      s_sc[e] = 0.f;
-      s_key[e] = 0u;  // below every real key
-    }
-  }
-  __syncthreads();
-  if (threadIdx.x >= 64) {
-    // the other waves meanwhile quantize this token's latent row into fp6 pieces
-    if (a.z) {
-      const float *zr = a.z + (size_t)t * a.L;
-      uint8_t *dst = a.zq + (size_t)t * (a.L / 32) * kGroupRec;
-      for (int q = threadIdx.x - 64; q < a.L / 8; q += blockDim.x - 64) {
-        const float4 lo = *(const float4 *)(zr + 8 * q), hi = *(const float4 *)(zr + 8 * q + 4);
-        float rv[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        quant_group_fp6(rv, q & 3, dst + (q >> 2) * kGroupRec);
-      }
-    }
+// (topk_body: k3moe_topk.h)
+// Blocks 0 .. T-1: one token's top-k each; the blocks after them (when a.z is set)
+// quantize z [T][L] into its piece records.
+__global__ __launch_bounds__(1024) void k_topk(TopkArgs a) {
+  if ((int)blockIdx.x < a.T) {
+    topk_body(a, blockIdx.x);
     return;
   }
-  const int K = a.K;
-  const int lane = threadIdx.x;
-  uint32_t key[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) key[i] = s_key[lane + 64 * i];
-  auto count_ge = [&](uint32_t v) {
-    int c = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) c += __popcll(__ballot(key[i] >= v));
-    return c;
-  };
-  // largest v with count(key >= v) >= K: the K-th largest key
-  uint32_t tau = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = tau | (1u << bit);
-    if (count_ge(cand) >= K) tau = cand;
-  }
-  int n_gt = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) n_gt += __popcll(__ballot(key[i] > tau));
-  const int need_eq = K - n_gt;
-  // ascending expert id e = lane + 64 i: i-major, then lane
-  const unsigned long long below = (1ull << lane) - 1ull;
-  int eq_before = 0, sel_before = 0;
-  float ssum = 0.f;
-  bool sel[16];
-  int pos[16];  // chosen experts with a lower id (for every lane, chosen or not)
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const bool eq = key[i] == tau;
-    const unsigned long long eqm = __ballot(eq);
-    const int eq_rank = eq_before + __popcll(eqm & below);
-    sel[i] = key[i] > tau || (eq && eq_rank < need_eq);
-    eq_before += __popcll(eqm);
-    const unsigned long long sm = __ballot(sel[i]);
-    pos[i] = sel_before + __popcll(sm & below);
-    sel_before += __popcll(sm);
-    if (sel[i]) ssum += s_sc[lane + 64 * i];
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) ssum += __shfl_xor(ssum, off, 64);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    if (sel[i]) {
-      const int ee = lane + 64 * i;
-      const float sc = s_sc[ee];
-      a.idx[(size_t)t * K + pos[i]] = ee;
-      a.w[(size_t)t * K + pos[i]] = ((a.renorm && ssum > 0.f) ? sc / ssum : sc) * a.rscale;
-    }
-  }
-  if (a.expert_off) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int ee = lane + 64 * i;
-      if (ee < E) a.expert_off[ee] = pos[i];
-      if (sel[i]) a.active[pos[i]] = ee;
-    }
-    for (int p = lane; p < K; p += 64) {
-      a.sorted_pair[p] = p;
-      a.pair_slot[p] = p;
-    }
-    if (lane == 0) {
-      a.expert_off[E] = K;
-      a.counters[0] = K;
-      a.counters[1] = 0;
-    }
-  }
+  const int q = ((int)blockIdx.x - a.T) * blockDim.x + threadIdx.x;
+  if (q < a.T * (a.L / 8)) quant_task(a.z, a.zq, q);  // whole 4-lane groups (L % 32 == 0)
 }
-
-__global__ __launch_bounds__(1024) void k_topk(TopkArgs a) { topk_body(a, blockIdx.x); }
 
 // The latent projection and the top-k in one launch: blocks 0 .. d_rb-1 of every token
 // tile stream W_down, blocks d_rb .. d_rb+T-1 of tile 0 select each token's experts
@@ -339,7 +230,10 @@ hipError_t launch_down_topk(const DenseArgs &d, const TopkArgs &tk, hipStream_t 
 }
 
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s) {
-  k_topk<<<a.T, 1024, 0, s>>>(a);
+  const int64_t tasks = a.z ? (int64_t)a.T * (a.L / 8) : 0;
+  const int64_t grid = a.T + (tasks + 1023) / 1024;
+  if (grid > INT32_MAX || tasks > INT32_MAX) return hipErrorInvalidValue;
+  k_topk<<<(unsigned)grid, 1024, 0, s>>>(a);
   return hipGetLastError();
 }
 
