@@ -142,7 +142,7 @@ hipError_t launch_active_from_off(const int32_t *expert_off, int E, int32_t *act
 hipError_t launch_split_planes(const float *src, size_t n, uint16_t *p0, uint16_t *p1,
                                uint16_t *p2, hipStream_t s);
 // tokens_per_tile: 1, 2 or 4 tokens' piece records staged in LDS per tile (grouped_dec_lds bytes)
-constexpr size_t kMaxBlockLds = 65536;
+constexpr size_t kMaxBlockLds = 81920;  // two blocks per compute unit
 size_t grouped_dec_lds(int K, int tokens_per_tile);
 hipError_t launch_grouped(const GroupedArgs &a, int epi, int tokens_per_tile, int grid_y, hipStream_t s);
 // column tiles of kMmBN slots per expert: at most ceil(P / kMmBN) + min(E, P) entries

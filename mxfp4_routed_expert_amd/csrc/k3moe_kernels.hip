@@ -442,22 +442,37 @@ __device__ __forceinline__ void dma16(rsrc_t r, uint8_t *lds, uint32_t voff, uin
 
 // ============================================================== grouped MXFP4 (decode)
 #ifndef K3_GATEUP_DEPTH
-#define K3_GATEUP_DEPTH 3
+#define K3_GATEUP_DEPTH 2
 #endif
 #ifndef K3_DOWN_DEPTH
-#define K3_DOWN_DEPTH 3
+#define K3_DOWN_DEPTH 2
 #endif
 // Grid: x = 64-row blocks, y = active-expert slots. The block's four waves share the
 // same 64 rows (four 16-row blocks). With one matrix (down) the waves split K four
 // ways; with two (gate w1 and up w3) waves 0-1 stream w1 and waves 2-3 stream w3, each
 // pair splitting K in halves. Partial sums meet in LDS, where wave w finishes row block
 // w (SiTU pairs the gate and up sums of the same row and token there).
-// The weights enter the matrix cores as stored: each lane's 16 packed bytes of one
-// 32-column group are the MXFP4 operand and the group's scale byte is its scale. The
-// activations enter as fp6 pieces: the 16 columns of a step are TT tokens x 4 pieces,
-// summed across lanes in the epilogue. A tile's piece records are staged in LDS once;
-// the block's scale bytes are staged once per block; weights stream from HBM through
-// DEPTH register sets (DEPTH-1 steps in flight while one is multiplied).
+// Weights stream from HBM in whole 128-byte lines: a step is 128 bytes (256 columns)
+// of each of the block's 64 rows, read by 8 loads of 8 rows x 128 B (lane i: row i / 8,
+// 16-byte unit i % 8), DEPTH steps in flight in registers. Each step is written to the
+// wave's LDS tile and read back as matrix-core fragments (16 rows x 16 B units); rows
+// are 128 bytes apart, so unit u of row r is kept at unit u ^ (r % 8) and the odd 8-row
+// chunks are shifted by 128 bytes, which makes both the writes and the fragment reads
+// free of bank conflicts. The weights enter the matrix cores as stored: each lane's 16
+// packed bytes of one 32-column group are the MXFP4 operand and the group's scale byte
+// is its scale. The activations enter as fp6 pieces: the 16 columns of a step are TT
+// tokens x 4 pieces, summed across lanes in the epilogue. A tile's piece records are
+// staged in LDS once; the block's scale bytes are staged once per block.
+constexpr int kDecPair = 2048 + 128;  // two 8-row chunks of a tile, the second shifted by 128 B
+constexpr int kDecTile = 4 * kDecPair;  // one wave's LDS tile: 64 rows x 128 B, padded
+
+__host__ __device__ inline size_t grouped_dec_tiles_off(int K, int tt) {
+  const size_t scales = ((size_t)2 * 64 * (K / kGroup) + 15) & ~(size_t)15;
+  const size_t stage = (size_t)tt * (K / kGroup) * kGroupRec;
+  const size_t red = (size_t)4 * 4 * 64 * 16 + (size_t)tt * 64 * 4;
+  return (scales + (stage > red ? stage : red) + 15) & ~(size_t)15;
+}
+
 template <int NA, int TT, int EPI, int DEPTH>
 __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
   constexpr int RB = 4;
@@ -483,23 +498,29 @@ __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
   // read as zero
   const rsrc_t rA = make_rsrc(mx.packed + (size_t)e * mx.pstride + (size_t)row0 * rowb,
                               (uint32_t)nrb * 16u * rowb);
-  const uint32_t aoff0 = (uint32_t)rl * rowb + (uint32_t)kq * 16u;
-  const int nsup = (a.ng + 3) >> 2;  // steps of 4 groups (128 columns)
+  const uint32_t lv = (uint32_t)(lane >> 3) * rowb + (uint32_t)(lane & 7) * 16u;  // load lane part
+  const int nsup = (a.ng + 7) >> 3;  // steps of 8 groups (256 columns, 128 bytes per row)
   const int spw = (nsup + KSPLIT - 1) / KSPLIT;
   const int s_lo = kp * spw, s_hi = min(nsup, s_lo + spw);
-  const int last_ok = a.ng - 4 * (nsup - 1);  // groups in the last step
 
   struct Step {
-    u32x4 a[RB];
-    uint32_t s[RB];
+    u32x4 a[8];             // load b: rows 8b .. 8b+7
+    uint32_t s[2][RB];      // scales of the step's two matrix-core k-steps
   };
+  // bytes past the row (a partial last step) belong to the next row or lie outside the
+  // descriptor; the k-blocks they would form are masked by their activations (zeros)
   auto load = [&](int S, Step &st) {
-    const bool gok = (S < s_hi) && ((S < nsup - 1) || (kq < last_ok));
-    const uint32_t va = gok ? aoff0 : kOOB;
-    const uint32_t Sc = (S < s_hi) ? (uint32_t)S : 0u;
+    const uint32_t Sc = (S < s_hi) ? (uint32_t)S * 128u : kOOB;
 #pragma unroll
-    for (int r = 0; r < RB; ++r) st.a[r] = bload16(rA, va, Sc * 64u + (uint32_t)r * 16u * rowb);
+    for (int b = 0; b < 8; ++b) st.a[b] = bload16(rA, lv, Sc == kOOB ? kOOB : Sc + (uint32_t)b * 8u * rowb);
   };
+  // this wave's LDS tile: the write slot of its load lanes and the fragment slot of its
+  // matrix-core lanes (row block 0; row block rb adds kDecPair bytes)
+  uint8_t *tile = smem + grouped_dec_tiles_off(a.K, TT) + wave * kDecTile;
+  const int wrr = lane >> 3, wu = lane & 7;
+  const uint32_t wslot = (uint32_t)(wrr * 128 + ((wu ^ wrr) * 16));
+  const int rr = rl & 7;  // fragment row inside its 8-row chunk
+  const uint32_t rslot0 = (uint32_t)((rl >> 3) * (1024 + 128) + rr * 128);
   // LDS: scale bytes [NA][64 rows][ng] | staged piece records [TT][ng * 128] (whose bytes
   // after the K loop hold the waves' partial sums, then the SiTU outputs)
   const int sc_bytes = (NA * 64 * (int)ng + 15) & ~15;
@@ -561,10 +582,13 @@ __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
   const uint8_t *sSw = sS + mw * 64 * (int)ng + rl * (int)ng;  // this lane's row of its matrix
 
   auto load_scales = [&](int S, Step &st) {
-    const int g = 4 * S + kq;
-    const bool gok = (S < s_hi) && g < a.ng;
 #pragma unroll
-    for (int r = 0; r < RB; ++r) st.s[r] = gok ? (uint32_t)sSw[r * 16 * (int)ng + g] : 127u;
+    for (int ks = 0; ks < 2; ++ks) {
+      const int g = 8 * S + 4 * ks + kq;
+      const bool gok = (S < s_hi) && g < a.ng;
+#pragma unroll
+      for (int r = 0; r < RB; ++r) st.s[ks][r] = gok ? (uint32_t)sSw[r * 16 * (int)ng + g] : 127u;
+    }
   };
 
   for (int n0 = lo; n0 < hi; n0 += TT) {
@@ -576,7 +600,7 @@ __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
     if (dma && n0 == lo) {
       // this wave's copies precede exactly the DEPTH-1 steps of weight loads issued since
       asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(RB * (DEPTH - 1)));
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(8 * (DEPTH - 1)));
     } else {
       // stage the tile's activation piece records (one row of ng * 128 bytes per token)
 #pragma unroll
@@ -596,19 +620,29 @@ __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
 #pragma unroll
     for (int r = 0; r < RB; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
     auto compute = [&](int S, const Step &sx) {
-      const int g = 4 * S + kq;
-      const bool gok = (S < s_hi) && g < a.ng;
-      const bool bv = bok && gok;
-      const u32x4 *bq = (const u32x4 *)(bl + (size_t)(gok ? g : 0) * kGroupRec);
-      const u32x4 b0 = bq[0], b1 = bq[1];
-      const uint32_t b[6] = {bv ? b0.x : 0u, bv ? b0.y : 0u, bv ? b0.z : 0u,
-                             bv ? b0.w : 0u, bv ? b1.x : 0u, bv ? b1.y : 0u};
-      const uint32_t sb = bv ? (b1.z & 255u) : 127u;
+      // the step's 8 KB into the tile (this wave's LDS operations run in order, so the
+      // previous step's fragment reads are done before these writes land)
 #pragma unroll
-      for (int r = 0; r < RB; ++r) {
-        const bool nan_scale = sx.s[r] == 255u;  // the pages' rule: the group is zero
-        const u32x4 av = nan_scale ? u32x4{0, 0, 0, 0} : sx.a[r];
-        acc[r] = mfma_fp4_fp6(av, b, nan_scale ? 127u : sx.s[r], sb, acc[r]);
+      for (int b = 0; b < 8; ++b)
+        *(u32x4 *)(tile + (b >> 1) * kDecPair + (b & 1) * (1024 + 128) + wslot) = sx.a[b];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int g = 8 * S + 4 * ks + kq;
+        const bool gok = (S < s_hi) && g < a.ng;
+        const bool bv = bok && gok;
+        const u32x4 *bq = (const u32x4 *)(bl + (size_t)(gok ? g : 0) * kGroupRec);
+        const u32x4 b0 = bq[0], b1 = bq[1];
+        const uint32_t b[6] = {bv ? b0.x : 0u, bv ? b0.y : 0u, bv ? b0.z : 0u,
+                               bv ? b0.w : 0u, bv ? b1.x : 0u, bv ? b1.y : 0u};
+        const uint32_t sb = bv ? (b1.z & 255u) : 127u;
+        const uint32_t uslot = (uint32_t)((((4 * ks + kq) ^ rr)) * 16);
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+          const u32x4 af = *(const u32x4 *)(tile + r * kDecPair + rslot0 + uslot);
+          const bool nan_scale = sx.s[ks][r] == 255u;  // the pages' rule: the group is zero
+          const u32x4 av = nan_scale ? u32x4{0, 0, 0, 0} : af;
+          acc[r] = mfma_fp4_fp6(av, b, nan_scale ? 127u : sx.s[ks][r], sb, acc[r]);
+        }
       }
     };
     // every wave runs the same number of steps; steps past its range read zeros
@@ -673,11 +707,22 @@ __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
 }
 
 size_t grouped_dec_lds(int K, int tt) {
-  // scale bytes of up to two matrices, then max(staged pieces, partial sums + SiTU outputs)
-  const size_t scales = ((size_t)2 * 64 * (K / kGroup) + 15) & ~(size_t)15;
-  const size_t stage = (size_t)tt * (K / kGroup) * kGroupRec;
-  const size_t red = (size_t)4 * 4 * 64 * 16 + (size_t)tt * 64 * 4;
-  return scales + (stage > red ? stage : red);
+  // scale bytes of up to two matrices, then max(staged pieces, partial sums + SiTU
+  // outputs), then the four waves' weight tiles
+  return grouped_dec_tiles_off(K, tt) + (size_t)4 * kDecTile;
+}
+
+template <int NA, int TT, int EPI, int DEPTH>
+static hipError_t launch_grouped_t(const GroupedArgs &a, dim3 grid, size_t lds, hipStream_t s) {
+  static bool attr = false;  // allow up to kMaxBlockLds of dynamic LDS (above the 64 KB default)
+  if (!attr) {
+    if (hipFuncSetAttribute((const void *)k_grouped_dec<NA, TT, EPI, DEPTH>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxBlockLds) != hipSuccess)
+      return hipErrorInvalidValue;
+    attr = true;
+  }
+  k_grouped_dec<NA, TT, EPI, DEPTH><<<grid, 256, lds, s>>>(a);
+  return hipGetLastError();
 }
 
 template <int NA, int EPI, int DEPTH>
@@ -685,11 +730,10 @@ static hipError_t launch_grouped_tt(const GroupedArgs &a, int tt, dim3 grid, hip
   const size_t lds = grouped_dec_lds(a.K, tt);
   if (lds > kMaxBlockLds) return hipErrorInvalidValue;
   switch (tt) {
-    case 1: k_grouped_dec<NA, 1, EPI, DEPTH><<<grid, 256, lds, s>>>(a); break;
-    case 2: k_grouped_dec<NA, 2, EPI, DEPTH><<<grid, 256, lds, s>>>(a); break;
-    default: k_grouped_dec<NA, 4, EPI, DEPTH><<<grid, 256, lds, s>>>(a); break;
+    case 1: return launch_grouped_t<NA, 1, EPI, DEPTH>(a, grid, lds, s);
+    case 2: return launch_grouped_t<NA, 2, EPI, DEPTH>(a, grid, lds, s);
+    default: return launch_grouped_t<NA, 4, EPI, DEPTH>(a, grid, lds, s);
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_grouped(const GroupedArgs &a, int epi, int tokens_per_tile, int grid_y, hipStream_t s) {
