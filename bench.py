@@ -92,7 +92,10 @@ def traffic_from_profile(kernel: str):
 
 
 def algorithmic(dims, T, n_distinct):
-    """Bytes the layer must move and flops it must do for one step."""
+    """Bytes the layer must move and flops it must do for one step: every distinct routed
+    expert's record once, the dense weights once, the token's input and output; flops count
+    the router, both projections and the three expert products of each (token, expert)
+    pair, at 2 per multiply-add."""
     import k3gen
     H, L, I, E, K = dims.hidden, dims.latent, dims.inter, dims.n_experts, dims.topk
     blob = k3gen.ExpertLayout(dims).blob_bytes
