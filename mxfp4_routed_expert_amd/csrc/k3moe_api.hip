@@ -399,10 +399,17 @@ int run_experts(const k3moe_dims *d, int32_t T, const float *z, bool zq_ready, c
   const bool mm_gu = use_mm(d, T, d->latent, (int64_t)T * d->latent * 4, ex->w1, ex->w3);
   const bool mm_dn = use_mm(d, T, d->inter, P * d->inter * 4, ex->w2, ex->w2);
   const int grid_y = (int)(P < d->n_experts ? P : d->n_experts);
-  // tokens staged per tile (an expert holds at most T tokens), as many as fit in LDS
-  const int kmax = d->latent > d->inter ? d->latent : d->inter;
+  // GEMV form: rows per block for about two resident blocks per compute unit; tokens
+  // staged per tile (an expert holds at most T tokens), as many as fit in LDS
+  const int ncu = num_cus();
+  int rb_gu = grouped_dec_rb(d->inter, grid_y, kEpiSitu, ncu);
+  int rb_dn = grouped_dec_rb(d->latent, grid_y, kEpiEdn, ncu);
   int tt = T <= 1 ? 1 : (T <= 2 ? 2 : 4);
-  while (tt > 1 && grouped_dec_lds(kmax, tt) > kMaxBlockLds) tt >>= 1;
+  while (tt > 1 && (grouped_dec_lds(d->latent, tt, rb_gu) > kMaxBlockLds ||
+                    grouped_dec_lds(d->inter, tt, rb_dn) > kMaxBlockLds))
+    tt >>= 1;
+  while (rb_gu > 4 && grouped_dec_lds(d->latent, tt, rb_gu) > kMaxBlockLds) rb_gu -= 2;
+  while (rb_dn > 4 && grouped_dec_lds(d->inter, tt, rb_dn) > kMaxBlockLds) rb_dn -= 1;
   if (mm_gu || mm_dn) K3_HIP(launch_mm_tiles(expert_off, d->n_experts, w.tiles, w.counters + 2, s));
   const int max_tiles = (int)max_mm_tiles(d, T);
 
@@ -449,7 +456,7 @@ int run_experts(const k3moe_dims *d, int32_t T, const float *z, bool zq_ready, c
     g.outq = w.actq;
     g.b1 = d->b1;
     g.b2 = d->b2;
-    K3_HIP(launch_grouped(g, kEpiSitu, tt, grid_y, s));
+    K3_HIP(launch_grouped(g, kEpiSitu, tt, rb_gu, grid_y, s));
   }
   K3_HIP(mark("expert_gateup_situ", s));
 
@@ -483,7 +490,7 @@ int run_experts(const k3moe_dims *d, int32_t T, const float *z, bool zq_ready, c
     h.active = active;
     h.n_active = counters;
     h.out = edn;
-    K3_HIP(launch_grouped(h, kEpiEdn, tt, grid_y, s));
+    K3_HIP(launch_grouped(h, kEpiEdn, tt, rb_dn, grid_y, s));
   }
   K3_HIP(mark("expert_down", s));
   return K3MOE_OK;

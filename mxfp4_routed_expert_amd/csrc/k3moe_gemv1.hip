@@ -188,18 +188,6 @@ __global__ __launch_bounds__(1024) void k_gemv1_front(Gemv1Args r, Gemv1Args d, 
   }
 }
 
-int num_cus() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cached[dev]) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
-
 // Waves per block for `items` equal wave items: the per-unit share, or its largest
 // divisor up to 16 (so whole blocks divide evenly over the compute units).
 int gemv1_waves(int items) {
@@ -219,6 +207,18 @@ bool gemv1_ok(const Gemv1Args &a, int esz) {
 }
 
 }  // namespace
+
+int num_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
 
 bool gemv1_supported(const Gemv1Args &a, int af) { return gemv1_ok(a, af == kA_F32 ? 4 : 2); }
 

@@ -143,8 +143,12 @@ hipError_t launch_split_planes(const float *src, size_t n, uint16_t *p0, uint16_
                                uint16_t *p2, hipStream_t s);
 // tokens_per_tile: 1, 2 or 4 tokens' piece records staged in LDS per tile (grouped_dec_lds bytes)
 constexpr size_t kMaxBlockLds = 81920;  // two blocks per compute unit
-size_t grouped_dec_lds(int K, int tokens_per_tile);
-hipError_t launch_grouped(const GroupedArgs &a, int epi, int tokens_per_tile, int grid_y, hipStream_t s);
+// rb: 16-row blocks per block (4, 6 or 8 for kEpiSitu; 4 to 8 for kEpiEdn), from grouped_dec_rb
+size_t grouped_dec_lds(int K, int tokens_per_tile, int rb);
+int grouped_dec_rb(int M, int grid_y, int epi, int ncu);
+// compute units of the current device
+int num_cus();
+hipError_t launch_grouped(const GroupedArgs &a, int epi, int tokens_per_tile, int rb, int grid_y, hipStream_t s);
 // column tiles of kMmBN slots per expert: at most ceil(P / kMmBN) + min(E, P) entries
 hipError_t launch_mm_tiles(const int32_t *expert_off, int E, int4 *tiles, int32_t *n_tiles, hipStream_t s);
 size_t grouped_mm_lds();

@@ -447,38 +447,43 @@ __device__ __forceinline__ void dma16(rsrc_t r, uint8_t *lds, uint32_t voff, uin
 #ifndef K3_DOWN_DEPTH
 #define K3_DOWN_DEPTH 2
 #endif
-// Grid: x = 64-row blocks, y = active-expert slots. The block's four waves share the
-// same 64 rows (four 16-row blocks). With one matrix (down) the waves split K four
-// ways; with two (gate w1 and up w3) waves 0-1 stream w1 and waves 2-3 stream w3, each
-// pair splitting K in halves. Partial sums meet in LDS, where wave w finishes row block
-// w (SiTU pairs the gate and up sums of the same row and token there).
+// Grid: x = blocks of RB 16-row blocks, y = active-expert slots. The block's four waves
+// share the same 16 RB rows. With one matrix (down) the waves split K four ways; with
+// two (gate w1 and up w3) waves 0-1 stream w1 and waves 2-3 stream w3, each pair
+// splitting K in halves. Partial sums meet in LDS, where wave w finishes row blocks w,
+// w+4, ... (SiTU pairs the gate and up sums of the same row and token there). RB is
+// chosen by the host so that the grid is about two blocks per compute unit, all
+// resident at once.
 // Weights stream from HBM in whole 128-byte lines: a step is 128 bytes (256 columns)
-// of each of the block's 64 rows, read by 8 loads of 8 rows x 128 B (lane i: row i / 8,
-// 16-byte unit i % 8), DEPTH steps in flight in registers. Each step is written to the
-// wave's LDS tile and read back as matrix-core fragments (16 rows x 16 B units); rows
-// are 128 bytes apart, so unit u of row r is kept at unit u ^ (r % 8) and the odd 8-row
-// chunks are shifted by 128 bytes, which makes both the writes and the fragment reads
-// free of bank conflicts. The weights enter the matrix cores as stored: each lane's 16
-// packed bytes of one 32-column group are the MXFP4 operand and the group's scale byte
-// is its scale. The activations enter as fp6 pieces: the 16 columns of a step are TT
-// tokens x 4 pieces, summed across lanes in the epilogue. A tile's piece records are
-// staged in LDS once; the block's scale bytes are staged once per block.
-constexpr int kDecPair = 2048 + 128;  // two 8-row chunks of a tile, the second shifted by 128 B
-constexpr int kDecTile = 4 * kDecPair;  // one wave's LDS tile: 64 rows x 128 B, padded
+// of each of the block's rows, read by 2 RB loads of 8 rows x 128 B (lane i: row i / 8,
+// 16-byte unit i % 8), DEPTH steps in flight in registers. Each 16-row block of a step
+// is written to the wave's LDS tile and read back as matrix-core fragments (16 rows x
+// 16 B units); rows are 128 bytes apart, so unit u of row r is kept at unit u ^ (r % 8)
+// and the second 8-row chunk is shifted by 128 bytes, which makes both the writes and
+// the fragment reads free of bank conflicts. The weights enter the matrix cores as
+// stored: each lane's 16 packed bytes of one 32-column group are the MXFP4 operand and
+// the group's scale byte is its scale. The activations enter as fp6 pieces: the 16
+// columns of a step are TT tokens x 4 pieces, summed across lanes in the epilogue. A
+// tile's piece records are staged in LDS once; the block's scale bytes are staged once
+// per block.
+constexpr int kDecPair = 2048 + 128;  // a wave's tile: two 8-row chunks, the second shifted by 128 B
 
-__host__ __device__ inline size_t grouped_dec_tiles_off(int K, int tt) {
-  const size_t scales = ((size_t)2 * 64 * (K / kGroup) + 15) & ~(size_t)15;
+__host__ __device__ inline size_t grouped_dec_sb_off(int K, int rb) {
+  return ((size_t)2 * 16 * rb * (K / kGroup) + 15) & ~(size_t)15;  // scale bytes of up to 2 matrices
+}
+__host__ __device__ inline size_t grouped_dec_tiles_off(int K, int tt, int rb) {
   const size_t stage = (size_t)tt * (K / kGroup) * kGroupRec;
-  const size_t red = (size_t)4 * 4 * 64 * 16 + (size_t)tt * 64 * 4;
-  return (scales + (stage > red ? stage : red) + 15) & ~(size_t)15;
+  const size_t red = (size_t)4 * rb * 64 * 16 + (size_t)tt * 16 * rb * 4;
+  return grouped_dec_sb_off(K, rb) + (((stage > red ? stage : red) + 15) & ~(size_t)15);
 }
 
-template <int NA, int TT, int EPI, int DEPTH>
+template <int NA, int TT, int EPI, int DEPTH, int RB>
 __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
-  constexpr int RB = 4;
   constexpr int KSPLIT = 4 / NA;
   constexpr int PB = kFp6Pieces;
+  constexpr int NL = 2 * RB;  // loads per step
   static_assert(TT * PB <= 16, "a tile's (token, piece) pairs fill at most 16 MFMA columns");
+  static_assert(EPI != kEpiSitu || RB % 2 == 0, "the SiTU epilogue quantizes whole 32-row groups");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rl = lane & 15, kq = lane >> 4;
@@ -489,7 +494,8 @@ __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
   const int e = __builtin_amdgcn_readfirstlane(a.active[j]);
   const int lo = __builtin_amdgcn_readfirstlane(a.expert_off[e]);
   const int hi = __builtin_amdgcn_readfirstlane(a.expert_off[e + 1]);
-  const int row0 = blockIdx.x * 64;
+  constexpr int ROWS = 16 * RB;
+  const int row0 = blockIdx.x * ROWS;
   const uint32_t rowb = (uint32_t)a.K / 2, ng = (uint32_t)a.ng;
   const int nrb = min(RB, (a.M - row0) >> 4);  // row blocks inside M (M % 32 == 0)
   const int mw = wave / KSPLIT, kp = wave % KSPLIT;
@@ -503,32 +509,36 @@ __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
   const int spw = (nsup + KSPLIT - 1) / KSPLIT;
   const int s_lo = kp * spw, s_hi = min(nsup, s_lo + spw);
 
-  struct Step {
-    u32x4 a[8];             // load b: rows 8b .. 8b+7
-    uint32_t s[2][RB];      // scales of the step's two matrix-core k-steps
-  };
-  // bytes past the row (a partial last step) belong to the next row or lie outside the
-  // descriptor; the k-blocks they would form are masked by their activations (zeros)
-  auto load = [&](int S, Step &st) {
+  // The step's loads live in one register set w[NL] (load b: rows 8b .. 8b+7): as soon
+  // as a 16-row block of step S has been multiplied, its two registers are reloaded
+  // with the same rows of step S+1, so the weight stream runs one step ahead.
+  // Bytes past the row (a partial last step) belong to the next row or lie outside the
+  // descriptor; the k-blocks they would form are masked by their activations (zeros).
+  u32x4 w[NL];
+  auto load_block = [&](int S, int r) {
     const uint32_t Sc = (S < s_hi) ? (uint32_t)S * 128u : kOOB;
 #pragma unroll
-    for (int b = 0; b < 8; ++b) st.a[b] = bload16(rA, lv, Sc == kOOB ? kOOB : Sc + (uint32_t)b * 8u * rowb);
+    for (int h = 0; h < 2; ++h)
+      w[2 * r + h] = bload16(rA, lv, Sc == kOOB ? kOOB : Sc + (uint32_t)(2 * r + h) * 8u * rowb);
+  };
+  auto load = [&](int S) {
+#pragma unroll
+    for (int r = 0; r < RB; ++r) load_block(S, r);
   };
   // this wave's LDS tile: the write slot of its load lanes and the fragment slot of its
-  // matrix-core lanes (row block 0; row block rb adds kDecPair bytes)
-  uint8_t *tile = smem + grouped_dec_tiles_off(a.K, TT) + wave * kDecTile;
+  // matrix-core lanes
+  uint8_t *tile = smem + grouped_dec_tiles_off(a.K, TT, RB) + wave * kDecPair;
   const int wrr = lane >> 3, wu = lane & 7;
   const uint32_t wslot = (uint32_t)(wrr * 128 + ((wu ^ wrr) * 16));
   const int rr = rl & 7;  // fragment row inside its 8-row chunk
   const uint32_t rslot0 = (uint32_t)((rl >> 3) * (1024 + 128) + rr * 128);
-  // LDS: scale bytes [NA][64 rows][ng] | staged piece records [TT][ng * 128] (whose bytes
-  // after the K loop hold the waves' partial sums, then the SiTU outputs)
-  const int sc_bytes = (NA * 64 * (int)ng + 15) & ~15;
+  // LDS: scale bytes [NA][ROWS][ng] | staged piece records [TT][ng * 128] (whose bytes
+  // after the K loop hold the waves' partial sums, then the SiTU outputs) | tiles
   uint8_t *sS = smem;
-  uint8_t *sB = smem + sc_bytes;
+  uint8_t *sB = smem + grouped_dec_sb_off(a.K, RB);
   const int brow_bytes = (int)ng * kGroupRec;
   f32x4(*red)[RB][64] = (f32x4(*)[RB][64])sB;
-  float *sAct = (float *)(sB + 4 * RB * 64 * 16);  // [TT][64] SiTU outputs of the tile
+  float *sAct = (float *)(sB + 4 * RB * 64 * 16);  // [TT][ROWS] SiTU outputs of the tile
   const int nb = nrb * 16 * (int)ng;  // scale bytes of one matrix for this block's rows
 
   // When the block's scale rows and token records are whole kilobytes, the memory unit
@@ -548,7 +558,7 @@ __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
     for (int i = wave; i < NA * nsc; i += 4) {
       const int m = i / nsc, c = i - m * nsc;
       const rsrc_t rS = make_rsrc(a.A[m].scales + (size_t)e * a.A[m].sstride + (size_t)row0 * ng, (uint32_t)nb);
-      dma16(rS, sS + m * 64 * (int)ng + c * 1024, (uint32_t)lane * 16u, (uint32_t)c * 1024u);
+      dma16(rS, sS + m * ROWS * (int)ng + c * 1024, (uint32_t)lane * 16u, (uint32_t)c * 1024u);
     }
     for (int i = wave; i < ntok0 * nbc; i += 4) {
       const int tt = i / nbc, c = i - tt * nbc;
@@ -563,15 +573,13 @@ __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
   __builtin_amdgcn_sched_barrier(0);
 
   // the weight stream of the first tile starts before any staged byte is needed
-  Step st[DEPTH];
-#pragma unroll
-  for (int d = 0; d + 1 < DEPTH; ++d) load(s_lo + d, st[d]);
+  load(s_lo);
 
   if (!dma) {
     // the scales depend on the rows only: one coalesced copy per block
     for (int m = 0; m < NA; ++m) {
       const uint8_t *src = a.A[m].scales + (size_t)e * a.A[m].sstride + (size_t)row0 * ng;
-      uint8_t *dst = sS + m * 64 * (int)ng;
+      uint8_t *dst = sS + m * ROWS * (int)ng;
       if ((((uintptr_t)src) & 15) == 0 && (nb & 15) == 0) {
         stage16<4>(dst, src, nb);
       } else {
@@ -579,28 +587,16 @@ __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
       }
     }
   }
-  const uint8_t *sSw = sS + mw * 64 * (int)ng + rl * (int)ng;  // this lane's row of its matrix
+  const uint8_t *sSw = sS + mw * ROWS * (int)ng + rl * (int)ng;  // this lane's row of its matrix
 
-  auto load_scales = [&](int S, Step &st) {
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int g = 8 * S + 4 * ks + kq;
-      const bool gok = (S < s_hi) && g < a.ng;
-#pragma unroll
-      for (int r = 0; r < RB; ++r) st.s[ks][r] = gok ? (uint32_t)sSw[r * 16 * (int)ng + g] : 127u;
-    }
-  };
 
   for (int n0 = lo; n0 < hi; n0 += TT) {
     const int ntok = min(TT, hi - n0);
-    if (n0 != lo) {
-#pragma unroll
-      for (int d = 0; d + 1 < DEPTH; ++d) load(s_lo + d, st[d]);
-    }
+    if (n0 != lo) load(s_lo);
     if (dma && n0 == lo) {
-      // this wave's copies precede exactly the DEPTH-1 steps of weight loads issued since
+      // this wave's copies precede exactly the one step of weight loads issued since
       asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(8 * (DEPTH - 1)));
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(NL));
     } else {
       // stage the tile's activation piece records (one row of ng * 128 bytes per token)
 #pragma unroll
@@ -619,128 +615,170 @@ __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
     f32x4 acc[RB];
 #pragma unroll
     for (int r = 0; r < RB; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-    auto compute = [&](int S, const Step &sx) {
-      // the step's 8 KB into the tile (this wave's LDS operations run in order, so the
-      // previous step's fragment reads are done before these writes land)
-#pragma unroll
-      for (int b = 0; b < 8; ++b)
-        *(u32x4 *)(tile + (b >> 1) * kDecPair + (b & 1) * (1024 + 128) + wslot) = sx.a[b];
+    auto compute = [&](int S) {
+      uint32_t b[2][6], sb[2];
+      bool gk[2];
+      int gg[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const int g = 8 * S + 4 * ks + kq;
         const bool gok = (S < s_hi) && g < a.ng;
+        gk[ks] = gok;
+        gg[ks] = gok ? g : 0;
         const bool bv = bok && gok;
         const u32x4 *bq = (const u32x4 *)(bl + (size_t)(gok ? g : 0) * kGroupRec);
         const u32x4 b0 = bq[0], b1 = bq[1];
-        const uint32_t b[6] = {bv ? b0.x : 0u, bv ? b0.y : 0u, bv ? b0.z : 0u,
-                               bv ? b0.w : 0u, bv ? b1.x : 0u, bv ? b1.y : 0u};
-        const uint32_t sb = bv ? (b1.z & 255u) : 127u;
-        const uint32_t uslot = (uint32_t)((((4 * ks + kq) ^ rr)) * 16);
+        b[ks][0] = bv ? b0.x : 0u; b[ks][1] = bv ? b0.y : 0u; b[ks][2] = bv ? b0.z : 0u;
+        b[ks][3] = bv ? b0.w : 0u; b[ks][4] = bv ? b1.x : 0u; b[ks][5] = bv ? b1.y : 0u;
+        sb[ks] = bv ? (b1.z & 255u) : 127u;
+      }
+      // each 16-row block: its two 8-row chunks into the tile, then its two fragments
+      // back (this wave's LDS operations run in order, so a block's fragment reads are
+      // done before the next block's writes land)
 #pragma unroll
-        for (int r = 0; r < RB; ++r) {
-          const u32x4 af = *(const u32x4 *)(tile + r * kDecPair + rslot0 + uslot);
-          const bool nan_scale = sx.s[ks][r] == 255u;  // the pages' rule: the group is zero
+      for (int r = 0; r < RB; ++r) {
+        *(u32x4 *)(tile + wslot) = w[2 * r];
+        *(u32x4 *)(tile + (1024 + 128) + wslot) = w[2 * r + 1];
+        load_block(S + 1, r);  // the registers are free once their bytes are in LDS
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const uint32_t uslot = (uint32_t)((((4 * ks + kq) ^ rr)) * 16);
+          const u32x4 af = *(const u32x4 *)(tile + rslot0 + uslot);
+          const uint32_t sa = gk[ks] ? (uint32_t)sSw[r * 16 * (int)ng + gg[ks]] : 127u;
+          const bool nan_scale = sa == 255u;  // the pages' rule: the group is zero
           const u32x4 av = nan_scale ? u32x4{0, 0, 0, 0} : af;
-          acc[r] = mfma_fp4_fp6(av, b, nan_scale ? 127u : sx.s[ks][r], sb, acc[r]);
+          acc[r] = mfma_fp4_fp6(av, b[ks], nan_scale ? 127u : sa, sb[ks], acc[r]);
         }
+        // one 16-row block's LDS traffic at a time: the scheduler would otherwise hoist
+        // every block's fragment reads (and their registers) ahead of the matrix cores
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
-    // every wave runs the same number of steps; steps past its range read zeros
-    load_scales(s_lo, st[0]);
-    for (int i = 0; i < spw; i += DEPTH) {
-#pragma unroll
-      for (int d = 0; d < DEPTH; ++d) {
-        load(s_lo + i + d + DEPTH - 1, st[(d + DEPTH - 1) % DEPTH]);
-        load_scales(s_lo + i + d + 1, st[(d + 1) % DEPTH]);
-        compute(s_lo + i + d, st[d]);
-      }
-    }
+    // every wave runs the same number of steps (its last issues loads past its range,
+    // which read zeros)
+    for (int i = 0; i < spw; ++i) compute(s_lo + i);
 
     __syncthreads();  // every wave is done reading the staged activations
 #pragma unroll
     for (int r = 0; r < RB; ++r) red[wave][r][lane] = acc[r];
     __syncthreads();
-    const int r = wave;
-    f32x4 v[NA];
 #pragma unroll
-    for (int m = 0; m < NA; ++m) {
-      v[m] = red[m * KSPLIT][r][lane];
+    for (int r0 = 0; r0 < RB; r0 += 4) {
+      const int r = r0 + wave;
+      if (r >= RB) break;
+      f32x4 v[NA];
 #pragma unroll
-      for (int k = 1; k < KSPLIT; ++k) v[m] += red[m * KSPLIT + k][r][lane];
-    }
-    // sum the 4 piece columns of each token (lanes tn*4 .. tn*4+3 of the row group)
+      for (int m = 0; m < NA; ++m) {
+        v[m] = red[m * KSPLIT][r][lane];
 #pragma unroll
-    for (int m = 0; m < NA; ++m) {
+        for (int k = 1; k < KSPLIT; ++k) v[m] += red[m * KSPLIT + k][r][lane];
+      }
+      // sum the 4 piece columns of each token (lanes tn*4 .. tn*4+3 of the row group)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float t = v[m][i];
-        t += __shfl_xor(t, 1, 4);
-        t += __shfl_xor(t, 2, 4);
-        v[m][i] = t;
+      for (int m = 0; m < NA; ++m) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float t = v[m][i];
+          t += __shfl_xor(t, 1, 4);
+          t += __shfl_xor(t, 2, 4);
+          v[m][i] = t;
+        }
+      }
+      const bool out_ok = piece == 0 && bok && r < nrb;
+      if constexpr (EPI == kEpiSitu) {
+        if (out_ok) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            sAct[tn * ROWS + 16 * r + 4 * kq + i] = situ(v[0][i], v[NA - 1][i], a.b1, a.b2);
+        }
+      } else {
+        if (out_ok) *(f32x4 *)(a.out + (size_t)(n0 + tn) * a.M + row0 + 16 * r + 4 * kq) = v[0];
       }
     }
-    const bool out_ok = piece == 0 && bok && r < nrb;
     if constexpr (EPI == kEpiSitu) {
-      // SiTU, then quantize each 32-row group of each token into fp6 piece records
-      if (out_ok) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sAct[tn * 64 + 16 * r + 4 * kq + i] = situ(v[0][i], v[NA - 1][i], a.b1, a.b2);
-      }
+      // quantize each 32-row group of each token into fp6 piece records
       __syncthreads();
+      constexpr int GPT = RB / 2;  // 32-row groups per token
       const int t = threadIdx.x;
-      const int grp = t >> 2, k4 = t & 3;  // 4 lanes per group, 2 groups per token
-      const int tt = grp >> 1, gq = grp & 1;
+      const int grp = t >> 2, k4 = t & 3;  // 4 lanes per group
+      const int tt = grp / GPT, gq = grp % GPT;
       if (tt < ntok && row0 + 32 * gq < a.M) {
         float rv[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) rv[i] = sAct[tt * 64 + 32 * gq + 8 * k4 + i];
+        for (int i = 0; i < 8; ++i) rv[i] = sAct[tt * ROWS + 32 * gq + 8 * k4 + i];
         uint8_t *rec = a.outq + (size_t)(n0 + tt) * (size_t)(a.M / 32) * kGroupRec +
                        (size_t)(row0 / 32 + gq) * kGroupRec;
         quant_group_fp6(rv, k4, rec);
       }
-    } else {
-      if (out_ok) *(f32x4 *)(a.out + (size_t)(n0 + tn) * a.M + row0 + 16 * r + 4 * kq) = v[0];
     }
     __syncthreads();  // the next tile rewrites the staged activations
   }
 }
 
-size_t grouped_dec_lds(int K, int tt) {
+size_t grouped_dec_lds(int K, int tt, int rb) {
   // scale bytes of up to two matrices, then max(staged pieces, partial sums + SiTU
   // outputs), then the four waves' weight tiles
-  return grouped_dec_tiles_off(K, tt) + (size_t)4 * kDecTile;
+  return grouped_dec_tiles_off(K, tt, rb) + (size_t)4 * kDecPair;
 }
 
-template <int NA, int TT, int EPI, int DEPTH>
+template <int NA, int TT, int EPI, int DEPTH, int RB>
 static hipError_t launch_grouped_t(const GroupedArgs &a, dim3 grid, size_t lds, hipStream_t s) {
   static bool attr = false;  // allow up to kMaxBlockLds of dynamic LDS (above the 64 KB default)
   if (!attr) {
-    if (hipFuncSetAttribute((const void *)k_grouped_dec<NA, TT, EPI, DEPTH>,
+    if (hipFuncSetAttribute((const void *)k_grouped_dec<NA, TT, EPI, DEPTH, RB>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxBlockLds) != hipSuccess)
       return hipErrorInvalidValue;
     attr = true;
   }
-  k_grouped_dec<NA, TT, EPI, DEPTH><<<grid, 256, lds, s>>>(a);
+  k_grouped_dec<NA, TT, EPI, DEPTH, RB><<<grid, 256, lds, s>>>(a);
   return hipGetLastError();
 }
 
-template <int NA, int EPI, int DEPTH>
-static hipError_t launch_grouped_tt(const GroupedArgs &a, int tt, dim3 grid, hipStream_t s) {
-  const size_t lds = grouped_dec_lds(a.K, tt);
+template <int NA, int EPI, int DEPTH, int RB>
+static hipError_t launch_grouped_tt(const GroupedArgs &a, int tt, int grid_y, hipStream_t s) {
+  const size_t lds = grouped_dec_lds(a.K, tt, RB);
   if (lds > kMaxBlockLds) return hipErrorInvalidValue;
+  const dim3 grid((a.M + 16 * RB - 1) / (16 * RB), grid_y);
   switch (tt) {
-    case 1: return launch_grouped_t<NA, 1, EPI, DEPTH>(a, grid, lds, s);
-    case 2: return launch_grouped_t<NA, 2, EPI, DEPTH>(a, grid, lds, s);
-    default: return launch_grouped_t<NA, 4, EPI, DEPTH>(a, grid, lds, s);
+    case 1: return launch_grouped_t<NA, 1, EPI, DEPTH, RB>(a, grid, lds, s);
+    case 2: return launch_grouped_t<NA, 2, EPI, DEPTH, RB>(a, grid, lds, s);
+    default: return launch_grouped_t<NA, 4, EPI, DEPTH, RB>(a, grid, lds, s);
   }
 }
 
-hipError_t launch_grouped(const GroupedArgs &a, int epi, int tokens_per_tile, int grid_y, hipStream_t s) {
+int grouped_dec_rb(int M, int grid_y, int epi, int ncu) {
+  // The per-unit critical path in 16-row blocks: rounds of two resident blocks per
+  // compute unit times the rows per block; ties go to the smaller block.
+  int best = 4;
+  long long best_cost = -1;
+  for (int rb = 4; rb <= 8; ++rb) {
+    if (epi == kEpiSitu && rb % 2) continue;
+    const long long blocks = (long long)((M / 16 + rb - 1) / rb) * grid_y;
+    const long long rounds = (blocks + 2LL * ncu - 1) / (2LL * ncu);
+    const long long cost = rounds * rb;
+    if (best_cost < 0 || cost < best_cost) { best_cost = cost; best = rb; }
+  }
+  return best;
+}
+
+hipError_t launch_grouped(const GroupedArgs &a, int epi, int tokens_per_tile, int rb, int grid_y, hipStream_t s) {
   if (grid_y <= 0) return hipSuccess;
-  dim3 grid((a.M + 63) / 64, grid_y);
-  if (epi == kEpiSitu) return launch_grouped_tt<2, kEpiSitu, K3_GATEUP_DEPTH>(a, tokens_per_tile, grid, s);
-  return launch_grouped_tt<1, kEpiEdn, K3_DOWN_DEPTH>(a, tokens_per_tile, grid, s);
+  if (epi == kEpiSitu) {
+    switch (rb) {
+      case 4: return launch_grouped_tt<2, kEpiSitu, K3_GATEUP_DEPTH, 4>(a, tokens_per_tile, grid_y, s);
+      case 6: return launch_grouped_tt<2, kEpiSitu, K3_GATEUP_DEPTH, 6>(a, tokens_per_tile, grid_y, s);
+      case 8: return launch_grouped_tt<2, kEpiSitu, K3_GATEUP_DEPTH, 8>(a, tokens_per_tile, grid_y, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  switch (rb) {
+    case 4: return launch_grouped_tt<1, kEpiEdn, K3_DOWN_DEPTH, 4>(a, tokens_per_tile, grid_y, s);
+    case 5: return launch_grouped_tt<1, kEpiEdn, K3_DOWN_DEPTH, 5>(a, tokens_per_tile, grid_y, s);
+    case 6: return launch_grouped_tt<1, kEpiEdn, K3_DOWN_DEPTH, 6>(a, tokens_per_tile, grid_y, s);
+    case 7: return launch_grouped_tt<1, kEpiEdn, K3_DOWN_DEPTH, 7>(a, tokens_per_tile, grid_y, s);
+    case 8: return launch_grouped_tt<1, kEpiEdn, K3_DOWN_DEPTH, 8>(a, tokens_per_tile, grid_y, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 // ============================================================== fp32 rows -> fp6 pieces
