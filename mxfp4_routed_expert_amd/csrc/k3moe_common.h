@@ -183,8 +183,9 @@ __device__ __forceinline__ void quant_group_fp6(float (&r)[8], int k4, uint8_t *
 
 // The same for a group laid out as a 16x16 matrix-core result: lanes l, l^16, l^32,
 // l^48 (kq = l / 16) hold the group's values 4kq .. 4kq+3 (r[0..3]) and 16+4kq .. 19+4kq
-// (r[4..7]). rec is the group's record (LDS or global).
-__device__ __forceinline__ void quant_group_fp6_kq(float (&r)[8], int kq, uint8_t *rec) {
+// (r[4..7]). rec is the group's record (LDS or global); every lane takes part in the
+// group maxima, and only lanes with st set write.
+__device__ __forceinline__ void quant_group_fp6_kq(float (&r)[8], int kq, uint8_t *rec, bool st = true) {
 #pragma unroll
   for (int p = 0; p < kFp6Pieces; ++p) {
     float m = 0.f;
@@ -196,14 +197,16 @@ __device__ __forceinline__ void quant_group_fp6_kq(float (&r)[8], int kq, uint8_
     const int e = fp6_piece(r, m, c);
     const uint32_t lo = c[0] | (c[1] << 6) | (c[2] << 12) | (c[3] << 18);  // values 4kq .. 4kq+3
     const uint32_t hi = c[4] | (c[5] << 6) | (c[6] << 12) | (c[7] << 18);  // values 16+4kq ..
-    uint8_t *dst = rec + p * kPieceRec;
-    dst[3 * kq] = (uint8_t)lo;
-    dst[3 * kq + 1] = (uint8_t)(lo >> 8);
-    dst[3 * kq + 2] = (uint8_t)(lo >> 16);
-    dst[12 + 3 * kq] = (uint8_t)hi;
-    dst[12 + 3 * kq + 1] = (uint8_t)(hi >> 8);
-    dst[12 + 3 * kq + 2] = (uint8_t)(hi >> 16);
-    if (kq == 0) dst[24] = (uint8_t)(e + 127);
+    if (st) {
+      uint8_t *dst = rec + p * kPieceRec;
+      dst[3 * kq] = (uint8_t)lo;
+      dst[3 * kq + 1] = (uint8_t)(lo >> 8);
+      dst[3 * kq + 2] = (uint8_t)(lo >> 16);
+      dst[12 + 3 * kq] = (uint8_t)hi;
+      dst[12 + 3 * kq + 1] = (uint8_t)(hi >> 8);
+      dst[12 + 3 * kq + 2] = (uint8_t)(hi >> 16);
+      if (kq == 0) dst[24] = (uint8_t)(e + 127);
+    }
   }
 }
 

@@ -473,7 +473,7 @@ __host__ __device__ inline size_t grouped_dec_sb_off(int K, int rb) {
 }
 __host__ __device__ inline size_t grouped_dec_tiles_off(int K, int tt, int rb) {
   const size_t stage = (size_t)tt * (K / kGroup) * kGroupRec;
-  const size_t red = (size_t)4 * rb * 64 * 16 + (size_t)tt * 16 * rb * 4;
+  const size_t red = (size_t)4 * rb * 64 * 16;
   return grouped_dec_sb_off(K, rb) + (((stage > red ? stage : red) + 15) & ~(size_t)15);
 }
 
@@ -533,12 +533,11 @@ __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
   const int rr = rl & 7;  // fragment row inside its 8-row chunk
   const uint32_t rslot0 = (uint32_t)((rl >> 3) * (1024 + 128) + rr * 128);
   // LDS: scale bytes [NA][ROWS][ng] | staged piece records [TT][ng * 128] (whose bytes
-  // after the K loop hold the waves' partial sums, then the SiTU outputs) | tiles
+  // after the K loop hold the waves' partial sums) | tiles
   uint8_t *sS = smem;
   uint8_t *sB = smem + grouped_dec_sb_off(a.K, RB);
   const int brow_bytes = (int)ng * kGroupRec;
   f32x4(*red)[RB][64] = (f32x4(*)[RB][64])sB;
-  float *sAct = (float *)(sB + 4 * RB * 64 * 16);  // [TT][ROWS] SiTU outputs of the tile
   const int nb = nrb * 16 * (int)ng;  // scale bytes of one matrix for this block's rows
 
   // When the block's scale rows and token records are whole kilobytes, the memory unit
@@ -662,20 +661,14 @@ __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
 #pragma unroll
     for (int r = 0; r < RB; ++r) red[wave][r][lane] = acc[r];
     __syncthreads();
-#pragma unroll
-    for (int r0 = 0; r0 < RB; r0 += 4) {
-      const int r = r0 + wave;
-      if (r >= RB) break;
-      f32x4 v[NA];
+    // the K parts of row block r, summed over the waves, then over the 4 piece columns
+    // of each token (lanes tn*4 .. tn*4+3 of the row group)
+    auto reduce_rb = [&](int r, f32x4 (&v)[NA]) {
 #pragma unroll
       for (int m = 0; m < NA; ++m) {
         v[m] = red[m * KSPLIT][r][lane];
 #pragma unroll
         for (int k = 1; k < KSPLIT; ++k) v[m] += red[m * KSPLIT + k][r][lane];
-      }
-      // sum the 4 piece columns of each token (lanes tn*4 .. tn*4+3 of the row group)
-#pragma unroll
-      for (int m = 0; m < NA; ++m) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float t = v[m][i];
@@ -684,31 +677,31 @@ __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
           v[m][i] = t;
         }
       }
-      const bool out_ok = piece == 0 && bok && r < nrb;
-      if constexpr (EPI == kEpiSitu) {
-        if (out_ok) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            sAct[tn * ROWS + 16 * r + 4 * kq + i] = situ(v[0][i], v[NA - 1][i], a.b1, a.b2);
-        }
-      } else {
-        if (out_ok) *(f32x4 *)(a.out + (size_t)(n0 + tn) * a.M + row0 + 16 * r + 4 * kq) = v[0];
-      }
-    }
+    };
+    const bool tok_ok = piece == 0 && bok;
     if constexpr (EPI == kEpiSitu) {
-      // quantize each 32-row group of each token into fp6 piece records
-      __syncthreads();
-      constexpr int GPT = RB / 2;  // 32-row groups per token
-      const int t = threadIdx.x;
-      const int grp = t >> 2, k4 = t & 3;  // 4 lanes per group
-      const int tt = grp / GPT, gq = grp % GPT;
-      if (tt < ntok && row0 + 32 * gq < a.M) {
-        float rv[8];
+      // wave w finishes row blocks 2w and 2w+1, one 32-row group: lane (r, kq) holds the
+      // group's values 4kq .. 4kq+3 and 16+4kq .. 19+4kq of token r / 4, which it
+      // quantizes with the lanes kq' of the same r
+      for (int w2 = wave; 2 * w2 < RB; w2 += 4) {
+        float act[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) rv[i] = sAct[tt * ROWS + 32 * gq + 8 * k4 + i];
-        uint8_t *rec = a.outq + (size_t)(n0 + tt) * (size_t)(a.M / 32) * kGroupRec +
-                       (size_t)(row0 / 32 + gq) * kGroupRec;
-        quant_group_fp6(rv, k4, rec);
+        for (int h = 0; h < 2; ++h) {
+          f32x4 v[NA];
+          reduce_rb(2 * w2 + h, v);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) act[4 * h + i] = situ(v[0][i], v[NA - 1][i], a.b1, a.b2);
+        }
+        const bool st = tok_ok && 2 * w2 < nrb;
+        uint8_t *rec = a.outq + (size_t)(n0 + (st ? tn : 0)) * (size_t)(a.M / 32) * kGroupRec +
+                       (size_t)(row0 / 32 + w2) * kGroupRec;
+        quant_group_fp6_kq(act, kq, rec, st);
+      }
+    } else {
+      for (int r = wave; r < RB; r += 4) {
+        f32x4 v[NA];
+        reduce_rb(r, v);
+        if (tok_ok && r < nrb) *(f32x4 *)(a.out + (size_t)(n0 + tn) * a.M + row0 + 16 * r + 4 * kq) = v[0];
       }
     }
     __syncthreads();  // the next tile rewrites the staged activations
@@ -716,8 +709,8 @@ __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
 }
 
 size_t grouped_dec_lds(int K, int tt, int rb) {
-  // scale bytes of up to two matrices, then max(staged pieces, partial sums + SiTU
-  // outputs), then the four waves' weight tiles
+  // scale bytes of up to two matrices, then max(staged pieces, partial sums), then the
+  // four waves' weight tiles
   return grouped_dec_tiles_off(K, tt, rb) + (size_t)4 * kDecPair;
 }
 
