@@ -514,7 +514,9 @@ int run_combine(const k3moe_dims *d, int32_t T, const float *edn, const int32_t 
     a.ss = w.ss;
     a.nss = (d->latent + 255) / 256;
     a.eps = d->eps;
-    K3_HIP(launch_dense_mm(a, kPieces, kEpiStoreScaled, s));
+    // two bf16 pieces (hi + lo) of the normed aggregate: the dropped third piece is
+    // below 2^-17 of each value
+    K3_HIP(launch_dense_mm(a, 2, kEpiStoreScaled, s));
   } else if (use_gemv1(d, T, nullptr)) {
     K3_HIP(launch_gemv1(up1_args(d, w_up, y, w), kA_BF16, kX_PLANES, kEpiStoreScaled, 2, s));
   } else {
