@@ -9,8 +9,9 @@ change from step to step, and the steps rotate over copies of the dense weights 
 default, 128 MB each), so those are not served from the 256 MB MALL either. A
 K3-shape prefill pass (T = 4096) is reported beside it.
 
-Prints one JSON line (rank 0). Per-kernel times come from HIP events recorded between
-the kernels of the same steps (k3moe_layer_profiled) on the stream they run on.
+Prints one JSON line (rank 0). Per-kernel times come from the same kind of steps run
+through k3moe_layer_profiled, which binds a pair of HIP events to each kernel launch's
+own start and end on the stream it runs on; a step's time is the sum over its launches.
 """
 from __future__ import annotations
 
@@ -60,6 +61,18 @@ class HipEvents:
     def close(self):
         for h in self.ev:
             self.hip.hipEventDestroy(h)
+
+
+MAX_LAUNCHES = 32  # timed kernel launches per profiled layer call, more than one layer call makes
+
+
+def launch_ms(events: HipEvents, names):
+    """Kernel time in ms per step name of one profiled call: launch i ran between
+    events[2i] and events[2i+1]."""
+    out = {}
+    for i, n in enumerate(names):
+        out[n] = out.get(n, 0.0) + events.ms(events.ev[2 * i], events.ev[2 * i + 1])
+    return out
 
 
 def traffic_from_profile(kernel: str):
@@ -121,7 +134,7 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=3)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=32)
+    ap.add_argument("--cpu-tokens", type=int, default=64)
     ap.add_argument("--dense-copies", type=int, default=4,
                     help="copies of the dense weights (router, projections) the decode steps rotate "
                          "over, so no step finds them still cached in the MALL from the step before")
@@ -217,18 +230,17 @@ def main():
 
     # per-kernel event marks over the same kind of steps
     nprof = min(args.steps, 100)
-    pe = HipEvents(16)
+    pe = HipEvents(2 * MAX_LAUNCHES)
     sums = {}
-    names = []
     for i in range(nprof):
         j = i % pool
         names = k3moe.k3moe_layer_profiled(dims, T, xs.data_ptr() + j * row, wts_rot[i % len(wts_rot)], y,
                                            idx[j], tw[j], ws, pe.ev, stream=stream)
         torch.cuda.synchronize()
-        for k, n in enumerate(names):
-            sums[n] = sums.get(n, 0.0) + pe.ms(pe.ev[k], pe.ev[k + 1])
+        for n, v in launch_ms(pe, names).items():
+            sums[n] = sums.get(n, 0.0) + v
     pe.close()
-    kern_us = {n: sums[n] / nprof * 1e3 for n in names}
+    kern_us = {n: v / nprof * 1e3 for n, v in sums.items()}
     log("per-kernel us: " + ", ".join(f"{n} {v:.1f}" for n, v in kern_us.items()))
 
     alg = algorithmic(dims, T, dims.topk)
@@ -262,10 +274,10 @@ def main():
         torch.cuda.synchronize()
         msp = evp.ms(evp.ev[0], evp.ev[1]) / args.prefill_steps
         evp.close()
-        pep = HipEvents(16)
+        pep = HipEvents(2 * MAX_LAUNCHES)
         names_p = k3moe.k3moe_layer_profiled(dims, Tp, xp, wts, yp, None, None, wsp, pep.ev, stream=stream)
         torch.cuda.synchronize()
-        kern_p = {n: round(pep.ms(pep.ev[k], pep.ev[k + 1]) * 1e3, 1) for k, n in enumerate(names_p)}
+        kern_p = {n: round(v * 1e3, 1) for n, v in launch_ms(pep, names_p).items()}
         pep.close()
         algp = algorithmic(dims, Tp, dims.n_experts)
         tf = algp["flops"] / (msp * 1e-3) / 1e12

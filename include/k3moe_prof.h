@@ -1,5 +1,5 @@
-/* k3moe profiling entry: the whole layer with an event mark after every kernel.
- * For measurement tools only; the result is identical to k3moe_layer. */
+/* k3moe profiling entry: the whole layer with every kernel launch timed by its own pair
+ * of events. For measurement tools only; the result is identical to k3moe_layer. */
 #ifndef K3MOE_PROF_H
 #define K3MOE_PROF_H
 
@@ -13,10 +13,13 @@ extern "C" {
 #endif
 
 /* As k3moe_layer. events[0 .. max_events-1] are hipEvent_t handles created by the
- * caller (timing enabled); events[0] is recorded on the stream before the first kernel
- * and events[i] right after kernel i-1, for as many kernels as fit. *n_kernels receives
- * the number of kernels marked; k3moe_prof_name(i) names kernel i of that call (static
- * storage). Not reentrant: one profiled call at a time per process. */
+ * caller (timing enabled). Kernel launch i of the call takes the pair events[2 i] and
+ * events[2 i + 1], which the HIP runtime binds to that kernel's own start and end
+ * (hipExtLaunchKernel), so their interval is the kernel's duration without the launch
+ * gaps around it. Launches beyond max_events / 2 (at most 64) run untimed. *n_kernels
+ * receives the number of timed launches; k3moe_prof_name(i) names the step launch i
+ * belongs to (static storage; a step such as the dispatch may take several launches).
+ * Not reentrant: one profiled call at a time per process. */
 int k3moe_layer_profiled(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_weights *w,
                          float *y, int32_t *topk_idx_out, float *topk_w_out, void *ws, size_t ws_bytes,
                          void *stream, void **events, int max_events, int *n_kernels);

@@ -10,6 +10,8 @@
 
 using namespace k3;
 
+k3::LaunchTimes k3::g_launch_times;
+
 namespace {
 
 constexpr int kRouterSplits = 7;  // K-splits of the router product (partials summed by top-k)
@@ -144,21 +146,19 @@ int check_ws(const k3moe_dims *d, int32_t T, void *ws, size_t ws_bytes, Ws *out)
   return K3MOE_OK;
 }
 
-// Optional per-kernel event marks (k3moe_layer_profiled): an event is recorded on the
-// stream before the first kernel and after each kernel of the call.
-struct ProfMarks {
-  void **events = nullptr;
-  int max_events = 0;
-  int n = 0;
-  const char *names[64];
+// Profiled calls (k3moe_layer_profiled): every kernel launch is timed by its own event
+// pair (k3::g_launch_times); mark(name) names the launches made since the previous mark.
+constexpr int kMaxProfLaunches = 64;
+struct ProfNames {
+  int named = 0;
+  const char *names[kMaxProfLaunches];
 };
-ProfMarks g_prof;
+ProfNames g_prof;
 
-hipError_t mark(const char *name, hipStream_t s) {
-  if (!g_prof.events || g_prof.n + 1 >= g_prof.max_events || g_prof.n >= 64) return hipSuccess;
-  g_prof.names[g_prof.n] = name;
-  ++g_prof.n;
-  return hipEventRecord((hipEvent_t)g_prof.events[g_prof.n], s);
+void mark(const char *name) {
+  if (!g_launch_times.events) return;
+  for (; g_prof.named < g_launch_times.n && g_prof.named < kMaxProfLaunches; ++g_prof.named)
+    g_prof.names[g_prof.named] = name;
 }
 
 #define K3_TRY(expr)                 \
@@ -179,7 +179,7 @@ int run_route_down_mm(const k3moe_dims *d, int32_t T, const uint16_t *x, const f
                       const uint16_t *wd, float *z, const Ws &w, hipStream_t s) {
   const size_t EH = (size_t)d->n_experts * d->hidden;
   K3_HIP(launch_split_planes(wr, EH, w.wr_planes, w.wr_planes + EH, w.wr_planes + 2 * EH, s));
-  K3_HIP(mark("router_weight_split", s));
+  mark("router_weight_split");
   DenseMmArgs a = {};
   const int E = d->n_experts;
   for (int p = 0; p < 3; ++p)
@@ -304,9 +304,9 @@ int run_route(const k3moe_dims *d, int32_t T, const uint16_t *x, const float *wr
   } else {
     K3_HIP(launch_route_down(router_args(d, T, x, wr, w), kRouterSplits, nullptr, s));
   }
-  K3_HIP(mark("router_gemv", s));
+  mark("router_gemv");
   K3_HIP(launch_topk(topk_args(d, T, w.router_part, splits, bias, idx, wt), s));
-  K3_HIP(mark("topk", s));
+  mark("topk");
   return K3MOE_OK;
 }
 
@@ -319,19 +319,19 @@ int run_front(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_wei
     // GEMM form: router planes and W_down in one launch, then the top-k, whose spare
     // waves quantize z
     K3_TRY(run_route_down_mm(d, T, x, wt->w_router, wt->w_down, w.z32, w, s));
-    K3_HIP(mark("router_and_latent_down", s));
+    mark("router_and_latent_down");
     TopkArgs tk = topk_args(d, T, w.router_part, 3, wt->bias, idx, tw);
     tk.z = w.z32;
     tk.zq = w.zq;
     K3_HIP(launch_topk(tk, s));
-    K3_HIP(mark("topk", s));
+    mark("topk");
     *zq_ready = true;
   } else if (use_gemv1(d, T, x)) {
     // one token: the router product and W_down stream in one launch; then one block
     // selects the experts and writes the token's dispatch while its other waves
     // quantize z
     K3_HIP(launch_gemv1_front(router1_args(d, x, wt->w_router, w), down1_args(d, x, wt->w_down, w.z32), s));
-    K3_HIP(mark("router_and_latent_down", s));
+    mark("router_and_latent_down");
     TopkArgs tk = topk_args(d, T, w.router_part, kRouterParts1, wt->bias, idx, tw);
     tk.expert_off = w.expert_off;
     tk.sorted_pair = w.sorted_pair;
@@ -341,13 +341,13 @@ int run_front(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_wei
     tk.z = w.z32;
     tk.zq = w.zq;
     K3_HIP(launch_topk(tk, s));
-    K3_HIP(mark("topk_dispatch_quant", s));
+    mark("topk_dispatch_quant");
     *zq_ready = true;
   } else {
     // GEMV form: the router alone, then W_down streams while other blocks of the same
     // launch select the experts; z is quantized once afterwards
     K3_HIP(launch_route_down(router_args(d, T, x, wt->w_router, w), kRouterSplits, nullptr, s));
-    K3_HIP(mark("router_gemv", s));
+    mark("router_gemv");
     TopkArgs tk = topk_args(d, T, w.router_part, kRouterSplits, wt->bias, idx, tw);
     if (T == 1) {
       tk.expert_off = w.expert_off;
@@ -357,13 +357,13 @@ int run_front(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_wei
       tk.counters = w.counters;
     }
     K3_HIP(launch_down_topk(down, tk, s));
-    K3_HIP(mark(T == 1 ? "latent_down_topk_dispatch" : "latent_down_topk", s));
+    mark(T == 1 ? "latent_down_topk_dispatch" : "latent_down_topk");
     *zq_ready = false;
   }
   if (T != 1) {
     K3_HIP(launch_dispatch(idx, T, d->topk, d->n_experts, w.expert_off, w.sorted_pair, w.pair_slot,
                            w.active, w.counters, w.lrank, w.cnt, s));
-    K3_HIP(mark("dispatch", s));
+    mark("dispatch");
   }
   return K3MOE_OK;
 }
@@ -386,7 +386,7 @@ int run_down(const k3moe_dims *d, int32_t T, const uint16_t *x, const uint16_t *
     const DenseArgs a = down_args(d, T, x, wd, z);
     K3_HIP(launch_dense_bf16(a, 1, kEpiStore, s));
   }
-  K3_HIP(mark("latent_down_gemv", s));
+  mark("latent_down_gemv");
   return K3MOE_OK;
 }
 
@@ -410,7 +410,10 @@ int run_experts(const k3moe_dims *d, int32_t T, const float *z, bool zq_ready, c
     tt >>= 1;
   while (rb_gu > 4 && grouped_dec_lds(d->latent, tt, rb_gu) > kMaxBlockLds) rb_gu -= 2;
   while (rb_dn > 4 && grouped_dec_lds(d->inter, tt, rb_dn) > kMaxBlockLds) rb_dn -= 1;
-  if (mm_gu || mm_dn) K3_HIP(launch_mm_tiles(expert_off, d->n_experts, w.tiles, w.counters + 2, s));
+  if (mm_gu || mm_dn) {
+    K3_HIP(launch_mm_tiles(expert_off, d->n_experts, w.tiles, w.counters + 2, s));
+    mark("expert_tile_table");
+  }
   const int max_tiles = (int)max_mm_tiles(d, T);
 
   const MxMat w1{ex->w1.packed, ex->w1.scales, ex->w1.packed_expert_stride, ex->w1.scales_expert_stride};
@@ -418,7 +421,7 @@ int run_experts(const k3moe_dims *d, int32_t T, const float *z, bool zq_ready, c
   const MxMat w2{ex->w2.packed, ex->w2.scales, ex->w2.packed_expert_stride, ex->w2.scales_expert_stride};
   if (!zq_ready) {
     K3_HIP(launch_quant_rows(z, (size_t)T * d->latent, w.zq, s));
-    K3_HIP(mark("latent_quant", s));
+    mark("latent_quant");
   }
   if (mm_gu) {
     MmArgs m = {};
@@ -458,7 +461,7 @@ int run_experts(const k3moe_dims *d, int32_t T, const float *z, bool zq_ready, c
     g.b2 = d->b2;
     K3_HIP(launch_grouped(g, kEpiSitu, tt, rb_gu, grid_y, s));
   }
-  K3_HIP(mark("expert_gateup_situ", s));
+  mark("expert_gateup_situ");
 
   if (mm_dn) {
     MmArgs m = {};
@@ -492,7 +495,7 @@ int run_experts(const k3moe_dims *d, int32_t T, const float *z, bool zq_ready, c
     h.out = edn;
     K3_HIP(launch_grouped(h, kEpiEdn, tt, rb_dn, grid_y, s));
   }
-  K3_HIP(mark("expert_down", s));
+  mark("expert_down");
   return K3MOE_OK;
 }
 
@@ -501,7 +504,7 @@ int run_combine(const k3moe_dims *d, int32_t T, const float *edn, const int32_t 
                 const Ws &w, hipStream_t s) {
   K3_HIP(launch_combine(edn, pair_slot, topk_w, norm_w, T, d->topk, d->latent, w.np[0], w.np[1],
                         w.np[2], w.ss, s));
-  K3_HIP(mark("combine", s));
+  mark("combine");
   if (use_dense_mm(d, T)) {
     DenseMmArgs a = {};
     a.seg[0] = DenseSeg{w_up, 0, d->hidden, y, d->hidden};
@@ -533,7 +536,7 @@ int run_combine(const k3moe_dims *d, int32_t T, const float *edn, const int32_t 
     a.eps = d->eps;
     K3_HIP(launch_dense_bf16(a, kPieces, kEpiStoreScaled, s));
   }
-  K3_HIP(mark("rmsnorm_up_gemv", s));
+  mark("rmsnorm_up_gemv");
   return K3MOE_OK;
 }
 
@@ -646,16 +649,13 @@ int k3moe_layer_profiled(const k3moe_dims *d, int32_t T, const uint16_t *x, cons
                          float *y, int32_t *topk_idx_out, float *topk_w_out, void *ws, size_t ws_bytes,
                          void *stream, void **events, int max_events, int *n_kernels) {
   if (!events || max_events < 2 || !n_kernels) return K3MOE_EINVAL;
-  g_prof = ProfMarks();
-  g_prof.events = events;
-  g_prof.max_events = max_events;
-  if (hipEventRecord((hipEvent_t)events[0], (hipStream_t)stream) != hipSuccess) {
-    g_prof = ProfMarks();
-    return K3MOE_EHIP;
-  }
+  g_prof = ProfNames();
+  g_launch_times = LaunchTimes();
+  g_launch_times.events = events;
+  g_launch_times.max_launches = (max_events / 2 < kMaxProfLaunches) ? max_events / 2 : kMaxProfLaunches;
   const int rc = k3moe_layer(d, T, x, wt, y, topk_idx_out, topk_w_out, ws, ws_bytes, stream);
-  *n_kernels = g_prof.n;
-  g_prof.events = nullptr;
+  *n_kernels = g_prof.named;
+  g_launch_times = LaunchTimes();
   return rc;
 }
 
@@ -667,7 +667,7 @@ int k3moe_set_expert_path(int mode) {
 }
 
 const char *k3moe_prof_name(int i) {
-  return (i >= 0 && i < g_prof.n && i < 64) ? g_prof.names[i] : "";
+  return (i >= 0 && i < g_prof.named) ? g_prof.names[i] : "";
 }
 
 const char *k3moe_status_str(int status) {

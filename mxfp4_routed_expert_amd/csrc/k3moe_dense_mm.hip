@@ -201,15 +201,18 @@ hipError_t launch_dense_mm(const DenseMmArgs &a, int pieces, int epi, hipStream_
   if (pieces == 1 && epi == kEpiStore) {
     constexpr int NJ = 8;
     const int64_t total = (int64_t)((a.M + 255) / 256) * ((a.N + 16 * NJ - 1) / (16 * NJ));
-    k_dense_mm<1, NJ, kEpiStore><<<(unsigned)(8 * ((total + 7) / 8)), 256, kDmStages * NJ * 1024 + 64 * NJ, s>>>(a);
+    launch_kernel(k_dense_mm<1, NJ, kEpiStore>, (unsigned)(8 * ((total + 7) / 8)), 256,
+                  kDmStages * NJ * 1024 + 64 * NJ, s, a);
   } else if (pieces == 2 && epi == kEpiStoreScaled) {
     constexpr int NJ = 8;
     const int64_t total = (int64_t)((a.M + 255) / 256) * ((a.N + 16 * NJ - 1) / (16 * NJ));
-    k_dense_mm<2, NJ, kEpiStoreScaled><<<(unsigned)(8 * ((total + 7) / 8)), 256, kDmStages * 2 * NJ * 1024 + 64 * NJ, s>>>(a);
+    launch_kernel(k_dense_mm<2, NJ, kEpiStoreScaled>, (unsigned)(8 * ((total + 7) / 8)), 256,
+                  kDmStages * 2 * NJ * 1024 + 64 * NJ, s, a);
   } else if (pieces == 3 && epi == kEpiStoreScaled) {
     constexpr int NJ = 4;
     const int64_t total = (int64_t)((a.M + 255) / 256) * ((a.N + 16 * NJ - 1) / (16 * NJ));
-    k_dense_mm<3, NJ, kEpiStoreScaled><<<(unsigned)(8 * ((total + 7) / 8)), 256, kDmStages * 3 * NJ * 1024 + 64 * NJ, s>>>(a);
+    launch_kernel(k_dense_mm<3, NJ, kEpiStoreScaled>, (unsigned)(8 * ((total + 7) / 8)), 256,
+                  kDmStages * 3 * NJ * 1024 + 64 * NJ, s, a);
   } else {
     return hipErrorInvalidValue;
   }

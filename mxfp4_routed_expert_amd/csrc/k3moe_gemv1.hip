@@ -230,7 +230,7 @@ hipError_t launch_gemv1(const Gemv1Args &a, int af, int xf, int epi, int rpw, hi
   const size_t lds = (size_t)a.K * 4;
 #define G1(AF_, XF_, EPI_, R_) \
   if (af == AF_ && xf == XF_ && epi == EPI_ && rpw == R_) { \
-    k_gemv1<AF_, XF_, EPI_, R_><<<grid, waves * 64, lds, s>>>(a, items); \
+    launch_kernel(k_gemv1<AF_, XF_, EPI_, R_>, grid, waves * 64, lds, s, a, items); \
     return hipGetLastError(); \
   }
   G1(kA_F32, kX_BF16, kEpiStore, 1)
@@ -247,7 +247,7 @@ hipError_t launch_gemv1_front(const Gemv1Args &r, const Gemv1Args &d, hipStream_
   const int r_items = r.M * r.ks, items = r_items + d.M;
   const int waves = gemv1_waves(items);
   const int grid = (items + waves - 1) / waves;
-  k_gemv1_front<<<grid, waves * 64, (size_t)d.K * 4, s>>>(r, d, r_items, items);
+  launch_kernel(k_gemv1_front, grid, waves * 64, (size_t)d.K * 4, s, r, d, r_items, items);
   return hipGetLastError();
 }
 

@@ -1,10 +1,36 @@
 // Kernel argument blocks and launcher declarations for the k3moe library (internal).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace k3 {
+
+// ---------------------------------------------------------------- launches
+// Per-kernel timing for profiled layer calls: while `events` is set, each launch made
+// through launch_kernel takes the next (start, stop) pair of caller-created events,
+// which the runtime binds to that kernel's own begin and end; otherwise (and once the
+// pairs run out) launches are plain. Host-side state, one profiled call at a time.
+struct LaunchTimes {
+  void **events = nullptr;  // events[2 i], events[2 i + 1]: launch i
+  int max_launches = 0;
+  int n = 0;                // launches timed so far
+};
+extern LaunchTimes g_launch_times;
+
+template <typename... P, typename... A>
+inline void launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t s,
+                          A... args) {
+  LaunchTimes &t = g_launch_times;
+  if (t.events && t.n < t.max_launches) {
+    const int i = t.n++;
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, s, (hipEvent_t)t.events[2 * i],
+                          (hipEvent_t)t.events[2 * i + 1], 0, args...);
+  } else {
+    kernel<<<grid, block, lds, s>>>(args...);
+  }
+}
 
 constexpr int kMaxRouterSplits = 8;  // partial router products summed by the top-k
 constexpr int kMaxNormParts = 64;    // column blocks of 256 in one latent row (latent <= 16384)

@@ -180,7 +180,7 @@ hipError_t launch_route_down(const DenseArgs &r, int ks, const DenseArgs *d, hip
   const int d_rb = d ? (d->M + 15) / 16 : 0;
   DenseArgs dd = d ? *d : r;
   dim3 grid(r_rb * ks + d_rb, 1, (r.N + 15) / 16);
-  k_route_down<<<grid, kRouteDownWaves * 64, 0, s>>>(r, r_rb, ks, dd, d_rb);
+  launch_kernel(k_route_down, grid, kRouteDownWaves * 64, 0, s, r, r_rb, ks, dd, d_rb);
   return hipGetLastError();
 }
 
@@ -188,9 +188,9 @@ hipError_t launch_dense_bf16(const DenseArgs &a, int pieces, int epi, hipStream_
   const int tpt = 16 / pieces;
   dim3 grid((a.M + 15) / 16, 1, (a.N + tpt - 1) / tpt);
   if (pieces == 1 && epi == kEpiStore)
-    k_dense<kA_BF16, 1, kEpiStore, 8><<<grid, 512, 0, s>>>(a);
+    launch_kernel(k_dense<kA_BF16, 1, kEpiStore, 8>, grid, 512, 0, s, a);
   else if (pieces == 3 && epi == kEpiStoreScaled)
-    k_dense<kA_BF16, 3, kEpiStoreScaled, 4><<<grid, 256, 0, s>>>(a);
+    launch_kernel(k_dense<kA_BF16, 3, kEpiStoreScaled, 4>, grid, 256, 0, s, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -225,7 +225,7 @@ __global__ __launch_bounds__(kRouteDownWaves * 64) void k_down_topk(DenseArgs d,
 hipError_t launch_down_topk(const DenseArgs &d, const TopkArgs &tk, hipStream_t s) {
   const int d_rb = (d.M + 15) / 16;
   dim3 grid(d_rb + tk.T, 1, (d.N + 15) / 16);
-  k_down_topk<<<grid, kRouteDownWaves * 64, 0, s>>>(d, d_rb, tk);
+  launch_kernel(k_down_topk, grid, kRouteDownWaves * 64, 0, s, d, d_rb, tk);
   return hipGetLastError();
 }
 
@@ -233,7 +233,7 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t s) {
   const int64_t tasks = a.z ? (int64_t)a.T * (a.L / 8) : 0;
   const int64_t grid = a.T + (tasks + 1023) / 1024;
   if (grid > INT32_MAX || tasks > INT32_MAX) return hipErrorInvalidValue;
-  k_topk<<<(unsigned)grid, 1024, 0, s>>>(a);
+  launch_kernel(k_topk, (unsigned)grid, 1024, 0, s, a);
   return hipGetLastError();
 }
 
@@ -358,16 +358,16 @@ hipError_t launch_dispatch(const int32_t *topk_idx, int T, int K, int E, int32_t
                            int32_t *sorted_pair, int32_t *pair_slot, int32_t *active,
                            int32_t *counters, int32_t *lrank, int32_t *cnt, hipStream_t s) {
   if (T <= kChunk) {
-    k_dispatch_one<<<1, 1024, 0, s>>>(topk_idx, T, K, E, expert_off, sorted_pair, pair_slot, active,
-                                      counters);
+    launch_kernel(k_dispatch_one, 1, 1024, 0, s, topk_idx, T, K, E, expert_off, sorted_pair, pair_slot,
+                  active, counters);
     return hipGetLastError();
   }
   const int nch = (T + kChunk - 1) / kChunk;
-  k_dispatch_count<<<nch, 256, 0, s>>>(topk_idx, T, K, E, lrank, cnt);
-  k_dispatch_scan<<<1, 1024, 0, s>>>(nch, E, T, K, cnt, expert_off, active, counters);
+  launch_kernel(k_dispatch_count, nch, 256, 0, s, topk_idx, T, K, E, lrank, cnt);
+  launch_kernel(k_dispatch_scan, 1, 1024, 0, s, nch, E, T, K, cnt, expert_off, active, counters);
   const int P = T * K;
-  k_dispatch_scatter<<<(P + 255) / 256, 256, 0, s>>>(topk_idx, T, K, E, lrank, cnt, sorted_pair,
-                                                     pair_slot);
+  launch_kernel(k_dispatch_scatter, (P + 255) / 256, 256, 0, s, topk_idx, T, K, E, lrank, cnt,
+                sorted_pair, pair_slot);
   return hipGetLastError();
 }
 
@@ -384,7 +384,7 @@ __global__ __launch_bounds__(1024) void k_active_from_off(const int32_t *__restr
 
 hipError_t launch_active_from_off(const int32_t *expert_off, int E, int32_t *active,
                                   int32_t *counters, hipStream_t s) {
-  k_active_from_off<<<1, 1024, 0, s>>>(expert_off, E, active, counters);
+  launch_kernel(k_active_from_off, 1, 1024, 0, s, expert_off, E, active, counters);
   return hipGetLastError();
 }
 
@@ -406,7 +406,7 @@ hipError_t launch_split_planes(const float *src, size_t n, uint16_t *p0, uint16_
   if (n == 0) return hipSuccess;
   size_t blocks = (n + 255) / 256;
   if (blocks > 8192) blocks = 8192;
-  k_split_planes<<<(unsigned)blocks, 256, 0, s>>>(src, n, p0, p1, p2);
+  launch_kernel(k_split_planes, (unsigned)blocks, 256, 0, s, src, n, p0, p1, p2);
   return hipGetLastError();
 }
 
@@ -723,7 +723,7 @@ static hipError_t launch_grouped_t(const GroupedArgs &a, dim3 grid, size_t lds, 
       return hipErrorInvalidValue;
     attr = true;
   }
-  k_grouped_dec<NA, TT, EPI, DEPTH, RB><<<grid, 256, lds, s>>>(a);
+  launch_kernel(k_grouped_dec<NA, TT, EPI, DEPTH, RB>, grid, 256, lds, s, a);
   return hipGetLastError();
 }
 
@@ -800,7 +800,7 @@ hipError_t launch_quant_rows(const float *src, size_t n, uint8_t *dst, hipStream
   const size_t n8 = n / 8;
   size_t blocks = (n8 + 255) / 256;
   if (blocks > 4096) blocks = 4096;
-  k_quant_rows<<<(unsigned)blocks, 256, 0, s>>>(src, n8, dst);
+  launch_kernel(k_quant_rows, (unsigned)blocks, 256, 0, s, src, n8, dst);
   return hipGetLastError();
 }
 
@@ -857,7 +857,7 @@ hipError_t launch_combine(const float *edn, const int32_t *pair_slot, const floa
                           uint16_t *p2, float *ss_part, hipStream_t s) {
   if (T == 0) return hipSuccess;
   dim3 grid((L + 255) / 256, T);
-  k_combine<<<grid, 256, 0, s>>>(edn, pair_slot, topk_w, gamma, K, L, p0, p1, p2, ss_part);
+  launch_kernel(k_combine, grid, 256, 0, s, edn, pair_slot, topk_w, gamma, K, L, p0, p1, p2, ss_part);
   return hipGetLastError();
 }
 

@@ -424,7 +424,7 @@ size_t grouped_mm_lds() { return (size_t)K3_MM_STAGES * kStageB; }
 
 hipError_t launch_mm_tiles(const int32_t *expert_off, int E, int4 *tiles, int32_t *n_tiles, hipStream_t s) {
   if (E > 1024) return hipErrorInvalidValue;
-  k_mm_tiles<<<1, 1024, 0, s>>>(expert_off, E, tiles, n_tiles);
+  launch_kernel(k_mm_tiles, 1, 1024, 0, s, expert_off, E, tiles, n_tiles);
   return hipGetLastError();
 }
 
@@ -441,7 +441,7 @@ static hipError_t launch_mm_t(const MmArgs &a, unsigned grid, size_t lds, hipStr
       return hipErrorInvalidValue;
     attr = true;
   }
-  k_grouped_mm<NA, EPI, K3_MM_WAVES, K3_MM_STAGES><<<grid, K3_MM_WAVES * 64, lds, s>>>(a);
+  launch_kernel(k_grouped_mm<NA, EPI, K3_MM_WAVES, K3_MM_STAGES>, grid, K3_MM_WAVES * 64, lds, s, a);
   return hipGetLastError();
 }
 

@@ -202,8 +202,8 @@ def k3moe_layer(dims, T, x, weights: k3moe_weights, y, topk_idx_out, topk_w_out,
 
 def k3moe_layer_profiled(dims, T, x, weights: k3moe_weights, y, topk_idx_out, topk_w_out, ws, events,
                          stream=None):
-    """As k3moe_layer, recording the given hipEvent_t handles around each kernel.
-    Returns the kernel names in launch order."""
+    """As k3moe_layer, each kernel launch i bound to the event pair events[2i], events[2i+1]
+    (its own start and end). Returns the step name of each timed launch, in launch order."""
     p, n = _ws(ws)
     arr = (ctypes.c_void_p * len(events))(*events)
     nk = ctypes.c_int(0)
