@@ -311,9 +311,12 @@ int run_route(const k3moe_dims *d, int32_t T, const uint16_t *x, const float *wr
 }
 
 // The layer's front: router, latent projection z (fp32, w.z32), top-k and dispatch.
-// Returns in *zq_ready whether z's piece records (w.zq) were written too.
+// Returns in *zq_ready whether z's piece records (w.zq) were written too. With `route`
+// given, a one-token batch whose gate/up pass runs in its GEMV form leaves the top-k,
+// the dispatch and z's quantization to that pass: *route receives their arguments
+// (route->T = 1; otherwise route->T stays 0).
 int run_front(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_weights *wt, int32_t *idx,
-              float *tw, const Ws &w, bool *zq_ready, hipStream_t s) {
+              float *tw, const Ws &w, bool *zq_ready, TopkArgs *route, hipStream_t s) {
   const DenseArgs down = down_args(d, T, x, wt->w_down, w.z32);
   if (use_dense_mm(d, T) && d->n_experts % 64 == 0) {
     // GEMM form: router planes and W_down in one launch, then the top-k, whose spare
@@ -327,9 +330,9 @@ int run_front(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_wei
     mark("topk");
     *zq_ready = true;
   } else if (use_gemv1(d, T, x)) {
-    // one token: the router product and W_down stream in one launch; then one block
-    // selects the experts and writes the token's dispatch while its other waves
-    // quantize z
+    // one token: the router product and W_down stream in one launch; then the gate/up
+    // pass selects the experts itself, or else one block selects them and writes the
+    // token's dispatch while the launch's other blocks quantize z
     K3_HIP(launch_gemv1_front(router1_args(d, x, wt->w_router, w), down1_args(d, x, wt->w_down, w.z32), s));
     mark("router_and_latent_down");
     TopkArgs tk = topk_args(d, T, w.router_part, kRouterParts1, wt->bias, idx, tw);
@@ -340,6 +343,16 @@ int run_front(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_wei
     tk.counters = w.counters;
     tk.z = w.z32;
     tk.zq = w.zq;
+    GroupedArgs g = {};
+    g.K = d->latent;
+    g.gather = 1;
+    g.tk = tk;
+    if (route && !use_mm(d, T, d->latent, (int64_t)T * d->latent * 4, wt->ex.w1, wt->ex.w3) &&
+        route_in_gateup_ok(g)) {
+      *route = tk;
+      *zq_ready = false;
+      return K3MOE_OK;
+    }
     K3_HIP(launch_topk(tk, s));
     mark("topk_dispatch_quant");
     *zq_ready = true;
@@ -390,10 +403,11 @@ int run_down(const k3moe_dims *d, int32_t T, const uint16_t *x, const uint16_t *
   return K3MOE_OK;
 }
 
-// z: the latent [T][L] fp32; zq_ready: w.zq already holds its piece records.
-int run_experts(const k3moe_dims *d, int32_t T, const float *z, bool zq_ready, const k3moe_experts *ex,
-                const int32_t *expert_off, const int32_t *sorted_pair, const int32_t *active,
-                const int32_t *counters, float *edn, const Ws &w, hipStream_t s) {
+// z: the latent [T][L] fp32; zq_ready: w.zq already holds its piece records. route
+// (nullable): a one-token selection that the gate/up pass runs itself (run_front).
+int run_experts(const k3moe_dims *d, int32_t T, const float *z, bool zq_ready, const TopkArgs *route,
+                const k3moe_experts *ex, const int32_t *expert_off, const int32_t *sorted_pair,
+                const int32_t *active, const int32_t *counters, float *edn, const Ws &w, hipStream_t s) {
   const uint8_t *zq = w.zq;
   const int64_t P = (int64_t)T * d->topk;
   const bool mm_gu = use_mm(d, T, d->latent, (int64_t)T * d->latent * 4, ex->w1, ex->w3);
@@ -419,7 +433,8 @@ int run_experts(const k3moe_dims *d, int32_t T, const float *z, bool zq_ready, c
   const MxMat w1{ex->w1.packed, ex->w1.scales, ex->w1.packed_expert_stride, ex->w1.scales_expert_stride};
   const MxMat w3{ex->w3.packed, ex->w3.scales, ex->w3.packed_expert_stride, ex->w3.scales_expert_stride};
   const MxMat w2{ex->w2.packed, ex->w2.scales, ex->w2.packed_expert_stride, ex->w2.scales_expert_stride};
-  if (!zq_ready) {
+  if (route && mm_gu) return K3MOE_EINVAL;  // run_front only defers to the GEMV form
+  if (!zq_ready && !route) {
     K3_HIP(launch_quant_rows(z, (size_t)T * d->latent, w.zq, s));
     mark("latent_quant");
   }
@@ -459,9 +474,10 @@ int run_experts(const k3moe_dims *d, int32_t T, const float *z, bool zq_ready, c
     g.outq = w.actq;
     g.b1 = d->b1;
     g.b2 = d->b2;
-    K3_HIP(launch_grouped(g, kEpiSitu, tt, rb_gu, grid_y, s));
+    if (route) g.tk = *route;
+    K3_HIP(launch_grouped(g, kEpiSitu, tt, rb_gu, grid_y, s, route != nullptr));
   }
-  mark("expert_gateup_situ");
+  mark(route ? "topk_expert_gateup_situ" : "expert_gateup_situ");
 
   if (mm_dn) {
     MmArgs m = {};
@@ -605,7 +621,7 @@ int k3moe_expert_glu_mxfp4(const k3moe_dims *d, int32_t T, const float *z, const
   if (T == 0) return K3MOE_OK;
   hipStream_t s = (hipStream_t)stream;
   K3_HIP(launch_active_from_off(expert_off, d->n_experts, w.active, w.counters, s));
-  return run_experts(d, T, z, false, ex, expert_off, sorted_pair, w.active, w.counters, edn, w, s);
+  return run_experts(d, T, z, false, nullptr, ex, expert_off, sorted_pair, w.active, w.counters, edn, w, s);
 }
 
 int k3moe_combine(const k3moe_dims *d, int32_t T, const float *edn, const int32_t *pair_slot,
@@ -639,9 +655,10 @@ int k3moe_layer(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_w
   int32_t *idx = topk_idx_out ? topk_idx_out : w.idx;
   float *tw = topk_w_out ? topk_w_out : w.w;
   bool zq_ready = false;
-  K3_TRY(run_front(d, T, x, wt, idx, tw, w, &zq_ready, s));
-  K3_TRY(run_experts(d, T, w.z32, zq_ready, &wt->ex, w.expert_off, w.sorted_pair, w.active, w.counters,
-                     w.edn, w, s));
+  TopkArgs route = {};
+  K3_TRY(run_front(d, T, x, wt, idx, tw, w, &zq_ready, &route, s));
+  K3_TRY(run_experts(d, T, w.z32, zq_ready, route.T ? &route : nullptr, &wt->ex, w.expert_off, w.sorted_pair,
+                     w.active, w.counters, w.edn, w, s));
   return run_combine(d, T, w.edn, w.pair_slot, tw, wt->norm_w, wt->w_up, y, w, s);
 }
 

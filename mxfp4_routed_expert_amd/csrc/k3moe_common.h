@@ -14,6 +14,55 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
+// ---- cross-lane moves without an LDS round trip (DPP and the gfx950 lane swaps)
+// x from lane l ^ 1 and from lane l ^ 2 (quad permutations)
+__device__ __forceinline__ float lane_xor1(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_xor2(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
+}
+// max of x over lanes l, l ^ 16, l ^ 32, l ^ 48: the row swaps hand every lane the
+// values of the other 16-lane row of its pair, then of the other 32-lane half
+__device__ __forceinline__ float max_rows4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+// inclusive prefix sum over the wave's 64 lanes (lane 0 first): Hillis-Steele inside
+// each 16-lane row, then each row adds the totals of the rows before it
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+  return x;
+}
+// integer sum over the wave (exact; the same in every lane)
+__device__ __forceinline__ int wave_sum_int(int x) {
+  x += __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+  x += __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+  x += __builtin_amdgcn_mov_dpp(x, 0x124, 0xF, 0xF, false);  // row_ror:4
+  x += __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false);  // row_ror:8
+  return __builtin_amdgcn_readlane(x, 0) + __builtin_amdgcn_readlane(x, 16) + __builtin_amdgcn_readlane(x, 32) +
+         __builtin_amdgcn_readlane(x, 48);
+}
+// sum over the wave in a fixed order: quads, then rows (rotations inside the row), then
+// the four row totals in row order; the result is the same in every lane
+__device__ __forceinline__ float wave_sum_fixed(float x) {
+  x += lane_xor1(x);
+  x += lane_xor2(x);
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xF, 0xF, false));  // row_ror:4
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false));  // row_ror:8
+  return (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0)) +
+          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16))) +
+         (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32)) +
+          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48)));
+}
+
 // Raw buffer loads: a uniform base and size (an SGPR descriptor) plus 32-bit per-lane
 // and uniform offsets. An access past the size returns zeros instead of faulting, so
 // masked lanes load branch-free by pointing past the end (kOOB).
@@ -119,84 +168,124 @@ __device__ __forceinline__ f32x4 mfma_fp4_fp6(u32x4 a, const uint32_t (&b)[6], u
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 2, 0, (int)sa, 0, (int)sb);
 }
 
-// Round |q| < 8 to the nearest e2m3 magnitude (ties to even), saturating at 7.5;
-// returns the code (sign in bit 5) and the rounded value. At or above 1 the value keeps
-// 3 mantissa bits (an fp32 round-to-nearest-even on the bit pattern, whose carry moves
-// into the exponent); below 1 the grid is the multiples of 1/8 (the subnormal codes).
-__device__ __forceinline__ uint32_t e2m3_round(float q, float &rounded) {
-  const float a = fabsf(q);
-  const uint32_t u = __float_as_uint(a);
-  const float big = fminf(__uint_as_float((u + 0x7FFFFu + ((u >> 20) & 1u)) & 0xFFF00000u), 7.5f);
-  // a * 8 + 2^23 rounds a * 8 to an integer (ties to even) in the low mantissa bits
-  const uint32_t k = __float_as_uint(fmaf(a, 8.f, 8388608.f)) & 15u;  // 0 .. 8
-  // both candidates are computed and blended with a mask (no divergent branch)
-  const uint32_t msk = (uint32_t)-(int32_t)(a < 1.f);
-  const uint32_t code = (k & msk) | (((__float_as_uint(big) >> 20) - (126u << 3)) & ~msk);
-  const uint32_t arb = (__float_as_uint((float)k * 0.125f) & msk) | (__float_as_uint(big) & ~msk);
-  const uint32_t sgn = __float_as_uint(q) & 0x80000000u;
-  rounded = __uint_as_float(arb | sgn);
-  return code | (sgn >> 26);
+typedef unsigned u32x6 __attribute__((ext_vector_type(6)));
+typedef int i32x6 __attribute__((ext_vector_type(6)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x32 __attribute__((ext_vector_type(32)));
+
+// A group's piece exponent: 2^-e puts its largest residual magnitude m in [4, 8)
+// (e = floor(log2 m) - 2, clamped to the ue8m0 range; 0 for an all-zero residual).
+__device__ __forceinline__ int fp6_piece_exp(float m) {
+  const int eb = (int)((__float_as_uint(m) >> 23) & 255u) - 127 - 2;
+  return m > 0.f ? max(-127, min(127, eb)) : 0;
 }
 
-// One piece of a group: m is the group's largest residual magnitude. The scale puts m in
-// [4, 8) (scale = 2^(floor(log2 m) - 2)); the lane's 8 residuals become codes c and lose
-// the rounded piece, which is exact. Returns the scale exponent.
-__device__ __forceinline__ int fp6_piece(float (&r)[8], float m, uint32_t (&c)[8]) {
-  int e = 0;
-  if (m > 0.f) e = (int)((__float_as_uint(m) >> 23) & 255u) - 127 - 2;
-  e = max(-127, min(127, e));
+// One fp6 piece of up to four 8-value slices at once, on the hardware e2m3 conversion:
+// y[n][0..7] are this lane's values of slice n in record order and ex[n] its group's
+// piece exponent. The values are scaled by 2^-ex exactly, rounded to e2m3 (nearest,
+// ties to even, saturating at 7.5), decoded back, and the rounded piece is subtracted
+// from y (exactly). Returns the codes: slice n's 8 codes at bits 48n .. 48n+47.
+template <int N>
+__device__ __forceinline__ u32x6 fp6_piece_hw(float (&y)[N][8], const int (&ex)[N]) {
+  static_assert(N >= 1 && N <= 4, "one conversion holds 32 values");
+  f32x16 va, vb;  // value 2i of slice n at va[4n + i], value 2i+1 at vb[4n + i]
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float rq;
-    c[i] = e2m3_round(ldexpf(r[i], -e), rq);
-    r[i] -= ldexpf(rq, e);
-  }
-  return e;
+  for (int n = 0; n < 4; ++n)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      va[4 * n + i] = n < N ? ldexpf(y[n < N ? n : 0][2 * i], -ex[n < N ? n : 0]) : 0.f;
+      vb[4 * n + i] = n < N ? ldexpf(y[n < N ? n : 0][2 * i + 1], -ex[n < N ? n : 0]) : 0.f;
+    }
+  const u32x6 c = __builtin_bit_cast(u32x6, __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(va, vb, 1.0f));
+  const f32x32 r = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(__builtin_bit_cast(i32x6, c), 1.0f);
+#pragma unroll
+  for (int n = 0; n < N; ++n)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) y[n][j] -= ldexpf(r[8 * n + j], ex[n]);
+  return c;
 }
 
-// Quantize one group of 32 values held by 4 consecutive lanes (8 values each, lane
-// k4 = 0..3 holding values 8*k4 .. 8*k4+7) into kFp6Pieces piece records at rec.
-// Each piece takes the residual of the previous ones; its scale puts the residual's
-// largest magnitude m in [4, 8) (scale = 2^(floor(log2 m) - 2)); every subtraction is
-// exact, so after 4 pieces the dropped remainder is below 2^-20 of the group maximum.
-__device__ __forceinline__ void quant_group_fp6(float (&r)[8], int k4, uint8_t *rec) {
+// Quantize N groups of 32 values (N <= 4), each held by 4 consecutive lanes (8 values
+// each: lane k4 = 0..3 holds values 8*k4 .. 8*k4+7 of every group), into kFp6Pieces
+// piece records at rec[n]; groups with ok[n] false are computed but not written (the
+// four lanes of a group agree on ok). Each piece takes the residual of the previous
+// ones at its own scale (fp6_piece_exp); every subtraction is exact, so after 4 pieces
+// the dropped remainder is below 2^-20 of the group maximum.
+template <int N>
+__device__ __forceinline__ void quant_groups_fp6(float (&r)[N][8], int k4, uint8_t *const (&rec)[N],
+                                                 const bool (&ok)[N]) {
+#pragma unroll
+  for (int p = 0; p < kFp6Pieces; ++p) {
+    int ex[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      float m = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(r[n][i]));
+      m = fmaxf(m, lane_xor1(m));
+      m = fmaxf(m, lane_xor2(m));
+      ex[n] = fp6_piece_exp(m);
+    }
+    const u32x6 c = fp6_piece_hw<N>(r, ex);
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      if (!ok[n]) continue;
+      // lane k4's 48 bits are bytes 6*k4 .. 6*k4+5 of the code stream
+      uint8_t *dst = rec[n] + p * kPieceRec;
+#pragma unroll
+      for (int h = 0; h < 3; ++h) {
+        const int bit = 48 * n + 16 * h;
+        *(uint16_t *)(dst + 6 * k4 + 2 * h) = (uint16_t)(c[bit >> 5] >> (bit & 31));
+      }
+      if (k4 == 0) dst[24] = (uint8_t)(ex[n] + 127);
+    }
+  }
+}
+
+// One group of 32 values held by one lane (v[i] = value i) into kFp6Pieces piece
+// records at rec (16-byte aligned; the pad bytes 25..27 of each record are written as
+// zero).
+__device__ __forceinline__ void quant_group32_fp6(float (&v)[32], uint8_t *rec) {
 #pragma unroll
   for (int p = 0; p < kFp6Pieces; ++p) {
     float m = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(r[i]));
-    m = fmaxf(m, __shfl_xor(m, 1, 4));
-    m = fmaxf(m, __shfl_xor(m, 2, 4));
-    uint32_t c[8];
-    const int e = fp6_piece(r, m, c);
-    uint64_t bits = 0;
+    for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(v[i]));
+    const int ex = fp6_piece_exp(m);
+    f32x16 va, vb;  // value 2i at va[i], value 2i+1 at vb[i]: codes in value order
 #pragma unroll
-    for (int i = 0; i < 8; ++i) bits |= (uint64_t)c[i] << (6 * i);
-    uint8_t *dst = rec + p * kPieceRec;
-    // lane k4's 48 bits are bytes 6*k4 .. 6*k4+5 of the code stream
-    *(uint16_t *)(dst + 6 * k4) = (uint16_t)bits;
-    *(uint16_t *)(dst + 6 * k4 + 2) = (uint16_t)(bits >> 16);
-    *(uint16_t *)(dst + 6 * k4 + 4) = (uint16_t)(bits >> 32);
-    if (k4 == 0) dst[24] = (uint8_t)(e + 127);
+    for (int i = 0; i < 16; ++i) {
+      va[i] = ldexpf(v[2 * i], -ex);
+      vb[i] = ldexpf(v[2 * i + 1], -ex);
+    }
+    const u32x6 c = __builtin_bit_cast(u32x6, __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(va, vb, 1.0f));
+    const f32x32 r = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(__builtin_bit_cast(i32x6, c), 1.0f);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] -= ldexpf(r[i], ex);
+    uint32_t *dst = (uint32_t *)(rec + p * kPieceRec);
+    *(u32x4 *)dst = u32x4{c[0], c[1], c[2], c[3]};
+    *(u32x2 *)(dst + 4) = u32x2{c[4], c[5]};
+    dst[6] = (uint32_t)(ex + 127);
   }
 }
 
-// The same for a group laid out as a 16x16 matrix-core result: lanes l, l^16, l^32,
+// The same for one group laid out as a 16x16 matrix-core result: lanes l, l^16, l^32,
 // l^48 (kq = l / 16) hold the group's values 4kq .. 4kq+3 (r[0..3]) and 16+4kq .. 19+4kq
 // (r[4..7]). rec is the group's record (LDS or global); every lane takes part in the
 // group maxima, and only lanes with st set write.
 __device__ __forceinline__ void quant_group_fp6_kq(float (&r)[8], int kq, uint8_t *rec, bool st = true) {
+  float y[1][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[0][i] = r[i];
 #pragma unroll
   for (int p = 0; p < kFp6Pieces; ++p) {
     float m = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(r[i]));
-    m = fmaxf(m, __shfl_xor(m, 16, 64));
-    m = fmaxf(m, __shfl_xor(m, 32, 64));
-    uint32_t c[8];
-    const int e = fp6_piece(r, m, c);
-    const uint32_t lo = c[0] | (c[1] << 6) | (c[2] << 12) | (c[3] << 18);  // values 4kq .. 4kq+3
-    const uint32_t hi = c[4] | (c[5] << 6) | (c[6] << 12) | (c[7] << 18);  // values 16+4kq ..
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(y[0][i]));
+    const int ex[1] = {fp6_piece_exp(max_rows4(m))};
+    const u32x6 c = fp6_piece_hw<1>(y, ex);
+    const uint32_t lo = c[0] & 0xFFFFFFu;                          // values 4kq .. 4kq+3
+    const uint32_t hi = ((c[0] >> 24) | (c[1] << 8)) & 0xFFFFFFu;  // values 16+4kq ..
     if (st) {
       uint8_t *dst = rec + p * kPieceRec;
       dst[3 * kq] = (uint8_t)lo;
@@ -205,7 +294,7 @@ __device__ __forceinline__ void quant_group_fp6_kq(float (&r)[8], int kq, uint8_
       dst[12 + 3 * kq] = (uint8_t)hi;
       dst[12 + 3 * kq + 1] = (uint8_t)(hi >> 8);
       dst[12 + 3 * kq + 2] = (uint8_t)(hi >> 16);
-      if (kq == 0) dst[24] = (uint8_t)(e + 127);
+      if (kq == 0) dst[24] = (uint8_t)(ex[0] + 127);
     }
   }
 }

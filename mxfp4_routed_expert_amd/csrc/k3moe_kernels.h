@@ -99,6 +99,21 @@ struct MxMat {
 
 enum GroupedEpi { kEpiSitu = 0, kEpiEdn = 1 };
 
+// One token's expert selection from the router's partial sums (k3moe_topk.h).
+struct TopkArgs {
+  const float *part;
+  int ks, T, E;
+  const float *bias;
+  int K, renorm;
+  float rscale;
+  int32_t *idx;
+  float *w;
+  const float *z;
+  int L;
+  uint8_t *zq;
+  int32_t *expert_off, *sorted_pair, *pair_slot, *active, *counters;
+};
+
 struct GroupedArgs {
   MxMat A[2];             // gate/up: {w1, w3}; down: {w2}
   int M, K, ng;           // rows, cols, groups per row
@@ -108,6 +123,7 @@ struct GroupedArgs {
   float *out;             // kEpiEdn: [slot][M] fp32
   uint8_t *outq;          // kEpiSitu: [slot][M/32] fp6 piece records of act
   float b1, b2;
+  TopkArgs tk;            // routed in the launch (one token): its selection and its z
 };
 
 // Grouped GEMM form of the same two passes (many tokens per expert); K % 128 == 0.
@@ -136,19 +152,6 @@ hipError_t launch_dense_mm(const DenseMmArgs &a, int pieces, int epi, hipStream_
 // Router top-k of T tokens from ks partial logit arrays [ks][T][E]. Optional: z [T][L]
 // fp32 quantized into zq piece records meanwhile; for T == 1, expert_off .. counters
 // receive that token's dispatch (as launch_dispatch would write it).
-struct TopkArgs {
-  const float *part;
-  int ks, T, E;
-  const float *bias;
-  int K, renorm;
-  float rscale;
-  int32_t *idx;
-  float *w;
-  const float *z;
-  int L;
-  uint8_t *zq;
-  int32_t *expert_off, *sorted_pair, *pair_slot, *active, *counters;
-};
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
 // one token: af kA_BF16/kA_F32, xf kX_BF16/kX_PLANES, epi kEpiStore/kEpiStoreScaled, rpw
 // rows per wave (1 or 2)
@@ -174,7 +177,13 @@ size_t grouped_dec_lds(int K, int tokens_per_tile, int rb);
 int grouped_dec_rb(int M, int grid_y, int epi, int ncu);
 // compute units of the current device
 int num_cus();
-hipError_t launch_grouped(const GroupedArgs &a, int epi, int tokens_per_tile, int rb, int grid_y, hipStream_t s);
+// route: a one-token gate/up pass (kEpiSitu, one token per tile) that first selects the
+// token's experts itself from a.tk (every block the same selection; block (0, 0) writes
+// the ids, weights and dispatch of a.tk) and quantizes a.tk.z; grid_y = a.tk.K slots,
+// a.tk.E <= 1024, a.tk.ks <= 2 and a.K <= 4096 (route_in_gateup_ok).
+bool route_in_gateup_ok(const GroupedArgs &a);
+hipError_t launch_grouped(const GroupedArgs &a, int epi, int tokens_per_tile, int rb, int grid_y, hipStream_t s,
+                          bool route = false);
 // column tiles of kMmBN slots per expert: at most ceil(P / kMmBN) + min(E, P) entries
 hipError_t launch_mm_tiles(const int32_t *expert_off, int E, int4 *tiles, int32_t *n_tiles, hipStream_t s);
 size_t grouped_mm_lds();

@@ -202,7 +202,7 @@ hipError_t launch_dense_bf16(const DenseArgs &a, int pieces, int epi, hipStream_
 // quantize z [T][L] into its piece records.
 __global__ __launch_bounds__(1024) void k_topk(TopkArgs a) {
   if ((int)blockIdx.x < a.T) {
-    topk_body(a, blockIdx.x);
+    topk_body<2>(a, blockIdx.x);
     return;
   }
   const int q = ((int)blockIdx.x - a.T) * blockDim.x + threadIdx.x;
@@ -219,7 +219,7 @@ __global__ __launch_bounds__(kRouteDownWaves * 64) void k_down_topk(DenseArgs d,
     return;
   }
   if (blockIdx.z != 0) return;
-  topk_body(tk, b - d_rb);
+  topk_body<2>(tk, b - d_rb);
 }
 
 hipError_t launch_down_topk(const DenseArgs &d, const TopkArgs &tk, hipStream_t s) {
@@ -441,12 +441,6 @@ __device__ __forceinline__ void dma16(rsrc_t r, uint8_t *lds, uint32_t voff, uin
 }
 
 // ============================================================== grouped MXFP4 (decode)
-#ifndef K3_GATEUP_DEPTH
-#define K3_GATEUP_DEPTH 2
-#endif
-#ifndef K3_DOWN_DEPTH
-#define K3_DOWN_DEPTH 2
-#endif
 // Grid: x = blocks of RB 16-row blocks, y = active-expert slots. The block's four waves
 // share the same 16 RB rows. With one matrix (down) the waves split K four ways; with
 // two (gate w1 and up w3) waves 0-1 stream w1 and waves 2-3 stream w3, each pair
@@ -456,7 +450,7 @@ __device__ __forceinline__ void dma16(rsrc_t r, uint8_t *lds, uint32_t voff, uin
 // resident at once.
 // Weights stream from HBM in whole 128-byte lines: a step is 128 bytes (256 columns)
 // of each of the block's rows, read by 2 RB loads of 8 rows x 128 B (lane i: row i / 8,
-// 16-byte unit i % 8), DEPTH steps in flight in registers. Each 16-row block of a step
+// 16-byte unit i % 8), the next step in flight in registers. Each 16-row block of a step
 // is written to the wave's LDS tile and read back as matrix-core fragments (16 rows x
 // 16 B units); rows are 128 bytes apart, so unit u of row r is kept at unit u ^ (r % 8)
 // and the second 8-row chunk is shifted by 128 bytes, which makes both the writes and
@@ -466,6 +460,10 @@ __device__ __forceinline__ void dma16(rsrc_t r, uint8_t *lds, uint32_t voff, uin
 // columns of a step are TT tokens x 4 pieces, summed across lanes in the epilogue. A
 // tile's piece records are staged in LDS once; the block's scale bytes are staged once
 // per block.
+// With RT (one token, gate/up) the launch also routes: every block runs the token's
+// expert selection (the same inputs and arithmetic, so the same result in every block)
+// and takes the expert in its slot, and quantizes the token's z straight into its LDS
+// records; block (0, 0) writes the selection and the dispatch for the later passes.
 constexpr int kDecPair = 2048 + 128;  // a wave's tile: two 8-row chunks, the second shifted by 128 B
 
 __host__ __device__ inline size_t grouped_dec_sb_off(int K, int rb) {
@@ -477,8 +475,9 @@ __host__ __device__ inline size_t grouped_dec_tiles_off(int K, int tt, int rb) {
   return grouped_dec_sb_off(K, rb) + (((stage > red ? stage : red) + 15) & ~(size_t)15);
 }
 
-template <int NA, int TT, int EPI, int DEPTH, int RB>
+template <int NA, int TT, int EPI, int RT, int RB>
 __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
+  static_assert(!RT || (NA == 2 && TT == 1 && EPI == kEpiSitu), "routing runs in the one-token gate/up pass");
   constexpr int KSPLIT = 4 / NA;
   constexpr int PB = kFp6Pieces;
   constexpr int NL = 2 * RB;  // loads per step
@@ -489,11 +488,44 @@ __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
   const int rl = lane & 15, kq = lane >> 4;
   const int tn = rl / PB, piece = rl % PB;
   const int j = blockIdx.y;
-  if (j >= *a.n_active) return;
   // uniform across the block: scalar registers, so the buffer descriptors are scalar
-  const int e = __builtin_amdgcn_readfirstlane(a.active[j]);
-  const int lo = __builtin_amdgcn_readfirstlane(a.expert_off[e]);
-  const int hi = __builtin_amdgcn_readfirstlane(a.expert_off[e + 1]);
+  int e, lo, hi;
+  if constexpr (RT) {
+    __shared__ int s_e;
+    __shared__ __attribute__((aligned(16))) uint32_t s_scr[448];
+    if (threadIdx.x == 0) s_e = 0;  // written again by the selecting lane
+    // wave 0 selects the token's experts from its own loads; waves 2-3 quantize one
+    // 32-value group of the token's z per lane into its piece records (token row 0 of
+    // the staged activations)
+    if (wave == 0) {
+      uint32_t key[16];
+      float sc[16];
+      bool real[16];
+      topk_keys_wave<16, 2>(a.tk, 0, key, sc, real);
+      topk_select_wave<16>(a.tk, 0, key, sc, real, s_scr, blockIdx.x == 0 && j == 0, j, &s_e);
+    } else if (wave >= 2) {
+      const int gz = (int)threadIdx.x - 128;
+      if (gz < a.K / 32) {
+        float zv[32];
+        const float4 *zp = (const float4 *)(a.tk.z + 32 * (size_t)gz);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float4 q = zp[i];
+          zv[4 * i] = q.x; zv[4 * i + 1] = q.y; zv[4 * i + 2] = q.z; zv[4 * i + 3] = q.w;
+        }
+        quant_group32_fp6(zv, smem + grouped_dec_sb_off(a.K, RB) + (size_t)gz * kGroupRec);
+      }
+    }
+    __syncthreads();
+    e = __builtin_amdgcn_readfirstlane(min(max(s_e, 0), a.tk.E - 1));
+    lo = j;
+    hi = j + 1;
+  } else {
+    if (j >= *a.n_active) return;
+    e = __builtin_amdgcn_readfirstlane(a.active[j]);
+    lo = __builtin_amdgcn_readfirstlane(a.expert_off[e]);
+    hi = __builtin_amdgcn_readfirstlane(a.expert_off[e + 1]);
+  }
   constexpr int ROWS = 16 * RB;
   const int row0 = blockIdx.x * ROWS;
   const uint32_t rowb = (uint32_t)a.K / 2, ng = (uint32_t)a.ng;
@@ -543,7 +575,7 @@ __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
   // When the block's scale rows and token records are whole kilobytes, the memory unit
   // copies them straight into LDS (buffer loads with an LDS destination) ahead of the
   // weight stream, and one wait before the K loop covers them.
-  bool dma = (nb % 1024 == 0) && (brow_bytes % 1024 == 0);
+  bool dma = (nb % 1024 == 0) && (RT || brow_bytes % 1024 == 0);
 #pragma unroll
   for (int m = 0; m < NA; ++m)
     dma = dma && ((((uintptr_t)(a.A[m].scales + (size_t)e * a.A[m].sstride + (size_t)row0 * ng)) & 15) == 0);
@@ -551,7 +583,7 @@ __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
   int brow0[TT];
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt)
-    brow0[tt] = __builtin_amdgcn_readfirstlane(tt < ntok0 ? (a.gather ? a.sorted_pair[lo + tt] / a.topk : lo + tt) : 0);
+    brow0[tt] = RT ? 0 : __builtin_amdgcn_readfirstlane(tt < ntok0 ? (a.gather ? a.sorted_pair[lo + tt] / a.topk : lo + tt) : 0);
   if (dma) {
     const int nsc = nb / 1024, nbc = brow_bytes / 1024;
     for (int i = wave; i < NA * nsc; i += 4) {
@@ -559,7 +591,7 @@ __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
       const rsrc_t rS = make_rsrc(a.A[m].scales + (size_t)e * a.A[m].sstride + (size_t)row0 * ng, (uint32_t)nb);
       dma16(rS, sS + m * ROWS * (int)ng + c * 1024, (uint32_t)lane * 16u, (uint32_t)c * 1024u);
     }
-    for (int i = wave; i < ntok0 * nbc; i += 4) {
+    for (int i = wave; i < (RT ? 0 : ntok0 * nbc); i += 4) {
       const int tt = i / nbc, c = i - tt * nbc;
       int br = brow0[0];
 #pragma unroll
@@ -592,10 +624,13 @@ __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
   for (int n0 = lo; n0 < hi; n0 += TT) {
     const int ntok = min(TT, hi - n0);
     if (n0 != lo) load(s_lo);
-    if (dma && n0 == lo) {
+    if (RT || (dma && n0 == lo)) {
       // this wave's copies precede exactly the one step of weight loads issued since
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(NL));
+      // (routed: the token's records are already in LDS)
+      if (dma) {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(NL));
+      }
     } else {
       // stage the tile's activation piece records (one row of ng * 128 bytes per token)
 #pragma unroll
@@ -672,8 +707,8 @@ __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float t = v[m][i];
-          t += __shfl_xor(t, 1, 4);
-          t += __shfl_xor(t, 2, 4);
+          t += lane_xor1(t);
+          t += lane_xor2(t);
           v[m][i] = t;
         }
       }
@@ -714,28 +749,31 @@ size_t grouped_dec_lds(int K, int tt, int rb) {
   return grouped_dec_tiles_off(K, tt, rb) + (size_t)4 * kDecPair;
 }
 
-template <int NA, int TT, int EPI, int DEPTH, int RB>
+template <int NA, int TT, int EPI, int RT, int RB>
 static hipError_t launch_grouped_t(const GroupedArgs &a, dim3 grid, size_t lds, hipStream_t s) {
   static bool attr = false;  // allow up to kMaxBlockLds of dynamic LDS (above the 64 KB default)
   if (!attr) {
-    if (hipFuncSetAttribute((const void *)k_grouped_dec<NA, TT, EPI, DEPTH, RB>,
+    if (hipFuncSetAttribute((const void *)k_grouped_dec<NA, TT, EPI, RT, RB>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxBlockLds) != hipSuccess)
       return hipErrorInvalidValue;
     attr = true;
   }
-  launch_kernel(k_grouped_dec<NA, TT, EPI, DEPTH, RB>, grid, 256, lds, s, a);
+  launch_kernel(k_grouped_dec<NA, TT, EPI, RT, RB>, grid, 256, lds, s, a);
   return hipGetLastError();
 }
 
-template <int NA, int EPI, int DEPTH, int RB>
-static hipError_t launch_grouped_tt(const GroupedArgs &a, int tt, int grid_y, hipStream_t s) {
+template <int NA, int EPI, int RB>
+static hipError_t launch_grouped_tt(const GroupedArgs &a, int tt, int grid_y, bool route, hipStream_t s) {
   const size_t lds = grouped_dec_lds(a.K, tt, RB);
   if (lds > kMaxBlockLds) return hipErrorInvalidValue;
   const dim3 grid((a.M + 16 * RB - 1) / (16 * RB), grid_y);
+  if constexpr (NA == 2 && EPI == kEpiSitu) {
+    if (route) return launch_grouped_t<NA, 1, EPI, 1, RB>(a, grid, lds, s);
+  }
   switch (tt) {
-    case 1: return launch_grouped_t<NA, 1, EPI, DEPTH, RB>(a, grid, lds, s);
-    case 2: return launch_grouped_t<NA, 2, EPI, DEPTH, RB>(a, grid, lds, s);
-    default: return launch_grouped_t<NA, 4, EPI, DEPTH, RB>(a, grid, lds, s);
+    case 1: return launch_grouped_t<NA, 1, EPI, 0, RB>(a, grid, lds, s);
+    case 2: return launch_grouped_t<NA, 2, EPI, 0, RB>(a, grid, lds, s);
+    default: return launch_grouped_t<NA, 4, EPI, 0, RB>(a, grid, lds, s);
   }
 }
 
@@ -754,22 +792,32 @@ int grouped_dec_rb(int M, int grid_y, int epi, int ncu) {
   return best;
 }
 
-hipError_t launch_grouped(const GroupedArgs &a, int epi, int tokens_per_tile, int rb, int grid_y, hipStream_t s) {
+bool route_in_gateup_ok(const GroupedArgs &a) {
+  const TopkArgs &t = a.tk;
+  return t.T == 1 && t.ks >= 1 && t.ks <= 2 && t.E >= 1 && t.E <= 1024 && t.K >= 1 && t.K <= t.E && t.K <= 64 &&
+         t.L == a.K && a.K % 32 == 0 &&
+         a.K <= 4096 && t.z && t.idx && t.w && t.expert_off && t.sorted_pair && t.pair_slot && t.active &&
+         t.counters && ((uintptr_t)t.z & 15) == 0 && a.gather == 1;
+}
+
+hipError_t launch_grouped(const GroupedArgs &a, int epi, int tokens_per_tile, int rb, int grid_y, hipStream_t s,
+                          bool route) {
   if (grid_y <= 0) return hipSuccess;
+  if (route && (epi != kEpiSitu || grid_y != a.tk.K || !route_in_gateup_ok(a))) return hipErrorInvalidValue;
   if (epi == kEpiSitu) {
     switch (rb) {
-      case 4: return launch_grouped_tt<2, kEpiSitu, K3_GATEUP_DEPTH, 4>(a, tokens_per_tile, grid_y, s);
-      case 6: return launch_grouped_tt<2, kEpiSitu, K3_GATEUP_DEPTH, 6>(a, tokens_per_tile, grid_y, s);
-      case 8: return launch_grouped_tt<2, kEpiSitu, K3_GATEUP_DEPTH, 8>(a, tokens_per_tile, grid_y, s);
+      case 4: return launch_grouped_tt<2, kEpiSitu, 4>(a, tokens_per_tile, grid_y, route, s);
+      case 6: return launch_grouped_tt<2, kEpiSitu, 6>(a, tokens_per_tile, grid_y, route, s);
+      case 8: return launch_grouped_tt<2, kEpiSitu, 8>(a, tokens_per_tile, grid_y, route, s);
       default: return hipErrorInvalidValue;
     }
   }
   switch (rb) {
-    case 4: return launch_grouped_tt<1, kEpiEdn, K3_DOWN_DEPTH, 4>(a, tokens_per_tile, grid_y, s);
-    case 5: return launch_grouped_tt<1, kEpiEdn, K3_DOWN_DEPTH, 5>(a, tokens_per_tile, grid_y, s);
-    case 6: return launch_grouped_tt<1, kEpiEdn, K3_DOWN_DEPTH, 6>(a, tokens_per_tile, grid_y, s);
-    case 7: return launch_grouped_tt<1, kEpiEdn, K3_DOWN_DEPTH, 7>(a, tokens_per_tile, grid_y, s);
-    case 8: return launch_grouped_tt<1, kEpiEdn, K3_DOWN_DEPTH, 8>(a, tokens_per_tile, grid_y, s);
+    case 4: return launch_grouped_tt<1, kEpiEdn, 4>(a, tokens_per_tile, grid_y, false, s);
+    case 5: return launch_grouped_tt<1, kEpiEdn, 5>(a, tokens_per_tile, grid_y, false, s);
+    case 6: return launch_grouped_tt<1, kEpiEdn, 6>(a, tokens_per_tile, grid_y, false, s);
+    case 7: return launch_grouped_tt<1, kEpiEdn, 7>(a, tokens_per_tile, grid_y, false, s);
+    case 8: return launch_grouped_tt<1, kEpiEdn, 8>(a, tokens_per_tile, grid_y, false, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -781,17 +829,19 @@ __global__ __launch_bounds__(256) void k_quant_rows(const float *__restrict__ sr
                                                     uint8_t *__restrict__ dst) {
   for (size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x; t < ((n8 + 3) & ~(size_t)3);
        t += (size_t)gridDim.x * blockDim.x) {
-    float rv[8];
+    float rv[1][8];
     const bool ok = t < n8;
     const float4 *p = (const float4 *)(src + (ok ? t : 0) * 8);
     const float4 lo = p[0], hi = p[1];
-    rv[0] = lo.x; rv[1] = lo.y; rv[2] = lo.z; rv[3] = lo.w;
-    rv[4] = hi.x; rv[5] = hi.y; rv[6] = hi.z; rv[7] = hi.w;
+    rv[0][0] = lo.x; rv[0][1] = lo.y; rv[0][2] = lo.z; rv[0][3] = lo.w;
+    rv[0][4] = hi.x; rv[0][5] = hi.y; rv[0][6] = hi.z; rv[0][7] = hi.w;
     if (!ok) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) rv[i] = 0.f;
+      for (int i = 0; i < 8; ++i) rv[0][i] = 0.f;
     }
-    quant_group_fp6(rv, (int)(t & 3), dst + (t >> 2) * kGroupRec);
+    uint8_t *const rec[1] = {dst + (t >> 2) * kGroupRec};
+    const bool wr[1] = {true};
+    quant_groups_fp6<1>(rv, (int)(t & 3), rec, wr);
   }
 }
 

@@ -56,10 +56,6 @@ __device__ __forceinline__ void dma16(rsrc_t r, uint8_t *lds, uint32_t voff, uin
 }
 
 typedef unsigned u32x3 __attribute__((ext_vector_type(3)));
-typedef unsigned u32x6 __attribute__((ext_vector_type(6)));
-typedef int i32x6 __attribute__((ext_vector_type(6)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x32 __attribute__((ext_vector_type(32)));
 
 }  // namespace
 
