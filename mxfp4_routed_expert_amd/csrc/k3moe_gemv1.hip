@@ -11,7 +11,6 @@
 // launch is one block per compute unit with equal work in every block.
 #include "k3moe_common.h"
 #include "k3moe_kernels.h"
-#include "k3moe_topk.h"
 
 namespace k3 {
 

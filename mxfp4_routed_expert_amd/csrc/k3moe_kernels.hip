@@ -197,15 +197,19 @@ hipError_t launch_dense_bf16(const DenseArgs &a, int pieces, int epi, hipStream_
 }
 
 // ============================================================== router top-k
-// (topk_body: k3moe_topk.h)
-// Blocks 0 .. T-1: one token's top-k each; the blocks after them (when a.z is set)
-// quantize z [T][L] into its piece records.
-__global__ __launch_bounds__(1024) void k_topk(TopkArgs a) {
-  if ((int)blockIdx.x < a.T) {
-    topk_body<2>(a, blockIdx.x);
+// (topk_wave: k3moe_topk.h) Blocks 0 .. ceil(T/4)-1: one token per wave; the blocks
+// after them (when a.z is set) quantize z [T][L] into its piece records.
+template <int KS>
+__global__ __launch_bounds__(256) void k_topk(TopkArgs a) {
+  __shared__ __attribute__((aligned(16))) uint32_t s_scr[4][448];
+  const int nsel = (a.T + 3) / 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if ((int)blockIdx.x < nsel) {
+    const int t = 4 * (int)blockIdx.x + wave;
+    if (t < a.T) topk_wave<KS>(a, t, s_scr[wave]);
     return;
   }
-  const int q = ((int)blockIdx.x - a.T) * blockDim.x + threadIdx.x;
+  const int q = ((int)blockIdx.x - nsel) * 256 + threadIdx.x;
   if (q < a.T * (a.L / 8)) quant_task(a.z, a.zq, q);  // whole 4-lane groups (L % 32 == 0)
 }
 
@@ -218,8 +222,9 @@ __global__ __launch_bounds__(kRouteDownWaves * 64) void k_down_topk(DenseArgs d,
     dense_body<kA_BF16, 1, kEpiStore, kRouteDownWaves>(d, b, 0, 1, blockIdx.z);
     return;
   }
-  if (blockIdx.z != 0) return;
-  topk_body<2>(tk, b - d_rb);
+  __shared__ __attribute__((aligned(16))) uint32_t s_scr[448];
+  if (blockIdx.z != 0 || threadIdx.x >= 64) return;
+  topk_wave<kMaxRouterSplits>(tk, b - d_rb, s_scr);
 }
 
 hipError_t launch_down_topk(const DenseArgs &d, const TopkArgs &tk, hipStream_t s) {
@@ -231,9 +236,16 @@ hipError_t launch_down_topk(const DenseArgs &d, const TopkArgs &tk, hipStream_t 
 
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s) {
   const int64_t tasks = a.z ? (int64_t)a.T * (a.L / 8) : 0;
-  const int64_t grid = a.T + (tasks + 1023) / 1024;
-  if (grid > INT32_MAX || tasks > INT32_MAX) return hipErrorInvalidValue;
-  launch_kernel(k_topk, (unsigned)grid, 1024, 0, s, a);
+  const int64_t grid = (a.T + 3) / 4 + (tasks + 255) / 256;
+  if (grid > INT32_MAX || tasks > INT32_MAX || a.ks < 1 || a.ks > kMaxRouterSplits || a.E > 1024)
+    return hipErrorInvalidValue;
+  if (a.ks <= 2) {
+    launch_kernel(k_topk<2>, (unsigned)grid, 256, 0, s, a);
+  } else if (a.ks == 3) {
+    launch_kernel(k_topk<3>, (unsigned)grid, 256, 0, s, a);
+  } else {
+    launch_kernel(k_topk<kMaxRouterSplits>, (unsigned)grid, 256, 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -7,209 +7,15 @@
 
 namespace k3 {
 
-// One block per token. Its threads turn the partial logits into unbiased scores
+// One wave per token. The wave turns the router's partial logits into unbiased scores
 // sc = sigmoid(logit) and selection scores ch = sc + bias, each held as ch's
-// order-preserving 32-bit key (expert e in thread e % blockDim, slot e / blockDim). The
-// K-th largest key tau is found by a radix select over the key bytes, most significant
-// first: per byte, a 256-bin LDS histogram of the keys that match the bytes chosen so
-// far, and one wave's scan of it from the top. Every expert above tau is chosen and,
-// among those equal to tau, the lowest ids (so equal selection scores go to the lower
-// id); the chosen ids are written in ascending order with their unbiased scores
-// renormalised over the chosen and times routed_scale.
+// order-preserving 32-bit key (expert e in lane e % 64, slot e / 64). The chosen are
+// the K first in the order (key descending, then id ascending, so equal selection
+// scores go to the lower id); they are written in ascending id order with their
+// unbiased scores renormalised over the chosen and times routed_scale.
 __device__ __forceinline__ uint32_t order_key(float f) {
   const uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Exclusive counts, in id order, of the block's true flags f[j] for ids j * blockDim +
-// tid (slot j, thread tid), and their total. s_w holds J * 16 ints, one count per slot
-// and wave; one block barrier, so a second call needs its own s_w.
-template <int J>
-__device__ __forceinline__ void block_excl_counts(const bool (&f)[J], int *s_w, int (&before)[J], int *total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  unsigned long long m[J];
-#pragma unroll
-  for (int j = 0; j < J; ++j) {
-    m[j] = __ballot(f[j]);
-    if (lane == 0) s_w[j * 16 + wave] = __popcll(m[j]);
-  }
-  __syncthreads();
-  int run = 0;
-#pragma unroll
-  for (int j = 0; j < J; ++j) {
-    int b = run + __popcll(m[j] & ((1ull << lane) - 1ull));
-    // all 16 slots read at once (the LDS reads overlap); waves past nw count zero
-#pragma unroll
-    for (int w = 0; w < 16; ++w) {
-      const int c = w < nw ? s_w[j * 16 + w] : 0;
-      b += w < wave ? c : 0;
-      run += c;
-    }
-    before[j] = b;
-  }
-  *total = run;
-}
-
-// Token t's router inputs for experts e = tid + j * blockDim: the partial logits and
-// the bias (ids past E: not real, zeros).
-template <int J>
-struct TopkIn {
-  float pv[J][kMaxRouterSplits], bs[J];
-  bool real[J];
-};
-template <int J>
-__device__ __forceinline__ void topk_load(const TopkArgs &a, int t, TopkIn<J> &in) {
-  const int E = a.E, bd = blockDim.x;
-  // the partial sums were written by blocks on every XCD: issue all loads at once
-#pragma unroll
-  for (int j = 0; j < J; ++j) {
-    const int e = threadIdx.x + j * bd;
-    in.real[j] = e < E;
-    const int ec = in.real[j] ? e : 0;
-#pragma unroll
-    for (int k = 0; k < kMaxRouterSplits; ++k)
-      in.pv[j][k] = k < a.ks ? a.part[((size_t)k * a.T + t) * E + ec] : 0.f;
-    in.bs[j] = a.bias[ec];
-  }
-}
-// The unbiased scores sc = sigmoid(logit) and the order keys of ch = sc + bias.
-template <int J>
-__device__ __forceinline__ void topk_keys(const TopkIn<J> &in, float (&sc)[J], uint32_t (&key)[J]) {
-#pragma unroll
-  for (int j = 0; j < J; ++j) {
-    float logit = 0.f;
-#pragma unroll
-    for (int k = 0; k < kMaxRouterSplits; ++k) logit += in.pv[j][k];
-    sc[j] = in.real[j] ? 1.0f / (1.0f + expf(-logit)) : 0.f;
-    key[j] = in.real[j] ? order_key(sc[j] + in.bs[j]) : 0u;
-  }
-}
-
-// The selection of token t from its scores: the K-th largest key tau by a radix select
-// (two barriers per byte: the histogram of the next byte is cleared while one wave
-// scans this one), then the chosen ids in ascending order with their weights. With
-// `out` the block writes the token's ids and weights (and, with a.expert_off set, the
-// dispatch of a one-token batch: its K pairs in ascending expert order are the K slots
-// themselves). With slot >= 0, *s_slot_e receives the chosen id at that position; it
-// is visible to the block after the caller's next barrier.
-template <int J>
-__device__ __forceinline__ void topk_select(const TopkArgs &a, int t, const float (&sc)[J],
-                                            const uint32_t (&key)[J], const bool (&real)[J], bool out,
-                                            int slot, int *s_slot_e) {
-  __shared__ uint32_t hist[2][256];
-  __shared__ uint32_t s_pick[2];
-  __shared__ int s_weq[J * 16], s_wsel[J * 16];
-  __shared__ float s_ws[16];
-  const int E = a.E, K = a.K, bd = blockDim.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = bd >> 6;
-  for (int i = threadIdx.x; i < 512; i += bd) (&hist[0][0])[i] = 0u;
-  __syncthreads();
-  // radix select of the K-th largest key, one byte per pass
-  uint32_t prefix = 0u, mask = 0u;
-  int krem = K;  // how many of the keys matching `prefix` are still to be taken
-#pragma unroll
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    uint32_t *h = hist[pass & 1];
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-      // the keys of a wave often share their leading bytes: the two bins of the first
-      // lanes still to count are added once per wave, the rest lane by lane
-      bool in = real[j] && (key[j] & mask) == prefix;
-      const uint32_t bin = (key[j] >> shift) & 255u;
-#pragma unroll
-      for (int peel = 0; peel < 2; ++peel) {
-        const unsigned long long mi = __ballot(in);
-        if (mi != 0ull) {
-          const int l0 = __builtin_ctzll(mi);
-          const uint32_t b0 = (uint32_t)__builtin_amdgcn_readlane((int)bin, l0);
-          const unsigned long long mb = __ballot(in && bin == b0);
-          if (lane == l0) atomicAdd(&h[b0], (uint32_t)__popcll(mb));
-          in = in && bin != b0;
-        }
-      }
-      if (in) atomicAdd(&h[bin], 1u);
-    }
-    __syncthreads();
-    if (wave == 0) {
-      // lane l holds the bins of digits 255-4l .. 252-4l (descending)
-      uint32_t c[4], loc = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        c[i] = h[255 - 4 * lane - i];
-        loc += c[i];
-      }
-      const uint32_t incl = wave_incl_scan(loc);
-      uint32_t run = incl - loc;  // keys in higher digits
-      if (run < (uint32_t)krem && (uint32_t)krem <= incl) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (run + c[i] >= (uint32_t)krem) {
-            s_pick[0] = prefix | ((uint32_t)(255 - 4 * lane - i) << shift);
-            s_pick[1] = (uint32_t)krem - run;
-            break;
-          }
-          run += c[i];
-        }
-      }
-    } else if (pass < 3) {
-      // the other buffer was last read by wave 0 in the previous pass
-      for (int i = threadIdx.x - 64; i < 256; i += bd - 64) hist[(pass + 1) & 1][i] = 0u;
-    }
-    __syncthreads();
-    prefix = s_pick[0];
-    krem = (int)s_pick[1];
-    mask |= 255u << shift;
-  }
-  const uint32_t tau = prefix;  // the K-th largest key; krem keys equal to it are taken
-  // choose, and place the chosen in ascending id order
-  bool eq[J], sel[J];
-  int eq_rank[J], pos[J], tot;
-#pragma unroll
-  for (int j = 0; j < J; ++j) eq[j] = real[j] && key[j] == tau;
-  block_excl_counts<J>(eq, s_weq, eq_rank, &tot);
-#pragma unroll
-  for (int j = 0; j < J; ++j) sel[j] = real[j] && (key[j] > tau || (eq[j] && eq_rank[j] < krem));
-  block_excl_counts<J>(sel, s_wsel, pos, &tot);
-  float ssum_part = 0.f;
-#pragma unroll
-  for (int j = 0; j < J; ++j) ssum_part += sel[j] ? sc[j] : 0.f;
-  // renormalisation sum: each wave's in a fixed order, then the waves in order
-  ssum_part = wave_sum_fixed(ssum_part);
-  if (lane == 0) s_ws[wave] = ssum_part;
-  __syncthreads();
-  float ssum = 0.f;
-#pragma unroll
-  for (int w = 0; w < 16; ++w) ssum += w < nw ? s_ws[w] : 0.f;
-#pragma unroll
-  for (int j = 0; j < J; ++j)
-    if (slot >= 0 && sel[j] && pos[j] == slot) *s_slot_e = threadIdx.x + j * bd;
-  if (!out) return;
-#pragma unroll
-  for (int j = 0; j < J; ++j) {
-    if (sel[j] && pos[j] < K) {  // exactly K are chosen; the bound keeps every write inside
-      const int e = threadIdx.x + j * bd;
-      a.idx[(size_t)t * K + pos[j]] = e;
-      a.w[(size_t)t * K + pos[j]] = ((a.renorm && ssum > 0.f) ? sc[j] / ssum : sc[j]) * a.rscale;
-    }
-  }
-  if (a.expert_off) {
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int e = threadIdx.x + j * bd;
-      if (real[j]) a.expert_off[e] = pos[j];
-      if (sel[j] && pos[j] < K) a.active[pos[j]] = e;
-    }
-    for (int p = threadIdx.x; p < K; p += bd) {
-      a.sorted_pair[p] = p;
-      a.pair_slot[p] = p;
-    }
-    if (threadIdx.x == 0) {
-      a.expert_off[E] = K;
-      a.counters[0] = K;
-      a.counters[1] = 0;
-    }
-  }
 }
 
 // ---- one wave per token: experts e = 64 s + lane (slot s < S, E <= 64 S)
@@ -391,15 +197,15 @@ __device__ __forceinline__ void topk_select_wave(const TopkArgs &a, int t, const
   }
 }
 
-// One token's top-k with the block's threads (a multiple of 64, at least 128, J * blockDim >= E).
-template <int J>
-__device__ __forceinline__ void topk_body(const TopkArgs &a, int t) {
-  TopkIn<J> in;
-  float sc[J];
-  uint32_t key[J];
-  topk_load<J>(a, t, in);
-  topk_keys<J>(in, sc, key);
-  topk_select<J>(a, t, sc, key, in.real, true, -1, nullptr);
+// Token t's top-k by the calling wave (E <= 1024, a.ks <= KS): ids and weights, and
+// with a.expert_off set the dispatch of a one-token batch.
+template <int KS>
+__device__ __forceinline__ void topk_wave(const TopkArgs &a, int t, uint32_t *s_scr) {
+  uint32_t key[16];
+  float sc[16];
+  bool real[16];
+  topk_keys_wave<16, KS>(a, t, key, sc, real);
+  topk_select_wave<16>(a, t, key, sc, real, s_scr, true, -1, nullptr);
 }
 
 // Rows of z [rows][L] into fp6 piece records: lane task q (of rows * L / 8) quantizes
