@@ -36,6 +36,7 @@ __device__ __forceinline__ void topk_keys_wave(const TopkArgs &a, int t, uint32_
     for (int k = 0; k < KS; ++k) pv[s][k] = a.part[((size_t)(k < a.ks ? k : 0) * a.T + t) * E + ec];
     bs[s] = a.bias[ec];
   }
+  __builtin_amdgcn_sched_barrier(0);  // every load in flight before the first wait
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     float logit = 0.f;
@@ -101,30 +102,46 @@ __device__ __forceinline__ void topk_select_wave(const TopkArgs &a, int t, const
   bool sel = false;
   float scc = 0.f;
   if (C <= 64) {
+    // the candidates (lane-major), each as one 64-bit number ordering (key, lower id
+    // first), and their scores
+    uint64_t *s_c64 = (uint64_t *)s_scr;  // words 0 .. 127 (the lane maxima are no longer needed)
     int p = incl - n;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
       if (real[s] && key[s] >= lb) {
-        s_scr[128 + p] = key[s];
-        s_scr[192 + p] = (uint32_t)(64 * s + lane);
-        s_scr[256 + p] = __float_as_uint(sc[s]);
+        s_c64[p] = ((uint64_t)key[s] << 32) | (uint32_t)(1023 - (64 * s + lane));
+        s_scr[128 + p] = __float_as_uint(sc[s]);
         ++p;
       }
     }
     wave_lds_sync();
     const bool valid = lane < C;
-    const uint32_t ck = valid ? s_scr[128 + lane] : 0u;
-    ce = valid ? (int)s_scr[192 + lane] : 0;
-    // rank among the candidates: (key, lower id first) as one 64-bit number
-    const uint64_t cm = ((uint64_t)ck << 32) | (uint32_t)(1023 - ce);
+    const uint64_t cm = valid ? s_c64[lane] : 0ull;
+    ce = 1023 - (int)(uint32_t)cm;
+    // rank: the candidates ordered before this one, eight per step
     int r = 0;
-    for (int i = 0; i < C; ++i) r += (((uint64_t)s_scr[128 + i] << 32) | (1023u - s_scr[192 + i])) > cm ? 1 : 0;
+    for (int i = 0; i < C; i += 8) {
+      uint64_t c8[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const u32x4 v = *(const u32x4 *)(s_scr + 2 * i + 4 * q);
+        c8[2 * q] = ((uint64_t)v.y << 32) | v.x;
+        c8[2 * q + 1] = ((uint64_t)v.w << 32) | v.z;
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) r += (i + q < C && c8[q] > cm) ? 1 : 0;
+    }
     sel = valid && r < K;
-    s_scr[320 + lane] = sel ? (uint32_t)ce : 0xFFFFFFFFu;
+    // the chosen ids, compacted, then this one's place among them
+    const unsigned long long ms = __builtin_amdgcn_ballot_w64(sel);
+    if (sel) s_scr[192 + __builtin_popcountll(ms & ((1ull << lane) - 1ull))] = (uint32_t)ce;
     wave_lds_sync();
-    // position among the chosen: chosen ids below this one
-    for (int i = 0; i < C; ++i) pos += s_scr[320 + i] < (uint32_t)ce ? 1 : 0;  // the unchosen hold ~0
-    scc = sel ? __uint_as_float(s_scr[256 + lane]) : 0.f;
+    for (int k = 0; k < K; k += 4) {
+      const u32x4 c = *(const u32x4 *)(s_scr + 192 + k);
+      pos += (c.x < (uint32_t)ce ? 1 : 0) + (k + 1 < K && c.y < (uint32_t)ce ? 1 : 0) +
+             (k + 2 < K && c.z < (uint32_t)ce ? 1 : 0) + (k + 3 < K && c.w < (uint32_t)ce ? 1 : 0);
+    }
+    scc = sel ? __uint_as_float(s_scr[128 + lane]) : 0.f;
   }
   if (C > 64) {
     uint32_t tau = 0u;

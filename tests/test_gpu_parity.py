@@ -250,6 +250,45 @@ def test_tiny_dispatch_chunked_and_invalid_ids(tiny):
     assert list(order) == sorted(valid, key=lambda p: (flat[p], p))
 
 
+# 128 experts (two slots per selection lane), top-8, and a router with no x dependence:
+# the selection scores are 0.5 + bias, with many equal values
+TINY_TIES = dataclasses.replace(k3gen.TINY, n_experts=128, topk=8)
+
+
+def ties_bias(kind: str) -> np.ndarray:
+    e = np.arange(TINY_TIES.n_experts)
+    if kind == "all_equal":        # every key equal: the 8 lowest ids
+        b = np.zeros(e.shape)
+    elif kind == "few_values":     # 5 values; the top one held by 26 experts
+        b = ((e * 7) % 5) * 0.01
+    elif kind == "above_and_ties":  # 3 above, then ties at the 8th place
+        b = ((e * 7) % 5) * 0.01
+        b[[3, 50, 100]] = 0.05
+    else:                          # 2 above, 126 equal below them
+        b = np.zeros(e.shape)
+        b[[100, 120]] = 0.05
+    return b.astype(np.float32)
+
+
+@pytest.fixture(scope="module", params=["all_equal", "few_values", "above_and_ties", "two_above_rest_equal"])
+def tiny_ties(request):
+    dense = k3gen.gen_dense(TINY_TIES, 5)
+    dense["w_router"][:] = 0.0
+    dense["bias"][:] = ties_bias(request.param)
+    return request.param, Host(TINY_TIES, 5, dense=dense)
+
+
+@pytest.mark.parametrize("T", [1, 4, 300])
+def test_tiny_selection_ties_lowest_ids(tiny_ties, T):
+    """Equal selection scores go to the lower id, in every top-k path (the one-token
+    launch, one wave per token, the GEMM-form router) and in both branches of the
+    selection (few keys at the bound, and more than 64 of them)."""
+    kind, h = tiny_ties
+    say(f"selection ties {kind} T={T}")
+    x = k3gen.gen_x(TINY_TIES, 7, T)
+    compare_layer(h, x, what=f"ties {kind} T={T}")
+
+
 def test_tiny_combine_random_gamma_and_scale(tiny):
     """RMSNorm weight and routed_scale other than 1 reach the result."""
     import dataclasses
