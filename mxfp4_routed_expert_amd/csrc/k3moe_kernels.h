@@ -127,8 +127,10 @@ struct GroupedArgs {
 };
 
 // Grouped GEMM form of the same two passes (many tokens per expert); K % 128 == 0.
-constexpr int kMmBN = 64;      // tokens per column tile
-constexpr int kMmStages = 3;   // LDS ring depth of the token stream (and weight register ring)
+#ifndef K3_MM_BN
+#define K3_MM_BN 96
+#endif
+constexpr int kMmBN = K3_MM_BN;  // tokens per column tile (a multiple of 32)
 
 struct MmArgs {
   MxMat A[2];             // gate/up: {w1, w3}; down: {w2}

@@ -2,21 +2,22 @@
 //
 // The same two passes as the grouped GEMV (gate/up with the SiTU-GLU epilogue, then
 // down), organised as a GEMM: a block of 8 waves owns 256 rows of w1 and of w3 (gate/up)
-// or 512 rows of w2 (down) of one expert and up to 64 of that expert's tokens, so each
-// weight byte is read from HBM once per 64 tokens.
+// or 512 rows of w2 (down) of one expert and up to kMmBN (96) of that expert's tokens,
+// so each weight byte is read from HBM once per 96 tokens: at 4096 tokens x top-16 of
+// 896 experts (73 pairs per expert on average) nearly every expert is one column tile.
 //
 // Operands, in the layout of the MXFP4 format (low nibble = even column, one ue8m0 scale
 // per 32 columns) and of the fp6 activation pieces:
 //  - A, the weights: every wave owns its rows (32 of w1 and the same 32 of w3, or 64 of
 //    w2: four 16-row fragments), so each lane loads its 16 packed bytes of a 128-column
 //    step (row l % 16, k-block l / 16) and the scale byte straight into registers,
-//    kMmStages-1 steps ahead.
-//  - B, the activations, are shared by the 8 waves: each step's 64 tokens x 512 bytes of
+//    NS-1 steps ahead.
+//  - B, the activations, are shared by the 8 waves: each step's 96 tokens x 512 bytes of
 //    piece records are copied by buffer loads with an LDS destination into a ring of
-//    kMmStages stages. One copy instruction moves two tokens' contiguous 512 bytes; a
+//    NS stages. One copy instruction moves two tokens' contiguous 512 bytes; a
 //    lane's 16-byte slot inside its token is rotated by the token's index, so that the
 //    16 tokens of a matrix-core operand read from 16 different bank groups.
-// A wave multiplies its 4 fragments by the 4 column blocks of 16 tokens, 4 pieces each:
+// A wave multiplies its 4 fragments by the 6 column blocks of 16 tokens, 4 pieces each:
 // the pieces of an activation are consecutive K-chunks against the same weights and sum
 // in the accumulator. The SiTU pairs of a w1 row and the same w3 row sit in one lane,
 // and a wave's 32 rows are exactly one 32-value group, quantized in registers.
@@ -32,7 +33,9 @@ namespace k3 {
 
 namespace {
 
-constexpr int kStageB = kMmBN * 4 * kGroupRec;  // 64 tokens x 4 groups of piece records
+constexpr int kStageB = kMmBN * 4 * kGroupRec;  // kMmBN tokens x 4 groups of piece records
+constexpr int kNcbMax = kMmBN / 16;              // 16-token column blocks per tile
+static_assert(kMmBN % 32 == 0 && kNcbMax <= 8, "two tokens per copy instruction; at most 8 column blocks");
 
 // s_waitcnt with vmcnt <= n and no wait on the other counters (gfx9 encoding)
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
@@ -101,11 +104,13 @@ void k_grouped_mm(MmArgs a) {
   constexpr int RW = BM / NWV;             // rows per wave of each matrix
   constexpr int FPM = RW / 16;             // fragments per matrix per wave
   constexpr int NF = NA * FPM;             // fragments per wave
-  constexpr int DPW = 32 / NWV;            // token copies per wave per step (32 per block)
+  constexpr int DPW = kMmBN / 2 / NWV;     // token copies per wave per step (2 tokens each)
   constexpr int GPW = RW / 32;             // 32-row quantization groups per wave
   constexpr int VMG = NF + DPW;            // loads of one step: weight fragments, token copies
   static_assert(RW % 32 == 0, "a wave's rows are whole quantization groups");
   static_assert(NS == 3 || NS == 4, "ring depth: one scale load (12 or 16 bytes) per ring turn");
+  static_assert((kMmBN / 2) % NWV == 0, "every wave issues the same number of token copies");
+  static_assert((size_t)NS * kStageB <= 160 * 1024, "the token ring fits in LDS");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -231,11 +236,11 @@ void k_grouped_mm(MmArgs a) {
     nan_scales = __builtin_amdgcn_ballot_w64(ff != 0u) != 0;
   };
 
-  f32x4 acc[NF][4];
+  f32x4 acc[NF][kNcbMax];
 #pragma unroll
   for (int i = 0; i < NF; ++i)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[i][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < kNcbMax; ++c) acc[i][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // one step on NCB column blocks; D = the step's place in its scale group. Consecutive
   // matrix-core instructions update different accumulators (all NCB x NF of them between
@@ -319,7 +324,11 @@ void k_grouped_mm(MmArgs a) {
     case 1: kloop(IC<1>{}); break;
     case 2: kloop(IC<2>{}); break;
     case 3: kloop(IC<3>{}); break;
-    default: kloop(IC<4>{}); break;
+    case 4: kloop(IC<4>{}); break;
+    case 5: if constexpr (kNcbMax >= 5) kloop(IC<5>{}); break;
+    case 6: if constexpr (kNcbMax >= 6) kloop(IC<6>{}); break;
+    case 7: if constexpr (kNcbMax >= 7) kloop(IC<7>{}); break;
+    default: if constexpr (kNcbMax >= 8) kloop(IC<8>{}); break;
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the ring's last copies land before LDS is reused
   __syncthreads();
@@ -332,12 +341,17 @@ void k_grouped_mm(MmArgs a) {
     // largest magnitude lies in [4, 8), rounded to e2m3 (nearest, ties to even,
     // saturating) by the hardware conversion, 32 values (4 groups) per instruction, and
     // converted back exactly to form the next residual.
-    constexpr int NG = 4 * GPW;  // groups per lane
+    constexpr int NG = kNcbMax * GPW;  // groups per lane
+    constexpr int NGP = (NG + 3) / 4 * 4;  // padded to whole conversions (4 groups each)
     uint8_t *recs = smem + wave * (kMmBN * GPW * kGroupRec);  // [token][group] records
     const float b1 = a.b1, b2 = a.b2;
-    float y[NG][8];
+    float y[NGP][8];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
+    for (int gi = NG; gi < NGP; ++gi)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) y[gi][j] = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < kNcbMax; ++cb)
 #pragma unroll
       for (int g = 0; g < GPW; ++g)
 #pragma unroll
@@ -347,9 +361,9 @@ void k_grouped_mm(MmArgs a) {
         }
 #pragma unroll
     for (int p = 0; p < kFp6Pieces; ++p) {
-      int ex[NG];
+      int ex[NGP];
 #pragma unroll
-      for (int gi = 0; gi < NG; ++gi) {
+      for (int gi = 0; gi < NGP; ++gi) {
         float m = 0.f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(y[gi][j]));
@@ -359,7 +373,7 @@ void k_grouped_mm(MmArgs a) {
         ex[gi] = m > 0.f ? max(-127, min(127, eb)) : 0;
       }
 #pragma unroll
-      for (int bt = 0; bt < NG / 4; ++bt) {
+      for (int bt = 0; bt < NGP / 4; ++bt) {
         f32x16 va, vb;  // value 2i of group q at va[4q + i], value 2i+1 at vb[4q + i]
 #pragma unroll
         for (int q = 0; q < 4; ++q)
@@ -376,7 +390,7 @@ void k_grouped_mm(MmArgs a) {
           const int gi = 4 * bt + q, cb = gi / GPW, g = gi % GPW;
 #pragma unroll
           for (int j = 0; j < 8; ++j) y[gi][j] -= ldexpf(r[8 * q + j], ex[gi]);
-          if (cb < ncb) {
+          if (gi < NG && cb < ncb) {
             uint8_t *dst = recs + ((16 * cb + rl) * GPW + g) * kGroupRec + p * kPieceRec;
 #pragma unroll
             for (int h = 0; h < 3; ++h) {
@@ -390,8 +404,7 @@ void k_grouped_mm(MmArgs a) {
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's record bytes are in LDS
     __builtin_amdgcn_wave_barrier();
-    const int t = lane;
-    if (t < ncols && nrw > 0) {
+    for (int t = lane; t < ncols && nrw > 0; t += 64) {
       uint8_t *dst = a.outq + (size_t)(s0 + t) * (size_t)(a.M / 32) * kGroupRec + (size_t)(rw0 / 32) * kGroupRec;
       const int nb = (nrw / 32) * kGroupRec;  // this wave's groups inside M
       for (int c = 0; c < nb / 16; ++c)
@@ -399,7 +412,7 @@ void k_grouped_mm(MmArgs a) {
     }
   } else {
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
+    for (int cb = 0; cb < kNcbMax; ++cb) {
       const int t = 16 * cb + rl;
       if (t >= ncols) continue;
       float *orow = a.out + (size_t)(s0 + t) * a.M + rw0;
@@ -413,7 +426,7 @@ void k_grouped_mm(MmArgs a) {
 }
 
 #ifndef K3_MM_STAGES
-#define K3_MM_STAGES 4
+#define K3_MM_STAGES 3
 #endif
 
 size_t grouped_mm_lds() { return (size_t)K3_MM_STAGES * kStageB; }
