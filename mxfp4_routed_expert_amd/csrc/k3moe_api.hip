@@ -405,9 +405,11 @@ int run_down(const k3moe_dims *d, int32_t T, const uint16_t *x, const uint16_t *
 
 // z: the latent [T][L] fp32; zq_ready: w.zq already holds its piece records. route
 // (nullable): a one-token selection that the gate/up pass runs itself (run_front).
+// one_token: the layer's own one-token dispatch (slot j = pair j, expert active[j]).
 int run_experts(const k3moe_dims *d, int32_t T, const float *z, bool zq_ready, const TopkArgs *route,
-                const k3moe_experts *ex, const int32_t *expert_off, const int32_t *sorted_pair,
-                const int32_t *active, const int32_t *counters, float *edn, const Ws &w, hipStream_t s) {
+                bool one_token, const k3moe_experts *ex, const int32_t *expert_off,
+                const int32_t *sorted_pair, const int32_t *active, const int32_t *counters, float *edn,
+                const Ws &w, hipStream_t s) {
   const uint8_t *zq = w.zq;
   const int64_t P = (int64_t)T * d->topk;
   const bool mm_gu = use_mm(d, T, d->latent, (int64_t)T * d->latent * 4, ex->w1, ex->w3);
@@ -509,17 +511,19 @@ int run_experts(const k3moe_dims *d, int32_t T, const float *z, bool zq_ready, c
     h.active = active;
     h.n_active = counters;
     h.out = edn;
+    h.one_token = one_token && T == 1;
     K3_HIP(launch_grouped(h, kEpiEdn, tt, rb_dn, grid_y, s));
   }
   mark("expert_down");
   return K3MOE_OK;
 }
 
+// one_token: the layer's own one-token dispatch (pair_slot is the identity).
 int run_combine(const k3moe_dims *d, int32_t T, const float *edn, const int32_t *pair_slot,
                 const float *topk_w, const float *norm_w, const uint16_t *w_up, float *y,
-                const Ws &w, hipStream_t s) {
+                bool one_token, const Ws &w, hipStream_t s) {
   K3_HIP(launch_combine(edn, pair_slot, topk_w, norm_w, T, d->topk, d->latent, w.np[0], w.np[1],
-                        w.np[2], w.ss, s));
+                        w.np[2], w.ss, one_token && T == 1, s));
   mark("combine");
   if (use_dense_mm(d, T)) {
     DenseMmArgs a = {};
@@ -621,7 +625,8 @@ int k3moe_expert_glu_mxfp4(const k3moe_dims *d, int32_t T, const float *z, const
   if (T == 0) return K3MOE_OK;
   hipStream_t s = (hipStream_t)stream;
   K3_HIP(launch_active_from_off(expert_off, d->n_experts, w.active, w.counters, s));
-  return run_experts(d, T, z, false, nullptr, ex, expert_off, sorted_pair, w.active, w.counters, edn, w, s);
+  return run_experts(d, T, z, false, nullptr, false, ex, expert_off, sorted_pair, w.active, w.counters, edn, w,
+                     s);
 }
 
 int k3moe_combine(const k3moe_dims *d, int32_t T, const float *edn, const int32_t *pair_slot,
@@ -634,7 +639,7 @@ int k3moe_combine(const k3moe_dims *d, int32_t T, const float *edn, const int32_
   Ws w;
   K3_TRY(check_ws(d, T, ws, ws_bytes, &w));
   if (T == 0) return K3MOE_OK;
-  return run_combine(d, T, edn, pair_slot, topk_w, norm_w, w_up, y, w, (hipStream_t)stream);
+  return run_combine(d, T, edn, pair_slot, topk_w, norm_w, w_up, y, false, w, (hipStream_t)stream);
 }
 
 int k3moe_layer(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_weights *wt, float *y,
@@ -657,9 +662,9 @@ int k3moe_layer(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_w
   bool zq_ready = false;
   TopkArgs route = {};
   K3_TRY(run_front(d, T, x, wt, idx, tw, w, &zq_ready, &route, s));
-  K3_TRY(run_experts(d, T, w.z32, zq_ready, route.T ? &route : nullptr, &wt->ex, w.expert_off, w.sorted_pair,
-                     w.active, w.counters, w.edn, w, s));
-  return run_combine(d, T, w.edn, w.pair_slot, tw, wt->norm_w, wt->w_up, y, w, s);
+  K3_TRY(run_experts(d, T, w.z32, zq_ready, route.T ? &route : nullptr, T == 1, &wt->ex, w.expert_off,
+                     w.sorted_pair, w.active, w.counters, w.edn, w, s));
+  return run_combine(d, T, w.edn, w.pair_slot, tw, wt->norm_w, wt->w_up, y, T == 1, w, s);
 }
 
 int k3moe_layer_profiled(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_weights *wt,

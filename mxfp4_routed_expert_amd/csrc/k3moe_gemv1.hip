@@ -22,12 +22,6 @@ constexpr int kG1MaxChunks = 16;  // 1 KB loads in flight per wave
 __device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
-
 // Stage x (the K activations, fp32) in LDS: from bf16, or as the exact sum of three bf16
 // planes. Each thread converts 8 consecutive values from one 16-byte load per source.
 template <int XF>
@@ -135,7 +129,7 @@ __device__ __forceinline__ void gemv1_item(const Gemv1Args &a, float *sx, int it
   if (!live) return;
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
-    const float v = wave_sum(acc[r]);
+    const float v = wave_sum_fixed(acc[r]);
     const int row = row0 + r;
     if (lane == 0 && row < a.M) {
       if constexpr (EPI == kEpiStore) a.out[(size_t)part * a.M + row] = v;

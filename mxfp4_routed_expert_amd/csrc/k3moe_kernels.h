@@ -124,6 +124,8 @@ struct GroupedArgs {
   uint8_t *outq;          // kEpiSitu: [slot][M/32] fp6 piece records of act
   float b1, b2;
   TopkArgs tk;            // routed in the launch (one token): its selection and its z
+  int one_token;          // a one-token layer batch: slot j is the only pair of expert
+                          // active[j] (the offsets and the active count are not read)
 };
 
 // Grouped GEMM form of the same two passes (many tokens per expert); K % 128 == 0.
@@ -190,8 +192,9 @@ hipError_t launch_grouped(const GroupedArgs &a, int epi, int tokens_per_tile, in
 hipError_t launch_mm_tiles(const int32_t *expert_off, int E, int4 *tiles, int32_t *n_tiles, hipStream_t s);
 size_t grouped_mm_lds();
 hipError_t launch_grouped_mm(const MmArgs &a, int epi, int max_tiles, hipStream_t s);
+// ident: pair_slot is the identity (a one-token layer batch), so it is not read
 hipError_t launch_combine(const float *edn, const int32_t *pair_slot, const float *topk_w,
                           const float *gamma, int T, int K, int L, uint16_t *p0, uint16_t *p1,
-                          uint16_t *p2, float *ss_part, hipStream_t s);
+                          uint16_t *p2, float *ss_part, bool ident, hipStream_t s);
 
 }  // namespace k3

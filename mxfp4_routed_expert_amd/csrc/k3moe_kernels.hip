@@ -532,6 +532,10 @@ __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
     e = __builtin_amdgcn_readfirstlane(min(max(s_e, 0), a.tk.E - 1));
     lo = j;
     hi = j + 1;
+  } else if (a.one_token) {
+    e = __builtin_amdgcn_readfirstlane(a.active[j]);
+    lo = j;
+    hi = j + 1;
   } else {
     if (j >= *a.n_active) return;
     e = __builtin_amdgcn_readfirstlane(a.active[j]);
@@ -870,7 +874,9 @@ hipError_t launch_quant_rows(const float *src, size_t n, uint8_t *dst, hipStream
 // Grid (column blocks of 256, tokens). acc = sum_j w_j edn[slot_j] in slot order
 // j = 0..K-1 (all K loads issued before the sums); the block writes gamma * acc as
 // three bf16 pieces for the up-projection and its share of sum(acc^2), from which the
-// up-projection's epilogue forms the RMSNorm factor 1/sqrt(mean(acc^2) + eps).
+// up-projection's epilogue forms the RMSNorm factor 1/sqrt(mean(acc^2) + eps). With
+// IDENT (one token, slot j = pair j) the edn rows and the weights load together.
+template <bool IDENT>
 __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ edn,
                                                  const int32_t *__restrict__ pair_slot,
                                                  const float *__restrict__ topk_w,
@@ -882,23 +888,25 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ edn,
   __shared__ float red[4];
   const int t = blockIdx.y;
   const int c = blockIdx.x * 256 + threadIdx.x;
-  if (threadIdx.x < 32) {
-    const bool ok = threadIdx.x < K;
-    slot[threadIdx.x] = ok ? pair_slot[(size_t)t * K + threadIdx.x] : -1;
-    wt[threadIdx.x] = ok ? topk_w[(size_t)t * K + threadIdx.x] : 0.f;
+  if constexpr (!IDENT) {
+    if (threadIdx.x < 32) {
+      const bool ok = threadIdx.x < K;
+      slot[threadIdx.x] = ok ? pair_slot[(size_t)t * K + threadIdx.x] : -1;
+      wt[threadIdx.x] = ok ? topk_w[(size_t)t * K + threadIdx.x] : 0.f;
+    }
+    __syncthreads();
   }
-  __syncthreads();
   float v = 0.f;
   if (c < L) {
     float ev[32];
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
-      const int sj = slot[j];
+      const int sj = IDENT ? j : slot[j];
       ev[j] = (j < K && sj >= 0) ? edn[(size_t)sj * L + c] : 0.f;
     }
 #pragma unroll
     for (int j = 0; j < 32; ++j)
-      if (j < K) v = fmaf(wt[j], ev[j], v);
+      if (j < K) v = fmaf(IDENT ? topk_w[j] : wt[j], ev[j], v);
     uint32_t p[3] = {0, 0, 0};
     split_bf16<3>(v * gamma[c], p);
     const size_t o = (size_t)t * L + c;
@@ -916,10 +924,15 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ edn,
 
 hipError_t launch_combine(const float *edn, const int32_t *pair_slot, const float *topk_w,
                           const float *gamma, int T, int K, int L, uint16_t *p0, uint16_t *p1,
-                          uint16_t *p2, float *ss_part, hipStream_t s) {
+                          uint16_t *p2, float *ss_part, bool ident, hipStream_t s) {
   if (T == 0) return hipSuccess;
+  if (ident && T != 1) return hipErrorInvalidValue;
   dim3 grid((L + 255) / 256, T);
-  launch_kernel(k_combine, grid, 256, 0, s, edn, pair_slot, topk_w, gamma, K, L, p0, p1, p2, ss_part);
+  if (ident) {
+    launch_kernel(k_combine<true>, grid, 256, 0, s, edn, pair_slot, topk_w, gamma, K, L, p0, p1, p2, ss_part);
+  } else {
+    launch_kernel(k_combine<false>, grid, 256, 0, s, edn, pair_slot, topk_w, gamma, K, L, p0, p1, p2, ss_part);
+  }
   return hipGetLastError();
 }
 
