@@ -257,28 +257,38 @@ void k_grouped_mm(MmArgs a) {
       }
     }
     const uint8_t *stage = smem + D * kStageB;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      // a quarter of the loads of a later step, kept after the previous piece's
-      // matrix-core instructions (the scheduler would otherwise hoist them all)
-      if (p > 0) __builtin_amdgcn_sched_barrier(0);
-      mid(p);
-      if (!work) continue;
+    // the (piece, column block) pairs in order, their B operands read two pairs ahead of
+    // the matrix-core instructions that use them (a ring of three register sets)
+    constexpr int NP = 4 * NCB;
+    uint32_t bw[3][6], sb[3];
+    auto rd = [&](int n) {
+      const int p = n / NCB, cb = n % NCB;
       const int c0 = kq * 8 + p * 2;
-      uint32_t bw[NCB][6], sb[NCB];
+      const uint8_t *tok = stage + (16 * cb + rl) * 512;
+      const u32x4 b0 = *(const u32x4 *)(tok + ((c0 + rl) & 31) * 16);
+      const u32x3 b1 = *(const u32x3 *)(tok + ((c0 + 1 + rl) & 31) * 16);
+      uint32_t *w = bw[n % 3];
+      w[0] = b0.x; w[1] = b0.y; w[2] = b0.z; w[3] = b0.w;
+      w[4] = b1.x; w[5] = b1.y;
+      sb[n % 3] = b1.z;  // the piece's scale byte (record offset 24) and padding
+    };
+    if (work) {
+      rd(0);
+      if (NP > 1) rd(1);
+    }
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        const uint8_t *tok = stage + (16 * cb + rl) * 512;
-        const u32x4 b0 = *(const u32x4 *)(tok + ((c0 + rl) & 31) * 16);
-        const u32x3 b1 = *(const u32x3 *)(tok + ((c0 + 1 + rl) & 31) * 16);
-        bw[cb][0] = b0.x; bw[cb][1] = b0.y; bw[cb][2] = b0.z; bw[cb][3] = b0.w;
-        bw[cb][4] = b1.x; bw[cb][5] = b1.y;
-        sb[cb] = b1.z;  // the piece's scale byte (record offset 24) and padding
+    for (int n = 0; n < NP; ++n) {
+      if (n % NCB == 0) {
+        // a quarter of the loads of a later step, kept between the pieces' matrix-core
+        // instructions (the scheduler would otherwise hoist them all)
+        if (n > 0) __builtin_amdgcn_sched_barrier(0);
+        mid(n / NCB);
       }
+      if (!work) continue;
+      if (n + 2 < NP) rd(n + 2);
+      const int cb = n % NCB;
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-        for (int i = 0; i < NF; ++i) acc[i][cb] = mfma_fp4_fp6_sel<D>(as.v[i], bw[cb], sp[i], sb[cb], acc[i][cb]);
+      for (int i = 0; i < NF; ++i) acc[i][cb] = mfma_fp4_fp6_sel<D>(as.v[i], bw[n % 3], sp[i], sb[n % 3], acc[i][cb]);
     }
   };
 
@@ -367,10 +377,7 @@ void k_grouped_mm(MmArgs a) {
         float m = 0.f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(y[gi][j]));
-        m = fmaxf(m, __shfl_xor(m, 16, 64));
-        m = fmaxf(m, __shfl_xor(m, 32, 64));
-        const int eb = (int)((__float_as_uint(m) >> 23) & 255u) - 127 - 2;
-        ex[gi] = m > 0.f ? max(-127, min(127, eb)) : 0;
+        ex[gi] = fp6_piece_exp(max_rows4(m));
       }
 #pragma unroll
       for (int bt = 0; bt < NGP / 4; ++bt) {
