@@ -289,6 +289,25 @@ def test_tiny_selection_ties_lowest_ids(tiny_ties, T):
     compare_layer(h, x, what=f"ties {kind} T={T}")
 
 
+# the largest expert count and top-k the library takes (1024 experts, top-32), on the
+# tiny layer widths
+TINY_MAX = dataclasses.replace(k3gen.TINY, n_experts=1024, topk=32)
+
+
+@pytest.fixture(scope="module")
+def tiny_max():
+    return Host(TINY_MAX, 11)
+
+
+@pytest.mark.parametrize("T", [1, 5, 200])
+def test_tiny_max_experts_and_topk(tiny_max, T):
+    """16 selection slots per lane, 32 chosen per token; at T = 200 the 6400 pairs run the
+    grouped GEMM form."""
+    say(f"1024 experts, top-32, T={T}")
+    x, _ = _inputs.gap_fixed_x(TINY_MAX, 30 + T, T, tiny_max.dense["w_router"], tiny_max.dense["bias"])
+    compare_layer(tiny_max, x, what=f"max experts T={T}")
+
+
 def test_tiny_combine_random_gamma_and_scale(tiny):
     """RMSNorm weight and routed_scale other than 1 reach the result."""
     import dataclasses
