@@ -11,6 +11,8 @@ Input recipe (shapes and distributions of the five workloads):
   * MXFP4 experts: packed bytes uniform (so each nibble is uniform over the 16 E2M1
     codes), ue8m0 scale bytes uniform in {118, ..., 124}.
   * RMSNorm weight gamma = 1.
+  * Shared experts (n_shared fused GLU experts of width inter, SI = n_shared * inter):
+    gate and up [SI, H] bf16 ~ N(0, 1/H); down [H, SI] bf16 ~ N(0, 1/SI).
 Expert storage follows the pages' per-expert record: the six tensors of expert e
 (w1 packed, w1 scales, w3 packed, w3 scales, w2 packed, w2 scales) lie back to back
 in one blob of ``blob_bytes`` bytes, blob e at byte e * blob_bytes.
@@ -33,6 +35,7 @@ _lib = None
 T_X, T_WR, T_BIAS, T_WDOWN, T_WUP = 1, 2, 3, 4, 5
 T_W1P, T_W1S, T_W3P, T_W3S, T_W2P, T_W2S = 6, 7, 8, 9, 10, 11
 T_ZPROBE, T_GAMMA = 12, 13
+T_SH1, T_SH3, T_SH2 = 14, 15, 16  # the shared experts (fused gate, up and down)
 _ATTEMPT_SHIFT = 40  # x row counter: (attempt << 40) + t * H + i
 
 
@@ -194,6 +197,16 @@ def gen_dense(dims: Dims, seed: int) -> dict:
         "w_down": normal_bf16(L * H, seed, T_WDOWN, std=1.0 / np.sqrt(H)).reshape(L, H),
         "w_up": normal_bf16(H * L, seed, T_WUP, std=1.0 / np.sqrt(L)).reshape(H, L),
         "norm_w": np.ones(L, np.float32),
+    }
+
+
+def gen_shared(dims: Dims, seed: int, n_shared: int = 2) -> dict:
+    """The fused shared experts: sh1 (gate) and sh3 (up) [SI][H], sh2 (down) [H][SI], bf16."""
+    H, SI = dims.hidden, n_shared * dims.inter
+    return {
+        "sh1": normal_bf16(SI * H, seed, T_SH1, std=1.0 / np.sqrt(H)).reshape(SI, H),
+        "sh3": normal_bf16(SI * H, seed, T_SH3, std=1.0 / np.sqrt(H)).reshape(SI, H),
+        "sh2": normal_bf16(H * SI, seed, T_SH2, std=1.0 / np.sqrt(SI)).reshape(H, SI),
     }
 
 

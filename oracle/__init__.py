@@ -85,6 +85,8 @@ def lib():
         L.k3o_scores_batch.restype = None
         L.k3o_expert_pairs.argtypes = [ctypes.POINTER(Dims), i, vp, vp, vp, ctypes.POINTER(Experts), vp, vp, i]
         L.k3o_expert_pairs.restype = None
+        L.k3o_shared.argtypes = [ctypes.POINTER(Dims), i, i, vp, vp, vp, vp, vp, i]
+        L.k3o_shared.restype = None
         _lib = L
     return _lib
 
@@ -259,3 +261,17 @@ def expert_pairs(dims, tok: np.ndarray, ex_id: np.ndarray, z: np.ndarray, ex: Ex
                            _p(np.ascontiguousarray(ex_id, np.int32)), _p(np.ascontiguousarray(z, np.float32)),
                            ctypes.byref(ex.c), _p(edn), _p(act), nthreads)
     return (edn, act) if want_act else edn
+
+
+def shared(dims, x: np.ndarray, sh: dict, y: np.ndarray, n_shared: int = 2, nthreads: int = 0) -> np.ndarray:
+    """y [T][H] plus the shared experts' output (k3o_shared); x [T][H] bf16 bits; sh as
+    k3gen.gen_shared. Returns a new array."""
+    x = np.ascontiguousarray(x, np.uint16)
+    T = x.shape[0]
+    out = np.ascontiguousarray(y, np.float32).copy()
+    sh1, sh3, sh2 = (np.ascontiguousarray(sh[k], np.uint16) for k in ("sh1", "sh3", "sh2"))
+    SI = n_shared * dims.inter
+    assert sh1.shape == (SI, dims.hidden) and sh3.shape == (SI, dims.hidden) and sh2.shape == (dims.hidden, SI)
+    lib().k3o_shared(ctypes.byref(make_dims(dims)), n_shared, T, _p(x), _p(sh1), _p(sh3), _p(sh2), _p(out),
+                     nthreads)
+    return out

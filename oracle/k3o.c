@@ -326,3 +326,33 @@ void k3o_expert_pairs(const k3o_dims *d, int npairs, const int *tok, const int *
                    z + (size_t)tok[q] * L, ex, ex_id[q], d);
     (void)nthreads;
 }
+
+/* [K3C-9], [K3C-2]: the shared experts, see k3o.h. The same bf16 matrix-vector product
+ * and SiTU-GLU as the routed path (fp64 sums, fp32 results). */
+void k3o_shared(const k3o_dims *d, int n_shared, int T, const uint16_t *x, const uint16_t *sh1,
+                const uint16_t *sh3, const uint16_t *sh2, float *y, int nthreads)
+{
+    const int H = d->hidden, SI = n_shared * d->inter;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+    for (int t = 0; t < T; t++) {
+        float *xf = (float *)malloc(sizeof(float) * (size_t)H);
+        float *g = (float *)malloc(sizeof(float) * (size_t)SI);
+        float *u = (float *)malloc(sizeof(float) * (size_t)SI);
+        float *out = (float *)malloc(sizeof(float) * (size_t)H);
+        for (int i = 0; i < H; i++) xf[i] = k3o_bf16_to_f32(x[(size_t)t * H + i]);
+        k3o_bf16_matvec(g, xf, sh1, H, SI);
+        k3o_bf16_matvec(u, xf, sh3, H, SI);
+        for (int r = 0; r < SI; r++) g[r] = k3o_situ(g[r], u[r], d->b1, d->b2);  /* act, in place */
+        k3o_bf16_matvec(out, g, sh2, SI, H);
+        float *yt = y + (size_t)t * H;
+        for (int i = 0; i < H; i++) yt[i] = yt[i] + out[i];
+        free(xf);
+        free(g);
+        free(u);
+        free(out);
+    }
+    (void)nthreads;
+}

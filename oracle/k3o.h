@@ -135,6 +135,15 @@ void k3o_expert_pairs(const k3o_dims *d, int npairs, const int *tok, const int *
                       const float *z, const k3o_experts *ex, float *edn, float *act,
                       int nthreads);
 
+/* [K3C-9] (the per-token order's last step), [K3C-2] (n_shared 2, full width): the
+ * shared experts run on the token's ORIGINAL input x (not on z) and are added to the
+ * layer output unweighted. Their n_shared GLU experts of width I are stored fused:
+ * gate rows sh1 [SI][H] and up rows sh3 [SI][H] (SI = n_shared * I), down sh2 [H][SI],
+ * all bf16 [out][in]. Per token: g = sh1 x, u = sh3 x (fp32), act = SiTU-GLU(g, u)
+ * (fp32), out = sh2 act (fp32), then y += out (one fp32 addition per element). */
+void k3o_shared(const k3o_dims *d, int n_shared, int T, const uint16_t *x, const uint16_t *sh1,
+                const uint16_t *sh3, const uint16_t *sh2, float *y, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif

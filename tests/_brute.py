@@ -91,3 +91,13 @@ def layer_token(dims, x_bf16: np.ndarray, dense: dict, expert_blob_fn, offsets: 
     nrm = (accf / np.sqrt(np.mean(accf * accf) + dims.eps) * gam).astype(np.float32)
     y = (bf16_bits_to_f64(dense["w_up"]) @ nrm.astype(np.float64)).astype(np.float32)
     return {"y": y, "idx": idx.astype(np.int32), "w": w, "z": z, "acc": accf.astype(np.float32), "nrm": nrm}
+
+
+def shared_token(dims, x_bf16: np.ndarray, sh: dict, n_shared: int = 2) -> np.ndarray:
+    """The fused shared experts on one token's original input: numpy fp64 products
+    rounded to fp32 at the same points as the routed experts."""
+    xf = bf16_bits_to_f64(x_bf16)
+    g = (bf16_bits_to_f64(sh["sh1"]) @ xf).astype(np.float32)
+    u = (bf16_bits_to_f64(sh["sh3"]) @ xf).astype(np.float32)
+    a = situ(g, u, dims.b1, dims.b2)
+    return (bf16_bits_to_f64(sh["sh2"]) @ a.astype(np.float64)).astype(np.float32)

@@ -350,3 +350,56 @@ def test_layer_matches_brute_force_k3_shape_subproblem():
     for k in ("z", "acc", "nrm", "y"):
         ref = b[k].astype(np.float64)
         assert np.linalg.norm(r[k][0] - ref) / np.linalg.norm(ref) < 1e-6, k
+
+
+# ---------------------------------------------------------------- shared experts
+def _tiny_shared(seed, T, n_shared=2):
+    d = k3gen.TINY
+    return d, k3gen.gen_shared(d, seed, n_shared), k3gen.gen_x(d, seed, T)
+
+
+def test_shared_matches_brute_force_tiny():
+    d, sh, x = _tiny_shared(0, 7)
+    y0 = np.asarray(np.random.default_rng(5).standard_normal((7, d.hidden)), np.float32)
+    y = oracle.shared(d, x, sh, y0)
+    for t in range(7):
+        ref = y0[t].astype(np.float64) + _brute.shared_token(d, x[t], sh).astype(np.float64)
+        err = np.linalg.norm(y[t] - ref) / np.linalg.norm(ref)
+        assert err < 1e-6, (t, err)
+
+
+def test_shared_zero_down_leaves_y_unchanged():
+    d, sh, x = _tiny_shared(1, 4)
+    sh = dict(sh, sh2=np.zeros_like(sh["sh2"]))
+    y0 = np.asarray(np.random.default_rng(6).standard_normal((4, d.hidden)), np.float32)
+    assert np.array_equal(oracle.shared(d, x, sh, y0), y0)
+
+
+def test_shared_fused_is_sum_of_its_experts():
+    # the fused [SI] layout is n_shared experts side by side: row block j of sh1/sh3 and
+    # column block j of sh2 form expert j; their outputs add
+    d, sh, x = _tiny_shared(2, 3)
+    I = d.inter
+    zero = np.zeros((3, d.hidden), np.float32)
+    fused = oracle.shared(d, x, sh, zero).astype(np.float64)
+    parts = sum(oracle.shared(d, x, {"sh1": sh["sh1"][j * I:(j + 1) * I], "sh3": sh["sh3"][j * I:(j + 1) * I],
+                                     "sh2": np.ascontiguousarray(sh["sh2"][:, j * I:(j + 1) * I])},
+                              zero, n_shared=1).astype(np.float64) for j in range(2))
+    assert np.max(np.abs(fused - parts)) <= 1e-5 * np.max(np.abs(fused))
+    # and a transposed down matrix (or the gate/up roles swapped) gives another function
+    swp = oracle.shared(d, x, {"sh1": sh["sh3"], "sh3": sh["sh1"], "sh2": sh["sh2"]}, zero)
+    assert np.linalg.norm(swp - fused) / np.linalg.norm(fused) > 1e-2
+
+
+def test_shared_one_hot_input_reads_one_column():
+    # x = e_c: g and u are column c of sh1 and sh3 exactly; the output is sh2 . SiTU(g, u)
+    d, sh, _ = _tiny_shared(3, 1)
+    c = 5
+    x = np.zeros((1, d.hidden), np.uint16)
+    x[0, c] = 0x3F80                      # bf16 1.0
+    y = oracle.shared(d, x, sh, np.zeros((1, d.hidden), np.float32))
+    g = _brute.bf16_bits_to_f64(sh["sh1"][:, c])
+    u = _brute.bf16_bits_to_f64(sh["sh3"][:, c])
+    a = _brute.situ(g, u, d.b1, d.b2).astype(np.float64)
+    ref = _brute.bf16_bits_to_f64(sh["sh2"]) @ a
+    assert np.max(np.abs(y[0] - ref)) <= 1e-6 * np.max(np.abs(ref))
