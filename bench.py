@@ -126,6 +126,93 @@ def algorithmic(dims, T, n_distinct):
     }
 
 
+def bench_shared(args, dims, stream, xs, pool, row, hip_record, n_shared=2):
+    """The fused shared experts (k3moe_shared_glu_bf16, y += on the layer output) at the
+    K3 shape: decode (T = 1, rotating over two copies of the 264 MB of weights, so they
+    come from HBM) and prefill (T = 4096)."""
+    import torch
+
+    import k3gen
+    from mxfp4_routed_expert_amd import device, k3moe
+    sh = k3gen.gen_shared(dims, 1, n_shared)
+    copies = [device.upload_shared(sh)]
+    copies.append({k: v.clone() for k, v in copies[0].items()})
+    del sh
+    SI, H = n_shared * dims.inter, dims.hidden
+    w_bytes = 3 * SI * H * 2
+    T = 1
+    y = torch.zeros((T, H), dtype=torch.float32, device="cuda")
+    ws = device.shared_workspace(dims, n_shared, T)
+
+    def call(i, **kw):
+        c = copies[i % 2]
+        return (k3moe.k3moe_shared_profiled if kw else k3moe.k3moe_shared_glu_bf16)(
+            dims, n_shared, T, xs.data_ptr() + (i % pool) * row, c["sh1"], c["sh3"], c["sh2"], y, ws,
+            stream=stream, **kw)
+
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    ev = HipEvents(2)
+    hip_record(ev.ev[0], stream.cuda_stream)
+    for i in range(args.steps):
+        call(i)
+    hip_record(ev.ev[1], stream.cuda_stream)
+    torch.cuda.synchronize()
+    ms = ev.ms(ev.ev[0], ev.ev[1]) / args.steps
+    ev.close()
+    pe = HipEvents(2 * MAX_LAUNCHES)
+    sums = {}
+    nprof = min(args.steps, 50)
+    for i in range(nprof):
+        names = call(i, events=pe.ev)
+        torch.cuda.synchronize()
+        for n, v in launch_ms(pe, names).items():
+            sums[n] = sums.get(n, 0.0) + v
+    pe.close()
+    kern = {n: round(v / nprof * 1e3, 2) for n, v in sums.items()}
+    gbs = (w_bytes + H * 2 + 2 * H * 4) / (ms * 1e-3) / 1e9
+    gu_us = kern.get("shared_gate_up_situ")
+    gu_gbs = (2 * SI * H * 2) / (gu_us * 1e-6) / 1e9 if gu_us else None
+    out = {"n_shared": n_shared, "inter": SI, "decode_us_per_step": round(ms * 1e3, 2),
+           "decode_GBs": round(gbs, 1), "decode_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+           "gate_up_GBs": round(gu_gbs, 1) if gu_gbs else None, "decode_kernel_us": kern}
+    log(f"shared experts decode T=1: {ms * 1e3:.1f} us/step, {gbs:.0f} GB/s; per-kernel us: "
+        + ", ".join(f"{n} {v:.1f}" for n, v in kern.items()))
+    if not args.no_prefill:
+        Tp = 4096
+        xp = torch.from_numpy(k3gen.gen_x(dims, 3, Tp).view(np.int16)).cuda()
+        yp = torch.zeros((Tp, H), dtype=torch.float32, device="cuda")
+        wsp = device.shared_workspace(dims, n_shared, Tp)
+        c = copies[0]
+        k3moe.k3moe_shared_glu_bf16(dims, n_shared, Tp, xp, c["sh1"], c["sh3"], c["sh2"], yp, wsp, stream=stream)
+        torch.cuda.synchronize()
+        evp = HipEvents(2)
+        hip_record(evp.ev[0], stream.cuda_stream)
+        for _ in range(args.prefill_steps):
+            k3moe.k3moe_shared_glu_bf16(dims, n_shared, Tp, xp, c["sh1"], c["sh3"], c["sh2"], yp, wsp,
+                                        stream=stream)
+        hip_record(evp.ev[1], stream.cuda_stream)
+        torch.cuda.synchronize()
+        msp = evp.ms(evp.ev[0], evp.ev[1]) / args.prefill_steps
+        evp.close()
+        pep = HipEvents(2 * MAX_LAUNCHES)
+        names = k3moe.k3moe_shared_profiled(dims, n_shared, Tp, xp, c["sh1"], c["sh3"], c["sh2"], yp, wsp, pep.ev,
+                                            stream=stream)
+        torch.cuda.synchronize()
+        kp = {n: round(v * 1e3, 1) for n, v in launch_ms(pep, names).items()}
+        pep.close()
+        tf = Tp * 2 * 3 * SI * H / (msp * 1e-3) / 1e12
+        out.update({"prefill_T": Tp, "prefill_ms_per_step": round(msp, 3), "prefill_TFLOPs": round(tf, 1),
+                    "prefill_bf16_peak_frac": round(tf / BF16_PEAK_TFLOPS, 4), "prefill_kernel_us": kp})
+        log(f"shared experts prefill T=4096: {msp:.2f} ms/step, {tf:.0f} TFLOP/s (2 bf16 pieces of act "
+            f"counted once); per-kernel us: " + ", ".join(f"{n} {v:.0f}" for n, v in kp.items()))
+        del xp, yp, wsp
+    del copies
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -134,6 +221,8 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=3)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-shared", action="store_true",
+                    help="skip the shared-expert measurement (a call of its own, after the layer)")
     ap.add_argument("--cpu-tokens", type=int, default=64)
     ap.add_argument("--dense-copies", type=int, default=4,
                     help="copies of the dense weights (router, projections) the decode steps rotate "
@@ -293,6 +382,11 @@ def main():
         del wsp, yp, xp
         torch.cuda.empty_cache()
 
+    # ---------------------------------------------------------------- shared experts
+    shared = None
+    if not args.no_shared:
+        shared = bench_shared(args, dims, stream, xs, pool, row, hip_record)
+
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -328,6 +422,7 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": roofline,
         "prefill": prefill,
+        "shared_experts": shared,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

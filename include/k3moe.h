@@ -16,6 +16,7 @@
  *      applied to the AGGREGATE (section 9; RMSNorm as in section 5 "Kernels with a
  *      floating point contract").
  *   5. y = W_up n (bf16 weights, [H][L]).
+ *   6. (k3moe_shared_glu_bf16, a call of its own) y += the shared experts on x.
  *
  * MXFP4 layout (section 4; colibri "Weights"): a matrix [rows][cols] is stored as
  * packed bytes [rows][cols/2], column 2k in the LOW nibble of byte k and column 2k+1
@@ -158,6 +159,26 @@ int k3moe_combine(const k3moe_dims *d, int32_t T, const float *edn, const int32_
 int k3moe_layer(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_weights *w,
                 float *y, int32_t *topk_idx_out, float *topk_w_out,
                 void *ws, size_t ws_bytes, void *stream);
+
+/* Step 6, the shared experts (README section 9, step 6; colibri "Architecture notes",
+ * Stable LatentMoE: two fused full-width shared experts, inter 6144 in K3). They run on
+ * the token's ORIGINAL input x, not on z, and are added to the layer output UNWEIGHTED,
+ * outside the top-k sum. The n_shared GLU experts of width inter are stored fused,
+ * SI = n_shared * inter: sh1 (gate) and sh3 (up) [SI][H] bf16, sh2 (down) [H][SI] bf16,
+ * expert j owning rows j*inter .. (j+1)*inter-1 of sh1 and sh3 and those columns of sh2.
+ * Per token: act = SiTU-GLU(sh1 x, sh3 x) (fp32), y += sh2 act.
+ * x [T][H] bf16 in; y [T][H] fp32 is read and written (typically the y of k3moe_layer or
+ * k3moe_combine, on the same stream, after it). ws: at least
+ * k3moe_shared_workspace_size(d, n_shared, T) bytes, 256-byte aligned (a workspace sized
+ * for a larger T works too). Supported: n_shared >= 1, SI a multiple of 64,
+ * SI * H < 2^30, T * H < 2^30, T * SI < 2^29; x, sh1, sh3, sh2 and y 16-byte aligned.
+ * Numerics: the gate and up products take bf16 x exactly; the down product takes act as
+ * two bf16 pieces (hi + lo, 16 significant bits, the rest below 2^-17 relative) for
+ * batches of two or more tokens and exactly (fp32) for one token. */
+int k3moe_shared_workspace_size(const k3moe_dims *d, int32_t n_shared, int32_t T, size_t *bytes);
+int k3moe_shared_glu_bf16(const k3moe_dims *d, int32_t n_shared, int32_t T, const uint16_t *x,
+                          const uint16_t *sh1, const uint16_t *sh3, const uint16_t *sh2, float *y,
+                          void *ws, size_t ws_bytes, void *stream);
 
 /* Human-readable name of a status code (static storage). */
 const char *k3moe_status_str(int status);

@@ -25,6 +25,12 @@ int k3moe_layer_profiled(const k3moe_dims *d, int32_t T, const uint16_t *x, cons
                          void *stream, void **events, int max_events, int *n_kernels);
 const char *k3moe_prof_name(int i);
 
+/* As k3moe_shared_glu_bf16, its launches timed as in k3moe_layer_profiled. */
+int k3moe_shared_profiled(const k3moe_dims *d, int32_t n_shared, int32_t T, const uint16_t *x,
+                          const uint16_t *sh1, const uint16_t *sh3, const uint16_t *sh2, float *y,
+                          void *ws, size_t ws_bytes, void *stream, void **events, int max_events,
+                          int *n_kernels);
+
 /* Which kernels run the expert passes, for tests and measurement that compare the two
  * forms on the same inputs: 0 = by batch size (the default: the grouped GEMM form when
  * the batch averages at least two token-expert pairs per expert), 1 = always the

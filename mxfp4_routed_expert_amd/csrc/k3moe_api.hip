@@ -560,6 +560,120 @@ int run_combine(const k3moe_dims *d, int32_t T, const float *edn, const int32_t 
   return K3MOE_OK;
 }
 
+// ---- the shared experts
+
+// The fused shared experts' width SI = n_shared * inter, or a negative status.
+int check_shared(const k3moe_dims *d, int32_t n_shared, int32_t T) {
+  K3_TRY(check_dims(d));
+  if (T < 0 || n_shared < 1) return K3MOE_EINVAL;
+  const int64_t SI = (int64_t)n_shared * d->inter, H = d->hidden;
+  // gate and up are row segments of one GEMM (placed at multiples of 64 rows); every
+  // matrix and token buffer is read through a 32-bit buffer descriptor
+  if (SI % 64 != 0 || SI * H * 2 >= ((int64_t)1 << 31)) return K3MOE_EUNSUPPORTED;
+  if ((int64_t)T * H * 2 >= ((int64_t)1 << 31) || (int64_t)T * SI * 4 + 1024 >= ((int64_t)1 << 31))
+    return K3MOE_EUNSUPPORTED;
+  return (int)SI;
+}
+
+// One-token form: both products' activations fit the GEMV's 64 KB of LDS.
+bool shared_gemv1(const k3moe_dims *d, int SI, int32_t T) { return T == 1 && d->hidden <= 16384 && SI <= 16384; }
+
+struct ShWs {
+  float *act;      // one token: [SI] SiTU-GLU output
+  float *gu;       // GEMM form: [T][2 SI] gate | up
+  uint16_t *p[2];  // GEMM form: [T][SI] bf16 pieces of the SiTU-GLU output
+  size_t bytes;
+};
+
+ShWs carve_shared(const k3moe_dims *d, int SI, int32_t T, void *base) {
+  ShWs w = {};
+  char *b = (char *)base;
+  size_t o = 0;
+  auto take = [&](size_t n) {
+    char *p = b ? b + o : nullptr;
+    o += (n + 255) & ~(size_t)255;
+    return (void *)p;
+  };
+  const size_t t = (size_t)T, si = (size_t)SI;
+  if (T <= 1) {
+    w.act = (float *)take(si * 4);
+  } else {
+    w.gu = (float *)take(t * 2 * si * 4);
+    for (int q = 0; q < 2; ++q) w.p[q] = (uint16_t *)take(t * si * 2);
+  }
+  w.bytes = o;
+  (void)d;
+  return w;
+}
+
+int run_shared(const k3moe_dims *d, int SI, int32_t T, const uint16_t *x, const uint16_t *sh1,
+               const uint16_t *sh3, const uint16_t *sh2, float *y, const ShWs &w, hipStream_t s) {
+  const int H = d->hidden;
+  if (shared_gemv1(d, SI, T)) {
+    Gemv1Args gu = {};
+    gu.A = sh1;
+    gu.A2 = sh3;
+    gu.M = SI;
+    gu.K = H;
+    gu.ks = 1;
+    gu.xb = x;
+    gu.out = w.act;
+    gu.b1 = d->b1;
+    gu.b2 = d->b2;
+    K3_HIP(launch_gemv1(gu, kA_BF16, kX_BF16, kEpiGluAct, 2, s));
+    mark("shared_gate_up_situ");
+    Gemv1Args dn = {};
+    dn.A = sh2;
+    dn.M = H;
+    dn.K = SI;
+    dn.ks = 1;
+    dn.xf = w.act;
+    dn.out = y;
+    K3_HIP(launch_gemv1(dn, kA_BF16, kX_F32, kEpiAdd, 1, s));
+    mark("shared_down_add");
+    return K3MOE_OK;
+  }
+  DenseMmArgs a = {};
+  a.seg[0] = DenseSeg{sh1, 0, SI, w.gu, 2 * SI};
+  a.seg[1] = DenseSeg{sh3, SI, SI, w.gu + SI, 2 * SI};
+  a.nseg = 2;
+  a.M = 2 * SI;
+  a.K = H;
+  a.N = T;
+  a.B = x;
+  a.plane_elems = (int64_t)T * H;
+  K3_HIP(launch_dense_mm(a, 1, kEpiStore, s));
+  mark("shared_gate_up");
+  K3_HIP(launch_glu_pieces(w.gu, T, SI, d->b1, d->b2, w.p[0], w.p[1], s));
+  mark("shared_situ");
+  DenseMmArgs dn = {};
+  dn.seg[0] = DenseSeg{sh2, 0, H, y, H};
+  dn.nseg = 1;
+  dn.M = H;
+  dn.K = SI;
+  dn.N = T;
+  dn.B = w.p[0];
+  dn.plane_elems = (int64_t)(w.p[1] - w.p[0]);  // the two pieces are carved back to back
+  // two bf16 pieces (hi + lo) of each SiTU-GLU output: the dropped remainder is below
+  // 2^-17 of the value
+  K3_HIP(launch_dense_mm(dn, 2, kEpiAdd, s));
+  mark("shared_down_add");
+  return K3MOE_OK;
+}
+
+// Profiled calls: bind the launches of one entry-point call to the caller's events.
+void prof_begin(void **events, int max_events) {
+  g_prof = ProfNames();
+  g_launch_times = LaunchTimes();
+  g_launch_times.events = events;
+  g_launch_times.max_launches = (max_events / 2 < kMaxProfLaunches) ? max_events / 2 : kMaxProfLaunches;
+}
+
+int prof_end() {
+  g_launch_times = LaunchTimes();
+  return g_prof.named;
+}
+
 }  // namespace
 
 extern "C" {
@@ -671,13 +785,41 @@ int k3moe_layer_profiled(const k3moe_dims *d, int32_t T, const uint16_t *x, cons
                          float *y, int32_t *topk_idx_out, float *topk_w_out, void *ws, size_t ws_bytes,
                          void *stream, void **events, int max_events, int *n_kernels) {
   if (!events || max_events < 2 || !n_kernels) return K3MOE_EINVAL;
-  g_prof = ProfNames();
-  g_launch_times = LaunchTimes();
-  g_launch_times.events = events;
-  g_launch_times.max_launches = (max_events / 2 < kMaxProfLaunches) ? max_events / 2 : kMaxProfLaunches;
+  prof_begin(events, max_events);
   const int rc = k3moe_layer(d, T, x, wt, y, topk_idx_out, topk_w_out, ws, ws_bytes, stream);
-  *n_kernels = g_prof.named;
-  g_launch_times = LaunchTimes();
+  *n_kernels = prof_end();
+  return rc;
+}
+
+int k3moe_shared_workspace_size(const k3moe_dims *d, int32_t n_shared, int32_t T, size_t *bytes) {
+  const int SI = check_shared(d, n_shared, T);
+  if (SI < 0) return SI;
+  if (!bytes) return K3MOE_EINVAL;
+  *bytes = carve_shared(d, SI, T, nullptr).bytes;
+  return K3MOE_OK;
+}
+
+int k3moe_shared_glu_bf16(const k3moe_dims *d, int32_t n_shared, int32_t T, const uint16_t *x,
+                          const uint16_t *sh1, const uint16_t *sh3, const uint16_t *sh2, float *y, void *ws,
+                          size_t ws_bytes, void *stream) {
+  const int SI = check_shared(d, n_shared, T);
+  if (SI < 0) return SI;
+  if (!x || !sh1 || !sh3 || !sh2 || !y) return K3MOE_EINVAL;
+  if (!al16(x) || !al16(sh1) || !al16(sh3) || !al16(sh2) || !al16(y)) return K3MOE_EUNSUPPORTED;
+  const ShWs need = carve_shared(d, SI, T, nullptr);
+  if (!ws || ws_bytes < need.bytes) return K3MOE_EWORKSPACE;
+  if (((uintptr_t)ws & 255u) != 0) return K3MOE_EUNSUPPORTED;
+  if (T == 0) return K3MOE_OK;
+  return run_shared(d, SI, T, x, sh1, sh3, sh2, y, carve_shared(d, SI, T, ws), (hipStream_t)stream);
+}
+
+int k3moe_shared_profiled(const k3moe_dims *d, int32_t n_shared, int32_t T, const uint16_t *x,
+                          const uint16_t *sh1, const uint16_t *sh3, const uint16_t *sh2, float *y, void *ws,
+                          size_t ws_bytes, void *stream, void **events, int max_events, int *n_kernels) {
+  if (!events || max_events < 2 || !n_kernels) return K3MOE_EINVAL;
+  prof_begin(events, max_events);
+  const int rc = k3moe_shared_glu_bf16(d, n_shared, T, x, sh1, sh3, sh2, y, ws, ws_bytes, stream);
+  *n_kernels = prof_end();
   return rc;
 }
 

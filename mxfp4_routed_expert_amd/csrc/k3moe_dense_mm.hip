@@ -5,6 +5,8 @@
 // PB bf16 planes [N][K] of the activations whose sum is the fp32 value (one plane for
 // the bf16 x; three for the fp32 aggregate, which makes the products exact), and the
 // planes are consecutive 32-column chunks of the reduction against the same weights.
+// The shared experts use the same kernel: gate and up as two row segments against x,
+// down against two bf16 pieces of the SiTU output, added to the layer output.
 // The fp32 router weights enter as three bf16 row segments (the pieces of each weight
 // row), whose three partial results the top-k adds; every product of bf16 values is
 // exact in the matrix core, so only the fp32 accumulation rounds.
@@ -184,7 +186,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (r < nrows) {
         f32x4 v = acc[i][j];
         if constexpr (EPI == kEpiStoreScaled) v *= sInv[16 * j + rl];
-        *(f32x4 *)(out + (size_t)n * seg.ld + r) = v;
+        f32x4 *o = (f32x4 *)(out + (size_t)n * seg.ld + r);
+        if constexpr (EPI == kEpiAdd) v = *o + v;
+        *o = v;
       }
     }
   }
@@ -207,6 +211,11 @@ hipError_t launch_dense_mm(const DenseMmArgs &a, int pieces, int epi, hipStream_
     constexpr int NJ = 8;
     const int64_t total = (int64_t)((a.M + 255) / 256) * ((a.N + 16 * NJ - 1) / (16 * NJ));
     launch_kernel(k_dense_mm<2, NJ, kEpiStoreScaled>, (unsigned)(8 * ((total + 7) / 8)), 256,
+                  kDmStages * 2 * NJ * 1024 + 64 * NJ, s, a);
+  } else if (pieces == 2 && epi == kEpiAdd) {
+    constexpr int NJ = 8;
+    const int64_t total = (int64_t)((a.M + 255) / 256) * ((a.N + 16 * NJ - 1) / (16 * NJ));
+    launch_kernel(k_dense_mm<2, NJ, kEpiAdd>, (unsigned)(8 * ((total + 7) / 8)), 256,
                   kDmStages * 2 * NJ * 1024 + 64 * NJ, s, a);
   } else if (pieces == 3 && epi == kEpiStoreScaled) {
     constexpr int NJ = 4;

@@ -1,5 +1,7 @@
-// Dense products of one token (decode): the router logits, the latent down-projection
-// and the RMSNormed up-projection, y[m] = sum_k A[m][k] * x[k], on the vector ALUs.
+// Dense products of one token (decode): the router logits, the latent down-projection,
+// the RMSNormed up-projection and the shared experts (gate and up rows in pairs with
+// the SiTU-GLU applied on the spot; down added to the layer output), y[m] = sum_k
+// A[m][k] * x[k], on the vector ALUs.
 //
 // With one token the matrix cores have nothing to reuse, so the weights are streamed
 // in the order that suits HBM: a wave owns RPW whole rows (or a K part of a row), and
@@ -22,13 +24,18 @@ constexpr int kG1MaxChunks = 16;  // 1 KB loads in flight per wave
 __device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
 
-// Stage x (the K activations, fp32) in LDS: from bf16, or as the exact sum of three bf16
-// planes. Each thread converts 8 consecutive values from one 16-byte load per source.
+// Stage x (the K activations, fp32) in LDS: from bf16, as the exact sum of three bf16
+// planes, or as fp32. Each thread converts 8 consecutive values from one 16-byte load per
+// source (two for fp32).
 template <int XF>
 __device__ __forceinline__ void stage_x(const Gemv1Args &a, float *sx) {
   for (int q = threadIdx.x; q < a.K / 8; q += blockDim.x) {
     float v[8];
-    if constexpr (XF == kX_BF16) {
+    if constexpr (XF == kX_F32) {
+      const float4 f0 = *(const float4 *)(a.xf + 8 * q), f1 = *(const float4 *)(a.xf + 8 * q + 4);
+      v[0] = f0.x; v[1] = f0.y; v[2] = f0.z; v[3] = f0.w;
+      v[4] = f1.x; v[5] = f1.y; v[6] = f1.z; v[7] = f1.w;
+    } else if constexpr (XF == kX_BF16) {
       const u32x4 b = *(const u32x4 *)(a.xb + 8 * q);
       const uint32_t w[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
@@ -51,9 +58,10 @@ __device__ __forceinline__ void stage_x(const Gemv1Args &a, float *sx) {
   }
 }
 
-// One wave item: rows row0 .. row0+RPW-1 over the columns of K part `part`. The
-// weight loads of the first batch are issued before the block stages x (they do not
-// depend on it); `staged` runs the staging and the block barrier.
+// One wave item: rows row0 .. row0+RPW-1 over the columns of K part `part` (kEpiGluAct:
+// row row0 of A and of A2). The weight loads of the first batch are issued before the
+// block stages x (they do not depend on it); `staged` runs the staging and the block
+// barrier.
 template <int AF, int EPI, int RPW, typename Stage>
 __device__ __forceinline__ void gemv1_item(const Gemv1Args &a, float *sx, int item, bool live, float scale,
                                            Stage &&staged) {
@@ -65,15 +73,18 @@ __device__ __forceinline__ void gemv1_item(const Gemv1Args &a, float *sx, int it
   // the buffer descriptors stay scalar
   const int kp = __builtin_amdgcn_readfirstlane(a.K / a.ks);  // columns per part
   const int part = __builtin_amdgcn_readfirstlane(item % a.ks);
-  const int row0 = __builtin_amdgcn_readfirstlane((item / a.ks) * RPW);
+  constexpr bool GLU = EPI == kEpiGluAct;
+  static_assert(!GLU || RPW == 2, "the GLU form pairs one gate row with one up row");
+  const int row0 = __builtin_amdgcn_readfirstlane((item / a.ks) * (GLU ? 1 : RPW));
   const int k0 = part * kp;
   const uint32_t slice = (uint32_t)kp * ESZ;  // bytes of one row part
   const int nchunk = live ? (int)((slice + 1023) / 1024) : 0;
   rsrc_t rA[RPW];
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
-    const int row = row0 + r;
-    rA[r] = make_rsrc((const uint8_t *)a.A + ((size_t)min(row, a.M - 1) * a.K + k0) * ESZ,
+    const int row = GLU ? row0 : row0 + r;
+    const void *base = (GLU && r == 1) ? a.A2 : a.A;
+    rA[r] = make_rsrc((const uint8_t *)base + ((size_t)min(row, a.M - 1) * a.K + k0) * ESZ,
                       (live && row < a.M) ? slice : 0u);
   }
   u32x4 w[RPW][NC];
@@ -127,12 +138,18 @@ __device__ __forceinline__ void gemv1_item(const Gemv1Args &a, float *sx, int it
     }
   }
   if (!live) return;
+  if constexpr (GLU) {
+    const float g = wave_sum_fixed(acc[0]), u = wave_sum_fixed(acc[1]);
+    if (lane == 0 && row0 < a.M) a.out[row0] = situ(g, u, a.b1, a.b2);
+    return;
+  }
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
     const float v = wave_sum_fixed(acc[r]);
     const int row = row0 + r;
     if (lane == 0 && row < a.M) {
       if constexpr (EPI == kEpiStore) a.out[(size_t)part * a.M + row] = v;
+      else if constexpr (EPI == kEpiAdd) a.out[row] = a.out[row] + v;
       else a.out[row] = v * scale;
     }
   }
@@ -217,7 +234,9 @@ bool gemv1_supported(const Gemv1Args &a, int af) { return gemv1_ok(a, af == kA_F
 
 hipError_t launch_gemv1(const Gemv1Args &a, int af, int xf, int epi, int rpw, hipStream_t s) {
   if (!gemv1_ok(a, af == kA_F32 ? 4 : 2) || (rpw != 1 && rpw != 2)) return hipErrorInvalidValue;
-  const int items = ((a.M + rpw - 1) / rpw) * a.ks;
+  if ((epi == kEpiGluAct || epi == kEpiAdd || epi == kEpiStoreScaled) && a.ks != 1) return hipErrorInvalidValue;
+  if (epi == kEpiGluAct && (rpw != 2 || !a.A2)) return hipErrorInvalidValue;
+  const int items = (epi == kEpiGluAct ? a.M : (a.M + rpw - 1) / rpw) * a.ks;
   const int waves = gemv1_waves(items);
   const int grid = (items + waves - 1) / waves;
   const size_t lds = (size_t)a.K * 4;
@@ -230,6 +249,8 @@ hipError_t launch_gemv1(const Gemv1Args &a, int af, int xf, int epi, int rpw, hi
   G1(kA_BF16, kX_BF16, kEpiStore, 1)
   G1(kA_BF16, kX_PLANES, kEpiStoreScaled, 1)
   G1(kA_BF16, kX_PLANES, kEpiStoreScaled, 2)
+  G1(kA_BF16, kX_BF16, kEpiGluAct, 2)
+  G1(kA_BF16, kX_F32, kEpiAdd, 1)
 #undef G1
   return hipErrorInvalidValue;
 }

@@ -40,7 +40,10 @@ constexpr int kMaxNormParts = 64;    // column blocks of 256 in one latent row (
 // into three bf16 pieces) and activations B [N][K] given as PB bf16 pieces that sum to
 // the fp32 value.
 enum AFormat { kA_BF16 = 0, kA_F32 = 1 };
-enum DenseEpi { kEpiStore = 0, kEpiStorePlanes = 1, kEpiStoreScaled = 2 };
+// kEpiAdd: out += the product (one fp32 addition per element; each element is owned by
+// one wave, so no atomics). kEpiGluAct (one-token form): a wave reads row m of A and row
+// m of A2 and writes out[m] = SiTU-GLU(A x, A2 x).
+enum DenseEpi { kEpiStore = 0, kEpiStorePlanes = 1, kEpiStoreScaled = 2, kEpiAdd = 3, kEpiGluAct = 4 };
 
 struct DenseArgs {
   const void *A;        // [M][K]
@@ -75,10 +78,12 @@ struct DenseMmArgs {
 };
 
 // One token's dense product on the vector ALUs: out = A x, A [M][K] (bf16 or fp32),
-// x [K] as bf16 (kX_BF16) or as three bf16 planes summing to the fp32 value (kX_PLANES).
-// K is cut into ks parts; kEpiStore writes the part products out[part][M], kEpiStoreScaled
-// (ks = 1) writes out[m] / sqrt(sum(ss)/K + eps).
-enum XFormat { kX_BF16 = 0, kX_PLANES = 1 };
+// x [K] as bf16 (kX_BF16), as three bf16 planes summing to the fp32 value (kX_PLANES) or
+// as fp32 (kX_F32). K is cut into ks parts; kEpiStore writes the part products
+// out[part][M], kEpiStoreScaled (ks = 1) writes out[m] / sqrt(sum(ss)/K + eps), kEpiAdd
+// (ks = 1) adds the product to out[m], kEpiGluAct (ks = 1, A2 given) writes
+// SiTU-GLU(A x, A2 x) with caps b1, b2.
+enum XFormat { kX_BF16 = 0, kX_PLANES = 1, kX_F32 = 2 };
 struct Gemv1Args {
   const void *A;
   int M, K, ks;
@@ -88,6 +93,9 @@ struct Gemv1Args {
   const float *ss;
   int nss;
   float eps;
+  const void *A2;  // kEpiGluAct: the up rows
+  const float *xf; // kX_F32
+  float b1, b2;
 };
 
 // ---------------------------------------------------------------- grouped MXFP4
@@ -151,14 +159,15 @@ struct MmArgs {
 // ---------------------------------------------------------------- launchers
 hipError_t launch_route_down(const DenseArgs &router, int ks, const DenseArgs *down, hipStream_t s);
 hipError_t launch_dense_bf16(const DenseArgs &a, int pieces, int epi, hipStream_t s);
-// pieces 1 with kEpiStore, or 3 with kEpiStoreScaled
+// pieces 1 with kEpiStore, 2 or 3 with kEpiStoreScaled, 2 with kEpiAdd
 hipError_t launch_dense_mm(const DenseMmArgs &a, int pieces, int epi, hipStream_t s);
 // Router top-k of T tokens from ks partial logit arrays [ks][T][E]. Optional: z [T][L]
 // fp32 quantized into zq piece records meanwhile; for T == 1, expert_off .. counters
 // receive that token's dispatch (as launch_dispatch would write it).
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
 // one token: af kA_BF16/kA_F32, xf kX_BF16/kX_PLANES, epi kEpiStore/kEpiStoreScaled, rpw
-// rows per wave (1 or 2)
+// rows per wave (1 or 2); bf16 kX_BF16 kEpiGluAct (rpw 2: the row of A and of A2); bf16
+// kX_F32 kEpiAdd (rpw 1)
 bool gemv1_supported(const Gemv1Args &a, int af);
 hipError_t launch_gemv1(const Gemv1Args &a, int af, int xf, int epi, int rpw, hipStream_t s);
 // the router product (fp32 weights, kEpiStore, its K parts) and the latent projection
@@ -174,6 +183,11 @@ hipError_t launch_active_from_off(const int32_t *expert_off, int E, int32_t *act
                                   int32_t *counters, hipStream_t s);
 hipError_t launch_split_planes(const float *src, size_t n, uint16_t *p0, uint16_t *p1,
                                uint16_t *p2, hipStream_t s);
+// act = SiTU-GLU(g, u) for gu [T][2 * SI] (g in columns 0 .. SI-1, u in SI .. 2 SI-1),
+// written as two bf16 pieces p0, p1 [T][SI] whose sum is act to 16 significant bits;
+// SI % 8 == 0
+hipError_t launch_glu_pieces(const float *gu, int T, int SI, float b1, float b2, uint16_t *p0,
+                             uint16_t *p1, hipStream_t s);
 // tokens_per_tile: 1, 2 or 4 tokens' piece records staged in LDS per tile (grouped_dec_lds bytes)
 constexpr size_t kMaxBlockLds = 81920;  // two blocks per compute unit
 // rb: 16-row blocks per block (4, 6 or 8 for kEpiSitu; 4 to 8 for kEpiEdn), from grouped_dec_rb

@@ -422,6 +422,43 @@ hipError_t launch_split_planes(const float *src, size_t n, uint16_t *p0, uint16_
   return hipGetLastError();
 }
 
+// ============================================================== shared-expert activation
+// Thread q: token t = q / (SI/8), columns 8c .. 8c+7 of it: reads g and u (two 32-byte
+// loads each), writes act's two bf16 pieces (one 16-byte store each).
+__global__ __launch_bounds__(256) void k_glu_pieces(const float *__restrict__ gu, int T, int SI, float b1,
+                                                    float b2, uint16_t *__restrict__ p0,
+                                                    uint16_t *__restrict__ p1) {
+  const int cpt = SI / 8;
+  const int64_t n = (int64_t)T * cpt;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < n; q += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = q / cpt;
+    const int c = (int)(q - t * cpt);
+    const float *g = gu + t * 2 * SI + 8 * c;
+    const float *u = g + SI;
+    const float4 g0 = *(const float4 *)g, g1 = *(const float4 *)(g + 4);
+    const float4 u0 = *(const float4 *)u, u1 = *(const float4 *)(u + 4);
+    const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    const float uv[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+    float a[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = situ(gv[i], uv[i], b1, b2);
+    u32x4 pc[3];
+    split_x8<2>(a, pc);
+    *(u32x4 *)(p0 + t * SI + 8 * c) = pc[0];
+    *(u32x4 *)(p1 + t * SI + 8 * c) = pc[1];
+  }
+}
+
+hipError_t launch_glu_pieces(const float *gu, int T, int SI, float b1, float b2, uint16_t *p0,
+                             uint16_t *p1, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (SI <= 0 || SI % 8 != 0) return hipErrorInvalidValue;
+  int64_t blocks = ((int64_t)T * (SI / 8) + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  launch_kernel(k_glu_pieces, (unsigned)blocks, 256, 0, s, gu, T, SI, b1, b2, p0, p1);
+  return hipGetLastError();
+}
+
 // Copy nbytes (a multiple of 16, 16-byte aligned) from global memory to LDS with the
 // whole block: each thread issues up to BATCH 16-byte loads before storing any, so
 // the loads overlap instead of paying one memory latency each.

@@ -62,3 +62,13 @@ def upload_layer(dims, dense: dict, expert_chunks, blob_bytes: int, offsets: dic
 def workspace(dims, T: int, device="cuda") -> torch.Tensor:
     n = k3moe.k3moe_workspace_size(dims, T)
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def shared_workspace(dims, n_shared: int, T: int, device="cuda") -> torch.Tensor:
+    n = k3moe.k3moe_shared_workspace_size(dims, n_shared, T)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def upload_shared(sh: dict, device="cuda") -> dict:
+    """The fused shared experts' sh1, sh3, sh2 (bf16 bits) as device tensors."""
+    return {k: _dev(sh[k].view(np.int16), device) for k in ("sh1", "sh3", "sh2")}

@@ -48,7 +48,8 @@ class k3moe_weights(ctypes.Structure):
 
 
 EXPORTS = ["k3moe_workspace_size", "k3moe_route", "k3moe_latent_proj_bf16", "k3moe_dispatch",
-           "k3moe_expert_glu_mxfp4", "k3moe_combine", "k3moe_layer", "k3moe_status_str"]
+           "k3moe_expert_glu_mxfp4", "k3moe_combine", "k3moe_layer", "k3moe_shared_workspace_size",
+           "k3moe_shared_glu_bf16", "k3moe_status_str"]
 
 _lib = None
 
@@ -73,6 +74,11 @@ def load(path: str | None = None):
     L.k3moe_expert_glu_mxfp4.argtypes = [D, i32, vp, ctypes.POINTER(k3moe_experts), vp, vp, vp, vp, sz, vp]
     L.k3moe_combine.argtypes = [D, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.k3moe_layer.argtypes = [D, i32, vp, ctypes.POINTER(k3moe_weights), vp, vp, vp, vp, sz, vp]
+    L.k3moe_shared_workspace_size.argtypes = [D, i32, i32, ctypes.POINTER(sz)]
+    L.k3moe_shared_glu_bf16.argtypes = [D, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.k3moe_shared_profiled.argtypes = [D, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp,
+                                        ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+    L.k3moe_shared_profiled.restype = ctypes.c_int
     L.k3moe_status_str.argtypes = [ctypes.c_int]
     L.k3moe_status_str.restype = ctypes.c_char_p
     L.k3moe_layer_profiled.argtypes = [D, i32, vp, ctypes.POINTER(k3moe_weights), vp, vp, vp, vp, sz, vp,
@@ -211,6 +217,35 @@ def k3moe_layer_profiled(dims, T, x, weights: k3moe_weights, y, topk_idx_out, to
                                      _ptr(topk_idx_out), _ptr(topk_w_out), p, n, _stream(stream), arr,
                                      len(events), ctypes.byref(nk))
     _check(rc, "k3moe_layer_profiled")
+    return [load().k3moe_prof_name(i).decode() for i in range(nk.value)]
+
+
+def k3moe_shared_workspace_size(dims, n_shared: int, T: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().k3moe_shared_workspace_size(ctypes.byref(_dims(dims)), n_shared, T, ctypes.byref(n)),
+           "k3moe_shared_workspace_size")
+    return n.value
+
+
+def k3moe_shared_glu_bf16(dims, n_shared, T, x, sh1, sh3, sh2, y, ws, stream=None, check=True):
+    """y += the fused shared experts on x (y is read and written)."""
+    p, n = _ws(ws)
+    rc = load().k3moe_shared_glu_bf16(ctypes.byref(_dims(dims)), n_shared, T, _ptr(x), _ptr(sh1), _ptr(sh3),
+                                      _ptr(sh2), _ptr(y), p, n, _stream(stream))
+    if check:
+        _check(rc, "k3moe_shared_glu_bf16")
+    return rc
+
+
+def k3moe_shared_profiled(dims, n_shared, T, x, sh1, sh3, sh2, y, ws, events, stream=None):
+    """As k3moe_shared_glu_bf16 with each launch timed (see k3moe_layer_profiled)."""
+    p, n = _ws(ws)
+    arr = (ctypes.c_void_p * len(events))(*events)
+    nk = ctypes.c_int(0)
+    rc = load().k3moe_shared_profiled(ctypes.byref(_dims(dims)), n_shared, T, _ptr(x), _ptr(sh1), _ptr(sh3),
+                                      _ptr(sh2), _ptr(y), p, n, _stream(stream), arr, len(events),
+                                      ctypes.byref(nk))
+    _check(rc, "k3moe_shared_profiled")
     return [load().k3moe_prof_name(i).decode() for i in range(nk.value)]
 
 

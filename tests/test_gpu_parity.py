@@ -361,6 +361,104 @@ def test_k3_layer_T256_both_expert_forms(k3, expert_path, mode):
     compare_layer(k3, x, what=f"K3 T=256 form {mode}")
 
 
+# ------------------------------------------------------------------ shared experts
+def run_shared(d, n_shared, x: np.ndarray, shd: dict, y0: np.ndarray):
+    T = x.shape[0]
+    y = t_(y0.astype(np.float32))
+    ws = device.shared_workspace(d, n_shared, T)
+    k3moe.k3moe_shared_glu_bf16(d, n_shared, T, t_(x.view(np.int16)), shd["sh1"], shd["sh3"], shd["sh2"], y, ws)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+@pytest.fixture(scope="module")
+def tiny_shared():
+    d = k3gen.TINY
+    sh = {n: k3gen.gen_shared(d, 7, n) for n in (2, 4)}
+    return d, sh, {n: device.upload_shared(v) for n, v in sh.items()}
+
+
+@pytest.mark.parametrize("n_shared", [2, 4])
+@pytest.mark.parametrize("T", [1, 3, 64, 300])
+def test_tiny_shared_experts(tiny_shared, n_shared, T):
+    d, sh, shd = tiny_shared
+    say(f"tiny shared experts n_shared={n_shared} T={T}")
+    x = k3gen.gen_x(d, 11 + T, T)
+    zero = np.zeros((T, d.hidden), np.float32)
+    got = run_shared(d, n_shared, x, shd[n_shared], zero)
+    check_rows(got, oracle.shared(d, x, sh[n_shared], zero, n_shared), f"shared n={n_shared} T={T} alone")
+    # added to an existing output, unweighted
+    y0 = np.random.default_rng(T).standard_normal((T, d.hidden)).astype(np.float32)
+    got = run_shared(d, n_shared, x, shd[n_shared], y0)
+    check_rows(got, oracle.shared(d, x, sh[n_shared], y0, n_shared), f"shared n={n_shared} T={T} added")
+
+
+def test_tiny_shared_host_checks(tiny_shared):
+    d, sh, shd = tiny_shared
+    x = t_(k3gen.gen_x(d, 1, 2).view(np.int16))
+    y0 = np.random.default_rng(0).standard_normal((2, d.hidden)).astype(np.float32)
+    y = t_(y0)
+    ws = device.shared_workspace(d, 2, 2)
+    lib = k3moe
+    # inter 96: one shared expert is 96 rows, not a multiple of 64
+    assert lib.k3moe_shared_glu_bf16(d, 1, 2, x, shd[2]["sh1"], shd[2]["sh3"], shd[2]["sh2"], y, ws,
+                                     check=False) == lib.K3MOE_EUNSUPPORTED
+    assert lib.k3moe_shared_glu_bf16(d, 0, 2, x, shd[2]["sh1"], shd[2]["sh3"], shd[2]["sh2"], y, ws,
+                                     check=False) == lib.K3MOE_EINVAL
+    small = device.shared_workspace(d, 2, 1)
+    assert lib.k3moe_shared_glu_bf16(d, 2, 2, x, shd[2]["sh1"], shd[2]["sh3"], shd[2]["sh2"], y, small,
+                                     check=False) == lib.K3MOE_EWORKSPACE
+    assert lib.k3moe_shared_glu_bf16(d, 2, 2, x, None, shd[2]["sh3"], shd[2]["sh2"], y, ws,
+                                     check=False) == lib.K3MOE_EINVAL
+    # T = 0 is a no-op; refused calls launched nothing
+    lib.k3moe_shared_glu_bf16(d, 2, 0, x, shd[2]["sh1"], shd[2]["sh3"], shd[2]["sh2"], y, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy(), y0)
+
+
+@pytest.fixture(scope="module")
+def k3_shared():
+    say("generating and uploading the K3 shared experts (2 x 3072 wide, 264 MB)")
+    sh = k3gen.gen_shared(k3gen.K3, 1, 2)
+    return sh, device.upload_shared(sh)
+
+
+def layer_plus_shared(h: Host, sh, shd, x: np.ndarray, rows, what: str):
+    d = h.dims
+    T = x.shape[0]
+    y, idx, w = run_layer(h, x)
+    y = run_shared(d, 2, x, shd, y)
+    ref = oracle.layer(d, x[rows], h.dense, h.ex)
+    assert np.array_equal(idx[rows], ref["idx"]), f"{what}: expert ids differ"
+    check_rows(y[rows], oracle.shared(d, x[rows], sh, ref["y"]), f"{what} y with shared experts")
+    # the shared part alone, on a zero output
+    zero = np.zeros((T, d.hidden), np.float32)
+    alone = run_shared(d, 2, x, shd, zero)
+    check_rows(alone[rows], oracle.shared(d, x[rows], sh, zero[rows]), f"{what} shared experts alone")
+
+
+def test_k3_layer_with_shared_T1(k3, k3_shared):
+    x = k3gen.gen_x(k3.dims, 1, 1)
+    layer_plus_shared(k3, *k3_shared, x, np.arange(1), "K3 T=1")
+
+
+def test_k3_layer_with_shared_T64(k3, k3_shared):
+    x = k3gen.gen_x(k3.dims, 2, 64)
+    layer_plus_shared(k3, *k3_shared, x, np.arange(64), "K3 T=64")
+
+
+def test_k3_shared_T4096_sampled(k3_shared):
+    sh, shd = k3_shared
+    d = k3gen.K3
+    T = 4096
+    x = k3gen.gen_x(d, 3, T)
+    y0 = np.random.default_rng(3).standard_normal((T, d.hidden)).astype(np.float32) * 0.05
+    got = run_shared(d, 2, x, shd, y0)
+    rng = np.random.default_rng(4)
+    rows = np.concatenate([[0, T - 1], rng.choice(T, 24, replace=False)])
+    check_rows(got[rows], oracle.shared(d, x[rows], sh, y0[rows]), "K3 T=4096 sampled shared")
+
+
 def check_dispatch_of(h: Host, ids: np.ndarray, what: str):
     d = h.dims
     T = ids.shape[0]
