@@ -250,7 +250,7 @@ hipError_t launch_gemv1(const Gemv1Args &a, int af, int xf, int epi, int rpw, hi
   G1(kA_BF16, kX_PLANES, kEpiStoreScaled, 1)
   G1(kA_BF16, kX_PLANES, kEpiStoreScaled, 2)
   G1(kA_BF16, kX_BF16, kEpiGluAct, 2)
-  G1(kA_BF16, kX_F32, kEpiAdd, 1)
+  G1(kA_BF16, kX_F32, kEpiAdd, 2)
 #undef G1
   return hipErrorInvalidValue;
 }

@@ -167,7 +167,7 @@ hipError_t launch_dense_mm(const DenseMmArgs &a, int pieces, int epi, hipStream_
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
 // one token: af kA_BF16/kA_F32, xf kX_BF16/kX_PLANES, epi kEpiStore/kEpiStoreScaled, rpw
 // rows per wave (1 or 2); bf16 kX_BF16 kEpiGluAct (rpw 2: the row of A and of A2); bf16
-// kX_F32 kEpiAdd (rpw 1)
+// kX_F32 kEpiAdd (rpw 2)
 bool gemv1_supported(const Gemv1Args &a, int af);
 hipError_t launch_gemv1(const Gemv1Args &a, int af, int xf, int epi, int rpw, hipStream_t s);
 // the router product (fp32 weights, kEpiStore, its K parts) and the latent projection

@@ -61,6 +61,12 @@ def load(path: str | None = None):
     if _lib is not None and path is None:
         return _lib
     p = path or LIB_PATH
+    try:
+        # torch ships a HIP runtime of its own: it must be the one loaded first, so that this
+        # library binds to it and its kernels run on torch's streams and memory
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(p):
         from . import build as _build
         _build.build()
