@@ -115,6 +115,7 @@ class Dims:
     routed_scale: float = 1.0
     b1: float = 4.0
     b2: float = 25.0
+    topp: float = 0.0  # top-p tail drop of the chosen experts (0 = off)
 
 
 # Kimi K3 MoE fields as the pages' config reader lists them (hidden 7168, 896

@@ -25,7 +25,7 @@ class Dims(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int), ("latent", ctypes.c_int), ("inter", ctypes.c_int),
                 ("n_experts", ctypes.c_int), ("topk", ctypes.c_int), ("group", ctypes.c_int),
                 ("renorm", ctypes.c_int), ("routed_scale", ctypes.c_float), ("eps", ctypes.c_float),
-                ("b1", ctypes.c_float), ("b2", ctypes.c_float)]
+                ("b1", ctypes.c_float), ("b2", ctypes.c_float), ("topp", ctypes.c_float)]
 
 
 class Mx(ctypes.Structure):
@@ -69,6 +69,8 @@ def lib():
         L.k3o_bf16_matvec.restype = None
         L.k3o_router.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f]
         L.k3o_router.restype = ctypes.c_double
+        L.k3o_router_topp.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, f, vp]
+        L.k3o_router_topp.restype = ctypes.c_double
         L.k3o_situ.argtypes = [f, f, f, f]
         L.k3o_situ.restype = f
         L.k3o_rmsnorm.argtypes = [vp, vp, vp, i, f]
@@ -79,7 +81,7 @@ def lib():
         L.k3o_dispatch.restype = i
         L.k3o_layer.argtypes = [ctypes.POINTER(Dims), i, vp, ctypes.POINTER(Weights), vp, vp, vp, vp, vp, vp, i]
         L.k3o_layer.restype = i
-        L.k3o_route_batch.argtypes = [ctypes.POINTER(Dims), i, vp, vp, vp, vp, vp, vp, i]
+        L.k3o_route_batch.argtypes = [ctypes.POINTER(Dims), i, vp, vp, vp, vp, vp, vp, vp, i]
         L.k3o_route_batch.restype = None
         L.k3o_scores_batch.argtypes = [ctypes.POINTER(Dims), i, vp, vp, vp, i]
         L.k3o_scores_batch.restype = None
@@ -101,7 +103,7 @@ def _p(a):
 def make_dims(d) -> Dims:
     """From any object with the layer's dimension fields (e.g. k3gen.Dims)."""
     return Dims(d.hidden, d.latent, d.inter, d.n_experts, d.topk, d.group, d.renorm,
-                d.routed_scale, d.eps, d.b1, d.b2)
+                d.routed_scale, d.eps, d.b1, d.b2, getattr(d, "topp", 0.0))
 
 
 class ExpertSet:
@@ -169,6 +171,21 @@ def router(x: np.ndarray, Wr: np.ndarray, bias, topk: int, renorm: int = 1, rout
     return idx, w, sel, gap
 
 
+def router_topp(x: np.ndarray, Wr: np.ndarray, bias, topk: int, topp: float, renorm: int = 1,
+                routed_scale: float = 1.0):
+    """One token with the top-p tail drop (k3o_router_topp). Returns (idx, weights, gap,
+    margin); dropped slots hold id -1 and weight 0."""
+    E, H = Wr.shape
+    idx = np.empty(topk, np.int32)
+    w = np.empty(topk, np.float32)
+    margin = np.empty(1, np.float64)
+    gap = lib().k3o_router_topp(_p(idx), _p(w), None, _p(np.ascontiguousarray(x, np.float32)),
+                                _p(np.ascontiguousarray(Wr, np.float32)),
+                                None if bias is None else _p(np.ascontiguousarray(bias, np.float32)),
+                                H, E, topk, renorm, routed_scale, topp, _p(margin))
+    return idx, w, gap, float(margin[0])
+
+
 def situ(g: float, u: float, b1: float = 4.0, b2: float = 25.0) -> float:
     return lib().k3o_situ(g, u, b1, b2)
 
@@ -227,18 +244,21 @@ def layer(dims, x: np.ndarray, dense: dict, ex: ExpertSet, nthreads: int = 0, wa
     return out
 
 
-def route_batch(dims, x: np.ndarray, Wr: np.ndarray, bias: np.ndarray, nthreads: int = 0):
-    """Router only for rows of x. Returns (idx [T,K], w [T,K], gaps [T])."""
+def route_batch(dims, x: np.ndarray, Wr: np.ndarray, bias: np.ndarray, nthreads: int = 0,
+                want_margins: bool = False):
+    """Router only for rows of x (with dims.topp's tail drop). Returns (idx [T,K], w [T,K],
+    gaps [T]), plus the top-p decision margins [T] when want_margins."""
     T = x.shape[0]
     K = dims.topk
     idx = np.empty((T, K), np.int32)
     w = np.empty((T, K), np.float32)
     gaps = np.empty(T, np.float64)
+    margins = np.empty(T, np.float64) if want_margins else None
     d = make_dims(dims)
     lib().k3o_route_batch(ctypes.byref(d), T, _p(np.ascontiguousarray(x, np.uint16)),
                           _p(np.ascontiguousarray(Wr, np.float32)), _p(np.ascontiguousarray(bias, np.float32)),
-                          _p(idx), _p(w), _p(gaps), nthreads)
-    return idx, w, gaps
+                          _p(idx), _p(w), _p(gaps), _p(margins), nthreads)
+    return (idx, w, gaps, margins) if want_margins else (idx, w, gaps)
 
 
 def scores_batch(dims, x: np.ndarray, Wr: np.ndarray, nthreads: int = 0) -> np.ndarray:

@@ -100,6 +100,15 @@ double k3o_router(int *idx, float *w, int *sel_order, const float *x, const floa
                   const float *bias, int hidden, int n_experts, int topk, int renorm,
                   float routed_scale)
 {
+    return k3o_router_topp(idx, w, sel_order, x, Wr, bias, hidden, n_experts, topk, renorm,
+                           routed_scale, 0.0f, NULL);
+}
+
+/* [COL-RT]: see k3o.h. */
+double k3o_router_topp(int *idx, float *w, int *sel_order, const float *x, const float *Wr,
+                       const float *bias, int hidden, int n_experts, int topk, int renorm,
+                       float routed_scale, float topp, double *margin)
+{
     float *sc = (float *)malloc(sizeof(float) * (size_t)n_experts);
     double *ch = (double *)malloc(sizeof(double) * (size_t)n_experts);
     unsigned char *taken = (unsigned char *)calloc((size_t)n_experts, 1);
@@ -139,6 +148,54 @@ double k3o_router(int *idx, float *w, int *sel_order, const float *x, const floa
         double v = (double)sc[idx[j]];
         if (renorm && s > 0.0) v /= s;
         w[j] = (float)(v * (double)routed_scale);
+    }
+
+    if (topp > 0.0f) {
+        /* [COL-RT]: fractions of the chosen total, walked largest first */
+        float *f = (float *)malloc(sizeof(float) * (size_t)topk);
+        int *ord = (int *)malloc(sizeof(int) * (size_t)topk);
+        unsigned char *keep = (unsigned char *)calloc((size_t)topk, 1);
+        for (int j = 0; j < topk; j++) {
+            f[j] = (float)((double)sc[idx[j]] / s);
+            ord[j] = j;
+        }
+        /* insertion sort of positions by (fraction descending, id ascending) */
+        for (int a = 1; a < topk; a++) {
+            const int v = ord[a];
+            int b = a - 1;
+            while (b >= 0 && (f[ord[b]] < f[v] || (f[ord[b]] == f[v] && idx[ord[b]] > idx[v]))) {
+                ord[b + 1] = ord[b];
+                b--;
+            }
+            ord[b + 1] = v;
+        }
+        float cum = 0.0f;
+        double closest = INFINITY;
+        for (int r = 0; r < topk; r++) {
+            const double dist = fabs((double)cum - (double)topp);
+            if (dist < closest) closest = dist;
+            if (cum < topp) keep[ord[r]] = 1;
+            cum = cum + f[ord[r]];
+        }
+        double sk = 0.0;
+        for (int j = 0; j < topk; j++)
+            if (keep[j]) sk += (double)sc[idx[j]];
+        for (int j = 0; j < topk; j++) {
+            if (!keep[j]) {
+                idx[j] = -1;
+                w[j] = 0.0f;
+                continue;
+            }
+            double v = (double)sc[idx[j]];
+            if (renorm && sk > 0.0) v /= sk;
+            w[j] = (float)(v * (double)routed_scale);
+        }
+        if (margin) *margin = closest;
+        free(f);
+        free(ord);
+        free(keep);
+    } else if (margin) {
+        *margin = INFINITY;
     }
 
     free(sc);
@@ -199,13 +256,18 @@ int k3o_dispatch(const int *topk_idx, int T, int K, int E, int *expert_off,
 {
     const int P = T * K;
     for (int p = 0; p < P; p++)
-        if (topk_idx[p] < 0 || topk_idx[p] >= E) return -1;
+        if (topk_idx[p] < -1 || topk_idx[p] >= E) return -1;
     int *fill = (int *)calloc((size_t)E, sizeof(int));
     for (int e = 0; e <= E; e++) expert_off[e] = 0;
-    for (int p = 0; p < P; p++) expert_off[topk_idx[p] + 1]++;
+    for (int p = 0; p < P; p++)
+        if (topk_idx[p] >= 0) expert_off[topk_idx[p] + 1]++;
     for (int e = 0; e < E; e++) expert_off[e + 1] += expert_off[e];
     for (int p = 0; p < P; p++) { /* p = t*K + j in increasing order: stable in t */
         const int e = topk_idx[p];
+        if (e < 0) { /* a slot the top-p tail rule dropped */
+            pair_slot[p] = -1;
+            continue;
+        }
         const int pos = expert_off[e] + fill[e]++;
         sorted_pair[pos] = p;
         pair_slot[p] = pos;
@@ -229,10 +291,11 @@ static void k3o_token(const k3o_dims *d, const uint16_t *xt_bf16, const k3o_weig
 
     /* [K3C-9] step order: route on the full width, project down to the latent,
      * run the chosen experts and sum them weighted, norm the AGGREGATE, project up. */
-    k3o_router(idx, wt, NULL, xf, w->w_router, w->bias, H, d->n_experts, K, d->renorm,
-               d->routed_scale);
+    k3o_router_topp(idx, wt, NULL, xf, w->w_router, w->bias, H, d->n_experts, K, d->renorm,
+                    d->routed_scale, d->topp, NULL);
     k3o_bf16_matvec(z, xf, w->w_down, H, L);
     for (int j = 0; j < K; j++) {
+        if (idx[j] < 0) continue; /* dropped by the top-p tail rule */
         k3o_expert(edn, NULL, NULL, NULL, z, &w->ex, idx[j], d);
         for (int c = 0; c < L; c++) acc[c] += (double)wt[j] * (double)edn[c];
     }
@@ -266,7 +329,8 @@ int k3o_layer(const k3o_dims *d, int T, const uint16_t *x, const k3o_weights *w,
 }
 
 void k3o_route_batch(const k3o_dims *d, int T, const uint16_t *x, const float *Wr,
-                     const float *bias, int *idx, float *wt, double *gaps, int nthreads)
+                     const float *bias, int *idx, float *wt, double *gaps, double *margins,
+                     int nthreads)
 {
     const int H = d->hidden, K = d->topk;
 #ifdef _OPENMP
@@ -278,8 +342,8 @@ void k3o_route_batch(const k3o_dims *d, int T, const uint16_t *x, const float *W
         int *ii = (int *)malloc(sizeof(int) * (size_t)K);
         float *ww = (float *)malloc(sizeof(float) * (size_t)K);
         for (int i = 0; i < H; i++) xf[i] = k3o_bf16_to_f32(x[(size_t)t * H + i]);
-        const double g = k3o_router(ii, ww, NULL, xf, Wr, bias, H, d->n_experts, K, d->renorm,
-                                    d->routed_scale);
+        const double g = k3o_router_topp(ii, ww, NULL, xf, Wr, bias, H, d->n_experts, K, d->renorm,
+                                         d->routed_scale, d->topp, margins ? margins + t : NULL);
         if (gaps) gaps[t] = g;
         if (idx) memcpy(idx + (size_t)t * K, ii, sizeof(int) * (size_t)K);
         if (wt) memcpy(wt + (size_t)t * K, ww, sizeof(float) * (size_t)K);

@@ -23,6 +23,9 @@
  *  [COL]   colibri docs/kimi_k3.md, "Architecture notes" (Stable LatentMoE) and
  *          "Weights" (MXFP4: low nibble = even column, bit 3 = sign, one ue8m0
  *          scale per 32 columns, w = v * 2^(scale - 127)).
+ *  [COL-RT] same page, "Streaming design" and "Environment variables" (K3_TOPP: an
+ *          optional top-p drop of the low-weight tail of the chosen experts,
+ *          renormalised; 0 = off).
  *
  * Readings taken where the pages leave a step open are listed at each function.
  */
@@ -47,6 +50,7 @@ typedef struct {
     float routed_scale; /* 1.0 */
     float eps;       /* RMSNorm epsilon, inside the square root */
     float b1, b2;    /* SiTU caps: 4 and 25 */
+    float topp;      /* 0: off; else keep the chosen experts up to cumulative weight topp */
 } k3o_dims;
 
 /* One MXFP4 matrix stacked over experts: expert e's packed bytes start at
@@ -96,6 +100,22 @@ double k3o_router(int *idx, float *w, int *sel_order, const float *x, const floa
                   const float *bias, int hidden, int n_experts, int topk, int renorm,
                   float routed_scale);
 
+/* [COL-RT] (the switch that keeps the routed experts up to a cumulative weight p, the
+ * low-weight tail of the top-K dropped and the rest renormalised): k3o_router, then the
+ * tail drop when 0 < topp. Readings: each chosen expert's fraction is its unbiased score
+ * over the chosen total (fp64, rounded to fp32); the chosen are ordered by fraction,
+ * larger first, equal fractions by lower id; walking that order with an fp32 running sum
+ * that starts at 0, an expert is kept while the sum of the fractions before it is below
+ * topp (so at least one is kept), and then the sum grows by its fraction. A dropped
+ * expert's slot keeps its place in the ascending id list with id -1 and weight 0; the
+ * kept weights are the router's weights renormalised over the kept set (fp64 sum of
+ * their unbiased scores; without renorm the router's weights unchanged). *margin (nullable)
+ * receives the smallest |prefix sum - topp| over the walk (how close the decision came),
+ * or +inf when the tail drop is off. */
+double k3o_router_topp(int *idx, float *w, int *sel_order, const float *x, const float *Wr,
+                       const float *bias, int hidden, int n_experts, int topk, int renorm,
+                       float routed_scale, float topp, double *margin);
+
 /* SiTU-GLU of one (gate, up) pair, fp64 inside, fp32 result */
 float k3o_situ(float g, float u, float b1, float b2);
 /* out = x / sqrt(mean(x^2) + eps) * w (w NULL = ones); fp64 inside, fp32 out; in place allowed */
@@ -108,7 +128,8 @@ void k3o_expert(float *edn, float *g, float *u, float *act, const float *z,
 
 /* Stable counting sort of the (token, slot) pairs by expert:
  * expert_off[E+1]; sorted_pair[P] = t*K + j ordered by (expert, t); pair_slot[p] = its
- * position. Returns 0, or -1 if an index is outside [0, E). */
+ * position. An index of -1 (a slot the top-p tail rule dropped) takes no position and
+ * gets pair_slot -1. Returns 0, or -1 if an index is outside [-1, E). */
 int k3o_dispatch(const int *topk_idx, int T, int K, int E, int *expert_off,
                  int *sorted_pair, int *pair_slot);
 
@@ -120,9 +141,11 @@ int k3o_dispatch(const int *topk_idx, int T, int K, int E, int *expert_off,
 int k3o_layer(const k3o_dims *d, int T, const uint16_t *x, const k3o_weights *w,
               float *y, int *idx, float *wt, float *z, float *acc, float *nrm, int nthreads);
 
-/* Router only, for T tokens: gaps[t] as returned by k3o_router; idx/wt nullable. */
+/* Router only, for T tokens (with d->topp's tail drop): gaps[t] as returned by
+ * k3o_router; idx/wt nullable. */
 void k3o_route_batch(const k3o_dims *d, int T, const uint16_t *x, const float *Wr,
-                     const float *bias, int *idx, float *wt, double *gaps, int nthreads);
+                     const float *bias, int *idx, float *wt, double *gaps, double *margins,
+                     int nthreads);
 
 /* Unbiased router scores sc[t][e] = sigmoid(Wr[e] . x_t) for T tokens (fp64 sum, fp32
  * result), the same values k3o_router weights by. OpenMP over tokens. */

@@ -67,6 +67,25 @@ def route(xf: np.ndarray, Wr: np.ndarray, bias: np.ndarray, K: int, renorm=1, ro
     return chosen, (w * routed_scale).astype(np.float32)
 
 
+def topp_drop(chosen: np.ndarray, sc_chosen: np.ndarray, p: float, renorm=1, routed_scale=1.0):
+    """The top-p tail drop on a routed token: fractions of the chosen total (fp32), walked
+    by (fraction descending, id ascending) with an fp32 running sum; kept while the sum
+    before is below p. Returns (ids with -1 for dropped, weights with 0 for dropped)."""
+    s = sc_chosen.astype(np.float64)
+    f = (s / s.sum()).astype(np.float32)
+    order = np.lexsort((chosen, -f))
+    before = np.zeros(len(f), np.float32)
+    run = np.float32(0.0)
+    for r, j in enumerate(order):
+        before[r] = run
+        run = np.float32(run + f[j])
+    keep = np.zeros(len(f), bool)
+    keep[order[before < np.float32(p)]] = True
+    sk = s[keep].sum()
+    w = np.where(keep, (s / sk if renorm else s) * routed_scale, 0.0).astype(np.float32)
+    return np.where(keep, chosen, -1).astype(np.int32), w
+
+
 def situ(g: np.ndarray, u: np.ndarray, b1=4.0, b2=25.0) -> np.ndarray:
     g = g.astype(np.float64)
     u = u.astype(np.float64)
@@ -77,9 +96,15 @@ def layer_token(dims, x_bf16: np.ndarray, dense: dict, expert_blob_fn, offsets: 
     """One token through the layer; expert_blob_fn(e) returns expert e's blob bytes."""
     xf = bf16_bits_to_f64(x_bf16)
     idx, w = route(xf, dense["w_router"], dense["bias"], dims.topk, dims.renorm, dims.routed_scale)
+    if getattr(dims, "topp", 0.0) > 0.0:
+        logit = dense["w_router"].astype(np.float64) @ xf
+        sc = (0.5 * (1.0 + np.tanh(0.5 * logit))).astype(np.float32)
+        idx, w = topp_drop(idx, sc[idx], dims.topp, dims.renorm, dims.routed_scale)
     z = (bf16_bits_to_f64(dense["w_down"]) @ xf).astype(np.float32)
     acc = np.zeros(dims.latent, np.float64)
     for e, wj in zip(idx, w):
+        if e < 0:
+            continue
         (p1, s1), (p3, s3), (p2, s2) = expert_views(expert_blob_fn(int(e)), dims, offsets)
         g = (decode_mxfp4(p1, s1, dims.group) @ z.astype(np.float64)).astype(np.float32)
         u = (decode_mxfp4(p3, s3, dims.group) @ z.astype(np.float64)).astype(np.float32)

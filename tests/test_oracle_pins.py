@@ -7,6 +7,7 @@ Each test is chosen so that a plausible slip in the oracle (a swapped nibble, a
 dropped scale, a wrong sign, the capped gate fed to the sigmoid, eps outside the
 root, biased scores used as weights, a transposed weight) fails at least one.
 """
+import dataclasses
 import json
 import math
 import os
@@ -403,3 +404,105 @@ def test_shared_one_hot_input_reads_one_column():
     a = _brute.situ(g, u, d.b1, d.b2).astype(np.float64)
     ref = _brute.bf16_bits_to_f64(sh["sh2"]) @ a
     assert np.max(np.abs(y[0] - ref)) <= 1e-6 * np.max(np.abs(ref))
+
+
+# ---------------------------------------------------------------- top-p tail drop
+def _one_hot_router(logits, K):
+    """A router whose scores are sigmoid(logits) exactly in fp64 terms: x = e_0."""
+    E = len(logits)
+    Wr = np.zeros((E, 4), np.float32)
+    Wr[:, 0] = logits
+    x = np.zeros(4, np.float32)
+    x[0] = 1.0
+    return x, Wr
+
+
+def test_topp_hand_case():
+    # scores sigmoid(2, 1, 0, -1) = .8808, .7311, .5, .2689: fractions .370, .307, .210, .113
+    logits = np.array([2.0, 1.0, 0.0, -1.0], np.float32)
+    x, Wr = _one_hot_router(logits, 4)
+    sc = 1.0 / (1.0 + np.exp(-logits.astype(np.float64)))
+    for p, kept in ((0.3, [0]), (0.6, [0, 1]), (0.7, [0, 1, 2]), (0.95, [0, 1, 2, 3])):
+        idx, w, _, margin = oracle.router_topp(x, Wr, np.zeros(4, np.float32), 4, p)
+        assert idx.tolist() == [e if e in kept else -1 for e in range(4)], p
+        ref = np.array([sc[e] / sc[kept].sum() if e in kept else 0.0 for e in range(4)])
+        assert np.allclose(w, ref, rtol=1e-6, atol=1e-7), p
+        assert margin > 1e-3
+    # without renorm the kept weights are the raw scores
+    idx, w, _, _ = oracle.router_topp(x, Wr, np.zeros(4, np.float32), 4, 0.6, renorm=0, routed_scale=2.0)
+    assert np.allclose(w, [2 * sc[0], 2 * sc[1], 0, 0], rtol=1e-6)
+
+
+def test_topp_equal_fractions_keep_lowest_ids():
+    x, Wr = _one_hot_router(np.zeros(6, np.float32), 4)
+    idx, w, _, _ = oracle.router_topp(x, Wr, np.zeros(6, np.float32), 4, 0.3)
+    # the four lowest ids are chosen; fractions all 1/4: 0 < .3 keeps id 0, .25 < .3 keeps id 1
+    assert idx.tolist() == [0, 1, -1, -1]
+    assert np.allclose(w, [0.5, 0.5, 0, 0])
+
+
+def test_topp_one_or_more_keeps_all():
+    d = k3gen.TINY
+    dense = k3gen.gen_dense(d, 0)
+    x = k3gen.gen_x(d, 0, 16)
+    a = oracle.route_batch(d, x, dense["w_router"], dense["bias"])
+    b = oracle.route_batch(dataclasses.replace(d, topp=1.0), x, dense["w_router"], dense["bias"])
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("p", [0.3, 0.5, 0.8, 0.95])
+def test_topp_brute_force_and_invariants(p):
+    d = dataclasses.replace(k3gen.TINY, n_experts=64, topk=8, topp=p)
+    dense = k3gen.gen_dense(d, 3)
+    x = k3gen.gen_x(d, 3, 200)
+    idx, w, _, margins = oracle.route_batch(d, x, dense["w_router"], dense["bias"], want_margins=True)
+    full, _, _ = oracle.route_batch(dataclasses.replace(d, topp=0.0), x, dense["w_router"], dense["bias"])
+    checked = 0
+    for t in range(x.shape[0]):
+        xf = _brute.bf16_bits_to_f64(x[t])
+        ch, _ = _brute.route(xf, dense["w_router"], dense["bias"], d.topk)
+        logit = dense["w_router"].astype(np.float64) @ xf
+        sc = (0.5 * (1.0 + np.tanh(0.5 * logit))).astype(np.float32)
+        bi, bw = _brute.topp_drop(ch, sc[ch], p)
+        kept = idx[t] >= 0
+        assert kept.any() and np.array_equal(idx[t][kept], full[t][kept])   # a subset, in place
+        assert np.isclose(w[t][kept].sum(), 1.0, atol=1e-6) and np.all(w[t][~kept] == 0)
+        f = sc[full[t]].astype(np.float64) / sc[full[t]].astype(np.float64).sum()
+        if not kept.all():
+            assert f[kept].sum() >= p - 1e-6                  # reaches p
+            assert f[kept].sum() - f[kept].min() < p + 1e-6   # and no kept expert is spare
+        if margins[t] > 1e-5:                                 # decisions far from the edge
+            assert np.array_equal(idx[t], bi), t
+            assert np.allclose(w[t], bw, rtol=1e-6, atol=1e-7)
+            checked += 1
+    assert checked > 150
+
+
+def test_dispatch_drops_minus_one():
+    ids = np.array([[0, -1, 5, 9], [-1, 5, -1, 7]], np.int32)
+    off, sp, ps = oracle.dispatch(ids, 10)
+    assert ps.tolist()[1] == -1 and ps.tolist()[4] == -1 and ps.tolist()[6] == -1
+    assert off[-1] == 5
+    flat = ids.reshape(-1)
+    valid = [q for q in range(8) if flat[q] >= 0]
+    assert sp[:5].tolist() == sorted(valid, key=lambda q: (flat[q], q))
+    with pytest.raises(ValueError):
+        oracle.dispatch(np.array([[0, -2, 1, 2]], np.int32), 10)
+
+
+def test_layer_topp_matches_brute_force_tiny():
+    d = dataclasses.replace(k3gen.TINY, topp=0.6)
+    dense = k3gen.gen_dense(d, 0)
+    lay = k3gen.ExpertLayout(d)
+    blobs = k3gen.gen_experts(d, 0, 0, d.n_experts)
+    ex = oracle.ExpertSet(blobs, lay.blob_bytes, lay.offsets)
+    x = k3gen.gen_x(d, 0, 8)
+    r = oracle.layer(d, x, dense, ex, want_inner=True)
+    assert (r["idx"] < 0).any()          # the rule dropped something
+    B = lay.blob_bytes
+    for t in range(x.shape[0]):
+        b = _brute.layer_token(d, x[t], dense, lambda e: blobs[e * B:(e + 1) * B], lay.offsets)
+        assert np.array_equal(r["idx"][t], b["idx"])
+        for k in ("acc", "y"):
+            ref = b[k].astype(np.float64)
+            assert np.linalg.norm(r[k][t] - ref) / np.linalg.norm(ref) < 1e-6, (t, k)
