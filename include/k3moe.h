@@ -18,6 +18,15 @@
  *   5. y = W_up n (bf16 weights, [H][L]).
  *   6. (k3moe_shared_glu_bf16, a call of its own) y += the shared experts on x.
  *
+ * Top-p tail drop (colibri docs/kimi_k3.md, "Streaming design" and "Environment
+ * variables", K3_TOPP; an approximation, off unless dims.topp > 0): after step 1 the K
+ * chosen are ordered by their fraction of the chosen score total (sc_e / sum sc, fp32),
+ * larger first, equal fractions by lower id; walking that order with an fp32 running sum
+ * from 0, an expert is kept while the sum of the fractions before it is below topp (so
+ * at least one is kept; topp >= 1 keeps all). A dropped slot keeps its place in
+ * topk_idx with id -1 and weight 0 (k3moe_dispatch and k3moe_combine skip it); the kept
+ * weights are renormalised over the kept set (when renorm is set), times routed_scale.
+ *
  * MXFP4 layout (section 4; colibri "Weights"): a matrix [rows][cols] is stored as
  * packed bytes [rows][cols/2], column 2k in the LOW nibble of byte k and column 2k+1
  * in the HIGH nibble, each nibble an E2M1 code (bit 3 = sign), plus scale bytes
@@ -85,6 +94,7 @@ typedef struct {
     float routed_scale; /* multiplies every routing weight (K3: 1.0) */
     float eps;          /* RMSNorm epsilon, inside the square root (K3: 1e-5) */
     float b1, b2;       /* SiTU-GLU caps (K3: 4 and 25) */
+    float topp;         /* 0: off (K3 default). > 0: the top-p tail drop, see below */
 } k3moe_dims;
 
 typedef struct {

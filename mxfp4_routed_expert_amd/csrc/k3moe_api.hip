@@ -28,7 +28,7 @@ int check_dims(const k3moe_dims *d) {
     return K3MOE_EINVAL;
   if (d->renorm != 0 && d->renorm != 1) return K3MOE_EINVAL;
   if (!(d->eps >= 0.f) || !isfinite(d->eps) || !isfinite(d->b1) || !isfinite(d->b2) ||
-      d->b1 == 0.f || d->b2 == 0.f || !isfinite(d->routed_scale))
+      d->b1 == 0.f || d->b2 == 0.f || !isfinite(d->routed_scale) || !(d->topp >= 0.f) || !isfinite(d->topp))
     return K3MOE_EINVAL;
   if (d->group != 32) return K3MOE_EUNSUPPORTED;
   if (d->hidden % 32 || d->latent % 32 || d->inter % 32) return K3MOE_EUNSUPPORTED;
@@ -288,6 +288,7 @@ TopkArgs topk_args(const k3moe_dims *d, int32_t T, const float *part, int ks, co
   a.idx = idx;
   a.w = wt;
   a.L = d->latent;
+  a.topp = d->topp;
   return a;
 }
 
@@ -347,7 +348,8 @@ int run_front(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_wei
     g.K = d->latent;
     g.gather = 1;
     g.tk = tk;
-    if (route && !use_mm(d, T, d->latent, (int64_t)T * d->latent * 4, wt->ex.w1, wt->ex.w3) &&
+    // (the selection at the head of the gate/up pass has no top-p tail drop)
+    if (route && !(d->topp > 0.f) && !use_mm(d, T, d->latent, (int64_t)T * d->latent * 4, wt->ex.w1, wt->ex.w3) &&
         route_in_gateup_ok(g)) {
       *route = tk;
       *zq_ready = false;
@@ -777,9 +779,11 @@ int k3moe_layer(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_w
   bool zq_ready = false;
   TopkArgs route = {};
   K3_TRY(run_front(d, T, x, wt, idx, tw, w, &zq_ready, &route, s));
-  K3_TRY(run_experts(d, T, w.z32, zq_ready, route.T ? &route : nullptr, T == 1, &wt->ex, w.expert_off,
+  // a one-token batch's pairs are its K slots in order, unless the top-p rule dropped some
+  const bool one_token = T == 1 && !(d->topp > 0.f);
+  K3_TRY(run_experts(d, T, w.z32, zq_ready, route.T ? &route : nullptr, one_token, &wt->ex, w.expert_off,
                      w.sorted_pair, w.active, w.counters, w.edn, w, s));
-  return run_combine(d, T, w.edn, w.pair_slot, tw, wt->norm_w, wt->w_up, y, T == 1, w, s);
+  return run_combine(d, T, w.edn, w.pair_slot, tw, wt->norm_w, wt->w_up, y, one_token, w, s);
 }
 
 int k3moe_layer_profiled(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_weights *wt,

@@ -120,6 +120,7 @@ struct TopkArgs {
   int L;
   uint8_t *zq;
   int32_t *expert_off, *sorted_pair, *pair_slot, *active, *counters;
+  float topp;  // > 0: the top-p tail drop (topk_select_wave with TP)
 };
 
 struct GroupedArgs {

@@ -54,6 +54,64 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// The top-p tail drop and the writes of one token's selection (topk_select_wave with TP):
+// lanes with sel hold chosen expert ce at ascending-id position pos with unbiased score
+// scc; ssum is the chosen total. Words 320 .. 383 of s_scr hold the fractions and ids,
+// 384 .. 415 the kept ids for the one-token dispatch.
+template <int S>
+__device__ __forceinline__ void topk_topp_write(const TopkArgs &a, int t, bool sel, int pos, int ce, float scc,
+                                             float ssum, uint32_t *s_scr, const bool (&real)[S]) {
+  const int E = a.E, K = a.K, lane = threadIdx.x & 63;
+  const float f = sel ? scc / ssum : 0.f;
+  if (sel) {
+    s_scr[320 + pos] = __float_as_uint(f);
+    s_scr[352 + pos] = (uint32_t)ce;
+  }
+  wave_lds_sync();
+  int rank = 0;
+  for (int k = 0; k < K; ++k) {
+    const float fk = __uint_as_float(s_scr[320 + k]);
+    const int ek = (int)s_scr[352 + k];
+    rank += (fk > f || (fk == f && ek < ce)) ? 1 : 0;
+  }
+  wave_lds_sync();
+  if (sel) s_scr[320 + rank] = __float_as_uint(f);
+  wave_lds_sync();
+  float before = 0.f;  // the fractions of the larger ones, summed largest first
+  for (int r = 0; r < rank; ++r) before = before + __uint_as_float(s_scr[320 + r]);
+  const bool keep = sel && before < a.topp;
+  const float ksum = wave_sum_fixed(keep ? scc : 0.f);
+  if (sel) {
+    a.idx[(size_t)t * K + pos] = keep ? ce : -1;
+    a.w[(size_t)t * K + pos] = keep ? ((a.renorm && ksum > 0.f) ? scc / ksum : scc) * a.rscale : 0.f;
+  }
+  if (!a.expert_off) return;
+  if (sel) s_scr[384 + pos] = keep ? (uint32_t)ce : 0x7FFFFFFFu;
+  wave_lds_sync();
+  int kpos = 0;  // place among the kept (ascending ids)
+  for (int k = 0; k < K; ++k) kpos += (int)s_scr[384 + k] < ce ? 1 : 0;
+  if (keep) {
+    a.active[kpos] = ce;
+    a.sorted_pair[kpos] = pos;
+  }
+  if (sel) a.pair_slot[pos] = keep ? kpos : -1;
+  // expert_off[e] = kept ids below e
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int e = 64 * s + lane;
+    int nb = 0;
+    for (int k = 0; k < K; ++k) nb += (int)s_scr[384 + k] < e ? 1 : 0;
+    if (real[s]) a.expert_off[e] = nb;
+  }
+  const int nk = wave_sum_int(keep ? 1 : 0);
+  if (lane == 0) {
+    a.expert_off[E] = nk;
+    a.counters[0] = nk;
+    a.counters[1] = K - nk;
+  }
+}
+
+
 // The selection from the keys in one wave's registers, with no block barrier, ranking
 // keys against each other (vector compares against LDS broadcasts) instead of counting
 // with lane masks. Order: by key, then the lower id first (so equal selection scores go
@@ -66,8 +124,13 @@ __device__ __forceinline__ void wave_lds_sync() {
 // set, the dispatch of a one-token batch: its K pairs in ascending expert order are
 // the K slots themselves); with slot >= 0, *s_slot_e receives the chosen id at that
 // position, visible to the block after the caller's next barrier. s_scr: 448 words of
-// LDS scratch, 16-byte aligned.
-template <int S>
+// LDS scratch, 16-byte aligned. TP: apply a.topp's tail drop (when a.topp > 0) before
+// writing: the chosen are walked by their fraction of the chosen score total, larger
+// first (equal: lower id first), with an fp32 running sum from 0; one is kept while the
+// sum of those before it is below a.topp; a dropped slot writes id -1 and weight 0, the
+// kept weights are renormalised over the kept, and the one-token dispatch lists only
+// the kept pairs.
+template <int S, bool TP = false>
 __device__ __forceinline__ void topk_select_wave(const TopkArgs &a, int t, const uint32_t (&key)[S],
                                                  const float (&sc)[S], const bool (&real)[S], uint32_t *s_scr,
                                                  bool out, int slot, int *s_slot_e) {
@@ -184,6 +247,12 @@ __device__ __forceinline__ void topk_select_wave(const TopkArgs &a, int t, const
   const float ssum = wave_sum_fixed(scc);
   if (slot >= 0 && sel && pos == slot) *s_slot_e = ce;
   if (!out) return;
+  if constexpr (TP) {
+    if (a.topp > 0.f) {
+      topk_topp_write(a, t, sel, pos, ce, scc, ssum, s_scr, real);
+      return;
+    }
+  }
   if (sel && pos < K) {
     a.idx[(size_t)t * K + pos] = ce;
     a.w[(size_t)t * K + pos] = ((a.renorm && ssum > 0.f) ? scc / ssum : scc) * a.rscale;
@@ -222,7 +291,7 @@ __device__ __forceinline__ void topk_wave(const TopkArgs &a, int t, uint32_t *s_
   float sc[16];
   bool real[16];
   topk_keys_wave<16, KS>(a, t, key, sc, real);
-  topk_select_wave<16>(a, t, key, sc, real, s_scr, true, -1, nullptr);
+  topk_select_wave<16, true>(a, t, key, sc, real, s_scr, true, -1, nullptr);
 }
 
 // Rows of z [rows][L] into fp6 piece records: lane task q (of rows * L / 8) quantizes

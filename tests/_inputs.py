@@ -17,21 +17,30 @@ import k3gen
 import oracle
 
 MIN_GAP = 1e-3
+# with the top-p tail drop on, a token whose walk passes within this of p is redrawn too
+# (the GPU's fractions and running sum agree with the oracle's to about 1e-6)
+MIN_TOPP_MARGIN = 1e-4
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _gaps(dims, x, w_router, bias, nthreads):
+    if getattr(dims, "topp", 0.0) > 0.0:
+        _, _, g, m = oracle.route_batch(dims, x, w_router, bias, nthreads, want_margins=True)
+        return np.where(m < MIN_TOPP_MARGIN, 0.0, g)
+    return oracle.route_batch(dims, x, w_router, bias, nthreads)[2]
 
 
 def gap_fixed_x(dims, seed, T, w_router, bias, nthreads=0, max_rounds=200):
     attempts = np.zeros(T, np.int64)
     x = k3gen.gen_x(dims, seed, T)
-    _, _, gaps = oracle.route_batch(dims, x, w_router, bias, nthreads)
+    gaps = _gaps(dims, x, w_router, bias, nthreads)
     for _ in range(max_rounds):
         bad = np.flatnonzero(gaps < MIN_GAP)
         if bad.size == 0:
             return x, attempts
         attempts[bad] += 1
         x[bad] = k3gen.gen_x_rows(dims, seed, bad, attempts[bad])
-        _, _, g = oracle.route_batch(dims, x[bad], w_router, bias, nthreads)
-        gaps[bad] = g
+        gaps[bad] = _gaps(dims, x[bad], w_router, bias, nthreads)
     raise RuntimeError("gap rule not met")
 
 

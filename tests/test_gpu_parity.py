@@ -4,6 +4,7 @@ token row within rel-L2 <= 1e-5 and max-abs <= 1e-4 * max|ref| (the layer's stat
 tolerance; stage outputs are held to the same bar)."""
 from __future__ import annotations
 
+import copy
 import dataclasses
 import sys
 
@@ -361,6 +362,63 @@ def test_k3_layer_T256_both_expert_forms(k3, expert_path, mode):
     compare_layer(k3, x, what=f"K3 T=256 form {mode}")
 
 
+# ------------------------------------------------------------------ top-p tail drop
+def with_topp(h: Host, p: float) -> Host:
+    """The same uploaded layer with the top-p tail drop set in its dims."""
+    v = copy.copy(h)
+    v.dims = dataclasses.replace(h.dims, topp=p)
+    return v
+
+
+def compare_topp(h: Host, p: float, T: int, seed: int, what: str):
+    v = with_topp(h, p)
+    x, _ = _inputs.gap_fixed_x(v.dims, seed, T, v.dense["w_router"], v.dense["bias"])
+    compare_layer(v, x, what=what)
+    ids = run_layer(v, x)[1]
+    say(f"  {what}: kept {np.mean(np.sum(ids >= 0, axis=1)):.2f} of {v.dims.topk} experts per token")
+    return ids
+
+
+@pytest.mark.parametrize("p", [0.5, 0.8])
+@pytest.mark.parametrize("T", [1, 3, 64, 300])
+def test_tiny_topp_layer(tiny, p, T):
+    ids = compare_topp(tiny, p, T, 20 + T, f"tiny top-p {p} T={T}")
+    if T >= 64:
+        assert (ids < 0).any()
+
+
+@pytest.mark.parametrize("mode", ["gemv", "gemm"])
+@pytest.mark.parametrize("T", [5, 300])
+def test_tiny_mm_topp_both_expert_forms(tiny_mm, expert_path, mode, T):
+    expert_path(k3moe.EXPERT_PATH_GEMV if mode == "gemv" else k3moe.EXPERT_PATH_GEMM)
+    ids = compare_topp(tiny_mm, 0.7, T, 30 + T, f"tiny-mm top-p 0.7 T={T} {mode}")
+    assert (ids < 0).any()
+
+
+def test_tiny_topp_route_and_dispatch(tiny):
+    # k3moe_route alone writes -1 in place; k3moe_dispatch drops those slots as the oracle does
+    v = with_topp(tiny, 0.6)
+    d, T = v.dims, 37
+    x, _ = _inputs.gap_fixed_x(d, 9, T, v.dense["w_router"], v.dense["bias"])
+    ws = device.workspace(d, T)
+    idx = torch.empty((T, d.topk), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, d.topk), dtype=torch.float32, device="cuda")
+    k3moe.k3moe_route(d, T, t_(x.view(np.int16)), v.dev.w_router, v.dev.bias, idx, w, ws)
+    torch.cuda.synchronize()
+    ridx, rw, _ = oracle.route_batch(d, x, v.dense["w_router"], v.dense["bias"])
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    check_rows(w.cpu().numpy(), rw, "tiny top-p route weights", rel=1e-6, absf=1e-6)
+    check_dispatch_of(v, ridx, "tiny top-p dispatch")
+
+
+def test_k3_topp_layer_T1(k3):
+    compare_topp(k3, 0.9, 1, 1, "K3 top-p 0.9 T=1")
+
+
+def test_k3_topp_layer_T64(k3):
+    compare_topp(k3, 0.8, 64, 2, "K3 top-p 0.8 T=64")
+
+
 # ------------------------------------------------------------------ shared experts
 def run_shared(d, n_shared, x: np.ndarray, shd: dict, y0: np.ndarray):
     T = x.shape[0]
@@ -469,8 +527,9 @@ def check_dispatch_of(h: Host, ids: np.ndarray, what: str):
     k3moe.k3moe_dispatch(d, T, t_(ids), off, sp, ps, ws)
     torch.cuda.synchronize()
     o, s_, p = oracle.dispatch(ids, d.n_experts)
+    n = int(o[-1])  # positions past the dispatched pairs (dropped slots) are unspecified
     assert np.array_equal(off.cpu().numpy(), o), what
-    assert np.array_equal(sp.cpu().numpy(), s_), what
+    assert np.array_equal(sp.cpu().numpy()[:n], s_[:n]), what
     assert np.array_equal(ps.cpu().numpy(), p), what
     return o
 
