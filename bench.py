@@ -221,6 +221,9 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=3)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--topp", type=float, default=0.9,
+                    help="also time decode with the top-p tail drop at this p (0 = skip); an approximation, "
+                         "reported beside the exact layer, never as the headline")
     ap.add_argument("--no-shared", action="store_true",
                     help="skip the shared-expert measurement (a call of its own, after the layer)")
     ap.add_argument("--cpu-tokens", type=int, default=64)
@@ -382,6 +385,33 @@ def main():
         del wsp, yp, xp
         torch.cuda.empty_cache()
 
+    # ---------------------------------------------------------------- top-p tail drop, T = 1
+    topp = None
+    if args.topp > 0:
+        import dataclasses
+        dp = dataclasses.replace(dims, topp=args.topp)
+
+        def step_p(i):
+            j = i % pool
+            k3moe.k3moe_layer(dp, T, xs.data_ptr() + j * row, wts_rot[i % len(wts_rot)], y, idx[j], tw[j], ws,
+                              stream=stream)
+
+        for i in range(args.warmup):
+            step_p(i)
+        torch.cuda.synchronize()
+        evt = HipEvents(2)
+        hip_record(evt.ev[0], stream.cuda_stream)
+        for i in range(args.steps):
+            step_p(i)
+        hip_record(evt.ev[1], stream.cuda_stream)
+        torch.cuda.synchronize()
+        ms_p = evt.ms(evt.ev[0], evt.ev[1]) / args.steps
+        evt.close()
+        kept = (idx[:min(pool, args.steps)] >= 0).sum(dim=1).float().mean().item()
+        topp = {"p": args.topp, "us_per_step": round(ms_p * 1e3, 2), "tokens_per_s": round(1.0 / (ms_p * 1e-3), 1),
+                "mean_experts_kept": round(kept, 2), "kind": "approximation (top-p tail drop), not the headline"}
+        log(f"decode T=1 with top-p {args.topp}: {ms_p * 1e3:.1f} us/step, {kept:.2f} experts kept on average")
+
     # ---------------------------------------------------------------- shared experts
     shared = None
     if not args.no_shared:
@@ -423,6 +453,7 @@ def main():
         "roofline": roofline,
         "prefill": prefill,
         "shared_experts": shared,
+        "topp_decode": topp,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
