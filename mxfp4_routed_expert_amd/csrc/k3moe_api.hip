@@ -348,10 +348,10 @@ int run_front(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_wei
     g.K = d->latent;
     g.gather = 1;
     g.tk = tk;
-    // (the selection at the head of the gate/up pass has no top-p tail drop)
-    if (route && !(d->topp > 0.f) && !use_mm(d, T, d->latent, (int64_t)T * d->latent * 4, wt->ex.w1, wt->ex.w3) &&
+    if (route && !use_mm(d, T, d->latent, (int64_t)T * d->latent * 4, wt->ex.w1, wt->ex.w3) &&
         route_in_gateup_ok(g)) {
       *route = tk;
+      route->positional = 1;  // the passes take slot j as pair j, dropped slots included
       *zq_ready = false;
       return K3MOE_OK;
     }
@@ -779,8 +779,10 @@ int k3moe_layer(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_w
   bool zq_ready = false;
   TopkArgs route = {};
   K3_TRY(run_front(d, T, x, wt, idx, tw, w, &zq_ready, &route, s));
-  // a one-token batch's pairs are its K slots in order, unless the top-p rule dropped some
-  const bool one_token = T == 1 && !(d->topp > 0.f);
+  // a one-token batch's pairs are its K slots in order: always when the gate/up pass
+  // selected the experts itself (a slot the top-p rule dropped is then marked in active[]),
+  // else unless the top-p rule compacted the dispatch
+  const bool one_token = T == 1 && (route.T != 0 || !(d->topp > 0.f));
   K3_TRY(run_experts(d, T, w.z32, zq_ready, route.T ? &route : nullptr, one_token, &wt->ex, w.expert_off,
                      w.sorted_pair, w.active, w.counters, w.edn, w, s));
   return run_combine(d, T, w.edn, w.pair_slot, tw, wt->norm_w, wt->w_up, y, one_token, w, s);

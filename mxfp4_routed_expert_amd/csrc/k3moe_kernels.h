@@ -120,7 +120,8 @@ struct TopkArgs {
   int L;
   uint8_t *zq;
   int32_t *expert_off, *sorted_pair, *pair_slot, *active, *counters;
-  float topp;  // > 0: the top-p tail drop (topk_select_wave with TP)
+  float topp;      // > 0: the top-p tail drop (topk_select_wave with TP)
+  int positional;  // with topp: a one-token dispatch that keeps slot j as pair j (topp_write)
 };
 
 struct GroupedArgs {
@@ -134,7 +135,9 @@ struct GroupedArgs {
   float b1, b2;
   TopkArgs tk;            // routed in the launch (one token): its selection and its z
   int one_token;          // a one-token layer batch: slot j is the only pair of expert
-                          // active[j] (the offsets and the active count are not read)
+                          // active[j] (the offsets and the active count are not read);
+                          // active[j] = -1: slot j was dropped (top-p), its output row
+                          // is written as zeros
 };
 
 // Grouped GEMM form of the same two passes (many tokens per expert); K % 128 == 0.

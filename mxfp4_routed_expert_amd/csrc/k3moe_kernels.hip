@@ -551,7 +551,7 @@ __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
       float sc[16];
       bool real[16];
       topk_keys_wave<16, 2>(a.tk, 0, key, sc, real);
-      topk_select_wave<16>(a.tk, 0, key, sc, real, s_scr, blockIdx.x == 0 && j == 0, j, &s_e);
+      topk_select_wave<16, true>(a.tk, 0, key, sc, real, s_scr, blockIdx.x == 0 && j == 0, j, &s_e);
     } else if (wave >= 2) {
       const int gz = (int)threadIdx.x - 128;
       if (gz < a.K / 32) {
@@ -566,11 +566,21 @@ __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
       }
     }
     __syncthreads();
-    e = __builtin_amdgcn_readfirstlane(min(max(s_e, 0), a.tk.E - 1));
+    if (s_e < 0) return;  // a slot the top-p rule dropped: no work (the whole block)
+    e = __builtin_amdgcn_readfirstlane(min(s_e, a.tk.E - 1));
     lo = j;
     hi = j + 1;
   } else if (a.one_token) {
     e = __builtin_amdgcn_readfirstlane(a.active[j]);
+    if (e < 0) {
+      // a dropped slot (top-p): its output row reads as zero in the weighted sum
+      if constexpr (EPI == kEpiEdn) {
+        const int r0 = blockIdx.x * 16 * RB;
+        for (int r = (int)threadIdx.x; r < 16 * RB && r0 + r < a.M; r += blockDim.x)
+          a.out[(size_t)j * a.M + r0 + r] = 0.f;
+      }
+      return;
+    }
     lo = j;
     hi = j + 1;
   } else {

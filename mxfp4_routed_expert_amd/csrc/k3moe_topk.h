@@ -54,14 +54,13 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// The top-p tail drop and the writes of one token's selection (topk_select_wave with TP):
-// lanes with sel hold chosen expert ce at ascending-id position pos with unbiased score
-// scc; ssum is the chosen total. Words 320 .. 383 of s_scr hold the fractions and ids,
-// 384 .. 415 the kept ids for the one-token dispatch.
-template <int S>
-__device__ __forceinline__ void topk_topp_write(const TopkArgs &a, int t, bool sel, int pos, int ce, float scc,
-                                             float ssum, uint32_t *s_scr, const bool (&real)[S]) {
-  const int E = a.E, K = a.K, lane = threadIdx.x & 63;
+// The top-p tail drop of one token's selection: lanes with sel hold chosen expert ce at
+// ascending-id position pos with unbiased score scc; ssum is the chosen total. Returns
+// whether this lane's expert is kept; *ksum receives the kept total. Words 320 .. 383 of
+// s_scr hold the fractions and ids.
+__device__ __forceinline__ bool topp_keep(const TopkArgs &a, bool sel, int pos, int ce, float scc, float ssum,
+                                          uint32_t *s_scr, float *ksum) {
+  const int K = a.K;
   const float f = sel ? scc / ssum : 0.f;
   if (sel) {
     s_scr[320 + pos] = __float_as_uint(f);
@@ -80,7 +79,20 @@ __device__ __forceinline__ void topk_topp_write(const TopkArgs &a, int t, bool s
   float before = 0.f;  // the fractions of the larger ones, summed largest first
   for (int r = 0; r < rank; ++r) before = before + __uint_as_float(s_scr[320 + r]);
   const bool keep = sel && before < a.topp;
-  const float ksum = wave_sum_fixed(keep ? scc : 0.f);
+  *ksum = wave_sum_fixed(keep ? scc : 0.f);
+  return keep;
+}
+
+// The writes of a selection with the top-p tail drop: ids (-1 where dropped) and
+// renormalised weights, and with a.expert_off the one-token dispatch. Compact (the
+// default): only the kept pairs are dispatched, in ascending expert order. Positional
+// (a.positional, for a one-token batch whose passes take slot j as pair j): every slot
+// stays pair j, and active[j] is its expert or -1 where dropped. Words 384 .. 415 of
+// s_scr hold the kept ids.
+template <int S>
+__device__ __forceinline__ void topp_write(const TopkArgs &a, int t, bool sel, bool keep, int pos, int ce,
+                                           float scc, float ksum, uint32_t *s_scr, const bool (&real)[S]) {
+  const int E = a.E, K = a.K, lane = threadIdx.x & 63;
   if (sel) {
     a.idx[(size_t)t * K + pos] = keep ? ce : -1;
     a.w[(size_t)t * K + pos] = keep ? ((a.renorm && ksum > 0.f) ? scc / ksum : scc) * a.rscale : 0.f;
@@ -90,11 +102,19 @@ __device__ __forceinline__ void topk_topp_write(const TopkArgs &a, int t, bool s
   wave_lds_sync();
   int kpos = 0;  // place among the kept (ascending ids)
   for (int k = 0; k < K; ++k) kpos += (int)s_scr[384 + k] < ce ? 1 : 0;
-  if (keep) {
-    a.active[kpos] = ce;
-    a.sorted_pair[kpos] = pos;
+  if (a.positional) {
+    if (sel) {
+      a.active[pos] = keep ? ce : -1;
+      a.sorted_pair[pos] = pos;
+      a.pair_slot[pos] = pos;
+    }
+  } else {
+    if (keep) {
+      a.active[kpos] = ce;
+      a.sorted_pair[kpos] = pos;
+    }
+    if (sel) a.pair_slot[pos] = keep ? kpos : -1;
   }
-  if (sel) a.pair_slot[pos] = keep ? kpos : -1;
   // expert_off[e] = kept ids below e
 #pragma unroll
   for (int s = 0; s < S; ++s) {
@@ -124,12 +144,11 @@ __device__ __forceinline__ void topk_topp_write(const TopkArgs &a, int t, bool s
 // set, the dispatch of a one-token batch: its K pairs in ascending expert order are
 // the K slots themselves); with slot >= 0, *s_slot_e receives the chosen id at that
 // position, visible to the block after the caller's next barrier. s_scr: 448 words of
-// LDS scratch, 16-byte aligned. TP: apply a.topp's tail drop (when a.topp > 0) before
-// writing: the chosen are walked by their fraction of the chosen score total, larger
-// first (equal: lower id first), with an fp32 running sum from 0; one is kept while the
-// sum of those before it is below a.topp; a dropped slot writes id -1 and weight 0, the
-// kept weights are renormalised over the kept, and the one-token dispatch lists only
-// the kept pairs.
+// LDS scratch, 16-byte aligned. TP: apply a.topp's tail drop (when a.topp > 0): the
+// chosen are walked by their fraction of the chosen score total, larger first (equal:
+// lower id first), with an fp32 running sum from 0; one is kept while the sum of those
+// before it is below a.topp; *s_slot_e is -1 for a dropped slot, and the writes are
+// topp_write's.
 template <int S, bool TP = false>
 __device__ __forceinline__ void topk_select_wave(const TopkArgs &a, int t, const uint32_t (&key)[S],
                                                  const float (&sc)[S], const bool (&real)[S], uint32_t *s_scr,
@@ -245,14 +264,17 @@ __device__ __forceinline__ void topk_select_wave(const TopkArgs &a, int t, const
     scc = sel ? __uint_as_float(s_scr[256 + lane]) : 0.f;
   }
   const float ssum = wave_sum_fixed(scc);
-  if (slot >= 0 && sel && pos == slot) *s_slot_e = ce;
-  if (!out) return;
   if constexpr (TP) {
     if (a.topp > 0.f) {
-      topk_topp_write(a, t, sel, pos, ce, scc, ssum, s_scr, real);
+      float ksum;
+      const bool keep = topp_keep(a, sel, pos, ce, scc, ssum, s_scr, &ksum);
+      if (slot >= 0 && sel && pos == slot) *s_slot_e = keep ? ce : -1;
+      if (out) topp_write<S>(a, t, sel, keep, pos, ce, scc, ksum, s_scr, real);
       return;
     }
   }
+  if (slot >= 0 && sel && pos == slot) *s_slot_e = ce;
+  if (!out) return;
   if (sel && pos < K) {
     a.idx[(size_t)t * K + pos] = ce;
     a.w[(size_t)t * K + pos] = ((a.renorm && ssum > 0.f) ? scc / ssum : scc) * a.rscale;
