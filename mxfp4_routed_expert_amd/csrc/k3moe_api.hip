@@ -73,6 +73,7 @@ struct Ws {
   uint16_t *np[3];             // [T][L] pieces of gamma * acc
   float *ss;                   // [T][ceil(L/256)] partial sums of acc^2
   uint16_t *wr_planes;         // [3][E][H] bf16 pieces of the router weights (GEMM form)
+  float *up_parts;             // [ks][T][H] K parts of the up-projection (GEMM form, small batches)
   size_t bytes;
 };
 
@@ -81,12 +82,18 @@ int g_expert_path = 0;  // k3moe_set_expert_path
 
 // The GEMM form reads its token planes through one 32-bit buffer descriptor: x [T][H]
 // bf16, and the three planes of gamma*acc [T][L] (each padded to 256 bytes).
-bool use_dense_mm(const k3moe_dims *d, int32_t T) {
-  if (T < kDenseMmMinT) return false;
+bool dense_mm_fits(const k3moe_dims *d, int32_t T) {
   const int64_t x_bytes = (int64_t)T * d->hidden * 2;
   const int64_t np_bytes = 3 * (((int64_t)T * d->latent * 2 + 255) & ~(int64_t)255);
   return x_bytes < ((int64_t)1 << 31) && np_bytes < ((int64_t)1 << 31);
 }
+
+bool use_dense_mm(const k3moe_dims *d, int32_t T) { return T >= kDenseMmMinT && dense_mm_fits(d, T); }
+
+// The up-projection runs as a GEMM from this many tokens on (its K split among blocks
+// below about 512 tiles): measured faster than the GEMV form from 8 tokens.
+constexpr int kUpMmMinT = 8;
+bool use_up_mm(const k3moe_dims *d, int32_t T) { return T >= kUpMmMinT && dense_mm_fits(d, T); }
 
 int64_t max_mm_tiles(const k3moe_dims *d, int32_t T) {
   const int64_t P = (int64_t)T * d->topk;
@@ -134,6 +141,9 @@ Ws carve(const k3moe_dims *d, int32_t T, void *base) {
   for (int q = 0; q < 3; ++q) w.np[q] = (uint16_t *)take(t * L * 2);
   w.ss = (float *)take(t * ((L + 255) / 256) * 4);
   w.wr_planes = use_dense_mm(d, T) ? (uint16_t *)take(3 * E * (size_t)d->hidden * 2) : nullptr;
+  // sized for the largest K-part count of any batch up to T (nondecreasing in T)
+  w.up_parts = T >= 2 ? (float *)take((size_t)dense_mm_parts_max(d->hidden, d->latent, T) * (size_t)d->hidden * 4)
+                      : nullptr;
   w.bytes = o;
   return w;
 }
@@ -527,9 +537,8 @@ int run_combine(const k3moe_dims *d, int32_t T, const float *edn, const int32_t 
   K3_HIP(launch_combine(edn, pair_slot, topk_w, norm_w, T, d->topk, d->latent, w.np[0], w.np[1],
                         w.np[2], w.ss, one_token && T == 1, s));
   mark("combine");
-  if (use_dense_mm(d, T)) {
+  if (use_up_mm(d, T)) {
     DenseMmArgs a = {};
-    a.seg[0] = DenseSeg{w_up, 0, d->hidden, y, d->hidden};
     a.nseg = 1;
     a.M = d->hidden;
     a.K = d->latent;
@@ -539,8 +548,20 @@ int run_combine(const k3moe_dims *d, int32_t T, const float *edn, const int32_t 
     a.ss = w.ss;
     a.nss = (d->latent + 255) / 256;
     a.eps = d->eps;
+    a.ks = dense_mm_ks(a.M, a.K, T);
     // two bf16 pieces (hi + lo) of the normed aggregate: the dropped third piece is
-    // below 2^-17 of each value
+    // below 2^-17 of each value. Each K part is scaled by the token's RMSNorm factor
+    // (linear), then the parts are summed into y in part order.
+    if (a.ks > 1) {
+      a.seg[0] = DenseSeg{w_up, 0, d->hidden, w.up_parts, d->hidden};
+      a.part_stride = (int64_t)T * d->hidden;
+      K3_HIP(launch_dense_mm(a, 2, kEpiStoreScaled, s));
+      mark("rmsnorm_up_gemv");
+      K3_HIP(launch_add_parts(w.up_parts, a.ks, a.part_stride, y, (int64_t)T * d->hidden, false, s));
+      mark("up_parts_sum");
+      return K3MOE_OK;
+    }
+    a.seg[0] = DenseSeg{w_up, 0, d->hidden, y, d->hidden};
     K3_HIP(launch_dense_mm(a, 2, kEpiStoreScaled, s));
   } else if (use_gemv1(d, T, nullptr)) {
     K3_HIP(launch_gemv1(up1_args(d, w_up, y, w), kA_BF16, kX_PLANES, kEpiStoreScaled, 2, s));
@@ -582,8 +603,9 @@ bool shared_gemv1(const k3moe_dims *d, int SI, int32_t T) { return T == 1 && d->
 
 struct ShWs {
   float *act;      // one token: [SI] SiTU-GLU output
-  float *gu;       // GEMM form: [T][2 SI] gate | up
+  float *gu;       // GEMM form: [ks][T][2 SI] gate | up (the K parts of the product)
   uint16_t *p[2];  // GEMM form: [T][SI] bf16 pieces of the SiTU-GLU output
+  float *dn;       // GEMM form with K parts: [ks][T][H] the down product's parts
   size_t bytes;
 };
 
@@ -600,11 +622,15 @@ ShWs carve_shared(const k3moe_dims *d, int SI, int32_t T, void *base) {
   if (T <= 1) {
     w.act = (float *)take(si * 4);
   } else {
-    w.gu = (float *)take(t * 2 * si * 4);
+    // sized for the largest K-part count any batch up to T uses, so that a workspace
+    // for a larger T serves a smaller one
+    const int H = d->hidden;
+    w.gu = (float *)take((size_t)dense_mm_parts_max(2 * SI, H, T) * 2 * si * 4);
     for (int q = 0; q < 2; ++q) w.p[q] = (uint16_t *)take(t * si * 2);
+    // (taken even where this T needs no parts: the size stays nondecreasing in T)
+    w.dn = (float *)take((size_t)dense_mm_parts_max(H, SI, T) * (size_t)H * 4);
   }
   w.bytes = o;
-  (void)d;
   return w;
 }
 
@@ -636,6 +662,9 @@ int run_shared(const k3moe_dims *d, int SI, int32_t T, const uint16_t *x, const 
     mark("shared_down_add");
     return K3MOE_OK;
   }
+  // Batches: both products as GEMMs; a batch too small to give the GEMM about 512 tiles (two
+  // blocks per compute unit)
+  // splits its K among blocks, whose parts the next step sums in part order.
   DenseMmArgs a = {};
   a.seg[0] = DenseSeg{sh1, 0, SI, w.gu, 2 * SI};
   a.seg[1] = DenseSeg{sh3, SI, SI, w.gu + SI, 2 * SI};
@@ -645,22 +674,34 @@ int run_shared(const k3moe_dims *d, int SI, int32_t T, const uint16_t *x, const 
   a.N = T;
   a.B = x;
   a.plane_elems = (int64_t)T * H;
+  a.ks = dense_mm_ks(a.M, a.K, T);
+  a.part_stride = (int64_t)T * 2 * SI;
   K3_HIP(launch_dense_mm(a, 1, kEpiStore, s));
   mark("shared_gate_up");
-  K3_HIP(launch_glu_pieces(w.gu, T, SI, d->b1, d->b2, w.p[0], w.p[1], s));
+  K3_HIP(launch_glu_pieces(w.gu, a.ks, a.part_stride, T, SI, d->b1, d->b2, w.p[0], w.p[1], s));
   mark("shared_situ");
   DenseMmArgs dn = {};
-  dn.seg[0] = DenseSeg{sh2, 0, H, y, H};
   dn.nseg = 1;
   dn.M = H;
   dn.K = SI;
   dn.N = T;
   dn.B = w.p[0];
   dn.plane_elems = (int64_t)(w.p[1] - w.p[0]);  // the two pieces are carved back to back
+  dn.ks = dense_mm_ks(H, SI, T);
   // two bf16 pieces (hi + lo) of each SiTU-GLU output: the dropped remainder is below
   // 2^-17 of the value
-  K3_HIP(launch_dense_mm(dn, 2, kEpiAdd, s));
-  mark("shared_down_add");
+  if (dn.ks > 1) {
+    dn.seg[0] = DenseSeg{sh2, 0, H, w.dn, H};
+    dn.part_stride = (int64_t)T * H;
+    K3_HIP(launch_dense_mm(dn, 2, kEpiStore, s));
+    mark("shared_down");
+    K3_HIP(launch_add_parts(w.dn, dn.ks, dn.part_stride, y, (int64_t)T * H, true, s));
+    mark("shared_add");
+  } else {
+    dn.seg[0] = DenseSeg{sh2, 0, H, y, H};
+    K3_HIP(launch_dense_mm(dn, 2, kEpiAdd, s));
+    mark("shared_down_add");
+  }
   return K3MOE_OK;
 }
 

@@ -59,14 +59,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rl = lane & 15, kq = lane >> 4;
 
-  // ---- tile: contiguous runs per XCD, 8 row blocks x every token block per group
+  // ---- tile: contiguous runs per XCD, 8 row blocks x every token block per group; the
+  // K parts of a tile are consecutive
   const int nM = (a.M + 255) / 256, nN = (a.N + BN - 1) / BN;
-  const int total = nM * nN;
+  const int ks = a.ks > 1 ? a.ks : 1;
+  const int total = nM * nN * ks;
   const int chunk = (total + 7) >> 3;
   const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
   if (idx >= chunk) return;
-  const int t = xcd * chunk + idx;
-  if (t >= total) return;
+  const int tk = xcd * chunk + idx;
+  if (tk >= total) return;
+  const int t = __builtin_amdgcn_readfirstlane(tk / ks);
+  const int kp = tk - t * ks;
   // integer division runs on the vector unit: pin the results to scalar registers
   const int grp = __builtin_amdgcn_readfirstlane(t / (8 * nN));
   const int in = t - grp * 8 * nN;
@@ -88,7 +92,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const uint32_t rowb = (uint32_t)a.K * 2u;
   const rsrc_t rA = make_rsrc(seg.A + (size_t)lr0 * a.K, (uint32_t)max(nrows, 0) * rowb);
   const rsrc_t rB = make_rsrc(a.B, (uint32_t)(PB * a.plane_elems * 2));
-  const int nsteps = a.K / 32;
+  // this K part's steps s_lo .. s_lo + nsteps - 1
+  const int spp = (a.K / 32 + ks - 1) / ks;
+  const int s_lo = kp * spp;
+  const int nsteps = max(0, min(a.K / 32 - s_lo, spp));
 
   uint32_t aoff[4];
 #pragma unroll
@@ -107,13 +114,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     u32x4 v[4];
   };
   auto aload = [&](int S, AStep &s) {
-    const uint32_t so = S < nsteps ? (uint32_t)S * 64u : kOOB;
+    const uint32_t so = S < nsteps ? (uint32_t)(s_lo + S) * 64u : kOOB;
 #pragma unroll
     for (int i = 0; i < 4; ++i) s.v[i] = bload16(rA, aoff[i], so);
   };
   auto issue = [&](int S, int st) {
     uint8_t *base = smem + st * STAGE;
-    const uint32_t so = S < nsteps ? (uint32_t)S * 64u : kOOB;
+    const uint32_t so = S < nsteps ? (uint32_t)(s_lo + S) * 64u : kOOB;
 #pragma unroll
     for (int u = 0; u < DMA_PER_WAVE; ++u) dma16(rB, base + (wave + 4 * u) * 1024, boff[u], so);
   };
@@ -175,7 +182,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // ---- epilogue: lane holds rows 16i + 4kq .. +3 of token 16j + l % 16
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the ring's trailing copies have landed
   if (!wave_on) return;
-  float *out = seg.out + lr0;
+  float *out = seg.out + lr0 + (size_t)kp * a.part_stride;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int n = n0 + 16 * j + rl;
@@ -194,9 +201,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
+#ifndef K3_DM_TARGET
+#define K3_DM_TARGET 512
+#endif
+
+int dense_mm_ks(int M, int K, int N) {
+  const int tiles = ((M + 255) / 256) * ((N + 127) / 128);
+  const int ks = (K3_DM_TARGET + tiles - 1) / tiles;
+  const int cap = K / 32 / 8;
+  return max(1, min(ks, cap));
+}
+
+int64_t dense_mm_parts_max(int M, int K, int N) {
+  // ks depends on N only through its 128-token blocks: within a block count, the
+  // largest N' gives the largest product
+  int64_t best = 0;
+  for (int64_t n = 128; n - 128 < N; n += 128) {
+    const int Nn = (int)(n < N ? n : (int64_t)N);
+    best = max(best, (int64_t)dense_mm_ks(M, K, Nn) * Nn);
+  }
+  return best;
+}
+
 hipError_t launch_dense_mm(const DenseMmArgs &a, int pieces, int epi, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if (a.K % 32 != 0 || a.nseg < 1 || a.nseg > kDmMaxSegs) return hipErrorInvalidValue;
+  const int ks = a.ks > 1 ? a.ks : 1;
+  if (ks > 1 && (epi == kEpiAdd || ks > a.K / 32)) return hipErrorInvalidValue;
   if (epi == kEpiStoreScaled && (a.nss < 1 || a.nss > kMaxNormParts)) return hipErrorInvalidValue;
   if ((int64_t)pieces * a.plane_elems * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   for (int i = 0; i < a.nseg; ++i)
@@ -204,22 +235,27 @@ hipError_t launch_dense_mm(const DenseMmArgs &a, int pieces, int epi, hipStream_
       return hipErrorInvalidValue;
   if (pieces == 1 && epi == kEpiStore) {
     constexpr int NJ = 8;
-    const int64_t total = (int64_t)((a.M + 255) / 256) * ((a.N + 16 * NJ - 1) / (16 * NJ));
+    const int64_t total = (int64_t)((a.M + 255) / 256) * ((a.N + 16 * NJ - 1) / (16 * NJ)) * ks;
     launch_kernel(k_dense_mm<1, NJ, kEpiStore>, (unsigned)(8 * ((total + 7) / 8)), 256,
                   kDmStages * NJ * 1024 + 64 * NJ, s, a);
   } else if (pieces == 2 && epi == kEpiStoreScaled) {
     constexpr int NJ = 8;
-    const int64_t total = (int64_t)((a.M + 255) / 256) * ((a.N + 16 * NJ - 1) / (16 * NJ));
+    const int64_t total = (int64_t)((a.M + 255) / 256) * ((a.N + 16 * NJ - 1) / (16 * NJ)) * ks;
     launch_kernel(k_dense_mm<2, NJ, kEpiStoreScaled>, (unsigned)(8 * ((total + 7) / 8)), 256,
+                  kDmStages * 2 * NJ * 1024 + 64 * NJ, s, a);
+  } else if (pieces == 2 && epi == kEpiStore) {
+    constexpr int NJ = 8;
+    const int64_t total = (int64_t)((a.M + 255) / 256) * ((a.N + 16 * NJ - 1) / (16 * NJ)) * ks;
+    launch_kernel(k_dense_mm<2, NJ, kEpiStore>, (unsigned)(8 * ((total + 7) / 8)), 256,
                   kDmStages * 2 * NJ * 1024 + 64 * NJ, s, a);
   } else if (pieces == 2 && epi == kEpiAdd) {
     constexpr int NJ = 8;
-    const int64_t total = (int64_t)((a.M + 255) / 256) * ((a.N + 16 * NJ - 1) / (16 * NJ));
+    const int64_t total = (int64_t)((a.M + 255) / 256) * ((a.N + 16 * NJ - 1) / (16 * NJ)) * ks;
     launch_kernel(k_dense_mm<2, NJ, kEpiAdd>, (unsigned)(8 * ((total + 7) / 8)), 256,
                   kDmStages * 2 * NJ * 1024 + 64 * NJ, s, a);
   } else if (pieces == 3 && epi == kEpiStoreScaled) {
     constexpr int NJ = 4;
-    const int64_t total = (int64_t)((a.M + 255) / 256) * ((a.N + 16 * NJ - 1) / (16 * NJ));
+    const int64_t total = (int64_t)((a.M + 255) / 256) * ((a.N + 16 * NJ - 1) / (16 * NJ)) * ks;
     launch_kernel(k_dense_mm<3, NJ, kEpiStoreScaled>, (unsigned)(8 * ((total + 7) / 8)), 256,
                   kDmStages * 3 * NJ * 1024 + 64 * NJ, s, a);
   } else {

@@ -75,7 +75,14 @@ struct DenseMmArgs {
   const float *ss;      // kEpiStoreScaled: as DenseArgs
   int nss;
   float eps;
+  int ks;               // K parts (0 or 1: none): part p covers steps p*ceil(K/32/ks) .., and
+  int64_t part_stride;  //   writes its product at seg.out + p * part_stride (not with kEpiAdd)
 };
+// K parts that give a dense GEMM of M rows, K columns and N tokens about 512 tiles
+// (at least 8 steps of 32 columns per part); and the largest ks(N') * N' over N' <= N
+// (partial-product buffer sizes that grow with N).
+int dense_mm_ks(int M, int K, int N);
+int64_t dense_mm_parts_max(int M, int K, int N);
 
 // One token's dense product on the vector ALUs: out = A x, A [M][K] (bf16 or fp32),
 // x [K] as bf16 (kX_BF16), as three bf16 planes summing to the fp32 value (kX_PLANES) or
@@ -163,7 +170,7 @@ struct MmArgs {
 // ---------------------------------------------------------------- launchers
 hipError_t launch_route_down(const DenseArgs &router, int ks, const DenseArgs *down, hipStream_t s);
 hipError_t launch_dense_bf16(const DenseArgs &a, int pieces, int epi, hipStream_t s);
-// pieces 1 with kEpiStore, 2 or 3 with kEpiStoreScaled, 2 with kEpiAdd
+// pieces 1 or 2 with kEpiStore, 2 or 3 with kEpiStoreScaled, 2 with kEpiAdd (ks <= 1)
 hipError_t launch_dense_mm(const DenseMmArgs &a, int pieces, int epi, hipStream_t s);
 // Router top-k of T tokens from ks partial logit arrays [ks][T][E]. Optional: z [T][L]
 // fp32 quantized into zq piece records meanwhile; for T == 1, expert_off .. counters
@@ -190,8 +197,14 @@ hipError_t launch_split_planes(const float *src, size_t n, uint16_t *p0, uint16_
 // act = SiTU-GLU(g, u) for gu [T][2 * SI] (g in columns 0 .. SI-1, u in SI .. 2 SI-1),
 // written as two bf16 pieces p0, p1 [T][SI] whose sum is act to 16 significant bits;
 // SI % 8 == 0
-hipError_t launch_glu_pieces(const float *gu, int T, int SI, float b1, float b2, uint16_t *p0,
-                             uint16_t *p1, hipStream_t s);
+// gu may hold ks K-part products of the gate|up GEMM, part p at gu + p * part_stride:
+// g and u are their sums (in part order).
+hipError_t launch_glu_pieces(const float *gu, int ks, int64_t part_stride, int T, int SI, float b1, float b2,
+                             uint16_t *p0, uint16_t *p1, hipStream_t s);
+// y[i] (+)= sum over p < ks of parts[p * stride + i] (in part order), i < n; n % 4 == 0;
+// accumulate: add to y, else overwrite it
+hipError_t launch_add_parts(const float *parts, int ks, int64_t stride, float *y, int64_t n, bool accumulate,
+                            hipStream_t s);
 // tokens_per_tile: 1, 2 or 4 tokens' piece records staged in LDS per tile (grouped_dec_lds bytes)
 constexpr size_t kMaxBlockLds = 81920;  // two blocks per compute unit
 // rb: 16-row blocks per block (4, 6 or 8 for kEpiSitu; 4 to 8 for kEpiEdn), from grouped_dec_rb

@@ -424,21 +424,30 @@ hipError_t launch_split_planes(const float *src, size_t n, uint16_t *p0, uint16_
 
 // ============================================================== shared-expert activation
 // Thread q: token t = q / (SI/8), columns 8c .. 8c+7 of it: reads g and u (two 32-byte
-// loads each), writes act's two bf16 pieces (one 16-byte store each).
-__global__ __launch_bounds__(256) void k_glu_pieces(const float *__restrict__ gu, int T, int SI, float b1,
-                                                    float b2, uint16_t *__restrict__ p0,
-                                                    uint16_t *__restrict__ p1) {
+// loads each, per K part, summed in part order), writes act's two bf16 pieces (one
+// 16-byte store each).
+__global__ __launch_bounds__(256) void k_glu_pieces(const float *__restrict__ gu, int ks, int64_t part_stride,
+                                                    int T, int SI, float b1, float b2,
+                                                    uint16_t *__restrict__ p0, uint16_t *__restrict__ p1) {
   const int cpt = SI / 8;
   const int64_t n = (int64_t)T * cpt;
   for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < n; q += (int64_t)gridDim.x * blockDim.x) {
     const int64_t t = q / cpt;
     const int c = (int)(q - t * cpt);
-    const float *g = gu + t * 2 * SI + 8 * c;
-    const float *u = g + SI;
-    const float4 g0 = *(const float4 *)g, g1 = *(const float4 *)(g + 4);
-    const float4 u0 = *(const float4 *)u, u1 = *(const float4 *)(u + 4);
-    const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-    const float uv[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+    float gv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, uv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < ks; ++p) {
+      const float *g = gu + p * part_stride + t * 2 * SI + 8 * c;
+      const float *u = g + SI;
+      const float4 g0 = *(const float4 *)g, g1 = *(const float4 *)(g + 4);
+      const float4 u0 = *(const float4 *)u, u1 = *(const float4 *)(u + 4);
+      const float gp[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+      const float up[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        gv[i] += gp[i];
+        uv[i] += up[i];
+      }
+    }
     float a[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) a[i] = situ(gv[i], uv[i], b1, b2);
@@ -449,13 +458,45 @@ __global__ __launch_bounds__(256) void k_glu_pieces(const float *__restrict__ gu
   }
 }
 
-hipError_t launch_glu_pieces(const float *gu, int T, int SI, float b1, float b2, uint16_t *p0,
-                             uint16_t *p1, hipStream_t s) {
+hipError_t launch_glu_pieces(const float *gu, int ks, int64_t part_stride, int T, int SI, float b1, float b2,
+                             uint16_t *p0, uint16_t *p1, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  if (SI <= 0 || SI % 8 != 0) return hipErrorInvalidValue;
+  if (SI <= 0 || SI % 8 != 0 || ks < 1 || (ks > 1 && part_stride < (int64_t)T * 2 * SI)) return hipErrorInvalidValue;
   int64_t blocks = ((int64_t)T * (SI / 8) + 255) / 256;
   if (blocks > 16384) blocks = 16384;
-  launch_kernel(k_glu_pieces, (unsigned)blocks, 256, 0, s, gu, T, SI, b1, b2, p0, p1);
+  launch_kernel(k_glu_pieces, (unsigned)blocks, 256, 0, s, gu, ks, part_stride, T, SI, b1, b2, p0, p1);
+  return hipGetLastError();
+}
+
+// y (+)= the sum of the K parts of a product, four values per thread
+template <bool ACC>
+__global__ __launch_bounds__(256) void k_add_parts(const float *__restrict__ parts, int ks, int64_t stride,
+                                                   float *__restrict__ y, int64_t n4) {
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < n4; q += (int64_t)gridDim.x * blockDim.x) {
+    float4 v = *(const float4 *)(parts + 4 * q);
+    for (int p = 1; p < ks; ++p) {
+      const float4 w = *(const float4 *)(parts + p * stride + 4 * q);
+      v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+    }
+    if constexpr (ACC) {
+      float4 o = *(float4 *)(y + 4 * q);
+      o.x = o.x + v.x; o.y = o.y + v.y; o.z = o.z + v.z; o.w = o.w + v.w;
+      v = o;
+    }
+    *(float4 *)(y + 4 * q) = v;
+  }
+}
+
+hipError_t launch_add_parts(const float *parts, int ks, int64_t stride, float *y, int64_t n, bool accumulate,
+                            hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (ks < 1 || n % 4 != 0 || (ks > 1 && stride < n)) return hipErrorInvalidValue;
+  int64_t blocks = (n / 4 + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  if (accumulate)
+    launch_kernel(k_add_parts<true>, (unsigned)blocks, 256, 0, s, parts, ks, stride, y, n / 4);
+  else
+    launch_kernel(k_add_parts<false>, (unsigned)blocks, 256, 0, s, parts, ks, stride, y, n / 4);
   return hipGetLastError();
 }
 

@@ -130,3 +130,14 @@ def test_expert_path_switch_host_only():
         assert k3moe.k3moe_set_expert_path(k3moe.EXPERT_PATH_AUTO) == k3moe.EXPERT_PATH_GEMV
     finally:
         k3moe.k3moe_set_expert_path(prev)
+
+
+def test_shared_workspace_size_grows_with_T():
+    # a workspace sized for a batch serves every smaller batch
+    lib = k3moe
+    for d in (k3gen.K3, k3gen.TINY):
+        prev = 0
+        for T in list(range(0, 300)) + list(range(300, 5000, 7)):
+            n = lib.k3moe_shared_workspace_size(d, 2, T)
+            assert n >= prev, (d, T)
+            prev = n

@@ -218,6 +218,22 @@ def test_tiny_mm_stages_gemm(tiny_mm, expert_path):
     stages(tiny_mm, x)
 
 
+# a shape whose up-projection (1024 x 1024) splits its K among blocks from 8 tokens on
+MID_UP = dataclasses.replace(k3gen.TINY, hidden=1024, latent=1024, inter=256, n_experts=64)
+
+
+@pytest.fixture(scope="module")
+def mid_up():
+    return Host(MID_UP, 3)
+
+
+@pytest.mark.parametrize("T", [7, 8, 37, 128, 200])
+def test_layer_up_projection_split_k(mid_up, T):
+    say(f"mid shape layer T={T} (up-projection K parts)")
+    x, _ = _inputs.gap_fixed_x(mid_up.dims, 50 + T, T, mid_up.dense["w_router"], mid_up.dense["bias"])
+    compare_layer(mid_up, x, what=f"mid T={T}")
+
+
 def test_tiny_dispatch_chunked_and_invalid_ids(tiny):
     d = tiny.dims
     rng = np.random.default_rng(7)
@@ -388,11 +404,14 @@ def test_tiny_topp_layer(tiny, p, T):
 
 
 @pytest.mark.parametrize("mode", ["gemv", "gemm"])
-@pytest.mark.parametrize("T", [5, 300])
+@pytest.mark.parametrize("T", [1, 5, 300])
 def test_tiny_mm_topp_both_expert_forms(tiny_mm, expert_path, mode, T):
     expert_path(k3moe.EXPERT_PATH_GEMV if mode == "gemv" else k3moe.EXPERT_PATH_GEMM)
+    # T = 1: forced GEMV selects in the gate/up pass (positional dispatch), forced GEMM
+    # selects in its own launch (compacted dispatch)
     ids = compare_topp(tiny_mm, 0.7, T, 30 + T, f"tiny-mm top-p 0.7 T={T} {mode}")
-    assert (ids < 0).any()
+    if T > 1:
+        assert (ids < 0).any()
 
 
 def test_tiny_topp_route_and_dispatch(tiny):
@@ -449,6 +468,28 @@ def test_tiny_shared_experts(tiny_shared, n_shared, T):
     y0 = np.random.default_rng(T).standard_normal((T, d.hidden)).astype(np.float32)
     got = run_shared(d, n_shared, x, shd[n_shared], y0)
     check_rows(got, oracle.shared(d, x, sh[n_shared], y0, n_shared), f"shared n={n_shared} T={T} added")
+
+
+# a shape whose batches split both shared-expert products along K (gate/up 4 parts,
+# down 8 parts below 129 tokens)
+SHARED_SPLIT = dataclasses.replace(k3gen.TINY, hidden=1024, inter=1024)
+
+
+@pytest.fixture(scope="module")
+def split_shared():
+    d = SHARED_SPLIT
+    sh = k3gen.gen_shared(d, 8, 2)
+    return d, sh, device.upload_shared(sh)
+
+
+@pytest.mark.parametrize("T", [2, 37, 128, 129, 300])
+def test_shared_experts_split_k(split_shared, T):
+    d, sh, shd = split_shared
+    say(f"shared experts split-K shape T={T}")
+    x = k3gen.gen_x(d, 40 + T, T)
+    y0 = np.random.default_rng(T).standard_normal((T, d.hidden)).astype(np.float32)
+    got = run_shared(d, 2, x, shd, y0)
+    check_rows(got, oracle.shared(d, x, sh, y0, 2), f"shared split-K T={T}")
 
 
 def test_tiny_shared_host_checks(tiny_shared):
