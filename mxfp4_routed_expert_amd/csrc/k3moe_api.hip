@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "k3moe.h"
 #include "k3moe_prof.h"
 #include "k3moe_kernels.h"
@@ -74,6 +76,7 @@ struct Ws {
   float *ss;                   // [T][ceil(L/256)] partial sums of acc^2
   uint16_t *wr_planes;         // [3][E][H] bf16 pieces of the router weights (GEMM form)
   float *up_parts;             // [ks][T][H] K parts of the up-projection (GEMM form, small batches)
+  float *z_parts;              // [ks][T][L] K parts of the latent projection (GEMM form, small batches)
   size_t bytes;
 };
 
@@ -89,6 +92,20 @@ bool dense_mm_fits(const k3moe_dims *d, int32_t T) {
 }
 
 bool use_dense_mm(const k3moe_dims *d, int32_t T) { return T >= kDenseMmMinT && dense_mm_fits(d, T); }
+
+// The router and latent projection run as one GEMM (the router's fp32 weights split into
+// three bf16 planes per call) from this many tokens on, their K split among blocks below
+// about 512 tiles: measured faster than the GEMV forms from 40 tokens (71 against 80 us;
+// at 32 tokens 70 against 65 us).
+#ifndef K3_FRONT_MM_MIN_T
+#define K3_FRONT_MM_MIN_T 40
+#endif
+constexpr int kFrontMmMinT = K3_FRONT_MM_MIN_T;
+bool use_front_mm(const k3moe_dims *d, int32_t T) {
+  return T >= kFrontMmMinT && d->n_experts % 64 == 0 && dense_mm_fits(d, T);
+}
+// rows of the front GEMM: three router planes, then W_down
+int front_rows(const k3moe_dims *d) { return 3 * d->n_experts + d->latent; }
 
 // The up-projection runs as a GEMM from this many tokens on (its K split among blocks
 // below about 512 tiles): measured faster than the GEMV form from 8 tokens.
@@ -123,7 +140,10 @@ Ws carve(const k3moe_dims *d, int32_t T, void *base) {
   const size_t t = (size_t)T, E = (size_t)d->n_experts, L = (size_t)d->latent, I = (size_t)d->inter;
   const size_t P = t * (size_t)d->topk;
   const size_t nch = (t + 63) / 64;
-  w.router_part = (float *)take(kRouterSplits * t * E * 4);
+  // router partial logits: the GEMV forms' K parts, or the GEMM form's three planes times
+  // its K parts (sized for the largest count of any batch up to T)
+  const int64_t front_parts = T >= kFrontMmMinT ? dense_mm_parts_max(front_rows(d), d->hidden, T) : 0;
+  w.router_part = (float *)take((size_t)std::max<int64_t>(kRouterSplits * (int64_t)t, 3 * front_parts) * E * 4);
   w.z32 = (float *)take(t * L * 4);
   w.zq = (uint8_t *)take(t * L * 4);
   w.idx = (int32_t *)take(P * 4);
@@ -140,7 +160,8 @@ Ws carve(const k3moe_dims *d, int32_t T, void *base) {
   w.edn = (float *)take(P * L * 4);
   for (int q = 0; q < 3; ++q) w.np[q] = (uint16_t *)take(t * L * 2);
   w.ss = (float *)take(t * ((L + 255) / 256) * 4);
-  w.wr_planes = use_dense_mm(d, T) ? (uint16_t *)take(3 * E * (size_t)d->hidden * 2) : nullptr;
+  w.wr_planes = T >= kFrontMmMinT ? (uint16_t *)take(3 * E * (size_t)d->hidden * 2) : nullptr;
+  w.z_parts = T >= kFrontMmMinT ? (float *)take((size_t)front_parts * L * 4) : nullptr;
   // sized for the largest K-part count of any batch up to T (nondecreasing in T)
   w.up_parts = T >= 2 ? (float *)take((size_t)dense_mm_parts_max(d->hidden, d->latent, T) * (size_t)d->hidden * 4)
                       : nullptr;
@@ -184,28 +205,44 @@ void mark(const char *name) {
 // ---- step launchers (arguments already checked)
 
 // The router's three weight planes (row segments 0..2) and optionally W_down
-// (segment 3), all against x.
+// (segment 3), all against x. Returns the number of router partial-logit arrays left in
+// w.router_part for the top-k (3, one per plane; or 1 where K parts were summed).
 int run_route_down_mm(const k3moe_dims *d, int32_t T, const uint16_t *x, const float *wr,
-                      const uint16_t *wd, float *z, const Ws &w, hipStream_t s) {
+                      const uint16_t *wd, float *z, const Ws &w, int *parts, hipStream_t s) {
   const size_t EH = (size_t)d->n_experts * d->hidden;
   K3_HIP(launch_split_planes(wr, EH, w.wr_planes, w.wr_planes + EH, w.wr_planes + 2 * EH, s));
   mark("router_weight_split");
   DenseMmArgs a = {};
-  const int E = d->n_experts;
+  const int E = d->n_experts, L = d->latent;
+  // K parts (the count for the full front, with or without W_down, so that the part
+  // buffers are never smaller than the workspace assumed)
+  const int ks = dense_mm_ks(front_rows(d), d->hidden, T);
+  const int64_t rs = (int64_t)T * E, zs = (int64_t)T * L;
+  // plane p's K part k at router_part + (p * ks + k) * T * E
   for (int p = 0; p < 3; ++p)
-    a.seg[p] = DenseSeg{w.wr_planes + p * EH, p * E, E, w.router_part + (size_t)p * T * E, E};
+    a.seg[p] = DenseSeg{w.wr_planes + p * EH, p * E, E, w.router_part + (size_t)p * ks * rs, E, rs};
   a.nseg = 3;
   a.M = 3 * E;
   if (wd) {
-    a.seg[3] = DenseSeg{wd, 3 * E, d->latent, z, d->latent};
+    a.seg[3] = DenseSeg{wd, 3 * E, L, ks > 1 ? w.z_parts : z, L, zs};
     a.nseg = 4;
-    a.M += d->latent;
+    a.M += L;
   }
   a.K = d->hidden;
   a.N = T;
   a.B = x;
   a.plane_elems = (int64_t)T * d->hidden;
+  a.ks = ks;
   K3_HIP(launch_dense_mm(a, 1, kEpiStore, s));
+  *parts = 3;
+  if (ks > 1) {
+    mark("router_and_latent_down");
+    // the 3 * ks partial logits summed in place into the first (plane order, then part order)
+    K3_HIP(launch_add_parts(w.router_part, 3 * ks, rs, w.router_part, rs, false, s));
+    *parts = 1;
+    if (wd) K3_HIP(launch_add_parts(w.z_parts, ks, zs, z, zs, false, s));
+    mark("front_parts_sum");
+  }
   return K3MOE_OK;
 }
 
@@ -306,9 +343,8 @@ TopkArgs topk_args(const k3moe_dims *d, int32_t T, const float *part, int ks, co
 int run_route(const k3moe_dims *d, int32_t T, const uint16_t *x, const float *wr, const float *bias,
               int32_t *idx, float *wt, const Ws &w, hipStream_t s) {
   int splits = kRouterSplits;
-  if (use_dense_mm(d, T) && d->n_experts % 64 == 0) {
-    K3_TRY(run_route_down_mm(d, T, x, wr, nullptr, nullptr, w, s));
-    splits = 3;
+  if (use_front_mm(d, T)) {
+    K3_TRY(run_route_down_mm(d, T, x, wr, nullptr, nullptr, w, &splits, s));
   } else if (use_gemv1(d, T, x)) {
     K3_HIP(launch_gemv1(router1_args(d, x, wr, w), kA_F32, kX_BF16, kEpiStore, 1, s));
     splits = kRouterParts1;
@@ -329,12 +365,13 @@ int run_route(const k3moe_dims *d, int32_t T, const uint16_t *x, const float *wr
 int run_front(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_weights *wt, int32_t *idx,
               float *tw, const Ws &w, bool *zq_ready, TopkArgs *route, hipStream_t s) {
   const DenseArgs down = down_args(d, T, x, wt->w_down, w.z32);
-  if (use_dense_mm(d, T) && d->n_experts % 64 == 0) {
+  if (use_front_mm(d, T)) {
     // GEMM form: router planes and W_down in one launch, then the top-k, whose spare
     // waves quantize z
-    K3_TRY(run_route_down_mm(d, T, x, wt->w_router, wt->w_down, w.z32, w, s));
+    int parts = 3;
+    K3_TRY(run_route_down_mm(d, T, x, wt->w_router, wt->w_down, w.z32, w, &parts, s));
     mark("router_and_latent_down");
-    TopkArgs tk = topk_args(d, T, w.router_part, 3, wt->bias, idx, tw);
+    TopkArgs tk = topk_args(d, T, w.router_part, parts, wt->bias, idx, tw);
     tk.z = w.z32;
     tk.zq = w.zq;
     K3_HIP(launch_topk(tk, s));
@@ -553,11 +590,10 @@ int run_combine(const k3moe_dims *d, int32_t T, const float *edn, const int32_t 
     // below 2^-17 of each value. Each K part is scaled by the token's RMSNorm factor
     // (linear), then the parts are summed into y in part order.
     if (a.ks > 1) {
-      a.seg[0] = DenseSeg{w_up, 0, d->hidden, w.up_parts, d->hidden};
-      a.part_stride = (int64_t)T * d->hidden;
+      a.seg[0] = DenseSeg{w_up, 0, d->hidden, w.up_parts, d->hidden, (int64_t)T * d->hidden};
       K3_HIP(launch_dense_mm(a, 2, kEpiStoreScaled, s));
       mark("rmsnorm_up_gemv");
-      K3_HIP(launch_add_parts(w.up_parts, a.ks, a.part_stride, y, (int64_t)T * d->hidden, false, s));
+      K3_HIP(launch_add_parts(w.up_parts, a.ks, a.seg[0].pstride, y, (int64_t)T * d->hidden, false, s));
       mark("up_parts_sum");
       return K3MOE_OK;
     }
@@ -666,8 +702,9 @@ int run_shared(const k3moe_dims *d, int SI, int32_t T, const uint16_t *x, const 
   // blocks per compute unit)
   // splits its K among blocks, whose parts the next step sums in part order.
   DenseMmArgs a = {};
-  a.seg[0] = DenseSeg{sh1, 0, SI, w.gu, 2 * SI};
-  a.seg[1] = DenseSeg{sh3, SI, SI, w.gu + SI, 2 * SI};
+  const int64_t gu_stride = (int64_t)T * 2 * SI;  // between K parts
+  a.seg[0] = DenseSeg{sh1, 0, SI, w.gu, 2 * SI, gu_stride};
+  a.seg[1] = DenseSeg{sh3, SI, SI, w.gu + SI, 2 * SI, gu_stride};
   a.nseg = 2;
   a.M = 2 * SI;
   a.K = H;
@@ -675,10 +712,9 @@ int run_shared(const k3moe_dims *d, int SI, int32_t T, const uint16_t *x, const 
   a.B = x;
   a.plane_elems = (int64_t)T * H;
   a.ks = dense_mm_ks(a.M, a.K, T);
-  a.part_stride = (int64_t)T * 2 * SI;
   K3_HIP(launch_dense_mm(a, 1, kEpiStore, s));
   mark("shared_gate_up");
-  K3_HIP(launch_glu_pieces(w.gu, a.ks, a.part_stride, T, SI, d->b1, d->b2, w.p[0], w.p[1], s));
+  K3_HIP(launch_glu_pieces(w.gu, a.ks, gu_stride, T, SI, d->b1, d->b2, w.p[0], w.p[1], s));
   mark("shared_situ");
   DenseMmArgs dn = {};
   dn.nseg = 1;
@@ -691,11 +727,10 @@ int run_shared(const k3moe_dims *d, int SI, int32_t T, const uint16_t *x, const 
   // two bf16 pieces (hi + lo) of each SiTU-GLU output: the dropped remainder is below
   // 2^-17 of the value
   if (dn.ks > 1) {
-    dn.seg[0] = DenseSeg{sh2, 0, H, w.dn, H};
-    dn.part_stride = (int64_t)T * H;
+    dn.seg[0] = DenseSeg{sh2, 0, H, w.dn, H, (int64_t)T * H};
     K3_HIP(launch_dense_mm(dn, 2, kEpiStore, s));
     mark("shared_down");
-    K3_HIP(launch_add_parts(w.dn, dn.ks, dn.part_stride, y, (int64_t)T * H, true, s));
+    K3_HIP(launch_add_parts(w.dn, dn.ks, dn.seg[0].pstride, y, (int64_t)T * H, true, s));
     mark("shared_add");
   } else {
     dn.seg[0] = DenseSeg{sh2, 0, H, y, H};

@@ -25,7 +25,10 @@ namespace k3 {
 
 namespace {
 
-constexpr int kDmStages = 3;
+#ifndef K3_DM_STAGES
+#define K3_DM_STAGES 3
+#endif
+constexpr int kDmStages = K3_DM_STAGES;
 
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
@@ -182,7 +185,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // ---- epilogue: lane holds rows 16i + 4kq .. +3 of token 16j + l % 16
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the ring's trailing copies have landed
   if (!wave_on) return;
-  float *out = seg.out + lr0 + (size_t)kp * a.part_stride;
+  float *out = seg.out + lr0 + (size_t)kp * seg.pstride;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int n = n0 + 16 * j + rl;

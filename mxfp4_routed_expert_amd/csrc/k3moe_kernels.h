@@ -66,6 +66,7 @@ struct DenseSeg {
   int row0, rows;     // place in the concatenated row space
   float *out;         // out[n * ld + (row - row0)]
   int ld;
+  int64_t pstride;    // with K parts: part p's product at out + p * pstride
 };
 struct DenseMmArgs {
   DenseSeg seg[kDmMaxSegs];
@@ -75,8 +76,8 @@ struct DenseMmArgs {
   const float *ss;      // kEpiStoreScaled: as DenseArgs
   int nss;
   float eps;
-  int ks;               // K parts (0 or 1: none): part p covers steps p*ceil(K/32/ks) .., and
-  int64_t part_stride;  //   writes its product at seg.out + p * part_stride (not with kEpiAdd)
+  int ks;               // K parts (0 or 1: none): part p covers steps p*ceil(K/32/ks) .. and
+                        //   writes its product at seg.out + p * seg.pstride (not with kEpiAdd)
 };
 // K parts that give a dense GEMM of M rows, K columns and N tokens about 512 tiles
 // (at least 8 steps of 32 columns per part); and the largest ks(N') * N' over N' <= N
@@ -202,7 +203,7 @@ hipError_t launch_split_planes(const float *src, size_t n, uint16_t *p0, uint16_
 hipError_t launch_glu_pieces(const float *gu, int ks, int64_t part_stride, int T, int SI, float b1, float b2,
                              uint16_t *p0, uint16_t *p1, hipStream_t s);
 // y[i] (+)= sum over p < ks of parts[p * stride + i] (in part order), i < n; n % 4 == 0;
-// accumulate: add to y, else overwrite it
+// accumulate: add to y, else overwrite it (y may then be parts itself)
 hipError_t launch_add_parts(const float *parts, int ks, int64_t stride, float *y, int64_t n, bool accumulate,
                             hipStream_t s);
 // tokens_per_tile: 1, 2 or 4 tokens' piece records staged in LDS per tile (grouped_dec_lds bytes)

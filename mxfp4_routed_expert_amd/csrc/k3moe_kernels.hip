@@ -468,13 +468,25 @@ hipError_t launch_glu_pieces(const float *gu, int ks, int64_t part_stride, int T
   return hipGetLastError();
 }
 
-// y (+)= the sum of the K parts of a product, four values per thread
+// y (+)= the sum of the K parts of a product, four values per thread. y may be part 0
+// itself (each thread reads its values of every part before it writes them).
 template <bool ACC>
-__global__ __launch_bounds__(256) void k_add_parts(const float *__restrict__ parts, int ks, int64_t stride,
-                                                   float *__restrict__ y, int64_t n4) {
+__global__ __launch_bounds__(256) void k_add_parts(const float *parts, int ks, int64_t stride, float *y,
+                                                   int64_t n4) {
   for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < n4; q += (int64_t)gridDim.x * blockDim.x) {
     float4 v = *(const float4 *)(parts + 4 * q);
-    for (int p = 1; p < ks; ++p) {
+    int p = 1;
+    // eight parts' loads in flight at a time, added in part order
+    for (; p + 8 <= ks; p += 8) {
+      float4 w[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[i] = *(const float4 *)(parts + (p + i) * stride + 4 * q);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        v.x += w[i].x; v.y += w[i].y; v.z += w[i].z; v.w += w[i].w;
+      }
+    }
+    for (; p < ks; ++p) {
       const float4 w = *(const float4 *)(parts + p * stride + 4 * q);
       v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
     }

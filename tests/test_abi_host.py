@@ -141,3 +141,13 @@ def test_shared_workspace_size_grows_with_T():
             n = lib.k3moe_shared_workspace_size(d, 2, T)
             assert n >= prev, (d, T)
             prev = n
+
+
+def test_layer_workspace_size_grows_with_T():
+    lib = k3moe
+    for d in (k3gen.K3, k3gen.TINY):
+        prev = 0
+        for T in list(range(0, 300)) + list(range(300, 5000, 7)):
+            n = lib.k3moe_workspace_size(d, T)
+            assert n >= prev, (d, T)
+            prev = n

@@ -414,6 +414,15 @@ def test_tiny_mm_topp_both_expert_forms(tiny_mm, expert_path, mode, T):
         assert (ids < 0).any()
 
 
+@pytest.mark.parametrize("T", [1, 50])
+def test_tiny_topp_without_renorm_and_scaled(tiny, T):
+    # renorm off: the kept weights are the raw scores times routed_scale
+    v = copy.copy(tiny)
+    v.dims = dataclasses.replace(tiny.dims, topp=0.55, renorm=0, routed_scale=2.5)
+    x, _ = _inputs.gap_fixed_x(v.dims, 60 + T, T, v.dense["w_router"], v.dense["bias"])
+    compare_layer(v, x, what=f"tiny top-p 0.55 renorm 0 scale 2.5 T={T}")
+
+
 def test_tiny_topp_route_and_dispatch(tiny):
     # k3moe_route alone writes -1 in place; k3moe_dispatch drops those slots as the oracle does
     v = with_topp(tiny, 0.6)
