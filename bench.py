@@ -221,6 +221,8 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=3)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--batch-sweep", type=lambda v: [int(t) for t in v.split(",") if t], default=[8, 64, 256],
+                    help="also time the layer at these batch sizes (comma list; empty to skip)")
     ap.add_argument("--topp", type=float, default=0.9,
                     help="also time decode with the top-p tail drop at this p (0 = skip); an approximation, "
                          "reported beside the exact layer, never as the headline")
@@ -385,6 +387,29 @@ def main():
         del wsp, yp, xp
         torch.cuda.empty_cache()
 
+    # ---------------------------------------------------------------- small batches
+    sweep = {}
+    for Tb in args.batch_sweep:
+        xb = torch.from_numpy(k3gen.gen_x(dims, 7, Tb).view(np.int16)).cuda()
+        yb = torch.empty((Tb, dims.hidden), dtype=torch.float32, device="cuda")
+        wsb = device.workspace(dims, Tb)
+        for i in range(3):
+            k3moe.k3moe_layer(dims, Tb, xb, wts_rot[i % len(wts_rot)], yb, None, None, wsb, stream=stream)
+        torch.cuda.synchronize()
+        evb = HipEvents(2)
+        nb = 10
+        hip_record(evb.ev[0], stream.cuda_stream)
+        for i in range(nb):
+            k3moe.k3moe_layer(dims, Tb, xb, wts_rot[i % len(wts_rot)], yb, None, None, wsb, stream=stream)
+        hip_record(evb.ev[1], stream.cuda_stream)
+        torch.cuda.synchronize()
+        msb = evb.ms(evb.ev[0], evb.ev[1]) / nb
+        evb.close()
+        sweep[str(Tb)] = {"us_per_step": round(msb * 1e3, 1), "tokens_per_s": round(Tb / (msb * 1e-3), 1)}
+        del xb, yb, wsb
+    if sweep:
+        log("layer at small batches: " + ", ".join(f"T={k} {v['us_per_step']} us" for k, v in sweep.items()))
+
     # ---------------------------------------------------------------- top-p tail drop, T = 1
     topp = None
     if args.topp > 0:
@@ -452,6 +477,7 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": roofline,
         "prefill": prefill,
+        "batch_sweep": sweep or None,
         "shared_experts": shared,
         "topp_decode": topp,
         "cpu_baseline": cpu,
