@@ -116,6 +116,7 @@ class Dims:
     b1: float = 4.0
     b2: float = 25.0
     topp: float = 0.0  # top-p tail drop of the chosen experts (0 = off)
+    idot: int = 0      # 1: int8-per-32 activations in the expert products
 
 
 # Kimi K3 MoE fields as the pages' config reader lists them (hidden 7168, 896

@@ -25,7 +25,8 @@ class Dims(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int), ("latent", ctypes.c_int), ("inter", ctypes.c_int),
                 ("n_experts", ctypes.c_int), ("topk", ctypes.c_int), ("group", ctypes.c_int),
                 ("renorm", ctypes.c_int), ("routed_scale", ctypes.c_float), ("eps", ctypes.c_float),
-                ("b1", ctypes.c_float), ("b2", ctypes.c_float), ("topp", ctypes.c_float)]
+                ("b1", ctypes.c_float), ("b2", ctypes.c_float), ("topp", ctypes.c_float),
+                ("idot", ctypes.c_int)]
 
 
 class Mx(ctypes.Structure):
@@ -89,6 +90,10 @@ def lib():
         L.k3o_expert_pairs.restype = None
         L.k3o_shared.argtypes = [ctypes.POINTER(Dims), i, i, vp, vp, vp, vp, vp, i]
         L.k3o_shared.restype = None
+        L.k3o_q8_round.argtypes = [vp, vp, i]
+        L.k3o_q8_round.restype = f
+        L.k3o_mxfp4_matvec_q8.argtypes = [vp, vp, vp, vp, vp, i, i, i]
+        L.k3o_mxfp4_matvec_q8.restype = None
         _lib = L
     return _lib
 
@@ -103,7 +108,7 @@ def _p(a):
 def make_dims(d) -> Dims:
     """From any object with the layer's dimension fields (e.g. k3gen.Dims)."""
     return Dims(d.hidden, d.latent, d.inter, d.n_experts, d.topk, d.group, d.renorm,
-                d.routed_scale, d.eps, d.b1, d.b2, getattr(d, "topp", 0.0))
+                d.routed_scale, d.eps, d.b1, d.b2, getattr(d, "topp", 0.0), getattr(d, "idot", 0))
 
 
 class ExpertSet:
@@ -295,3 +300,21 @@ def shared(dims, x: np.ndarray, sh: dict, y: np.ndarray, n_shared: int = 2, nthr
     lib().k3o_shared(ctypes.byref(make_dims(dims)), n_shared, T, _p(x), _p(sh1), _p(sh3), _p(sh2), _p(out),
                      nthreads)
     return out
+
+
+def q8_round(v: np.ndarray):
+    """One group (n <= 32) of activations to int8 (k3o_q8_round). Returns (q, d)."""
+    v = np.ascontiguousarray(v, np.float32)
+    q = np.empty(v.size, np.int8)
+    d = lib().k3o_q8_round(_p(q), _p(v), v.size)
+    return q, float(d)
+
+
+def mxfp4_matvec_q8(q: np.ndarray, d: np.ndarray, packed: np.ndarray, scales: np.ndarray, cols: int, rows: int,
+                    group: int = 32) -> np.ndarray:
+    """k3o_mxfp4_matvec_q8: int8 activations q [cols] with group scales d."""
+    y = np.empty(rows, np.float32)
+    lib().k3o_mxfp4_matvec_q8(_p(y), _p(np.ascontiguousarray(q, np.int8)), _p(np.ascontiguousarray(d, np.float32)),
+                              _p(np.ascontiguousarray(packed, np.uint8)), _p(np.ascontiguousarray(scales, np.uint8)),
+                              cols, rows, group)
+    return y

@@ -69,6 +69,47 @@ void k3o_mxfp4_matvec(float *y, const float *x, const uint8_t *packed, const uin
     free(w);
 }
 
+/* [COL-IDOT]: see k3o.h. */
+float k3o_q8_round(int8_t *q, const float *v, int n)
+{
+    float amax = 0.0f;
+    for (int i = 0; i < n; i++) amax = fmaxf(amax, fabsf(v[i]));
+    const float d = amax / 127.0f;
+    for (int i = 0; i < n; i++) {
+        float r = d > 0.0f ? roundf(v[i] / d) : 0.0f;
+        if (r > 127.0f) r = 127.0f;
+        if (r < -127.0f) r = -127.0f;
+        q[i] = (int8_t)r;
+    }
+    return d;
+}
+
+/* [COL-IDOT], [K3C-4]: see k3o.h. */
+void k3o_mxfp4_matvec_q8(float *y, const int8_t *q, const float *d, const uint8_t *packed,
+                         const uint8_t *scales, int cols, int rows, int group)
+{
+    const size_t row_bytes = (size_t)(cols + 1) / 2;
+    const size_t row_groups = (size_t)(cols + group - 1) / group;
+    for (int r = 0; r < rows; r++) {
+        const uint8_t *prow = packed + (size_t)r * row_bytes;
+        const uint8_t *srow = scales + (size_t)r * row_groups;
+        double acc = 0.0;
+        for (int g0 = 0; g0 < cols; g0 += group) {
+            const int gi = g0 / group;
+            if (srow[gi] == 255) continue;
+            long isum = 0;
+            for (int c = g0; c < g0 + group && c < cols; c++) {
+                const uint8_t byte = prow[c / 2];
+                const int code = (c % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
+                const int w2 = (int)(2.0f * k3o_e2m1(code));  /* exact: 0, 1, 2, 3, 4, 6, 8, 12 */
+                isum += (long)w2 * (long)q[c];
+            }
+            acc += (double)isum * (double)k3o_e8m0(srow[gi]) * (double)d[gi] * 0.5;
+        }
+        y[r] = (float)acc;
+    }
+}
+
 /* [K3C-5]: W is [out][in] bf16, widened exactly; fp64 sum, fp32 result. */
 void k3o_bf16_matvec(float *y, const float *x, const uint16_t *W, int in, int out)
 {
@@ -231,16 +272,34 @@ void k3o_rmsnorm(float *out, const float *x, const float *w, int n, float eps)
 void k3o_expert(float *edn, float *g, float *u, float *act, const float *z,
                 const k3o_experts *ex, int e, const k3o_dims *d)
 {
-    const int L = d->latent, I = d->inter;
+    const int L = d->latent, I = d->inter, G = d->group;
     float *gg = (float *)malloc(sizeof(float) * (size_t)I * 3);
     float *uu = gg + I, *aa = uu + I;
-    k3o_mxfp4_matvec(gg, z, ex->w1.packed + (size_t)e * ex->w1.packed_stride,
-                     ex->w1.scales + (size_t)e * ex->w1.scales_stride, L, I, d->group);
-    k3o_mxfp4_matvec(uu, z, ex->w3.packed + (size_t)e * ex->w3.packed_stride,
-                     ex->w3.scales + (size_t)e * ex->w3.scales_stride, L, I, d->group);
-    for (int r = 0; r < I; r++) aa[r] = k3o_situ(gg[r], uu[r], d->b1, d->b2);
-    k3o_mxfp4_matvec(edn, aa, ex->w2.packed + (size_t)e * ex->w2.packed_stride,
-                     ex->w2.scales + (size_t)e * ex->w2.scales_stride, I, L, d->group);
+    if (d->idot) {
+        /* [COL-IDOT]: z and act as int8 per group, integer dots */
+        const int n = L > I ? L : I;
+        int8_t *q = (int8_t *)malloc((size_t)n);
+        float *dq = (float *)malloc(sizeof(float) * (size_t)(n / G + 1));
+        for (int g0 = 0; g0 < L; g0 += G) dq[g0 / G] = k3o_q8_round(q + g0, z + g0, L - g0 < G ? L - g0 : G);
+        k3o_mxfp4_matvec_q8(gg, q, dq, ex->w1.packed + (size_t)e * ex->w1.packed_stride,
+                            ex->w1.scales + (size_t)e * ex->w1.scales_stride, L, I, G);
+        k3o_mxfp4_matvec_q8(uu, q, dq, ex->w3.packed + (size_t)e * ex->w3.packed_stride,
+                            ex->w3.scales + (size_t)e * ex->w3.scales_stride, L, I, G);
+        for (int r = 0; r < I; r++) aa[r] = k3o_situ(gg[r], uu[r], d->b1, d->b2);
+        for (int g0 = 0; g0 < I; g0 += G) dq[g0 / G] = k3o_q8_round(q + g0, aa + g0, I - g0 < G ? I - g0 : G);
+        k3o_mxfp4_matvec_q8(edn, q, dq, ex->w2.packed + (size_t)e * ex->w2.packed_stride,
+                            ex->w2.scales + (size_t)e * ex->w2.scales_stride, I, L, G);
+        free(q);
+        free(dq);
+    } else {
+        k3o_mxfp4_matvec(gg, z, ex->w1.packed + (size_t)e * ex->w1.packed_stride,
+                         ex->w1.scales + (size_t)e * ex->w1.scales_stride, L, I, G);
+        k3o_mxfp4_matvec(uu, z, ex->w3.packed + (size_t)e * ex->w3.packed_stride,
+                         ex->w3.scales + (size_t)e * ex->w3.scales_stride, L, I, G);
+        for (int r = 0; r < I; r++) aa[r] = k3o_situ(gg[r], uu[r], d->b1, d->b2);
+        k3o_mxfp4_matvec(edn, aa, ex->w2.packed + (size_t)e * ex->w2.packed_stride,
+                         ex->w2.scales + (size_t)e * ex->w2.scales_stride, I, L, G);
+    }
     if (g) memcpy(g, gg, sizeof(float) * (size_t)I);
     if (u) memcpy(u, uu, sizeof(float) * (size_t)I);
     if (act) memcpy(act, aa, sizeof(float) * (size_t)I);

@@ -23,6 +23,10 @@
  *  [COL]   colibri docs/kimi_k3.md, "Architecture notes" (Stable LatentMoE) and
  *          "Weights" (MXFP4: low nibble = even column, bit 3 = sign, one ue8m0
  *          scale per 32 columns, w = v * 2^(scale - 127)).
+ *  [COL-IDOT] same page, "Streaming design" and "Environment variables" (K3_IDOT:
+ *          the expert products with each 32-value group of the activations rounded
+ *          to int8 and the doubled e2m1 weight codes, exact int8 values, dotted as
+ *          integers).
  *  [COL-RT] same page, "Streaming design" and "Environment variables" (K3_TOPP: an
  *          optional top-p drop of the low-weight tail of the chosen experts,
  *          renormalised; 0 = off).
@@ -51,6 +55,7 @@ typedef struct {
     float eps;       /* RMSNorm epsilon, inside the square root */
     float b1, b2;    /* SiTU caps: 4 and 25 */
     float topp;      /* 0: off; else keep the chosen experts up to cumulative weight topp */
+    int idot;        /* 1: the experts' products take int8-per-32 activations (k3o_q8_round) */
 } k3o_dims;
 
 /* One MXFP4 matrix stacked over experts: expert e's packed bytes start at
@@ -121,8 +126,23 @@ float k3o_situ(float g, float u, float b1, float b2);
 /* out = x / sqrt(mean(x^2) + eps) * w (w NULL = ones); fp64 inside, fp32 out; in place allowed */
 void k3o_rmsnorm(float *out, const float *x, const float *w, int n, float eps);
 
+/* [COL-IDOT]: one group of n <= 32 activations to int8: amax = max |v| (fp32),
+ * d = amax / 127 (fp32), q = roundf(v / d) (nearest, ties away from zero; |q| <= 127).
+ * Readings: a symmetric scale from the group maximum; an all-zero group gives d = 0 and
+ * q = 0. Writes q[n] and returns d. */
+float k3o_q8_round(int8_t *q, const float *v, int n);
+
+/* [COL-IDOT], [K3C-4]: y = W x for MXFP4 W and int8 activations q with one scale d per
+ * 32-column group: per row and group, the integer sum of (2 * E2M1(code)) * q (each
+ * doubled code an exact integer), then times 2^(scale - 127) * d / 2, the groups summed
+ * in fp64, one rounding to fp32 per row. A scale byte of 255 zeroes its group. */
+void k3o_mxfp4_matvec_q8(float *y, const int8_t *q, const float *d, const uint8_t *packed,
+                         const uint8_t *scales, int cols, int rows, int group);
+
 /* One expert on one latent vector z[L]: g = W1 z, u = W3 z (fp32), act = SiTU (fp32),
- * edn = W2 act (fp32). g, u, act (nullable) receive the intermediates [I]. */
+ * edn = W2 act (fp32). g, u, act (nullable) receive the intermediates [I]. With
+ * d->idot, z and act enter their products as int8 per 32-value group
+ * (k3o_q8_round, k3o_mxfp4_matvec_q8). */
 void k3o_expert(float *edn, float *g, float *u, float *act, const float *z,
                 const k3o_experts *ex, int e, const k3o_dims *d);
 

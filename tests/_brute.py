@@ -86,6 +86,23 @@ def topp_drop(chosen: np.ndarray, sc_chosen: np.ndarray, p: float, renorm=1, rou
     return np.where(keep, chosen, -1).astype(np.int32), w
 
 
+def q8_dequant(v: np.ndarray, group: int = 32) -> np.ndarray:
+    """Activations rounded to int8 per group (symmetric absmax scale, nearest with ties away
+    from zero), returned as the values the integer dot stands for: q * d in fp64."""
+    v = np.asarray(v, np.float32)
+    out = np.empty(v.size, np.float64)
+    for g0 in range(0, v.size, group):
+        x = v[g0:g0 + group]
+        d = np.float32(np.max(np.abs(x))) / np.float32(127.0)
+        if d == 0:
+            out[g0:g0 + group] = 0.0
+            continue
+        r = (x / d).astype(np.float32)
+        q = np.clip(np.sign(r) * np.floor(np.abs(r) + np.float32(0.5)), -127, 127)
+        out[g0:g0 + group] = q.astype(np.float64) * np.float64(d)
+    return out
+
+
 def situ(g: np.ndarray, u: np.ndarray, b1=4.0, b2=25.0) -> np.ndarray:
     g = g.astype(np.float64)
     u = u.astype(np.float64)
@@ -106,10 +123,13 @@ def layer_token(dims, x_bf16: np.ndarray, dense: dict, expert_blob_fn, offsets: 
         if e < 0:
             continue
         (p1, s1), (p3, s3), (p2, s2) = expert_views(expert_blob_fn(int(e)), dims, offsets)
-        g = (decode_mxfp4(p1, s1, dims.group) @ z.astype(np.float64)).astype(np.float32)
-        u = (decode_mxfp4(p3, s3, dims.group) @ z.astype(np.float64)).astype(np.float32)
+        idot = getattr(dims, "idot", 0)
+        zin = q8_dequant(z, dims.group) if idot else z.astype(np.float64)
+        g = (decode_mxfp4(p1, s1, dims.group) @ zin).astype(np.float32)
+        u = (decode_mxfp4(p3, s3, dims.group) @ zin).astype(np.float32)
         a = situ(g, u, dims.b1, dims.b2)
-        edn = (decode_mxfp4(p2, s2, dims.group) @ a.astype(np.float64)).astype(np.float32)
+        ain = q8_dequant(a, dims.group) if idot else a.astype(np.float64)
+        edn = (decode_mxfp4(p2, s2, dims.group) @ ain).astype(np.float32)
         acc += np.float64(wj) * edn.astype(np.float64)
     accf = acc.astype(np.float32).astype(np.float64)
     gam = dense["norm_w"].astype(np.float64)

@@ -506,3 +506,67 @@ def test_layer_topp_matches_brute_force_tiny():
         for k in ("acc", "y"):
             ref = b[k].astype(np.float64)
             assert np.linalg.norm(r[k][t] - ref) / np.linalg.norm(ref) < 1e-6, (t, k)
+
+
+# ---------------------------------------------------------------- int8-activation products
+def test_q8_round_hand_cases():
+    # amax 127 gives d = 1: q is v rounded to nearest, ties away from zero
+    v = np.zeros(32, np.float32)
+    v[:6] = [127.0, -2.5, 2.5, 0.49, -0.51, 3.75]
+    q, d = oracle.q8_round(v)
+    assert d == 1.0
+    assert q[:6].tolist() == [127, -3, 3, 0, -1, 4] and not q[6:].any()
+    # the largest magnitude maps to +-127 exactly; d = amax / 127 in fp32
+    v = np.linspace(-0.8, 0.3, 32).astype(np.float32)
+    q, d = oracle.q8_round(v)
+    assert q[0] == -127 and d == np.float32(np.float32(0.8) / np.float32(127.0))
+    assert np.all(np.abs(q.astype(np.float64) * d - v) <= d / 2 + 1e-9)
+    # an all-zero group
+    q, d = oracle.q8_round(np.zeros(32, np.float32))
+    assert d == 0.0 and not q.any()
+
+
+def test_matvec_q8_integer_dot_vs_dense_decode():
+    # the integer form (doubled codes times q, then 2^(s-127) * d / 2) equals a dense fp64
+    # product of the decoded weights with q * d
+    rng = np.random.default_rng(11)
+    rows, cols = 40, 96
+    packed = rng.integers(0, 256, (rows, cols // 2), dtype=np.uint8)
+    scales = rng.integers(118, 131, (rows, cols // 32), dtype=np.uint8)
+    scales[3, 1] = 255
+    q = rng.integers(-127, 128, cols).astype(np.int8)
+    d = rng.uniform(1e-3, 2e-2, cols // 32).astype(np.float32)
+    y = oracle.mxfp4_matvec_q8(q, d, packed, scales, cols, rows)
+    xd = q.astype(np.float64) * np.repeat(d.astype(np.float64), 32)
+    W = _brute.decode_mxfp4(packed, scales, 32)
+    ref = W @ xd
+    assert np.all(np.abs(y - ref) <= 2 ** -23 * np.abs(ref) + 1e-12)
+
+
+def _tiny_layer_idot(seed, T):
+    d = dataclasses.replace(k3gen.TINY, idot=1)
+    dense = k3gen.gen_dense(d, seed)
+    lay = k3gen.ExpertLayout(d)
+    blobs = k3gen.gen_experts(d, seed, 0, d.n_experts)
+    ex = oracle.ExpertSet(blobs, lay.blob_bytes, lay.offsets)
+    return d, dense, lay, blobs, ex, k3gen.gen_x(d, seed, T)
+
+
+def test_layer_idot_matches_brute_force_tiny():
+    d, dense, lay, blobs, ex, x = _tiny_layer_idot(0, 8)
+    r = oracle.layer(d, x, dense, ex, want_inner=True)
+    B = lay.blob_bytes
+    for t in range(x.shape[0]):
+        b = _brute.layer_token(d, x[t], dense, lambda e: blobs[e * B:(e + 1) * B], lay.offsets)
+        for k in ("acc", "y"):
+            ref = b[k].astype(np.float64)
+            assert np.linalg.norm(r[k][t] - ref) / np.linalg.norm(ref) < 1e-6, (t, k)
+
+
+def test_layer_idot_is_an_approximation_of_the_exact_layer():
+    d, dense, lay, blobs, ex, x = _tiny_layer_idot(1, 16)
+    a = oracle.layer(d, x, dense, ex)["y"].astype(np.float64)
+    e = oracle.layer(dataclasses.replace(d, idot=0), x, dense, ex)["y"].astype(np.float64)
+    rel = np.linalg.norm(a - e, axis=1) / np.linalg.norm(e, axis=1)
+    # int8 per 32 leaves about 2^-8 of each group's maximum: a change of about 1e-2
+    assert np.all(rel > 1e-3) and np.all(rel < 5e-2), rel
