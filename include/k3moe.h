@@ -27,6 +27,15 @@
  * topk_idx with id -1 and weight 0 (k3moe_dispatch and k3moe_combine skip it); the kept
  * weights are renormalised over the kept set (when renorm is set), times routed_scale.
  *
+ * Int8 activations (same page, K3_IDOT; an approximation, off unless dims.idot = 1): in
+ * step 3 the expert products take z and act with each 32-value group rounded to int8,
+ * d = max|v| / 127 (fp32), q = roundf(v / d) (nearest, ties away from zero), the value
+ * q * d standing for the pair (q, d), whose product with the MXFP4 weights is the pages'
+ * integer dot of doubled e2m1 codes and q times the two scales. It moves the output by
+ * about 1e-2 relative; the GPU and an fp64 evaluation of the same rule agree to about
+ * 1e-6 except where a value sits within rounding of a half-step boundary and one side
+ * rounds it the other way (about one value per token at the K3 shape).
+ *
  * MXFP4 layout (section 4; colibri "Weights"): a matrix [rows][cols] is stored as
  * packed bytes [rows][cols/2], column 2k in the LOW nibble of byte k and column 2k+1
  * in the HIGH nibble, each nibble an E2M1 code (bit 3 = sign), plus scale bytes
@@ -96,6 +105,7 @@ typedef struct {
     float eps;          /* RMSNorm epsilon, inside the square root (K3: 1e-5) */
     float b1, b2;       /* SiTU-GLU caps (K3: 4 and 25) */
     float topp;         /* 0: off (K3 default). > 0: the top-p tail drop, see below */
+    int32_t idot;       /* 0: exact (K3 default). 1: int8-per-32 activations in step 3, see below */
 } k3moe_dims;
 
 typedef struct {

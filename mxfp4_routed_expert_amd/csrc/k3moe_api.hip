@@ -32,6 +32,7 @@ int check_dims(const k3moe_dims *d) {
   if (!(d->eps >= 0.f) || !isfinite(d->eps) || !isfinite(d->b1) || !isfinite(d->b2) ||
       d->b1 == 0.f || d->b2 == 0.f || !isfinite(d->routed_scale) || !(d->topp >= 0.f) || !isfinite(d->topp))
     return K3MOE_EINVAL;
+  if (d->idot != 0 && d->idot != 1) return K3MOE_EINVAL;
   if (d->group != 32) return K3MOE_EUNSUPPORTED;
   if (d->hidden % 32 || d->latent % 32 || d->inter % 32) return K3MOE_EUNSUPPORTED;
   if (d->topk > 32 || d->topk > d->n_experts || d->n_experts > 1024) return K3MOE_EUNSUPPORTED;
@@ -372,11 +373,14 @@ int run_front(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_wei
     K3_TRY(run_route_down_mm(d, T, x, wt->w_router, wt->w_down, w.z32, w, &parts, s));
     mark("router_and_latent_down");
     TopkArgs tk = topk_args(d, T, w.router_part, parts, wt->bias, idx, tw);
-    tk.z = w.z32;
-    tk.zq = w.zq;
+    // (with int8 activations z is rounded and quantized by the expert pass instead)
+    if (!d->idot) {
+      tk.z = w.z32;
+      tk.zq = w.zq;
+    }
     K3_HIP(launch_topk(tk, s));
     mark("topk");
-    *zq_ready = true;
+    *zq_ready = !d->idot;
   } else if (use_gemv1(d, T, x)) {
     // one token: the router product and W_down stream in one launch; then the gate/up
     // pass selects the experts itself, or else one block selects them and writes the
@@ -389,13 +393,16 @@ int run_front(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_wei
     tk.pair_slot = w.pair_slot;
     tk.active = w.active;
     tk.counters = w.counters;
-    tk.z = w.z32;
-    tk.zq = w.zq;
+    if (!d->idot) {
+      tk.z = w.z32;
+      tk.zq = w.zq;
+    }
     GroupedArgs g = {};
     g.K = d->latent;
     g.gather = 1;
     g.tk = tk;
-    if (route && !use_mm(d, T, d->latent, (int64_t)T * d->latent * 4, wt->ex.w1, wt->ex.w3) &&
+    // (the selection at the head of the gate/up pass quantizes z without int8 rounding)
+    if (route && !d->idot && !use_mm(d, T, d->latent, (int64_t)T * d->latent * 4, wt->ex.w1, wt->ex.w3) &&
         route_in_gateup_ok(g)) {
       *route = tk;
       route->positional = 1;  // the passes take slot j as pair j, dropped slots included
@@ -404,7 +411,7 @@ int run_front(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_wei
     }
     K3_HIP(launch_topk(tk, s));
     mark("topk_dispatch_quant");
-    *zq_ready = true;
+    *zq_ready = !d->idot;
   } else {
     // GEMV form: the router alone, then W_down streams while other blocks of the same
     // launch select the experts; z is quantized once afterwards
@@ -485,8 +492,9 @@ int run_experts(const k3moe_dims *d, int32_t T, const float *z, bool zq_ready, c
   const MxMat w3{ex->w3.packed, ex->w3.scales, ex->w3.packed_expert_stride, ex->w3.scales_expert_stride};
   const MxMat w2{ex->w2.packed, ex->w2.scales, ex->w2.packed_expert_stride, ex->w2.scales_expert_stride};
   if (route && mm_gu) return K3MOE_EINVAL;  // run_front only defers to the GEMV form
-  if (!zq_ready && !route) {
-    K3_HIP(launch_quant_rows(z, (size_t)T * d->latent, w.zq, s));
+  if (d->idot || (!zq_ready && !route)) {
+    // int8 activations: each 32-value group of z rounded to int8 before its pieces
+    K3_HIP(launch_quant_rows(z, (size_t)T * d->latent, w.zq, d->idot != 0, s));
     mark("latent_quant");
   }
   if (mm_gu) {
@@ -529,6 +537,11 @@ int run_experts(const k3moe_dims *d, int32_t T, const float *z, bool zq_ready, c
     K3_HIP(launch_grouped(g, kEpiSitu, tt, rb_gu, grid_y, s, route != nullptr));
   }
   mark(route ? "topk_expert_gateup_situ" : "expert_gateup_situ");
+  if (d->idot) {
+    // int8 activations: the SiTU outputs rounded to int8 per 32-value group
+    K3_HIP(launch_q8_requant(w.actq, P * (d->inter / 32), s));
+    mark("act_int8_round");
+  }
 
   if (mm_dn) {
     MmArgs m = {};

@@ -299,6 +299,34 @@ __device__ __forceinline__ void quant_group_fp6_kq(float (&r)[8], int kq, uint8_
   }
 }
 
+// int8 rounding of one 32-value group of activations (the int8-activation expert
+// products): d = max |v| / 127, v -> roundf(v / d) * d (nearest, ties away from zero;
+// |q| <= 127); an all-zero group stays zero. The value q * d stands for the int8 code q
+// with the group scale d; its four fp6 pieces carry it to 2^-20 of the group maximum.
+__device__ __forceinline__ float q8_value(float v, float d) {
+  return d > 0.f ? fminf(fmaxf(roundf(v / d), -127.f), 127.f) * d : 0.f;
+}
+// the group held by 4 consecutive lanes, 8 values each (lane order = value order)
+__device__ __forceinline__ void q8_round_lanes4(float (&v)[8]) {
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+  m = fmaxf(m, lane_xor1(m));
+  m = fmaxf(m, lane_xor2(m));
+  const float d = m / 127.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = q8_value(v[i], d);
+}
+// the group held by one lane
+__device__ __forceinline__ void q8_round32(float (&v)[32]) {
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(v[i]));
+  const float d = m / 127.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v[i] = q8_value(v[i], d);
+}
+
 // Exclusive prefix sum of one int per thread over the block (blockDim.x <= 1024);
 // sh_wave holds 16 ints. Every thread gets the block total.
 __device__ __forceinline__ int block_excl_scan(int v, int *sh_wave, int *total) {

@@ -187,7 +187,11 @@ hipError_t launch_gemv1(const Gemv1Args &a, int af, int xf, int epi, int rpw, hi
 hipError_t launch_gemv1_front(const Gemv1Args &r, const Gemv1Args &d, hipStream_t s);
 // the latent projection (DenseArgs, bf16 weights, kEpiStore) and the top-k in one launch
 hipError_t launch_down_topk(const DenseArgs &d, const TopkArgs &tk, hipStream_t s);
-hipError_t launch_quant_rows(const float *src, size_t n, uint8_t *dst, hipStream_t s);
+// rows of fp32 values into fp6 piece records (n % 32 == 0); q8: each 32-value group
+// rounded to int8 first (q8_round_lanes4)
+hipError_t launch_quant_rows(const float *src, size_t n, uint8_t *dst, bool q8, hipStream_t s);
+// fp6 piece records of ngroups 32-value groups rounded to int8 in place (k_q8_requant)
+hipError_t launch_q8_requant(uint8_t *rec, int64_t ngroups, hipStream_t s);
 hipError_t launch_dispatch(const int32_t *topk_idx, int T, int K, int E, int32_t *expert_off,
                            int32_t *sorted_pair, int32_t *pair_slot, int32_t *active,
                            int32_t *counters, int32_t *lrank, int32_t *cnt, hipStream_t s);

@@ -941,6 +941,7 @@ hipError_t launch_grouped(const GroupedArgs &a, int epi, int tokens_per_tile, in
 // ============================================================== fp32 rows -> fp6 pieces
 // Thread t quantizes values 8t .. 8t+7 of the flattened [rows][K] array; four
 // consecutive threads form one 32-value group (K % 32 == 0).
+template <bool Q8>
 __global__ __launch_bounds__(256) void k_quant_rows(const float *__restrict__ src, size_t n8,
                                                     uint8_t *__restrict__ dst) {
   for (size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x; t < ((n8 + 3) & ~(size_t)3);
@@ -955,18 +956,56 @@ __global__ __launch_bounds__(256) void k_quant_rows(const float *__restrict__ sr
 #pragma unroll
       for (int i = 0; i < 8; ++i) rv[0][i] = 0.f;
     }
+    if constexpr (Q8) q8_round_lanes4(rv[0]);
     uint8_t *const rec[1] = {dst + (t >> 2) * kGroupRec};
     const bool wr[1] = {true};
     quant_groups_fp6<1>(rv, (int)(t & 3), rec, wr);
   }
 }
 
-hipError_t launch_quant_rows(const float *src, size_t n, uint8_t *dst, hipStream_t s) {
+// The int8 rounding of activations already stored as fp6 piece records (the SiTU outputs
+// of the gate/up pass): one thread per 32-value group decodes its four pieces, rounds the
+// group to int8 and writes the pieces of the rounded values back in place.
+__global__ __launch_bounds__(256) void k_q8_requant(uint8_t *__restrict__ rec, int64_t ngroups) {
+  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < ngroups;
+       g += (int64_t)gridDim.x * blockDim.x) {
+    uint8_t *r = rec + g * kGroupRec;
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = 0.f;
+#pragma unroll
+    for (int p = 0; p < kFp6Pieces; ++p) {
+      const uint32_t *src = (const uint32_t *)(r + p * kPieceRec);
+      const u32x4 c0 = *(const u32x4 *)src;
+      const u32x2 c1 = *(const u32x2 *)(src + 4);
+      const int ex = (int)(src[6] & 255u) - 127;
+      const u32x6 c = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y};
+      const f32x32 f = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(__builtin_bit_cast(i32x6, c), 1.0f);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) v[i] += ldexpf(f[i], ex);
+    }
+    q8_round32(v);
+    quant_group32_fp6(v, r);
+  }
+}
+
+hipError_t launch_q8_requant(uint8_t *rec, int64_t ngroups, hipStream_t s) {
+  if (ngroups <= 0) return hipSuccess;
+  int64_t blocks = (ngroups + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  launch_kernel(k_q8_requant, (unsigned)blocks, 256, 0, s, rec, ngroups);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_rows(const float *src, size_t n, uint8_t *dst, bool q8, hipStream_t s) {
   if (n == 0) return hipSuccess;
   const size_t n8 = n / 8;
   size_t blocks = (n8 + 255) / 256;
   if (blocks > 4096) blocks = 4096;
-  launch_kernel(k_quant_rows, (unsigned)blocks, 256, 0, s, src, n8, dst);
+  if (q8)
+    launch_kernel(k_quant_rows<true>, (unsigned)blocks, 256, 0, s, src, n8, dst);
+  else
+    launch_kernel(k_quant_rows<false>, (unsigned)blocks, 256, 0, s, src, n8, dst);
   return hipGetLastError();
 }
 

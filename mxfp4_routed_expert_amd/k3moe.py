@@ -30,7 +30,8 @@ class k3moe_dims(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("latent", ctypes.c_int32), ("inter", ctypes.c_int32),
                 ("n_experts", ctypes.c_int32), ("topk", ctypes.c_int32), ("group", ctypes.c_int32),
                 ("renorm", ctypes.c_int32), ("routed_scale", ctypes.c_float), ("eps", ctypes.c_float),
-                ("b1", ctypes.c_float), ("b2", ctypes.c_float), ("topp", ctypes.c_float)]
+                ("b1", ctypes.c_float), ("b2", ctypes.c_float), ("topp", ctypes.c_float),
+                ("idot", ctypes.c_int32)]
 
 
 class k3moe_mxfp4(ctypes.Structure):
@@ -107,7 +108,7 @@ def status_str(status: int) -> str:
 
 def make_dims(d) -> k3moe_dims:
     return k3moe_dims(d.hidden, d.latent, d.inter, d.n_experts, d.topk, d.group, d.renorm,
-                      d.routed_scale, d.eps, d.b1, d.b2, getattr(d, "topp", 0.0))
+                      d.routed_scale, d.eps, d.b1, d.b2, getattr(d, "topp", 0.0), getattr(d, "idot", 0))
 
 
 def _ptr(a):

@@ -447,6 +447,56 @@ def test_k3_topp_layer_T64(k3):
     compare_topp(k3, 0.8, 64, 2, "K3 top-p 0.8 T=64")
 
 
+# ------------------------------------------------------------------ int8 activations
+# The int8 rounding of z and act is a float decision on values the GPU and the oracle
+# compute about 1e-6 apart (fp32 matrix-core sums against fp64), so a value lying that
+# close to a half-step boundary may round the other way on one side. Such a value moves
+# its group's input by d = max/127: an act value moves the row's output by about 1e-4
+# relative, a z value (it feeds all 16 experts) by up to about 2e-3. At the K3 shape a
+# token has a few such act values (measured: most rows near 1e-4), at the tiny shapes
+# almost none (rows at the exact bar). The bar for this approximation, from that: rel-L2
+# <= 5e-3 and max-abs <= 1e-2 * max|ref| per row, the median row within 5e-4; and the
+# rule's own effect, about 1e-2 from the exact layer, must be there (median above 3e-3).
+IDOT_REL, IDOT_ABSF, IDOT_MEDIAN = 5e-3, 1e-2, 5e-4
+
+
+def compare_idot(h: Host, T: int, seed: int, what: str):
+    v = copy.copy(h)
+    v.dims = dataclasses.replace(h.dims, idot=1)
+    x, _ = _inputs.gap_fixed_x(v.dims, seed, T, v.dense["w_router"], v.dense["bias"])
+    y, idx, w = run_layer(v, x)
+    ref = oracle.layer(v.dims, x, v.dense, v.ex)
+    assert np.array_equal(idx, ref["idx"]), f"{what}: expert ids differ"
+    check_rows(w, ref["w"], f"{what} weights", rel=1e-6, absf=1e-6)
+    check_rows(y, ref["y"], f"{what} y", rel=IDOT_REL, absf=IDOT_ABSF)
+    err = np.linalg.norm(y.astype(np.float64) - ref["y"], axis=1) / np.linalg.norm(ref["y"].astype(np.float64), axis=1)
+    exact = oracle.layer(h.dims, x, h.dense, h.ex)["y"].astype(np.float64)
+    gap = np.linalg.norm(y - exact, axis=1) / np.linalg.norm(exact, axis=1)
+    say(f"  {what}: rows past 1e-5 {np.mean(err > 1e-5):.2f}, median distance from the exact layer {np.median(gap):.2e}")
+    assert np.median(err) <= IDOT_MEDIAN
+    assert np.median(gap) > 3e-3
+
+
+@pytest.mark.parametrize("T", [1, 3, 64, 300])
+def test_tiny_idot_layer(tiny, T):
+    compare_idot(tiny, T, 120 + T, f"tiny int8 activations T={T}")
+
+
+@pytest.mark.parametrize("mode", ["gemv", "gemm"])
+@pytest.mark.parametrize("T", [5, 300])
+def test_tiny_mm_idot_both_expert_forms(tiny_mm, expert_path, mode, T):
+    expert_path(k3moe.EXPERT_PATH_GEMV if mode == "gemv" else k3moe.EXPERT_PATH_GEMM)
+    compare_idot(tiny_mm, T, 130 + T, f"tiny-mm int8 activations T={T} {mode}")
+
+
+def test_k3_idot_layer_T1(k3):
+    compare_idot(k3, 1, 1, "K3 int8 activations T=1")
+
+
+def test_k3_idot_layer_T64(k3):
+    compare_idot(k3, 64, 2, "K3 int8 activations T=64")
+
+
 # ------------------------------------------------------------------ shared experts
 def run_shared(d, n_shared, x: np.ndarray, shd: dict, y0: np.ndarray):
     T = x.shape[0]
