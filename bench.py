@@ -226,6 +226,8 @@ def main():
     ap.add_argument("--topp", type=float, default=0.9,
                     help="also time decode with the top-p tail drop at this p (0 = skip); an approximation, "
                          "reported beside the exact layer, never as the headline")
+    ap.add_argument("--no-idot", action="store_true",
+                    help="skip timing the int8-activation expert variant (an approximation, never the headline)")
     ap.add_argument("--no-shared", action="store_true",
                     help="skip the shared-expert measurement (a call of its own, after the layer)")
     ap.add_argument("--cpu-tokens", type=int, default=64)
@@ -437,6 +439,32 @@ def main():
                 "mean_experts_kept": round(kept, 2), "kind": "approximation (top-p tail drop), not the headline"}
         log(f"decode T=1 with top-p {args.topp}: {ms_p * 1e3:.1f} us/step, {kept:.2f} experts kept on average")
 
+    # ---------------------------------------------------------------- int8 activations, T = 1
+    idot = None
+    if not args.no_idot:
+        import dataclasses
+        di = dataclasses.replace(dims, idot=1)
+
+        def step_i(i):
+            j = i % pool
+            k3moe.k3moe_layer(di, T, xs.data_ptr() + j * row, wts_rot[i % len(wts_rot)], y, idx[j], tw[j], ws,
+                              stream=stream)
+
+        for i in range(args.warmup):
+            step_i(i)
+        torch.cuda.synchronize()
+        evi = HipEvents(2)
+        hip_record(evi.ev[0], stream.cuda_stream)
+        for i in range(args.steps):
+            step_i(i)
+        hip_record(evi.ev[1], stream.cuda_stream)
+        torch.cuda.synchronize()
+        ms_i = evi.ms(evi.ev[0], evi.ev[1]) / args.steps
+        evi.close()
+        idot = {"us_per_step": round(ms_i * 1e3, 2), "tokens_per_s": round(1.0 / (ms_i * 1e-3), 1),
+                "kind": "approximation (int8-per-32 expert activations), not the headline"}
+        log(f"decode T=1 with int8 activations: {ms_i * 1e3:.1f} us/step")
+
     # ---------------------------------------------------------------- shared experts
     shared = None
     if not args.no_shared:
@@ -480,6 +508,7 @@ def main():
         "batch_sweep": sweep or None,
         "shared_experts": shared,
         "topp_decode": topp,
+        "idot_decode": idot,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
