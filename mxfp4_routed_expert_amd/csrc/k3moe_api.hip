@@ -401,9 +401,14 @@ int run_front(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_wei
     g.K = d->latent;
     g.gather = 1;
     g.tk = tk;
-    // (the selection at the head of the gate/up pass quantizes z without int8 rounding)
-    if (route && !d->idot && !use_mm(d, T, d->latent, (int64_t)T * d->latent * 4, wt->ex.w1, wt->ex.w3) &&
+    // (the selection at the head of the gate/up pass quantizes z itself, int8-rounded
+    // with d->idot)
+    g.tk.z = w.z32;
+    g.tk.zq = w.zq;
+    if (route && !use_mm(d, T, d->latent, (int64_t)T * d->latent * 4, wt->ex.w1, wt->ex.w3) &&
         route_in_gateup_ok(g)) {
+      tk.z = w.z32;
+      tk.zq = w.zq;
       *route = tk;
       route->positional = 1;  // the passes take slot j as pair j, dropped slots included
       *zq_ready = false;
@@ -492,7 +497,7 @@ int run_experts(const k3moe_dims *d, int32_t T, const float *z, bool zq_ready, c
   const MxMat w3{ex->w3.packed, ex->w3.scales, ex->w3.packed_expert_stride, ex->w3.scales_expert_stride};
   const MxMat w2{ex->w2.packed, ex->w2.scales, ex->w2.packed_expert_stride, ex->w2.scales_expert_stride};
   if (route && mm_gu) return K3MOE_EINVAL;  // run_front only defers to the GEMV form
-  if (d->idot || (!zq_ready && !route)) {
+  if (!route && (d->idot || !zq_ready)) {
     // int8 activations: each 32-value group of z rounded to int8 before its pieces
     K3_HIP(launch_quant_rows(z, (size_t)T * d->latent, w.zq, d->idot != 0, s));
     mark("latent_quant");
@@ -534,6 +539,7 @@ int run_experts(const k3moe_dims *d, int32_t T, const float *z, bool zq_ready, c
     g.b1 = d->b1;
     g.b2 = d->b2;
     if (route) g.tk = *route;
+    g.q8 = d->idot;
     K3_HIP(launch_grouped(g, kEpiSitu, tt, rb_gu, grid_y, s, route != nullptr));
   }
   mark(route ? "topk_expert_gateup_situ" : "expert_gateup_situ");

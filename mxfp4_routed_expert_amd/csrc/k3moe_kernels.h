@@ -142,6 +142,7 @@ struct GroupedArgs {
   uint8_t *outq;          // kEpiSitu: [slot][M/32] fp6 piece records of act
   float b1, b2;
   TopkArgs tk;            // routed in the launch (one token): its selection and its z
+  int q8;                 // routed: z rounded to int8 per 32-value group before its pieces
   int one_token;          // a one-token layer batch: slot j is the only pair of expert
                           // active[j] (the offsets and the active count are not read);
                           // active[j] = -1: slot j was dropped (top-p), its output row

@@ -615,6 +615,7 @@ __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
           const float4 q = zp[i];
           zv[4 * i] = q.x; zv[4 * i + 1] = q.y; zv[4 * i + 2] = q.z; zv[4 * i + 3] = q.w;
         }
+        if (a.q8) q8_round32(zv);
         quant_group32_fp6(zv, smem + grouped_dec_sb_off(a.K, RB) + (size_t)gz * kGroupRec);
       }
     }
