@@ -12,7 +12,7 @@ import pytest
 
 import k3gen
 from tests import _inputs
-from tests.test_gpu_parity import Host, compare_layer, say
+from tests.test_gpu_parity import Host, compare_idot, compare_layer, say
 
 pytestmark = pytest.mark.gpu
 
@@ -61,3 +61,23 @@ def test_random_shape_shared_experts(seed):
     y0 = np.random.default_rng(seed).standard_normal((T, H)).astype(np.float32)
     got = run_shared(d, n_shared, x, device.upload_shared(sh), y0)
     check_rows(got, oracle.shared(d, x, sh, y0, n_shared), f"random shared {seed}")
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_shape_int8_activations(seed):
+    # the int8-activation variant on the random shapes (its own bar: compare_idot)
+    d, T = random_case(100 + seed)
+    say(f"random shape {100 + seed} with int8 activations: {d}, T={T}")
+    h = Host(d, 170 + seed)
+    compare_idot(h, T, 180 + seed, f"random shape {100 + seed} int8 T={T}")
+
+
+@pytest.mark.parametrize("E,K,p", [(32, 1, 0.5), (8, 8, 0.6), (8, 8, 0.0)])
+@pytest.mark.parametrize("T", [1, 40])
+def test_degenerate_routing(E, K, p, T):
+    # one expert per token (top-p keeps it, weight 1); every expert chosen (the top-k is
+    # the whole set; top-p drops its tail)
+    d = dataclasses.replace(k3gen.TINY, n_experts=E, topk=K, topp=p)
+    h = Host(d, 60 + E + K)
+    x, _ = _inputs.gap_fixed_x(d, 61 + T, T, h.dense["w_router"], h.dense["bias"])
+    compare_layer(h, x, what=f"E={E} K={K} top-p {p} T={T}")
