@@ -34,7 +34,8 @@
  * integer dot of doubled e2m1 codes and q times the two scales. It moves the output by
  * about 1e-2 relative; the GPU and an fp64 evaluation of the same rule agree to about
  * 1e-6 except where a value sits within rounding of a half-step boundary and one side
- * rounds it the other way (about one value per token at the K3 shape).
+ * rounds it the other way (a few values per token at the K3 shape, each moving the
+ * token's output by about 1e-4 relative, up to 2e-3 for a value of z).
  *
  * MXFP4 layout (section 4; colibri "Weights"): a matrix [rows][cols] is stored as
  * packed bytes [rows][cols/2], column 2k in the LOW nibble of byte k and column 2k+1
