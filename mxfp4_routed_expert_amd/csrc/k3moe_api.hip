@@ -653,8 +653,11 @@ int check_shared(const k3moe_dims *d, int32_t n_shared, int32_t T) {
   return (int)SI;
 }
 
-// One-token form: both products' activations fit the GEMV's 64 KB of LDS.
-bool shared_gemv1(const k3moe_dims *d, int SI, int32_t T) { return T == 1 && d->hidden <= 16384 && SI <= 16384; }
+// One- and two-token form: both products' activations (all tokens) fit the GEMV's 64 KB
+// of LDS.
+bool shared_gemv1(const k3moe_dims *d, int SI, int32_t T) {
+  return T >= 1 && T <= 2 && (int64_t)T * d->hidden * 4 <= 65536 && (int64_t)T * SI * 4 <= 65536;
+}
 
 struct ShWs {
   float *act;      // one token: [SI] SiTU-GLU output
@@ -684,6 +687,8 @@ ShWs carve_shared(const k3moe_dims *d, int SI, int32_t T, void *base) {
     for (int q = 0; q < 2; ++q) w.p[q] = (uint16_t *)take(t * si * 2);
     // (taken even where this T needs no parts: the size stays nondecreasing in T)
     w.dn = (float *)take((size_t)dense_mm_parts_max(H, SI, T) * (size_t)H * 4);
+    // two tokens in the GEMV form keep act [2][SI] at the start of the gate|up buffer
+    w.act = w.gu;
   }
   w.bytes = o;
   return w;
@@ -703,6 +708,7 @@ int run_shared(const k3moe_dims *d, int SI, int32_t T, const uint16_t *x, const 
     gu.out = w.act;
     gu.b1 = d->b1;
     gu.b2 = d->b2;
+    gu.T = T;
     K3_HIP(launch_gemv1(gu, kA_BF16, kX_BF16, kEpiGluAct, 2, s));
     mark("shared_gate_up_situ");
     Gemv1Args dn = {};
@@ -712,6 +718,7 @@ int run_shared(const k3moe_dims *d, int SI, int32_t T, const uint16_t *x, const 
     dn.ks = 1;
     dn.xf = w.act;
     dn.out = y;
+    dn.T = T;
     // two rows per wave item (24 KB of row bytes): measured 16.7 us against 19.9 us with one
     K3_HIP(launch_gemv1(dn, kA_BF16, kX_F32, kEpiAdd, 2, s));
     mark("shared_down_add");

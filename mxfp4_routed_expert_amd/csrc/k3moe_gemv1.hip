@@ -27,16 +27,20 @@ __device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 
 // Stage x (the K activations, fp32) in LDS: from bf16, as the exact sum of three bf16
 // planes, or as fp32. Each thread converts 8 consecutive values from one 16-byte load per
 // source (two for fp32).
-template <int XF>
+template <int XF, int TT = 1>
 __device__ __forceinline__ void stage_x(const Gemv1Args &a, float *sx) {
-  for (int q = threadIdx.x; q < a.K / 8; q += blockDim.x) {
+  for (int qt = threadIdx.x; qt < TT * (a.K / 8); qt += blockDim.x) {
+    // token t's values land at sx + t * K
+    const int t = TT == 1 ? 0 : qt / (a.K / 8);
+    const int q = qt - t * (a.K / 8);
+    const size_t xo = (size_t)t * a.K;
     float v[8];
     if constexpr (XF == kX_F32) {
-      const float4 f0 = *(const float4 *)(a.xf + 8 * q), f1 = *(const float4 *)(a.xf + 8 * q + 4);
+      const float4 f0 = *(const float4 *)(a.xf + xo + 8 * q), f1 = *(const float4 *)(a.xf + xo + 8 * q + 4);
       v[0] = f0.x; v[1] = f0.y; v[2] = f0.z; v[3] = f0.w;
       v[4] = f1.x; v[5] = f1.y; v[6] = f1.z; v[7] = f1.w;
     } else if constexpr (XF == kX_BF16) {
-      const u32x4 b = *(const u32x4 *)(a.xb + 8 * q);
+      const u32x4 b = *(const u32x4 *)(a.xb + xo + 8 * q);
       const uint32_t w[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) { v[2 * i] = bf_lo(w[i]); v[2 * i + 1] = bf_hi(w[i]); }
@@ -53,8 +57,8 @@ __device__ __forceinline__ void stage_x(const Gemv1Args &a, float *sx) {
         v[2 * i + 1] = (bf_hi(w0[i]) + bf_hi(w1[i])) + bf_hi(w2[i]);
       }
     }
-    *(float4 *)(sx + 8 * q) = float4{v[0], v[1], v[2], v[3]};
-    *(float4 *)(sx + 8 * q + 4) = float4{v[4], v[5], v[6], v[7]};
+    *(float4 *)(sx + xo + 8 * q) = float4{v[0], v[1], v[2], v[3]};
+    *(float4 *)(sx + xo + 8 * q + 4) = float4{v[4], v[5], v[6], v[7]};
   }
 }
 
@@ -62,9 +66,10 @@ __device__ __forceinline__ void stage_x(const Gemv1Args &a, float *sx) {
 // row row0 of A and of A2). The weight loads of the first batch are issued before the
 // block stages x (they do not depend on it); `staged` runs the staging and the block
 // barrier.
-template <int AF, int EPI, int RPW, typename Stage>
+template <int AF, int EPI, int RPW, int TT = 1, typename Stage>
 __device__ __forceinline__ void gemv1_item(const Gemv1Args &a, float *sx, int item, bool live, float scale,
                                            Stage &&staged) {
+  static_assert(TT == 1 || EPI == kEpiGluAct || EPI == kEpiAdd, "two tokens: the shared-expert forms");
   constexpr int ESZ = AF == kA_F32 ? 4 : 2;
   constexpr int VPL = 16 / ESZ;  // weights per lane per load
   constexpr int NC = kG1MaxChunks / RPW;
@@ -96,9 +101,11 @@ __device__ __forceinline__ void gemv1_item(const Gemv1Args &a, float *sx, int it
       for (int c = 0; c < NC; ++c)
         w[r][c] = bload16(rA[r], (uint32_t)lane * 16u, c0 + c < nchunk ? (uint32_t)(c0 + c) * 1024u : kOOB);
   };
-  float acc[RPW];
+  float acc[TT][RPW];
 #pragma unroll
-  for (int r = 0; r < RPW; ++r) acc[r] = 0.f;
+  for (int t = 0; t < TT; ++t)
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) acc[t][r] = 0.f;
   load(0);
   staged();
   for (int c0 = 0; c0 < nchunk; c0 += NC) {
@@ -108,49 +115,58 @@ __device__ __forceinline__ void gemv1_item(const Gemv1Args &a, float *sx, int it
     for (int c = 0; c < NC; ++c) {
       const int e0 = ((c0 + c) * 1024 + lane * 16) / ESZ;  // first column of the lane's bytes
       const bool in = e0 < kp;
-      const float *xs = sx + k0 + (in ? e0 : 0);
-      float xv[VPL];
 #pragma unroll
-      for (int i = 0; i < VPL; i += 4) {
-        const float4 t = *(const float4 *)(xs + i);
-        xv[i] = in ? t.x : 0.f; xv[i + 1] = in ? t.y : 0.f;
-        xv[i + 2] = in ? t.z : 0.f; xv[i + 3] = in ? t.w : 0.f;
-      }
+      for (int t = 0; t < TT; ++t) {
+        // each token's activations against the same weight bytes
+        const float *xs = sx + (size_t)t * a.K + k0 + (in ? e0 : 0);
+        float xv[VPL];
 #pragma unroll
-      for (int r = 0; r < RPW; ++r) {
-        const u32x4 q = w[r][c];
-        if constexpr (AF == kA_F32) {
-          acc[r] = fmaf(__uint_as_float(q.x), xv[0], acc[r]);
-          acc[r] = fmaf(__uint_as_float(q.y), xv[1], acc[r]);
-          acc[r] = fmaf(__uint_as_float(q.z), xv[2], acc[r]);
-          acc[r] = fmaf(__uint_as_float(q.w), xv[3], acc[r]);
-        } else {
-          acc[r] = fmaf(bf_lo(q.x), xv[0], acc[r]);
-          acc[r] = fmaf(bf_hi(q.x), xv[1], acc[r]);
-          acc[r] = fmaf(bf_lo(q.y), xv[2], acc[r]);
-          acc[r] = fmaf(bf_hi(q.y), xv[3], acc[r]);
-          acc[r] = fmaf(bf_lo(q.z), xv[4], acc[r]);
-          acc[r] = fmaf(bf_hi(q.z), xv[5], acc[r]);
-          acc[r] = fmaf(bf_lo(q.w), xv[6], acc[r]);
-          acc[r] = fmaf(bf_hi(q.w), xv[7], acc[r]);
+        for (int i = 0; i < VPL; i += 4) {
+          const float4 f = *(const float4 *)(xs + i);
+          xv[i] = in ? f.x : 0.f; xv[i + 1] = in ? f.y : 0.f;
+          xv[i + 2] = in ? f.z : 0.f; xv[i + 3] = in ? f.w : 0.f;
+        }
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+          const u32x4 q = w[r][c];
+          float &ac = acc[t][r];
+          if constexpr (AF == kA_F32) {
+            ac = fmaf(__uint_as_float(q.x), xv[0], ac);
+            ac = fmaf(__uint_as_float(q.y), xv[1], ac);
+            ac = fmaf(__uint_as_float(q.z), xv[2], ac);
+            ac = fmaf(__uint_as_float(q.w), xv[3], ac);
+          } else {
+            ac = fmaf(bf_lo(q.x), xv[0], ac);
+            ac = fmaf(bf_hi(q.x), xv[1], ac);
+            ac = fmaf(bf_lo(q.y), xv[2], ac);
+            ac = fmaf(bf_hi(q.y), xv[3], ac);
+            ac = fmaf(bf_lo(q.z), xv[4], ac);
+            ac = fmaf(bf_hi(q.z), xv[5], ac);
+            ac = fmaf(bf_lo(q.w), xv[6], ac);
+            ac = fmaf(bf_hi(q.w), xv[7], ac);
+          }
         }
       }
     }
   }
   if (!live) return;
-  if constexpr (GLU) {
-    const float g = wave_sum_fixed(acc[0]), u = wave_sum_fixed(acc[1]);
-    if (lane == 0 && row0 < a.M) a.out[row0] = situ(g, u, a.b1, a.b2);
-    return;
-  }
 #pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    const float v = wave_sum_fixed(acc[r]);
-    const int row = row0 + r;
-    if (lane == 0 && row < a.M) {
-      if constexpr (EPI == kEpiStore) a.out[(size_t)part * a.M + row] = v;
-      else if constexpr (EPI == kEpiAdd) a.out[row] = a.out[row] + v;
-      else a.out[row] = v * scale;
+  for (int t = 0; t < TT; ++t) {
+    float *out = a.out + (size_t)t * a.M;
+    if constexpr (GLU) {
+      const float g = wave_sum_fixed(acc[t][0]), u = wave_sum_fixed(acc[t][1]);
+      if (lane == 0 && row0 < a.M) out[row0] = situ(g, u, a.b1, a.b2);
+      continue;
+    }
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const float v = wave_sum_fixed(acc[t][r]);
+      const int row = row0 + r;
+      if (lane == 0 && row < a.M) {
+        if constexpr (EPI == kEpiStore) out[(size_t)part * a.M + row] = v;
+        else if constexpr (EPI == kEpiAdd) out[row] = out[row] + v;
+        else out[row] = v * scale;
+      }
     }
   }
 }
@@ -162,7 +178,7 @@ __device__ __forceinline__ float rms_inv(const Gemv1Args &a) {
   return 1.0f / sqrtf(ss / (float)a.K + a.eps);
 }
 
-template <int AF, int XF, int EPI, int RPW>
+template <int AF, int XF, int EPI, int RPW, int TT = 1>
 __global__ __launch_bounds__(1024) void k_gemv1(Gemv1Args a, int items) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   float *sx = (float *)smem;
@@ -170,8 +186,8 @@ __global__ __launch_bounds__(1024) void k_gemv1(Gemv1Args a, int items) {
   const int item = blockIdx.x * (blockDim.x >> 6) + wave;
   const bool live = item < items;  // every wave takes part in the staging
   const float scale = EPI == kEpiStoreScaled ? rms_inv(a) : 1.f;
-  gemv1_item<AF, EPI, RPW>(a, sx, live ? item : 0, live, scale, [&] {
-    stage_x<XF>(a, sx);
+  gemv1_item<AF, EPI, RPW, TT>(a, sx, live ? item : 0, live, scale, [&] {
+    stage_x<XF, TT>(a, sx);
     __syncthreads();
   });
 }
@@ -209,10 +225,11 @@ int gemv1_waves(int items) {
 }
 
 bool gemv1_ok(const Gemv1Args &a, int esz) {
-  if (a.M <= 0 || a.K <= 0 || a.K % 8 != 0 || a.ks < 1 || a.K % a.ks != 0) return false;
+  if (a.M <= 0 || a.K <= 0 || a.K % 8 != 0 || a.ks < 1 || a.K % a.ks != 0 || a.T > 2) return false;
   const int kp = a.K / a.ks;
-  // 16-byte aligned row parts; x fits the LDS
-  return ((size_t)kp * esz) % 16 == 0 && ((size_t)a.K * esz) % 16 == 0 && (size_t)a.K * 4 <= 65536 &&
+  const size_t tt = a.T > 1 ? (size_t)a.T : 1;
+  // 16-byte aligned row parts; every token's x fits the LDS
+  return ((size_t)kp * esz) % 16 == 0 && ((size_t)a.K * esz) % 16 == 0 && tt * a.K * 4 <= 65536 &&
          ((size_t)a.M * a.K * esz) < ((size_t)1 << 40);
 }
 
@@ -236,21 +253,25 @@ hipError_t launch_gemv1(const Gemv1Args &a, int af, int xf, int epi, int rpw, hi
   if (!gemv1_ok(a, af == kA_F32 ? 4 : 2) || (rpw != 1 && rpw != 2)) return hipErrorInvalidValue;
   if ((epi == kEpiGluAct || epi == kEpiAdd || epi == kEpiStoreScaled) && a.ks != 1) return hipErrorInvalidValue;
   if (epi == kEpiGluAct && (rpw != 2 || !a.A2)) return hipErrorInvalidValue;
+  const int tt = a.T == 2 ? 2 : 1;
+  if (tt == 2 && epi != kEpiGluAct && epi != kEpiAdd) return hipErrorInvalidValue;
   const int items = (epi == kEpiGluAct ? a.M : (a.M + rpw - 1) / rpw) * a.ks;
   const int waves = gemv1_waves(items);
   const int grid = (items + waves - 1) / waves;
-  const size_t lds = (size_t)a.K * 4;
-#define G1(AF_, XF_, EPI_, R_) \
-  if (af == AF_ && xf == XF_ && epi == EPI_ && rpw == R_) { \
-    launch_kernel(k_gemv1<AF_, XF_, EPI_, R_>, grid, waves * 64, lds, s, a, items); \
+  const size_t lds = (size_t)tt * a.K * 4;
+#define G1(AF_, XF_, EPI_, R_, TT_) \
+  if (af == AF_ && xf == XF_ && epi == EPI_ && rpw == R_ && tt == TT_) { \
+    launch_kernel(k_gemv1<AF_, XF_, EPI_, R_, TT_>, grid, waves * 64, lds, s, a, items); \
     return hipGetLastError(); \
   }
-  G1(kA_F32, kX_BF16, kEpiStore, 1)
-  G1(kA_BF16, kX_BF16, kEpiStore, 1)
-  G1(kA_BF16, kX_PLANES, kEpiStoreScaled, 1)
-  G1(kA_BF16, kX_PLANES, kEpiStoreScaled, 2)
-  G1(kA_BF16, kX_BF16, kEpiGluAct, 2)
-  G1(kA_BF16, kX_F32, kEpiAdd, 2)
+  G1(kA_F32, kX_BF16, kEpiStore, 1, 1)
+  G1(kA_BF16, kX_BF16, kEpiStore, 1, 1)
+  G1(kA_BF16, kX_PLANES, kEpiStoreScaled, 1, 1)
+  G1(kA_BF16, kX_PLANES, kEpiStoreScaled, 2, 1)
+  G1(kA_BF16, kX_BF16, kEpiGluAct, 2, 1)
+  G1(kA_BF16, kX_F32, kEpiAdd, 2, 1)
+  G1(kA_BF16, kX_BF16, kEpiGluAct, 2, 2)
+  G1(kA_BF16, kX_F32, kEpiAdd, 2, 2)
 #undef G1
   return hipErrorInvalidValue;
 }

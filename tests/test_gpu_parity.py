@@ -515,7 +515,7 @@ def tiny_shared():
 
 
 @pytest.mark.parametrize("n_shared", [2, 4])
-@pytest.mark.parametrize("T", [1, 3, 64, 300])
+@pytest.mark.parametrize("T", [1, 2, 3, 64, 300])
 def test_tiny_shared_experts(tiny_shared, n_shared, T):
     d, sh, shd = tiny_shared
     say(f"tiny shared experts n_shared={n_shared} T={T}")
@@ -598,6 +598,12 @@ def layer_plus_shared(h: Host, sh, shd, x: np.ndarray, rows, what: str):
 def test_k3_layer_with_shared_T1(k3, k3_shared):
     x = k3gen.gen_x(k3.dims, 1, 1)
     layer_plus_shared(k3, *k3_shared, x, np.arange(1), "K3 T=1")
+
+
+def test_k3_layer_with_shared_T2(k3, k3_shared):
+    # two tokens: the shared experts' two-token GEMV form
+    x = k3gen.gen_x(k3.dims, 3, 2)
+    layer_plus_shared(k3, *k3_shared, x, np.arange(2), "K3 T=2")
 
 
 def test_k3_layer_with_shared_T64(k3, k3_shared):
