@@ -618,8 +618,11 @@ int run_combine(const k3moe_dims *d, int32_t T, const float *edn, const int32_t 
     }
     a.seg[0] = DenseSeg{w_up, 0, d->hidden, y, d->hidden};
     K3_HIP(launch_dense_mm(a, 2, kEpiStoreScaled, s));
-  } else if (use_gemv1(d, T, nullptr)) {
-    K3_HIP(launch_gemv1(up1_args(d, w_up, y, w), kA_BF16, kX_PLANES, kEpiStoreScaled, 2, s));
+  } else if (use_gemv1(d, T, nullptr) || (T == 2 && (int64_t)2 * d->latent * 4 <= 65536)) {
+    // one or two tokens on the vector ALUs (two: both against one weight stream)
+    Gemv1Args a = up1_args(d, w_up, y, w);
+    a.T = T;
+    K3_HIP(launch_gemv1(a, kA_BF16, kX_PLANES, kEpiStoreScaled, 2, s));
   } else {
     DenseArgs a = {};
     a.A = w_up;

@@ -45,9 +45,9 @@ __device__ __forceinline__ void stage_x(const Gemv1Args &a, float *sx) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) { v[2 * i] = bf_lo(w[i]); v[2 * i + 1] = bf_hi(w[i]); }
     } else {
-      const u32x4 b0 = *(const u32x4 *)(a.xp[0] + 8 * q);
-      const u32x4 b1 = *(const u32x4 *)(a.xp[1] + 8 * q);
-      const u32x4 b2 = *(const u32x4 *)(a.xp[2] + 8 * q);
+      const u32x4 b0 = *(const u32x4 *)(a.xp[0] + xo + 8 * q);
+      const u32x4 b1 = *(const u32x4 *)(a.xp[1] + xo + 8 * q);
+      const u32x4 b2 = *(const u32x4 *)(a.xp[2] + xo + 8 * q);
       const uint32_t w0[4] = {b0.x, b0.y, b0.z, b0.w}, w1[4] = {b1.x, b1.y, b1.z, b1.w},
                      w2[4] = {b2.x, b2.y, b2.z, b2.w};
       // the planes are the exact pieces of one fp32 value
@@ -62,14 +62,21 @@ __device__ __forceinline__ void stage_x(const Gemv1Args &a, float *sx) {
   }
 }
 
+// RMSNorm factor 1 / sqrt(mean(acc^2) + eps) of token t from its partial sums of squares
+__device__ __forceinline__ float rms_inv(const Gemv1Args &a, int t = 0) {
+  float ss = 0.f;
+  for (int i = 0; i < a.nss; ++i) ss += a.ss[(size_t)t * a.nss + i];
+  return 1.0f / sqrtf(ss / (float)a.K + a.eps);
+}
+
 // One wave item: rows row0 .. row0+RPW-1 over the columns of K part `part` (kEpiGluAct:
 // row row0 of A and of A2). The weight loads of the first batch are issued before the
 // block stages x (they do not depend on it); `staged` runs the staging and the block
 // barrier.
 template <int AF, int EPI, int RPW, int TT = 1, typename Stage>
 __device__ __forceinline__ void gemv1_item(const Gemv1Args &a, float *sx, int item, bool live, float scale,
-                                           Stage &&staged) {
-  static_assert(TT == 1 || EPI == kEpiGluAct || EPI == kEpiAdd, "two tokens: the shared-expert forms");
+                                           float scale1, Stage &&staged) {
+  static_assert(TT == 1 || EPI != kEpiStore, "two tokens: one K part (the token-major outputs)");
   constexpr int ESZ = AF == kA_F32 ? 4 : 2;
   constexpr int VPL = 16 / ESZ;  // weights per lane per load
   constexpr int NC = kG1MaxChunks / RPW;
@@ -165,17 +172,10 @@ __device__ __forceinline__ void gemv1_item(const Gemv1Args &a, float *sx, int it
       if (lane == 0 && row < a.M) {
         if constexpr (EPI == kEpiStore) out[(size_t)part * a.M + row] = v;
         else if constexpr (EPI == kEpiAdd) out[row] = out[row] + v;
-        else out[row] = v * scale;
+        else out[row] = v * (t == 0 ? scale : scale1);
       }
     }
   }
-}
-
-// RMSNorm factor 1 / sqrt(mean(acc^2) + eps) from the partial sums of squares
-__device__ __forceinline__ float rms_inv(const Gemv1Args &a) {
-  float ss = 0.f;
-  for (int i = 0; i < a.nss; ++i) ss += a.ss[i];
-  return 1.0f / sqrtf(ss / (float)a.K + a.eps);
 }
 
 template <int AF, int XF, int EPI, int RPW, int TT = 1>
@@ -185,8 +185,10 @@ __global__ __launch_bounds__(1024) void k_gemv1(Gemv1Args a, int items) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int item = blockIdx.x * (blockDim.x >> 6) + wave;
   const bool live = item < items;  // every wave takes part in the staging
+  // the RMSNorm factors (kEpiStoreScaled) of the launch's tokens
   const float scale = EPI == kEpiStoreScaled ? rms_inv(a) : 1.f;
-  gemv1_item<AF, EPI, RPW, TT>(a, sx, live ? item : 0, live, scale, [&] {
+  const float scale1 = (EPI == kEpiStoreScaled && TT == 2) ? rms_inv(a, 1) : 1.f;
+  gemv1_item<AF, EPI, RPW, TT>(a, sx, live ? item : 0, live, scale, scale1, [&] {
     stage_x<XF, TT>(a, sx);
     __syncthreads();
   });
@@ -207,10 +209,10 @@ __global__ __launch_bounds__(1024) void k_gemv1_front(Gemv1Args r, Gemv1Args d, 
     __syncthreads();
   };
   if (item < r_items) {
-    gemv1_item<kA_F32, kEpiStore, 2>(r, sx, item, true, 1.f, staged);
+    gemv1_item<kA_F32, kEpiStore, 2>(r, sx, item, true, 1.f, 1.f, staged);
   } else {
     const bool live = item < items;
-    gemv1_item<kA_BF16, kEpiStore, 2>(d, sx, live ? item - r_items : 0, live, 1.f, staged);
+    gemv1_item<kA_BF16, kEpiStore, 2>(d, sx, live ? item - r_items : 0, live, 1.f, 1.f, staged);
   }
 }
 
@@ -254,7 +256,7 @@ hipError_t launch_gemv1(const Gemv1Args &a, int af, int xf, int epi, int rpw, hi
   if ((epi == kEpiGluAct || epi == kEpiAdd || epi == kEpiStoreScaled) && a.ks != 1) return hipErrorInvalidValue;
   if (epi == kEpiGluAct && (rpw != 2 || !a.A2)) return hipErrorInvalidValue;
   const int tt = a.T == 2 ? 2 : 1;
-  if (tt == 2 && epi != kEpiGluAct && epi != kEpiAdd) return hipErrorInvalidValue;
+  if (tt == 2 && epi == kEpiStore) return hipErrorInvalidValue;
   const int items = (epi == kEpiGluAct ? a.M : (a.M + rpw - 1) / rpw) * a.ks;
   const int waves = gemv1_waves(items);
   const int grid = (items + waves - 1) / waves;
@@ -272,6 +274,7 @@ hipError_t launch_gemv1(const Gemv1Args &a, int af, int xf, int epi, int rpw, hi
   G1(kA_BF16, kX_F32, kEpiAdd, 2, 1)
   G1(kA_BF16, kX_BF16, kEpiGluAct, 2, 2)
   G1(kA_BF16, kX_F32, kEpiAdd, 2, 2)
+  G1(kA_BF16, kX_PLANES, kEpiStoreScaled, 2, 2)
 #undef G1
   return hipErrorInvalidValue;
 }

@@ -184,7 +184,7 @@ def test_tiny_layer_config0(tiny):
     compare_layer(tiny, x, what="tiny T=4")
 
 
-@pytest.mark.parametrize("T", [1, 3, 16, 64, 65, 129, 300])
+@pytest.mark.parametrize("T", [1, 2, 3, 16, 64, 65, 129, 300])
 def test_tiny_layer_ragged_T(tiny, T):
     say(f"tiny layer T={T}")
     x, _ = _inputs.gap_fixed_x(tiny.dims, 100 + T, T, tiny.dense["w_router"], tiny.dense["bias"])
@@ -358,6 +358,12 @@ def test_k3_stages_T1(k3):
 def test_k3_layer_config1_T1(k3):
     x, _ = _inputs.gap_fixed_x(k3.dims, 1, 1, k3.dense["w_router"], k3.dense["bias"])
     compare_layer(k3, x, what="K3 T=1")
+
+
+def test_k3_layer_T2(k3):
+    # two tokens: the up-projection's two-token GEMV form
+    x, _ = _inputs.gap_fixed_x(k3.dims, 6, 2, k3.dense["w_router"], k3.dense["bias"])
+    compare_layer(k3, x, what="K3 T=2")
 
 
 def test_k3_layer_config2_T64(k3):
