@@ -417,6 +417,21 @@ int run_front(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_wei
     K3_HIP(launch_topk(tk, s));
     mark("topk_dispatch_quant");
     *zq_ready = !d->idot;
+  } else if (T == 2 && (int64_t)2 * d->hidden * 4 <= 65536 && use_gemv1(d, 1, x)) {
+    // two tokens: the one-token front with both tokens against one weight stream, then
+    // the top-k (whose spare blocks quantize z) and the dispatch below
+    Gemv1Args r = router1_args(d, x, wt->w_router, w), dn = down1_args(d, x, wt->w_down, w.z32);
+    r.T = dn.T = 2;
+    K3_HIP(launch_gemv1_front(r, dn, s));
+    mark("router_and_latent_down");
+    TopkArgs tk = topk_args(d, T, w.router_part, kRouterParts1, wt->bias, idx, tw);
+    if (!d->idot) {
+      tk.z = w.z32;
+      tk.zq = w.zq;
+    }
+    K3_HIP(launch_topk(tk, s));
+    mark("topk");
+    *zq_ready = !d->idot;
   } else {
     // GEMV form: the router alone, then W_down streams while other blocks of the same
     // launch select the experts; z is quantized once afterwards

@@ -76,7 +76,7 @@ __device__ __forceinline__ float rms_inv(const Gemv1Args &a, int t = 0) {
 template <int AF, int EPI, int RPW, int TT = 1, typename Stage>
 __device__ __forceinline__ void gemv1_item(const Gemv1Args &a, float *sx, int item, bool live, float scale,
                                            float scale1, Stage &&staged) {
-  static_assert(TT == 1 || EPI != kEpiStore, "two tokens: one K part (the token-major outputs)");
+  // outputs: kEpiStore out[(part * TT + t) * M + row] (part-major), else out[t * M + row]
   constexpr int ESZ = AF == kA_F32 ? 4 : 2;
   constexpr int VPL = 16 / ESZ;  // weights per lane per load
   constexpr int NC = kG1MaxChunks / RPW;
@@ -159,7 +159,7 @@ __device__ __forceinline__ void gemv1_item(const Gemv1Args &a, float *sx, int it
   if (!live) return;
 #pragma unroll
   for (int t = 0; t < TT; ++t) {
-    float *out = a.out + (size_t)t * a.M;
+    float *out = a.out + (size_t)t * a.M + (EPI == kEpiStore ? (size_t)part * (TT - 1) * a.M : 0);
     if constexpr (GLU) {
       const float g = wave_sum_fixed(acc[t][0]), u = wave_sum_fixed(acc[t][1]);
       if (lane == 0 && row0 < a.M) out[row0] = situ(g, u, a.b1, a.b2);
@@ -199,20 +199,21 @@ __global__ __launch_bounds__(1024) void k_gemv1(Gemv1Args a, int items) {
 // pairs. The two kinds of item stream the same number of bytes. Every wave reaches
 // exactly one block barrier, inside the staging of whichever branch it takes (the branch
 // is uniform per wave).
+template <int TT>
 __global__ __launch_bounds__(1024) void k_gemv1_front(Gemv1Args r, Gemv1Args d, int r_items, int items) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   float *sx = (float *)smem;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int item = blockIdx.x * (blockDim.x >> 6) + wave;
   auto staged = [&] {
-    stage_x<kX_BF16>(d, sx);
+    stage_x<kX_BF16, TT>(d, sx);
     __syncthreads();
   };
   if (item < r_items) {
-    gemv1_item<kA_F32, kEpiStore, 2>(r, sx, item, true, 1.f, 1.f, staged);
+    gemv1_item<kA_F32, kEpiStore, 2, TT>(r, sx, item, true, 1.f, 1.f, staged);
   } else {
     const bool live = item < items;
-    gemv1_item<kA_BF16, kEpiStore, 2>(d, sx, live ? item - r_items : 0, live, 1.f, 1.f, staged);
+    gemv1_item<kA_BF16, kEpiStore, 2, TT>(d, sx, live ? item - r_items : 0, live, 1.f, 1.f, staged);
   }
 }
 
@@ -287,7 +288,13 @@ hipError_t launch_gemv1_front(const Gemv1Args &r, const Gemv1Args &d, hipStream_
   const int r_items = ((r.M + 1) / 2) * r.ks, items = r_items + (d.M + 1) / 2;
   const int waves = gemv1_waves(items);
   const int grid = (items + waves - 1) / waves;
-  launch_kernel(k_gemv1_front, grid, waves * 64, (size_t)d.K * 4, s, r, d, r_items, items);
+  // one or two tokens (both against one weight stream)
+  const int tt = r.T == 2 ? 2 : 1;
+  if ((d.T == 2 ? 2 : 1) != tt) return hipErrorInvalidValue;
+  if (tt == 2)
+    launch_kernel(k_gemv1_front<2>, grid, waves * 64, (size_t)2 * d.K * 4, s, r, d, r_items, items);
+  else
+    launch_kernel(k_gemv1_front<1>, grid, waves * 64, (size_t)d.K * 4, s, r, d, r_items, items);
   return hipGetLastError();
 }
 

@@ -402,7 +402,7 @@ def compare_topp(h: Host, p: float, T: int, seed: int, what: str):
 
 
 @pytest.mark.parametrize("p", [0.5, 0.8])
-@pytest.mark.parametrize("T", [1, 3, 64, 300])
+@pytest.mark.parametrize("T", [1, 2, 3, 64, 300])
 def test_tiny_topp_layer(tiny, p, T):
     ids = compare_topp(tiny, p, T, 20 + T, f"tiny top-p {p} T={T}")
     if T >= 64:
@@ -483,7 +483,7 @@ def compare_idot(h: Host, T: int, seed: int, what: str):
     assert np.median(gap) > 3e-3
 
 
-@pytest.mark.parametrize("T", [1, 3, 64, 300])
+@pytest.mark.parametrize("T", [1, 2, 3, 64, 300])
 def test_tiny_idot_layer(tiny, T):
     compare_idot(tiny, T, 120 + T, f"tiny int8 activations T={T}")
 
