@@ -151,3 +151,21 @@ def test_layer_workspace_size_grows_with_T():
             n = lib.k3moe_workspace_size(d, T)
             assert n >= prev, (d, T)
             prev = n
+
+
+def test_variant_fields_checked_on_the_host():
+    # the approximation switches are validated before anything runs (host-only size query)
+    import dataclasses
+    lib = k3moe
+    base = k3gen.TINY
+    assert lib.k3moe_workspace_size(dataclasses.replace(base, topp=0.7, idot=1), 4) > 0
+    for bad in (dict(topp=-0.1), dict(topp=float("nan")), dict(topp=float("inf")), dict(idot=2), dict(idot=-1)):
+        with pytest.raises(lib.K3MoeError) as e:
+            lib.k3moe_workspace_size(dataclasses.replace(base, **bad), 4)
+        assert e.value.status == lib.K3MOE_EINVAL, bad
+    # the shared experts' own checks
+    assert lib.k3moe_shared_workspace_size(base, 2, 5) > 0
+    for n_shared, T, code in ((0, 5, lib.K3MOE_EINVAL), (1, 5, lib.K3MOE_EUNSUPPORTED), (2, -1, lib.K3MOE_EINVAL)):
+        with pytest.raises(lib.K3MoeError) as e:
+            lib.k3moe_shared_workspace_size(base, n_shared, T)
+        assert e.value.status == code, (n_shared, T)
