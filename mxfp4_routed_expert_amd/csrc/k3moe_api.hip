@@ -671,10 +671,11 @@ int check_shared(const k3moe_dims *d, int32_t n_shared, int32_t T) {
   return (int)SI;
 }
 
-// One- and two-token form: both products' activations (all tokens) fit the GEMV's 64 KB
-// of LDS.
+// GEMV form for one to four tokens (all against one weight stream): both products'
+// activations, every token's, fit the GEMV's LDS (64 KB for one token, 128 KB for more).
 bool shared_gemv1(const k3moe_dims *d, int SI, int32_t T) {
-  return T >= 1 && T <= 2 && (int64_t)T * d->hidden * 4 <= 65536 && (int64_t)T * SI * 4 <= 65536;
+  const int64_t cap = T == 1 ? 65536 : 131072;
+  return T >= 1 && T <= 4 && (int64_t)T * d->hidden * 4 <= cap && (int64_t)T * SI * 4 <= cap;
 }
 
 struct ShWs {
@@ -705,7 +706,7 @@ ShWs carve_shared(const k3moe_dims *d, int SI, int32_t T, void *base) {
     for (int q = 0; q < 2; ++q) w.p[q] = (uint16_t *)take(t * si * 2);
     // (taken even where this T needs no parts: the size stays nondecreasing in T)
     w.dn = (float *)take((size_t)dense_mm_parts_max(H, SI, T) * (size_t)H * 4);
-    // two tokens in the GEMV form keep act [2][SI] at the start of the gate|up buffer
+    // two to four tokens in the GEMV form keep act [T][SI] at the start of the gate|up buffer
     w.act = w.gu;
   }
   w.bytes = o;

@@ -227,13 +227,33 @@ int gemv1_waves(int items) {
   return 16;
 }
 
+// LDS for the staged activations: 64 KB by default, up to 128 KB (one block per compute
+// unit) for three or four tokens
+constexpr size_t kG1MaxLds = 131072;
+
 bool gemv1_ok(const Gemv1Args &a, int esz) {
-  if (a.M <= 0 || a.K <= 0 || a.K % 8 != 0 || a.ks < 1 || a.K % a.ks != 0 || a.T > 2) return false;
+  if (a.M <= 0 || a.K <= 0 || a.K % 8 != 0 || a.ks < 1 || a.K % a.ks != 0 || a.T > 4) return false;
   const int kp = a.K / a.ks;
   const size_t tt = a.T > 1 ? (size_t)a.T : 1;
-  // 16-byte aligned row parts; every token's x fits the LDS
-  return ((size_t)kp * esz) % 16 == 0 && ((size_t)a.K * esz) % 16 == 0 && tt * a.K * 4 <= 65536 &&
-         ((size_t)a.M * a.K * esz) < ((size_t)1 << 40);
+  // 16-byte aligned row parts; every token's x fits the LDS (one token: 64 KB)
+  return ((size_t)kp * esz) % 16 == 0 && ((size_t)a.K * esz) % 16 == 0 &&
+         tt * a.K * 4 <= (tt == 1 ? (size_t)65536 : kG1MaxLds) && ((size_t)a.M * a.K * esz) < ((size_t)1 << 40);
+}
+
+// Launch with more than the default 64 KB of dynamic LDS allowed (once per kernel).
+template <int AF, int XF, int EPI, int RPW, int TT>
+hipError_t launch_gemv1_t(const Gemv1Args &a, int grid, int threads, size_t lds, int items, hipStream_t s) {
+  if (lds > 65536) {
+    static bool attr = false;
+    if (!attr) {
+      if (hipFuncSetAttribute((const void *)k_gemv1<AF, XF, EPI, RPW, TT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)kG1MaxLds) != hipSuccess)
+        return hipErrorInvalidValue;
+      attr = true;
+    }
+  }
+  launch_kernel(k_gemv1<AF, XF, EPI, RPW, TT>, grid, threads, lds, s, a, items);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -256,17 +276,15 @@ hipError_t launch_gemv1(const Gemv1Args &a, int af, int xf, int epi, int rpw, hi
   if (!gemv1_ok(a, af == kA_F32 ? 4 : 2) || (rpw != 1 && rpw != 2)) return hipErrorInvalidValue;
   if ((epi == kEpiGluAct || epi == kEpiAdd || epi == kEpiStoreScaled) && a.ks != 1) return hipErrorInvalidValue;
   if (epi == kEpiGluAct && (rpw != 2 || !a.A2)) return hipErrorInvalidValue;
-  const int tt = a.T == 2 ? 2 : 1;
-  if (tt == 2 && epi == kEpiStore) return hipErrorInvalidValue;
+  const int tt = a.T > 1 ? a.T : 1;
+  if (tt > 2 && epi != kEpiGluAct && epi != kEpiAdd) return hipErrorInvalidValue;
   const int items = (epi == kEpiGluAct ? a.M : (a.M + rpw - 1) / rpw) * a.ks;
   const int waves = gemv1_waves(items);
   const int grid = (items + waves - 1) / waves;
   const size_t lds = (size_t)tt * a.K * 4;
 #define G1(AF_, XF_, EPI_, R_, TT_) \
-  if (af == AF_ && xf == XF_ && epi == EPI_ && rpw == R_ && tt == TT_) { \
-    launch_kernel(k_gemv1<AF_, XF_, EPI_, R_, TT_>, grid, waves * 64, lds, s, a, items); \
-    return hipGetLastError(); \
-  }
+  if (af == AF_ && xf == XF_ && epi == EPI_ && rpw == R_ && tt == TT_) \
+    return launch_gemv1_t<AF_, XF_, EPI_, R_, TT_>(a, grid, waves * 64, lds, items, s);
   G1(kA_F32, kX_BF16, kEpiStore, 1, 1)
   G1(kA_BF16, kX_BF16, kEpiStore, 1, 1)
   G1(kA_BF16, kX_PLANES, kEpiStoreScaled, 1, 1)
@@ -275,14 +293,20 @@ hipError_t launch_gemv1(const Gemv1Args &a, int af, int xf, int epi, int rpw, hi
   G1(kA_BF16, kX_F32, kEpiAdd, 2, 1)
   G1(kA_BF16, kX_BF16, kEpiGluAct, 2, 2)
   G1(kA_BF16, kX_F32, kEpiAdd, 2, 2)
+  G1(kA_BF16, kX_BF16, kEpiGluAct, 2, 3)
+  G1(kA_BF16, kX_F32, kEpiAdd, 2, 3)
+  G1(kA_BF16, kX_BF16, kEpiGluAct, 2, 4)
+  G1(kA_BF16, kX_F32, kEpiAdd, 2, 4)
   G1(kA_BF16, kX_PLANES, kEpiStoreScaled, 2, 2)
 #undef G1
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemv1_front(const Gemv1Args &r, const Gemv1Args &d, hipStream_t s) {
-  // one x for both; the item kinds must stream the same bytes for the blocks to balance
-  if (!gemv1_ok(r, 4) || !gemv1_ok(d, 2) || r.K != d.K || r.xb != d.xb || d.ks != 1) return hipErrorInvalidValue;
+  // one x for both; the item kinds must stream the same bytes for the blocks to balance;
+  // one or two tokens
+  if (!gemv1_ok(r, 4) || !gemv1_ok(d, 2) || r.K != d.K || r.xb != d.xb || d.ks != 1 || r.T > 2 || d.T > 2)
+    return hipErrorInvalidValue;
   // two rows per wave item (28 KB of row bytes for both kinds): measured 0.6-0.8 us per
   // decode step faster than one row
   const int r_items = ((r.M + 1) / 2) * r.ks, items = r_items + (d.M + 1) / 2;

@@ -104,8 +104,9 @@ struct Gemv1Args {
   const void *A2;  // kEpiGluAct: the up rows
   const float *xf; // kX_F32
   float b1, b2;
-  int T;           // tokens (0 or 1: one; 2: two, ks = 1): token t's x at x + t * K, its
-                   // output at out + t * M, its sums of squares at ss + t * nss
+  int T;           // tokens (0 or 1: one; 2; 3 or 4 with kEpiGluAct / kEpiAdd): token t's x
+                   // at x + t * K, its output at out + t * M (kEpiStore: part-major), its sums
+                   // of squares at ss + t * nss
 };
 
 // ---------------------------------------------------------------- grouped MXFP4

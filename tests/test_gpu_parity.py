@@ -521,7 +521,7 @@ def tiny_shared():
 
 
 @pytest.mark.parametrize("n_shared", [2, 4])
-@pytest.mark.parametrize("T", [1, 2, 3, 64, 300])
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 64, 300])
 def test_tiny_shared_experts(tiny_shared, n_shared, T):
     d, sh, shd = tiny_shared
     say(f"tiny shared experts n_shared={n_shared} T={T}")
@@ -610,6 +610,12 @@ def test_k3_layer_with_shared_T2(k3, k3_shared):
     # two tokens: the shared experts' two-token GEMV form
     x = k3gen.gen_x(k3.dims, 3, 2)
     layer_plus_shared(k3, *k3_shared, x, np.arange(2), "K3 T=2")
+
+
+def test_k3_layer_with_shared_T4(k3, k3_shared):
+    # four tokens: the shared experts' GEMV form with 112 KB of staged activations
+    x = k3gen.gen_x(k3.dims, 4, 4)
+    layer_plus_shared(k3, *k3_shared, x, np.arange(4), "K3 T=4")
 
 
 def test_k3_layer_with_shared_T64(k3, k3_shared):
