@@ -419,9 +419,10 @@ int run_front(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_wei
     *zq_ready = !d->idot;
   } else if (T == 2 && (int64_t)2 * d->hidden * 4 <= 65536 && use_gemv1(d, 1, x)) {
     // two tokens: the one-token front with both tokens against one weight stream, then
-    // the top-k (whose spare blocks quantize z) and the dispatch below
+    // the top-k (whose spare blocks quantize z) and the dispatch below (three and four
+    // tokens this way measured no faster than the GEMV forms)
     Gemv1Args r = router1_args(d, x, wt->w_router, w), dn = down1_args(d, x, wt->w_down, w.z32);
-    r.T = dn.T = 2;
+    r.T = dn.T = T;
     K3_HIP(launch_gemv1_front(r, dn, s));
     mark("router_and_latent_down");
     TopkArgs tk = topk_args(d, T, w.router_part, kRouterParts1, wt->bias, idx, tw);
@@ -634,7 +635,8 @@ int run_combine(const k3moe_dims *d, int32_t T, const float *edn, const int32_t 
     a.seg[0] = DenseSeg{w_up, 0, d->hidden, y, d->hidden};
     K3_HIP(launch_dense_mm(a, 2, kEpiStoreScaled, s));
   } else if (use_gemv1(d, T, nullptr) || (T == 2 && (int64_t)2 * d->latent * 4 <= 65536)) {
-    // one or two tokens on the vector ALUs (two: both against one weight stream)
+    // one or two tokens on the vector ALUs (both against one weight stream; three and
+    // four this way measured slower than the dense GEMV form: 17.5 against 16.7 us)
     Gemv1Args a = up1_args(d, w_up, y, w);
     a.T = T;
     K3_HIP(launch_gemv1(a, kA_BF16, kX_PLANES, kEpiStoreScaled, 2, s));

@@ -19,6 +19,7 @@ namespace k3 {
 namespace {
 
 constexpr int kG1MaxChunks = 16;  // 1 KB loads in flight per wave
+__device__ constexpr float kOnes[4] = {1.f, 1.f, 1.f, 1.f};  // unscaled epilogues
 
 // bf16 bits -> fp32 (exact)
 __device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
@@ -74,8 +75,8 @@ __device__ __forceinline__ float rms_inv(const Gemv1Args &a, int t = 0) {
 // block stages x (they do not depend on it); `staged` runs the staging and the block
 // barrier.
 template <int AF, int EPI, int RPW, int TT = 1, typename Stage>
-__device__ __forceinline__ void gemv1_item(const Gemv1Args &a, float *sx, int item, bool live, float scale,
-                                           float scale1, Stage &&staged) {
+__device__ __forceinline__ void gemv1_item(const Gemv1Args &a, float *sx, int item, bool live,
+                                           const float (&scale)[4], Stage &&staged) {
   // outputs: kEpiStore out[(part * TT + t) * M + row] (part-major), else out[t * M + row]
   constexpr int ESZ = AF == kA_F32 ? 4 : 2;
   constexpr int VPL = 16 / ESZ;  // weights per lane per load
@@ -172,7 +173,7 @@ __device__ __forceinline__ void gemv1_item(const Gemv1Args &a, float *sx, int it
       if (lane == 0 && row < a.M) {
         if constexpr (EPI == kEpiStore) out[(size_t)part * a.M + row] = v;
         else if constexpr (EPI == kEpiAdd) out[row] = out[row] + v;
-        else out[row] = v * (t == 0 ? scale : scale1);
+        else out[row] = v * scale[t];
       }
     }
   }
@@ -186,9 +187,12 @@ __global__ __launch_bounds__(1024) void k_gemv1(Gemv1Args a, int items) {
   const int item = blockIdx.x * (blockDim.x >> 6) + wave;
   const bool live = item < items;  // every wave takes part in the staging
   // the RMSNorm factors (kEpiStoreScaled) of the launch's tokens
-  const float scale = EPI == kEpiStoreScaled ? rms_inv(a) : 1.f;
-  const float scale1 = (EPI == kEpiStoreScaled && TT == 2) ? rms_inv(a, 1) : 1.f;
-  gemv1_item<AF, EPI, RPW, TT>(a, sx, live ? item : 0, live, scale, scale1, [&] {
+  float scale[4] = {1.f, 1.f, 1.f, 1.f};
+  if constexpr (EPI == kEpiStoreScaled) {
+#pragma unroll
+    for (int t = 0; t < TT; ++t) scale[t] = rms_inv(a, t);
+  }
+  gemv1_item<AF, EPI, RPW, TT>(a, sx, live ? item : 0, live, scale, [&] {
     stage_x<XF, TT>(a, sx);
     __syncthreads();
   });
@@ -210,10 +214,10 @@ __global__ __launch_bounds__(1024) void k_gemv1_front(Gemv1Args r, Gemv1Args d, 
     __syncthreads();
   };
   if (item < r_items) {
-    gemv1_item<kA_F32, kEpiStore, 2, TT>(r, sx, item, true, 1.f, 1.f, staged);
+    gemv1_item<kA_F32, kEpiStore, 2, TT>(r, sx, item, true, kOnes, staged);
   } else {
     const bool live = item < items;
-    gemv1_item<kA_BF16, kEpiStore, 2, TT>(d, sx, live ? item - r_items : 0, live, 1.f, 1.f, staged);
+    gemv1_item<kA_BF16, kEpiStore, 2, TT>(d, sx, live ? item - r_items : 0, live, kOnes, staged);
   }
 }
 
@@ -277,7 +281,7 @@ hipError_t launch_gemv1(const Gemv1Args &a, int af, int xf, int epi, int rpw, hi
   if ((epi == kEpiGluAct || epi == kEpiAdd || epi == kEpiStoreScaled) && a.ks != 1) return hipErrorInvalidValue;
   if (epi == kEpiGluAct && (rpw != 2 || !a.A2)) return hipErrorInvalidValue;
   const int tt = a.T > 1 ? a.T : 1;
-  if (tt > 2 && epi != kEpiGluAct && epi != kEpiAdd) return hipErrorInvalidValue;
+  if (tt > 1 && epi == kEpiStore) return hipErrorInvalidValue;
   const int items = (epi == kEpiGluAct ? a.M : (a.M + rpw - 1) / rpw) * a.ks;
   const int waves = gemv1_waves(items);
   const int grid = (items + waves - 1) / waves;
@@ -302,24 +306,41 @@ hipError_t launch_gemv1(const Gemv1Args &a, int af, int xf, int epi, int rpw, hi
   return hipErrorInvalidValue;
 }
 
+template <int TT>
+hipError_t launch_front_t(const Gemv1Args &r, const Gemv1Args &d, int r_items, int items, int grid, int threads,
+                          size_t lds, hipStream_t s) {
+  if (lds > 65536) {
+    static bool attr = false;
+    if (!attr) {
+      if (hipFuncSetAttribute((const void *)k_gemv1_front<TT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)kG1MaxLds) != hipSuccess)
+        return hipErrorInvalidValue;
+      attr = true;
+    }
+  }
+  launch_kernel(k_gemv1_front<TT>, grid, threads, lds, s, r, d, r_items, items);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemv1_front(const Gemv1Args &r, const Gemv1Args &d, hipStream_t s) {
   // one x for both; the item kinds must stream the same bytes for the blocks to balance;
-  // one or two tokens
-  if (!gemv1_ok(r, 4) || !gemv1_ok(d, 2) || r.K != d.K || r.xb != d.xb || d.ks != 1 || r.T > 2 || d.T > 2)
+  // one to four tokens
+  if (!gemv1_ok(r, 4) || !gemv1_ok(d, 2) || r.K != d.K || r.xb != d.xb || d.ks != 1 || r.T != d.T)
     return hipErrorInvalidValue;
   // two rows per wave item (28 KB of row bytes for both kinds): measured 0.6-0.8 us per
   // decode step faster than one row
   const int r_items = ((r.M + 1) / 2) * r.ks, items = r_items + (d.M + 1) / 2;
   const int waves = gemv1_waves(items);
   const int grid = (items + waves - 1) / waves;
-  // one or two tokens (both against one weight stream)
-  const int tt = r.T == 2 ? 2 : 1;
-  if ((d.T == 2 ? 2 : 1) != tt) return hipErrorInvalidValue;
-  if (tt == 2)
-    launch_kernel(k_gemv1_front<2>, grid, waves * 64, (size_t)2 * d.K * 4, s, r, d, r_items, items);
-  else
-    launch_kernel(k_gemv1_front<1>, grid, waves * 64, (size_t)d.K * 4, s, r, d, r_items, items);
-  return hipGetLastError();
+  // one or two tokens, both against one weight stream (three and four, with 84 and 112
+  // KB of staged x and one block per compute unit, measured no faster than the GEMV forms)
+  const int tt = r.T > 1 ? r.T : 1;
+  const size_t lds = (size_t)tt * d.K * 4;
+  switch (tt) {
+    case 1: return launch_front_t<1>(r, d, r_items, items, grid, waves * 64, lds, s);
+    case 2: return launch_front_t<2>(r, d, r_items, items, grid, waves * 64, lds, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace k3

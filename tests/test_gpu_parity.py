@@ -184,7 +184,7 @@ def test_tiny_layer_config0(tiny):
     compare_layer(tiny, x, what="tiny T=4")
 
 
-@pytest.mark.parametrize("T", [1, 2, 3, 16, 64, 65, 129, 300])
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 16, 64, 65, 129, 300])
 def test_tiny_layer_ragged_T(tiny, T):
     say(f"tiny layer T={T}")
     x, _ = _inputs.gap_fixed_x(tiny.dims, 100 + T, T, tiny.dense["w_router"], tiny.dense["bias"])
@@ -360,10 +360,12 @@ def test_k3_layer_config1_T1(k3):
     compare_layer(k3, x, what="K3 T=1")
 
 
-def test_k3_layer_T2(k3):
-    # two tokens: the up-projection's two-token GEMV form
-    x, _ = _inputs.gap_fixed_x(k3.dims, 6, 2, k3.dense["w_router"], k3.dense["bias"])
-    compare_layer(k3, x, what="K3 T=2")
+@pytest.mark.parametrize("T", [2, 3, 4])
+def test_k3_layer_few_tokens(k3, T):
+    # two to four tokens: the front and the up-projection take every token against one
+    # weight stream (three and four: 84 and 112 KB of staged activations)
+    x, _ = _inputs.gap_fixed_x(k3.dims, 6 + T, T, k3.dense["w_router"], k3.dense["bias"])
+    compare_layer(k3, x, what=f"K3 T={T}")
 
 
 def test_k3_layer_config2_T64(k3):
