@@ -60,6 +60,10 @@
  *    32; latent, inter <= 8192; latent * hidden < 2^30 and n_experts * hidden < 2^29; group == 32; topk <= 32 and topk <= n_experts <= 1024; T >= 0 (T == 0 is a
  *    no-op); T * topk < 2^31. Scale bytes 2..254 and 255 are exact on the GPU path;
  *    0 and 1 give weights below 2^-126, which the matrix cores may flush to zero.
+ *  - Threads: entry points keep no state between calls and may be called from several
+ *    host threads at once, each call with its own workspace (calls that share a
+ *    workspace must be ordered on one stream). The only per-process state is each
+ *    kernel's dynamic-LDS attribute, set once per device on first use.
  *  - Errors: every call returns K3MOE_OK (0) or a negative code. All argument
  *    checks happen on the host before any launch, so a refused call has launched
  *    nothing; on K3MOE_EHIP the outputs are unspecified. Nothing prints or aborts.

@@ -19,7 +19,9 @@ extern "C" {
  * gaps around it. Launches beyond max_events / 2 (at most 64) run untimed. *n_kernels
  * receives the number of timed launches; k3moe_prof_name(i) names the step launch i
  * belongs to (static storage; a step such as the dispatch may take several launches).
- * Not reentrant: one profiled call at a time per process. */
+ * The binding of events to launches is per host thread: a profiled call times the
+ * launches its own thread makes, and plain calls on other threads meanwhile take no
+ * events. k3moe_prof_name reads the calling thread's last profiled call. */
 int k3moe_layer_profiled(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_weights *w,
                          float *y, int32_t *topk_idx_out, float *topk_w_out, void *ws, size_t ws_bytes,
                          void *stream, void **events, int max_events, int *n_kernels);
@@ -31,14 +33,14 @@ int k3moe_shared_profiled(const k3moe_dims *d, int32_t n_shared, int32_t T, cons
                           void *ws, size_t ws_bytes, void *stream, void **events, int max_events,
                           int *n_kernels);
 
-/* Which kernels run the expert passes, for tests and measurement that compare the two
- * forms on the same inputs: 0 = by batch size (the default: the grouped GEMM form when
- * the batch averages at least two token-expert pairs per expert), 1 = always the
- * grouped GEMV form, 2 = the grouped GEMM form wherever its shape limits allow (the
- * pass's K a multiple of 128 and its activation records under 2 GiB). Both forms give
- * the same result up to fp32 summation order. Process-wide, not synchronised with calls
- * in flight on other threads. Returns the previous mode, or K3MOE_EINVAL for another
- * value. */
+/* TESTS AND MEASUREMENT ONLY. Which kernels run the expert passes, for tests and
+ * measurement that compare the two forms on the same inputs: 0 = by batch size (the
+ * default: the grouped GEMM form when the batch averages at least two token-expert pairs
+ * per expert), 1 = always the grouped GEMV form, 2 = the grouped GEMM form wherever its
+ * shape limits allow (the pass's K a multiple of 128 and its activation records under
+ * 2 GiB). Both forms give the same result up to fp32 summation order. The mode is per
+ * host thread: it applies to the later calls of the thread that set it and to no other
+ * thread's. Returns the thread's previous mode, or K3MOE_EINVAL for another value. */
 int k3moe_set_expert_path(int mode);
 
 #ifdef __cplusplus

@@ -22,16 +22,28 @@ FLAGS = [
 
 
 def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *srcs, "-o", tmp]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    out = r.stdout + r.stderr
+    """Compile every source to an object in parallel, then link the shared library."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
     # the host pass does not know the device feature flag; that notice is expected
     noise = "is not a recognized feature for this target"
-    msgs = [l for l in out.splitlines() if noise not in l]
-    if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+
+    def run(cmd):
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        msgs = [l for l in (r.stdout + r.stderr).splitlines() if noise not in l]
+        if r.returncode != 0:
+            raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+        return msgs
+
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+    objs = [os.path.join(objdir, s.replace(".hip", ".o")) for s in SOURCES]
+    jobs = [[HIPCC, *compile_flags, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+    with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1)) as ex:
+        msgs = [m for ms in ex.map(run, jobs) for m in ms]
+    tmp = LIB + ".tmp"
+    msgs += run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
     if verbose and msgs:
         print("\n".join(msgs), file=sys.stderr)
     os.replace(tmp, LIB)

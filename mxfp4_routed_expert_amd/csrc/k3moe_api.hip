@@ -12,7 +12,7 @@
 
 using namespace k3;
 
-k3::LaunchTimes k3::g_launch_times;
+thread_local k3::LaunchTimes k3::g_launch_times;
 
 namespace {
 
@@ -81,7 +81,9 @@ struct Ws {
   size_t bytes;
 };
 
-int g_expert_path = 0;  // k3moe_set_expert_path
+// k3moe_set_expert_path (tests and measurement only): per host thread, so that a test
+// forcing one form never changes the calls of another thread
+thread_local int g_expert_path = 0;
 
 
 // The GEMM form reads its token planes through one 32-bit buffer descriptor: x [T][H]
@@ -185,7 +187,7 @@ struct ProfNames {
   int named = 0;
   const char *names[kMaxProfLaunches];
 };
-ProfNames g_prof;
+thread_local ProfNames g_prof;  // the calling thread's last profiled call
 
 void mark(const char *name) {
   if (!g_launch_times.events) return;
@@ -698,7 +700,9 @@ ShWs carve_shared(const k3moe_dims *d, int SI, int32_t T, void *base) {
     return (void *)p;
   };
   const size_t t = (size_t)T, si = (size_t)SI;
-  if (T <= 1) {
+  // the buffers of the form run_shared takes: one token in the GEMV form needs act only;
+  // a shape too wide for the GEMV form takes the GEMM form even at one token
+  if (T <= 1 && shared_gemv1(d, SI, 1)) {
     w.act = (float *)take(si * 4);
   } else {
     // sized for the largest K-part count any batch up to T uses, so that a workspace

@@ -63,20 +63,29 @@ __device__ __forceinline__ float wave_sum_fixed(float x) {
           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48)));
 }
 
-// Raw buffer loads: a uniform base and size (an SGPR descriptor) plus 32-bit per-lane
-// and uniform offsets. An access past the size returns zeros instead of faulting, so
-// masked lanes load branch-free by pointing past the end (kOOB).
+// Raw buffer loads: a uniform base and size (an SGPR descriptor) plus a 32-bit per-lane
+// offset. An access whose lane offset lies past the size returns zeros instead of
+// reaching memory, so masked lanes load branch-free by pointing past the end (kOOB).
+// The range check of a raw buffer access covers the lane (VGPR) offset and the
+// instruction's immediate offset only; the uniform SGPR offset is added to the address
+// after the check (LLVM's AMDGPU raw buffer intrinsics document soffset as excluded from
+// bounds checking). So every load here passes its whole offset in the lane operand and 0
+// as soffset: each access is checked against the descriptor's size as a whole.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
-constexpr uint32_t kOOB = 0x80000000u;
+constexpr uint32_t kOOB = 0x80000000u;  // above every descriptor size used (< 2^31)
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
-__device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+__device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
-__device__ __forceinline__ uint32_t bload8(rsrc_t r, uint32_t voff, uint32_t soff) {
-  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
+__device__ __forceinline__ uint32_t bload8(rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+}
+// 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at lds + 16 l
+__device__ __forceinline__ void dma16(rsrc_t r, uint8_t *lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, off, 0, 0, 0);
 }
 constexpr int kGroup = 32;  // MXFP4 group: 32 columns share one ue8m0 scale
 

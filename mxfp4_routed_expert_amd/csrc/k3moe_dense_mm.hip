@@ -32,11 +32,6 @@ constexpr int kDmStages = K3_DM_STAGES;
 
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-__device__ __forceinline__ void dma16(rsrc_t r, uint8_t *lds, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voff,
-                                           soff, 0, 0);
-}
-
 template <int N_OUTSTANDING>
 __device__ __forceinline__ void wait_ring_barrier() {
   asm volatile("" ::: "memory");
@@ -116,16 +111,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   struct AStep {
     u32x4 v[4];
   };
+  // (rows past the segment and steps past the part read zeros: their offsets lie past
+  // the descriptors' sizes)
   auto aload = [&](int S, AStep &s) {
-    const uint32_t so = S < nsteps ? (uint32_t)(s_lo + S) * 64u : kOOB;
+    const bool ok = S < nsteps;
+    const uint32_t so = (uint32_t)(s_lo + S) * 64u;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s.v[i] = bload16(rA, aoff[i], so);
+    for (int i = 0; i < 4; ++i) s.v[i] = bload16(rA, ok ? aoff[i] + so : kOOB);
   };
   auto issue = [&](int S, int st) {
     uint8_t *base = smem + st * STAGE;
-    const uint32_t so = S < nsteps ? (uint32_t)(s_lo + S) * 64u : kOOB;
+    const bool ok = S < nsteps;
+    const uint32_t so = (uint32_t)(s_lo + S) * 64u;
 #pragma unroll
-    for (int u = 0; u < DMA_PER_WAVE; ++u) dma16(rB, base + (wave + 4 * u) * 1024, boff[u], so);
+    for (int u = 0; u < DMA_PER_WAVE; ++u) dma16(rB, base + (wave + 4 * u) * 1024, ok ? boff[u] + so : kOOB);
   };
 
   f32x4 acc[4][NJ];

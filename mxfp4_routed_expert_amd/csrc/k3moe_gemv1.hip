@@ -107,7 +107,7 @@ __device__ __forceinline__ void gemv1_item(const Gemv1Args &a, float *sx, int it
     for (int r = 0; r < RPW; ++r)
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        w[r][c] = bload16(rA[r], (uint32_t)lane * 16u, c0 + c < nchunk ? (uint32_t)(c0 + c) * 1024u : kOOB);
+        w[r][c] = bload16(rA[r], c0 + c < nchunk ? (uint32_t)(c0 + c) * 1024u + (uint32_t)lane * 16u : kOOB);
   };
   float acc[TT][RPW];
 #pragma unroll
@@ -248,13 +248,7 @@ bool gemv1_ok(const Gemv1Args &a, int esz) {
 template <int AF, int XF, int EPI, int RPW, int TT>
 hipError_t launch_gemv1_t(const Gemv1Args &a, int grid, int threads, size_t lds, int items, hipStream_t s) {
   if (lds > 65536) {
-    static bool attr = false;
-    if (!attr) {
-      if (hipFuncSetAttribute((const void *)k_gemv1<AF, XF, EPI, RPW, TT>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)kG1MaxLds) != hipSuccess)
-        return hipErrorInvalidValue;
-      attr = true;
-    }
+    if (lds_limit_once<k_gemv1<AF, XF, EPI, RPW, TT>>((int)kG1MaxLds) != hipSuccess) return hipErrorInvalidValue;
   }
   launch_kernel(k_gemv1<AF, XF, EPI, RPW, TT>, grid, threads, lds, s, a, items);
   return hipGetLastError();
@@ -310,13 +304,7 @@ template <int TT>
 hipError_t launch_front_t(const Gemv1Args &r, const Gemv1Args &d, int r_items, int items, int grid, int threads,
                           size_t lds, hipStream_t s) {
   if (lds > 65536) {
-    static bool attr = false;
-    if (!attr) {
-      if (hipFuncSetAttribute((const void *)k_gemv1_front<TT>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)kG1MaxLds) != hipSuccess)
-        return hipErrorInvalidValue;
-      attr = true;
-    }
+    if (lds_limit_once<k_gemv1_front<TT>>((int)kG1MaxLds) != hipSuccess) return hipErrorInvalidValue;
   }
   launch_kernel(k_gemv1_front<TT>, grid, threads, lds, s, r, d, r_items, items);
   return hipGetLastError();

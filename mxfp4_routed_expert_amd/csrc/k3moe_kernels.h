@@ -5,19 +5,22 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace k3 {
 
 // ---------------------------------------------------------------- launches
 // Per-kernel timing for profiled layer calls: while `events` is set, each launch made
 // through launch_kernel takes the next (start, stop) pair of caller-created events,
 // which the runtime binds to that kernel's own begin and end; otherwise (and once the
-// pairs run out) launches are plain. Host-side state, one profiled call at a time.
+// pairs run out) launches are plain. The state is per host thread: a profiled call
+// times only the launches its own thread makes, and calls on other threads are unaffected.
 struct LaunchTimes {
   void **events = nullptr;  // events[2 i], events[2 i + 1]: launch i
   int max_launches = 0;
   int n = 0;                // launches timed so far
 };
-extern LaunchTimes g_launch_times;
+extern thread_local LaunchTimes g_launch_times;
 
 template <typename... P, typename... A>
 inline void launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t s,
@@ -30,6 +33,20 @@ inline void launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, size_t ld
   } else {
     kernel<<<grid, block, lds, s>>>(args...);
   }
+}
+
+// Raise a kernel's dynamic LDS limit above the 64 KB default. The attribute belongs to
+// the device current when it is set, so it is set once per device (64 at most).
+template <auto Kernel>
+inline hipError_t lds_limit_once(int bytes) {
+  static std::atomic<uint64_t> done{0};  // bit d: set on device d
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  const uint64_t bit = (uint64_t)1 << dev;
+  if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute((const void *)Kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.fetch_or(bit, std::memory_order_release);
+  return e;
 }
 
 constexpr int kMaxRouterSplits = 8;  // partial router products summed by the top-k

@@ -1,16 +1,22 @@
-// HIP kernels of the k3moe library, written for gfx950 (MI355X, CDNA4).
+// HIP kernels of the k3moe library, written for gfx950 (MI355X, CDNA4): the dense
+// products of small batches (router and latent projection, up-projection) on the bf16
+// matrix cores, the grouped MXFP4 expert GEMV of decode, the dispatch, the fp6
+// quantizers of the expert activations and the combine.
 //
-// Matrix products run on the bf16 matrix cores (16x16x32 MFMA). Weights enter as bf16
-// (W_down, W_up), as fp32 split into three bf16 pieces (router), or as MXFP4 decoded in
-// registers to bf16 (experts): e2m1 * 2^k has two significant bits, so the decode is
-// exact. fp32 activations enter as bf16 pieces whose sum is the fp32 value, so the
-// products are exact and only the fp32 accumulation rounds.
+// Dense products (dense_body): bf16 weights (W_down, W_up), or the router's fp32 weights
+// split into three bf16 pieces, on 16x16x32 bf16 MFMA; fp32 activations enter as bf16
+// pieces whose sum is the fp32 value, so every product is exact and only the fp32
+// accumulation rounds. K order inside a wave: lane l = 16 * kq + r handles row r of A
+// and column r of B; in each 128-column step lane group kq holds one 32-column group
+// and its four 8-column sub-steps feed four MFMAs. Any assignment of columns to (lane
+// group, sub-step) gives the same sum as long as A and B use the same one; this one makes
+// every lane's loads 16..128 contiguous bytes.
 //
-// K (reduction) order inside a wave: lane l = 16 * kq + r handles row r of A and
-// column r of B; in each 128-column super-step lane group kq holds one 32-column MXFP4
-// group (one scale byte), and the four 8-column sub-steps of that group feed four MFMAs.
-// Any assignment of columns to (lane group, sub-step) gives the same sum as long as A
-// and B use the same one; this one makes every lane's loads 16..128 contiguous bytes.
+// Expert products (k_grouped_dec): the MXFP4 weights go to the gfx950 scaled matrix core
+// as stored (e2m1 codes with their ue8m0 group scale), against the activations as four
+// e2m3 (fp6) pieces per 32-value group, each with its own power-of-two scale
+// (v_mfma_scale_f32_16x16x128_f8f6f4); the pieces carry the fp32 activation to 2^-20 of
+// its group maximum, and the products are exact.
 #include "k3moe_common.h"
 #include "k3moe_kernels.h"
 #include "k3moe_topk.h"
@@ -63,10 +69,9 @@ __device__ __forceinline__ void dense_body(const DenseArgs &a, int rbk, int ks, 
   auto load = [&](int S, Step &st) {
     const bool in = S < w_hi;
     const bool gok = in && ((S < nsup - 1) || (kq < last_ok));
-    const uint32_t va = gok ? aoff : kOOB;
     const uint32_t sa = (in ? (uint32_t)S : 0u) * 4u * kGroup * ESZ;
 #pragma unroll
-    for (int i = 0; i < NRAW; ++i) st.a[i] = bload16(rA, va + 16u * i, sa);
+    for (int i = 0; i < NRAW; ++i) st.a[i] = bload16(rA, gok ? aoff + sa + 16u * i : kOOB);
     st.bv = bok && gok;
     const u32x4 *p = (const u32x4 *)(brow + (size_t)(gok ? S : 0) * 4 * kGroup);
 #pragma unroll
@@ -537,10 +542,6 @@ __device__ __forceinline__ void stage16(uint8_t *dst, const uint8_t *src, int nb
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 // 16 bytes per lane from a buffer into LDS at lds + 16 * lane (an LDS-destination load)
-__device__ __forceinline__ void dma16(rsrc_t r, uint8_t *lds, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voff,
-                                           soff, 0, 0);
-}
 
 // ============================================================== grouped MXFP4 (decode)
 // Grid: x = blocks of RB 16-row blocks, y = active-expert slots. The block's four waves
@@ -665,10 +666,10 @@ __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
   // descriptor; the k-blocks they would form are masked by their activations (zeros).
   u32x4 w[NL];
   auto load_block = [&](int S, int r) {
-    const uint32_t Sc = (S < s_hi) ? (uint32_t)S * 128u : kOOB;
+    const bool ok = S < s_hi;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-      w[2 * r + h] = bload16(rA, lv, Sc == kOOB ? kOOB : Sc + (uint32_t)(2 * r + h) * 8u * rowb);
+      w[2 * r + h] = bload16(rA, ok ? lv + (uint32_t)S * 128u + (uint32_t)(2 * r + h) * 8u * rowb : kOOB);
   };
   auto load = [&](int S) {
 #pragma unroll
@@ -706,7 +707,7 @@ __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
     for (int i = wave; i < NA * nsc; i += 4) {
       const int m = i / nsc, c = i - m * nsc;
       const rsrc_t rS = make_rsrc(a.A[m].scales + (size_t)e * a.A[m].sstride + (size_t)row0 * ng, (uint32_t)nb);
-      dma16(rS, sS + m * ROWS * (int)ng + c * 1024, (uint32_t)lane * 16u, (uint32_t)c * 1024u);
+      dma16(rS, sS + m * ROWS * (int)ng + c * 1024, (uint32_t)c * 1024u + (uint32_t)lane * 16u);
     }
     for (int i = wave; i < (RT ? 0 : ntok0 * nbc); i += 4) {
       const int tt = i / nbc, c = i - tt * nbc;
@@ -714,7 +715,7 @@ __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
 #pragma unroll
       for (int u = 1; u < TT; ++u) br = tt == u ? brow0[u] : br;
       const rsrc_t rB = make_rsrc(a.Bq + (size_t)br * brow_bytes, (uint32_t)brow_bytes);
-      dma16(rB, sB + tt * brow_bytes + c * 1024, (uint32_t)lane * 16u, (uint32_t)c * 1024u);
+      dma16(rB, sB + tt * brow_bytes + c * 1024, (uint32_t)c * 1024u + (uint32_t)lane * 16u);
     }
   }
   asm volatile("" ::: "memory");
@@ -868,13 +869,8 @@ size_t grouped_dec_lds(int K, int tt, int rb) {
 
 template <int NA, int TT, int EPI, int RT, int RB>
 static hipError_t launch_grouped_t(const GroupedArgs &a, dim3 grid, size_t lds, hipStream_t s) {
-  static bool attr = false;  // allow up to kMaxBlockLds of dynamic LDS (above the 64 KB default)
-  if (!attr) {
-    if (hipFuncSetAttribute((const void *)k_grouped_dec<NA, TT, EPI, RT, RB>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxBlockLds) != hipSuccess)
-      return hipErrorInvalidValue;
-    attr = true;
-  }
+  // allow up to kMaxBlockLds of dynamic LDS (above the 64 KB default)
+  if (lds_limit_once<k_grouped_dec<NA, TT, EPI, RT, RB>>((int)kMaxBlockLds) != hipSuccess) return hipErrorInvalidValue;
   launch_kernel(k_grouped_dec<NA, TT, EPI, RT, RB>, grid, 256, lds, s, a);
   return hipGetLastError();
 }

@@ -53,11 +53,6 @@ __device__ __forceinline__ void wait_ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
-__device__ __forceinline__ void dma16(rsrc_t r, uint8_t *lds, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voff,
-                                           soff, 0, 0);
-}
-
 typedef unsigned u32x3 __attribute__((ext_vector_type(3)));
 
 }  // namespace
@@ -81,8 +76,8 @@ struct IC {
   static constexpr int value = N;
 };
 
-__device__ __forceinline__ u32x3 bload12(rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(u32x3, __builtin_amdgcn_raw_buffer_load_b96(r, voff, soff, 0));
+__device__ __forceinline__ u32x3 bload12(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x3, __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0));
 }
 
 // The scaled matrix-core step with the A scale taken from byte SEL of sa (the instruction's
@@ -156,9 +151,14 @@ void k_grouped_mm(MmArgs a) {
     rA[m] = make_rsrc(a.A[m].packed + (size_t)e * a.A[m].pstride + (size_t)rw0 * rowb, (uint32_t)nrw * rowb);
     rS[m] = make_rsrc(a.A[m].scales + (size_t)e * a.A[m].sstride + (size_t)rw0 * ng, (uint32_t)nrw * ng);
   }
-  // lane part of the offsets; a fragment's 16-row offset is uniform and rides in soffset
-  const uint32_t aoff = (uint32_t)lrow * rowb + (uint32_t)kq * 16u;
-  const uint32_t soff = (uint32_t)lrow * ng;
+  // each fragment's lane offsets into the wave's rows (packed bytes, scale bytes); rows
+  // past the matrix lie past the descriptors' sizes and read as zeros
+  uint32_t aoff[FPM], soff[FPM];
+#pragma unroll
+  for (int f = 0; f < FPM; ++f) {
+    aoff[f] = (uint32_t)(frow(f) + lrow) * rowb + (uint32_t)kq * 16u;
+    soff[f] = (uint32_t)(frow(f) + lrow) * ng;
+  }
 
   // ---- token copies: wave w issues copies DPW*w .. DPW*w+DPW-1; copy j moves tokens 2j
   // (lanes 0-31) and 2j+1 (lanes 32-63), lane slot i of token t holding its 16-byte chunk
@@ -190,12 +190,13 @@ void k_grouped_mm(MmArgs a) {
     const bool ok = S < nsteps;
 #pragma unroll
     for (int i = part * NF / 4; i < (part + 1) * NF / 4; ++i)
-      as.v[i] = bload16(rA[i / FPM], aoff, ok ? (uint32_t)S * 64u + (uint32_t)frow(i % FPM) * rowb : kOOB);
+      as.v[i] = bload16(rA[i / FPM], ok ? aoff[i % FPM] + (uint32_t)S * 64u : kOOB);
     uint8_t *stage = smem + (S % NS) * kStageB;
-    const uint32_t sb = ok ? (uint32_t)S * (4u * kGroupRec) : kOOB;
+    // (a token past the tile has bsrc = kOOB, which stays past every size with the step added)
+    const uint32_t sb = (uint32_t)S * (4u * kGroupRec);
 #pragma unroll
     for (int u = part * DPW / 4; u < (part + 1) * DPW / 4; ++u)
-      dma16(rB, stage + (DPW * wave + u) * 1024, bsrc[u], sb);
+      dma16(rB, stage + (DPW * wave + u) * 1024, ok ? bsrc[u] + sb : kOOB);
   };
   auto issue = [&](int S, AStep &as) {
 #pragma unroll
@@ -210,9 +211,9 @@ void k_grouped_mm(MmArgs a) {
     const bool ok = NS * j < nsteps;
 #pragma unroll
     for (int i = 0; i < NF; ++i) {
-      const uint32_t so = ok ? (uint32_t)j * (4u * NS) + (uint32_t)frow(i % FPM) * ng : kOOB;
-      if constexpr (NS == 3) sraw[i] = bload12(rS[i / FPM], soff, so);
-      else sraw[i] = bload16(rS[i / FPM], soff, so);
+      const uint32_t so = ok ? soff[i % FPM] + (uint32_t)j * (4u * NS) : kOOB;
+      if constexpr (NS == 3) sraw[i] = bload12(rS[i / FPM], so);
+      else sraw[i] = bload16(rS[i / FPM], so);
     }
   };
   const uint32_t sel1 = (uint32_t)kq | ((4u + kq) << 8) | 0x0c0c0000u;    // x[kq], y[kq], 0, 0
@@ -450,13 +451,8 @@ hipError_t launch_mm_tiles(const int32_t *expert_off, int E, int4 *tiles, int32_
 
 template <int NA, int EPI>
 static hipError_t launch_mm_t(const MmArgs &a, unsigned grid, size_t lds, hipStream_t s) {
-  static bool attr = false;
-  if (!attr) {
-    if (hipFuncSetAttribute((const void *)k_grouped_mm<NA, EPI, K3_MM_WAVES, K3_MM_STAGES>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-      return hipErrorInvalidValue;
-    attr = true;
-  }
+  if (lds_limit_once<k_grouped_mm<NA, EPI, K3_MM_WAVES, K3_MM_STAGES>>((int)lds) != hipSuccess)
+    return hipErrorInvalidValue;
   launch_kernel(k_grouped_mm<NA, EPI, K3_MM_WAVES, K3_MM_STAGES>, grid, K3_MM_WAVES * 64, lds, s, a);
   return hipGetLastError();
 }

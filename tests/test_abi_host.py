@@ -169,3 +169,45 @@ def test_variant_fields_checked_on_the_host():
         with pytest.raises(lib.K3MoeError) as e:
             lib.k3moe_shared_workspace_size(base, n_shared, T)
         assert e.value.status == code, (n_shared, T)
+
+
+def test_shared_workspace_covers_the_gemm_form_at_one_token():
+    # a shared-expert width whose one-token activations do not fit the GEMV form's LDS
+    # (SI * 4 > 64 KB, or H * 4 > 64 KB) runs the GEMM form even at T = 1: its workspace
+    # must then hold the GEMM's buffers (gate|up products, act's two bf16 pieces, the
+    # down product), not only the one-token act row
+    import dataclasses
+    lib = k3moe
+    cases = [(dataclasses.replace(k3gen.TINY, inter=6144), 3),      # SI = 18432
+             (dataclasses.replace(k3gen.TINY, hidden=20480), 2)]    # H * 4 = 80 KB
+    for d, n_shared in cases:
+        SI, H = n_shared * d.inter, d.hidden
+        one = lib.k3moe_shared_workspace_size(d, n_shared, 1)
+        # at least the gate|up product (2 SI fp32), the two pieces of act (2 SI bf16) and
+        # the down product (H fp32), each region 256-byte aligned
+        need = 2 * SI * 4 + 2 * (SI * 2) + H * 4
+        assert one >= need, (d, n_shared, one, need)
+        prev = 0
+        for T in range(0, 40):
+            n = lib.k3moe_shared_workspace_size(d, n_shared, T)
+            assert n >= prev, (d, T)
+            prev = n
+    # the narrow shape keeps the one-token GEMV form's single act row
+    assert lib.k3moe_shared_workspace_size(k3gen.TINY, 2, 1) < 2 * 2 * k3gen.TINY.inter * 4
+
+
+def test_expert_path_switch_is_per_thread():
+    import threading
+    prev = k3moe.k3moe_set_expert_path(k3moe.EXPERT_PATH_GEMV)
+    seen = []
+    try:
+        def other():
+            # another thread starts from the default and its setting stays its own
+            seen.append(k3moe.k3moe_set_expert_path(k3moe.EXPERT_PATH_GEMM))
+        th = threading.Thread(target=other)
+        th.start()
+        th.join()
+        assert seen == [k3moe.EXPERT_PATH_AUTO]
+        assert k3moe.k3moe_set_expert_path(k3moe.EXPERT_PATH_AUTO) == k3moe.EXPERT_PATH_GEMV
+    finally:
+        k3moe.k3moe_set_expert_path(prev)

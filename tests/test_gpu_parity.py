@@ -582,6 +582,24 @@ def test_tiny_shared_host_checks(tiny_shared):
     assert np.array_equal(y.cpu().numpy(), y0)
 
 
+# shared-expert widths whose one-token activations do not fit the GEMV form's LDS: one
+# token runs the GEMM form (its workspace carved for it)
+@pytest.mark.parametrize("kind", ["wide_inter", "wide_hidden"])
+@pytest.mark.parametrize("T", [1, 2])
+def test_shared_experts_gemm_form_at_one_token(kind, T):
+    if kind == "wide_inter":
+        d, n_shared = dataclasses.replace(k3gen.TINY, inter=6144), 3   # SI = 18432
+    else:
+        d, n_shared = dataclasses.replace(k3gen.TINY, hidden=20480), 2  # H * 4 = 80 KB
+    say(f"shared experts {kind} (H {d.hidden}, SI {n_shared * d.inter}) T={T}")
+    sh = k3gen.gen_shared(d, 9, n_shared)
+    shd = device.upload_shared(sh)
+    x = k3gen.gen_x(d, 70 + T, T)
+    y0 = np.random.default_rng(T).standard_normal((T, d.hidden)).astype(np.float32)
+    got = run_shared(d, n_shared, x, shd, y0)
+    check_rows(got, oracle.shared(d, x, sh, y0, n_shared), f"shared {kind} T={T}")
+
+
 @pytest.fixture(scope="module")
 def k3_shared():
     say("generating and uploading the K3 shared experts (2 x 3072 wide, 264 MB)")
