@@ -127,16 +127,87 @@ static int k3o_cmp_int(const void *a, const void *b)
     return (x > y) - (x < y);
 }
 
+/* An expert with its selection score, ranked by the selection rule. */
+typedef struct {
+    double ch;
+    int id;
+} k3o_ranked;
+
+/* The selection order as a total order: the larger selection score first; equal scores
+ * by the lower id (the pages' tie rule). Two distinct experts never compare equal. */
+static int k3o_rank_before(const void *a, const void *b)
+{
+    const k3o_ranked *p = (const k3o_ranked *)a, *q = (const k3o_ranked *)b;
+    if (p->ch != q->ch) return p->ch > q->ch ? -1 : 1;
+    return (p->id > q->id) - (p->id < q->id);
+}
+
+/* Each expert's unbiased score sc = sigmoid(Wr[e] . x) (fp64 logit and sigmoid, rounded
+ * to fp32) and its selection score ch = sc + bias (fp64). */
+static void k3o_router_scores(float *sc, k3o_ranked *rank, const float *x, const float *Wr,
+                              const float *bias, int hidden, int n_experts)
+{
+    for (int e = 0; e < n_experts; e++) {
+        const float *row = Wr + (size_t)e * hidden;
+        double logit = 0.0;
+        for (int i = 0; i < hidden; i++) logit += (double)x[i] * (double)row[i];
+        sc[e] = (float)(1.0 / (1.0 + exp(-logit)));
+        rank[e].ch = (double)sc[e] + (bias ? (double)bias[e] : 0.0);
+        rank[e].id = e;
+    }
+}
+
+/* [COL-RT] the tail drop over the chosen (ids ascending in idx, weights in w): see k3o.h. */
+static void k3o_topp_tail(int *idx, float *w, const float *sc, double chosen_sum, int topk,
+                          int renorm, float routed_scale, float topp, double *margin)
+{
+    float *frac = (float *)malloc(sizeof(float) * (size_t)topk);
+    k3o_ranked *walk = (k3o_ranked *)malloc(sizeof(k3o_ranked) * (size_t)topk);
+    unsigned char *keep = (unsigned char *)calloc((size_t)topk, 1);
+    /* each chosen expert's fraction of the chosen total, in fp32; the walk order is the
+     * larger fraction first, equal fractions by the lower id (ids ascend with the slot) */
+    for (int j = 0; j < topk; j++) {
+        frac[j] = (float)((double)sc[idx[j]] / chosen_sum);
+        walk[j].ch = (double)frac[j];
+        walk[j].id = j;
+    }
+    qsort(walk, (size_t)topk, sizeof(k3o_ranked), k3o_rank_before);
+    float before = 0.0f;  /* fp32 sum of the fractions walked so far */
+    double closest = INFINITY;
+    for (int r = 0; r < topk; r++) {
+        const double dist = fabs((double)before - (double)topp);
+        if (dist < closest) closest = dist;
+        keep[walk[r].id] = before < topp;
+        before = before + frac[walk[r].id];
+    }
+    double kept_sum = 0.0;
+    for (int j = 0; j < topk; j++)
+        if (keep[j]) kept_sum += (double)sc[idx[j]];
+    for (int j = 0; j < topk; j++) {
+        if (!keep[j]) {
+            idx[j] = -1;
+            w[j] = 0.0f;
+        } else {
+            const double v = (double)sc[idx[j]];
+            w[j] = (float)((renorm && kept_sum > 0.0 ? v / kept_sum : v) * (double)routed_scale);
+        }
+    }
+    if (margin) *margin = closest;
+    free(frac);
+    free(walk);
+    free(keep);
+}
+
 /* [K3C-9], [COL]: score every expert with a sigmoid of its logit (the unbiased
- * score sc); add the score-correction bias to get the selection score ch; take K
- * times the not-yet-chosen expert with the largest ch, where a later expert must be
- * strictly larger to win (so the lowest id wins a tie); weight each chosen expert
- * by its unbiased score, renormalised over the K chosen when renorm is set, then
- * multiplied by routed_scale.
+ * score sc); add the score-correction bias to get the selection score ch; choose the K
+ * experts that come first when all are ranked by ch, larger first, with the lower id
+ * first among equal ch (the pages' tie rule); weight each chosen expert by its unbiased
+ * score, renormalised over the K chosen when renorm is set, then multiplied by
+ * routed_scale.
  * Readings: the logit is an fp64 sum; sc is the fp64 sigmoid rounded to fp32;
- * ch = sc + bias in fp64; the renormalisation sum and division are fp64 and the
- * weight is rounded to fp32 once; the K ids are returned in ascending order (the
- * selection order is available separately). */
+ * ch = sc + bias in fp64; the renormalisation sum (over the chosen in ascending id order)
+ * and the division are fp64 and the weight is rounded to fp32 once; the K ids are
+ * returned in ascending order (the ranking order is available separately). */
 double k3o_router(int *idx, float *w, int *sel_order, const float *x, const float *Wr,
                   const float *bias, int hidden, int n_experts, int topk, int renorm,
                   float routed_scale)
@@ -151,98 +222,30 @@ double k3o_router_topp(int *idx, float *w, int *sel_order, const float *x, const
                        float routed_scale, float topp, double *margin)
 {
     float *sc = (float *)malloc(sizeof(float) * (size_t)n_experts);
-    double *ch = (double *)malloc(sizeof(double) * (size_t)n_experts);
-    unsigned char *taken = (unsigned char *)calloc((size_t)n_experts, 1);
-    int *pick = (int *)malloc(sizeof(int) * (size_t)topk);
+    k3o_ranked *rank = (k3o_ranked *)malloc(sizeof(k3o_ranked) * (size_t)n_experts);
+    k3o_router_scores(sc, rank, x, Wr, bias, hidden, n_experts);
+    qsort(rank, (size_t)n_experts, sizeof(k3o_ranked), k3o_rank_before);
 
-    for (int e = 0; e < n_experts; e++) {
-        const float *row = Wr + (size_t)e * hidden;
-        double logit = 0.0;
-        for (int i = 0; i < hidden; i++) logit += (double)x[i] * (double)row[i];
-        sc[e] = (float)(1.0 / (1.0 + exp(-logit)));
-        ch[e] = (double)sc[e] + (bias ? (double)bias[e] : 0.0);
-    }
-
-    double last = 0.0;
-    for (int j = 0; j < topk; j++) {
-        int best = -1;
-        for (int e = 0; e < n_experts; e++) {
-            if (taken[e]) continue;
-            if (best < 0 || ch[e] > ch[best]) best = e;
-        }
-        taken[best] = 1;
-        pick[j] = best;
-        last = ch[best];
-    }
-    double next = -INFINITY;
-    for (int e = 0; e < n_experts; e++)
-        if (!taken[e] && ch[e] > next) next = ch[e];
-    const double gap = (topk < n_experts) ? (last - next) : INFINITY;
-
-    if (sel_order) memcpy(sel_order, pick, sizeof(int) * (size_t)topk);
-    memcpy(idx, pick, sizeof(int) * (size_t)topk);
+    /* the gap between the last chosen and the first not chosen selection score */
+    const double gap = (topk < n_experts) ? rank[topk - 1].ch - rank[topk].ch : INFINITY;
+    for (int j = 0; j < topk; j++) idx[j] = rank[j].id;
+    if (sel_order) memcpy(sel_order, idx, sizeof(int) * (size_t)topk);
     qsort(idx, (size_t)topk, sizeof(int), k3o_cmp_int);
 
-    double s = 0.0;
-    for (int j = 0; j < topk; j++) s += (double)sc[idx[j]];
+    double chosen_sum = 0.0;
+    for (int j = 0; j < topk; j++) chosen_sum += (double)sc[idx[j]];
     for (int j = 0; j < topk; j++) {
-        double v = (double)sc[idx[j]];
-        if (renorm && s > 0.0) v /= s;
-        w[j] = (float)(v * (double)routed_scale);
+        const double v = (double)sc[idx[j]];
+        w[j] = (float)((renorm && chosen_sum > 0.0 ? v / chosen_sum : v) * (double)routed_scale);
     }
 
-    if (topp > 0.0f) {
-        /* [COL-RT]: fractions of the chosen total, walked largest first */
-        float *f = (float *)malloc(sizeof(float) * (size_t)topk);
-        int *ord = (int *)malloc(sizeof(int) * (size_t)topk);
-        unsigned char *keep = (unsigned char *)calloc((size_t)topk, 1);
-        for (int j = 0; j < topk; j++) {
-            f[j] = (float)((double)sc[idx[j]] / s);
-            ord[j] = j;
-        }
-        /* insertion sort of positions by (fraction descending, id ascending) */
-        for (int a = 1; a < topk; a++) {
-            const int v = ord[a];
-            int b = a - 1;
-            while (b >= 0 && (f[ord[b]] < f[v] || (f[ord[b]] == f[v] && idx[ord[b]] > idx[v]))) {
-                ord[b + 1] = ord[b];
-                b--;
-            }
-            ord[b + 1] = v;
-        }
-        float cum = 0.0f;
-        double closest = INFINITY;
-        for (int r = 0; r < topk; r++) {
-            const double dist = fabs((double)cum - (double)topp);
-            if (dist < closest) closest = dist;
-            if (cum < topp) keep[ord[r]] = 1;
-            cum = cum + f[ord[r]];
-        }
-        double sk = 0.0;
-        for (int j = 0; j < topk; j++)
-            if (keep[j]) sk += (double)sc[idx[j]];
-        for (int j = 0; j < topk; j++) {
-            if (!keep[j]) {
-                idx[j] = -1;
-                w[j] = 0.0f;
-                continue;
-            }
-            double v = (double)sc[idx[j]];
-            if (renorm && sk > 0.0) v /= sk;
-            w[j] = (float)(v * (double)routed_scale);
-        }
-        if (margin) *margin = closest;
-        free(f);
-        free(ord);
-        free(keep);
-    } else if (margin) {
+    if (topp > 0.0f)
+        k3o_topp_tail(idx, w, sc, chosen_sum, topk, renorm, routed_scale, topp, margin);
+    else if (margin)
         *margin = INFINITY;
-    }
 
     free(sc);
-    free(ch);
-    free(taken);
-    free(pick);
+    free(rank);
     return gap;
 }
 
@@ -256,15 +259,24 @@ float k3o_situ(float g, float u, float b1, float b2)
     return (float)(a * v);
 }
 
-/* [K3C-5]: inv = 1/sqrt(sum(x^2)/n + eps), eps inside the root; out = x*inv*w.
- * Reading: fp64 throughout, one rounding per output element. */
-void k3o_rmsnorm(float *out, const float *x, const float *w, int n, float eps)
+/* The mean of the squares of n values, summed in fp64 in index order. */
+static double k3o_mean_square(const float *x, int n)
 {
     double ss = 0.0;
     for (int i = 0; i < n; i++) ss += (double)x[i] * (double)x[i];
-    const double inv = 1.0 / sqrt(ss / (double)n + (double)eps);
-    for (int i = 0; i < n; i++)
-        out[i] = (float)((double)x[i] * inv * (w ? (double)w[i] : 1.0));
+    return ss / (double)n;
+}
+
+/* [K3C-5]: RMSNorm divides each value by the root of (mean square + eps), the eps inside
+ * the root, and multiplies it by its weight. Reading: fp64 throughout, one rounding per
+ * output element. */
+void k3o_rmsnorm(float *out, const float *x, const float *w, int n, float eps)
+{
+    const double factor = 1.0 / sqrt(k3o_mean_square(x, n) + (double)eps);
+    for (int i = 0; i < n; i++) {
+        const double gamma = w ? (double)w[i] : 1.0;
+        out[i] = (float)((double)x[i] * factor * gamma);
+    }
 }
 
 /* [K3C-9], [COL]: one routed expert in the latent space: gate and up rows of w1, w3

@@ -3,8 +3,8 @@
 It shares nothing with oracle/k3o.c: the E2M1 values are derived from the element
 format's bit fields (OCP Microscaling Formats v1.0, E2M1: 1 sign bit, 2 exponent
 bits with bias 1, 1 mantissa bit; exponent field 0 is subnormal), not read from a
-table; MXFP4 matrices are decoded whole with numpy; routing takes a full stable sort
-instead of repeated maxima; products are numpy fp64 matmuls.
+table; MXFP4 matrices are decoded whole with numpy; the logistic is taken through tanh;
+routing ranks with numpy's lexsort; products are numpy fp64 matmuls.
 """
 from __future__ import annotations
 

@@ -286,6 +286,46 @@ def _tiny_layer(seed=0, T=4):
     return d, dense, lay, blobs, ex, x
 
 
+def _brute_expert(d, blob, offsets, z):
+    """One expert on one latent row by numpy: whole-matrix decode, fp64 products."""
+    (p1, s1), (p3, s3), (p2, s2) = _brute.expert_views(blob, d, offsets)
+    zin = z.astype(np.float64)
+    g = (_brute.decode_mxfp4(p1, s1, d.group) @ zin).astype(np.float32)
+    u = (_brute.decode_mxfp4(p3, s3, d.group) @ zin).astype(np.float32)
+    a = _brute.situ(g, u, d.b1, d.b2)
+    return (_brute.decode_mxfp4(p2, s2, d.group) @ a.astype(np.float64)).astype(np.float32), a
+
+
+def test_expert_pairs_reads_z_by_token():
+    """The expert stage's checker (k3o_expert_pairs): pair q runs expert ex_id[q] on z row
+    tok[q]. Pinned to a numpy expert per pair, on pairs whose token differs from their
+    position and whose order is shuffled; reading z by pair position instead of by token
+    would give other rows, so the pin tells the two apart."""
+    d, dense, lay, blobs, ex, x = _tiny_layer(0, 4)
+    B = lay.blob_bytes
+    n = 24
+    T = n  # as many z rows as pairs, so a by-position reading stays in bounds
+    rng = np.random.default_rng(11)
+    z = rng.standard_normal((T, d.latent)).astype(np.float32)
+    tok = ((np.arange(n) + 1 + rng.integers(0, T - 1, n)) % T).astype(np.int32)  # tok[q] != q
+    exid = rng.integers(0, d.n_experts, n).astype(np.int32)
+    edn, act = oracle.expert_pairs(d, tok, exid, z, ex, want_act=True)
+    for q in range(n):
+        bref, aref = _brute_expert(d, blobs[exid[q] * B:(exid[q] + 1) * B], lay.offsets, z[tok[q]])
+        err = np.linalg.norm(edn[q] - bref.astype(np.float64)) / np.linalg.norm(bref.astype(np.float64))
+        assert err < 1e-6, (q, err)
+        assert np.allclose(act[q], aref, rtol=1e-6, atol=1e-7), q
+        # the same as the one-expert oracle call, bit for bit
+        assert np.array_equal(edn[q], oracle.expert(d, ex, int(exid[q]), z[tok[q]])[0]), q
+    # shuffled pairs: the same rows, permuted
+    perm = rng.permutation(n)
+    assert np.array_equal(oracle.expert_pairs(d, tok[perm], exid[perm], z, ex), edn[perm])
+    # a by-position reading of z differs from the by-token result
+    assert np.all(tok != np.arange(n))
+    by_pos = np.stack([oracle.expert(d, ex, int(exid[q]), z[q])[0] for q in range(n)])
+    assert not np.any([np.allclose(by_pos[q], edn[q]) for q in range(n)])
+
+
 def test_layer_matches_brute_force_tiny():
     d, dense, lay, blobs, ex, x = _tiny_layer(0, 8)
     r = oracle.layer(d, x, dense, ex, want_inner=True)
