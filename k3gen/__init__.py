@@ -28,7 +28,11 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "k3gen.c")
-_LIB_PATH = os.path.join(_HERE, "libk3gen.so")
+# K3_HOST_SANITIZE=1 selects a build with AddressSanitizer and UndefinedBehaviorSanitizer
+# (host code only; the process must preload the ASan runtime)
+SANITIZE = os.environ.get("K3_HOST_SANITIZE") == "1"
+SAN_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined", "-fno-sanitize-recover=all"]
+_LIB_PATH = os.path.join(_HERE, "libk3gen_san.so" if SANITIZE else "libk3gen.so")
 _lib = None
 
 # tensor ids of the counter-based streams
@@ -40,7 +44,8 @@ _ATTEMPT_SHIFT = 40  # x row counter: (attempt << 40) + t * H + i
 
 
 def build() -> str:
-    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
+    opt = SAN_FLAGS if SANITIZE else ["-O2"]
+    subprocess.check_call(["gcc", *opt, "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
                            "-std=c99", "-Wall", "-Wextra", _SRC, "-o", _LIB_PATH, "-lm"])
     return _LIB_PATH
 
