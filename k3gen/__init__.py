@@ -234,14 +234,14 @@ def gen_x(dims: Dims, seed: int, T: int, attempts=None) -> np.ndarray:
     return gen_x_rows(dims, seed, np.arange(T), attempts)
 
 
-def skew_bias(base: np.ndarray, beta: float, gamma: float, hot_every: int = 10) -> np.ndarray:
-    """Skewed score-correction bias: experts e % hot_every == 0 (90 of 896) get +beta;
-    the others get a graded offset falling linearly from 0 to -gamma in id order."""
+def skew_bias(base: np.ndarray, beta: float, tail_offset: float, hot_every: int = 10,
+              tail_from: int = 4) -> np.ndarray:
+    """Skewed score-correction bias. Hot experts (e % hot_every == 0: 90 of 896) keep
+    their bias plus beta. The cold experts' own bias is replaced, so that the offset alone
+    decides their rank: 0 for the warm ones (1 <= e % hot_every < tail_from) and
+    -tail_offset for the tail (e % hot_every >= tail_from)."""
     E = base.size
-    hot = (np.arange(E) % hot_every) == 0
-    off = np.zeros(E, np.float64)
-    off[hot] = beta
-    cold = np.flatnonzero(~hot)
-    off[cold] = -gamma * np.arange(cold.size) / max(cold.size - 1, 1)
-    return (base.astype(np.float64) + off).astype(np.float32)
+    r = np.arange(E) % hot_every
+    out = np.where(r == 0, base.astype(np.float64) + beta, np.where(r < tail_from, 0.0, -tail_offset))
+    return out.astype(np.float32)
 

@@ -49,6 +49,12 @@ def skew_params():
         return json.load(f)
 
 
+def skewed_bias(base: np.ndarray) -> np.ndarray:
+    """The skewed workload's bias on a layer's own bias (parameters in skew_bias.json)."""
+    p = skew_params()
+    return k3gen.skew_bias(base, p["beta"], p["tail_offset"], p["hot_every"], p["tail_from"])
+
+
 def layer_seed(wl: k3gen.Workload) -> int:
     """All K3-shape workloads share one layer (the decode layer's seed); tiny has its own."""
     return wl.seed if wl.dims is k3gen.TINY else 1
@@ -60,7 +66,7 @@ def dense_for(wl_index: int):
     dense = k3gen.gen_dense(wl.dims, layer_seed(wl))
     if wl.skewed:
         p = skew_params()
-        dense["bias"] = k3gen.skew_bias(dense["bias"], p["beta"], p["gamma"], p["hot_every"])
+        dense["bias"] = skewed_bias(dense["bias"])
     return dense
 
 
