@@ -6,8 +6,10 @@ resident in HBM. The headline workload is the K3-shape decode layer: T = 1 token
 step, hidden 7168, latent 3584, inter 3072, 896 MXFP4 experts (15.7 GB resident),
 top-16. Each step reads a different token from a pool of 64, so the routed experts
 change from step to step, and the steps rotate over copies of the dense weights (4 by
-default, 128 MB each), so those are not served from the 256 MB MALL either. A
-K3-shape prefill pass (T = 4096) is reported beside it.
+default, 128 MB each), so those are not served from the 256 MB MALL either. Beside it:
+the K3-shape prefill (T = 4096), the skewed prefill (T = 8192, 90 hot experts taking 80%
+of the pairs), the layer at 8, 64 and 256 tokens, the shared experts, the two
+approximate variants, and the CPU oracle on the host's cores.
 
 Prints one JSON line (rank 0). Per-kernel times come from the same kind of steps run
 through k3moe_layer_profiled, which binds a pair of HIP events to each kernel launch's
@@ -75,11 +77,11 @@ def launch_ms(events: HipEvents, names):
     return out
 
 
-def traffic_from_profile(kernel: str):
-    """HBM-side bytes per launch of `kernel` from the committed counter summary
-    (calibrated FETCH_SIZE + WRITE_SIZE), or None when the kernel sources have changed
-    since the counters were taken (their sha256 is recorded with the figures)."""
-    path = os.path.join(ROOT, "profiles", "expert_gateup_decode_T1_traffic.txt")
+def figures_from_profile(name: str, key: str, kernel: str):
+    """A per-kernel figure recorded in a committed counter summary (profiles/<name>), or
+    None when the kernel sources have changed since the counters were taken (their sha256
+    is recorded with the figures)."""
+    path = os.path.join(ROOT, "profiles", name)
     try:
         lines = open(path).read().splitlines()
     except OSError:
@@ -87,8 +89,8 @@ def traffic_from_profile(kernel: str):
     vals, srcs, sha = {}, [], None
     for line in lines:
         parts = line.split()
-        if len(parts) == 3 and parts[0] == "traffic_bytes_per_launch":
-            vals[parts[1]] = int(parts[2])
+        if len(parts) == 3 and parts[0] == key:
+            vals[parts[1]] = float(parts[2])
         elif parts and parts[0] == "kernel_sources":
             srcs = parts[1:]
         elif len(parts) == 2 and parts[0] == "kernel_source_sha256":
@@ -102,6 +104,12 @@ def traffic_from_profile(kernel: str):
     if sha is None or h.hexdigest() != sha:
         return None
     return vals.get(kernel)
+
+
+def traffic_from_profile(kernel: str):
+    """HBM-side bytes per launch of `kernel` (calibrated FETCH_SIZE + WRITE_SIZE)."""
+    v = figures_from_profile("expert_gateup_decode_T1_traffic.txt", "traffic_bytes_per_launch", kernel)
+    return int(v) if v is not None else None
 
 
 def algorithmic(dims, T, n_distinct):
@@ -213,13 +221,155 @@ def bench_shared(args, dims, stream, xs, pool, row, hip_record, n_shared=2):
     return out
 
 
+def time_block(step, n, stream, hip_record):
+    """ms per step over n steps between one pair of events on the stream."""
+    import torch
+    ev = HipEvents(2)
+    torch.cuda.synchronize()
+    hip_record(ev.ev[0], stream.cuda_stream)
+    for i in range(n):
+        step(i)
+    hip_record(ev.ev[1], stream.cuda_stream)
+    torch.cuda.synchronize()
+    ms = ev.ms(ev.ev[0], ev.ev[1]) / n
+    ev.close()
+    return ms
+
+
+def time_each(step, n, stream, hip_record):
+    """ms of each of n steps, one event pair around each (steps back to back)."""
+    import torch
+    ev = HipEvents(2 * n)
+    torch.cuda.synchronize()
+    for i in range(n):
+        hip_record(ev.ev[2 * i], stream.cuda_stream)
+        step(i)
+        hip_record(ev.ev[2 * i + 1], stream.cuda_stream)
+    torch.cuda.synchronize()
+    out = [ev.ms(ev.ev[2 * i], ev.ev[2 * i + 1]) for i in range(n)]
+    ev.close()
+    return out
+
+
+def profiled_kernels(call, n):
+    """Mean per-step-name kernel time (us) over n profiled calls; call(events) runs one."""
+    import torch
+    pe = HipEvents(2 * MAX_LAUNCHES)
+    sums = {}
+    for i in range(n):
+        names = call(i, pe.ev)
+        torch.cuda.synchronize()
+        for k, v in launch_ms(pe, names).items():
+            sums[k] = sums.get(k, 0.0) + v
+    pe.close()
+    return {k: round(v / n * 1e3, 2) for k, v in sums.items()}
+
+
+def routing_stats(dims, idx: np.ndarray, hot=None):
+    """Load balance of one batch's routing: tokens per expert, and the grouped GEMM's
+    column tiles and their split over the XCDs (the kernels' own tiling)."""
+    from mxfp4_routed_expert_amd import k3moe
+    E = dims.n_experts
+    counts = np.bincount(idx[idx >= 0].ravel(), minlength=E)
+    out = {"distinct_experts": int(np.count_nonzero(counts)), "tokens_per_expert_max": int(counts.max()),
+           "tokens_per_expert_median": float(np.median(counts)),
+           "tokens_per_expert_mean": round(float(counts.mean()), 2)}
+    if hot is not None:
+        cold = counts[~hot]
+        out.update({"hot_share": round(float(counts[hot].sum() / counts.sum()), 4),
+                    "hot_tokens_mean": round(float(counts[hot].mean()), 1),
+                    "cold_with_1_to_5_tokens": round(float(np.mean((cold >= 1) & (cold <= 5))), 4),
+                    "cold_with_0_tokens": round(float(np.mean(cold == 0)), 4)})
+    tile, rows_gu, rows_dn = k3moe.gemm_tiling()
+    ncol = (counts + tile - 1) // tile
+    # the GEMM form walks (column tile, row block) entries; entry q runs on XCD q // ceil(n / 8)
+    cols = np.concatenate([np.minimum(tile, c - tile * np.arange(n)) for c, n in zip(counts, ncol) if n])
+    for name, rows, M in (("gateup", rows_gu, dims.inter), ("down", rows_dn, dims.latent)):
+        rb = (M + rows - 1) // rows  # row blocks of each column tile
+        work = np.repeat((cols + 15) // 16, rb)  # 16-token column blocks of each entry
+        chunk = (work.size + 7) // 8
+        per_xcd = np.array([work[x * chunk:(x + 1) * chunk].sum() for x in range(8)], np.float64)
+        out[f"{name}_entries"] = int(work.size)
+        out[f"{name}_entries_per_xcd"] = int(chunk)
+        out[f"{name}_column_blocks_per_xcd_max_over_mean"] = round(float(per_xcd.max() / per_xcd.mean()), 4)
+    out["column_tiles"] = int(ncol.sum())
+    return out
+
+
+def bench_prefill(args, dims, wts, x, bias_dev, stream, hip_record, what):
+    """One prefill workload (x already on the device): ms per step, per-kernel us of a warm
+    profiled call, the routing's load balance, algorithmic TFLOP/s."""
+    import torch
+
+    from mxfp4_routed_expert_amd import device, k3moe
+    T = x.shape[0]
+    y = torch.empty((T, dims.hidden), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, dims.topk), dtype=torch.int32, device="cuda")
+    ws = device.workspace(dims, T)
+    w = wts
+    if bias_dev is not None:
+        w = type(wts).from_buffer_copy(wts)
+        w.bias = bias_dev.data_ptr()
+
+    def step(i):
+        k3moe.k3moe_layer(dims, T, x, w, y, idx, None, ws, stream=stream)
+
+    for i in range(2):
+        step(i)
+    ms = time_block(step, args.prefill_steps, stream, hip_record)
+    kern = profiled_kernels(lambda i, ev: k3moe.k3moe_layer_profiled(dims, T, x, w, y, idx, None, ws, ev,
+                                                                     stream=stream), 2)
+    alg = algorithmic(dims, T, dims.n_experts)
+    tf = alg["flops"] / (ms * 1e-3) / 1e12
+    ex_us = kern.get("expert_gateup_situ", 0.0) + kern.get("expert_down", 0.0)
+    ex_tf = alg["expert_flops"] / (ex_us * 1e-6) / 1e12 if ex_us > 0 else None
+    out = {"T": T, "ms_per_step": round(ms, 3), "tokens_per_s": round(T / (ms * 1e-3), 1),
+           "algorithmic_TFLOPs": round(tf, 2), "bf16_peak_frac": round(tf / BF16_PEAK_TFLOPS, 4),
+           "algorithmic_flops": alg["flops"], "expert_TFLOPs": round(ex_tf, 2) if ex_tf else None,
+           "kernel_us": kern, "steps": args.prefill_steps}
+    ids = idx.cpu().numpy()
+    del y, idx, ws
+    torch.cuda.empty_cache()
+    log(f"{what}: {ms:.2f} ms/step, {tf:.1f} TFLOP/s algorithmic; per-kernel us: "
+        + ", ".join(f"{n} {v:.0f}" for n, v in kern.items()))
+    return out, ids
+
+
+def cpu_baseline(dims, dense, host_blobs, lay, tokens_1, tokens_n):
+    """The oracle (plain C, fp64 sums) on K3-shape decode tokens on the host's cores: one
+    thread, then OpenMP over tokens on every core of this process's CPU share (at most
+    16, the GPU machine's share per GPU)."""
+    import k3gen
+    import oracle
+    ex = oracle.ExpertSet(host_blobs, lay.blob_bytes, lay.offsets)
+    try:
+        ncores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        ncores = os.cpu_count() or 1
+    ncores = max(1, min(16, ncores))
+    res = {}
+    for name, nthreads, n in (("single_thread", 1, tokens_1), ("all_cores", ncores, tokens_n)):
+        x = k3gen.gen_x(dims, 1, n)
+        c0 = time.perf_counter()
+        oracle.layer(dims, x, dense, ex, nthreads=nthreads)
+        cs = time.perf_counter() - c0
+        res[name] = {"value": round(n / cs, 3), "unit": "tokens/s", "cores": nthreads,
+                     "sample": f"{n} K3-shape decode tokens, {cs:.1f} s wall"}
+        log(f"cpu oracle: {n / cs:.2f} tokens/s on {nthreads} thread(s)")
+    top = dict(res["all_cores"])
+    top.update({"kind": "oracle", "sample": top["sample"] + " (OpenMP over tokens); single_thread: "
+                + res["single_thread"]["sample"], "single_thread": res["single_thread"]})
+    return top
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--prefill-steps", type=int, default=3)
-    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--no-prefill", action="store_true", help="skip both prefill workloads")
+    ap.add_argument("--no-skewed", action="store_true", help="skip the skewed T = 8192 prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--batch-sweep", type=lambda v: [int(t) for t in v.split(",") if t], default=[8, 64, 256],
                     help="also time the layer at these batch sizes (comma list; empty to skip)")
@@ -230,7 +380,8 @@ def main():
                     help="skip timing the int8-activation expert variant (an approximation, never the headline)")
     ap.add_argument("--no-shared", action="store_true",
                     help="skip the shared-expert measurement (a call of its own, after the layer)")
-    ap.add_argument("--cpu-tokens", type=int, default=64)
+    ap.add_argument("--cpu-tokens", type=int, default=64, help="oracle tokens on all cores")
+    ap.add_argument("--cpu-tokens-1", type=int, default=4, help="oracle tokens on one thread")
     ap.add_argument("--dense-copies", type=int, default=4,
                     help="copies of the dense weights (router, projections) the decode steps rotate "
                          "over, so no step finds them still cached in the MALL from the step before")
@@ -279,6 +430,8 @@ def main():
                                          norm_w=dev.norm_w.clone(), experts=dev.experts,
                                          blob_bytes=dev.blob_bytes, offsets=dev.offsets))
     wts_rot = [c.weights_struct() for c in copies]
+    hip_record = ctypes.CDLL("libamdhip64.so").hipEventRecord
+    hip_record.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
     if args.copy_calib_mib:
         n = args.copy_calib_mib << 20
@@ -305,38 +458,22 @@ def main():
         k3moe.k3moe_layer(dims, T, xs.data_ptr() + j * row, wts_rot[i % len(wts_rot)], y, idx[j], tw[j], ws,
                           stream=stream)
 
-    with torch.cuda.stream(stream):
-        for i in range(args.warmup):
-            step(i)
-    torch.cuda.synchronize()
-    ev = HipEvents(2)
-    hip_record = ctypes.CDLL("libamdhip64.so").hipEventRecord
-    hip_record.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
-    hip_record(ev.ev[0], stream.cuda_stream)
-    for i in range(args.steps):
-        step(i)
-    hip_record(ev.ev[1], stream.cuda_stream)
-    torch.cuda.synchronize()
+    ms_step = time_block(step, args.steps, stream, hip_record)
     wall = time.perf_counter() - w0
-    ms_step = ev.ms(ev.ev[0], ev.ev[1]) / args.steps
-    ev.close()
     log(f"decode T=1: {ms_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us/step)")
+    # the same kind of steps, each between its own pair of events
+    each = np.array(time_each(step, max(20, min(args.steps, 200)), stream, hip_record)) * 1e3
+    log(f"decode T=1 per step: median {np.median(each):.1f} us, min {each.min():.1f} us")
 
     # per-kernel event marks over the same kind of steps
     nprof = min(args.steps, 100)
-    pe = HipEvents(2 * MAX_LAUNCHES)
-    sums = {}
-    for i in range(nprof):
-        j = i % pool
-        names = k3moe.k3moe_layer_profiled(dims, T, xs.data_ptr() + j * row, wts_rot[i % len(wts_rot)], y,
-                                           idx[j], tw[j], ws, pe.ev, stream=stream)
-        torch.cuda.synchronize()
-        for n, v in launch_ms(pe, names).items():
-            sums[n] = sums.get(n, 0.0) + v
-    pe.close()
-    kern_us = {n: v / nprof * 1e3 for n, v in sums.items()}
+    kern_us = profiled_kernels(
+        lambda i, ev: k3moe.k3moe_layer_profiled(dims, T, xs.data_ptr() + (i % pool) * row, wts_rot[i % len(wts_rot)],
+                                                 y, idx[i % pool], tw[i % pool], ws, ev, stream=stream), nprof)
     log("per-kernel us: " + ", ".join(f"{n} {v:.1f}" for n, v in kern_us.items()))
 
     alg = algorithmic(dims, T, dims.topk)
@@ -352,41 +489,37 @@ def main():
                 "traffic_unit": "bytes per launch", "algorithmic_bytes": dom_bytes,
                 "traffic_over_algorithmic": round(traffic / dom_bytes, 4) if traffic else None,
                 "layer_achieved": round(layer_gbs, 1), "layer_frac": round(layer_gbs / HBM_PEAK_GBS, 4),
-                "kernel_us": {k: round(v, 2) for k, v in kern_us.items()}}
+                "layer_bytes": alg["layer_bytes"], "kernel_us": kern_us}
+    decode_steps = {"us_mean_block": round(ms_step * 1e3, 2), "us_median": round(float(np.median(each)), 2),
+                    "us_min": round(float(each.min()), 2), "us_max": round(float(each.max()), 2),
+                    "n_each": int(each.size)}
 
-    # ---------------------------------------------------------------- prefill, T = 4096
-    prefill = None
+    # ---------------------------------------------------------------- prefill, T = 4096 and skewed T = 8192
+    prefill = skewed = None
     if not args.no_prefill:
-        Tp = 4096
-        xp = torch.from_numpy(k3gen.gen_x(dims, 3, Tp).view(np.int16)).cuda()
-        yp = torch.empty((Tp, dims.hidden), dtype=torch.float32, device="cuda")
-        wsp = device.workspace(dims, Tp)
-        with torch.cuda.stream(stream):
-            k3moe.k3moe_layer(dims, Tp, xp, wts, yp, None, None, wsp, stream=stream)
-        torch.cuda.synchronize()
-        evp = HipEvents(2)
-        hip_record(evp.ev[0], stream.cuda_stream)
-        for _ in range(args.prefill_steps):
-            k3moe.k3moe_layer(dims, Tp, xp, wts, yp, None, None, wsp, stream=stream)
-        hip_record(evp.ev[1], stream.cuda_stream)
-        torch.cuda.synchronize()
-        msp = evp.ms(evp.ev[0], evp.ev[1]) / args.prefill_steps
-        evp.close()
-        pep = HipEvents(2 * MAX_LAUNCHES)
-        names_p = k3moe.k3moe_layer_profiled(dims, Tp, xp, wts, yp, None, None, wsp, pep.ev, stream=stream)
-        torch.cuda.synchronize()
-        kern_p = {n: round(v * 1e3, 1) for n, v in launch_ms(pep, names_p).items()}
-        pep.close()
-        algp = algorithmic(dims, Tp, dims.n_experts)
-        tf = algp["flops"] / (msp * 1e-3) / 1e12
-        ex_us = kern_p.get("expert_gateup_situ", 0.0) + kern_p.get("expert_down", 0.0)
-        ex_tf = algp["expert_flops"] / (ex_us * 1e-6) / 1e12 if ex_us > 0 else None
-        prefill = {"T": Tp, "ms_per_step": round(msp, 3), "tokens_per_s": round(Tp / (msp * 1e-3), 1),
-                   "algorithmic_TFLOPs": round(tf, 2), "bf16_peak_frac": round(tf / BF16_PEAK_TFLOPS, 4),
-                   "expert_TFLOPs": round(ex_tf, 2) if ex_tf else None, "kernel_us": kern_p}
-        log(f"prefill T=4096: {msp:.2f} ms/step, {tf:.1f} TFLOP/s algorithmic; per-kernel us: "
-            + ", ".join(f"{n} {v:.0f}" for n, v in kern_p.items()))
-        del wsp, yp, xp
+        xp = torch.from_numpy(k3gen.gen_x(dims, 3, 4096).view(np.int16)).cuda()
+        prefill, ids = bench_prefill(args, dims, wts, xp, None, stream, hip_record, "prefill T=4096")
+        prefill["routing"] = routing_stats(dims, ids)
+        del xp
+        if not args.no_skewed:
+            with open(os.path.join(ROOT, "tests", "golden", "skew_bias.json")) as f:
+                sp = json.load(f)
+            sbias = k3gen.skew_bias(dense["bias"], sp["beta"], sp["tail_offset"], sp["hot_every"], sp["tail_from"])
+            bias_dev = torch.from_numpy(sbias).cuda()
+            xk = torch.from_numpy(k3gen.gen_x(dims, 4, 8192).view(np.int16)).cuda()
+            skewed, ids = bench_prefill(args, dims, wts, xk, bias_dev, stream, hip_record,
+                                        "skewed prefill T=8192")
+            hot = (np.arange(dims.n_experts) % sp["hot_every"]) == 0
+            skewed["routing"] = routing_stats(dims, ids, hot)
+            del xk, bias_dev
+        # MFMA utilisation of the expert GEMMs from the committed counter summary of this
+        # same command's prefill (null once the kernel sources differ from the counted ones)
+        for obj, tag in ((prefill, "T4096"), (skewed, "T8192")):
+            if obj is None:
+                continue
+            util = {k: figures_from_profile("expert_gemm_prefill_counters.txt", "mfma_util", f"{tag}:{k}")
+                    for k in ("expert_gateup_situ", "expert_down")}
+            obj["mfma_util"] = util if any(v is not None for v in util.values()) else None
         torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- small batches
@@ -394,23 +527,27 @@ def main():
     for Tb in args.batch_sweep:
         xb = torch.from_numpy(k3gen.gen_x(dims, 7, Tb).view(np.int16)).cuda()
         yb = torch.empty((Tb, dims.hidden), dtype=torch.float32, device="cuda")
+        ib = torch.empty((Tb, dims.topk), dtype=torch.int32, device="cuda")
         wsb = device.workspace(dims, Tb)
+
+        def step_b(i):
+            k3moe.k3moe_layer(dims, Tb, xb, wts_rot[i % len(wts_rot)], yb, ib, None, wsb, stream=stream)
+
         for i in range(3):
-            k3moe.k3moe_layer(dims, Tb, xb, wts_rot[i % len(wts_rot)], yb, None, None, wsb, stream=stream)
-        torch.cuda.synchronize()
-        evb = HipEvents(2)
-        nb = 10
-        hip_record(evb.ev[0], stream.cuda_stream)
-        for i in range(nb):
-            k3moe.k3moe_layer(dims, Tb, xb, wts_rot[i % len(wts_rot)], yb, None, None, wsb, stream=stream)
-        hip_record(evb.ev[1], stream.cuda_stream)
-        torch.cuda.synchronize()
-        msb = evb.ms(evb.ev[0], evb.ev[1]) / nb
-        evb.close()
-        sweep[str(Tb)] = {"us_per_step": round(msb * 1e3, 1), "tokens_per_s": round(Tb / (msb * 1e-3), 1)}
-        del xb, yb, wsb
+            step_b(i)
+        msb = time_block(step_b, 10, stream, hip_record)
+        ids = ib.cpu().numpy()
+        nd = int(np.unique(ids[ids >= 0]).size)
+        algb = algorithmic(dims, Tb, nd)
+        gbs = algb["layer_bytes"] / (msb * 1e-3) / 1e9
+        sweep[str(Tb)] = {"us_per_step": round(msb * 1e3, 1), "tokens_per_s": round(Tb / (msb * 1e-3), 1),
+                          "distinct_experts": nd, "algorithmic_bytes": algb["layer_bytes"],
+                          "GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        del xb, yb, ib, wsb
     if sweep:
-        log("layer at small batches: " + ", ".join(f"T={k} {v['us_per_step']} us" for k, v in sweep.items()))
+        log("layer at small batches: " + ", ".join(
+            f"T={k} {v['us_per_step']} us ({v['distinct_experts']} experts, {v['GBs']:.0f} GB/s)"
+            for k, v in sweep.items()))
 
     # ---------------------------------------------------------------- top-p tail drop, T = 1
     topp = None
@@ -425,15 +562,7 @@ def main():
 
         for i in range(args.warmup):
             step_p(i)
-        torch.cuda.synchronize()
-        evt = HipEvents(2)
-        hip_record(evt.ev[0], stream.cuda_stream)
-        for i in range(args.steps):
-            step_p(i)
-        hip_record(evt.ev[1], stream.cuda_stream)
-        torch.cuda.synchronize()
-        ms_p = evt.ms(evt.ev[0], evt.ev[1]) / args.steps
-        evt.close()
+        ms_p = time_block(step_p, args.steps, stream, hip_record)
         kept = (idx[:min(pool, args.steps)] >= 0).sum(dim=1).float().mean().item()
         topp = {"p": args.topp, "us_per_step": round(ms_p * 1e3, 2), "tokens_per_s": round(1.0 / (ms_p * 1e-3), 1),
                 "mean_experts_kept": round(kept, 2), "kind": "approximation (top-p tail drop), not the headline"}
@@ -452,15 +581,7 @@ def main():
 
         for i in range(args.warmup):
             step_i(i)
-        torch.cuda.synchronize()
-        evi = HipEvents(2)
-        hip_record(evi.ev[0], stream.cuda_stream)
-        for i in range(args.steps):
-            step_i(i)
-        hip_record(evi.ev[1], stream.cuda_stream)
-        torch.cuda.synchronize()
-        ms_i = evi.ms(evi.ev[0], evi.ev[1]) / args.steps
-        evi.close()
+        ms_i = time_block(step_i, args.steps, stream, hip_record)
         idot = {"us_per_step": round(ms_i * 1e3, 2), "tokens_per_s": round(1.0 / (ms_i * 1e-3), 1),
                 "kind": "approximation (int8-per-32 expert activations), not the headline"}
         log(f"decode T=1 with int8 activations: {ms_i * 1e3:.1f} us/step")
@@ -473,18 +594,7 @@ def main():
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
-        import oracle
-        nthreads = min(16, os.cpu_count() or 1)
-        n = args.cpu_tokens
-        x = k3gen.gen_x(dims, 1, n)
-        ex = oracle.ExpertSet(host_blobs, B, lay.offsets)
-        c0 = time.perf_counter()
-        oracle.layer(dims, x, dense, ex, nthreads=nthreads)
-        cs = time.perf_counter() - c0
-        cpu = {"value": round(n / cs, 3), "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
-               "sample": f"{n} K3-shape decode tokens (T=1 problems, one per thread at a time), "
-                         f"{cs:.1f} s wall"}
-        log(f"cpu oracle: {n / cs:.2f} tokens/s on {nthreads} threads")
+        cpu = cpu_baseline(dims, dense, host_blobs, lay, args.cpu_tokens_1, args.cpu_tokens)
 
     out = {
         "metric": "LatentMoE layer tokens/s (K3 decode, T=1); HBM GB/s @T=1, TFLOP/s @T=4096, % of MI355X peak",
@@ -504,7 +614,9 @@ def main():
                                f"rotated over {len(wts_rot)} copies", "T": T, "global_batch": T,
                    "parallelism": "single GPU"},
         "roofline": roofline,
+        "decode_steps": decode_steps,
         "prefill": prefill,
+        "skewed_prefill": skewed,
         "batch_sweep": sweep or None,
         "shared_experts": shared,
         "topp_decode": topp,

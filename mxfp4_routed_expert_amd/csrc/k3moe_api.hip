@@ -964,6 +964,12 @@ int k3moe_set_expert_path(int mode) {
   return prev;
 }
 
+int k3moe_prof_gemm_tiling(int *tile_tokens, int *rows_gateup, int *rows_down) {
+  if (!tile_tokens || !rows_gateup || !rows_down) return K3MOE_EINVAL;
+  grouped_mm_tiling(tile_tokens, rows_gateup, rows_down);
+  return K3MOE_OK;
+}
+
 const char *k3moe_prof_name(int i) {
   return (i >= 0 && i < g_prof.named) ? g_prof.names[i] : "";
 }

@@ -248,6 +248,8 @@ hipError_t launch_grouped(const GroupedArgs &a, int epi, int tokens_per_tile, in
 // column tiles of kMmBN slots per expert: at most ceil(P / kMmBN) + min(E, P) entries
 hipError_t launch_mm_tiles(const int32_t *expert_off, int E, int4 *tiles, int32_t *n_tiles, hipStream_t s);
 size_t grouped_mm_lds();
+// tokens per column tile, rows per block of the gate/up pass (each matrix) and of the down pass
+void grouped_mm_tiling(int *tile_tokens, int *rows_gateup, int *rows_down);
 hipError_t launch_grouped_mm(const MmArgs &a, int epi, int max_tiles, hipStream_t s);
 // ident: pair_slot is the identity (a one-token layer batch), so it is not read
 hipError_t launch_combine(const float *edn, const int32_t *pair_slot, const float *topk_w,

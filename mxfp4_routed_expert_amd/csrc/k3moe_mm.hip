@@ -439,6 +439,12 @@ void k_grouped_mm(MmArgs a) {
 
 size_t grouped_mm_lds() { return (size_t)K3_MM_STAGES * kStageB; }
 
+void grouped_mm_tiling(int *tile_tokens, int *rows_gateup, int *rows_down) {
+  *tile_tokens = kMmBN;
+  *rows_gateup = 256;
+  *rows_down = 512;
+}
+
 hipError_t launch_mm_tiles(const int32_t *expert_off, int E, int4 *tiles, int32_t *n_tiles, hipStream_t s) {
   if (E > 1024) return hipErrorInvalidValue;
   launch_kernel(k_mm_tiles, 1, 1024, 0, s, expert_off, E, tiles, n_tiles);

@@ -49,8 +49,8 @@ class k3moe_weights(ctypes.Structure):
 
 
 EXPORTS = ["k3moe_workspace_size", "k3moe_route", "k3moe_latent_proj_bf16", "k3moe_dispatch",
-           "k3moe_expert_glu_mxfp4", "k3moe_combine", "k3moe_layer", "k3moe_shared_workspace_size",
-           "k3moe_shared_glu_bf16", "k3moe_status_str"]
+           "k3moe_expert_glu_mxfp4", "k3moe_combine", "k3moe_layer",
+           "k3moe_shared_workspace_size", "k3moe_shared_glu_bf16", "k3moe_status_str"]
 
 _lib = None
 
@@ -93,6 +93,9 @@ def load(path: str | None = None):
     L.k3moe_layer_profiled.restype = ctypes.c_int
     L.k3moe_prof_name.argtypes = [ctypes.c_int]
     L.k3moe_prof_name.restype = ctypes.c_char_p
+    ip = ctypes.POINTER(ctypes.c_int)
+    L.k3moe_prof_gemm_tiling.argtypes = [ip, ip, ip]
+    L.k3moe_prof_gemm_tiling.restype = ctypes.c_int
     L.k3moe_set_expert_path.argtypes = [ctypes.c_int]
     L.k3moe_set_expert_path.restype = ctypes.c_int
     for n in EXPORTS[:-1]:
@@ -266,3 +269,11 @@ def k3moe_set_expert_path(mode: int) -> int:
     if rc < 0:
         raise K3MoeError(rc, "k3moe_set_expert_path")
     return rc
+
+
+def gemm_tiling():
+    """(tokens per column tile, gate/up rows per block, down rows per block) of the grouped
+    GEMM form (k3moe_prof_gemm_tiling)."""
+    a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(load().k3moe_prof_gemm_tiling(ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)), "k3moe_prof_gemm_tiling")
+    return a.value, b.value, c.value

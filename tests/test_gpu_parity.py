@@ -497,6 +497,42 @@ def test_tiny_mm_idot_both_expert_forms(tiny_mm, expert_path, mode, T):
     compare_idot(tiny_mm, T, 130 + T, f"tiny-mm int8 activations T={T} {mode}")
 
 
+@pytest.mark.parametrize("mode", ["gemv", "gemm"])
+@pytest.mark.parametrize("T", [3, 64, 300])
+def test_tiny_mm_idot_expert_stage_exact_bar(tiny_mm, expert_path, mode, T):
+    """The int8-activation expert products alone, on the oracle's own z (so both sides
+    round z to int8 identically): edn against the oracle's int8 expert at the exact bar.
+    The one decision the two sides can take apart is the rounding of an act value whose
+    scaled value a / d lies within the GPU's act error of a half step (the GPU's act is
+    about 1e-6 from the fp64 oracle's, so its a / d is within about 1e-4 of it). Pairs with
+    such a value (margin 5e-4, by the oracle's act) take the variant's relaxed bar; every
+    other pair is held to the exact bar, and they are most pairs."""
+    expert_path(k3moe.EXPERT_PATH_GEMV if mode == "gemv" else k3moe.EXPERT_PATH_GEMM)
+    d = dataclasses.replace(tiny_mm.dims, idot=1)
+    K, L, E = d.topk, d.latent, d.n_experts
+    x, _ = _inputs.gap_fixed_x(d, 140 + T, T, tiny_mm.dense["w_router"], tiny_mm.dense["bias"])
+    ref = oracle.layer(d, x, tiny_mm.dense, tiny_mm.ex, want_inner=True)
+    off, sp, _ = oracle.dispatch(ref["idx"], E)
+    ws = device.workspace(d, T)
+    edn = torch.empty((T * K, L), dtype=torch.float32, device="cuda")
+    k3moe.k3moe_expert_glu_mxfp4(d, T, t_(ref["z"]), tiny_mm.dev.experts_struct(), t_(off), t_(sp), edn, ws)
+    torch.cuda.synchronize()
+    got = edn.cpu().numpy()
+    tok = sp // K
+    exid = ref["idx"].reshape(-1)[sp]
+    edn_ref, act = oracle.expert_pairs(d, tok, exid, ref["z"], tiny_mm.ex, want_act=True)
+    # each act value's distance from a rounding boundary, in steps of its group's scale
+    g = act.reshape(act.shape[0], -1, 32)
+    dq = (np.max(np.abs(g), axis=2, keepdims=True) / np.float32(127.0)).astype(np.float32)
+    r = np.divide(g, dq, out=np.zeros_like(g), where=dq > 0).astype(np.float32)
+    dist = np.abs(np.abs(r - np.floor(r)) - np.float32(0.5))
+    clean = np.all(dist.reshape(act.shape[0], -1) > 5e-4, axis=1)
+    say(f"  int8 expert stage T={T} {mode}: {clean.mean():.2f} of {clean.size} pairs at the exact bar")
+    assert clean.mean() >= 0.8
+    check_rows(got[clean], edn_ref[clean], f"int8 expert stage T={T} {mode} (exact bar)")
+    check_rows(got, edn_ref, f"int8 expert stage T={T} {mode} (all pairs)", rel=IDOT_REL, absf=IDOT_ABSF)
+
+
 def test_k3_idot_layer_T1(k3):
     compare_idot(k3, 1, 1, "K3 int8 activations T=1")
 
@@ -650,9 +686,16 @@ def test_k3_shared_T4096_sampled(k3_shared):
     x = k3gen.gen_x(d, 3, T)
     y0 = np.random.default_rng(3).standard_normal((T, d.hidden)).astype(np.float32) * 0.05
     got = run_shared(d, 2, x, shd, y0)
+    # the first and last token of every 128-token tile of the GEMMs, then random tokens up
+    # to 512
+    tiles = np.arange(0, T, 128)
+    edge = np.unique(np.concatenate([tiles, np.minimum(tiles + 127, T - 1)]))
     rng = np.random.default_rng(4)
-    rows = np.concatenate([[0, T - 1], rng.choice(T, 24, replace=False)])
-    check_rows(got[rows], oracle.shared(d, x[rows], sh, y0[rows]), "K3 T=4096 sampled shared")
+    rows = np.sort(np.concatenate([edge, rng.choice(np.setdiff1d(np.arange(T), edge), 512 - edge.size,
+                                                    replace=False)]))
+    ref = np.concatenate([oracle.shared(d, x[rows[i:i + 128]], sh, y0[rows[i:i + 128]])
+                          for i in range(0, rows.size, 128)])
+    check_rows(got[rows], ref, f"K3 T=4096 shared on {rows.size} rows")
 
 
 def check_dispatch_of(h: Host, ids: np.ndarray, what: str):
@@ -672,7 +715,53 @@ def check_dispatch_of(h: Host, ids: np.ndarray, what: str):
     return o
 
 
-def prefill_case(h: Host, dense: dict, T: int, x_seed: int, nsample: int, what: str):
+def cover_rows(idx: np.ndarray, off: np.ndarray, sp: np.ndarray, total: int, seed: int, unit: int = 32):
+    """Tokens whose y rows are compared at full-batch sizes. Every run of `unit` consecutive
+    dispatched slots of every expert (so every column tile of the grouped GEMM, whose
+    tiles are whole multiples of 32 slots, and every expert's partial last tile) holds a
+    pair of a chosen token: a greedy cover, each step taking, for the first slot run not
+    yet covered, its token that covers the most runs not yet covered. Then random tokens
+    up to `total`, and the first and last token."""
+    T, K = idx.shape
+    n = int(off[-1])
+    slot_of = np.empty(T * K, np.int64)
+    slot_of[sp[:n]] = np.arange(n)
+    e_of = idx.reshape(-1).astype(np.int64)
+    runs_e = (np.diff(off).astype(np.int64) + unit - 1) // unit
+    first_run = np.concatenate([[0], np.cumsum(runs_e)])
+    run_of = first_run[e_of] + (slot_of - off[e_of]) // unit     # each pair's slot run
+    tok_runs = run_of.reshape(T, K)
+    covered = np.zeros(int(first_run[-1]), bool)
+    by_run = np.argsort(run_of, kind="stable")
+    starts = np.searchsorted(run_of[by_run], np.arange(covered.size + 1))
+    chosen = {0, T - 1}
+    for t in chosen:
+        covered[tok_runs[t]] = True
+    for u in range(covered.size):
+        if covered[u]:
+            continue
+        cand = by_run[starts[u]:starts[u + 1]] // K
+        gain = [np.count_nonzero(~covered[tok_runs[t]]) for t in cand]
+        t = int(cand[int(np.argmax(gain))])
+        chosen.add(t)
+        covered[tok_runs[t]] = True
+    assert covered.all()
+    rng = np.random.default_rng(seed)
+    rest = np.setdiff1d(np.arange(T), np.fromiter(chosen, np.int64))
+    extra = rng.choice(rest, max(0, min(total - len(chosen), rest.size)), replace=False)
+    return np.sort(np.concatenate([np.fromiter(chosen, np.int64), extra]))
+
+
+def oracle_rows(dims, x: np.ndarray, rows: np.ndarray, dense: dict, ex, what: str, chunk: int = 64):
+    """The oracle's layer on x[rows], in chunks, printing progress (a few seconds each)."""
+    outs = []
+    for i in range(0, len(rows), chunk):
+        outs.append(oracle.layer(dims, x[rows[i:i + chunk]], dense, ex))
+        say(f"  {what}: oracle rows {min(i + chunk, len(rows))}/{len(rows)}")
+    return {k: np.concatenate([o[k] for o in outs]) for k in outs[0]}
+
+
+def prefill_case(h: Host, dense: dict, T: int, x_seed: int, nrows: int, what: str):
     say(f"{what}: gap rule over all tokens (oracle router)")
     x, _ = _inputs.gap_fixed_x(h.dims, x_seed, T, dense["w_router"], dense["bias"])
     xd = t_(x.view(np.int16))
@@ -690,15 +779,17 @@ def prefill_case(h: Host, dense: dict, T: int, x_seed: int, nsample: int, what: 
     assert np.array_equal(idx, ridx), f"{what}: expert ids differ"
     check_rows(w, rw, f"{what} weights", rel=1e-6, absf=1e-6)
     off = check_dispatch_of(h, ridx, what)
-    rng = np.random.default_rng(x_seed)
-    rows = np.concatenate([[0, T - 1], rng.choice(T, nsample, replace=False)])
-    ref = oracle.layer(h.dims, x[rows], dense, h.ex)
-    check_rows(y[rows], ref["y"], f"{what} sampled y")
+    _, sp, _ = oracle.dispatch(ridx, h.dims.n_experts)
+    rows = cover_rows(ridx, off, sp, nrows, x_seed)
+    say(f"{what}: y compared on {len(rows)} rows covering every 32-slot run of every expert")
+    ref = oracle_rows(h.dims, x, rows, dense, h.ex, what)
+    assert np.array_equal(ref["idx"], ridx[rows])
+    check_rows(y[rows], ref["y"], f"{what} y on the covering rows")
     return off
 
 
 def test_k3_layer_config3_T4096_sampled(k3):
-    off = prefill_case(k3, k3.dense, 4096, 3, 24, "K3 T=4096")
+    off = prefill_case(k3, k3.dense, 4096, 3, 512, "K3 T=4096")
     counts = np.diff(off)
     say(f"  experts touched {np.count_nonzero(counts)}/{k3.dims.n_experts}, max tokens {counts.max()}")
     # the bias spread makes routing uneven: both empty experts and experts whose token
@@ -710,7 +801,7 @@ def test_k3_layer_config4_T8192_skewed_sampled(k3):
     dense = dict(k3.dense)
     p = _inputs.skew_params()
     dense["bias"] = _inputs.skewed_bias(k3.dense["bias"])
-    off = prefill_case(k3, dense, 8192, 4, 24, "K3 skewed T=8192")
+    off = prefill_case(k3, dense, 8192, 4, 512, "K3 skewed T=8192")
     counts = np.diff(off)
     hot = (np.arange(k3.dims.n_experts) % p["hot_every"]) == 0
     share = counts[hot].sum() / counts.sum()
