@@ -63,7 +63,8 @@
  *  - Threads: entry points keep no state between calls and may be called from several
  *    host threads at once, each call with its own workspace (calls that share a
  *    workspace must be ordered on one stream). The only per-process state is each
- *    kernel's dynamic-LDS attribute, set once per device on first use.
+ *    kernel's dynamic-LDS attribute, set once per device on first use, and the fixed
+ *    workspace array of k3moe_layer_noalloc (one per device).
  *  - Errors: every call returns K3MOE_OK (0) or a negative code. All argument
  *    checks happen on the host before any launch, so a refused call has launched
  *    nothing; on K3MOE_EHIP the outputs are unspecified. Nothing prints or aborts.
@@ -185,6 +186,20 @@ int k3moe_combine(const k3moe_dims *d, int32_t T, const float *edn, const int32_
 int k3moe_layer(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_weights *w,
                 float *y, int32_t *topk_idx_out, float *topk_w_out,
                 void *ws, size_t ws_bytes, void *stream);
+
+/* The whole layer as k3moe_layer, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation): the
+ * call takes no workspace argument and allocates nothing; its workspace is a fixed
+ * device array of K3MOE_NOALLOC_SCRATCH_BYTES inside the library, one per device (each
+ * device that runs the call holds it until the process ends; its address is looked up
+ * on the call's first use on that device). Batches whose k3moe_workspace_size exceeds
+ * that size are refused with K3MOE_EWORKSPACE before anything runs (at the K3 shape, up
+ * to 32 tokens fit). The array's content on entry does not matter. All calls on one
+ * device share its array: calls that overlap on one device (on two streams, or from two
+ * threads without ordering) race and give unspecified results. */
+#define K3MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+int k3moe_layer_noalloc(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_weights *w,
+                        float *y, int32_t *topk_idx_out, float *topk_w_out, void *stream);
 
 /* Step 6, the shared experts (README section 9, step 6; colibri "Architecture notes",
  * Stable LatentMoE: two fused full-width shared experts, inter 6144 in K3). They run on

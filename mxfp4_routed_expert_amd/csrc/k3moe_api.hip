@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "k3moe.h"
 #include "k3moe_prof.h"
@@ -806,7 +807,47 @@ int prof_end() {
 
 }  // namespace
 
+// ---- the entry point that allocates nothing (k3moe_layer_noalloc): its workspace is this
+// file-scope device array, one copy per device, held until the process ends. In host code
+// the name `scratch` is only a host-side stand-in: the device address of each device's
+// copy comes from hipGetSymbolAddress, taken once per device with that device current,
+// and only that address is ever handed to kernels.
+static __device__ __align__(256) uint8_t scratch[K3MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxDevices];  // device d's address of `scratch`, once looked up
+
+// The current device's copy of `scratch` (looked up on the first call on that device).
+int scratch_for_current_device(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return K3MOE_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return K3MOE_EHIP;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return K3MOE_OK;
+}
+
+}  // namespace
+
 extern "C" {
+
+int k3moe_layer_noalloc(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_weights *wt, float *y,
+                        int32_t *topk_idx_out, float *topk_w_out, void *stream) {
+  K3_TRY(check_dims(d));
+  K3_TRY(check_T(d, T));
+  // the workspace this call needs must fit the fixed array
+  if (carve(d, T, nullptr).bytes > (size_t)K3MOE_NOALLOC_SCRATCH_BYTES) return K3MOE_EWORKSPACE;
+  void *ws = nullptr;
+  K3_TRY(scratch_for_current_device(&ws));
+  return k3moe_layer(d, T, x, wt, y, topk_idx_out, topk_w_out, ws, (size_t)K3MOE_NOALLOC_SCRATCH_BYTES, stream);
+}
 
 int k3moe_workspace_size(const k3moe_dims *d, int32_t T, size_t *bytes) {
   K3_TRY(check_dims(d));

@@ -49,7 +49,7 @@ class k3moe_weights(ctypes.Structure):
 
 
 EXPORTS = ["k3moe_workspace_size", "k3moe_route", "k3moe_latent_proj_bf16", "k3moe_dispatch",
-           "k3moe_expert_glu_mxfp4", "k3moe_combine", "k3moe_layer",
+           "k3moe_expert_glu_mxfp4", "k3moe_combine", "k3moe_layer", "k3moe_layer_noalloc",
            "k3moe_shared_workspace_size", "k3moe_shared_glu_bf16", "k3moe_status_str"]
 
 _lib = None
@@ -81,6 +81,7 @@ def load(path: str | None = None):
     L.k3moe_expert_glu_mxfp4.argtypes = [D, i32, vp, ctypes.POINTER(k3moe_experts), vp, vp, vp, vp, sz, vp]
     L.k3moe_combine.argtypes = [D, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.k3moe_layer.argtypes = [D, i32, vp, ctypes.POINTER(k3moe_weights), vp, vp, vp, vp, sz, vp]
+    L.k3moe_layer_noalloc.argtypes = [D, i32, vp, ctypes.POINTER(k3moe_weights), vp, vp, vp, vp]
     L.k3moe_shared_workspace_size.argtypes = [D, i32, i32, ctypes.POINTER(sz)]
     L.k3moe_shared_glu_bf16.argtypes = [D, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     L.k3moe_shared_profiled.argtypes = [D, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp,
@@ -213,6 +214,19 @@ def k3moe_layer(dims, T, x, weights: k3moe_weights, y, topk_idx_out, topk_w_out,
                             _ptr(topk_idx_out), _ptr(topk_w_out), p, n, _stream(stream))
     if check:
         _check(rc, "k3moe_layer")
+    return rc
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # K3MOE_NOALLOC_SCRATCH_BYTES
+
+
+def k3moe_layer_noalloc(dims, T, x, weights: k3moe_weights, y, topk_idx_out, topk_w_out, stream=None, check=True):
+    """k3moe_layer with the library's own fixed device array as workspace (allocates nothing)."""
+    rc = load().k3moe_layer_noalloc(ctypes.byref(_dims(dims)), T, _ptr(x),
+                                    ctypes.byref(weights) if weights is not None else None, _ptr(y),
+                                    _ptr(topk_idx_out), _ptr(topk_w_out), _stream(stream))
+    if check:
+        _check(rc, "k3moe_layer_noalloc")
     return rc
 
 

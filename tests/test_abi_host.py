@@ -211,3 +211,16 @@ def test_expert_path_switch_is_per_thread():
         assert k3moe.k3moe_set_expert_path(k3moe.EXPERT_PATH_AUTO) == k3moe.EXPERT_PATH_GEMV
     finally:
         k3moe.k3moe_set_expert_path(prev)
+
+
+def test_noalloc_refuses_on_the_host():
+    # the no-allocation layer: bad arguments and batches whose workspace exceeds its fixed
+    # device array are refused before any HIP call
+    L = k3moe.load()
+    fake = FAKE
+    w = k3moe.k3moe_weights(fake, fake, fake, fake, fake, _experts())
+    assert k3moe.k3moe_workspace_size(k3gen.K3, 64) > k3moe.NOALLOC_SCRATCH_BYTES
+    assert k3moe.k3moe_layer_noalloc(k3gen.K3, 64, fake, w, fake, None, None, check=False) == k3moe.K3MOE_EWORKSPACE
+    assert k3moe.k3moe_layer_noalloc(_d(hidden=0), 4, fake, w, fake, None, None, check=False) == k3moe.K3MOE_EINVAL
+    assert k3moe.k3moe_layer_noalloc(_d(), -1, fake, w, fake, None, None, check=False) == k3moe.K3MOE_EINVAL
+    assert L.k3moe_layer_noalloc(None, 4, fake, ctypes.byref(w), fake, None, None, None) == k3moe.K3MOE_EINVAL
