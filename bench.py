@@ -296,6 +296,46 @@ def routing_stats(dims, idx: np.ndarray, hot=None):
     return out
 
 
+def bench_graph(dims, xs, pool, row, wts_rot, ws, y, stream, hip_record, steps=64, replays=5):
+    """The decode step's kernel launches captured into one HIP graph of `steps` consecutive
+    layer calls (tokens from the pool, dense weights rotated as in the eager steps) and
+    replayed: the launch gaps between the layer's kernels without the host's launch path.
+    Every replay's last output is checked against an eager call on the same token."""
+    import torch
+
+    from mxfp4_routed_expert_amd import k3moe
+    T = 1
+    last = (steps - 1) % pool
+
+    def call(i, out):
+        k3moe.k3moe_layer(dims, T, xs.data_ptr() + (i % pool) * row, wts_rot[i % len(wts_rot)], out, None, None,
+                          ws, stream=stream)
+
+    y_ref = torch.empty_like(y)
+    call(steps - 1, y_ref)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(steps):
+            call(i, y)
+    torch.cuda.synchronize()
+    ok = True
+    with torch.cuda.stream(stream):  # replays run on the stream the events are recorded on
+        for _ in range(2):  # replays with eager work and synchronisations between them
+            g.replay()
+            torch.cuda.synchronize()
+            ok = ok and bool(torch.equal(y, y_ref))
+            call(0, y)
+            torch.cuda.synchronize()
+        ms = time_block(lambda i: g.replay(), replays, stream, hip_record) / steps
+    torch.cuda.synchronize()
+    ok = ok and bool(torch.equal(y, y_ref))
+    del g
+    log(f"decode T=1 from a HIP graph of {steps} layer steps: {ms * 1e3:.1f} us/step (replays match eager: {ok})")
+    return {"us_per_step": round(ms * 1e3, 2), "tokens_per_s": round(1.0 / (ms * 1e-3), 1),
+            "steps_per_graph": steps, "replays": replays, "matches_eager": ok, "token_of_last_step": last}
+
+
 def bench_prefill(args, dims, wts, x, bias_dev, stream, hip_record, what):
     """One prefill workload (x already on the device): ms per step, per-kernel us of a warm
     profiled call, the routing's load balance, algorithmic TFLOP/s."""
@@ -380,6 +420,7 @@ def main():
                     help="skip timing the int8-activation expert variant (an approximation, never the headline)")
     ap.add_argument("--no-shared", action="store_true",
                     help="skip the shared-expert measurement (a call of its own, after the layer)")
+    ap.add_argument("--no-graph", action="store_true", help="skip the decode steps replayed from a HIP graph")
     ap.add_argument("--cpu-tokens", type=int, default=64, help="oracle tokens on all cores")
     ap.add_argument("--cpu-tokens-1", type=int, default=4, help="oracle tokens on one thread")
     ap.add_argument("--dense-copies", type=int, default=4,
@@ -493,6 +534,7 @@ def main():
     decode_steps = {"us_mean_block": round(ms_step * 1e3, 2), "us_median": round(float(np.median(each)), 2),
                     "us_min": round(float(each.min()), 2), "us_max": round(float(each.max()), 2),
                     "n_each": int(each.size)}
+    graph = None if args.no_graph else bench_graph(dims, xs, pool, row, wts_rot, ws, y, stream, hip_record)
 
     # ---------------------------------------------------------------- prefill, T = 4096 and skewed T = 8192
     prefill = skewed = None
@@ -615,6 +657,7 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": roofline,
         "decode_steps": decode_steps,
+        "decode_graph": graph,
         "prefill": prefill,
         "skewed_prefill": skewed,
         "batch_sweep": sweep or None,

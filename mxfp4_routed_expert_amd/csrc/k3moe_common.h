@@ -192,25 +192,34 @@ __device__ __forceinline__ int fp6_piece_exp(float m) {
 // One fp6 piece of up to four 8-value slices at once, on the hardware e2m3 conversion:
 // y[n][0..7] are this lane's values of slice n in record order and ex[n] its group's
 // piece exponent. The values are scaled by 2^-ex exactly, rounded to e2m3 (nearest,
-// ties to even, saturating at 7.5), decoded back, and the rounded piece is subtracted
-// from y (exactly). Returns the codes: slice n's 8 codes at bits 48n .. 48n+47.
-template <int N>
+// ties to even, saturating at 7.5), and (unless LAST: no piece follows) decoded back and
+// subtracted from y: the rounded piece times 2^ex is exact, and so is the difference.
+// Returns the codes: slice n's 8 codes at bits 48n .. 48n+47.
+template <int N, bool LAST = false>
 __device__ __forceinline__ u32x6 fp6_piece_hw(float (&y)[N][8], const int (&ex)[N]) {
   static_assert(N >= 1 && N <= 4, "one conversion holds 32 values");
+  float dn[N], up[N];
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    dn[n] = ldexpf(1.f, -ex[n]);  // exact powers of two (2^-127 as a denormal)
+    up[n] = ldexpf(1.f, ex[n]);
+  }
   f32x16 va, vb;  // value 2i of slice n at va[4n + i], value 2i+1 at vb[4n + i]
 #pragma unroll
   for (int n = 0; n < 4; ++n)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      va[4 * n + i] = n < N ? ldexpf(y[n < N ? n : 0][2 * i], -ex[n < N ? n : 0]) : 0.f;
-      vb[4 * n + i] = n < N ? ldexpf(y[n < N ? n : 0][2 * i + 1], -ex[n < N ? n : 0]) : 0.f;
+      va[4 * n + i] = n < N ? y[n < N ? n : 0][2 * i] * dn[n < N ? n : 0] : 0.f;
+      vb[4 * n + i] = n < N ? y[n < N ? n : 0][2 * i + 1] * dn[n < N ? n : 0] : 0.f;
     }
   const u32x6 c = __builtin_bit_cast(u32x6, __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(va, vb, 1.0f));
-  const f32x32 r = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(__builtin_bit_cast(i32x6, c), 1.0f);
+  if constexpr (!LAST) {
+    const f32x32 r = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(__builtin_bit_cast(i32x6, c), 1.0f);
 #pragma unroll
-  for (int n = 0; n < N; ++n)
+    for (int n = 0; n < N; ++n)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) y[n][j] -= ldexpf(r[8 * n + j], ex[n]);
+      for (int j = 0; j < 8; ++j) y[n][j] = fmaf(-r[8 * n + j], up[n], y[n][j]);
+  }
   return c;
 }
 
@@ -235,7 +244,7 @@ __device__ __forceinline__ void quant_groups_fp6(float (&r)[N][8], int k4, uint8
       m = fmaxf(m, lane_xor2(m));
       ex[n] = fp6_piece_exp(m);
     }
-    const u32x6 c = fp6_piece_hw<N>(r, ex);
+    const u32x6 c = p + 1 < kFp6Pieces ? fp6_piece_hw<N>(r, ex) : fp6_piece_hw<N, true>(r, ex);
 #pragma unroll
     for (int n = 0; n < N; ++n) {
       if (!ok[n]) continue;
@@ -261,16 +270,19 @@ __device__ __forceinline__ void quant_group32_fp6(float (&v)[32], uint8_t *rec) 
 #pragma unroll
     for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(v[i]));
     const int ex = fp6_piece_exp(m);
+    const float dn = ldexpf(1.f, -ex), up = ldexpf(1.f, ex);  // exact powers of two
     f32x16 va, vb;  // value 2i at va[i], value 2i+1 at vb[i]: codes in value order
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      va[i] = ldexpf(v[2 * i], -ex);
-      vb[i] = ldexpf(v[2 * i + 1], -ex);
+      va[i] = v[2 * i] * dn;
+      vb[i] = v[2 * i + 1] * dn;
     }
     const u32x6 c = __builtin_bit_cast(u32x6, __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(va, vb, 1.0f));
-    const f32x32 r = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(__builtin_bit_cast(i32x6, c), 1.0f);
+    if (p + 1 < kFp6Pieces) {  // the residual for the next piece (exact)
+      const f32x32 r = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(__builtin_bit_cast(i32x6, c), 1.0f);
 #pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] -= ldexpf(r[i], ex);
+      for (int i = 0; i < 32; ++i) v[i] = fmaf(-r[i], up, v[i]);
+    }
     uint32_t *dst = (uint32_t *)(rec + p * kPieceRec);
     *(u32x4 *)dst = u32x4{c[0], c[1], c[2], c[3]};
     *(u32x2 *)(dst + 4) = u32x2{c[4], c[5]};
@@ -292,7 +304,7 @@ __device__ __forceinline__ void quant_group_fp6_kq(float (&r)[8], int kq, uint8_
 #pragma unroll
     for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(y[0][i]));
     const int ex[1] = {fp6_piece_exp(max_rows4(m))};
-    const u32x6 c = fp6_piece_hw<1>(y, ex);
+    const u32x6 c = p + 1 < kFp6Pieces ? fp6_piece_hw<1>(y, ex) : fp6_piece_hw<1, true>(y, ex);
     const uint32_t lo = c[0] & 0xFFFFFFu;                          // values 4kq .. 4kq+3
     const uint32_t hi = ((c[0] >> 24) | (c[1] << 8)) & 0xFFFFFFu;  // values 16+4kq ..
     if (st) {
@@ -360,24 +372,19 @@ __device__ __forceinline__ int block_excl_scan(int v, int *sh_wave, int *total) 
   return base + x - v;
 }
 
-// tanh in fp32 to about 2e-7 relative: below |x| = 0.55 its odd Taylor series through
-// x^17 (next term under 3e-9), above it 1 - 2 / (exp(2|x|) + 1) with the hardware exp2
-// and reciprocal (the relative error stays near that of exp there).
+// tanh in fp32 to about 4e-7 relative: below |x| = 0.25 its odd Taylor series through
+// x^9 (the next term is under 1e-8 relative there), above it (e^2x - 1) / (e^2x + 1) with
+// the hardware exp2 and reciprocal, x clamped to +-9.5 (where tanh rounds to +-1 in fp32).
 __device__ __forceinline__ float tanh_f(float x) {
-  const float a = fabsf(x);
   const float x2 = x * x;
-  float p = 6404582.f / 10854718875.f;
-  p = fmaf(p, x2, -929569.f / 638512875.f);
-  p = fmaf(p, x2, 21844.f / 6081075.f);
-  p = fmaf(p, x2, -1382.f / 155925.f);
-  p = fmaf(p, x2, 62.f / 2835.f);
+  float p = 62.f / 2835.f;
   p = fmaf(p, x2, -17.f / 315.f);
   p = fmaf(p, x2, 2.f / 15.f);
   p = fmaf(p, x2, -1.f / 3.f);
   const float series = fmaf(x * x2, p, x);
-  const float e = __builtin_amdgcn_exp2f(2.8853900817779268f * a);  // exp(2a)
-  const float big = copysignf(1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f), x);
-  return a < 0.55f ? series : big;
+  const float e = __builtin_amdgcn_exp2f(2.8853900817779268f * __builtin_amdgcn_fmed3f(x, -9.5f, 9.5f));
+  const float big = (e - 1.f) * __builtin_amdgcn_rcpf(e + 1.f);
+  return fabsf(x) < 0.25f ? series : big;
 }
 
 // logistic 1 / (1 + exp(-g)) with the hardware exp2 and reciprocal

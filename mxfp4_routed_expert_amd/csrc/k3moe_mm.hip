@@ -106,6 +106,8 @@ void k_grouped_mm(MmArgs a) {
   static_assert(NS == 3 || NS == 4, "ring depth: one scale load (12 or 16 bytes) per ring turn");
   static_assert((kMmBN / 2) % NWV == 0, "every wave issues the same number of token copies");
   static_assert((size_t)NS * kStageB <= 160 * 1024, "the token ring fits in LDS");
+  static_assert(EPI != kEpiSitu || (size_t)NWV * kMmBN * (RW / 32 * kGroupRec + 16) <= (size_t)NS * kStageB,
+                "the epilogue's records fit in the ring's LDS");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -353,59 +355,84 @@ void k_grouped_mm(MmArgs a) {
     // saturating) by the hardware conversion, 32 values (4 groups) per instruction, and
     // converted back exactly to form the next residual.
     constexpr int NG = kNcbMax * GPW;  // groups per lane
-    constexpr int NGP = (NG + 3) / 4 * 4;  // padded to whole conversions (4 groups each)
-    uint8_t *recs = smem + wave * (kMmBN * GPW * kGroupRec);  // [token][group] records
+    constexpr int NB = (NG + 3) / 4;    // conversions of 4 groups (32 values) each
+    // [token][group] records; a token's row is padded by 16 bytes so that the 16 tokens
+    // of one store instruction, and the 8 lanes of one 16-byte read, fall on distinct banks
+    constexpr int RSTR = GPW * kGroupRec + 16;
+    uint8_t *recs = smem + wave * (kMmBN * RSTR);
     const float b1 = a.b1, b2 = a.b2;
-    float y[NGP][8];
+    float y[NG][8];
 #pragma unroll
-    for (int gi = NG; gi < NGP; ++gi)
+    for (int cb = 0; cb < kNcbMax; ++cb) {
+      if (cb < ncb) {  // (uniform) column blocks past the tile's tokens are not computed
 #pragma unroll
-      for (int j = 0; j < 8; ++j) y[gi][j] = 0.f;
+        for (int g = 0; g < GPW; ++g)
 #pragma unroll
-    for (int cb = 0; cb < kNcbMax; ++cb)
+          for (int j = 0; j < 8; ++j) {
+            const int f = 2 * g + (j >> 2);
+            y[cb * GPW + g][j] = situ(acc[f][cb][j & 3], acc[FPM + f][cb][j & 3], b1, b2);
+          }
+      } else {
 #pragma unroll
-      for (int g = 0; g < GPW; ++g)
+        for (int g = 0; g < GPW; ++g)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int f = 2 * g + (j >> 2);
-          y[cb * GPW + g][j] = cb < ncb ? situ(acc[f][cb][j & 3], acc[FPM + f][cb][j & 3], b1, b2) : 0.f;
-        }
+          for (int j = 0; j < 8; ++j) y[cb * GPW + g][j] = 0.f;
+      }
+    }
 #pragma unroll
     for (int p = 0; p < kFp6Pieces; ++p) {
-      int ex[NGP];
 #pragma unroll
-      for (int gi = 0; gi < NGP; ++gi) {
-        float m = 0.f;
+      for (int bt = 0; bt < NB; ++bt) {
+        if ((4 * bt) / GPW >= ncb) continue;  // (uniform) no real group in this conversion
+        int ex[4];
+        float dn[4], up[4];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(y[gi][j]));
-        ex[gi] = fp6_piece_exp(max_rows4(m));
-      }
+        for (int q = 0; q < 4; ++q) {
+          const int gi = 4 * bt + q;
+          ex[q] = 0;
+          if (gi < NG) {
+            float m = 0.f;
 #pragma unroll
-      for (int bt = 0; bt < NGP / 4; ++bt) {
+            for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(y[gi][j]));
+            ex[q] = fp6_piece_exp(max_rows4(m));
+          }
+          dn[q] = ldexpf(1.f, -ex[q]);  // exact powers of two (2^-127 as a denormal)
+          up[q] = ldexpf(1.f, ex[q]);
+        }
         f32x16 va, vb;  // value 2i of group q at va[4q + i], value 2i+1 at vb[4q + i]
 #pragma unroll
         for (int q = 0; q < 4; ++q)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            va[4 * q + i] = ldexpf(y[4 * bt + q][2 * i], -ex[4 * bt + q]);
-            vb[4 * q + i] = ldexpf(y[4 * bt + q][2 * i + 1], -ex[4 * bt + q]);
+            const int gi = 4 * bt + q;
+            va[4 * q + i] = gi < NG ? y[gi < NG ? gi : 0][2 * i] * dn[q] : 0.f;
+            vb[4 * q + i] = gi < NG ? y[gi < NG ? gi : 0][2 * i + 1] * dn[q] : 0.f;
           }
         // codes in value order: group q's 8 codes are bits 48q .. 48q+47
         const u32x6 c = __builtin_bit_cast(u32x6, __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(va, vb, 1.0f));
-        const f32x32 r = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(__builtin_bit_cast(i32x6, c), 1.0f);
+        if (p + 1 < kFp6Pieces) {
+          // the next piece takes the residual: the rounded piece, decoded exactly and scaled
+          // back by its power of two, is subtracted without rounding error
+          const f32x32 r = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(__builtin_bit_cast(i32x6, c), 1.0f);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int gi = 4 * bt + q;
+            if (gi < NG)
+#pragma unroll
+              for (int j = 0; j < 8; ++j) y[gi][j] = fmaf(-r[8 * q + j], up[q], y[gi][j]);
+          }
+        }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int gi = 4 * bt + q, cb = gi / GPW, g = gi % GPW;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) y[gi][j] -= ldexpf(r[8 * q + j], ex[gi]);
           if (gi < NG && cb < ncb) {
-            uint8_t *dst = recs + ((16 * cb + rl) * GPW + g) * kGroupRec + p * kPieceRec;
+            uint8_t *dst = recs + (16 * cb + rl) * RSTR + g * kGroupRec + p * kPieceRec;
 #pragma unroll
             for (int h = 0; h < 3; ++h) {
               const int bit = 48 * q + 16 * h;
               *(uint16_t *)(dst + 6 * kq + 2 * h) = (uint16_t)(c[bit >> 5] >> (bit & 31));
             }
-            if (kq == 0) dst[24] = (uint8_t)(ex[gi] + 127);
+            if (kq == 0) dst[24] = (uint8_t)(ex[q] + 127);
           }
         }
       }
@@ -416,7 +443,7 @@ void k_grouped_mm(MmArgs a) {
       uint8_t *dst = a.outq + (size_t)(s0 + t) * (size_t)(a.M / 32) * kGroupRec + (size_t)(rw0 / 32) * kGroupRec;
       const int nb = (nrw / 32) * kGroupRec;  // this wave's groups inside M
       for (int c = 0; c < nb / 16; ++c)
-        *(u32x4 *)(dst + 16 * c) = *(const u32x4 *)(recs + t * GPW * kGroupRec + 16 * c);
+        *(u32x4 *)(dst + 16 * c) = *(const u32x4 *)(recs + t * RSTR + 16 * c);
     }
   } else {
 #pragma unroll
