@@ -121,7 +121,11 @@ int64_t max_mm_tiles(const k3moe_dims *d, int32_t T) {
   return (P + kMmBN - 1) / kMmBN + (P < d->n_experts ? P : d->n_experts);
 }
 
-// grouped GEMM form for a pass with K columns and activation records of rec_bytes
+// grouped GEMM form for a pass with K columns and activation records of rec_bytes.
+// Measured at the K3 shape (both passes, whole layer): the GEMV form is faster up to
+// about 3 pairs per expert (T = 128: 1.99 against 2.32 ms), the two meet near 3.4
+// (T = 192: 2.65 against 2.59 ms) and the GEMM form wins beyond (T = 256: 2.75 against
+// 3.23 ms).
 bool use_mm(const k3moe_dims *d, int32_t T, int K, int64_t rec_bytes, const k3moe_mxfp4 &m0,
             const k3moe_mxfp4 &m1) {
   if (g_expert_path == 1 || K % 128 != 0 || rec_bytes >= ((int64_t)1 << 31)) return false;
@@ -129,7 +133,7 @@ bool use_mm(const k3moe_dims *d, int32_t T, int K, int64_t rec_bytes, const k3mo
   for (const k3moe_mxfp4 *m : {&m0, &m1})
     if (((uintptr_t)m->scales & 3u) || (m->scales_expert_stride & 3)) return false;
   if (g_expert_path == 2) return true;
-  return (int64_t)T * d->topk >= 2 * (int64_t)d->n_experts;
+  return (int64_t)T * d->topk >= 3 * (int64_t)d->n_experts;
 }
 
 Ws carve(const k3moe_dims *d, int32_t T, void *base) {
