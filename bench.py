@@ -283,7 +283,9 @@ def routing_stats(dims, idx: np.ndarray, hot=None):
     tile, rows_gu, rows_dn = k3moe.gemm_tiling()
     ncol = (counts + tile - 1) // tile
     # the GEMM form walks (column tile, row block) entries; entry q runs on XCD q // ceil(n / 8)
-    cols = np.concatenate([np.minimum(tile, c - tile * np.arange(n)) for c, n in zip(counts, ncol) if n])
+    # an expert's tokens split evenly over its tiles, each size rounded up to 32 (the last takes the rest)
+    size = [-(-c // n) + 31 & ~31 if n else 0 for c, n in zip(counts, ncol)]
+    cols = np.concatenate([np.minimum(z, c - z * np.arange(n)) for c, n, z in zip(counts, ncol, size) if n])
     for name, rows, M in (("gateup", rows_gu, dims.inter), ("down", rows_dn, dims.latent)):
         rb = (M + rows - 1) // rows  # row blocks of each column tile
         work = np.repeat((cols + 15) // 16, rb)  # 16-token column blocks of each entry

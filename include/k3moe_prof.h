@@ -43,10 +43,12 @@ int k3moe_shared_profiled(const k3moe_dims *d, int32_t n_shared, int32_t T, cons
  * thread's. Returns the thread's previous mode, or K3MOE_EINVAL for another value. */
 int k3moe_set_expert_path(int mode);
 
-/* MEASUREMENT ONLY. The grouped GEMM form's tiling, for load-balance reports: tokens per
- * column tile, and rows per block of the gate/up pass (of w1 and of w3 each) and of the
- * down pass. Entry q of the (column tile, row block) list, tiles in expert order, runs on
- * XCD q / ceil(entries / 8). */
+/* MEASUREMENT ONLY. The grouped GEMM form's tiling, for load-balance reports: the most
+ * tokens per column tile, and rows per block of the gate/up pass (of w1 and of w3 each) and
+ * of the down pass. An expert's n tokens take ceil(n / tile_tokens) column tiles of
+ * ceil(n / tiles) tokens rounded up to a multiple of 32 (the last tile takes the rest).
+ * Entry q of the (column tile, row block) list, tiles in expert order, runs on XCD
+ * q / ceil(entries / 8). */
 int k3moe_prof_gemm_tiling(int *tile_tokens, int *rows_gateup, int *rows_down);
 
 #ifdef __cplusplus

@@ -2,9 +2,9 @@
 //
 // The same two passes as the grouped GEMV (gate/up with the SiTU-GLU epilogue, then
 // down), organised as a GEMM: a block of 8 waves owns 256 rows of w1 and of w3 (gate/up)
-// or 512 rows of w2 (down) of one expert and up to kMmBN (96) of that expert's tokens,
-// so each weight byte is read from HBM once per 96 tokens: at 4096 tokens x top-16 of
-// 896 experts (73 pairs per expert on average) nearly every expert is one column tile.
+// or 512 rows of w2 (down) of one expert and up to kMmBN (96) of that expert's tokens
+// (one column tile). An expert's column tiles run side by side and share its weights in
+// L2: at 4096 tokens x top-16 of 896 experts the 739 experts touched take 1154 tiles.
 //
 // Operands, in the layout of the MXFP4 format (low nibble = even column, one ue8m0 scale
 // per 32 columns) and of the fp6 activation pieces:
@@ -57,8 +57,12 @@ typedef unsigned u32x3 __attribute__((ext_vector_type(3)));
 
 }  // namespace
 
-// One block: entry e's column tiles are numbered first .. first+n-1, each a run of up to
-// kMmBN sorted slots. tiles[j] = {expert, first tile of that expert, its tile count, 0}.
+// One block: entry e's column tiles are numbered first .. first+n-1. An expert with n
+// sorted slots takes ceil(n / kMmBN) tiles of equal size rounded up to 32 slots (the last
+// takes the rest): its tiles' blocks run side by side on one XCD and stream the same
+// weight lines, and tiles of equal width keep pace, so the lines are fetched from HBM
+// once more often (measured 1.7% faster than tiles of kMmBN and a remainder at 4096
+// tokens). tiles[j] = {expert, first tile of that expert, its tile count, slots per tile}.
 __global__ __launch_bounds__(1024) void k_mm_tiles(const int32_t *__restrict__ expert_off, int E,
                                                    int4 *__restrict__ tiles, int32_t *__restrict__ n_tiles) {
   __shared__ int sh_wave[16];
@@ -67,7 +71,10 @@ __global__ __launch_bounds__(1024) void k_mm_tiles(const int32_t *__restrict__ e
   if (e < E) ncol = (expert_off[e + 1] - expert_off[e] + kMmBN - 1) / kMmBN;
   int total;
   const int first = block_excl_scan(ncol, sh_wave, &total);
-  for (int c = 0; c < ncol; ++c) tiles[first + c] = int4{e, first, ncol, 0};
+  // (n / ncol <= kMmBN, a multiple of 32, so the size stays within kMmBN and every tile,
+  // the last included, holds at least one slot)
+  const int sz = ncol > 0 ? (((expert_off[e + 1] - expert_off[e] + ncol - 1) / ncol + 31) & ~31) : 0;
+  for (int c = 0; c < ncol; ++c) tiles[first + c] = int4{e, first, ncol, sz};
   if (threadIdx.x == 0) *n_tiles = total;
 }
 
@@ -130,8 +137,9 @@ void k_grouped_mm(MmArgs a) {
   const int ct = local - rb * ntile;
   const int lo = __builtin_amdgcn_readfirstlane(a.expert_off[e]);
   const int hi = __builtin_amdgcn_readfirstlane(a.expert_off[e + 1]);
-  const int s0 = lo + ct * kMmBN;
-  const int ncols = min(kMmBN, hi - s0);
+  const int tsz = __builtin_amdgcn_readfirstlane(tl.w);  // slots per tile of this expert
+  const int s0 = lo + ct * tsz;
+  const int ncols = min(tsz, hi - s0);
   const int ncb = __builtin_amdgcn_readfirstlane((ncols + 15) >> 4);  // 16-token column blocks
   const uint32_t rowb = (uint32_t)a.K / 2, ng = (uint32_t)a.ng;
   const int nsteps = a.ng >> 2;
