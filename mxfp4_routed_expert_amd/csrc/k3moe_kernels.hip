@@ -326,6 +326,12 @@ __global__ __launch_bounds__(256) void k_dispatch_count(const int32_t *__restric
   for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[(size_t)c * E + e] = __popcll(mask[e]);
 }
 
+// One thread per expert walks the chunks' counts: first their total, then (once the
+// block has scanned the totals into expert offsets) each chunk's exclusive start. Each
+// pass reads kScanBatch chunks' counts at a time, so that many loads are in flight at once
+// instead of one dependent load per chunk.
+constexpr int kScanBatch = 16;
+
 __global__ __launch_bounds__(1024) void k_dispatch_scan(int nch, int E, int T, int K, int32_t *cnt,
                                                         int32_t *expert_off, int32_t *active,
                                                         int32_t *counters) {
@@ -333,10 +339,12 @@ __global__ __launch_bounds__(1024) void k_dispatch_scan(int nch, int E, int T, i
   const int e = threadIdx.x;
   int run = 0;
   if (e < E) {
-    for (int c = 0; c < nch; ++c) {
-      const int v = cnt[(size_t)c * E + e];
-      cnt[(size_t)c * E + e] = run;
-      run += v;
+    for (int c0 = 0; c0 < nch; c0 += kScanBatch) {
+      int v[kScanBatch];
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) v[i] = c0 + i < nch ? cnt[(size_t)(c0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) run += v[i];
     }
   }
   int total, nact;
@@ -345,7 +353,17 @@ __global__ __launch_bounds__(1024) void k_dispatch_scan(int nch, int E, int T, i
   if (e < E) {
     expert_off[e] = o;
     if (run > 0) active[a] = e;
-    for (int c = 0; c < nch; ++c) cnt[(size_t)c * E + e] += o;
+    int start = o;
+    for (int c0 = 0; c0 < nch; c0 += kScanBatch) {
+      int v[kScanBatch];
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) v[i] = c0 + i < nch ? cnt[(size_t)(c0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) {
+        if (c0 + i < nch) cnt[(size_t)(c0 + i) * E + e] = start;
+        start += v[i];
+      }
+    }
   }
   if (e == 0) {
     expert_off[E] = total;
