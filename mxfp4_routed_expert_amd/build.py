@@ -9,7 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libk3moe.so")
-SOURCES = ["k3moe_kernels.hip", "k3moe_mm.hip", "k3moe_dense_mm.hip", "k3moe_gemv1.hip", "k3moe_api.hip"]
+SOURCES = ["k3moe_kernels.hip", "k3moe_mm.hip", "k3moe_gv.hip", "k3moe_dense_mm.hip", "k3moe_gemv1.hip", "k3moe_api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

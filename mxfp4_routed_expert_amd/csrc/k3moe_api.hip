@@ -121,11 +121,16 @@ int64_t max_mm_tiles(const k3moe_dims *d, int32_t T) {
   return (P + kMmBN - 1) / kMmBN + (P < d->n_experts ? P : d->n_experts);
 }
 
+// The GEMV form from five tokens on runs each pass as two launches: the decode kernel
+// (one pass over an expert's weights for up to four of its tokens) for the experts of at
+// most kGvBig pairs, then the rows-split kernel (up to 12 tokens per pass) for the others.
+constexpr int kGvMinT = 5;
+
 // grouped GEMM form for a pass with K columns and activation records of rec_bytes.
-// Measured at the K3 shape (both passes, whole layer): the GEMV form is faster up to
-// about 3 pairs per expert (T = 128: 1.99 against 2.32 ms), the two meet near 3.4
-// (T = 192: 2.65 against 2.59 ms) and the GEMM form wins beyond (T = 256: 2.75 against
-// 3.23 ms).
+// Measured at the K3 shape (both passes, whole layer, the GEMV form with its two kernels
+// against the GEMM form): T = 256: 2.44 against 2.75 ms; T = 320: 2.69 against 2.86;
+// T = 384: 2.91 against 2.95; T = 448: 3.22 against 3.08; T = 512: 3.43 against 3.14.
+// The two meet near 7 pairs per expert.
 bool use_mm(const k3moe_dims *d, int32_t T, int K, int64_t rec_bytes, const k3moe_mxfp4 &m0,
             const k3moe_mxfp4 &m1) {
   if (g_expert_path == 1 || K % 128 != 0 || rec_bytes >= ((int64_t)1 << 31)) return false;
@@ -133,7 +138,7 @@ bool use_mm(const k3moe_dims *d, int32_t T, int K, int64_t rec_bytes, const k3mo
   for (const k3moe_mxfp4 *m : {&m0, &m1})
     if (((uintptr_t)m->scales & 3u) || (m->scales_expert_stride & 3)) return false;
   if (g_expert_path == 2) return true;
-  return (int64_t)T * d->topk >= 3 * (int64_t)d->n_experts;
+  return (int64_t)T * d->topk >= 7 * (int64_t)d->n_experts;
 }
 
 Ws carve(const k3moe_dims *d, int32_t T, void *base) {
@@ -499,6 +504,7 @@ int run_experts(const k3moe_dims *d, int32_t T, const float *z, bool zq_ready, c
   const bool mm_gu = use_mm(d, T, d->latent, (int64_t)T * d->latent * 4, ex->w1, ex->w3);
   const bool mm_dn = use_mm(d, T, d->inter, P * d->inter * 4, ex->w2, ex->w2);
   const int grid_y = (int)(P < d->n_experts ? P : d->n_experts);
+  const int grid_big = (int)std::min<int64_t>(P / (kGvBig + 1), d->n_experts);  // experts of > kGvBig pairs
   // GEMV form: rows per block for about two resident blocks per compute unit; tokens
   // staged per tile (an expert holds at most T tokens), as many as fit in LDS
   const int ncu = num_cus();
@@ -563,7 +569,9 @@ int run_experts(const k3moe_dims *d, int32_t T, const float *z, bool zq_ready, c
     g.b2 = d->b2;
     if (route) g.tk = *route;
     g.q8 = d->idot;
+    g.split = !route && !one_token && T >= kGvMinT && grouped_gv_fits(g, kEpiSitu);
     K3_HIP(launch_grouped(g, kEpiSitu, tt, rb_gu, grid_y, s, route != nullptr));
+    if (g.split) K3_HIP(launch_grouped_gv(g, kEpiSitu, grid_big, s));
   }
   mark(route ? "topk_expert_gateup_situ" : "expert_gateup_situ");
   if (d->idot) {
@@ -603,7 +611,9 @@ int run_experts(const k3moe_dims *d, int32_t T, const float *z, bool zq_ready, c
     h.n_active = counters;
     h.out = edn;
     h.one_token = one_token && T == 1;
+    h.split = !one_token && T >= kGvMinT && grouped_gv_fits(h, kEpiEdn);
     K3_HIP(launch_grouped(h, kEpiEdn, tt, rb_dn, grid_y, s));
+    if (h.split) K3_HIP(launch_grouped_gv(h, kEpiEdn, grid_big, s));
   }
   mark("expert_down");
   return K3MOE_OK;

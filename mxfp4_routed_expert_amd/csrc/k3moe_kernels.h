@@ -167,7 +167,15 @@ struct GroupedArgs {
                           // active[j] (the offsets and the active count are not read);
                           // active[j] = -1: slot j was dropped (top-p), its output row
                           // is written as zeros
+  int split;              // the pass runs as two launches: k_grouped_dec takes the experts
+                          // of at most kGvBig pairs, k_grouped_gv the others (listed first
+                          // in active, their number in n_active[3])
 };
+
+// Experts with more pairs than this are listed first in the active list (dispatch), so
+// that a GEMV-form pass can give them to the kernel that streams their weights once for
+// up to 12 tokens.
+constexpr int kGvBig = 4;
 
 // Grouped GEMM form of the same two passes (many tokens per expert); K % 128 == 0.
 #ifndef K3_MM_BN
@@ -243,6 +251,12 @@ int num_cus();
 // the ids, weights and dispatch of a.tk) and quantizes a.tk.z; grid_y = a.tk.K slots,
 // a.tk.E <= 1024, a.tk.ks <= 2 and a.K <= 4096 (route_in_gateup_ok).
 bool route_in_gateup_ok(const GroupedArgs &a);
+// The GEMV form for the experts of more than kGvBig pairs (k3moe_gv.hip): active[j],
+// j < n_active[3]; each wave owns its own rows over the whole K range and a pass takes up
+// to 12 of an expert's tokens.
+bool grouped_gv_fits(const GroupedArgs &a, int epi);
+hipError_t launch_grouped_gv(const GroupedArgs &a, int epi, int grid_y, hipStream_t s);
+
 hipError_t launch_grouped(const GroupedArgs &a, int epi, int tokens_per_tile, int rb, int grid_y, hipStream_t s,
                           bool route = false);
 // column tiles of kMmBN slots per expert: at most ceil(P / kMmBN) + min(E, P) entries

@@ -276,6 +276,17 @@ __device__ __forceinline__ int pair_rank(const unsigned long long *mask, int e, 
   return __popcll(mask[e] & ((1ull << tl) - 1ull));
 }
 
+// The place of an expert with cnt pairs in the active list (one thread per expert, the
+// whole block): the experts of more than kGvBig pairs first, then the others with any,
+// each group in expert order; *nact experts in all, *nbig in the first group.
+__device__ __forceinline__ int active_slot(int cnt, int *sh_wave, int *nact, int *nbig) {
+  int nsmall;
+  const int ab = block_excl_scan(cnt > kGvBig ? 1 : 0, sh_wave, nbig);
+  const int as = block_excl_scan(cnt > 0 && cnt <= kGvBig ? 1 : 0, sh_wave, &nsmall);
+  *nact = *nbig + nsmall;
+  return cnt > kGvBig ? ab : *nbig + as;
+}
+
 // T <= 64: one block does all of it.
 __global__ __launch_bounds__(1024) void k_dispatch_one(const int32_t *__restrict__ topk_idx, int T,
                                                        int K, int E, int32_t *expert_off,
@@ -287,9 +298,9 @@ __global__ __launch_bounds__(1024) void k_dispatch_one(const int32_t *__restrict
   chunk_masks(topk_idx, T, K, E, 0, mask);
   const int e = threadIdx.x;
   const int cnt = e < E ? __popcll(mask[e]) : 0;
-  int total, nact;
+  int total, nact, nbig;
   const int o = block_excl_scan(cnt, sh_wave, &total);
-  const int a = block_excl_scan(cnt > 0 ? 1 : 0, sh_wave, &nact);
+  const int a = active_slot(cnt, sh_wave, &nact, &nbig);
   if (e < E) {
     off[e] = o;
     expert_off[e] = o;
@@ -299,6 +310,7 @@ __global__ __launch_bounds__(1024) void k_dispatch_one(const int32_t *__restrict
     expert_off[E] = total;
     counters[0] = nact;
     counters[1] = T * K - total;
+    counters[3] = nbig;
   }
   __syncthreads();
   for (int p = threadIdx.x; p < T * K; p += blockDim.x) {
@@ -347,9 +359,9 @@ __global__ __launch_bounds__(1024) void k_dispatch_scan(int nch, int E, int T, i
       for (int i = 0; i < kScanBatch; ++i) run += v[i];
     }
   }
-  int total, nact;
+  int total, nact, nbig;
   const int o = block_excl_scan(run, sh_wave, &total);
-  const int a = block_excl_scan(run > 0 ? 1 : 0, sh_wave, &nact);
+  const int a = active_slot(run, sh_wave, &nact, &nbig);
   if (e < E) {
     expert_off[e] = o;
     if (run > 0) active[a] = e;
@@ -369,6 +381,7 @@ __global__ __launch_bounds__(1024) void k_dispatch_scan(int nch, int E, int T, i
     expert_off[E] = total;
     counters[0] = nact;
     counters[1] = T * K - total;
+    counters[3] = nbig;
   }
 }
 
@@ -410,11 +423,14 @@ __global__ __launch_bounds__(1024) void k_active_from_off(const int32_t *__restr
                                                           int E, int32_t *active, int32_t *counters) {
   __shared__ int sh_wave[16];
   const int e = threadIdx.x;
-  const int has = (e < E) && (expert_off[e + 1] > expert_off[e]);
-  int nact;
-  const int a = block_excl_scan(has, sh_wave, &nact);
-  if (has) active[a] = e;
-  if (e == 0) counters[0] = nact;
+  const int cnt = e < E ? expert_off[e + 1] - expert_off[e] : 0;
+  int nact, nbig;
+  const int a = active_slot(cnt, sh_wave, &nact, &nbig);
+  if (cnt > 0) active[a] = e;
+  if (e == 0) {
+    counters[0] = nact;
+    counters[3] = nbig;
+  }
 }
 
 hipError_t launch_active_from_off(const int32_t *expert_off, int E, int32_t *active,
@@ -657,8 +673,10 @@ __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
     lo = j;
     hi = j + 1;
   } else {
-    if (j >= *a.n_active) return;
-    e = __builtin_amdgcn_readfirstlane(a.active[j]);
+    // split: the experts of more than kGvBig pairs (listed first) are another launch's
+    const int ja = j + (a.split ? a.n_active[3] : 0);
+    if (ja >= *a.n_active) return;
+    e = __builtin_amdgcn_readfirstlane(a.active[ja]);
     lo = __builtin_amdgcn_readfirstlane(a.expert_off[e]);
     hi = __builtin_amdgcn_readfirstlane(a.expert_off[e + 1]);
   }

@@ -218,6 +218,55 @@ def test_tiny_mm_stages_gemm(tiny_mm, expert_path):
     stages(tiny_mm, x)
 
 
+# a shape whose expert passes have several 256-column steps with a partial last one
+# (latent 384: 12 groups; inter 160: 5 groups) and row blocks that end inside M
+RAGGED_STEPS = dataclasses.replace(k3gen.TINY, latent=384, inter=160, n_experts=24)
+
+
+@pytest.fixture(scope="module")
+def ragged_steps():
+    return Host(RAGGED_STEPS, 5)
+
+
+def crafted_pairs(E: int, K: int, counts, seed: int) -> np.ndarray:
+    """Expert ids [T, K] whose per-expert pair counts start with `counts` (experts 0, 1,
+    ...) and are filled up to a multiple of K with one pair each on the later experts, in
+    a seeded random order over the pairs."""
+    ids = [e for e, c in enumerate(counts) for _ in range(c)]
+    e = len(counts)
+    while len(ids) % K:
+        ids.append(e % E)
+        e += 1
+    rng = np.random.default_rng(seed)
+    return rng.permutation(np.asarray(ids, np.int32)).reshape(-1, K)
+
+
+@pytest.mark.parametrize("mode", [k3moe.EXPERT_PATH_GEMV, k3moe.EXPERT_PATH_GEMM])
+@pytest.mark.parametrize("shape", ["tiny_mm", "ragged_steps"])
+def test_expert_pass_counts_around_the_gemv_split(request, expert_path, shape, mode):
+    """The expert stage on a dispatch whose experts hold 0, 1, 4 (the most the decode
+    kernel takes in one pass), 5 (the fewest the rows-split kernel takes), 12 and 13 (one
+    and two of its passes), 24, 25 and 61 pairs: every pair's output row against the
+    oracle's, in the GEMV form and in the GEMM form where the shape allows it (the ragged
+    shape's down pass, K = 160, stays a GEMV)."""
+    h = request.getfixturevalue(shape)
+    d = h.dims
+    expert_path(mode)
+    counts = [0, 1, 4, 5, 12, 13, 24, 25, 61, 0, 3]
+    idx = crafted_pairs(d.n_experts, d.topk, counts, 17)
+    T, K = idx.shape
+    say(f"{shape}: crafted dispatch, T={T}, expert form {mode}")
+    z = k3gen.normal_f32(T * d.latent, 900 + T, k3gen.T_ZPROBE).reshape(T, d.latent)
+    off, sp, _ = oracle.dispatch(idx, d.n_experts)
+    assert list(np.diff(off)[:len(counts)]) == counts
+    ws = device.workspace(d, T)
+    edn = torch.empty((T * K, d.latent), dtype=torch.float32, device="cuda")
+    k3moe.k3moe_expert_glu_mxfp4(d, T, t_(z), h.dev.experts_struct(), t_(off), t_(sp), edn, ws)
+    torch.cuda.synchronize()
+    ref = oracle.expert_pairs(d, sp // K, idx.reshape(-1)[sp], z, h.ex)
+    check_rows(edn.cpu().numpy(), ref, f"{shape} crafted expert edn")
+
+
 # a shape whose up-projection (1024 x 1024) splits its K among blocks from 8 tokens on
 MID_UP = dataclasses.replace(k3gen.TINY, hidden=1024, latent=1024, inter=256, n_experts=64)
 
@@ -316,10 +365,11 @@ def tiny_max():
     return Host(TINY_MAX, 11)
 
 
-@pytest.mark.parametrize("T", [1, 5, 200])
+@pytest.mark.parametrize("T", [1, 5, 200, 240])
 def test_tiny_max_experts_and_topk(tiny_max, T):
     """16 selection slots per lane, 32 chosen per token; at T = 200 the 6400 pairs run the
-    grouped GEMM form."""
+    GEMV form's two kernels over 1024 experts, at T = 240 (7680 pairs) the grouped GEMM
+    form."""
     say(f"1024 experts, top-32, T={T}")
     x, _ = _inputs.gap_fixed_x(TINY_MAX, 30 + T, T, tiny_max.dense["w_router"], tiny_max.dense["bias"])
     compare_layer(tiny_max, x, what=f"max experts T={T}")
@@ -788,6 +838,8 @@ def prefill_case(h: Host, dense: dict, T: int, x_seed: int, nrows: int, what: st
     return off
 
 
+# the oracle's rows take about 10 s per 64 on 16 host threads
+@pytest.mark.timeout(400)
 def test_k3_layer_config3_T4096_sampled(k3):
     off = prefill_case(k3, k3.dense, 4096, 3, 512, "K3 T=4096")
     counts = np.diff(off)
@@ -797,6 +849,8 @@ def test_k3_layer_config3_T4096_sampled(k3):
     assert (counts == 0).any() and counts.max() > 64
 
 
+# the oracle's rows take about 10 s per 64 on 16 host threads
+@pytest.mark.timeout(400)
 def test_k3_layer_config4_T8192_skewed_sampled(k3):
     dense = dict(k3.dense)
     p = _inputs.skew_params()
