@@ -35,7 +35,7 @@ int k3moe_shared_profiled(const k3moe_dims *d, int32_t n_shared, int32_t T, cons
 
 /* TESTS AND MEASUREMENT ONLY. Which kernels run the expert passes, for tests and
  * measurement that compare the two forms on the same inputs: 0 = by batch size (the
- * default: the grouped GEMM form when the batch averages at least seven token-expert pairs
+ * default: the grouped GEMM form when the batch averages at least 7.5 token-expert pairs
  * per expert), 1 = always the grouped GEMV form, 2 = the grouped GEMM form wherever its
  * shape limits allow (the pass's K a multiple of 128 and its activation records under
  * 2 GiB). Both forms give the same result up to fp32 summation order. The mode is per

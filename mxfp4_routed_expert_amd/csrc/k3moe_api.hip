@@ -121,16 +121,21 @@ int64_t max_mm_tiles(const k3moe_dims *d, int32_t T) {
   return (P + kMmBN - 1) / kMmBN + (P < d->n_experts ? P : d->n_experts);
 }
 
-// The GEMV form from five tokens on runs each pass as two launches: the decode kernel
-// (one pass over an expert's weights for up to four of its tokens) for the experts of at
-// most kGvBig pairs, then the rows-split kernel (up to 12 tokens per pass) for the others.
+// The GEMV form from five tokens and one pair per expert on average runs each pass as two
+// launches: the decode kernel (one pass over an expert's weights for up to four of its
+// tokens) for the experts of at most kGvBig pairs, then the rows-split kernel (up to 12
+// tokens per pass) for the others. With fewer pairs the few such experts do not pay for
+// a launch of their own (K3 shape, T = 32: 1.01 ms split against 0.98 ms).
 constexpr int kGvMinT = 5;
+bool gv_split(const k3moe_dims *d, int32_t T) {
+  return T >= kGvMinT && (int64_t)T * d->topk >= d->n_experts;
+}
 
 // grouped GEMM form for a pass with K columns and activation records of rec_bytes.
 // Measured at the K3 shape (both passes, whole layer, the GEMV form with its two kernels
-// against the GEMM form): T = 256: 2.44 against 2.75 ms; T = 320: 2.69 against 2.86;
-// T = 384: 2.91 against 2.95; T = 448: 3.22 against 3.08; T = 512: 3.43 against 3.14.
-// The two meet near 7 pairs per expert.
+// against the GEMM form): T = 320: 2.55 against 2.86 ms; T = 384: 2.79 against 2.95;
+// T = 448: 3.11 against 3.07; T = 512: 3.32 against 3.14. The two meet near 7.5 pairs
+// per expert.
 bool use_mm(const k3moe_dims *d, int32_t T, int K, int64_t rec_bytes, const k3moe_mxfp4 &m0,
             const k3moe_mxfp4 &m1) {
   if (g_expert_path == 1 || K % 128 != 0 || rec_bytes >= ((int64_t)1 << 31)) return false;
@@ -138,7 +143,7 @@ bool use_mm(const k3moe_dims *d, int32_t T, int K, int64_t rec_bytes, const k3mo
   for (const k3moe_mxfp4 *m : {&m0, &m1})
     if (((uintptr_t)m->scales & 3u) || (m->scales_expert_stride & 3)) return false;
   if (g_expert_path == 2) return true;
-  return (int64_t)T * d->topk >= 7 * (int64_t)d->n_experts;
+  return 2 * (int64_t)T * d->topk >= 15 * (int64_t)d->n_experts;
 }
 
 Ws carve(const k3moe_dims *d, int32_t T, void *base) {
@@ -569,7 +574,7 @@ int run_experts(const k3moe_dims *d, int32_t T, const float *z, bool zq_ready, c
     g.b2 = d->b2;
     if (route) g.tk = *route;
     g.q8 = d->idot;
-    g.split = !route && !one_token && T >= kGvMinT && grouped_gv_fits(g, kEpiSitu);
+    g.split = !route && !one_token && gv_split(d, T) && grouped_gv_fits(g, kEpiSitu);
     K3_HIP(launch_grouped(g, kEpiSitu, tt, rb_gu, grid_y, s, route != nullptr));
     if (g.split) K3_HIP(launch_grouped_gv(g, kEpiSitu, grid_big, s));
   }
@@ -611,7 +616,7 @@ int run_experts(const k3moe_dims *d, int32_t T, const float *z, bool zq_ready, c
     h.n_active = counters;
     h.out = edn;
     h.one_token = one_token && T == 1;
-    h.split = !one_token && T >= kGvMinT && grouped_gv_fits(h, kEpiEdn);
+    h.split = !one_token && gv_split(d, T) && grouped_gv_fits(h, kEpiEdn);
     K3_HIP(launch_grouped(h, kEpiEdn, tt, rb_dn, grid_y, s));
     if (h.split) K3_HIP(launch_grouped_gv(h, kEpiEdn, grid_big, s));
   }

@@ -100,20 +100,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   uint8_t *ring = smem + gv_scale_bytes<NA, RBW>(a.ng);
   uint8_t *tile = ring + NST * STAGE + wave * kGvTile;
 
-  // ---- the block's scale rows, once (rows past M read as zeros)
-#pragma unroll
-  for (int m = 0; m < NA; ++m) {
-    const uint8_t *src = a.A[m].scales + (size_t)e * a.A[m].sstride + (size_t)row0 * ng;
-    uint8_t *dst = sS + (size_t)m * ROWS * ng;
-    const int nb = nbr * (int)ng;
-    if ((((uintptr_t)src) & 3) == 0) {
-      for (int i = threadIdx.x; i < ROWS * (int)ng / 4; i += blockDim.x)
-        ((uint32_t *)dst)[i] = 4 * i < nb ? ((const uint32_t *)src)[i] : 0u;
-    } else {
-      for (int i = threadIdx.x; i < ROWS * (int)ng; i += blockDim.x) dst[i] = i < nb ? src[i] : (uint8_t)0;
-    }
-  }
-
   // ---- weight stream of this wave: NA matrices x RBW row blocks x 2 loads per step
   rsrc_t rA[NA];
 #pragma unroll
@@ -162,17 +148,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   };
 
-  const uint8_t *sSw = sS + (size_t)(wave * WR + rl) * ng;  // this lane's row (matrix 0)
-  __syncthreads();  // the scale rows are in LDS
-
-  for (int n0 = lo; n0 < hi; n0 += TT) {
-    const int ntok = min(TT, hi - n0);
+  auto start_pass = [&](int n0) {
     set_tokens(n0);
     copy_step(0);
 #pragma unroll
     for (int m = 0; m < NA; ++m)
 #pragma unroll
       for (int r = 0; r < RBW; ++r) load_rb(0, m, r);
+  };
+  // the first pass's first step is requested before the scale rows
+  start_pass(lo);
+
+  // ---- the block's scale rows, once: copied straight into LDS when they are whole
+  // kilobytes (the first step's wait covers them; rows past M keep stale bytes, against
+  // weights that read as zero), else through registers with rows past M as zeros
+#pragma unroll
+  for (int m = 0; m < NA; ++m) {
+    const uint8_t *src = a.A[m].scales + (size_t)e * a.A[m].sstride + (size_t)row0 * ng;
+    uint8_t *dst = sS + (size_t)m * ROWS * ng;
+    const int nb = nbr * (int)ng;
+    if ((((uintptr_t)src) & 15) == 0 && nb % 1024 == 0) {
+      const rsrc_t rS = make_rsrc(src, (uint32_t)nb);
+      for (int c = wave; c < nb / 1024; c += 4) dma16(rS, dst + c * 1024, (uint32_t)c * 1024u + (uint32_t)lane * 16u);
+    } else if ((((uintptr_t)src) & 3) == 0) {
+      for (int i = threadIdx.x; i < ROWS * (int)ng / 4; i += blockDim.x)
+        ((uint32_t *)dst)[i] = 4 * i < nb ? ((const uint32_t *)src)[i] : 0u;
+    } else {
+      for (int i = threadIdx.x; i < ROWS * (int)ng; i += blockDim.x) dst[i] = i < nb ? src[i] : (uint8_t)0;
+    }
+  }
+  const uint8_t *sSw = sS + (size_t)(wave * WR + rl) * ng;  // this lane's row (matrix 0)
+  __syncthreads();  // the scale rows written through registers are in LDS
+
+  for (int n0 = lo; n0 < hi; n0 += TT) {
+    const int ntok = min(TT, hi - n0);
+    if (n0 != lo) start_pass(n0);
 
     f32x4 acc[NA][RBW][NCT];
 #pragma unroll
