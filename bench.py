@@ -280,8 +280,11 @@ def routing_stats(dims, idx: np.ndarray, hot=None):
                     "hot_tokens_mean": round(float(counts[hot].mean()), 1),
                     "cold_with_1_to_5_tokens": round(float(np.mean((cold >= 1) & (cold <= 5))), 4),
                     "cold_with_0_tokens": round(float(np.mean(cold == 0)), 4)})
-    tile, rows_gu, rows_dn = k3moe.gemm_tiling()
-    ncol = (counts + tile - 1) // tile
+    tile, rows_gu, rows_dn, small = k3moe.gemm_tiling()
+    # the experts of at most `small` pairs take the decode kernel, the others column tiles
+    out["experts_to_decode_kernel"] = int(np.count_nonzero((counts > 0) & (counts <= small)))
+    out["pairs_to_decode_kernel"] = int(counts[(counts > 0) & (counts <= small)].sum())
+    ncol = np.where(counts > small, (counts + tile - 1) // tile, 0)
     # the GEMM form walks (column tile, row block) entries; entry q runs on XCD q // ceil(n / 8)
     # an expert's tokens split evenly over its tiles, each size rounded up to 32 (the last takes the rest)
     size = [-(-c // n) + 31 & ~31 if n else 0 for c, n in zip(counts, ncol)]

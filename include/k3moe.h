@@ -78,7 +78,7 @@
  *    over). Results match an fp64 evaluation of the same steps to about 1e-6
  *    relative per token row.
  *  - Two kernel forms: small batches run the products as grouped / dense GEMVs, large
- *    ones as GEMMs (the expert passes from 7.5 token-expert pairs per expert on
+ *    ones as GEMMs (the expert passes from 6.25 token-expert pairs per expert on
  *    average; the up-projection from 8 tokens, the router and latent projection from
  *    40). A GEMM with few tiles splits its K range among blocks and sums the parts in a
  *    fixed order. Every form gives the same result up to fp32 summation order.

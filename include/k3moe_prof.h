@@ -35,7 +35,7 @@ int k3moe_shared_profiled(const k3moe_dims *d, int32_t n_shared, int32_t T, cons
 
 /* TESTS AND MEASUREMENT ONLY. Which kernels run the expert passes, for tests and
  * measurement that compare the two forms on the same inputs: 0 = by batch size (the
- * default: the grouped GEMM form when the batch averages at least 7.5 token-expert pairs
+ * default: the grouped GEMM form when the batch averages at least 6.25 token-expert pairs
  * per expert), 1 = always the grouped GEMV form, 2 = the grouped GEMM form wherever its
  * shape limits allow (the pass's K a multiple of 128 and its activation records under
  * 2 GiB). Both forms give the same result up to fp32 summation order. The mode is per
@@ -48,8 +48,10 @@ int k3moe_set_expert_path(int mode);
  * of the down pass. An expert's n tokens take ceil(n / tile_tokens) column tiles of
  * ceil(n / tiles) tokens rounded up to a multiple of 32 (the last tile takes the rest).
  * Entry q of the (column tile, row block) list, tiles in expert order, runs on XCD
- * q / ceil(entries / 8). */
-int k3moe_prof_gemm_tiling(int *tile_tokens, int *rows_gateup, int *rows_down);
+ * q / ceil(entries / 8). In the GEMM form chosen by batch size (not a forced one), the
+ * experts of at most *small_pairs pairs take no tiles: the grouped GEMV's decode kernel
+ * runs them. */
+int k3moe_prof_gemm_tiling(int *tile_tokens, int *rows_gateup, int *rows_down, int *small_pairs);
 
 #ifdef __cplusplus
 }

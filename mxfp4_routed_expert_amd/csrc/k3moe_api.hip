@@ -133,9 +133,9 @@ bool gv_split(const k3moe_dims *d, int32_t T) {
 
 // grouped GEMM form for a pass with K columns and activation records of rec_bytes.
 // Measured at the K3 shape (both passes, whole layer, the GEMV form with its two kernels
-// against the GEMM form): T = 320: 2.55 against 2.86 ms; T = 384: 2.79 against 2.95;
-// T = 448: 3.11 against 3.07; T = 512: 3.32 against 3.14. The two meet near 7.5 pairs
-// per expert.
+// against the GEMM form with the small experts on the decode kernel): T = 256: 2.28
+// against 2.45 ms; T = 320: 2.53 against 2.62; T = 384: 2.76 against 2.70. The two meet
+// near 6.25 pairs per expert.
 bool use_mm(const k3moe_dims *d, int32_t T, int K, int64_t rec_bytes, const k3moe_mxfp4 &m0,
             const k3moe_mxfp4 &m1) {
   if (g_expert_path == 1 || K % 128 != 0 || rec_bytes >= ((int64_t)1 << 31)) return false;
@@ -143,7 +143,7 @@ bool use_mm(const k3moe_dims *d, int32_t T, int K, int64_t rec_bytes, const k3mo
   for (const k3moe_mxfp4 *m : {&m0, &m1})
     if (((uintptr_t)m->scales & 3u) || (m->scales_expert_stride & 3)) return false;
   if (g_expert_path == 2) return true;
-  return 2 * (int64_t)T * d->topk >= 15 * (int64_t)d->n_experts;
+  return 4 * (int64_t)T * d->topk >= 25 * (int64_t)d->n_experts;
 }
 
 Ws carve(const k3moe_dims *d, int32_t T, void *base) {
@@ -521,8 +521,14 @@ int run_experts(const k3moe_dims *d, int32_t T, const float *z, bool zq_ready, c
     tt >>= 1;
   while (rb_gu > 4 && grouped_dec_lds(d->latent, tt, rb_gu) > kMaxBlockLds) rb_gu -= 2;
   while (rb_dn > 4 && grouped_dec_lds(d->inter, tt, rb_dn) > kMaxBlockLds) rb_dn -= 1;
+  // In the GEMM form chosen by batch size, the experts of at most kGvBig pairs (listed
+  // last in the active list) get no column tiles: the decode kernel streams their weights
+  // once for their few tokens, where a tile each would cost the GEMM about as much as a
+  // full one (K3 shape: T = 4096 gate/up + down 6.78 -> 6.33 ms of GEMM without them,
+  // skewed T = 8192 12.14 -> 10.47 ms). The forms forced for tests stay whole.
+  const bool mm_small = (mm_gu || mm_dn) && g_expert_path == 0;
   if (mm_gu || mm_dn) {
-    K3_HIP(launch_mm_tiles(expert_off, d->n_experts, w.tiles, w.counters + 2, s));
+    K3_HIP(launch_mm_tiles(expert_off, d->n_experts, mm_small ? kGvBig : 0, w.tiles, w.counters + 2, s));
     mark("expert_tile_table");
   }
   const int max_tiles = (int)max_mm_tiles(d, T);
@@ -536,7 +542,29 @@ int run_experts(const k3moe_dims *d, int32_t T, const float *z, bool zq_ready, c
     K3_HIP(launch_quant_rows(z, (size_t)T * d->latent, w.zq, d->idot != 0, s));
     mark("latent_quant");
   }
+  GroupedArgs g = {};
+  g.A[0] = w1;
+  g.A[1] = w3;
+  g.M = d->inter;
+  g.K = d->latent;
+  g.ng = d->latent / 32;
+  g.Bq = zq;
+  g.gather = 1;
+  g.topk = d->topk;
+  g.expert_off = expert_off;
+  g.sorted_pair = sorted_pair;
+  g.active = active;
+  g.n_active = counters;
+  g.outq = w.actq;
+  g.b1 = d->b1;
+  g.b2 = d->b2;
+  if (route) g.tk = *route;
+  g.q8 = d->idot;
   if (mm_gu) {
+    if (mm_small) {
+      g.split = 1;  // the decode kernel takes the experts past the first n_active[3]
+      K3_HIP(launch_grouped(g, kEpiSitu, tt, rb_gu, grid_y, s));
+    }
     MmArgs m = {};
     m.A[0] = w1;
     m.A[1] = w3;
@@ -556,24 +584,6 @@ int run_experts(const k3moe_dims *d, int32_t T, const float *z, bool zq_ready, c
     m.b2 = d->b2;
     K3_HIP(launch_grouped_mm(m, kEpiSitu, max_tiles, s));
   } else {
-    GroupedArgs g = {};
-    g.A[0] = w1;
-    g.A[1] = w3;
-    g.M = d->inter;
-    g.K = d->latent;
-    g.ng = d->latent / 32;
-    g.Bq = zq;
-    g.gather = 1;
-    g.topk = d->topk;
-    g.expert_off = expert_off;
-    g.sorted_pair = sorted_pair;
-    g.active = active;
-    g.n_active = counters;
-    g.outq = w.actq;
-    g.b1 = d->b1;
-    g.b2 = d->b2;
-    if (route) g.tk = *route;
-    g.q8 = d->idot;
     g.split = !route && !one_token && gv_split(d, T) && grouped_gv_fits(g, kEpiSitu);
     K3_HIP(launch_grouped(g, kEpiSitu, tt, rb_gu, grid_y, s, route != nullptr));
     if (g.split) K3_HIP(launch_grouped_gv(g, kEpiSitu, grid_big, s));
@@ -585,7 +595,25 @@ int run_experts(const k3moe_dims *d, int32_t T, const float *z, bool zq_ready, c
     mark("act_int8_round");
   }
 
+  GroupedArgs h = {};
+  h.A[0] = h.A[1] = w2;
+  h.M = d->latent;
+  h.K = d->inter;
+  h.ng = d->inter / 32;
+  h.Bq = w.actq;
+  h.gather = 0;
+  h.topk = d->topk;
+  h.expert_off = expert_off;
+  h.sorted_pair = sorted_pair;
+  h.active = active;
+  h.n_active = counters;
+  h.out = edn;
+  h.one_token = one_token && T == 1;
   if (mm_dn) {
+    if (mm_small) {
+      h.split = 1;
+      K3_HIP(launch_grouped(h, kEpiEdn, tt, rb_dn, grid_y, s));
+    }
     MmArgs m = {};
     m.A[0] = m.A[1] = w2;
     m.M = d->latent;
@@ -602,20 +630,6 @@ int run_experts(const k3moe_dims *d, int32_t T, const float *z, bool zq_ready, c
     m.out = edn;
     K3_HIP(launch_grouped_mm(m, kEpiEdn, max_tiles, s));
   } else {
-    GroupedArgs h = {};
-    h.A[0] = h.A[1] = w2;
-    h.M = d->latent;
-    h.K = d->inter;
-    h.ng = d->inter / 32;
-    h.Bq = w.actq;
-    h.gather = 0;
-    h.topk = d->topk;
-    h.expert_off = expert_off;
-    h.sorted_pair = sorted_pair;
-    h.active = active;
-    h.n_active = counters;
-    h.out = edn;
-    h.one_token = one_token && T == 1;
     h.split = !one_token && gv_split(d, T) && grouped_gv_fits(h, kEpiEdn);
     K3_HIP(launch_grouped(h, kEpiEdn, tt, rb_dn, grid_y, s));
     if (h.split) K3_HIP(launch_grouped_gv(h, kEpiEdn, grid_big, s));
@@ -1024,9 +1038,10 @@ int k3moe_set_expert_path(int mode) {
   return prev;
 }
 
-int k3moe_prof_gemm_tiling(int *tile_tokens, int *rows_gateup, int *rows_down) {
-  if (!tile_tokens || !rows_gateup || !rows_down) return K3MOE_EINVAL;
+int k3moe_prof_gemm_tiling(int *tile_tokens, int *rows_gateup, int *rows_down, int *small_pairs) {
+  if (!tile_tokens || !rows_gateup || !rows_down || !small_pairs) return K3MOE_EINVAL;
   grouped_mm_tiling(tile_tokens, rows_gateup, rows_down);
+  *small_pairs = kGvBig;
   return K3MOE_OK;
 }
 

@@ -168,13 +168,13 @@ struct GroupedArgs {
                           // active[j] = -1: slot j was dropped (top-p), its output row
                           // is written as zeros
   int split;              // the pass runs as two launches: k_grouped_dec takes the experts
-                          // of at most kGvBig pairs, k_grouped_gv the others (listed first
-                          // in active, their number in n_active[3])
+                          // of at most kGvBig pairs, k_grouped_gv or the grouped GEMM the
+                          // others (listed first in active, their number in n_active[3])
 };
 
-// Experts with more pairs than this are listed first in the active list (dispatch), so
-// that a GEMV-form pass can give them to the kernel that streams their weights once for
-// up to 12 tokens.
+// Experts with more pairs than this are listed first in the active list (dispatch): a
+// GEMV-form pass gives them to the kernel that streams their weights once for up to 12
+// tokens, a GEMM-form pass to its column tiles, and the others to the decode kernel.
 constexpr int kGvBig = 4;
 
 // Grouped GEMM form of the same two passes (many tokens per expert); K % 128 == 0.
@@ -259,8 +259,10 @@ hipError_t launch_grouped_gv(const GroupedArgs &a, int epi, int grid_y, hipStrea
 
 hipError_t launch_grouped(const GroupedArgs &a, int epi, int tokens_per_tile, int rb, int grid_y, hipStream_t s,
                           bool route = false);
-// column tiles of kMmBN slots per expert: at most ceil(P / kMmBN) + min(E, P) entries
-hipError_t launch_mm_tiles(const int32_t *expert_off, int E, int4 *tiles, int32_t *n_tiles, hipStream_t s);
+// column tiles of kMmBN slots per expert of more than min_pairs pairs: at most
+// ceil(P / kMmBN) + min(E, P) entries
+hipError_t launch_mm_tiles(const int32_t *expert_off, int E, int min_pairs, int4 *tiles, int32_t *n_tiles,
+                           hipStream_t s);
 size_t grouped_mm_lds();
 // tokens per column tile, rows per block of the gate/up pass (each matrix) and of the down pass
 void grouped_mm_tiling(int *tile_tokens, int *rows_gateup, int *rows_down);

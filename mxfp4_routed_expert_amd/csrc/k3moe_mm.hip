@@ -58,22 +58,22 @@ typedef unsigned u32x3 __attribute__((ext_vector_type(3)));
 }  // namespace
 
 // One block: entry e's column tiles are numbered first .. first+n-1. An expert with n
-// sorted slots takes ceil(n / kMmBN) tiles of equal size rounded up to 32 slots (the last
-// takes the rest): its tiles' blocks run side by side on one XCD and stream the same
+// sorted slots, n > min_pairs, takes ceil(n / kMmBN) tiles of equal size rounded up to 32
+// slots (the last takes the rest; the experts of at most min_pairs pairs get none): its tiles' blocks run side by side on one XCD and stream the same
 // weight lines, and tiles of equal width keep pace, so the lines are fetched from HBM
 // once more often (measured 1.7% faster than tiles of kMmBN and a remainder at 4096
 // tokens). tiles[j] = {expert, first tile of that expert, its tile count, slots per tile}.
-__global__ __launch_bounds__(1024) void k_mm_tiles(const int32_t *__restrict__ expert_off, int E,
+__global__ __launch_bounds__(1024) void k_mm_tiles(const int32_t *__restrict__ expert_off, int E, int min_pairs,
                                                    int4 *__restrict__ tiles, int32_t *__restrict__ n_tiles) {
   __shared__ int sh_wave[16];
   const int e = threadIdx.x;
-  int ncol = 0;
-  if (e < E) ncol = (expert_off[e + 1] - expert_off[e] + kMmBN - 1) / kMmBN;
+  const int n = e < E ? expert_off[e + 1] - expert_off[e] : 0;
+  const int ncol = n > min_pairs ? (n + kMmBN - 1) / kMmBN : 0;
   int total;
   const int first = block_excl_scan(ncol, sh_wave, &total);
   // (n / ncol <= kMmBN, a multiple of 32, so the size stays within kMmBN and every tile,
   // the last included, holds at least one slot)
-  const int sz = ncol > 0 ? (((expert_off[e + 1] - expert_off[e] + ncol - 1) / ncol + 31) & ~31) : 0;
+  const int sz = ncol > 0 ? (((n + ncol - 1) / ncol + 31) & ~31) : 0;
   for (int c = 0; c < ncol; ++c) tiles[first + c] = int4{e, first, ncol, sz};
   if (threadIdx.x == 0) *n_tiles = total;
 }
@@ -480,9 +480,10 @@ void grouped_mm_tiling(int *tile_tokens, int *rows_gateup, int *rows_down) {
   *rows_down = 512;
 }
 
-hipError_t launch_mm_tiles(const int32_t *expert_off, int E, int4 *tiles, int32_t *n_tiles, hipStream_t s) {
+hipError_t launch_mm_tiles(const int32_t *expert_off, int E, int min_pairs, int4 *tiles, int32_t *n_tiles,
+                           hipStream_t s) {
   if (E > 1024) return hipErrorInvalidValue;
-  launch_kernel(k_mm_tiles, 1, 1024, 0, s, expert_off, E, tiles, n_tiles);
+  launch_kernel(k_mm_tiles, 1, 1024, 0, s, expert_off, E, min_pairs, tiles, n_tiles);
   return hipGetLastError();
 }
 

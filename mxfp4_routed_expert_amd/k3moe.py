@@ -95,7 +95,7 @@ def load(path: str | None = None):
     L.k3moe_prof_name.argtypes = [ctypes.c_int]
     L.k3moe_prof_name.restype = ctypes.c_char_p
     ip = ctypes.POINTER(ctypes.c_int)
-    L.k3moe_prof_gemm_tiling.argtypes = [ip, ip, ip]
+    L.k3moe_prof_gemm_tiling.argtypes = [ip, ip, ip, ip]
     L.k3moe_prof_gemm_tiling.restype = ctypes.c_int
     L.k3moe_set_expert_path.argtypes = [ctypes.c_int]
     L.k3moe_set_expert_path.restype = ctypes.c_int
@@ -286,8 +286,10 @@ def k3moe_set_expert_path(mode: int) -> int:
 
 
 def gemm_tiling():
-    """(tokens per column tile, gate/up rows per block, down rows per block) of the grouped
+    """(tokens per column tile, gate/up rows per block, down rows per block, the most pairs
+    of an expert that the batch-size GEMM form leaves to the decode kernel) of the grouped
     GEMM form (k3moe_prof_gemm_tiling)."""
-    a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
-    _check(load().k3moe_prof_gemm_tiling(ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)), "k3moe_prof_gemm_tiling")
-    return a.value, b.value, c.value
+    a, b, c, n = ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(load().k3moe_prof_gemm_tiling(ctypes.byref(a), ctypes.byref(b), ctypes.byref(c), ctypes.byref(n)),
+           "k3moe_prof_gemm_tiling")
+    return a.value, b.value, c.value, n.value
