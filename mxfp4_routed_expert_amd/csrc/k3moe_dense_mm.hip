@@ -11,11 +11,18 @@
 // row), whose three partial results the top-k adds; every product of bf16 values is
 // exact in the matrix core, so only the fp32 accumulation rounds.
 //
-// Block: 4 waves x 64 weight rows (four 16-row fragments each) by BN tokens. Weight
-// fragments load per lane straight into registers (each wave's rows are its own); the
-// token tile of every step is copied by buffer loads with an LDS destination into a
-// ring of kDmStages stages, lane l's 16 bytes landing at 16*l, which is the register
-// image of a 16x16x32 bf16 MFMA operand (token l % 16, columns 8*(l/16) .. +8).
+// Block: 4 waves x 64 weight rows (four 16-row fragments each) by BN tokens; each wave's
+// rows are its own. The token tile of every step is copied by buffer loads with an LDS
+// destination into a ring, lane l's 16 bytes landing at 16*l, which is the register image
+// of a 16x16x32 bf16 MFMA operand (token l % 16, columns 8*(l/16) .. +8). The weights:
+//  - one token plane (the router and latent projections, the shared gate/up): 64 columns
+//    a step, read in whole 128-byte lines (8 rows x 128 B per load, one step ahead in
+//    registers), each 16-row block turned into fragments through a swizzled LDS tile (as
+//    in the grouped GEMV); a ring of 2 token stages. A load that touches 16 rows x 64 B
+//    keeps the texture-address units busy for longer than one of 8 rows x 128 B;
+//  - two or three planes (more matrix work per weight byte): 32 columns a step, the
+//    fragments loaded straight into registers (16 rows x 64 B per load) kDmStages-1
+//    steps ahead, a ring of kDmStages token stages (whole lines measured slower here).
 // Tiles are numbered so that each XCD works through a contiguous run in which 8 row
 // blocks share each token block, keeping both operands' current K slices in its L2.
 #include "k3moe_common.h"
@@ -29,6 +36,7 @@ namespace {
 #define K3_DM_STAGES 3
 #endif
 constexpr int kDmStages = K3_DM_STAGES;
+constexpr int kDmTile = 2048 + 128;  // a wave's weight tile: two 8-row chunks, the second shifted by 128 B
 
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
@@ -44,14 +52,17 @@ __device__ __forceinline__ void wait_ring_barrier() {
 
 }  // namespace
 
+// LDS of a block: the token ring (and with one plane the waves' weight tiles), then the
+// RMSNorm factors of its tokens
+template <int PB, int NJ>
+__host__ __device__ constexpr size_t dense_mm_inv_off() {
+  return PB == 1 ? (size_t)2 * 2 * NJ * 1024 + 4 * kDmTile : (size_t)kDmStages * PB * NJ * 1024;
+}
+
 template <int PB, int NJ, int EPI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_dense_mm(DenseMmArgs a) {
   constexpr int BN = 16 * NJ;
-  constexpr int NS = kDmStages;
-  constexpr int DMA_PER_WAVE = PB * NJ / 4;
-  static_assert((PB * NJ) % 4 == 0, "the token tile's fragments split evenly over 4 waves");
-  constexpr int VM_PER_STEP = 4 + DMA_PER_WAVE;
-  constexpr int STAGE = PB * NJ * 1024;
+  constexpr bool WL = PB == 1;  // whole-line weight loads
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -90,65 +101,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const uint32_t rowb = (uint32_t)a.K * 2u;
   const rsrc_t rA = make_rsrc(seg.A + (size_t)lr0 * a.K, (uint32_t)max(nrows, 0) * rowb);
   const rsrc_t rB = make_rsrc(a.B, (uint32_t)(PB * a.plane_elems * 2));
-  // this K part's steps s_lo .. s_lo + nsteps - 1
-  const int spp = (a.K / 32 + ks - 1) / ks;
-  const int s_lo = kp * spp;
-  const int nsteps = max(0, min(a.K / 32 - s_lo, spp));
-
-  uint32_t aoff[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) aoff[i] = (uint32_t)(16 * i + rl) * rowb + (uint32_t)kq * 16u;
-  // token tile DMA: wave w copies fragments w, w+4, ... of the PB x NJ (plane, token
-  // block) fragments; lane l: token 16j + l % 16, columns 8 * (l / 16) .. +8
-  uint32_t boff[DMA_PER_WAVE];
-#pragma unroll
-  for (int u = 0; u < DMA_PER_WAVE; ++u) {
-    const int f = wave + 4 * u, p = f / NJ, j = f % NJ;
-    const int n = n0 + 16 * j + rl;
-    boff[u] = (uint32_t)p * (uint32_t)a.plane_elems * 2u + (uint32_t)n * rowb + (uint32_t)kq * 16u;
-  }
-
-  struct AStep {
-    u32x4 v[4];
-  };
-  // (rows past the segment and steps past the part read zeros: their offsets lie past
-  // the descriptors' sizes)
-  auto aload = [&](int S, AStep &s) {
-    const bool ok = S < nsteps;
-    const uint32_t so = (uint32_t)(s_lo + S) * 64u;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s.v[i] = bload16(rA, ok ? aoff[i] + so : kOOB);
-  };
-  auto issue = [&](int S, int st) {
-    uint8_t *base = smem + st * STAGE;
-    const bool ok = S < nsteps;
-    const uint32_t so = (uint32_t)(s_lo + S) * 64u;
-#pragma unroll
-    for (int u = 0; u < DMA_PER_WAVE; ++u) dma16(rB, base + (wave + 4 * u) * 1024, ok ? boff[u] + so : kOOB);
-  };
-
   f32x4 acc[4][NJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int st, const AStep &as) {
-    const uint8_t *base = smem + st * STAGE;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-#pragma unroll
-      for (int p = 0; p < PB; ++p) {
-        const u32x4 b = *(const u32x4 *)(base + (p * NJ + j) * 1024 + lane * 16);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i][j] = mfma16(as.v[i], b, acc[i][j]);
-      }
-    }
-  };
-
-  // RMSNorm factor of each of the tile's tokens (kEpiStoreScaled), computed while the
-  // first stages load: y = W (gamma * acc) / sqrt(mean(acc^2) + eps)
-  float *sInv = (float *)(smem + NS * STAGE);
+  // RMSNorm factor of each of the tile's tokens (kEpiStoreScaled), computed before the K
+  // loop and read in the epilogue: y = W (gamma * acc) / sqrt(mean(acc^2) + eps)
+  float *sInv = (float *)(smem + dense_mm_inv_off<PB, NJ>());
   if constexpr (EPI == kEpiStoreScaled) {
     if (threadIdx.x < BN) {
       const int n = min(n0 + (int)threadIdx.x, a.N - 1);
@@ -162,27 +123,186 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   }
 
-  // ---- K loop: A registers and token stages run NS-1 steps ahead; every step issues
-  // the same loads (zeros past the end), so the wait count is exact.
-  AStep as[NS];
+  if constexpr (WL) {
+    constexpr int NS = 2;            // token stages of 64 columns
+    constexpr int NF = 2 * PB * NJ;  // token fragments of a step (two 32-column chunks)
+    constexpr int DMA_PER_WAVE = NF / 4;
+    static_assert(NF % 4 == 0, "the token tile's fragments split evenly over 4 waves");
+    constexpr int STAGE = NF * 1024;
+    // this K part's 32-column chunks s_lo .. s_lo + n32 - 1, s_lo even, taken 64 columns
+    // (128 bytes of a row) per step
+    const int tot32 = a.K / 32;
+    const int spp = ((tot32 + ks - 1) / ks + 1) & ~1;
+    const int s_lo = kp * spp;
+    const int n32 = max(0, min(tot32 - s_lo, spp));
+    const int nsteps = (n32 + 1) >> 1;
+
+    // weights in whole 128-byte lines: load h reads rows 8h .. 8h+7 of the wave's 64 (lane
+    // l: row 8h + l / 8, 16-byte unit l % 8); units 4-7 are the step's second chunk, read
+    // as zeros past the part
+    uint32_t aoff[8];
 #pragma unroll
-  for (int d = 0; d + 1 < NS; ++d) {
-    aload(d, as[d]);
-    issue(d, d);
-  }
-  for (int S0 = 0; S0 < nsteps; S0 += NS) {
+    for (int h = 0; h < 8; ++h) aoff[h] = (uint32_t)(8 * h + (lane >> 3)) * rowb + (uint32_t)(lane & 7) * 16u;
+    const bool hi_unit = (lane & 7) >= 4;
+    // token tile DMA: wave w copies fragments w, w+4, ... of the 2 x PB x NJ (chunk, plane,
+    // token block) fragments; lane l: token 16j + l % 16, columns 8 * (l / 16) .. +8 of the
+    // chunk
+    uint32_t boff[DMA_PER_WAVE];
+    int bchunk[DMA_PER_WAVE];
 #pragma unroll
-    for (int d = 0; d < NS; ++d) {
-      const int S = S0 + d;
-      wait_ring_barrier<(NS - 2) * VM_PER_STEP>();
-      aload(S + NS - 1, as[(d + NS - 1) % NS]);
-      issue(S + NS - 1, (d + NS - 1) % NS);
-      if (wave_on && S < nsteps) compute(d, as[d]);
+    for (int u = 0; u < DMA_PER_WAVE; ++u) {
+      const int f = wave + 4 * u, c = f / (PB * NJ), p = (f % (PB * NJ)) / NJ, j = f % NJ;
+      const int n = n0 + 16 * j + rl;
+      bchunk[u] = c;
+      boff[u] = (uint32_t)p * (uint32_t)a.plane_elems * 2u + (uint32_t)n * rowb + (uint32_t)kq * 16u + (uint32_t)c * 64u;
+    }
+
+    struct AStep {
+      u32x4 v[8];
+    };
+    // (rows past the segment and steps past the part read zeros: their offsets lie past
+    // the descriptors' sizes)
+    auto aload2 = [&](int S, AStep &s, int i) {  // the two loads of 16-row block i
+      const bool ok = S < nsteps && !(hi_unit && 2 * S + 1 >= n32);
+      const uint32_t so = (uint32_t)(s_lo + 2 * S) * 64u;
+#pragma unroll
+      for (int h = 2 * i; h < 2 * i + 2; ++h) s.v[h] = bload16(rA, ok ? aoff[h] + so : kOOB);
+    };
+    auto issue = [&](int S, int st) {
+      uint8_t *base = smem + st * STAGE;
+      const uint32_t so = (uint32_t)(s_lo + 2 * S) * 64u;
+#pragma unroll
+      for (int u = 0; u < DMA_PER_WAVE; ++u) {
+        const bool ok = S < nsteps && 2 * S + bchunk[u] < n32;
+        dma16(rB, base + (wave + 4 * u) * 1024, ok ? boff[u] + so : kOOB);
+      }
+    };
+    // this wave's LDS tile: 16 rows x 128 bytes, unit u of row r at unit u ^ (r % 8), rows
+    // 8-15 shifted by 128 bytes (conflict-free writes and fragment reads)
+    uint8_t *tile = smem + NS * STAGE + wave * kDmTile;
+    const uint32_t wslot = (uint32_t)((lane >> 3) * 128 + (((lane & 7) ^ (lane >> 3)) * 16));
+    const uint32_t rslot0 = (uint32_t)((rl >> 3) * (1024 + 128) + (rl & 7) * 128);
+
+    // step S: each 16-row block into the tile, its registers reloaded with step S+1, its two
+    // chunks' fragments back (this wave's LDS operations run in order), then the products
+    auto compute = [&](int S, AStep &as, bool on) {
+      const uint8_t *base = smem + (S & 1) * STAGE;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        *(u32x4 *)(tile + wslot) = as.v[2 * i];
+        *(u32x4 *)(tile + (1024 + 128) + wslot) = as.v[2 * i + 1];
+        aload2(S + 1, as, i);
+        if (on) {
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const u32x4 af = *(const u32x4 *)(tile + rslot0 + (((4 * c + kq) ^ (rl & 7)) * 16));
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+              for (int p = 0; p < PB; ++p) {
+                const u32x4 b = *(const u32x4 *)(base + ((c * PB + p) * NJ + j) * 1024 + lane * 16);
+                acc[i][j] = mfma16(af, b, acc[i][j]);
+              }
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+
+    // ---- K loop: A registers and the token stage of the next step load during this one
+    AStep as;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) aload2(0, as, i);
+    issue(0, 0);
+    for (int S = 0; S < nsteps; ++S) {
+      // step S's weights and tokens have landed, and every wave is done with the other stage
+      wait_ring_barrier<0>();
+      issue(S + 1, (S + 1) & 1);
+      compute(S, as, wave_on);
+    }
+  } else {
+    constexpr int NS = kDmStages;
+    constexpr int DMA_PER_WAVE = PB * NJ / 4;
+    static_assert((PB * NJ) % 4 == 0, "the token tile's fragments split evenly over 4 waves");
+    constexpr int VM_PER_STEP = 4 + DMA_PER_WAVE;
+    constexpr int STAGE = PB * NJ * 1024;
+    // this K part's steps s_lo .. s_lo + nsteps - 1
+    const int spp = (a.K / 32 + ks - 1) / ks;
+    const int s_lo = kp * spp;
+    const int nsteps = max(0, min(a.K / 32 - s_lo, spp));
+
+    uint32_t aoff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) aoff[i] = (uint32_t)(16 * i + rl) * rowb + (uint32_t)kq * 16u;
+    // token tile DMA: wave w copies fragments w, w+4, ... of the PB x NJ (plane, token
+    // block) fragments; lane l: token 16j + l % 16, columns 8 * (l / 16) .. +8
+    uint32_t boff[DMA_PER_WAVE];
+#pragma unroll
+    for (int u = 0; u < DMA_PER_WAVE; ++u) {
+      const int f = wave + 4 * u, p = f / NJ, j = f % NJ;
+      const int n = n0 + 16 * j + rl;
+      boff[u] = (uint32_t)p * (uint32_t)a.plane_elems * 2u + (uint32_t)n * rowb + (uint32_t)kq * 16u;
+    }
+
+    struct AStep {
+      u32x4 v[4];
+    };
+    // (rows past the segment and steps past the part read zeros: their offsets lie past
+    // the descriptors' sizes)
+    auto aload = [&](int S, AStep &s) {
+      const bool ok = S < nsteps;
+      const uint32_t so = (uint32_t)(s_lo + S) * 64u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s.v[i] = bload16(rA, ok ? aoff[i] + so : kOOB);
+    };
+    auto issue = [&](int S, int st) {
+      uint8_t *base = smem + st * STAGE;
+      const bool ok = S < nsteps;
+      const uint32_t so = (uint32_t)(s_lo + S) * 64u;
+#pragma unroll
+      for (int u = 0; u < DMA_PER_WAVE; ++u) dma16(rB, base + (wave + 4 * u) * 1024, ok ? boff[u] + so : kOOB);
+    };
+
+
+    auto compute = [&](int st, const AStep &as) {
+      const uint8_t *base = smem + st * STAGE;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+        for (int p = 0; p < PB; ++p) {
+          const u32x4 b = *(const u32x4 *)(base + (p * NJ + j) * 1024 + lane * 16);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[i][j] = mfma16(as.v[i], b, acc[i][j]);
+        }
+      }
+    };
+
+    // ---- K loop: A registers and token stages run NS-1 steps ahead; every step issues
+    // the same loads (zeros past the end), so the wait count is exact.
+    AStep as[NS];
+#pragma unroll
+    for (int d = 0; d + 1 < NS; ++d) {
+      aload(d, as[d]);
+      issue(d, d);
+    }
+    for (int S0 = 0; S0 < nsteps; S0 += NS) {
+#pragma unroll
+      for (int d = 0; d < NS; ++d) {
+        const int S = S0 + d;
+        wait_ring_barrier<(NS - 2) * VM_PER_STEP>();
+        aload(S + NS - 1, as[(d + NS - 1) % NS]);
+        issue(S + NS - 1, (d + NS - 1) % NS);
+        if (wave_on && S < nsteps) compute(d, as[d]);
+      }
     }
   }
 
   // ---- epilogue: lane holds rows 16i + 4kq .. +3 of token 16j + l % 16
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the ring's trailing copies have landed
+  // the factors are visible to every wave (a K part can be empty: then its loop has no
+  // barrier)
+  if constexpr (EPI == kEpiStoreScaled) __syncthreads();
   if (!wave_on) return;
   float *out = seg.out + lr0 + (size_t)kp * seg.pstride;
 #pragma unroll
@@ -225,6 +345,16 @@ int64_t dense_mm_parts_max(int M, int K, int N) {
   return best;
 }
 
+template <int PB, int NJ, int EPI>
+static hipError_t launch_dense_mm_t(const DenseMmArgs &a, int ks, hipStream_t s) {
+  const size_t lds = dense_mm_inv_off<PB, NJ>() + 64 * NJ;
+  if (lds > 65536 && lds_limit_once<k_dense_mm<PB, NJ, EPI>>((int)kMaxBlockLds) != hipSuccess)
+    return hipErrorInvalidValue;
+  const int64_t total = (int64_t)((a.M + 255) / 256) * ((a.N + 16 * NJ - 1) / (16 * NJ)) * ks;
+  launch_kernel(k_dense_mm<PB, NJ, EPI>, (unsigned)(8 * ((total + 7) / 8)), 256, lds, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_dense_mm(const DenseMmArgs &a, int pieces, int epi, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if (a.K % 32 != 0 || a.nseg < 1 || a.nseg > kDmMaxSegs) return hipErrorInvalidValue;
@@ -235,35 +365,12 @@ hipError_t launch_dense_mm(const DenseMmArgs &a, int pieces, int epi, hipStream_
   for (int i = 0; i < a.nseg; ++i)
     if (a.seg[i].row0 % 64 != 0 || (int64_t)a.seg[i].rows * a.K * 2 >= ((int64_t)1 << 31))
       return hipErrorInvalidValue;
-  if (pieces == 1 && epi == kEpiStore) {
-    constexpr int NJ = 8;
-    const int64_t total = (int64_t)((a.M + 255) / 256) * ((a.N + 16 * NJ - 1) / (16 * NJ)) * ks;
-    launch_kernel(k_dense_mm<1, NJ, kEpiStore>, (unsigned)(8 * ((total + 7) / 8)), 256,
-                  kDmStages * NJ * 1024 + 64 * NJ, s, a);
-  } else if (pieces == 2 && epi == kEpiStoreScaled) {
-    constexpr int NJ = 8;
-    const int64_t total = (int64_t)((a.M + 255) / 256) * ((a.N + 16 * NJ - 1) / (16 * NJ)) * ks;
-    launch_kernel(k_dense_mm<2, NJ, kEpiStoreScaled>, (unsigned)(8 * ((total + 7) / 8)), 256,
-                  kDmStages * 2 * NJ * 1024 + 64 * NJ, s, a);
-  } else if (pieces == 2 && epi == kEpiStore) {
-    constexpr int NJ = 8;
-    const int64_t total = (int64_t)((a.M + 255) / 256) * ((a.N + 16 * NJ - 1) / (16 * NJ)) * ks;
-    launch_kernel(k_dense_mm<2, NJ, kEpiStore>, (unsigned)(8 * ((total + 7) / 8)), 256,
-                  kDmStages * 2 * NJ * 1024 + 64 * NJ, s, a);
-  } else if (pieces == 2 && epi == kEpiAdd) {
-    constexpr int NJ = 8;
-    const int64_t total = (int64_t)((a.M + 255) / 256) * ((a.N + 16 * NJ - 1) / (16 * NJ)) * ks;
-    launch_kernel(k_dense_mm<2, NJ, kEpiAdd>, (unsigned)(8 * ((total + 7) / 8)), 256,
-                  kDmStages * 2 * NJ * 1024 + 64 * NJ, s, a);
-  } else if (pieces == 3 && epi == kEpiStoreScaled) {
-    constexpr int NJ = 4;
-    const int64_t total = (int64_t)((a.M + 255) / 256) * ((a.N + 16 * NJ - 1) / (16 * NJ)) * ks;
-    launch_kernel(k_dense_mm<3, NJ, kEpiStoreScaled>, (unsigned)(8 * ((total + 7) / 8)), 256,
-                  kDmStages * 3 * NJ * 1024 + 64 * NJ, s, a);
-  } else {
-    return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  if (pieces == 1 && epi == kEpiStore) return launch_dense_mm_t<1, 8, kEpiStore>(a, ks, s);
+  if (pieces == 2 && epi == kEpiStoreScaled) return launch_dense_mm_t<2, 8, kEpiStoreScaled>(a, ks, s);
+  if (pieces == 2 && epi == kEpiStore) return launch_dense_mm_t<2, 8, kEpiStore>(a, ks, s);
+  if (pieces == 2 && epi == kEpiAdd) return launch_dense_mm_t<2, 8, kEpiAdd>(a, ks, s);
+  if (pieces == 3 && epi == kEpiStoreScaled) return launch_dense_mm_t<3, 4, kEpiStoreScaled>(a, ks, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace k3
