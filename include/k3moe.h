@@ -80,7 +80,11 @@
  *  - Two kernel forms: small batches run the products as grouped / dense GEMVs, large
  *    ones as GEMMs (the expert passes from 6.25 token-expert pairs per expert on
  *    average; the up-projection from 8 tokens, the router and latent projection from
- *    40). A GEMM with few tiles splits its K range among blocks and sums the parts in a
+ *    40). From one pair per expert on average, an expert pass runs as two launches:
+ *    the experts of more than four pairs take the rows-split grouped GEMV (GEMV form)
+ *    or the grouped GEMM (GEMM form), the others the grouped GEMV that takes up to
+ *    four tokens per pass over an expert's weights (one pass each).
+ *    A GEMM with few tiles splits its K range among blocks and sums the parts in a
  *    fixed order. Every form gives the same result up to fp32 summation order.
  */
 #ifndef K3MOE_H
