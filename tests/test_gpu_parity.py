@@ -267,6 +267,29 @@ def test_expert_pass_counts_around_the_gemv_split(request, expert_path, shape, m
     check_rows(edn.cpu().numpy(), ref, f"{shape} crafted expert edn")
 
 
+# a latent width whose gate/up pass does not fit the rows-split kernel's LDS (224 scale
+# bytes per row) and makes the decode kernel take one token per pass, with an inter
+# width (64) that the grouped GEMM form cannot take for the down pass (K % 128 != 0)
+WIDE_LATENT = dataclasses.replace(k3gen.TINY, latent=7168, inter=64, n_experts=8, topk=2)
+
+
+@pytest.fixture(scope="module")
+def wide_latent():
+    return Host(WIDE_LATENT, 6)
+
+
+@pytest.mark.parametrize("mode", [k3moe.EXPERT_PATH_AUTO, k3moe.EXPERT_PATH_GEMV, k3moe.EXPERT_PATH_GEMM])
+@pytest.mark.parametrize("T", [3, 40])
+def test_wide_latent_form_fallbacks(wide_latent, expert_path, mode, T):
+    """At T = 40 the 80 pairs over 8 experts take the GEMM form's gate/up pass (auto and
+    forced) next to a GEMV-form down pass, or with the GEMV form forced the decode kernel
+    over every expert, several passes each (the rows-split kernel does not fit)."""
+    expert_path(mode)
+    say(f"wide latent (7168) layer T={T} expert form {mode}")
+    x, _ = _inputs.gap_fixed_x(WIDE_LATENT, 60 + T, T, wide_latent.dense["w_router"], wide_latent.dense["bias"])
+    compare_layer(wide_latent, x, what=f"wide latent T={T} form {mode}")
+
+
 # a shape whose up-projection (1024 x 1024) splits its K among blocks from 8 tokens on
 MID_UP = dataclasses.replace(k3gen.TINY, hidden=1024, latent=1024, inter=256, n_experts=64)
 
