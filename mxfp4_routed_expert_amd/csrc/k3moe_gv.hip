@@ -41,8 +41,6 @@ constexpr int kGvTile = 2048 + 128;  // a wave's tile: two 8-row chunks, the sec
 
 // s_waitcnt with vmcnt <= n and no wait on the other counters (gfx9 encoding)
 constexpr int gv_waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-// s_waitcnt lgkmcnt(0) only
-constexpr int gv_waitcnt_lgkm0 = 15 | (3 << 14) | (7 << 4);
 
 __device__ __forceinline__ int gv_rot(int t) { return (t & 1) + 8 * ((t >> 1) & 1); }
 
@@ -63,13 +61,13 @@ __device__ __forceinline__ void gv_dispatch_nc(int n, F &f) {
 }  // namespace
 
 // LDS of one block: scale rows [NA][ROWS][ng] (16-byte aligned) | activation ring
-// [NST][TT][1 KB] | the four waves' tiles
+// [2][TT][1 KB] | the four waves' tiles
 template <int NA, int RBW>
 __host__ __device__ inline size_t gv_scale_bytes(int ng) {
   return ((size_t)NA * 4 * 16 * RBW * ng + 15) & ~(size_t)15;
 }
 
-template <int NA, int EPI, int RBW, int NCT, int NST>
+template <int NA, int EPI, int RBW, int NCT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_grouped_gv(GroupedArgs a) {
   constexpr int TT = 4 * NCT;             // tokens per pass over the weights
   constexpr int WR = 16 * RBW;            // rows per wave of each matrix
@@ -78,7 +76,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int STAGE = TT * 1024;        // one step of the pass's activations
   static_assert(EPI != kEpiSitu || (NA == 2 && RBW % 2 == 0), "the SiTU epilogue quantizes whole 32-row groups");
   static_assert(TT % 4 == 0 && TT / 4 <= 4, "token copies split evenly over the four waves");
-  static_assert(NST == 1 || NST == 2, "one ring stage (the next step's copy waits for every wave's reads) or two");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rl = lane & 15, kq = lane >> 4;
@@ -98,7 +95,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   uint8_t *sS = smem;
   uint8_t *ring = smem + gv_scale_bytes<NA, RBW>(a.ng);
-  uint8_t *tile = ring + NST * STAGE + wave * kGvTile;
+  uint8_t *tile = ring + 2 * STAGE + wave * kGvTile;
 
   // ---- weight stream of this wave: NA matrices x RBW row blocks x 2 loads per step
   rsrc_t rA[NA];
@@ -137,7 +134,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
   const uint32_t bunit = (uint32_t)lane;
   auto copy_step = [&](int S) {
-    uint8_t *stage = ring + (NST == 2 ? (S & 1) * STAGE : 0);
+    uint8_t *stage = ring + (S & 1) * STAGE;
     const bool ok = S < nsup;
 #pragma unroll
     for (int u = 0; u < TT / 4; ++u) {
@@ -198,16 +195,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       constexpr int NC = decltype(nc_tag)::value;
       for (int S = 0; S < nsup; ++S) {
         // step S's weights and activations have landed (and, at S = 0, the scale rows are
-        // in LDS); with two stages, every wave is done with stage (S+1) & 1, which the next
-        // copy overwrites
+        // in LDS); every wave is done with stage (S+1) & 1, which the next copy overwrites
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(gv_waitcnt_vm(0));
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         asm volatile("" ::: "memory");
-        if constexpr (NST == 2) copy_step(S + 1);
-        const uint8_t *stage = ring + (NST == 2 ? (S & 1) * STAGE : 0);
+        copy_step(S + 1);
+        const uint8_t *stage = ring + (S & 1) * STAGE;
         // B operands of the step: k-chunk ks, column tile c (token 4c + tn, piece)
         uint32_t b[2][NC][6], sb[2][NC];
         bool gk[2];
@@ -229,16 +225,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             b[ks][c][3] = bv ? b0.w : 0u; b[ks][c][4] = bv ? b1.x : 0u; b[ks][c][5] = bv ? b1.y : 0u;
             sb[ks][c] = bv ? (b1.z & 255u) : 127u;
           }
-        }
-        if constexpr (NST == 1) {
-          // one stage: every wave has its B operands in registers before the next copy
-          asm volatile("" ::: "memory");
-          __builtin_amdgcn_sched_barrier(0);
-          __builtin_amdgcn_s_waitcnt(gv_waitcnt_lgkm0);
-          __builtin_amdgcn_s_barrier();
-          __builtin_amdgcn_sched_barrier(0);
-          asm volatile("" ::: "memory");
-          copy_step(S + 1);
         }
 #pragma unroll
         for (int m = 0; m < NA; ++m) {
@@ -316,34 +302,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
-template <int NA, int EPI, int RBW, int NCT, int NST>
+template <int NA, int EPI, int RBW, int NCT>
 static size_t gv_lds(int ng) {
-  return gv_scale_bytes<NA, RBW>(ng) + (size_t)NST * 4 * NCT * 1024 + (size_t)4 * kGvTile;
+  return gv_scale_bytes<NA, RBW>(ng) + (size_t)2 * 4 * NCT * 1024 + (size_t)4 * kGvTile;
 }
 
-template <int NA, int EPI, int RBW, int NCT, int NST>
+template <int NA, int EPI, int RBW, int NCT>
 static hipError_t launch_gv_t(const GroupedArgs &a, int grid_y, hipStream_t s) {
-  const size_t lds = gv_lds<NA, EPI, RBW, NCT, NST>(a.ng);
+  const size_t lds = gv_lds<NA, EPI, RBW, NCT>(a.ng);
   if (lds > kMaxBlockLds) return hipErrorInvalidValue;
-  if (lds_limit_once<k_grouped_gv<NA, EPI, RBW, NCT, NST>>((int)kMaxBlockLds) != hipSuccess)
+  if (lds_limit_once<k_grouped_gv<NA, EPI, RBW, NCT>>((int)kMaxBlockLds) != hipSuccess)
     return hipErrorInvalidValue;
   const unsigned gx = (unsigned)((a.M + 4 * 16 * RBW - 1) / (4 * 16 * RBW));
-  launch_kernel(k_grouped_gv<NA, EPI, RBW, NCT, NST>, dim3(gx, (unsigned)grid_y), 256, lds, s, a);
+  launch_kernel(k_grouped_gv<NA, EPI, RBW, NCT>, dim3(gx, (unsigned)grid_y), 256, lds, s, a);
   return hipGetLastError();
 }
 
 // gate/up: 32 rows of w1 and of w3 per wave; down: 64 rows of w2 per wave; 12 tokens a
 // pass
 bool grouped_gv_fits(const GroupedArgs &a, int epi) {
-  const size_t lds = epi == kEpiSitu ? gv_lds<2, kEpiSitu, 2, 3, 2>(a.ng) : gv_lds<1, kEpiEdn, 4, 3, 2>(a.ng);
+  const size_t lds = epi == kEpiSitu ? gv_lds<2, kEpiSitu, 2, 3>(a.ng) : gv_lds<1, kEpiEdn, 4, 3>(a.ng);
   return lds <= kMaxBlockLds && a.M % 32 == 0 && a.K % 32 == 0 && (size_t)a.ng * kGroupRec < ((size_t)1 << 31);
 }
 
 hipError_t launch_grouped_gv(const GroupedArgs &a, int epi, int grid_y, hipStream_t s) {
   if (grid_y <= 0) return hipSuccess;
   if (!grouped_gv_fits(a, epi)) return hipErrorInvalidValue;
-  if (epi == kEpiSitu) return launch_gv_t<2, kEpiSitu, 2, 3, 2>(a, grid_y, s);
-  return launch_gv_t<1, kEpiEdn, 4, 3, 2>(a, grid_y, s);
+  if (epi == kEpiSitu) return launch_gv_t<2, kEpiSitu, 2, 3>(a, grid_y, s);
+  return launch_gv_t<1, kEpiEdn, 4, 3>(a, grid_y, s);
 }
 
 }  // namespace k3
