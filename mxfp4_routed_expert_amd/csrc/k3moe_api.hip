@@ -520,6 +520,11 @@ int run_experts(const k3moe_dims *d, int32_t T, const float *z, bool zq_ready, c
                     grouped_dec_lds(d->inter, tt, rb_dn) > kMaxBlockLds))
     tt >>= 1;
   while (rb_gu > 4 && grouped_dec_lds(d->latent, tt, rb_gu) > kMaxBlockLds) rb_gu -= 2;
+  // the routed one-token gate/up pass (every block first selects the token's experts):
+  // 4 sixteen-row blocks per block, 768 blocks at the K3 shape, measured 0.6-0.8 us per
+  // layer step faster than the 6 (512 blocks, one round) of the estimate above; 2 (1536
+  // blocks) 5 us slower
+  if (route && rb_gu > 4) rb_gu = 4;
   while (rb_dn > 4 && grouped_dec_lds(d->inter, tt, rb_dn) > kMaxBlockLds) rb_dn -= 1;
   // In the GEMM form chosen by batch size, the experts of at most kGvBig pairs (listed
   // last in the active list) get no column tiles: the decode kernel streams their weights
