@@ -290,6 +290,12 @@ DenseArgs down_args(const k3moe_dims *d, int32_t T, const uint16_t *x, const uin
 
 // one-token forms (vector-ALU products over contiguous weight streams)
 constexpr int kRouterParts1 = 2;  // K parts of the one-token router product
+// The layer's one-token front and up-projection GEMVs run 4-wave blocks (672 and 896 of
+// them at the K3 shape) rather than one block per compute unit: alternating A/B, 91.7-91.9
+// against 92.7-92.9 us per layer step. The shared experts' one-token GEMVs and the
+// two-token launches measured slower that way (shared 44.5 against 43.4 us, layer at two
+// tokens 156 against 151 us) and keep theirs.
+constexpr int kGemv1OneTokenWaves = 4;
 
 Gemv1Args router1_args(const k3moe_dims *d, const uint16_t *x, const float *wr, const Ws &w) {
   Gemv1Args a = {};
@@ -402,7 +408,8 @@ int run_front(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_wei
     // one token: the router product and W_down stream in one launch; then the gate/up
     // pass selects the experts itself, or else one block selects them and writes the
     // token's dispatch while the launch's other blocks quantize z
-    K3_HIP(launch_gemv1_front(router1_args(d, x, wt->w_router, w), down1_args(d, x, wt->w_down, w.z32), s));
+    K3_HIP(launch_gemv1_front(router1_args(d, x, wt->w_router, w), down1_args(d, x, wt->w_down, w.z32), s,
+                              kGemv1OneTokenWaves));
     mark("router_and_latent_down");
     TopkArgs tk = topk_args(d, T, w.router_part, kRouterParts1, wt->bias, idx, tw);
     tk.expert_off = w.expert_off;
@@ -680,7 +687,7 @@ int run_combine(const k3moe_dims *d, int32_t T, const float *edn, const int32_t 
     // four this way measured slower than the dense GEMV form: 17.5 against 16.7 us)
     Gemv1Args a = up1_args(d, w_up, y, w);
     a.T = T;
-    K3_HIP(launch_gemv1(a, kA_BF16, kX_PLANES, kEpiStoreScaled, 2, s));
+    K3_HIP(launch_gemv1(a, kA_BF16, kX_PLANES, kEpiStoreScaled, 2, s, T == 1 ? kGemv1OneTokenWaves : 16));
   } else {
     DenseArgs a = {};
     a.A = w_up;

@@ -222,13 +222,21 @@ __global__ __launch_bounds__(1024) void k_gemv1_front(Gemv1Args r, Gemv1Args d, 
 }
 
 // Waves per block for `items` equal wave items: the per-unit share, or its largest
-// divisor up to 16 (so whole blocks divide evenly over the compute units).
-int gemv1_waves(int items) {
+// divisor up to 16 (so whole blocks divide evenly over the compute units), at most
+// max_waves.
+int gemv1_waves(int items, int max_waves) {
   const int per = (items + num_cus() - 1) / num_cus();
-  if (per <= 16) return per < 1 ? 1 : per;
-  for (int w = 16; w >= 4; --w)
-    if (per % w == 0) return w;
-  return 16;
+  int w = 16;
+  if (per <= 16) {
+    w = per < 1 ? 1 : per;
+  } else {
+    for (int v = 16; v >= 4; --v)
+      if (per % v == 0) {
+        w = v;
+        break;
+      }
+  }
+  return w < max_waves ? w : max_waves;
 }
 
 // LDS for the staged activations: 64 KB by default, up to 128 KB (one block per compute
@@ -270,14 +278,14 @@ int num_cus() {
 
 bool gemv1_supported(const Gemv1Args &a, int af) { return gemv1_ok(a, af == kA_F32 ? 4 : 2); }
 
-hipError_t launch_gemv1(const Gemv1Args &a, int af, int xf, int epi, int rpw, hipStream_t s) {
+hipError_t launch_gemv1(const Gemv1Args &a, int af, int xf, int epi, int rpw, hipStream_t s, int max_waves) {
   if (!gemv1_ok(a, af == kA_F32 ? 4 : 2) || (rpw != 1 && rpw != 2)) return hipErrorInvalidValue;
   if ((epi == kEpiGluAct || epi == kEpiAdd || epi == kEpiStoreScaled) && a.ks != 1) return hipErrorInvalidValue;
   if (epi == kEpiGluAct && (rpw != 2 || !a.A2)) return hipErrorInvalidValue;
   const int tt = a.T > 1 ? a.T : 1;
   if (tt > 1 && epi == kEpiStore) return hipErrorInvalidValue;
   const int items = (epi == kEpiGluAct ? a.M : (a.M + rpw - 1) / rpw) * a.ks;
-  const int waves = gemv1_waves(items);
+  const int waves = gemv1_waves(items, max_waves);
   const int grid = (items + waves - 1) / waves;
   const size_t lds = (size_t)tt * a.K * 4;
 #define G1(AF_, XF_, EPI_, R_, TT_) \
@@ -310,7 +318,7 @@ hipError_t launch_front_t(const Gemv1Args &r, const Gemv1Args &d, int r_items, i
   return hipGetLastError();
 }
 
-hipError_t launch_gemv1_front(const Gemv1Args &r, const Gemv1Args &d, hipStream_t s) {
+hipError_t launch_gemv1_front(const Gemv1Args &r, const Gemv1Args &d, hipStream_t s, int max_waves) {
   // one x for both; the item kinds must stream the same bytes for the blocks to balance;
   // one to four tokens
   if (!gemv1_ok(r, 4) || !gemv1_ok(d, 2) || r.K != d.K || r.xb != d.xb || d.ks != 1 || r.T != d.T)
@@ -318,7 +326,7 @@ hipError_t launch_gemv1_front(const Gemv1Args &r, const Gemv1Args &d, hipStream_
   // two rows per wave item (28 KB of row bytes for both kinds): measured 0.6-0.8 us per
   // decode step faster than one row
   const int r_items = ((r.M + 1) / 2) * r.ks, items = r_items + (d.M + 1) / 2;
-  const int waves = gemv1_waves(items);
+  const int waves = gemv1_waves(items, max_waves);
   const int grid = (items + waves - 1) / waves;
   // one or two tokens, both against one weight stream (three and four, with 84 and 112
   // KB of staged x and one block per compute unit, measured no faster than the GEMV forms)

@@ -210,10 +210,11 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
 // rows per wave (1 or 2); bf16 kX_BF16 kEpiGluAct (rpw 2: the row of A and of A2); bf16
 // kX_F32 kEpiAdd (rpw 2)
 bool gemv1_supported(const Gemv1Args &a, int af);
-hipError_t launch_gemv1(const Gemv1Args &a, int af, int xf, int epi, int rpw, hipStream_t s);
+// max_waves caps the waves per block (one block per compute unit by default)
+hipError_t launch_gemv1(const Gemv1Args &a, int af, int xf, int epi, int rpw, hipStream_t s, int max_waves = 16);
 // the router product (fp32 weights, kEpiStore, its K parts) and the latent projection
 // (bf16 weights, ks = 1) of one token, same x, in one launch
-hipError_t launch_gemv1_front(const Gemv1Args &r, const Gemv1Args &d, hipStream_t s);
+hipError_t launch_gemv1_front(const Gemv1Args &r, const Gemv1Args &d, hipStream_t s, int max_waves = 16);
 // the latent projection (DenseArgs, bf16 weights, kEpiStore) and the top-k in one launch
 hipError_t launch_down_topk(const DenseArgs &d, const TopkArgs &tk, hipStream_t s);
 // rows of fp32 values into fp6 piece records (n % 32 == 0); q8: each 32-value group
