@@ -13,16 +13,21 @@
 //
 // Block: 4 waves x 64 weight rows (four 16-row fragments each) by BN tokens; each wave's
 // rows are its own. The token tile of every step is copied by buffer loads with an LDS
-// destination into a ring, lane l's 16 bytes landing at 16*l, which is the register image
-// of a 16x16x32 bf16 MFMA operand (token l % 16, columns 8*(l/16) .. +8). The weights:
+// destination into a ring. A copy instruction reads 16 tokens x 64 bytes row by row (lane
+// l: token l / 4, four consecutive lanes one token's 64 contiguous bytes); reading 16 rows
+// at one 16-byte column per group of 16 lanes instead (the operand's own lane order) made
+// the copies and the weight loads together cost about twice the matrix work of a step. In
+// LDS, token t of a 16-token fragment sits at 64 t with its 16-byte unit u at slot
+// u ^ tswz(t), so that the operand reads (lane l: token l % 16, unit l / 16) meet no bank
+// conflict. The weights:
 //  - one token plane (the router and latent projections, the shared gate/up): 64 columns
 //    a step, read in whole 128-byte lines (8 rows x 128 B per load, one step ahead in
 //    registers), each 16-row block turned into fragments through a swizzled LDS tile (as
-//    in the grouped GEMV); a ring of 2 token stages. A load that touches 16 rows x 64 B
-//    keeps the texture-address units busy for longer than one of 8 rows x 128 B;
-//  - two or three planes (more matrix work per weight byte): 32 columns a step, the
-//    fragments loaded straight into registers (16 rows x 64 B per load) kDmStages-1
-//    steps ahead, a ring of kDmStages token stages (whole lines measured slower here).
+//    in the grouped GEMV); a ring of 2 token stages;
+//  - two or three planes (more matrix work per weight byte): 32 columns a step, read row
+//    by row like the tokens (16 rows x 64 B per load) kDmStages-1 steps ahead in
+//    registers, and turned into fragments through the wave's LDS tile in the tokens'
+//    layout; a ring of kDmStages token stages (whole lines measured no faster here).
 // Tiles are numbered so that each XCD works through a contiguous run in which 8 row
 // blocks share each token block, keeping both operands' current K slices in its L2.
 #include "k3moe_common.h"
@@ -56,7 +61,7 @@ __device__ __forceinline__ void wait_ring_barrier() {
 // RMSNorm factors of its tokens
 template <int PB, int NJ>
 __host__ __device__ constexpr size_t dense_mm_inv_off() {
-  return PB == 1 ? (size_t)2 * 2 * NJ * 1024 + 4 * kDmTile : (size_t)kDmStages * PB * NJ * 1024;
+  return PB == 1 ? (size_t)2 * 2 * NJ * 1024 + 4 * kDmTile : (size_t)kDmStages * PB * NJ * 1024 + 4 * 4096;
 }
 
 template <int PB, int NJ, int EPI>
@@ -67,6 +72,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rl = lane & 15, kq = lane >> 4;
+  // token fragments in LDS: token t of a 16-token block at 64 t, its 16-byte unit u at slot
+  // u ^ tswz(t); the copy of lane l reads token l / 4, so that four consecutive lanes read
+  // 64 contiguous bytes of one token row
+  auto tswz = [](int t) { return ((t >> 1) ^ (t >> 3)) & 3; };
+  const int dtok = lane >> 2, dunit = (lane & 3) ^ tswz(lane >> 2);
+  const uint32_t rsw = (uint32_t)(rl * 64 + ((kq ^ tswz(rl)) & 3) * 16);
 
   // ---- tile: contiguous runs per XCD, 8 row blocks x every token block per group; the
   // K parts of a tile are consecutive
@@ -152,9 +163,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int u = 0; u < DMA_PER_WAVE; ++u) {
       const int f = wave + 4 * u, c = f / (PB * NJ), p = (f % (PB * NJ)) / NJ, j = f % NJ;
-      const int n = n0 + 16 * j + rl;
+      const int n = n0 + 16 * j + dtok;
       bchunk[u] = c;
-      boff[u] = (uint32_t)p * (uint32_t)a.plane_elems * 2u + (uint32_t)n * rowb + (uint32_t)kq * 16u + (uint32_t)c * 64u;
+      boff[u] = (uint32_t)p * (uint32_t)a.plane_elems * 2u + (uint32_t)n * rowb + (uint32_t)dunit * 16u + (uint32_t)c * 64u;
     }
 
     struct AStep {
@@ -184,30 +195,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const uint32_t rslot0 = (uint32_t)((rl >> 3) * (1024 + 128) + (rl & 7) * 128);
 
     // step S: each 16-row block into the tile, its registers reloaded with step S+1, its two
-    // chunks' fragments back (this wave's LDS operations run in order), then the products
+    // chunks' fragments back into registers (this wave's LDS operations run in order); then
+    // the products, each token fragment read from LDS once for the four row blocks (one
+    // read per product would ask more of LDS than it delivers)
     auto compute = [&](int S, AStep &as, bool on) {
       const uint8_t *base = smem + (S & 1) * STAGE;
+      u32x4 af[4][2];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         *(u32x4 *)(tile + wslot) = as.v[2 * i];
         *(u32x4 *)(tile + (1024 + 128) + wslot) = as.v[2 * i + 1];
         aload2(S + 1, as, i);
-        if (on) {
 #pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            const u32x4 af = *(const u32x4 *)(tile + rslot0 + (((4 * c + kq) ^ (rl & 7)) * 16));
+        for (int c = 0; c < 2; ++c) af[i][c] = *(const u32x4 *)(tile + rslot0 + (((4 * c + kq) ^ (rl & 7)) * 16));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (on) {
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) {
+        for (int c = 0; c < 2; ++c) {
 #pragma unroll
-              for (int p = 0; p < PB; ++p) {
-                const u32x4 b = *(const u32x4 *)(base + ((c * PB + p) * NJ + j) * 1024 + lane * 16);
-                acc[i][j] = mfma16(af, b, acc[i][j]);
-              }
+          for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+            for (int p = 0; p < PB; ++p) {
+              const u32x4 b = *(const u32x4 *)(base + ((c * PB + p) * NJ + j) * 1024 + rsw);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[i][j] = mfma16(af[i][c], b, acc[i][j]);
             }
           }
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
+      __builtin_amdgcn_sched_barrier(0);
     };
 
     // ---- K loop: A registers and the token stage of the next step load during this one
@@ -234,15 +251,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
     uint32_t aoff[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) aoff[i] = (uint32_t)(16 * i + rl) * rowb + (uint32_t)kq * 16u;
+    for (int i = 0; i < 4; ++i) aoff[i] = (uint32_t)(16 * i + dtok) * rowb + (uint32_t)dunit * 16u;
+    // this wave's weight tile: the step's four 16-row blocks in the token fragments' layout
+    uint8_t *atile = smem + (size_t)NS * STAGE + wave * 4096;
     // token tile DMA: wave w copies fragments w, w+4, ... of the PB x NJ (plane, token
     // block) fragments; lane l: token 16j + l % 16, columns 8 * (l / 16) .. +8
     uint32_t boff[DMA_PER_WAVE];
 #pragma unroll
     for (int u = 0; u < DMA_PER_WAVE; ++u) {
       const int f = wave + 4 * u, p = f / NJ, j = f % NJ;
-      const int n = n0 + 16 * j + rl;
-      boff[u] = (uint32_t)p * (uint32_t)a.plane_elems * 2u + (uint32_t)n * rowb + (uint32_t)kq * 16u;
+      const int n = n0 + 16 * j + dtok;
+      boff[u] = (uint32_t)p * (uint32_t)a.plane_elems * 2u + (uint32_t)n * rowb + (uint32_t)dunit * 16u;
     }
 
     struct AStep {
@@ -267,13 +286,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
     auto compute = [&](int st, const AStep &as) {
       const uint8_t *base = smem + st * STAGE;
+      // the weight rows, loaded row-major, back as fragments through the wave's tile (this
+      // wave's LDS operations run in order, so the previous step's reads are done)
+      u32x4 af[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *(u32x4 *)(atile + i * 1024 + lane * 16) = as.v[i];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = *(const u32x4 *)(atile + i * 1024 + rsw);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
 #pragma unroll
         for (int p = 0; p < PB; ++p) {
-          const u32x4 b = *(const u32x4 *)(base + (p * NJ + j) * 1024 + lane * 16);
+          const u32x4 b = *(const u32x4 *)(base + (p * NJ + j) * 1024 + rsw);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[i][j] = mfma16(as.v[i], b, acc[i][j]);
+          for (int i = 0; i < 4; ++i) acc[i][j] = mfma16(af[i], b, acc[i][j]);
         }
       }
     };
