@@ -130,6 +130,14 @@ constexpr int kGvMinT = 5;
 bool gv_split(const k3moe_dims *d, int32_t T) {
   return T >= kGvMinT && (int64_t)T * d->topk >= d->n_experts;
 }
+// The rows-split launch streams its experts' weights with streaming loads while most of
+// them fit one 12-token pass: up to K3_GV_NT_PPE pairs per expert on average.
+#ifndef K3_GV_NT_PPE
+#define K3_GV_NT_PPE 2
+#endif
+bool gv_stream_once(const k3moe_dims *d, int32_t T) {
+  return (int64_t)T * d->topk <= (int64_t)K3_GV_NT_PPE * d->n_experts;
+}
 
 // grouped GEMM form for a pass with K columns and activation records of rec_bytes.
 // Measured at the K3 shape (both passes, whole layer, the GEMV form with its two kernels
@@ -598,7 +606,7 @@ int run_experts(const k3moe_dims *d, int32_t T, const float *z, bool zq_ready, c
   } else {
     g.split = !route && !one_token && gv_split(d, T) && grouped_gv_fits(g, kEpiSitu);
     K3_HIP(launch_grouped(g, kEpiSitu, tt, rb_gu, grid_y, s, route != nullptr));
-    if (g.split) K3_HIP(launch_grouped_gv(g, kEpiSitu, grid_big, s));
+    if (g.split) K3_HIP(launch_grouped_gv(g, kEpiSitu, grid_big, gv_stream_once(d, T), s));
   }
   mark(route ? "topk_expert_gateup_situ" : "expert_gateup_situ");
   if (d->idot) {
@@ -644,7 +652,7 @@ int run_experts(const k3moe_dims *d, int32_t T, const float *z, bool zq_ready, c
   } else {
     h.split = !one_token && gv_split(d, T) && grouped_gv_fits(h, kEpiEdn);
     K3_HIP(launch_grouped(h, kEpiEdn, tt, rb_dn, grid_y, s));
-    if (h.split) K3_HIP(launch_grouped_gv(h, kEpiEdn, grid_big, s));
+    if (h.split) K3_HIP(launch_grouped_gv(h, kEpiEdn, grid_big, gv_stream_once(d, T), s));
   }
   mark("expert_down");
   return K3MOE_OK;

@@ -84,6 +84,16 @@ __device__ __forceinline__ uint32_t bload8(rsrc_t r, uint32_t off) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
 }
 // 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at lds + 16 l
+// Streaming loads (the nt cache policy) for bytes read once per launch: weight rows that a
+// kernel streams exactly once. A plain 8 GiB read runs at 7.0-7.1 TB/s with them against
+// 6.0-6.3 TB/s without; bytes read again soon (shared tiles, passes over the same rows)
+// must not use them, since they are not kept for a second read.
+__device__ __forceinline__ u32x4 bload16_nt(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
+}
+__device__ __forceinline__ void dma16_nt(rsrc_t r, uint8_t *lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, off, 0, 0, 2);
+}
 __device__ __forceinline__ void dma16(rsrc_t r, uint8_t *lds, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, off, 0, 0, 0);
 }

@@ -107,7 +107,7 @@ __device__ __forceinline__ void gemv1_item(const Gemv1Args &a, float *sx, int it
     for (int r = 0; r < RPW; ++r)
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        w[r][c] = bload16(rA[r], c0 + c < nchunk ? (uint32_t)(c0 + c) * 1024u + (uint32_t)lane * 16u : kOOB);
+        w[r][c] = bload16_nt(rA[r], c0 + c < nchunk ? (uint32_t)(c0 + c) * 1024u + (uint32_t)lane * 16u : kOOB);
   };
   float acc[TT][RPW];
 #pragma unroll

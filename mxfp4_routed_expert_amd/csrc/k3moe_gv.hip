@@ -67,7 +67,7 @@ __host__ __device__ inline size_t gv_scale_bytes(int ng) {
   return ((size_t)NA * 4 * 16 * RBW * ng + 15) & ~(size_t)15;
 }
 
-template <int NA, int EPI, int RBW, int NCT>
+template <int NA, int EPI, int RBW, int NCT, bool NTW>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_grouped_gv(GroupedArgs a) {
   constexpr int TT = 4 * NCT;             // tokens per pass over the weights
   constexpr int WR = 16 * RBW;            // rows per wave of each matrix
@@ -103,12 +103,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int m = 0; m < NA; ++m)
     rA[m] = make_rsrc(a.A[m].packed + (size_t)e * a.A[m].pstride + (size_t)wr0 * rowb, (uint32_t)nwr * rowb);
   const uint32_t lv = (uint32_t)(lane >> 3) * rowb + (uint32_t)(lane & 7) * 16u;
+  // NTW: streaming loads, for launches whose experts mostly fit one pass (streamed once);
+  // with several passes the plain loads keep an expert's rows cached for the next pass.
   u32x4 w[NL];
   auto load_rb = [&](int S, int m, int r) {
     const bool ok = S < nsup;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-      w[(m * RBW + r) * 2 + h] = bload16(rA[m], ok ? lv + (uint32_t)S * 128u + (uint32_t)(2 * r + h) * 8u * rowb : kOOB);
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t off = ok ? lv + (uint32_t)S * 128u + (uint32_t)(2 * r + h) * 8u * rowb : kOOB;
+      if constexpr (NTW) w[(m * RBW + r) * 2 + h] = bload16_nt(rA[m], off);
+      else w[(m * RBW + r) * 2 + h] = bload16(rA[m], off);
+    }
   };
   const int wrr = lane >> 3, wu = lane & 7;
   const uint32_t wslot = (uint32_t)(wrr * 128 + ((wu ^ wrr) * 16));
@@ -166,7 +171,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int nb = nbr * (int)ng;
     if ((((uintptr_t)src) & 15) == 0 && nb % 1024 == 0) {
       const rsrc_t rS = make_rsrc(src, (uint32_t)nb);
-      for (int c = wave; c < nb / 1024; c += 4) dma16(rS, dst + c * 1024, (uint32_t)c * 1024u + (uint32_t)lane * 16u);
+      for (int c = wave; c < nb / 1024; c += 4) dma16_nt(rS, dst + c * 1024, (uint32_t)c * 1024u + (uint32_t)lane * 16u);
     } else if ((((uintptr_t)src) & 3) == 0) {
       for (int i = threadIdx.x; i < ROWS * (int)ng / 4; i += blockDim.x)
         ((uint32_t *)dst)[i] = 4 * i < nb ? ((const uint32_t *)src)[i] : 0u;
@@ -307,14 +312,14 @@ static size_t gv_lds(int ng) {
   return gv_scale_bytes<NA, RBW>(ng) + (size_t)2 * 4 * NCT * 1024 + (size_t)4 * kGvTile;
 }
 
-template <int NA, int EPI, int RBW, int NCT>
+template <int NA, int EPI, int RBW, int NCT, bool NTW>
 static hipError_t launch_gv_t(const GroupedArgs &a, int grid_y, hipStream_t s) {
   const size_t lds = gv_lds<NA, EPI, RBW, NCT>(a.ng);
   if (lds > kMaxBlockLds) return hipErrorInvalidValue;
-  if (lds_limit_once<k_grouped_gv<NA, EPI, RBW, NCT>>((int)kMaxBlockLds) != hipSuccess)
+  if (lds_limit_once<k_grouped_gv<NA, EPI, RBW, NCT, NTW>>((int)kMaxBlockLds) != hipSuccess)
     return hipErrorInvalidValue;
   const unsigned gx = (unsigned)((a.M + 4 * 16 * RBW - 1) / (4 * 16 * RBW));
-  launch_kernel(k_grouped_gv<NA, EPI, RBW, NCT>, dim3(gx, (unsigned)grid_y), 256, lds, s, a);
+  launch_kernel(k_grouped_gv<NA, EPI, RBW, NCT, NTW>, dim3(gx, (unsigned)grid_y), 256, lds, s, a);
   return hipGetLastError();
 }
 
@@ -325,11 +330,12 @@ bool grouped_gv_fits(const GroupedArgs &a, int epi) {
   return lds <= kMaxBlockLds && a.M % 32 == 0 && a.K % 32 == 0 && (size_t)a.ng * kGroupRec < ((size_t)1 << 31);
 }
 
-hipError_t launch_grouped_gv(const GroupedArgs &a, int epi, int grid_y, hipStream_t s) {
+hipError_t launch_grouped_gv(const GroupedArgs &a, int epi, int grid_y, bool stream_once, hipStream_t s) {
   if (grid_y <= 0) return hipSuccess;
   if (!grouped_gv_fits(a, epi)) return hipErrorInvalidValue;
-  if (epi == kEpiSitu) return launch_gv_t<2, kEpiSitu, 2, 3>(a, grid_y, s);
-  return launch_gv_t<1, kEpiEdn, 4, 3>(a, grid_y, s);
+  if (epi == kEpiSitu)
+    return stream_once ? launch_gv_t<2, kEpiSitu, 2, 3, true>(a, grid_y, s) : launch_gv_t<2, kEpiSitu, 2, 3, false>(a, grid_y, s);
+  return stream_once ? launch_gv_t<1, kEpiEdn, 4, 3, true>(a, grid_y, s) : launch_gv_t<1, kEpiEdn, 4, 3, false>(a, grid_y, s);
 }
 
 }  // namespace k3

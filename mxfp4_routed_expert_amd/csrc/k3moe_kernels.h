@@ -256,7 +256,9 @@ bool route_in_gateup_ok(const GroupedArgs &a);
 // j < n_active[3]; each wave owns its own rows over the whole K range and a pass takes up
 // to 12 of an expert's tokens.
 bool grouped_gv_fits(const GroupedArgs &a, int epi);
-hipError_t launch_grouped_gv(const GroupedArgs &a, int epi, int grid_y, hipStream_t s);
+// stream_once: the weights take streaming loads (for batches whose experts mostly fit one
+// 12-token pass)
+hipError_t launch_grouped_gv(const GroupedArgs &a, int epi, int grid_y, bool stream_once, hipStream_t s);
 
 hipError_t launch_grouped(const GroupedArgs &a, int epi, int tokens_per_tile, int rb, int grid_y, hipStream_t s,
                           bool route = false);

@@ -700,12 +700,15 @@ __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
   // with the same rows of step S+1, so the weight stream runs one step ahead.
   // Bytes past the row (a partial last step) belong to the next row or lie outside the
   // descriptor; the k-blocks they would form are masked by their activations (zeros).
+  // The weights take streaming loads: an expert is streamed once per launch, except in a
+  // GEMV-form batch of 5 to about 55 tokens whose expert holds more than TT pairs (rare
+  // at such sizes), whose later passes then re-read it from HBM.
   u32x4 w[NL];
   auto load_block = [&](int S, int r) {
     const bool ok = S < s_hi;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-      w[2 * r + h] = bload16(rA, ok ? lv + (uint32_t)S * 128u + (uint32_t)(2 * r + h) * 8u * rowb : kOOB);
+      w[2 * r + h] = bload16_nt(rA, ok ? lv + (uint32_t)S * 128u + (uint32_t)(2 * r + h) * 8u * rowb : kOOB);
   };
   auto load = [&](int S) {
 #pragma unroll
@@ -743,7 +746,7 @@ __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
     for (int i = wave; i < NA * nsc; i += 4) {
       const int m = i / nsc, c = i - m * nsc;
       const rsrc_t rS = make_rsrc(a.A[m].scales + (size_t)e * a.A[m].sstride + (size_t)row0 * ng, (uint32_t)nb);
-      dma16(rS, sS + m * ROWS * (int)ng + c * 1024, (uint32_t)c * 1024u + (uint32_t)lane * 16u);
+      dma16_nt(rS, sS + m * ROWS * (int)ng + c * 1024, (uint32_t)c * 1024u + (uint32_t)lane * 16u);
     }
     for (int i = wave; i < (RT ? 0 : ntok0 * nbc); i += 4) {
       const int tt = i / nbc, c = i - tt * nbc;
