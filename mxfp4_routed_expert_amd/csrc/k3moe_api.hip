@@ -185,7 +185,7 @@ Ws carve(const k3moe_dims *d, int32_t T, void *base) {
   w.actq = (uint8_t *)take(P * I * 4);
   w.edn = (float *)take(P * L * 4);
   for (int q = 0; q < 3; ++q) w.np[q] = (uint16_t *)take(t * L * 2);
-  w.ss = (float *)take(t * ((L + 255) / 256) * 4);
+  w.ss = (float *)take(t * combine_norm_parts(L) * 4);
   w.wr_planes = T >= kFrontMmMinT ? (uint16_t *)take(3 * E * (size_t)d->hidden * 2) : nullptr;
   w.z_parts = T >= kFrontMmMinT ? (float *)take((size_t)front_parts * L * 4) : nullptr;
   // sized for the largest K-part count of any batch up to T (nondecreasing in T)
@@ -336,7 +336,7 @@ Gemv1Args up1_args(const k3moe_dims *d, const uint16_t *w_up, float *y, const Ws
   for (int q = 0; q < 3; ++q) a.xp[q] = w.np[q];
   a.out = y;
   a.ss = w.ss;
-  a.nss = (d->latent + 255) / 256;
+  a.nss = combine_norm_parts(d->latent);
   a.eps = d->eps;
   return a;
 }
@@ -674,7 +674,7 @@ int run_combine(const k3moe_dims *d, int32_t T, const float *edn, const int32_t 
     a.B = w.np[0];
     a.plane_elems = (int64_t)(w.np[1] - w.np[0]);  // the three planes are carved back to back
     a.ss = w.ss;
-    a.nss = (d->latent + 255) / 256;
+    a.nss = combine_norm_parts(d->latent);
     a.eps = d->eps;
     a.ks = dense_mm_ks(a.M, a.K, T);
     // two bf16 pieces (hi + lo) of the normed aggregate: the dropped third piece is
@@ -706,7 +706,7 @@ int run_combine(const k3moe_dims *d, int32_t T, const float *edn, const int32_t 
     a.N = T;
     a.out = y;
     a.ss = w.ss;
-    a.nss = (d->latent + 255) / 256;
+    a.nss = combine_norm_parts(d->latent);
     a.eps = d->eps;
     K3_HIP(launch_dense_bf16(a, kPieces, kEpiStoreScaled, s));
   }

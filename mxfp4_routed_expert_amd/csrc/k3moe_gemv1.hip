@@ -186,14 +186,16 @@ __global__ __launch_bounds__(1024) void k_gemv1(Gemv1Args a, int items) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int item = blockIdx.x * (blockDim.x >> 6) + wave;
   const bool live = item < items;  // every wave takes part in the staging
-  // the RMSNorm factors (kEpiStoreScaled) of the launch's tokens
+  // the RMSNorm factors (kEpiStoreScaled) of the launch's tokens, read in the epilogue:
+  // formed with the staging, after the first weight loads are in flight (their partial
+  // sums, just written by the previous launch, would otherwise hold back the stream)
   float scale[4] = {1.f, 1.f, 1.f, 1.f};
-  if constexpr (EPI == kEpiStoreScaled) {
-#pragma unroll
-    for (int t = 0; t < TT; ++t) scale[t] = rms_inv(a, t);
-  }
   gemv1_item<AF, EPI, RPW, TT>(a, sx, live ? item : 0, live, scale, [&] {
     stage_x<XF, TT>(a, sx);
+    if constexpr (EPI == kEpiStoreScaled) {
+#pragma unroll
+      for (int t = 0; t < TT; ++t) scale[t] = rms_inv(a, t);
+    }
     __syncthreads();
   });
 }

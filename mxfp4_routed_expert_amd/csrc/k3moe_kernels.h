@@ -50,6 +50,8 @@ inline hipError_t lds_limit_once(int bytes) {
 }
 
 constexpr int kMaxRouterSplits = 8;  // partial router products summed by the top-k
+// RMSNorm partial sums of a latent row that the combine writes (one per 1024 columns)
+inline int combine_norm_parts(int L) { return (L + 1023) / 1024; }
 constexpr int kMaxNormParts = 64;    // column blocks of 256 in one latent row (latent <= 16384)
 
 // ---------------------------------------------------------------- dense products

@@ -1046,8 +1046,9 @@ hipError_t launch_quant_rows(const float *src, size_t n, uint8_t *dst, bool q8, 
 }
 
 // ============================================================== combine
-// Grid (column blocks of 256, tokens). acc = sum_j w_j edn[slot_j] in slot order
-// j = 0..K-1 (all K loads issued before the sums); the block writes gamma * acc as
+// Grid (column blocks of 1024, four columns per thread, tokens). acc = sum_j w_j
+// edn[slot_j] in slot order j = 0..K-1 (16-byte streaming loads, 16 in flight: edn is read
+// once; at 4096 tokens 206 -> 181 us against one 4-byte load per row); the block writes gamma * acc as
 // three bf16 pieces for the up-projection and its share of sum(acc^2), from which the
 // up-projection's epilogue forms the RMSNorm factor 1/sqrt(mean(acc^2) + eps). With
 // IDENT (one token, slot j = pair j) the edn rows and the weights load together.
@@ -1062,7 +1063,7 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ edn,
   __shared__ float wt[32];
   __shared__ float red[4];
   const int t = blockIdx.y;
-  const int c = blockIdx.x * 256 + threadIdx.x;
+  const int c = 4 * (blockIdx.x * 256 + threadIdx.x);  // four columns per thread
   if constexpr (!IDENT) {
     if (threadIdx.x < 32) {
       const bool ok = threadIdx.x < K;
@@ -1071,25 +1072,48 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ edn,
     }
     __syncthreads();
   }
-  float v = 0.f;
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
   if (c < L) {
-    float ev[32];
+    // the edn rows are read once: streaming loads, 16 of them in flight
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const int sj = IDENT ? j : slot[j];
-      ev[j] = (j < K && sj >= 0) ? edn[(size_t)sj * L + c] : 0.f;
+    for (int j0 = 0; j0 < 32; j0 += 16) {
+      if (j0 >= K) break;
+      f32x4 ev[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int jj = j0 + j;
+        const int sj = IDENT ? jj : slot[jj];
+        ev[j] = (jj < K && sj >= 0) ? __builtin_nontemporal_load((const f32x4 *)(edn + (size_t)sj * L + c))
+                                    : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int jj = j0 + j;
+        if (jj < K) {
+          const float w = IDENT ? topk_w[jj] : wt[jj];
+          v[0] = fmaf(w, ev[j][0], v[0]);
+          v[1] = fmaf(w, ev[j][1], v[1]);
+          v[2] = fmaf(w, ev[j][2], v[2]);
+          v[3] = fmaf(w, ev[j][3], v[3]);
+        }
+      }
     }
+    const float4 g = *(const float4 *)(gamma + c);
+    const float gv[4] = {g.x, g.y, g.z, g.w};
+    uint32_t q[3][4];
 #pragma unroll
-    for (int j = 0; j < 32; ++j)
-      if (j < K) v = fmaf(IDENT ? topk_w[j] : wt[j], ev[j], v);
-    uint32_t p[3] = {0, 0, 0};
-    split_bf16<3>(v * gamma[c], p);
+    for (int i = 0; i < 4; ++i) {
+      uint32_t p[3] = {0, 0, 0};
+      split_bf16<3>(v[i] * gv[i], p);
+      q[0][i] = p[0]; q[1][i] = p[1]; q[2][i] = p[2];
+    }
     const size_t o = (size_t)t * L + c;
-    p0[o] = (uint16_t)p[0];
-    p1[o] = (uint16_t)p[1];
-    p2[o] = (uint16_t)p[2];
+    uint16_t *const dst[3] = {p0, p1, p2};
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+      *(uint2 *)(dst[k] + o) = uint2{q[k][0] | (q[k][1] << 16), q[k][2] | (q[k][3] << 16)};
   }
-  float ss = v * v;
+  float ss = (v[0] * v[0] + v[1] * v[1]) + (v[2] * v[2] + v[3] * v[3]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
@@ -1101,8 +1125,8 @@ hipError_t launch_combine(const float *edn, const int32_t *pair_slot, const floa
                           const float *gamma, int T, int K, int L, uint16_t *p0, uint16_t *p1,
                           uint16_t *p2, float *ss_part, bool ident, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  if (ident && T != 1) return hipErrorInvalidValue;
-  dim3 grid((L + 255) / 256, T);
+  if ((ident && T != 1) || L % 4 != 0 || K > 32) return hipErrorInvalidValue;
+  dim3 grid(combine_norm_parts(L), T);
   if (ident) {
     launch_kernel(k_combine<true>, grid, 256, 0, s, edn, pair_slot, topk_w, gamma, K, L, p0, p1, p2, ss_part);
   } else {
