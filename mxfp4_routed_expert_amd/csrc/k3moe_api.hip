@@ -58,6 +58,25 @@ int check_mx(const k3moe_mxfp4 &m) {
   return K3MOE_OK;
 }
 
+// The turn-major scale copy (k3moe_prepare_gemm_scales): w1, w3 and w2 regions, each
+// [E][gemm_scale_turns(ng)][rows][kGemmScaleTurn] bytes, at 256-byte aligned offsets.
+struct GemmScalesLayout {
+  int64_t stride_gu, stride_dn;  // bytes per expert: w1 and w3, w2
+  size_t off_w1, off_w3, off_w2, bytes;
+};
+GemmScalesLayout gemm_scales_layout(const k3moe_dims *d) {
+  GemmScalesLayout g;
+  const size_t E = (size_t)d->n_experts;
+  g.stride_gu = (int64_t)gemm_scale_turns(d->latent / 32) * d->inter * kGemmScaleTurn;
+  g.stride_dn = (int64_t)gemm_scale_turns(d->inter / 32) * d->latent * kGemmScaleTurn;
+  auto up = [](size_t n) { return (n + 255) & ~(size_t)255; };
+  g.off_w1 = 0;
+  g.off_w3 = up(E * (size_t)g.stride_gu);
+  g.off_w2 = g.off_w3 + up(E * (size_t)g.stride_gu);
+  g.bytes = g.off_w2 + up(E * (size_t)g.stride_dn);
+  return g;
+}
+
 struct Ws {
   float *router_part;          // [splits][T][E]
   float *z32;                  // [T][L] latent (layer path)
@@ -515,10 +534,12 @@ int run_down(const k3moe_dims *d, int32_t T, const uint16_t *x, const uint16_t *
 // z: the latent [T][L] fp32; zq_ready: w.zq already holds its piece records. route
 // (nullable): a one-token selection that the gate/up pass runs itself (run_front).
 // one_token: the layer's own one-token dispatch (slot j = pair j, expert active[j]).
+// tscales (nullable): the turn-major scale copy, read by the GEMM form.
 int run_experts(const k3moe_dims *d, int32_t T, const float *z, bool zq_ready, const TopkArgs *route,
-                bool one_token, const k3moe_experts *ex, const int32_t *expert_off,
+                bool one_token, const k3moe_experts *ex, const uint8_t *tscales, const int32_t *expert_off,
                 const int32_t *sorted_pair, const int32_t *active, const int32_t *counters, float *edn,
                 const Ws &w, hipStream_t s) {
+  const GemmScalesLayout gsl = gemm_scales_layout(d);
   const uint8_t *zq = w.zq;
   const int64_t P = (int64_t)T * d->topk;
   const bool mm_gu = use_mm(d, T, d->latent, (int64_t)T * d->latent * 4, ex->w1, ex->w3);
@@ -602,6 +623,11 @@ int run_experts(const k3moe_dims *d, int32_t T, const float *z, bool zq_ready, c
     m.outq = w.actq;
     m.b1 = d->b1;
     m.b2 = d->b2;
+    if (tscales) {
+      m.tscales[0] = tscales + gsl.off_w1;
+      m.tscales[1] = tscales + gsl.off_w3;
+      m.tscales_stride = gsl.stride_gu;
+    }
     K3_HIP(launch_grouped_mm(m, kEpiSitu, max_tiles, s));
   } else {
     g.split = !route && !one_token && gv_split(d, T) && grouped_gv_fits(g, kEpiSitu);
@@ -648,6 +674,10 @@ int run_experts(const k3moe_dims *d, int32_t T, const float *z, bool zq_ready, c
     m.tiles = w.tiles;
     m.n_tiles = w.counters + 2;
     m.out = edn;
+    if (tscales) {
+      m.tscales[0] = m.tscales[1] = tscales + gsl.off_w2;
+      m.tscales_stride = gsl.stride_dn;
+    }
     K3_HIP(launch_grouped_mm(m, kEpiEdn, max_tiles, s));
   } else {
     h.split = !one_token && gv_split(d, T) && grouped_gv_fits(h, kEpiEdn);
@@ -902,6 +932,35 @@ int k3moe_layer_noalloc(const k3moe_dims *d, int32_t T, const uint16_t *x, const
   return k3moe_layer(d, T, x, wt, y, topk_idx_out, topk_w_out, ws, (size_t)K3MOE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
+int k3moe_gemm_scales_size(const k3moe_dims *d, size_t *bytes) {
+  K3_TRY(check_dims(d));
+  if (!bytes) return K3MOE_EINVAL;
+  *bytes = gemm_scales_layout(d).bytes;
+  return K3MOE_OK;
+}
+
+int k3moe_prepare_gemm_scales(const k3moe_dims *d, const k3moe_experts *ex, void *dst, size_t bytes,
+                              void *stream) {
+  K3_TRY(check_dims(d));
+  if (!ex || !dst) return K3MOE_EINVAL;
+  const k3moe_mxfp4 *mats[3] = {&ex->w1, &ex->w3, &ex->w2};
+  for (const k3moe_mxfp4 *m : mats) K3_TRY(check_mx(*m));
+  if (((uintptr_t)dst & 255u) != 0) return K3MOE_EUNSUPPORTED;
+  const GemmScalesLayout g = gemm_scales_layout(d);
+  if (bytes < g.bytes) return K3MOE_EWORKSPACE;
+  if (g.stride_gu >= ((int64_t)1 << 31) || g.stride_dn >= ((int64_t)1 << 31)) return K3MOE_EUNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t *o = (uint8_t *)dst;
+  const int E = d->n_experts, L = d->latent, I = d->inter;
+  K3_HIP(launch_turn_major_scales(ex->w1.scales, ex->w1.scales_expert_stride, E, I, L / 32, o + g.off_w1,
+                                  g.stride_gu, s));
+  K3_HIP(launch_turn_major_scales(ex->w3.scales, ex->w3.scales_expert_stride, E, I, L / 32, o + g.off_w3,
+                                  g.stride_gu, s));
+  K3_HIP(launch_turn_major_scales(ex->w2.scales, ex->w2.scales_expert_stride, E, L, I / 32, o + g.off_w2,
+                                  g.stride_dn, s));
+  return K3MOE_OK;
+}
+
 int k3moe_workspace_size(const k3moe_dims *d, int32_t T, size_t *bytes) {
   K3_TRY(check_dims(d));
   K3_TRY(check_T(d, T));
@@ -963,8 +1022,8 @@ int k3moe_expert_glu_mxfp4(const k3moe_dims *d, int32_t T, const float *z, const
   if (T == 0) return K3MOE_OK;
   hipStream_t s = (hipStream_t)stream;
   K3_HIP(launch_active_from_off(expert_off, d->n_experts, w.active, w.counters, s));
-  return run_experts(d, T, z, false, nullptr, false, ex, expert_off, sorted_pair, w.active, w.counters, edn, w,
-                     s);
+  return run_experts(d, T, z, false, nullptr, false, ex, nullptr, expert_off, sorted_pair, w.active, w.counters,
+                     edn, w, s);
 }
 
 int k3moe_combine(const k3moe_dims *d, int32_t T, const float *edn, const int32_t *pair_slot,
@@ -989,7 +1048,8 @@ int k3moe_layer(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_w
   K3_TRY(check_mx(wt->ex.w1));
   K3_TRY(check_mx(wt->ex.w3));
   K3_TRY(check_mx(wt->ex.w2));
-  if (!al16(x) || !al16(wt->w_router) || !al16(wt->w_down) || !al16(wt->w_up))
+  if (!al16(x) || !al16(wt->w_router) || !al16(wt->w_down) || !al16(wt->w_up) ||
+      ((uintptr_t)wt->gemm_scales & 255u) != 0)
     return K3MOE_EUNSUPPORTED;
   Ws w;
   K3_TRY(check_ws(d, T, ws, ws_bytes, &w));
@@ -1004,8 +1064,8 @@ int k3moe_layer(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_w
   // selected the experts itself (a slot the top-p rule dropped is then marked in active[]),
   // else unless the top-p rule compacted the dispatch
   const bool one_token = T == 1 && (route.T != 0 || !(d->topp > 0.f));
-  K3_TRY(run_experts(d, T, w.z32, zq_ready, route.T ? &route : nullptr, one_token, &wt->ex, w.expert_off,
-                     w.sorted_pair, w.active, w.counters, w.edn, w, s));
+  K3_TRY(run_experts(d, T, w.z32, zq_ready, route.T ? &route : nullptr, one_token, &wt->ex, wt->gemm_scales,
+                     w.expert_off, w.sorted_pair, w.active, w.counters, w.edn, w, s));
   return run_combine(d, T, w.edn, w.pair_slot, tw, wt->norm_w, wt->w_up, y, one_token, w, s);
 }
 

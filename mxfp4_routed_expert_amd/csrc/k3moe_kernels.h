@@ -197,7 +197,18 @@ struct MmArgs {
   float *out;             // kEpiEdn: [slot][M] fp32
   uint8_t *outq;          // kEpiSitu: [slot][M/32] fp6 piece records of act
   float b1, b2;
+  // optional: the scales turn-major (k3moe_prepare_gemm_scales), expert e of matrix m at
+  // tscales[m] + e * tscales_stride, [gemm_scale_turns(ng)][M][kGemmScaleTurn]
+  const uint8_t *tscales[2];
+  int64_t tscales_stride;
 };
+// The GEMM reads each row's scale bytes a ring turn (three 128-column steps, 12 bytes) at
+// a time; the turn-major copy puts a turn's bytes of consecutive rows next to each other.
+constexpr int kGemmScaleTurn = 12;
+__host__ __device__ inline int gemm_scale_turns(int ng) { return (ng + kGemmScaleTurn - 1) / kGemmScaleTurn; }
+// one matrix's turn-major scales for E experts of M rows and ng groups per row
+hipError_t launch_turn_major_scales(const uint8_t *src, int64_t sstride, int E, int M, int ng, uint8_t *dst,
+                                    int64_t dstride, hipStream_t s);
 
 // ---------------------------------------------------------------- launchers
 hipError_t launch_route_down(const DenseArgs &router, int ks, const DenseArgs *down, hipStream_t s);

@@ -155,19 +155,27 @@ void k_grouped_mm(MmArgs a) {
   auto frow = [](int f) { return PERM ? 32 * (f >> 1) + 4 * (f & 1) : 16 * f; };
   const int rw0 = rb * BM + RW * wave;
   const int nrw = __builtin_amdgcn_readfirstlane(max(0, min(RW, a.M - rw0)));
+  // scale bytes: row-major ([M][ng], a row's turns 12 bytes apart) or turn-major
+  // ([turns][M][12], a turn's rows 12 bytes apart: the 16 rows of a fragment read 192
+  // contiguous bytes instead of 12 bytes from each of 16 lines, which are evicted between
+  // turns; 2-3% faster GEMMs)
   rsrc_t rA[NA], rS[NA];
+  const bool tmaj = a.tscales[0] != nullptr;
 #pragma unroll
   for (int m = 0; m < NA; ++m) {
     rA[m] = make_rsrc(a.A[m].packed + (size_t)e * a.A[m].pstride + (size_t)rw0 * rowb, (uint32_t)nrw * rowb);
-    rS[m] = make_rsrc(a.A[m].scales + (size_t)e * a.A[m].sstride + (size_t)rw0 * ng, (uint32_t)nrw * ng);
+    rS[m] = tmaj ? make_rsrc(a.tscales[m] + (size_t)e * a.tscales_stride, (uint32_t)a.tscales_stride)
+                 : make_rsrc(a.A[m].scales + (size_t)e * a.A[m].sstride + (size_t)rw0 * ng, (uint32_t)nrw * ng);
   }
+  static_assert(4 * NS == kGemmScaleTurn, "one turn-major record per ring turn");
+  const uint32_t sturn = tmaj ? (uint32_t)a.M * kGemmScaleTurn : 4u * NS;  // bytes between turns
   // each fragment's lane offsets into the wave's rows (packed bytes, scale bytes); rows
   // past the matrix lie past the descriptors' sizes and read as zeros
   uint32_t aoff[FPM], soff[FPM];
 #pragma unroll
   for (int f = 0; f < FPM; ++f) {
     aoff[f] = (uint32_t)(frow(f) + lrow) * rowb + (uint32_t)kq * 16u;
-    soff[f] = (uint32_t)(frow(f) + lrow) * ng;
+    soff[f] = tmaj ? (uint32_t)(rw0 + frow(f) + lrow) * kGemmScaleTurn : (uint32_t)(frow(f) + lrow) * ng;
   }
 
   // ---- token copies: wave w issues copies DPW*w .. DPW*w+DPW-1; copy j moves tokens 2j
@@ -221,7 +229,7 @@ void k_grouped_mm(MmArgs a) {
     const bool ok = NS * j < nsteps;
 #pragma unroll
     for (int i = 0; i < NF; ++i) {
-      const uint32_t so = ok ? soff[i % FPM] + (uint32_t)j * (4u * NS) : kOOB;
+      const uint32_t so = ok ? soff[i % FPM] + (uint32_t)j * sturn : kOOB;
       if constexpr (NS == 3) sraw[i] = bload12(rS[i / FPM], so);
       else sraw[i] = bload16(rS[i / FPM], so);
     }
@@ -471,6 +479,44 @@ void k_grouped_mm(MmArgs a) {
 #ifndef K3_MM_STAGES
 #define K3_MM_STAGES 3
 #endif
+
+// dst[e][j][r][0..11] = the scale bytes 12j .. 12j+11 of row r of expert e (zeros past
+// the row's ng), one thread per (expert, turn, row): dword copies where the rows and the
+// source are 4-byte aligned (DW), else byte copies
+template <bool DW>
+__global__ __launch_bounds__(256) void k_turn_major_scales(const uint8_t *__restrict__ src, int64_t sstride, int E,
+                                                           int M, int ng, uint8_t *__restrict__ dst, int64_t dstride) {
+  const int nturn = gemm_scale_turns(ng);
+  const int64_t per = (int64_t)M * nturn, n = (int64_t)E * per;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < n; q += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e = q / per, rem = q - e * per;
+    const int j = (int)(rem / M), r = (int)(rem - (int64_t)j * M);
+    const int c0 = kGemmScaleTurn * j;
+    const uint8_t *sp = src + e * sstride + (int64_t)r * ng + c0;
+    uint8_t *dp = dst + e * dstride + ((int64_t)j * M + r) * kGemmScaleTurn;
+    if constexpr (DW) {
+      uint32_t v[3];
+#pragma unroll
+      for (int i = 0; i < 3; ++i) v[i] = c0 + 4 * i + 4 <= ng ? *(const uint32_t *)(sp + 4 * i) : 0u;
+#pragma unroll
+      for (int i = 0; i < 3; ++i) ((uint32_t *)dp)[i] = v[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < kGemmScaleTurn; ++i) dp[i] = c0 + i < ng ? sp[i] : (uint8_t)0;
+    }
+  }
+}
+
+hipError_t launch_turn_major_scales(const uint8_t *src, int64_t sstride, int E, int M, int ng, uint8_t *dst,
+                                    int64_t dstride, hipStream_t s) {
+  if (E <= 0 || M <= 0 || ng <= 0) return hipSuccess;
+  if (dstride < (int64_t)gemm_scale_turns(ng) * M * kGemmScaleTurn) return hipErrorInvalidValue;
+  const bool dw = ng % 4 == 0 && sstride % 4 == 0 && ((uintptr_t)src & 3) == 0 && ((uintptr_t)dst & 3) == 0 &&
+                  dstride % 4 == 0;
+  if (dw) launch_kernel(k_turn_major_scales<true>, 8192, 256, 0, s, src, sstride, E, M, ng, dst, dstride);
+  else launch_kernel(k_turn_major_scales<false>, 8192, 256, 0, s, src, sstride, E, M, ng, dst, dstride);
+  return hipGetLastError();
+}
 
 size_t grouped_mm_lds() { return (size_t)K3_MM_STAGES * kStageB; }
 

@@ -26,6 +26,7 @@ class DeviceLayer:
     experts: torch.Tensor       # uint8 [E * blob_bytes]: per-expert records back to back
     blob_bytes: int
     offsets: dict
+    gemm_scales: torch.Tensor | None = None  # the experts' scales turn-major (k3moe_prepare_gemm_scales)
 
     def experts_struct(self) -> k3moe.k3moe_experts:
         base = self.experts.data_ptr()
@@ -35,21 +36,32 @@ class DeviceLayer:
             return k3moe.k3moe_mxfp4(base + self.offsets[p], base + self.offsets[s], B, B)
         return k3moe.k3moe_experts(mx("w1p", "w1s"), mx("w3p", "w3s"), mx("w2p", "w2s"))
 
-    def weights_struct(self) -> k3moe.k3moe_weights:
+    def weights_struct(self, gemm_scales: bool = True) -> k3moe.k3moe_weights:
+        """gemm_scales=False leaves the turn-major copy out (the GEMM then reads the plain scales)."""
+        gs = self.gemm_scales.data_ptr() if (gemm_scales and self.gemm_scales is not None) else None
         return k3moe.k3moe_weights(self.w_router.data_ptr(), self.bias.data_ptr(), self.w_down.data_ptr(),
-                                   self.w_up.data_ptr(), self.norm_w.data_ptr(), self.experts_struct())
+                                   self.w_up.data_ptr(), self.norm_w.data_ptr(), self.experts_struct(), gs)
+
+    def prepare_gemm_scales(self):
+        """Allocate and fill the turn-major scale copy (once per set of expert weights)."""
+        n = k3moe.k3moe_gemm_scales_size(self.dims)
+        self.gemm_scales = torch.empty(max(n, 256), dtype=torch.uint8, device=self.experts.device)
+        k3moe.k3moe_prepare_gemm_scales(self.dims, self.experts_struct(), self.gemm_scales)
+        torch.cuda.synchronize(self.experts.device)
 
 
-def upload_layer(dims, dense: dict, expert_chunks, blob_bytes: int, offsets: dict, device="cuda") -> DeviceLayer:
+def upload_layer(dims, dense: dict, expert_chunks, blob_bytes: int, offsets: dict, device="cuda",
+                 gemm_scales: bool = True) -> DeviceLayer:
     """dense: host arrays (w_router fp32 [E,H], bias fp32 [E], w_down/w_up bf16 bits, norm_w fp32).
     expert_chunks: iterable of (first expert, uint8 blob array) covering experts 0..E-1 in order;
-    each chunk is copied into one preallocated device buffer, so host memory stays at one chunk."""
+    each chunk is copied into one preallocated device buffer, so host memory stays at one chunk.
+    gemm_scales: also make the turn-major scale copy that the prefill GEMM reads."""
     E = dims.n_experts
     ex = torch.empty(E * blob_bytes, dtype=torch.uint8, device=device)
     for e0, arr in expert_chunks:
         n = arr.size
         ex[e0 * blob_bytes: e0 * blob_bytes + n].copy_(torch.from_numpy(arr), non_blocking=False)
-    return DeviceLayer(
+    layer = DeviceLayer(
         dims=dims,
         w_router=_dev(dense["w_router"].astype(np.float32), device),
         bias=_dev(dense["bias"].astype(np.float32), device),
@@ -57,6 +69,9 @@ def upload_layer(dims, dense: dict, expert_chunks, blob_bytes: int, offsets: dic
         w_up=_dev(dense["w_up"].view(np.int16), device),
         norm_w=_dev(dense["norm_w"].astype(np.float32), device),
         experts=ex, blob_bytes=blob_bytes, offsets=dict(offsets))
+    if gemm_scales:
+        layer.prepare_gemm_scales()
+    return layer
 
 
 def workspace(dims, T: int, device="cuda") -> torch.Tensor:

@@ -103,6 +103,24 @@ def test_expert_stage_refuses_before_launch():
     assert f(d, 0, FAKE, _experts(), FAKE, FAKE, FAKE, WS, check=False) == k3moe.K3MOE_OK
 
 
+def test_gemm_scales_size_and_refusals():
+    d = _d()
+    n = k3moe.k3moe_gemm_scales_size(d)
+    # three 256-byte aligned regions of E experts x ceil(ng / 12) turns x rows x 12 bytes
+    up = lambda v: (v + 255) // 256 * 256
+    gu = -(-(d.latent // 32) // 12) * d.inter * 12
+    dn = -(-(d.inter // 32) // 12) * d.latent * 12
+    assert n == 2 * up(d.n_experts * gu) + up(d.n_experts * dn)
+    f = k3moe.k3moe_prepare_gemm_scales
+    assert f(d, _experts(), None, check=False) == k3moe.K3MOE_EINVAL
+    assert f(d, _experts(), (FAKE, n - 1), check=False) == k3moe.K3MOE_EWORKSPACE
+    assert f(d, _experts(), (FAKE + 16, n), check=False) == k3moe.K3MOE_EUNSUPPORTED
+    assert f(d, _experts(stride=-16), (FAKE, n), check=False) == k3moe.K3MOE_EINVAL
+    # the layer refuses a copy that is not 256-byte aligned
+    w = k3moe.k3moe_weights(FAKE, FAKE, FAKE, FAKE, FAKE, _experts(), FAKE + 16)
+    assert k3moe.k3moe_layer(d, 4, FAKE, w, FAKE, None, None, WS, check=False) == k3moe.K3MOE_EUNSUPPORTED
+
+
 def test_other_entry_points_refuse_before_launch():
     d = _d()
     assert k3moe.k3moe_latent_proj_bf16(d, 4, FAKE, None, FAKE, WS, check=False) == k3moe.K3MOE_EINVAL

@@ -107,7 +107,7 @@ def t_(a, dtype=None):
     return t if dtype is None else t.to(dtype)
 
 
-def run_layer(h: Host, x: np.ndarray):
+def run_layer(h: Host, x: np.ndarray, gemm_scales: bool = True):
     d = h.dims
     T = x.shape[0]
     xd = t_(x.view(np.int16))
@@ -115,7 +115,7 @@ def run_layer(h: Host, x: np.ndarray):
     idx = torch.empty((T, d.topk), dtype=torch.int32, device="cuda")
     w = torch.empty((T, d.topk), dtype=torch.float32, device="cuda")
     ws = device.workspace(d, T)
-    k3moe.k3moe_layer(d, T, xd, h.dev.weights_struct(), y, idx, w, ws)
+    k3moe.k3moe_layer(d, T, xd, h.dev.weights_struct(gemm_scales), y, idx, w, ws)
     torch.cuda.synchronize()
     return y.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
 
@@ -444,6 +444,65 @@ def test_k3_layer_few_tokens(k3, T):
 def test_k3_layer_config2_T64(k3):
     x, _ = _inputs.gap_fixed_x(k3.dims, 2, 64, k3.dense["w_router"], k3.dense["bias"])
     compare_layer(k3, x, what="K3 T=64")
+
+
+def turn_major_reference(dims, blobs: np.ndarray) -> np.ndarray:
+    """The turn-major scale copy written out from the expert blobs' scale bytes (numpy):
+    regions for w1, w3, w2 at 256-byte aligned offsets, each [E][ceil(ng/12)][rows][12]
+    holding bytes 12j .. 12j+11 of each row (zeros past ng)."""
+    lay = k3gen.ExpertLayout(dims)
+    per = blobs.reshape(dims.n_experts, lay.blob_bytes)
+    sizes = dict(lay.sizes)
+    out = []
+    for name, rows, ng in (("w1s", dims.inter, dims.latent // 32), ("w3s", dims.inter, dims.latent // 32),
+                           ("w2s", dims.latent, dims.inter // 32)):
+        o = lay.offsets[name]
+        s = per[:, o:o + sizes[name]].reshape(dims.n_experts, rows, ng)
+        nt = -(-ng // 12)
+        pad = np.zeros((dims.n_experts, rows, nt * 12), np.uint8)
+        pad[:, :, :ng] = s
+        region = pad.reshape(dims.n_experts, rows, nt, 12).transpose(0, 2, 1, 3).reshape(-1)
+        out.append(np.concatenate([region, np.zeros((-region.size) % 256, np.uint8)]))
+    return np.concatenate(out)
+
+
+@pytest.mark.parametrize("which", ["tiny_mm", "tiny_mm_nan"])
+def test_turn_major_scales_bytes(which, request):
+    """k3moe_prepare_gemm_scales writes exactly the turn-major relayout of the blobs'
+    scale bytes (NaN codes and padding included)."""
+    h = request.getfixturevalue(which)
+    say(f"turn-major scale copy of {which}")
+    ref = turn_major_reference(h.dims, h.blobs)
+    got = h.dev.gemm_scales.cpu().numpy()
+    assert got.size >= ref.size == k3moe.k3moe_gemm_scales_size(h.dims)
+    assert np.array_equal(got[:ref.size], ref)
+
+
+@pytest.mark.parametrize("which,T", [("tiny_mm", 700), ("tiny_mm", 300), ("tiny_mm_nan", 300), ("k3", 64)])
+def test_gemm_scales_copy_or_not_same_result(which, T, expert_path, request):
+    """The grouped GEMM reading the turn-major copy or the plain scale bytes gives the same
+    bits; the plain path is checked against the oracle as well."""
+    h = request.getfixturevalue(which)
+    expert_path(k3moe.EXPERT_PATH_GEMM)
+    say(f"{which} T={T} GEMM form with and without the turn-major scales")
+    x, _ = _inputs.gap_fixed_x(h.dims, 300 + T, T, h.dense["w_router"], h.dense["bias"])
+    y1, i1, w1 = run_layer(h, x, gemm_scales=True)
+    y0, i0, w0 = run_layer(h, x, gemm_scales=False)
+    assert np.array_equal(i0, i1) and np.array_equal(w0, w1)
+    assert np.array_equal(y0.view(np.uint32), y1.view(np.uint32))
+    rows = np.arange(T) if T <= 300 else np.arange(0, T, 7)
+    ref = oracle.layer(h.dims, x[rows], h.dense, h.ex)
+    assert np.array_equal(i0[rows], ref["idx"])
+    check_rows(y0[rows], ref["y"], f"{which} T={T} plain scales y")
+
+
+def test_gemm_scales_ignored_by_gemv_form(tiny_mm, expert_path):
+    """The GEMV form never reads the copy: the same bits with or without it."""
+    expert_path(k3moe.EXPERT_PATH_GEMV)
+    x, _ = _inputs.gap_fixed_x(TINY_MM, 77, 64, tiny_mm.dense["w_router"], tiny_mm.dense["bias"])
+    y1, _, _ = run_layer(tiny_mm, x, gemm_scales=True)
+    y0, _, _ = run_layer(tiny_mm, x, gemm_scales=False)
+    assert np.array_equal(y0.view(np.uint32), y1.view(np.uint32))
 
 
 def test_k3_layer_T64_grouped_gemm(k3, expert_path):
