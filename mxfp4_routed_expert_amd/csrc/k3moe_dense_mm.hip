@@ -137,8 +137,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if constexpr (WL) {
     constexpr int NS = 2;            // token stages of 64 columns
     constexpr int NF = 2 * PB * NJ;  // token fragments of a step (two 32-column chunks)
-    constexpr int DMA_PER_WAVE = NF / 4;
-    static_assert(NF % 4 == 0, "the token tile's fragments split evenly over 4 waves");
+    constexpr int DMA_PER_WAVE = (NF + 3) / 4;  // wave w copies fragments w, w+4, ... below NF
+    static_assert(NF % 2 == 0, "two chunks of every (plane, token block) fragment");
     constexpr int STAGE = NF * 1024;
     // this K part's 32-column chunks s_lo .. s_lo + n32 - 1, s_lo even, taken 64 columns
     // (128 bytes of a row) per step
@@ -184,6 +184,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const uint32_t so = (uint32_t)(s_lo + 2 * S) * 64u;
 #pragma unroll
       for (int u = 0; u < DMA_PER_WAVE; ++u) {
+        if (NF % 4 != 0 && wave + 4 * u >= NF) continue;  // (uniform per wave)
         const bool ok = S < nsteps && 2 * S + bchunk[u] < n32;
         dma16(rB, base + (wave + 4 * u) * 1024, ok ? boff[u] + so : kOOB);
       }
@@ -391,7 +392,23 @@ hipError_t launch_dense_mm(const DenseMmArgs &a, int pieces, int epi, hipStream_
   for (int i = 0; i < a.nseg; ++i)
     if (a.seg[i].row0 % 64 != 0 || (int64_t)a.seg[i].rows * a.K * 2 >= ((int64_t)1 << 31))
       return hipErrorInvalidValue;
-  if (pieces == 1 && epi == kEpiStore) return launch_dense_mm_t<1, 8, kEpiStore>(a, ks, s);
+  if (pieces == 1 && epi == kEpiStore) {
+    // Without a K split, 112-token tiles where they fill the rounds of two blocks per
+    // compute unit better than 128-token ones, by at least 5%: the cost is the rounds
+    // times the tile width, a last round of at most one block per compute unit counting
+    // 0.6 (such a block runs alone). At the K3 shape, T = 4096: 800 tiles (1.56 rounds)
+    // against 925 (1.81), router and latent projection 0.465 -> 0.432 ms; T = 8192 keeps
+    // 128 (1600 tiles, whose fourth round is 64 blocks).
+    if (ks == 1) {
+      const int64_t nm = (a.M + 255) / 256, ncu = num_cus();
+      auto cost = [&](int nj) {
+        const int64_t tiles = nm * ((a.N + 16 * nj - 1) / (16 * nj)), full = tiles / (2 * ncu), rem = tiles % (2 * ncu);
+        return ((double)full + (rem == 0 ? 0.0 : rem > ncu ? 1.0 : 0.6)) * nj;
+      };
+      if (cost(7) < 0.95 * cost(8)) return launch_dense_mm_t<1, 7, kEpiStore>(a, ks, s);
+    }
+    return launch_dense_mm_t<1, 8, kEpiStore>(a, ks, s);
+  }
   if (pieces == 2 && epi == kEpiStoreScaled) return launch_dense_mm_t<2, 8, kEpiStoreScaled>(a, ks, s);
   if (pieces == 2 && epi == kEpiStore) return launch_dense_mm_t<2, 8, kEpiStore>(a, ks, s);
   if (pieces == 2 && epi == kEpiAdd) return launch_dense_mm_t<2, 8, kEpiAdd>(a, ks, s);
