@@ -94,7 +94,7 @@ struct Ws {
   uint8_t *actq;               // [P][I/32] fp6 piece records of the SiTU outputs
   float *edn;                  // [P][L]
   uint16_t *np[3];             // [T][L] pieces of gamma * acc
-  float *ss;                   // [T][ceil(L/256)] partial sums of acc^2
+  float *ss;                   // [T][ceil(L/1024)] partial sums of acc^2 (combine_norm_parts)
   uint16_t *wr_planes;         // [3][E][H] bf16 pieces of the router weights (GEMM form)
   float *up_parts;             // [ks][T][H] K parts of the up-projection (GEMM form, small batches)
   float *z_parts;              // [ks][T][L] K parts of the latent projection (GEMM form, small batches)
