@@ -692,8 +692,9 @@ int run_experts(const k3moe_dims *d, int32_t T, const float *z, bool zq_ready, c
 int run_combine(const k3moe_dims *d, int32_t T, const float *edn, const int32_t *pair_slot,
                 const float *topk_w, const float *norm_w, const uint16_t *w_up, float *y,
                 bool one_token, const Ws &w, hipStream_t s) {
+  // the GEMM-form up-projection reads two of the three bf16 pieces: the third is not written
   K3_HIP(launch_combine(edn, pair_slot, topk_w, norm_w, T, d->topk, d->latent, w.np[0], w.np[1],
-                        w.np[2], w.ss, one_token && T == 1, s));
+                        use_up_mm(d, T) ? nullptr : w.np[2], w.ss, one_token && T == 1, s));
   mark("combine");
   if (use_up_mm(d, T)) {
     DenseMmArgs a = {};

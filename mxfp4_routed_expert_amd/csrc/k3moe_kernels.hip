@@ -1111,7 +1111,8 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ edn,
     uint16_t *const dst[3] = {p0, p1, p2};
 #pragma unroll
     for (int k = 0; k < 3; ++k)
-      *(uint2 *)(dst[k] + o) = uint2{q[k][0] | (q[k][1] << 16), q[k][2] | (q[k][3] << 16)};
+      if (k < 2 || p2)  // (a null p2: the up-projection reads two pieces)
+        *(uint2 *)(dst[k] + o) = uint2{q[k][0] | (q[k][1] << 16), q[k][2] | (q[k][3] << 16)};
   }
   float ss = (v[0] * v[0] + v[1] * v[1]) + (v[2] * v[2] + v[3] * v[3]);
 #pragma unroll
