@@ -316,7 +316,7 @@ DenseArgs down_args(const k3moe_dims *d, int32_t T, const uint16_t *x, const uin
 }
 
 // one-token forms (vector-ALU products over contiguous weight streams)
-constexpr int kRouterParts1 = 2;  // K parts of the one-token router product
+constexpr int kRouterParts1 = 1;  // K parts of the one-token router product (whole rows)
 // The layer's one-token front and up-projection GEMVs run 4-wave blocks (672 and 896 of
 // them at the K3 shape) rather than one block per compute unit: alternating A/B, 91.7-91.9
 // against 92.7-92.9 us per layer step. The shared experts' one-token GEMVs and the

@@ -201,8 +201,8 @@ __global__ __launch_bounds__(1024) void k_gemv1(Gemv1Args a, int items) {
 }
 
 // The router product and the latent down-projection of one token in one launch (both
-// read only x): wave items [0, r_items) are router row-pair parts, the rest W_down row
-// pairs. The two kinds of item stream the same number of bytes. Every wave reaches
+// read only x): wave items [0, r_items) are router rows (or their K parts), the rest
+// W_down row pairs. The two kinds of item stream the same number of bytes. Every wave reaches
 // exactly one block barrier, inside the staging of whichever branch it takes (the branch
 // is uniform per wave).
 template <int TT>
@@ -216,7 +216,7 @@ __global__ __launch_bounds__(1024) void k_gemv1_front(Gemv1Args r, Gemv1Args d, 
     __syncthreads();
   };
   if (item < r_items) {
-    gemv1_item<kA_F32, kEpiStore, 2, TT>(r, sx, item, true, kOnes, staged);
+    gemv1_item<kA_F32, kEpiStore, 1, TT>(r, sx, item, true, kOnes, staged);
   } else {
     const bool live = item < items;
     gemv1_item<kA_BF16, kEpiStore, 2, TT>(d, sx, live ? item - r_items : 0, live, kOnes, staged);
@@ -325,9 +325,11 @@ hipError_t launch_gemv1_front(const Gemv1Args &r, const Gemv1Args &d, hipStream_
   // one to four tokens
   if (!gemv1_ok(r, 4) || !gemv1_ok(d, 2) || r.K != d.K || r.xb != d.xb || d.ks != 1 || r.T != d.T)
     return hipErrorInvalidValue;
-  // two rows per wave item (28 KB of row bytes for both kinds): measured 0.6-0.8 us per
-  // decode step faster than one row
-  const int r_items = ((r.M + 1) / 2) * r.ks, items = r_items + (d.M + 1) / 2;
+  // 28 KB of row bytes per wave item for both kinds: one fp32 router row (K parts of it
+  // if r.ks > 1), two bf16 W_down rows. (Two W_down rows per item measured 0.6-0.8 us
+  // per decode step faster than one; one whole router row instead of two rows' K halves
+  // lets the selection read one partial sum per expert, 0.3-0.4 us faster.)
+  const int r_items = r.M * r.ks, items = r_items + (d.M + 1) / 2;
   const int waves = gemv1_waves(items, max_waves);
   const int grid = (items + waves - 1) / waves;
   // one or two tokens, both against one weight stream (three and four, with 84 and 112

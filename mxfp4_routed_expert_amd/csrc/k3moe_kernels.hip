@@ -638,7 +638,7 @@ __global__ __launch_bounds__(256) void k_grouped_dec(GroupedArgs a) {
       uint32_t key[16];
       float sc[16];
       bool real[16];
-      topk_keys_wave<16, 2>(a.tk, 0, key, sc, real);
+      topk_keys_wave<16, 1>(a.tk, 0, key, sc, real);
       topk_select_wave<16, true>(a.tk, 0, key, sc, real, s_scr, blockIdx.x == 0 && j == 0, j, &s_e);
     } else if (wave >= 2) {
       const int gz = (int)threadIdx.x - 128;
@@ -946,7 +946,7 @@ int grouped_dec_rb(int M, int grid_y, int epi, int ncu) {
 
 bool route_in_gateup_ok(const GroupedArgs &a) {
   const TopkArgs &t = a.tk;
-  return t.T == 1 && t.ks >= 1 && t.ks <= 2 && t.E >= 1 && t.E <= 1024 && t.K >= 1 && t.K <= t.E && t.K <= 64 &&
+  return t.T == 1 && t.ks == 1 && t.E >= 1 && t.E <= 1024 && t.K >= 1 && t.K <= t.E && t.K <= 64 &&
          t.L == a.K && a.K % 32 == 0 &&
          a.K <= 4096 && t.z && t.idx && t.w && t.expert_off && t.sorted_pair && t.pair_slot && t.active &&
          t.counters && ((uintptr_t)t.z & 15) == 0 && a.gather == 1;
