@@ -474,7 +474,9 @@ def main():
         copies.append(device.DeviceLayer(dims=dims, w_router=dev.w_router.clone(), bias=dev.bias.clone(),
                                          w_down=dev.w_down.clone(), w_up=dev.w_up.clone(),
                                          norm_w=dev.norm_w.clone(), experts=dev.experts,
-                                         blob_bytes=dev.blob_bytes, offsets=dev.offsets))
+                                         blob_bytes=dev.blob_bytes, offsets=dev.offsets,
+                                         gemm_scales=dev.gemm_scales))
+        copies[-1].prepare_router_planes()  # of this copy's own router weights
     wts_rot = [c.weights_struct() for c in copies]
     hip_record = ctypes.CDLL("libamdhip64.so").hipEventRecord
     hip_record.argtypes = [ctypes.c_void_p, ctypes.c_void_p]

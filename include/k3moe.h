@@ -144,6 +144,13 @@ typedef struct {
      * results are bit-identical either way. The copy must be remade when ex's scales
      * change. */
     const uint8_t *gemm_scales;
+    /* Optional (NULL: not used): the router weights as three bf16 planes, written by
+     * k3moe_prepare_router_planes from the same w_router, 16-byte aligned. Batches of 40
+     * tokens and more multiply the router on the bf16 matrix cores as these three pieces
+     * (whose sum is the fp32 weight); without the copy every such call first splits
+     * w_router into the workspace (about 16 us at K3's size). Results are bit-identical
+     * either way. The copy must be remade when w_router changes. */
+    const uint16_t *router_planes;
 } k3moe_weights;
 
 /* Host-only. Bytes of the turn-major scale copy for these dims (K3: about 0.97 GB). */
@@ -159,6 +166,20 @@ int k3moe_gemm_scales_size(const k3moe_dims *d, size_t *bytes);
  * per row. */
 int k3moe_prepare_gemm_scales(const k3moe_dims *d, const k3moe_experts *ex, void *dst, size_t bytes,
                               void *stream);
+
+/* Host-only. Bytes of the router plane copy for these dims: 3 * n_experts * hidden * 2
+ * (K3: about 38.5 MB). */
+int k3moe_router_planes_size(const k3moe_dims *d, size_t *bytes);
+
+/* Splits w_router ([E][H] fp32, 16-byte aligned) into three bf16 planes in dst (bytes >=
+ * k3moe_router_planes_size, 16-byte aligned, owned by the caller), on the stream; for
+ * k3moe_weights.router_planes. Not an operation of the layer: the same fp32 weights as
+ * three exact pieces, made once per router matrix. Layout: plane p at dst + p * E * H * 2,
+ * each [E][H] bf16; plane 0 is w rounded to bf16, plane 1 the remainder w - plane 0
+ * rounded to bf16, plane 2 the remainder after both (exact: an fp32 significand fits
+ * three bf16 ones). */
+int k3moe_prepare_router_planes(const k3moe_dims *d, const float *w_router, void *dst, size_t bytes,
+                                void *stream);
 
 /* Host-only. Bytes of workspace every entry point below needs for this dims and T.
  * Returns K3MOE_EINVAL / K3MOE_EUNSUPPORTED for bad arguments. */

@@ -250,13 +250,19 @@ void mark(const char *name) {
 // ---- step launchers (arguments already checked)
 
 // The router's three weight planes (row segments 0..2) and optionally W_down
-// (segment 3), all against x. Returns the number of router partial-logit arrays left in
-// w.router_part for the top-k (3, one per plane; or 1 where K parts were summed).
+// (segment 3), all against x. The planes are the caller's copy (k3moe_prepare_router_planes)
+// when given, else split from wr into the workspace first. Returns the number of router
+// partial-logit arrays left in w.router_part for the top-k (3, one per plane; or 1 where
+// K parts were summed).
 int run_route_down_mm(const k3moe_dims *d, int32_t T, const uint16_t *x, const float *wr,
-                      const uint16_t *wd, float *z, const Ws &w, int *parts, hipStream_t s) {
+                      const uint16_t *planes, const uint16_t *wd, float *z, const Ws &w, int *parts,
+                      hipStream_t s) {
   const size_t EH = (size_t)d->n_experts * d->hidden;
-  K3_HIP(launch_split_planes(wr, EH, w.wr_planes, w.wr_planes + EH, w.wr_planes + 2 * EH, s));
-  mark("router_weight_split");
+  if (!planes) {
+    K3_HIP(launch_split_planes(wr, EH, w.wr_planes, w.wr_planes + EH, w.wr_planes + 2 * EH, s));
+    mark("router_weight_split");
+    planes = w.wr_planes;
+  }
   DenseMmArgs a = {};
   const int E = d->n_experts, L = d->latent;
   // K parts (the count for the full front, with or without W_down, so that the part
@@ -265,7 +271,7 @@ int run_route_down_mm(const k3moe_dims *d, int32_t T, const uint16_t *x, const f
   const int64_t rs = (int64_t)T * E, zs = (int64_t)T * L;
   // plane p's K part k at router_part + (p * ks + k) * T * E
   for (int p = 0; p < 3; ++p)
-    a.seg[p] = DenseSeg{w.wr_planes + p * EH, p * E, E, w.router_part + (size_t)p * ks * rs, E, rs};
+    a.seg[p] = DenseSeg{planes + p * EH, p * E, E, w.router_part + (size_t)p * ks * rs, E, rs};
   a.nseg = 3;
   a.M = 3 * E;
   if (wd) {
@@ -395,7 +401,7 @@ int run_route(const k3moe_dims *d, int32_t T, const uint16_t *x, const float *wr
               int32_t *idx, float *wt, const Ws &w, hipStream_t s) {
   int splits = kRouterSplits;
   if (use_front_mm(d, T)) {
-    K3_TRY(run_route_down_mm(d, T, x, wr, nullptr, nullptr, w, &splits, s));
+    K3_TRY(run_route_down_mm(d, T, x, wr, nullptr, nullptr, nullptr, w, &splits, s));
   } else if (use_gemv1(d, T, x)) {
     K3_HIP(launch_gemv1(router1_args(d, x, wr, w), kA_F32, kX_BF16, kEpiStore, 1, s));
     splits = kRouterParts1;
@@ -420,7 +426,7 @@ int run_front(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_wei
     // GEMM form: router planes and W_down in one launch, then the top-k, whose spare
     // waves quantize z
     int parts = 3;
-    K3_TRY(run_route_down_mm(d, T, x, wt->w_router, wt->w_down, w.z32, w, &parts, s));
+    K3_TRY(run_route_down_mm(d, T, x, wt->w_router, wt->router_planes, wt->w_down, w.z32, w, &parts, s));
     mark("router_and_latent_down");
     TopkArgs tk = topk_args(d, T, w.router_part, parts, wt->bias, idx, tw);
     // (with int8 activations z is rounded and quantized by the expert pass instead)
@@ -962,6 +968,25 @@ int k3moe_prepare_gemm_scales(const k3moe_dims *d, const k3moe_experts *ex, void
   return K3MOE_OK;
 }
 
+int k3moe_router_planes_size(const k3moe_dims *d, size_t *bytes) {
+  K3_TRY(check_dims(d));
+  if (!bytes) return K3MOE_EINVAL;
+  *bytes = (size_t)3 * d->n_experts * d->hidden * 2;
+  return K3MOE_OK;
+}
+
+int k3moe_prepare_router_planes(const k3moe_dims *d, const float *w_router, void *dst, size_t bytes,
+                                void *stream) {
+  K3_TRY(check_dims(d));
+  if (!w_router || !dst) return K3MOE_EINVAL;
+  if (!al16(w_router) || !al16(dst)) return K3MOE_EUNSUPPORTED;
+  const size_t EH = (size_t)d->n_experts * d->hidden;
+  if (bytes < 3 * EH * 2) return K3MOE_EWORKSPACE;
+  uint16_t *o = (uint16_t *)dst;
+  K3_HIP(launch_split_planes(w_router, EH, o, o + EH, o + 2 * EH, (hipStream_t)stream));
+  return K3MOE_OK;
+}
+
 int k3moe_workspace_size(const k3moe_dims *d, int32_t T, size_t *bytes) {
   K3_TRY(check_dims(d));
   K3_TRY(check_T(d, T));
@@ -1050,7 +1075,7 @@ int k3moe_layer(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_w
   K3_TRY(check_mx(wt->ex.w3));
   K3_TRY(check_mx(wt->ex.w2));
   if (!al16(x) || !al16(wt->w_router) || !al16(wt->w_down) || !al16(wt->w_up) ||
-      ((uintptr_t)wt->gemm_scales & 255u) != 0)
+      ((uintptr_t)wt->gemm_scales & 255u) != 0 || !al16(wt->router_planes))
     return K3MOE_EUNSUPPORTED;
   Ws w;
   K3_TRY(check_ws(d, T, ws, ws_bytes, &w));

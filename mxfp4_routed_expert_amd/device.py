@@ -27,6 +27,7 @@ class DeviceLayer:
     blob_bytes: int
     offsets: dict
     gemm_scales: torch.Tensor | None = None  # the experts' scales turn-major (k3moe_prepare_gemm_scales)
+    router_planes: torch.Tensor | None = None  # w_router as three bf16 planes (k3moe_prepare_router_planes)
 
     def experts_struct(self) -> k3moe.k3moe_experts:
         base = self.experts.data_ptr()
@@ -36,11 +37,20 @@ class DeviceLayer:
             return k3moe.k3moe_mxfp4(base + self.offsets[p], base + self.offsets[s], B, B)
         return k3moe.k3moe_experts(mx("w1p", "w1s"), mx("w3p", "w3s"), mx("w2p", "w2s"))
 
-    def weights_struct(self, gemm_scales: bool = True) -> k3moe.k3moe_weights:
-        """gemm_scales=False leaves the turn-major copy out (the GEMM then reads the plain scales)."""
+    def weights_struct(self, gemm_scales: bool = True, router_planes: bool = True) -> k3moe.k3moe_weights:
+        """gemm_scales=False leaves the turn-major copy out (the GEMM then reads the plain scales);
+        router_planes=False leaves the router plane copy out (split on every call instead)."""
         gs = self.gemm_scales.data_ptr() if (gemm_scales and self.gemm_scales is not None) else None
+        rp = self.router_planes.data_ptr() if (router_planes and self.router_planes is not None) else None
         return k3moe.k3moe_weights(self.w_router.data_ptr(), self.bias.data_ptr(), self.w_down.data_ptr(),
-                                   self.w_up.data_ptr(), self.norm_w.data_ptr(), self.experts_struct(), gs)
+                                   self.w_up.data_ptr(), self.norm_w.data_ptr(), self.experts_struct(), gs, rp)
+
+    def prepare_router_planes(self):
+        """Allocate and fill the router's three bf16 planes (once per router matrix)."""
+        n = k3moe.k3moe_router_planes_size(self.dims)
+        self.router_planes = torch.empty(max(n, 16) // 2, dtype=torch.int16, device=self.w_router.device)
+        k3moe.k3moe_prepare_router_planes(self.dims, self.w_router, self.router_planes)
+        torch.cuda.synchronize(self.w_router.device)
 
     def prepare_gemm_scales(self):
         """Allocate and fill the turn-major scale copy (once per set of expert weights)."""
@@ -51,11 +61,12 @@ class DeviceLayer:
 
 
 def upload_layer(dims, dense: dict, expert_chunks, blob_bytes: int, offsets: dict, device="cuda",
-                 gemm_scales: bool = True) -> DeviceLayer:
+                 gemm_scales: bool = True, router_planes: bool = True) -> DeviceLayer:
     """dense: host arrays (w_router fp32 [E,H], bias fp32 [E], w_down/w_up bf16 bits, norm_w fp32).
     expert_chunks: iterable of (first expert, uint8 blob array) covering experts 0..E-1 in order;
     each chunk is copied into one preallocated device buffer, so host memory stays at one chunk.
-    gemm_scales: also make the turn-major scale copy that the prefill GEMM reads."""
+    gemm_scales: also make the turn-major scale copy that the prefill GEMM reads.
+    router_planes: also make the router's bf16 plane copy that the front's GEMM form reads."""
     E = dims.n_experts
     ex = torch.empty(E * blob_bytes, dtype=torch.uint8, device=device)
     for e0, arr in expert_chunks:
@@ -71,6 +82,8 @@ def upload_layer(dims, dense: dict, expert_chunks, blob_bytes: int, offsets: dic
         experts=ex, blob_bytes=blob_bytes, offsets=dict(offsets))
     if gemm_scales:
         layer.prepare_gemm_scales()
+    if router_planes:
+        layer.prepare_router_planes()
     return layer
 
 

@@ -46,13 +46,14 @@ class k3moe_experts(ctypes.Structure):
 class k3moe_weights(ctypes.Structure):
     _fields_ = [("w_router", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
                 ("w_up", ctypes.c_void_p), ("norm_w", ctypes.c_void_p), ("ex", k3moe_experts),
-                ("gemm_scales", ctypes.c_void_p)]
+                ("gemm_scales", ctypes.c_void_p), ("router_planes", ctypes.c_void_p)]
 
 
 EXPORTS = ["k3moe_workspace_size", "k3moe_route", "k3moe_latent_proj_bf16", "k3moe_dispatch",
            "k3moe_expert_glu_mxfp4", "k3moe_combine", "k3moe_layer", "k3moe_layer_noalloc",
            "k3moe_shared_workspace_size", "k3moe_shared_glu_bf16", "k3moe_gemm_scales_size",
-           "k3moe_prepare_gemm_scales", "k3moe_status_str"]
+           "k3moe_prepare_gemm_scales", "k3moe_router_planes_size", "k3moe_prepare_router_planes",
+           "k3moe_status_str"]
 
 _lib = None
 
@@ -79,6 +80,8 @@ def load(path: str | None = None):
     L.k3moe_workspace_size.argtypes = [D, i32, ctypes.POINTER(sz)]
     L.k3moe_gemm_scales_size.argtypes = [D, ctypes.POINTER(sz)]
     L.k3moe_prepare_gemm_scales.argtypes = [D, ctypes.POINTER(k3moe_experts), vp, sz, vp]
+    L.k3moe_router_planes_size.argtypes = [D, ctypes.POINTER(sz)]
+    L.k3moe_prepare_router_planes.argtypes = [D, vp, vp, sz, vp]
     L.k3moe_route.argtypes = [D, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     L.k3moe_latent_proj_bf16.argtypes = [D, i32, vp, vp, vp, vp, sz, vp]
     L.k3moe_dispatch.argtypes = [D, i32, vp, vp, vp, vp, vp, sz, vp]
@@ -176,6 +179,22 @@ def k3moe_prepare_gemm_scales(dims, experts: k3moe_experts, dst, stream=None, ch
     rc = load().k3moe_prepare_gemm_scales(ctypes.byref(_dims(dims)), ctypes.byref(experts), p, n, _stream(stream))
     if check:
         _check(rc, "k3moe_prepare_gemm_scales")
+    return rc
+
+
+def k3moe_router_planes_size(dims) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().k3moe_router_planes_size(ctypes.byref(_dims(dims)), ctypes.byref(n)), "k3moe_router_planes_size")
+    return n.value
+
+
+def k3moe_prepare_router_planes(dims, w_router, dst, stream=None, check=True):
+    """w_router: device fp32 [E][H]; dst: a device buffer (tensor, or (pointer, bytes)) of
+    k3moe_router_planes_size bytes."""
+    p, n = _ws(dst)
+    rc = load().k3moe_prepare_router_planes(ctypes.byref(_dims(dims)), _ptr(w_router), p, n, _stream(stream))
+    if check:
+        _check(rc, "k3moe_prepare_router_planes")
     return rc
 
 

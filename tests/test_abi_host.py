@@ -121,6 +121,21 @@ def test_gemm_scales_size_and_refusals():
     assert k3moe.k3moe_layer(d, 4, FAKE, w, FAKE, None, None, WS, check=False) == k3moe.K3MOE_EUNSUPPORTED
 
 
+def test_router_planes_size_and_refusals():
+    d = _d()
+    n = k3moe.k3moe_router_planes_size(d)
+    assert n == 3 * d.n_experts * d.hidden * 2  # three bf16 planes of [E][H]
+    f = k3moe.k3moe_prepare_router_planes
+    assert f(d, FAKE, None, check=False) == k3moe.K3MOE_EINVAL
+    assert f(d, None, (FAKE, n), check=False) == k3moe.K3MOE_EINVAL
+    assert f(d, FAKE, (FAKE, n - 1), check=False) == k3moe.K3MOE_EWORKSPACE
+    assert f(d, FAKE, (FAKE + 8, n), check=False) == k3moe.K3MOE_EUNSUPPORTED
+    assert f(d, FAKE + 4, (FAKE, n), check=False) == k3moe.K3MOE_EUNSUPPORTED
+    # the layer refuses a plane copy that is not 16-byte aligned
+    w = k3moe.k3moe_weights(FAKE, FAKE, FAKE, FAKE, FAKE, _experts(), None, FAKE + 8)
+    assert k3moe.k3moe_layer(d, 4, FAKE, w, FAKE, None, None, WS, check=False) == k3moe.K3MOE_EUNSUPPORTED
+
+
 def test_other_entry_points_refuse_before_launch():
     d = _d()
     assert k3moe.k3moe_latent_proj_bf16(d, 4, FAKE, None, FAKE, WS, check=False) == k3moe.K3MOE_EINVAL

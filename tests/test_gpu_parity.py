@@ -107,7 +107,7 @@ def t_(a, dtype=None):
     return t if dtype is None else t.to(dtype)
 
 
-def run_layer(h: Host, x: np.ndarray, gemm_scales: bool = True):
+def run_layer(h: Host, x: np.ndarray, gemm_scales: bool = True, router_planes: bool = True):
     d = h.dims
     T = x.shape[0]
     xd = t_(x.view(np.int16))
@@ -115,7 +115,7 @@ def run_layer(h: Host, x: np.ndarray, gemm_scales: bool = True):
     idx = torch.empty((T, d.topk), dtype=torch.int32, device="cuda")
     w = torch.empty((T, d.topk), dtype=torch.float32, device="cuda")
     ws = device.workspace(d, T)
-    k3moe.k3moe_layer(d, T, xd, h.dev.weights_struct(gemm_scales), y, idx, w, ws)
+    k3moe.k3moe_layer(d, T, xd, h.dev.weights_struct(gemm_scales, router_planes), y, idx, w, ws)
     torch.cuda.synchronize()
     return y.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
 
@@ -503,6 +503,53 @@ def test_gemm_scales_ignored_by_gemv_form(tiny_mm, expert_path):
     y1, _, _ = run_layer(tiny_mm, x, gemm_scales=True)
     y0, _, _ = run_layer(tiny_mm, x, gemm_scales=False)
     assert np.array_equal(y0.view(np.uint32), y1.view(np.uint32))
+
+
+def bf16_round_bits(v: np.ndarray) -> np.ndarray:
+    """The bf16 nearest to each finite fp32 value (ties to the even significand), as the
+    upper 16 bits of its fp32 pattern."""
+    u = v.astype(np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def bf16_to_f64(b: np.ndarray) -> np.ndarray:
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+@pytest.mark.parametrize("which", ["tiny_mm", "k3"])
+def test_router_planes_exact_split(which, request):
+    """k3moe_prepare_router_planes: plane 0 is each router weight rounded to the nearest
+    bf16, plane 1 the remainder rounded to bf16, and the three planes sum to the fp32
+    weight exactly."""
+    h = request.getfixturevalue(which)
+    say(f"router planes of {which}")
+    E, H = h.dims.n_experts, h.dims.hidden
+    assert k3moe.k3moe_router_planes_size(h.dims) == 3 * E * H * 2
+    p = h.dev.router_planes.cpu().numpy().view(np.uint16)[:3 * E * H].reshape(3, E, H)
+    w = h.dense["w_router"].astype(np.float32)
+    assert np.array_equal(p[0], bf16_round_bits(w))
+    r1 = (w.astype(np.float64) - bf16_to_f64(p[0])).astype(np.float32)  # exact in fp32
+    assert np.array_equal(p[1], bf16_round_bits(r1))
+    total = bf16_to_f64(p[0]) + bf16_to_f64(p[1]) + bf16_to_f64(p[2])
+    assert np.array_equal(total, w.astype(np.float64))
+
+
+@pytest.mark.parametrize("which,T", [("tiny_mm", 64), ("tiny_mm", 300), ("k3", 64)])
+def test_router_planes_copy_or_not_same_result(which, T, request):
+    """The front's GEMM form (40 tokens and more) reading the caller's plane copy or
+    splitting the router weights itself gives the same bits; the split path is checked
+    against the oracle as well."""
+    h = request.getfixturevalue(which)
+    say(f"{which} T={T} front GEMM with and without the router plane copy")
+    x, _ = _inputs.gap_fixed_x(h.dims, 400 + T, T, h.dense["w_router"], h.dense["bias"])
+    y1, i1, w1 = run_layer(h, x, router_planes=True)
+    y0, i0, w0 = run_layer(h, x, router_planes=False)
+    assert np.array_equal(i0, i1) and np.array_equal(w0.view(np.uint32), w1.view(np.uint32))
+    assert np.array_equal(y0.view(np.uint32), y1.view(np.uint32))
+    rows = np.arange(T) if T <= 64 else np.arange(0, T, 5)
+    ref = oracle.layer(h.dims, x[rows], h.dense, h.ex)
+    assert np.array_equal(i0[rows], ref["idx"])
+    check_rows(y0[rows], ref["y"], f"{which} T={T} split router planes y")
 
 
 def test_k3_layer_T64_grouped_gemm(k3, expert_path):
