@@ -239,10 +239,10 @@ int k3moe_layer(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_w
  * device that runs the call holds it until the process ends; its address is looked up
  * on the call's first use on that device). Batches whose k3moe_workspace_size exceeds
  * that size are refused with K3MOE_EWORKSPACE before anything runs (at the K3 shape, up
- * to 32 tokens fit). The array's content on entry does not matter. All calls on one
+ * to 39 tokens fit). The array's content on entry does not matter. All calls on one
  * device share its array: calls that overlap on one device (on two streams, or from two
  * threads without ordering) race and give unspecified results. */
-#define K3MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+#define K3MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
 int k3moe_layer_noalloc(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_weights *w,
                         float *y, int32_t *topk_idx_out, float *topk_w_out, void *stream);
 

@@ -116,16 +116,22 @@ bool dense_mm_fits(const k3moe_dims *d, int32_t T) {
 
 bool use_dense_mm(const k3moe_dims *d, int32_t T) { return T >= kDenseMmMinT && dense_mm_fits(d, T); }
 
-// The router and latent projection run as one GEMM (the router's fp32 weights split into
-// three bf16 planes per call) from this many tokens on, their K split among blocks below
-// about 512 tiles: measured faster than the GEMV forms from 40 tokens (71 against 80 us;
-// at 32 tokens 70 against 65 us).
+// The router and latent projection run as one GEMM, their K split among blocks below
+// about 512 tiles, from this many tokens on: with the router's fp32 weights split into
+// three bf16 planes per call, from 40 tokens (measured 71 against 80 us for the GEMV
+// forms; at 32 tokens 70 against 65 us); with the caller's plane copy, from 16 tokens
+// (front 35 against 37 us at 16 tokens, 38 against 57 us at 32; at 8, 36 against 34 us).
 #ifndef K3_FRONT_MM_MIN_T
 #define K3_FRONT_MM_MIN_T 40
 #endif
+#ifndef K3_FRONT_MM_PLANES_MIN_T
+#define K3_FRONT_MM_PLANES_MIN_T 16
+#endif
 constexpr int kFrontMmMinT = K3_FRONT_MM_MIN_T;
-bool use_front_mm(const k3moe_dims *d, int32_t T) {
-  return T >= kFrontMmMinT && d->n_experts % 64 == 0 && dense_mm_fits(d, T);
+constexpr int kFrontMmPlanesMinT = K3_FRONT_MM_PLANES_MIN_T;
+constexpr int kFrontMmAnyMinT = kFrontMmMinT < kFrontMmPlanesMinT ? kFrontMmMinT : kFrontMmPlanesMinT;
+bool use_front_mm(const k3moe_dims *d, int32_t T, bool planes) {
+  return T >= (planes ? kFrontMmPlanesMinT : kFrontMmMinT) && d->n_experts % 64 == 0 && dense_mm_fits(d, T);
 }
 // rows of the front GEMM: three router planes, then W_down
 int front_rows(const k3moe_dims *d) { return 3 * d->n_experts + d->latent; }
@@ -187,7 +193,7 @@ Ws carve(const k3moe_dims *d, int32_t T, void *base) {
   const size_t nch = (t + 63) / 64;
   // router partial logits: the GEMV forms' K parts, or the GEMM form's three planes times
   // its K parts (sized for the largest count of any batch up to T)
-  const int64_t front_parts = T >= kFrontMmMinT ? dense_mm_parts_max(front_rows(d), d->hidden, T) : 0;
+  const int64_t front_parts = T >= kFrontMmAnyMinT ? dense_mm_parts_max(front_rows(d), d->hidden, T) : 0;
   w.router_part = (float *)take((size_t)std::max<int64_t>(kRouterSplits * (int64_t)t, 3 * front_parts) * E * 4);
   w.z32 = (float *)take(t * L * 4);
   w.zq = (uint8_t *)take(t * L * 4);
@@ -205,8 +211,9 @@ Ws carve(const k3moe_dims *d, int32_t T, void *base) {
   w.edn = (float *)take(P * L * 4);
   for (int q = 0; q < 3; ++q) w.np[q] = (uint16_t *)take(t * L * 2);
   w.ss = (float *)take(t * combine_norm_parts(L) * 4);
+  // the per-call split of the router weights (when the caller gives no plane copy)
   w.wr_planes = T >= kFrontMmMinT ? (uint16_t *)take(3 * E * (size_t)d->hidden * 2) : nullptr;
-  w.z_parts = T >= kFrontMmMinT ? (float *)take((size_t)front_parts * L * 4) : nullptr;
+  w.z_parts = T >= kFrontMmAnyMinT ? (float *)take((size_t)front_parts * L * 4) : nullptr;
   // sized for the largest K-part count of any batch up to T (nondecreasing in T)
   w.up_parts = T >= 2 ? (float *)take((size_t)dense_mm_parts_max(d->hidden, d->latent, T) * (size_t)d->hidden * 4)
                       : nullptr;
@@ -259,6 +266,7 @@ int run_route_down_mm(const k3moe_dims *d, int32_t T, const uint16_t *x, const f
                       hipStream_t s) {
   const size_t EH = (size_t)d->n_experts * d->hidden;
   if (!planes) {
+    if (!w.wr_planes) return K3MOE_EINVAL;  // (not carved below the split form's batch size)
     K3_HIP(launch_split_planes(wr, EH, w.wr_planes, w.wr_planes + EH, w.wr_planes + 2 * EH, s));
     mark("router_weight_split");
     planes = w.wr_planes;
@@ -400,7 +408,7 @@ TopkArgs topk_args(const k3moe_dims *d, int32_t T, const float *part, int ks, co
 int run_route(const k3moe_dims *d, int32_t T, const uint16_t *x, const float *wr, const float *bias,
               int32_t *idx, float *wt, const Ws &w, hipStream_t s) {
   int splits = kRouterSplits;
-  if (use_front_mm(d, T)) {
+  if (use_front_mm(d, T, false)) {
     K3_TRY(run_route_down_mm(d, T, x, wr, nullptr, nullptr, nullptr, w, &splits, s));
   } else if (use_gemv1(d, T, x)) {
     K3_HIP(launch_gemv1(router1_args(d, x, wr, w), kA_F32, kX_BF16, kEpiStore, 1, s));
@@ -422,7 +430,7 @@ int run_route(const k3moe_dims *d, int32_t T, const uint16_t *x, const float *wr
 int run_front(const k3moe_dims *d, int32_t T, const uint16_t *x, const k3moe_weights *wt, int32_t *idx,
               float *tw, const Ws &w, bool *zq_ready, TopkArgs *route, hipStream_t s) {
   const DenseArgs down = down_args(d, T, x, wt->w_down, w.z32);
-  if (use_front_mm(d, T)) {
+  if (use_front_mm(d, T, wt->router_planes != nullptr)) {
     // GEMM form: router planes and W_down in one launch, then the top-k, whose spare
     // waves quantize z
     int parts = 3;

@@ -255,7 +255,7 @@ def k3moe_layer(dims, T, x, weights: k3moe_weights, y, topk_idx_out, topk_w_out,
     return rc
 
 
-NOALLOC_SCRATCH_BYTES = 32 << 20  # K3MOE_NOALLOC_SCRATCH_BYTES
+NOALLOC_SCRATCH_BYTES = 64 << 20  # K3MOE_NOALLOC_SCRATCH_BYTES
 
 
 def k3moe_layer_noalloc(dims, T, x, weights: k3moe_weights, y, topk_idx_out, topk_w_out, stream=None, check=True):

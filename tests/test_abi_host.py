@@ -252,6 +252,10 @@ def test_noalloc_refuses_on_the_host():
     L = k3moe.load()
     fake = FAKE
     w = k3moe.k3moe_weights(fake, fake, fake, fake, fake, _experts())
+    hdr = open(os.path.join(INCLUDE, "k3moe.h")).read()
+    m = re.search(r"#define K3MOE_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", hdr)
+    assert m and k3moe.NOALLOC_SCRATCH_BYTES == int(m.group(1)) << int(m.group(2))
+    assert k3moe.k3moe_workspace_size(k3gen.K3, 39) <= k3moe.NOALLOC_SCRATCH_BYTES
     assert k3moe.k3moe_workspace_size(k3gen.K3, 64) > k3moe.NOALLOC_SCRATCH_BYTES
     assert k3moe.k3moe_layer_noalloc(k3gen.K3, 64, fake, w, fake, None, None, check=False) == k3moe.K3MOE_EWORKSPACE
     assert k3moe.k3moe_layer_noalloc(_d(hidden=0), 4, fake, w, fake, None, None, check=False) == k3moe.K3MOE_EINVAL

@@ -552,6 +552,21 @@ def test_router_planes_copy_or_not_same_result(which, T, request):
     check_rows(y0[rows], ref["y"], f"{which} T={T} split router planes y")
 
 
+@pytest.mark.parametrize("which,T", [("tiny_mm", 15), ("tiny_mm", 39), ("k3", 16), ("k3", 32)])
+def test_front_form_by_plane_copy(which, T, request):
+    """Below 40 tokens the front runs as a GEMM only when the caller gives the router
+    plane copy (from 16 tokens), else as the GEMV forms: both against the oracle."""
+    h = request.getfixturevalue(which)
+    x, _ = _inputs.gap_fixed_x(h.dims, 500 + T, T, h.dense["w_router"], h.dense["bias"])
+    ref = oracle.layer(h.dims, x, h.dense, h.ex)
+    for planes in (True, False):
+        say(f"{which} T={T} front with router plane copy={planes}")
+        y, idx, w = run_layer(h, x, router_planes=planes)
+        assert np.array_equal(idx, ref["idx"])
+        check_rows(w, ref["w"], f"{which} T={T} planes={planes} weights", rel=1e-6, absf=1e-6)
+        check_rows(y, ref["y"], f"{which} T={T} planes={planes} y")
+
+
 def test_k3_layer_T64_grouped_gemm(k3, expert_path):
     expert_path(k3moe.EXPERT_PATH_GEMM)
     x, _ = _inputs.gap_fixed_x(k3.dims, 2, 64, k3.dense["w_router"], k3.dense["bias"])
