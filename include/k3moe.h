@@ -145,11 +145,13 @@ typedef struct {
      * change. */
     const uint8_t *gemm_scales;
     /* Optional (NULL: not used): the router weights as three bf16 planes, written by
-     * k3moe_prepare_router_planes from the same w_router, 16-byte aligned. Batches of 40
-     * tokens and more multiply the router on the bf16 matrix cores as these three pieces
+     * k3moe_prepare_router_planes from the same w_router, 16-byte aligned. The router of
+     * a batch of 40 tokens and more runs on the bf16 matrix cores as these three pieces
      * (whose sum is the fp32 weight); without the copy every such call first splits
-     * w_router into the workspace (about 16 us at K3's size). Results are bit-identical
-     * either way. The copy must be remade when w_router changes. */
+     * w_router into the workspace (about 16 us at K3's size), with it the split is skipped
+     * and bits are identical. With the copy, batches of 16 to 39 tokens take the matrix-core
+     * form too (without it, the vector-ALU form): the same result up to fp32 summation
+     * order. The copy must be remade when w_router changes. */
     const uint16_t *router_planes;
 } k3moe_weights;
 
