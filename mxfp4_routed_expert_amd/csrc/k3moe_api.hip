@@ -296,10 +296,10 @@ int run_route_down_mm(const k3moe_dims *d, int32_t T, const uint16_t *x, const f
   *parts = 3;
   if (ks > 1) {
     mark("router_and_latent_down");
-    // the 3 * ks partial logits summed in place into the first (plane order, then part order)
-    K3_HIP(launch_add_parts(w.router_part, 3 * ks, rs, w.router_part, rs, false, s));
+    // the 3 * ks partial logits summed in place into the first (plane order, then part
+    // order), and z's K parts, in one launch
+    K3_HIP(launch_add_parts2(w.router_part, 3 * ks, rs, w.router_part, rs, w.z_parts, ks, zs, z, wd ? zs : 0, s));
     *parts = 1;
-    if (wd) K3_HIP(launch_add_parts(w.z_parts, ks, zs, z, zs, false, s));
     mark("front_parts_sum");
   }
   return K3MOE_OK;

@@ -253,6 +253,9 @@ hipError_t launch_glu_pieces(const float *gu, int ks, int64_t part_stride, int T
 // accumulate: add to y, else overwrite it (y may then be parts itself)
 hipError_t launch_add_parts(const float *parts, int ks, int64_t stride, float *y, int64_t n, bool accumulate,
                             hipStream_t s);
+// Two sums of K parts (as launch_add_parts without accumulation) in one launch.
+hipError_t launch_add_parts2(const float *pa, int ksa, int64_t sa, float *ya, int64_t na, const float *pb,
+                             int ksb, int64_t sb, float *yb, int64_t nb, hipStream_t s);
 // tokens_per_tile: 1, 2 or 4 tokens' piece records staged in LDS per tile (grouped_dec_lds bytes)
 constexpr size_t kMaxBlockLds = 81920;  // two blocks per compute unit
 // rb: 16-row blocks per block (4, 6 or 8 for kEpiSitu; 4 to 8 for kEpiEdn), from grouped_dec_rb

@@ -507,12 +507,13 @@ hipError_t launch_glu_pieces(const float *gu, int ks, int64_t part_stride, int T
   return hipGetLastError();
 }
 
-// y (+)= the sum of the K parts of a product, four values per thread. y may be part 0
-// itself (each thread reads its values of every part before it writes them).
+// y (+)= the sum of the K parts of a product, four values per thread, over the float4
+// indices q0, q0 + qstep, ... below n4. y may be part 0 itself (each thread reads its
+// values of every part before it writes them).
 template <bool ACC>
-__global__ __launch_bounds__(256) void k_add_parts(const float *parts, int ks, int64_t stride, float *y,
-                                                   int64_t n4) {
-  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < n4; q += (int64_t)gridDim.x * blockDim.x) {
+__device__ __forceinline__ void add_parts_range(const float *parts, int ks, int64_t stride, float *y, int64_t n4,
+                                                int64_t q0, int64_t qstep) {
+  for (int64_t q = q0; q < n4; q += qstep) {
     float4 v = *(const float4 *)(parts + 4 * q);
     int p = 1;
     // eight parts' loads in flight at a time, added in part order
@@ -538,6 +539,26 @@ __global__ __launch_bounds__(256) void k_add_parts(const float *parts, int ks, i
   }
 }
 
+template <bool ACC>
+__global__ __launch_bounds__(256) void k_add_parts(const float *parts, int ks, int64_t stride, float *y,
+                                                   int64_t n4) {
+  add_parts_range<ACC>(parts, ks, stride, y, n4, (int64_t)blockIdx.x * blockDim.x + threadIdx.x,
+                       (int64_t)gridDim.x * blockDim.x);
+}
+
+// Two independent sums of K parts in one launch (the front's router logits and its
+// latent projection): blocks 0 .. ba-1 take the first, the others the second.
+__global__ __launch_bounds__(256) void k_add_parts2(const float *pa, int ksa, int64_t sa, float *ya, int64_t na4,
+                                                    int ba, const float *pb, int ksb, int64_t sb, float *yb,
+                                                    int64_t nb4) {
+  const int b = (int)blockIdx.x;
+  if (b < ba)
+    add_parts_range<false>(pa, ksa, sa, ya, na4, (int64_t)b * blockDim.x + threadIdx.x, (int64_t)ba * blockDim.x);
+  else
+    add_parts_range<false>(pb, ksb, sb, yb, nb4, (int64_t)(b - ba) * blockDim.x + threadIdx.x,
+                           (int64_t)((int)gridDim.x - ba) * blockDim.x);
+}
+
 hipError_t launch_add_parts(const float *parts, int ks, int64_t stride, float *y, int64_t n, bool accumulate,
                             hipStream_t s) {
   if (n <= 0) return hipSuccess;
@@ -548,6 +569,20 @@ hipError_t launch_add_parts(const float *parts, int ks, int64_t stride, float *y
     launch_kernel(k_add_parts<true>, (unsigned)blocks, 256, 0, s, parts, ks, stride, y, n / 4);
   else
     launch_kernel(k_add_parts<false>, (unsigned)blocks, 256, 0, s, parts, ks, stride, y, n / 4);
+  return hipGetLastError();
+}
+
+hipError_t launch_add_parts2(const float *pa, int ksa, int64_t sa, float *ya, int64_t na, const float *pb,
+                             int ksb, int64_t sb, float *yb, int64_t nb, hipStream_t s) {
+  if (nb <= 0) return launch_add_parts(pa, ksa, sa, ya, na, false, s);
+  if (na <= 0) return launch_add_parts(pb, ksb, sb, yb, nb, false, s);
+  if (ksa < 1 || na % 4 != 0 || (ksa > 1 && sa < na)) return hipErrorInvalidValue;
+  if (ksb < 1 || nb % 4 != 0 || (ksb > 1 && sb < nb)) return hipErrorInvalidValue;
+  int64_t ba = (na / 4 + 255) / 256, bb = (nb / 4 + 255) / 256;
+  if (ba > 8192) ba = 8192;
+  if (bb > 8192) bb = 8192;
+  launch_kernel(k_add_parts2, (unsigned)(ba + bb), 256, 0, s, pa, ksa, sa, ya, na / 4, (int)ba, pb, ksb, sb, yb,
+                nb / 4);
   return hipGetLastError();
 }
 
